@@ -1,0 +1,52 @@
+"""Build libuno.so (HIP, gfx950) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libuno.so")
+SOURCES = ["uno_api.cpp", "filter_kernels.hip", "sample_kernels.hip"]
+HEADERS = ["uno_device.h", "uno_internal.h", os.path.join("..", "..", "include", "uno.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    # packed fp32 ops stay off (see DESIGN notes on packed-math traps)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    srcs = []
+    for s in SOURCES:
+        p = os.path.join(CSRC, s)
+        srcs += (["-x", "hip", p] if s.endswith(".hip") else ["-x", "hip", p])
+    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include"), "-o", tmp] + srcs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed (exit %d)" % res.returncode)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    for s in SOURCES + HEADERS:
+        if os.path.getmtime(os.path.join(CSRC, s)) > t:
+            return True
+    return False
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,817 @@
+// sample_kernels.hip -- proposal / rejection / residual sampling, tree build and
+// tree walk for the UNO decode cycle on gfx950.
+//
+// Method: SGLang PR #37667 ("native SGLang serving support for UNO"),
+// Motivation (linear and tree samplers) and Modifications (sparse and dense
+// proposal + rejection sampling; tree sampling with EAGLE tree verification and
+// sparse target sampling); the run_math_eval walk-through's startup
+// constraints fix both acceptance thresholds at 1.0.
+//
+// Sampling from a distribution is an inverse CDF in ascending token-id order.
+// Sparse supports (<= 256 ids) are sorted by id in LDS and scanned
+// sequentially in double precision, which reproduces the reference arithmetic
+// exactly.  Dense rows are located chunk by chunk from per-chunk statistics and
+// finished inside one 2048-logit chunk.
+#include "uno_device.h"
+#include "uno_internal.h"
+
+#include <math.h>
+
+namespace uno {
+
+namespace {
+
+constexpr int kMaxK = 256;
+constexpr int kMaxLinearB = 128;
+constexpr int kMaxNodes = 129;          // V + 1 with V <= 128
+constexpr int kFrontierCap = 192;       // >= V + 2, three slots per lane
+
+// ---- sparse helpers ------------------------------------------------------------
+// Copy a support (filter order) into LDS sorted by token id.
+__device__ void stage_sorted_by_id(const int32_t* ids_in, const double* p_in, int n, int32_t* raw,
+                                   int32_t* out_id, double* out_p, int lane)
+{
+    for (int i = lane; i < n; i += kWave) raw[i] = ids_in[i];
+    wave_sync();
+    for (int i = lane; i < n; i += kWave) {
+        const int32_t me = raw[i];
+        int r = 0;
+        for (int j = 0; j < n; ++j) r += (raw[j] < me) ? 1 : 0;
+        out_id[r] = me;
+        out_p[r] = p_in[i];
+    }
+    wave_sync();
+}
+
+// Inverse CDF over an id-sorted list (all lanes run it identically).
+__device__ int32_t sample_sorted(const int32_t* ids, const double* w, int n, double u, double* wpick)
+{
+    double W = 0.0;
+    for (int i = 0; i < n; ++i) W += w[i];
+    *wpick = 0.0;
+    if (!(W > 0.0)) return -1;
+    const double t = u * W;
+    double c = 0.0;
+    for (int i = 0; i < n; ++i) {
+        c += w[i];
+        if (c > t) { *wpick = w[i]; return ids[i]; }
+    }
+    for (int i = n - 1; i >= 0; --i)
+        if (w[i] > 0.0) { *wpick = w[i]; return ids[i]; }
+    return -1;
+}
+
+// Probability of token y in an unordered support (0 when absent).
+__device__ double lookup_prob(const int32_t* ids, const double* p, int n, int32_t y, int lane)
+{
+    for (int base = 0; base < n; base += kWave) {
+        const int i = base + lane;
+        const bool hit = (i < n) && ids[i] == y;
+        const uint64_t m = __ballot(hit);
+        if (m) {
+            const int src = wave_first_lane(m);
+            const double pv = hit ? p[i] : 0.0;
+            return __shfl(pv, src, kWave);
+        }
+    }
+    return 0.0;
+}
+
+// ---- linear, sparse supports -----------------------------------------------------
+constexpr int kLinThreads = 256;
+constexpr int kLinWaves = kLinThreads / kWave;
+
+__global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
+    int32_t batch, int32_t B, SparseOut sup, uint64_t seed, uint64_t offset,
+    const uint32_t* req_ids, LinearOut o)
+{
+    __shared__ int32_t s_raw[kLinWaves][kMaxK];
+    __shared__ int32_t s_sid[kLinWaves][kMaxK];
+    __shared__ double s_sp[kLinWaves][kMaxK];
+    __shared__ int32_t s_y[kMaxLinearB];
+    __shared__ int32_t s_acc[kMaxLinearB];
+    __shared__ uint32_t s_flags;
+
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int b = blockIdx.x;
+    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+    const int64_t qbase = (int64_t)b * B;
+    const int64_t pbase = (int64_t)batch * B + (int64_t)b * (B + 1);
+    const int cap = sup.cap;
+    if (threadIdx.x == 0) s_flags = 0;
+    __syncthreads();
+
+    uint32_t flags = 0;
+    for (int j = w; j < B; j += kLinWaves) {
+        const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
+        const int64_t qr = qbase + j, pr = pbase + j;
+        const int nq = sup.count[qr];
+        int32_t y = -1;
+        double qy = 0.0;
+        if (nq > 0) {
+            stage_sorted_by_id(sup.ids + qr * cap, sup.probs + qr * cap, nq, s_raw[w], s_sid[w], s_sp[w], lane);
+            y = sample_sorted(s_sid[w], s_sp[w], nq, d.u[0], &qy);
+        } else {
+            flags |= 1u;
+        }
+        int acc = 0;
+        if (y >= 0) {
+            const int np = sup.count[pr];
+            double py = 0.0;
+            if (np > 0) py = lookup_prob(sup.ids + pr * cap, sup.probs + pr * cap, np, y, lane);
+            else flags |= 1u;
+            acc = (d.u[1] * qy < py) ? 1 : 0;
+        }
+        if (lane == 0) {
+            s_y[j] = y;
+            s_acc[j] = acc;
+            if (o.proposals) o.proposals[(int64_t)b * B + j] = y;
+        }
+        wave_sync();
+    }
+    if (flags && lane == 0) atomicOr(&s_flags, flags);
+    __syncthreads();
+    if (w != 0) return;
+
+    int jstar = B;
+    for (int base = 0; base < B; base += kWave) {
+        const int j = base + lane;
+        const uint64_t m = __ballot(j < B && s_acc[j] == 0);
+        if (m) { jstar = base + wave_first_lane(m); break; }
+    }
+    const Draw d = uno_draw(seed, req, (uint32_t)jstar, offset);
+    int32_t fin = -1;
+    double dummy;
+    uint32_t fl = 0;
+    if (jstar < B) {
+        const int64_t pr = pbase + jstar, qr = qbase + jstar;
+        const int np = sup.count[pr], nq = sup.count[qr];
+        if (np > 0) {
+            stage_sorted_by_id(sup.ids + pr * cap, sup.probs + pr * cap, np, s_raw[0], s_sid[0], s_sp[0], lane);
+            // draft support, unordered, for lookups
+            const int nqq = nq > 0 ? nq : 0;
+            for (int i = lane; i < nqq; i += kWave) {
+                s_raw[2][i] = sup.ids[qr * cap + i];
+                s_sp[2][i] = sup.probs[qr * cap + i];
+            }
+            wave_sync();
+            // residual max(0, p - q) over p's support in id order; ids outside p's
+            // support have zero residual
+            for (int i = lane; i < np; i += kWave) {
+                const int32_t id = s_sid[0][i];
+                double qv = 0.0;
+                for (int j = 0; j < nqq; ++j)
+                    if (s_raw[2][j] == id) { qv = s_sp[2][j]; break; }
+                const double dlt = s_sp[0][i] - qv;
+                s_sp[1][i] = dlt > 0.0 ? dlt : 0.0;
+            }
+            wave_sync();
+            fin = sample_sorted(s_sid[0], s_sp[1], np, d.u[2], &dummy);
+            if (fin < 0) {
+                fl |= 2u;
+                fin = sample_sorted(s_sid[0], s_sp[0], np, d.u[2], &dummy);
+            }
+        } else {
+            fl |= 1u;
+        }
+    } else {
+        const int64_t pr = pbase + B;
+        const int np = sup.count[pr];
+        if (np > 0) {
+            stage_sorted_by_id(sup.ids + pr * cap, sup.probs + pr * cap, np, s_raw[0], s_sid[0], s_sp[0], lane);
+            fin = sample_sorted(s_sid[0], s_sp[0], np, d.u[2], &dummy);
+        } else {
+            fl |= 1u;
+        }
+    }
+    int32_t* tok = o.tokens + (int64_t)b * (B + 1);
+    for (int j = lane; j <= B; j += kWave) tok[j] = (j < jstar) ? s_y[j] : (j == jstar ? fin : -1);
+    if (lane == 0) {
+        o.accept_len[b] = jstar + 1;
+        if (o.flags) o.flags[b] = s_flags | fl;
+    }
+}
+
+// ---- tree build (one wave per request) ------------------------------------------
+struct FrontierEntry {
+    double score;
+    int32_t depth, parent, rank;
+};
+
+__device__ __forceinline__ bool fr_better(double sa, int da, int pa, int ra, double sb, int db, int pb,
+                                          int rb)
+{
+    if (sa != sb) return sa > sb;
+    if (da != db) return da < db;
+    if (pa != pb) return pa < pb;
+    return ra < rb;
+}
+
+__global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_t B, int32_t K, int32_t V,
+                                                           SparseOut sup, TreeOut o)
+{
+    __shared__ double f_score[kFrontierCap];
+    __shared__ int32_t f_depth[kFrontierCap], f_parent[kFrontierCap], f_rank[kFrontierCap];
+    __shared__ double n_score[kMaxNodes];
+    __shared__ int32_t n_tok[kMaxNodes], n_par[kMaxNodes], n_dep[kMaxNodes];
+    __shared__ int32_t s_cn[kMaxNodes];
+
+    const int lane = lane_id();
+    const int b = blockIdx.x;
+    const int cap = sup.cap;
+    const int64_t rbase = (int64_t)b * B;
+    for (int d = lane; d < B; d += kWave) {
+        const int n = sup.count[rbase + d];
+        s_cn[d] = n > 0 ? (n < K ? n : K) : 0;
+    }
+    if (lane == 0) { n_score[0] = 1.0; n_tok[0] = -1; n_par[0] = -1; n_dep[0] = 0; }
+    wave_sync();
+
+    auto qprob = [&](int d, int r) { return sup.probs[(rbase + d) * cap + r]; };
+    int fs = 0;
+    auto insert = [&](double s, int dd, int pp, int rr) {
+        int pos = 0;
+        for (int base = 0; base < fs; base += kWave) {
+            const int i = base + lane;
+            const bool bt = i < fs && fr_better(f_score[i], f_depth[i], f_parent[i], f_rank[i], s, dd, pp, rr);
+            pos += __popcll(__ballot(bt));
+        }
+        double rs[3];
+        int rd[3], rp[3], rk[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const int i = q * kWave + lane;
+            if (i >= pos && i < fs) { rs[q] = f_score[i]; rd[q] = f_depth[i]; rp[q] = f_parent[i]; rk[q] = f_rank[i]; }
+        }
+        wave_sync();
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const int i = q * kWave + lane;
+            if (i >= pos && i < fs && i + 1 < kFrontierCap) {
+                f_score[i + 1] = rs[q]; f_depth[i + 1] = rd[q]; f_parent[i + 1] = rp[q]; f_rank[i + 1] = rk[q];
+            }
+        }
+        if (lane == 0) { f_score[pos] = s; f_depth[pos] = dd; f_parent[pos] = pp; f_rank[pos] = rr; }
+        wave_sync();
+        ++fs;
+    };
+    auto pop = [&](FrontierEntry& e) {
+        e.score = f_score[0]; e.depth = f_depth[0]; e.parent = f_parent[0]; e.rank = f_rank[0];
+        double rs[3];
+        int rd[3], rp[3], rk[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const int i = q * kWave + lane + 1;
+            if (i < fs) { rs[q] = f_score[i]; rd[q] = f_depth[i]; rp[q] = f_parent[i]; rk[q] = f_rank[i]; }
+        }
+        wave_sync();
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const int i = q * kWave + lane + 1;
+            if (i < fs) { f_score[i - 1] = rs[q]; f_depth[i - 1] = rd[q]; f_parent[i - 1] = rp[q]; f_rank[i - 1] = rk[q]; }
+        }
+        wave_sync();
+        --fs;
+    };
+
+    // Best-first expansion with lazily pushed siblings: a popped node pushes its
+    // next sibling and its first child.  Siblings come in non-increasing score
+    // (candidate order), so the frontier always holds the best unexpanded entry.
+    if (B > 0 && s_cn[0] > 0) insert(1.0 * qprob(0, 0), 1, 0, 0);
+    int num = 1;
+    while (num <= V && fs > 0) {
+        FrontierEntry e;
+        pop(e);
+        const int32_t tok = sup.ids[(rbase + e.depth - 1) * cap + e.rank];
+        if (lane == 0) { n_score[num] = e.score; n_tok[num] = tok; n_par[num] = e.parent; n_dep[num] = e.depth; }
+        wave_sync();
+        if (e.rank + 1 < s_cn[e.depth - 1])
+            insert(n_score[e.parent] * qprob(e.depth - 1, e.rank + 1), e.depth, e.parent, e.rank + 1);
+        if (e.depth < B && s_cn[e.depth] > 0) insert(e.score * qprob(e.depth, 0), e.depth + 1, num, 0);
+        ++num;
+    }
+    const int64_t ob = (int64_t)b * (V + 1);
+    for (int n = lane; n <= V; n += kWave) {
+        const bool used = n < num;
+        o.node_token[ob + n] = used ? n_tok[n] : -1;
+        o.node_parent[ob + n] = used ? n_par[n] : -1;
+        o.node_depth[ob + n] = used ? n_dep[n] : -1;
+        if (o.node_score) o.node_score[ob + n] = used ? n_score[n] : 0.0;
+    }
+    if (lane == 0) o.num_nodes[b] = num;
+}
+
+// ---- tree walk (one workgroup per request) ---------------------------------------
+constexpr int kWalkThreads = 256;
+constexpr int kWalkWaves = kWalkThreads / kWave;
+
+__global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
+    int32_t batch, int32_t B, int32_t V, SparseOut sup, uint64_t seed, uint64_t offset,
+    const uint32_t* req_ids, const int32_t* node_token, const int32_t* node_parent,
+    const int32_t* num_nodes, WalkOut o)
+{
+    __shared__ int32_t s_raw[kWalkWaves][kMaxK];
+    __shared__ int32_t s_sid[kWalkWaves][kMaxK];
+    __shared__ double s_sp[kWalkWaves][kMaxK];
+    __shared__ int32_t s_dep[kMaxNodes], s_t[kMaxNodes], s_tok[kMaxNodes], s_par[kMaxNodes];
+
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int b = blockIdx.x;
+    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+    const int cap = sup.cap;
+    int nn = num_nodes[b];
+    nn = nn < 1 ? 1 : (nn > V + 1 ? V + 1 : nn);
+    const int64_t ob = (int64_t)b * (V + 1);
+    if (threadIdx.x == 0) {
+        s_dep[0] = 0; s_tok[0] = -1; s_par[0] = -1;
+        for (int n = 1; n < nn; ++n) {
+            const int p = node_parent[ob + n];
+            s_par[n] = p;
+            s_tok[n] = node_token[ob + n];
+            s_dep[n] = (p >= 0 && p < n && s_dep[p] >= 0) ? s_dep[p] + 1 : -1;
+        }
+    }
+    __syncthreads();
+    // every node's sample, drawn with the uniform of its depth
+    for (int n = w; n < nn; n += kWalkWaves) {
+        const int dep = s_dep[n];
+        int32_t t = -1;
+        const int64_t row = ob + n;
+        const int cnt = sup.count[row];
+        if (dep >= 0 && dep <= B && cnt > 0) {
+            const Draw d = uno_draw(seed, req, (uint32_t)dep, offset);
+            stage_sorted_by_id(sup.ids + row * cap, sup.probs + row * cap, cnt, s_raw[w], s_sid[w], s_sp[w], lane);
+            double dummy;
+            t = sample_sorted(s_sid[w], s_sp[w], cnt, d.u[2], &dummy);
+        }
+        if (lane == 0) s_t[n] = t;
+        wave_sync();
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    int32_t* tok = o.tokens + (int64_t)b * (B + 1);
+    int32_t* pth = o.path + (int64_t)b * (B + 1);
+    int n = 0, d = 0;
+    uint32_t fl = 0;
+    for (;;) {
+        const int32_t t = s_t[n];
+        tok[d] = t;
+        pth[d] = n;
+        if (t < 0) fl |= 1u;
+        int child = -1;
+        if (t >= 0 && d < B)
+            for (int c = 1; c < nn; ++c)
+                if (s_par[c] == n && s_tok[c] == t) { child = c; break; }
+        if (child < 0) break;
+        n = child;
+        ++d;
+    }
+    for (int j = d + 1; j <= B; ++j) { tok[j] = -1; pth[j] = -1; }
+    o.accept_len[b] = d + 1;
+    if (o.flags) o.flags[b] = fl;
+}
+
+// ---- dense linear ------------------------------------------------------------------
+constexpr int kDenseThreads = 256;
+constexpr int kDenseWaves = kDenseThreads / kWave;
+constexpr int kPerLane = kDenseChunk / kWave;   // 32 logits per lane per chunk
+
+// Chunk c of a row into registers: element (j*64 + lane)*EPV + e at x[j*EPV + e];
+// -inf past the end of the row.
+template <bool BF16>
+__device__ __forceinline__ void load_chunk(const char* row, int64_t N, int64_t c, float* x, int lane)
+{
+    using V = Vec<BF16>;
+    constexpr int EPV = V::EPV, ESZ = V::ESZ, NV = kPerLane / EPV;
+    const int64_t beg = c * kDenseChunk;
+    const int64_t n = (N - beg < kDenseChunk) ? (N - beg) : kDenseChunk;
+    const bool vec_ok = (n == kDenseChunk) && ((((uintptr_t)(row + beg * ESZ)) & 15u) == 0);
+    if (vec_ok) {
+        const typename V::T* p = reinterpret_cast<const typename V::T*>(row + beg * ESZ);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const typename V::T v = p[j * kWave + lane];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) x[j * EPV + e] = V::get(v, e);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const int64_t i = (int64_t)(j * kWave + lane) * EPV + e;
+                x[j * EPV + e] = (i < n) ? load_scalar<BF16>(row, beg + i) : -INFINITY;
+            }
+    }
+}
+
+// Chunk-stat term of chunk c relative to the row max m.
+__device__ __forceinline__ double chunk_term(const float* cm, const double* cs, int c, float m, const DenseExp& ex)
+{
+    return (cm[c] > -INFINITY) ? cs[c] * ex((double)cm[c] - (double)m) : 0.0;
+}
+
+// Row max m and normaliser S from chunk statistics; S accumulates 64-chunk
+// blocks of an inclusive wave scan, the same sums dense_locate walks.
+__device__ bool dense_row_stat(const float* cm, const double* cs, int nc, const DenseExp& ex, int lane,
+                               float* m_out, double* S_out)
+{
+    float m = -INFINITY;
+    bool bad = false;
+    for (int c = lane; c < nc; c += kWave) {
+        m = fmaxf(m, cm[c]);
+        bad |= (cm[c] == INFINITY);
+    }
+    m = wave_max_f32(m);
+    bad = __ballot(bad) != 0ull;
+    if (bad || !(m > -INFINITY)) { *m_out = NAN; *S_out = NAN; return false; }
+    double S = 0.0;
+    for (int base = 0; base < nc; base += kWave) {
+        const int c = base + lane;
+        const double term = (c < nc) ? chunk_term(cm, cs, c, m, ex) : 0.0;
+        const double incl = wave_incl_scan_f64(term, lane);
+        S += __shfl(incl, kWave - 1, kWave);
+    }
+    *m_out = m;
+    *S_out = S;
+    return S > 0.0;
+}
+
+// First chunk whose cumulative term exceeds t; *before = cumulative before it.
+// -1 if none (t at or past the total).
+template <typename TermF>
+__device__ int dense_locate(int nc, double t, TermF term_of, int lane, double* before)
+{
+    double C = 0.0;
+    for (int base = 0; base < nc; base += kWave) {
+        const int c = base + lane;
+        const double term = (c < nc) ? term_of(c) : 0.0;
+        const double incl = wave_incl_scan_f64(term, lane);
+        const uint64_t hit = __ballot(c < nc && term > 0.0 && C + incl > t);
+        if (hit) {
+            const int l = wave_first_lane(hit);
+            *before = C + __shfl(incl - term, l, kWave);
+            return base + l;
+        }
+        C += __shfl(incl, kWave - 1, kWave);
+    }
+    *before = C;
+    return -1;
+}
+
+// Last chunk with a positive term (-1 if none).
+template <typename TermF>
+__device__ int dense_last_positive_chunk(int nc, TermF term_of, int lane)
+{
+    int best = -1;
+    for (int c = lane; c < nc; c += kWave)
+        if (term_of(c) > 0.0) best = c;
+    for (int d = kWave / 2; d >= 1; d >>= 1) best = max(best, __shfl_xor(best, d, kWave));
+    return best;
+}
+
+// Smallest element of a chunk (weights from wf, element layout of load_chunk)
+// whose cumulative weight exceeds tau; the last positive element if none does.
+template <int EPV, typename WeightF>
+__device__ int pick_in_chunk(WeightF wf, double tau, int lane)
+{
+    constexpr int NV = kPerLane / EPV;
+    double run = 0.0;
+    int last_pos = -1;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        double wl[EPV];
+        double lsum = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            wl[e] = wf(j * EPV + e);
+            lsum += wl[e];
+            if (wl[e] > 0.0) last_pos = (j * kWave + lane) * EPV + e;
+        }
+        const double incl = wave_incl_scan_f64(lsum, lane);
+        const uint64_t hit = __ballot(run + incl > tau);
+        if (hit) {
+            const int l = wave_first_lane(hit);
+            int ep = -1;
+            if (lane == l) {
+                double cc = run + (incl - lsum);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    cc += wl[e];
+                    if (ep < 0 && cc > tau) ep = e;
+                }
+                if (ep < 0) {
+#pragma unroll
+                    for (int e = EPV - 1; e >= 0; --e)
+                        if (ep < 0 && wl[e] > 0.0) ep = e;
+                }
+            }
+            ep = __shfl(ep, l, kWave);
+            return (j * kWave + l) * EPV + ep;
+        }
+        run += __shfl(incl, kWave - 1, kWave);
+    }
+    for (int d = kWave / 2; d >= 1; d >>= 1) last_pos = max(last_pos, __shfl_xor(last_pos, d, kWave));
+    return last_pos;
+}
+
+// Chunk total with the accumulation order of pick_in_chunk.
+template <int EPV, typename WeightF>
+__device__ double chunk_total(WeightF wf, int lane)
+{
+    constexpr int NV = kPerLane / EPV;
+    double run = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        double lsum = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) lsum += wf(j * EPV + e);
+        const double incl = wave_incl_scan_f64(lsum, lane);
+        run += __shfl(incl, kWave - 1, kWave);
+    }
+    return run;
+}
+
+// Sample a dense filtered row p = exp((z - m)/T) / S with uniform u.
+template <bool BF16>
+__device__ int32_t dense_sample_row(const char* row, int64_t N, const float* cm, const double* cs, int nc,
+                                    float m, double S, double u, const DenseExp& ex, int lane)
+{
+    auto term = [&](int c) { return chunk_term(cm, cs, c, m, ex); };
+    const double t = u * S;
+    double before;
+    int c = dense_locate(nc, t, term, lane, &before);
+    double tau;
+    if (c < 0) {
+        c = dense_last_positive_chunk(nc, term, lane);
+        if (c < 0) return -1;
+        tau = INFINITY;
+    } else {
+        tau = (t - before) / ex((double)cm[c] - (double)m);
+    }
+    float x[kPerLane];
+    load_chunk<BF16>(row, N, c, x, lane);
+    const double mc = (double)cm[c];
+    auto wf = [&](int i) { return finite_f32(x[i]) ? ex((double)x[i] - mc) : 0.0; };
+    const int l = pick_in_chunk<Vec<BF16>::EPV>(wf, tau, lane);
+    return l < 0 ? -1 : (int32_t)(c * (int64_t)kDenseChunk + l);
+}
+
+// Global row index of local row i of request b (draft rows 0..B-1, then target 0..B).
+__device__ __forceinline__ int64_t linear_row(int32_t batch, int32_t B, int b, int i)
+{
+    return i < B ? (int64_t)b * B + i : (int64_t)batch * B + (int64_t)b * (B + 1) + (i - B);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_one(const char* row, int64_t i)
+{
+    if constexpr (BF16) {
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[i] << 16);
+    } else {
+        return reinterpret_cast<const float*>(row)[i];
+    }
+}
+
+// Row stats of every row, proposals, acceptance and the first rejection.
+template <bool BF16>
+__global__ __launch_bounds__(kDenseThreads) void dense_propose_kernel(
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
+    uint64_t seed, uint64_t offset, const uint32_t* req_ids, float* row_m, double* row_S,
+    int32_t* jstar_out, int32_t* y_out, uint32_t* flag_out, LinearOut o)
+{
+    __shared__ double s_exp2[kDenseWaves][64];
+    __shared__ int32_t s_acc[kMaxLinearB];
+    __shared__ uint32_t s_flags;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int b = blockIdx.x;
+    fill_exp2_table(s_exp2[w], lane);
+    const DenseExp ex{ log2e_over_T, s_exp2[w] };
+    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+    const int nc = dc.nchunks;
+    const int64_t row_bytes = N * Vec<BF16>::ESZ;
+    if (threadIdx.x == 0) s_flags = 0;
+
+    for (int i = w; i < 2 * B + 1; i += kDenseWaves) {
+        const int64_t r = linear_row(batch, B, b, i);
+        float m;
+        double S;
+        dense_row_stat(dc.cmax + r * nc, dc.csum + r * nc, nc, ex, lane, &m, &S);
+        if (lane == 0) { row_m[r] = m; row_S[r] = S; }
+    }
+    __syncthreads();
+
+    uint32_t flags = 0;
+    for (int j = w; j < B; j += kDenseWaves) {
+        const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
+        const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
+        const float mq = row_m[qr], mp = row_m[pr];
+        const double Sq = row_S[qr], Sp = row_S[pr];
+        const char* qrow = row_pointer(src, qr, row_bytes);
+        const char* prow = row_pointer(src, pr, row_bytes);
+        int32_t y = -1;
+        int acc = 0;
+        if (Sq > 0.0) {
+            y = dense_sample_row<BF16>(qrow, N, dc.cmax + qr * nc, dc.csum + qr * nc, nc, mq, Sq, d.u[0], ex, lane);
+        } else {
+            flags |= 1u;
+        }
+        if (y >= 0) {
+            const double qy = ex((double)load_one<BF16>(qrow, y) - (double)mq) / Sq;
+            double py = 0.0;
+            if (Sp > 0.0) {
+                const float zp = load_one<BF16>(prow, y);
+                if (finite_f32(zp)) py = ex((double)zp - (double)mp) / Sp;
+            } else {
+                flags |= 1u;
+            }
+            acc = (d.u[1] * qy < py) ? 1 : 0;
+        }
+        if (lane == 0) {
+            s_acc[j] = acc;
+            y_out[(int64_t)b * B + j] = y;
+            if (o.proposals) o.proposals[(int64_t)b * B + j] = y;
+        }
+    }
+    if (flags && lane == 0) atomicOr(&s_flags, flags);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int js = B;
+        for (int j = 0; j < B; ++j)
+            if (!s_acc[j]) { js = j; break; }
+        jstar_out[b] = js;
+        flag_out[b] = s_flags;
+    }
+}
+
+// Residual mass per chunk for requests that rejected a proposal.
+template <bool BF16>
+__global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, int32_t nc,
+    const float* row_m, const double* row_S, const int32_t* jstar_in, double* resid)
+{
+    __shared__ double s_exp2[kDenseWaves][64];
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int b = blockIdx.x;
+    const int c = blockIdx.y * kDenseWaves + w;
+    const int js = jstar_in[b];
+    if (js >= B || c >= nc) return;
+    fill_exp2_table(s_exp2[w], lane);
+    const DenseExp ex{ log2e_over_T, s_exp2[w] };
+    const int64_t qr = linear_row(batch, B, b, js), pr = linear_row(batch, B, b, B + js);
+    const double Sp = row_S[pr], Sq = row_S[qr];
+    double total = 0.0;
+    if (Sp > 0.0) {
+        const int64_t row_bytes = N * Vec<BF16>::ESZ;
+        const bool q_ok = Sq > 0.0;
+        float xp[kPerLane], xq[kPerLane];
+        load_chunk<BF16>(row_pointer(src, pr, row_bytes), N, c, xp, lane);
+        if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
+        const double mp = (double)row_m[pr], mq = (double)row_m[qr];
+        const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
+        auto wf = [&](int i) {
+            const double pv = finite_f32(xp[i]) ? ex((double)xp[i] - mp) * iSp : 0.0;
+            const double qv = (q_ok && finite_f32(xq[i])) ? ex((double)xq[i] - mq) * iSq : 0.0;
+            const double dl = pv - qv;
+            return dl > 0.0 ? dl : 0.0;
+        };
+        total = chunk_total<Vec<BF16>::EPV>(wf, lane);
+    }
+    if (lane == 0) resid[(int64_t)b * nc + c] = total;
+}
+
+// Residual (or bonus) sample and the cycle's outputs.
+template <bool BF16>
+__global__ __launch_bounds__(kWave) void dense_finish_kernel(
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
+    uint64_t seed, uint64_t offset, const uint32_t* req_ids, const float* row_m, const double* row_S,
+    const int32_t* jstar_in, const int32_t* y_in, const uint32_t* flag_in, const double* resid,
+    LinearOut o)
+{
+    __shared__ double s_exp2[64];
+    const int lane = lane_id();
+    const int b = blockIdx.x;
+    fill_exp2_table(s_exp2, lane);
+    const DenseExp ex{ log2e_over_T, s_exp2 };
+    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+    const int nc = dc.nchunks;
+    const int64_t row_bytes = N * Vec<BF16>::ESZ;
+    const int js = jstar_in[b];
+    const Draw d = uno_draw(seed, req, (uint32_t)js, offset);
+    uint32_t fl = flag_in[b];
+    int32_t fin = -1;
+    const int64_t pr = linear_row(batch, B, b, B + js);
+    const char* prow = row_pointer(src, pr, row_bytes);
+    const float mp = row_m[pr];
+    const double Sp = row_S[pr];
+    if (!(Sp > 0.0)) {
+        fl |= 1u;
+    } else if (js < B) {
+        const int64_t qr = linear_row(batch, B, b, js);
+        const double Sq = row_S[qr];
+        const bool q_ok = Sq > 0.0;
+        const double* R = resid + (int64_t)b * nc;
+        auto rterm = [&](int c) { return R[c]; };
+        double Rtot = 0.0;
+        for (int base = 0; base < nc; base += kWave) {
+            const int c = base + lane;
+            const double incl = wave_incl_scan_f64(c < nc ? R[c] : 0.0, lane);
+            Rtot += __shfl(incl, kWave - 1, kWave);
+        }
+        if (Rtot > 0.0) {
+            const double t = d.u[2] * Rtot;
+            double before;
+            int c = dense_locate(nc, t, rterm, lane, &before);
+            double tau = t - before;
+            if (c < 0) { c = dense_last_positive_chunk(nc, rterm, lane); tau = INFINITY; }
+            float xp[kPerLane], xq[kPerLane];
+            load_chunk<BF16>(prow, N, c, xp, lane);
+            if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
+            const double mpd = (double)mp, mq = (double)row_m[qr];
+            const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
+            auto wf = [&](int i) {
+                const double pv = finite_f32(xp[i]) ? ex((double)xp[i] - mpd) * iSp : 0.0;
+                const double qv = (q_ok && finite_f32(xq[i])) ? ex((double)xq[i] - mq) * iSq : 0.0;
+                const double dl = pv - qv;
+                return dl > 0.0 ? dl : 0.0;
+            };
+            const int l = pick_in_chunk<Vec<BF16>::EPV>(wf, tau, lane);
+            fin = l < 0 ? -1 : (int32_t)(c * (int64_t)kDenseChunk + l);
+        } else {
+            fl |= 2u;
+        }
+        if (fin < 0)
+            fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp, d.u[2], ex, lane);
+    } else {
+        fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp, d.u[2], ex, lane);
+    }
+    int32_t* tok = o.tokens + (int64_t)b * (B + 1);
+    for (int j = lane; j <= B; j += kWave) tok[j] = (j < js) ? y_in[(int64_t)b * B + j] : (j == js ? fin : -1);
+    if (lane == 0) {
+        o.accept_len[b] = js + 1;
+        if (o.flags) o.flags[b] = fl;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_linear_sparse(int32_t batch, int32_t B, const SparseOut& sup, uint64_t seed,
+                                uint64_t offset, const uint32_t* request_ids, const LinearOut& o,
+                                hipStream_t stream)
+{
+    linear_sparse_kernel<<<dim3((unsigned)batch), kLinThreads, 0, stream>>>(batch, B, sup, seed, offset,
+                                                                           request_ids, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, int64_t vocab,
+                               bool bf16, float temperature, const DenseChunks& dc,
+                               const DenseScratch& sc, uint64_t seed, uint64_t offset,
+                               const uint32_t* request_ids, const LinearOut& o, hipStream_t stream)
+{
+    const double c = 1.4426950408889634074 / (double)temperature;
+    const dim3 rgrid((unsigned)batch, (unsigned)((dc.nchunks + kDenseWaves - 1) / kDenseWaves));
+    if (bf16) {
+        dense_propose_kernel<true><<<dim3((unsigned)batch), kDenseThreads, 0, stream>>>(
+            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
+            sc.flags, o);
+        dense_residual_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(
+            src, batch, B, vocab, c, dc.nchunks, sc.row_m, sc.row_S, sc.jstar, sc.resid);
+        dense_finish_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
+            sc.flags, sc.resid, o);
+    } else {
+        dense_propose_kernel<false><<<dim3((unsigned)batch), kDenseThreads, 0, stream>>>(
+            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
+            sc.flags, o);
+        dense_residual_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(
+            src, batch, B, vocab, c, dc.nchunks, sc.row_m, sc.row_S, sc.jstar, sc.resid);
+        dense_finish_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
+            sc.flags, sc.resid, o);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_build(int32_t batch, int32_t B, int32_t K, int32_t V, const SparseOut& sup,
+                             const TreeOut& o, hipStream_t stream)
+{
+    tree_build_kernel<<<dim3((unsigned)batch), kWave, 0, stream>>>(batch, B, K, V, sup, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_walk(int32_t batch, int32_t B, int32_t V, const SparseOut& sup, uint64_t seed,
+                            uint64_t offset, const uint32_t* request_ids, const int32_t* node_token,
+                            const int32_t* node_parent, const int32_t* num_nodes, const WalkOut& o,
+                            hipStream_t stream)
+{
+    tree_walk_kernel<<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
+        batch, B, V, sup, seed, offset, request_ids, node_token, node_parent, num_nodes, o);
+    return hipGetLastError();
+}
+
+}  // namespace uno

@@ -1,0 +1,383 @@
+// uno_api.cpp -- C ABI of the UNO sampling library: argument checks, workspace
+// layout and kernel launches.  Every check runs on the host before any launch.
+#include "../../include/uno.h"
+#include "uno_internal.h"
+
+#include <math.h>
+#include <string.h>
+
+using namespace uno;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+
+// Sampling mode of a parameter set.
+struct Mode {
+    bool greedy;
+    bool topk_on;
+    bool topp_on;
+    bool sparse;     // support from a top-k selection (greedy: k = 1)
+    int32_t k;       // effective k on the sparse path
+};
+
+int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
+{
+    if (sp == nullptr) return UNO_ERR_INVALID_ARG;
+    const float T = sp->temperature, p = sp->top_p;
+    if (!(T >= 0.0f) || !isfinite(T)) return UNO_ERR_INVALID_ARG;       // temperature >= 0
+    if (!(p > 0.0f && p <= 1.0f)) return UNO_ERR_INVALID_ARG;           // top_p in (0, 1]
+    m->greedy = (T == 0.0f);
+    m->topk_on = sp->top_k > 0 && (int64_t)sp->top_k < vocab;
+    m->topp_on = p < 1.0f;
+    // a vocabulary of at most UNO_MAX_TOP_K ids is filtered whole by the top-k path
+    m->sparse = m->greedy || m->topk_on || vocab <= UNO_MAX_TOP_K;
+    m->k = m->greedy ? 1 : (m->topk_on ? sp->top_k : (int32_t)vocab);
+    if (m->sparse && m->k > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
+    if (!m->sparse && m->topp_on) return UNO_ERR_UNSUPPORTED;           // full-vocabulary nucleus
+    if (!m->sparse && vocab > (int64_t)65535 * 4 * kDenseChunk) return UNO_ERR_UNSUPPORTED;
+    return UNO_OK;
+}
+
+int check_common(int32_t dtype, int64_t vocab)
+{
+    if (dtype != UNO_F32 && dtype != UNO_BF16) return UNO_ERR_UNSUPPORTED;
+    if (vocab < 1 || vocab > 0x7FFFFFFFLL) return UNO_ERR_INVALID_ARG;
+    return UNO_OK;
+}
+
+size_t elem_size(int32_t dtype) { return dtype == UNO_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Bump allocator over the caller's workspace (or a size-only dry run).
+struct Carve {
+    char* base;
+    size_t used = 0;
+    template <typename T>
+    T* take(size_t n)
+    {
+        const size_t off = used;
+        used = align_up(used + n * sizeof(T), kAlign);
+        return base ? reinterpret_cast<T*>(base + off) : nullptr;
+    }
+};
+
+struct SparseWs {
+    SparseOut sup;
+    int S;
+    uint32_t* part_key;
+    int32_t* part_id;
+    int32_t* part_n;
+};
+
+// Supports (when own_supports) and segment partials for `rows` sparse rows.
+void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool own_supports, SparseWs* w)
+{
+    w->S = topk_segments(rows, vocab, m.k);
+    if (own_supports) {
+        w->sup.cap = m.k;
+        w->sup.ids = cv.take<int32_t>((size_t)rows * m.k);
+        w->sup.probs = cv.take<double>((size_t)rows * m.k);
+        w->sup.count = cv.take<int32_t>((size_t)rows);
+        w->sup.stats = nullptr;
+    }
+    w->part_key = nullptr;
+    w->part_id = nullptr;
+    w->part_n = nullptr;
+    if (w->S > 1) {
+        w->part_key = cv.take<uint32_t>((size_t)rows * w->S * m.k);
+        w->part_id = cv.take<int32_t>((size_t)rows * w->S * m.k);
+        w->part_n = cv.take<int32_t>((size_t)rows * w->S);
+    }
+}
+
+DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab)
+{
+    DenseChunks dc;
+    dc.nchunks = dense_nchunks(vocab);
+    dc.cmax = cv.take<float>((size_t)rows * dc.nchunks);
+    dc.csum = cv.take<double>((size_t)rows * dc.nchunks);
+    dc.ccount = cv.take<int32_t>((size_t)rows * dc.nchunks);
+    return dc;
+}
+
+DenseScratch carve_dense_scratch(Carve& cv, int64_t rows, int32_t batch, int32_t B, int32_t nchunks)
+{
+    DenseScratch s;
+    s.row_m = cv.take<float>((size_t)rows);
+    s.row_S = cv.take<double>((size_t)rows);
+    s.jstar = cv.take<int32_t>((size_t)batch);
+    s.y = cv.take<int32_t>((size_t)batch * B);
+    s.flags = cv.take<uint32_t>((size_t)batch);
+    s.resid = cv.take<double>((size_t)batch * nchunks);
+    return s;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need)
+{
+    if (need == 0) return UNO_OK;
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, kAlign)) return UNO_ERR_WORKSPACE;
+    return UNO_OK;
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return UNO_OK;
+    g_last_hip_error = (int)e;
+    return UNO_ERR_HIP;
+}
+
+FilterParams filter_params(const uno_sampling_t* sp, const Mode& m)
+{
+    FilterParams fp;
+    fp.temperature = sp->temperature;
+    fp.top_p = sp->top_p;
+    fp.k = m.k;
+    fp.greedy = m.greedy ? 1 : 0;
+    fp.topp_on = m.topp_on ? 1 : 0;
+    return fp;
+}
+
+int check_tree_shape(int32_t B, int32_t K, int32_t V, bool need_k)
+{
+    if (B < 1 || V < B || V > UNO_MAX_TREE_NODES) return UNO_ERR_INVALID_ARG;
+    if (need_k && (K < 1 || (int64_t)V * K > UNO_MAX_TREE_VK)) return UNO_ERR_INVALID_ARG;
+    return UNO_OK;
+}
+
+// ---- per-op layout (shared by the size query and the calls) ---------------------
+int layout_filter(int64_t rows, int64_t vocab, int32_t dtype, const uno_sampling_t* sp, Carve& cv,
+                  Mode* m, SparseWs* sw, DenseChunks* dc)
+{
+    int st = check_common(dtype, vocab);
+    if (st) return st;
+    if (rows < 0 || rows > 0x7FFFFFFF) return UNO_ERR_INVALID_ARG;
+    st = check_sampling(sp, vocab, m);
+    if (st) return st;
+    if (rows == 0) return UNO_OK;
+    if (m->sparse) carve_sparse(cv, rows, vocab, *m, false, sw);
+    else *dc = carve_chunks(cv, rows, vocab);
+    return UNO_OK;
+}
+
+int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const uno_sampling_t* sp,
+                  Carve& cv, Mode* m, SparseWs* sw, DenseChunks* dc, DenseScratch* ds)
+{
+    int st = check_common(dtype, vocab);
+    if (st) return st;
+    if (batch < 0 || B < 1 || B > 128 || batch * (2 * (int64_t)B + 1) > 0x7FFFFFFF) return UNO_ERR_INVALID_ARG;
+    st = check_sampling(sp, vocab, m);
+    if (st) return st;
+    if (batch == 0) return UNO_OK;
+    const int64_t rows = batch * (2 * (int64_t)B + 1);
+    if (m->sparse) {
+        carve_sparse(cv, rows, vocab, *m, true, sw);
+    } else {
+        *dc = carve_chunks(cv, rows, vocab);
+        *ds = carve_dense_scratch(cv, rows, (int32_t)batch, B, dc->nchunks);
+    }
+    return UNO_OK;
+}
+
+int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int64_t vocab, int32_t dtype,
+                const uno_sampling_t* sp, Carve& cv, Mode* m, SparseWs* sw)
+{
+    int st = check_common(dtype, vocab);
+    if (st) return st;
+    if (batch < 0 || batch * ((int64_t)V + 1) > 0x7FFFFFFF) return UNO_ERR_INVALID_ARG;
+    st = check_tree_shape(B, K, V, op == UNO_OP_BUILD_TREE);
+    if (st) return st;
+    st = check_sampling(sp, vocab, m);
+    if (st) return st;
+    if (!m->sparse) return UNO_ERR_UNSUPPORTED;      // dense tree sampling is not built
+    if (batch == 0) return UNO_OK;
+    const int64_t rows = batch * (op == UNO_OP_BUILD_TREE ? (int64_t)B : (int64_t)V + 1);
+    carve_sparse(cv, rows, vocab, *m, true, sw);
+    return UNO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int uno_workspace_bytes(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K, int32_t V, int64_t vocab,
+                        int32_t dtype, const uno_sampling_t* sp, size_t* out_bytes)
+{
+    if (out_bytes == nullptr) return UNO_ERR_INVALID_ARG;
+    Carve cv{ nullptr };
+    Mode m;
+    SparseWs sw;
+    DenseChunks dc;
+    DenseScratch ds;
+    int st;
+    switch (op) {
+    case UNO_OP_FILTER: st = layout_filter(batch_or_rows, vocab, dtype, sp, cv, &m, &sw, &dc); break;
+    case UNO_OP_SAMPLE_LINEAR: st = layout_linear(batch_or_rows, B, vocab, dtype, sp, cv, &m, &sw, &dc, &ds); break;
+    case UNO_OP_BUILD_TREE:
+    case UNO_OP_VERIFY_TREE: st = layout_tree(op, batch_or_rows, B, K, V, vocab, dtype, sp, cv, &m, &sw); break;
+    default: return UNO_ERR_INVALID_ARG;
+    }
+    if (st) return st;
+    *out_bytes = cv.used;
+    return UNO_OK;
+}
+
+int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab, const uno_sampling_t* sp,
+               int32_t cap, int32_t* out_ids, double* out_probs, int32_t* out_count, double* out_stats,
+               void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    Carve sizing{ nullptr };
+    Mode m;
+    SparseWs sw;
+    DenseChunks dc;
+    int st = layout_filter(rows, vocab, dtype, sp, sizing, &m, &sw, &dc);
+    if (st) return st;
+    if (rows == 0) return UNO_OK;
+    if (logits == nullptr || out_count == nullptr || !aligned(logits, elem_size(dtype))) return UNO_ERR_INVALID_ARG;
+    if (m.sparse) {
+        if (out_ids == nullptr || out_probs == nullptr || cap < m.k) return UNO_ERR_INVALID_ARG;
+    } else if (out_stats == nullptr) {
+        return UNO_ERR_INVALID_ARG;
+    }
+    st = check_ws(ws, ws_bytes, sizing.used);
+    if (st) return st;
+    Carve cv{ static_cast<char*>(ws) };
+    layout_filter(rows, vocab, dtype, sp, cv, &m, &sw, &dc);
+
+    RowSource src{ static_cast<const char*>(logits), rows, nullptr, nullptr, 1 };
+    const bool bf16 = dtype == UNO_BF16;
+    if (m.sparse) {
+        SparseOut out{ out_ids, out_probs, out_count, out_stats, cap };
+        return hip_status(launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, m), out, sw.S,
+                                             sw.part_key, sw.part_id, sw.part_n, stream));
+    }
+    hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, stream);
+    if (e == hipSuccess) e = launch_dense_row_stats(rows, sp->temperature, dc, out_count, out_stats, stream);
+    return hip_status(e);
+}
+
+int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int32_t batch, int32_t B,
+                      int64_t vocab, const uno_sampling_t* sp, uint64_t seed, uint64_t offset,
+                      const uint32_t* request_ids, int32_t* out_tokens, int32_t* out_accept_len,
+                      int32_t* out_proposals, uint32_t* out_flags, void* ws, size_t ws_bytes,
+                      hipStream_t stream)
+{
+    Carve sizing{ nullptr };
+    Mode m;
+    SparseWs sw;
+    DenseChunks dc;
+    DenseScratch ds;
+    int st = layout_linear(batch, B, vocab, dtype, sp, sizing, &m, &sw, &dc, &ds);
+    if (st) return st;
+    if (batch == 0) return UNO_OK;
+    const size_t es = elem_size(dtype);
+    if (draft == nullptr || target == nullptr || out_tokens == nullptr || out_accept_len == nullptr ||
+        !aligned(draft, es) || !aligned(target, es))
+        return UNO_ERR_INVALID_ARG;
+    st = check_ws(ws, ws_bytes, sizing.used);
+    if (st) return st;
+    Carve cv{ static_cast<char*>(ws) };
+    layout_linear(batch, B, vocab, dtype, sp, cv, &m, &sw, &dc, &ds);
+
+    const int64_t rows = (int64_t)batch * (2 * B + 1);
+    RowSource src{ static_cast<const char*>(draft), (int64_t)batch * B, static_cast<const char*>(target),
+                   nullptr, 1 };
+    const bool bf16 = dtype == UNO_BF16;
+    LinearOut o{ out_tokens, out_accept_len, out_proposals, out_flags };
+    hipError_t e;
+    if (m.sparse) {
+        e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, m), sw.sup, sw.S, sw.part_key,
+                               sw.part_id, sw.part_n, stream);
+        if (e == hipSuccess) e = launch_linear_sparse(batch, B, sw.sup, seed, offset, request_ids, o, stream);
+    } else {
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, stream);
+        if (e == hipSuccess)
+            e = launch_linear_dense(src, batch, B, vocab, bf16, sp->temperature, dc, ds, seed, offset,
+                                    request_ids, o, stream);
+    }
+    return hip_status(e);
+}
+
+int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, int32_t K, int32_t V,
+                   int64_t vocab, const uno_sampling_t* sp, int32_t* node_token, int32_t* node_parent,
+                   int32_t* node_depth, double* node_score, int32_t* num_nodes, void* ws, size_t ws_bytes,
+                   hipStream_t stream)
+{
+    Carve sizing{ nullptr };
+    Mode m;
+    SparseWs sw;
+    int st = layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sp, sizing, &m, &sw);
+    if (st) return st;
+    if (batch == 0) return UNO_OK;
+    if (draft == nullptr || node_token == nullptr || node_parent == nullptr || node_depth == nullptr ||
+        num_nodes == nullptr || !aligned(draft, elem_size(dtype)))
+        return UNO_ERR_INVALID_ARG;
+    st = check_ws(ws, ws_bytes, sizing.used);
+    if (st) return st;
+    Carve cv{ static_cast<char*>(ws) };
+    layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sp, cv, &m, &sw);
+
+    const int64_t rows = (int64_t)batch * B;
+    RowSource src{ static_cast<const char*>(draft), rows, nullptr, nullptr, 1 };
+    hipError_t e = launch_topk_filter(src, rows, vocab, dtype == UNO_BF16, filter_params(sp, m), sw.sup, sw.S,
+                                      sw.part_key, sw.part_id, sw.part_n, stream);
+    if (e == hipSuccess) {
+        TreeOut o{ node_token, node_parent, node_depth, node_score, num_nodes };
+        e = launch_tree_build(batch, B, K, V, sw.sup, o, stream);
+    }
+    return hip_status(e);
+}
+
+int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B, int32_t V, int64_t vocab,
+                    const uno_sampling_t* sp, uint64_t seed, uint64_t offset, const uint32_t* request_ids,
+                    const int32_t* node_token, const int32_t* node_parent, const int32_t* num_nodes,
+                    int32_t* out_tokens, int32_t* out_path, int32_t* out_accept_len, uint32_t* out_flags,
+                    void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    Carve sizing{ nullptr };
+    Mode m;
+    SparseWs sw;
+    int st = layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sp, sizing, &m, &sw);
+    if (st) return st;
+    if (batch == 0) return UNO_OK;
+    if (target == nullptr || node_token == nullptr || node_parent == nullptr || num_nodes == nullptr ||
+        out_tokens == nullptr || out_path == nullptr || out_accept_len == nullptr ||
+        !aligned(target, elem_size(dtype)))
+        return UNO_ERR_INVALID_ARG;
+    st = check_ws(ws, ws_bytes, sizing.used);
+    if (st) return st;
+    Carve cv{ static_cast<char*>(ws) };
+    layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sp, cv, &m, &sw);
+
+    const int64_t rows = (int64_t)batch * (V + 1);
+    RowSource src{ static_cast<const char*>(target), rows, nullptr, num_nodes, V + 1 };
+    hipError_t e = launch_topk_filter(src, rows, vocab, dtype == UNO_BF16, filter_params(sp, m), sw.sup, sw.S,
+                                      sw.part_key, sw.part_id, sw.part_n, stream);
+    if (e == hipSuccess) {
+        WalkOut o{ out_tokens, out_path, out_accept_len, out_flags };
+        e = launch_tree_walk(batch, B, V, sw.sup, seed, offset, request_ids, node_token, node_parent, num_nodes,
+                             o, stream);
+    }
+    return hip_status(e);
+}
+
+const char* uno_status_string(int status)
+{
+    switch (status) {
+    case UNO_OK: return "ok";
+    case UNO_ERR_INVALID_ARG: return "invalid argument";
+    case UNO_ERR_UNSUPPORTED: return "unsupported configuration";
+    case UNO_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case UNO_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+    }
+}
+
+int uno_last_hip_error(void) { return g_last_hip_error; }
+
+const char* uno_version(void) { return "uno-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,230 @@
+// uno_device.h -- device helpers shared by the UNO sampling kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "uno_internal.h"
+
+namespace uno {
+
+constexpr int kWave = 64;
+
+// Wave-level ordering point for LDS traffic between lanes of one wave.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint64_t lanes_below(int lane)
+{
+    return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Order-preserving unsigned key of a float: a > b (as floats, -0 == +0) iff
+// key(a) > key(b).  -0 is folded onto +0 first.  NaN never reaches a key.
+__device__ __forceinline__ uint32_t float_key(float v)
+{
+    const uint32_t b = __float_as_uint(v + 0.0f);
+    return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_float(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+constexpr uint32_t kKeyPosInf = 0xFF800000u;   // float_key(+inf)
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // float_key(-inf)
+
+// Predicates that must treat NaN exactly are integer tests on the bit pattern
+// or the key: float compares feeding a ballot are not lowered consistently
+// for NaN operands.
+// Admission test on keys: above `thr_key` and not NaN (NaN keys lie above
+// +inf or below -inf).
+__device__ __forceinline__ bool key_admits(uint32_t key, uint32_t thr_key)
+{
+    return (key > thr_key) & (key <= kKeyPosInf);
+}
+
+// Finite (neither NaN nor +-inf).
+__device__ __forceinline__ bool finite_f32(float v)
+{
+    return (__float_as_uint(v) & 0x7FFFFFFFu) < 0x7F800000u;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Philox4x32-10, Salmon et al. (SC'11): 10 rounds, key bumped by the Weyl
+// constants between rounds.  Counter (c0..c3), key (k0, k1).
+struct Philox4 { uint32_t w[4]; };
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                  uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        const uint32_t n0 = hi1 ^ c1 ^ k0;
+        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    }
+    Philox4 o;
+    o.w[0] = c0; o.w[1] = c1; o.w[2] = c2; o.w[3] = c3;
+    return o;
+}
+
+// Uniform in [0, 1) from one Philox word (exact in double).
+__device__ __forceinline__ double unit_uniform(uint32_t w) { return (double)w * 0x1p-32; }
+
+// The four uniforms of draw (request, position) at cycle `offset`.
+struct Draw { double u[4]; };
+
+__device__ __forceinline__ Draw uno_draw(uint64_t seed, uint32_t req, uint32_t pos, uint64_t offset)
+{
+    const Philox4 p = philox4x32_10(req, pos, (uint32_t)offset, (uint32_t)(offset >> 32),
+                                    (uint32_t)seed, (uint32_t)(seed >> 32));
+    Draw d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d.u[i] = unit_uniform(p.w[i]);
+    return d;
+}
+
+// ---- wave reductions --------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ double wave_incl_scan_f64(double v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const double o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v)
+{
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int wave_first_lane(uint64_t mask) { return __ffsll((long long)mask) - 1; }
+
+// ---- logit rows --------------------------------------------------------------
+template <bool BF16> struct Vec;
+template <> struct Vec<false> {
+    using T = float4;
+    static constexpr int EPV = 4, ESZ = 4;
+    __device__ static T neg_inf() { return make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY); }
+    __device__ static float get(const T& v, int e)
+    {
+        return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    }
+};
+template <> struct Vec<true> {
+    using T = uint4;
+    static constexpr int EPV = 8, ESZ = 2;
+    __device__ static T neg_inf() { return make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u); }
+    __device__ static float get(const T& v, int e)
+    {
+        const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+};
+
+template <bool BF16>
+__device__ __forceinline__ float load_scalar(const char* row, int64_t i)
+{
+    if constexpr (BF16) {
+        const uint16_t h = reinterpret_cast<const uint16_t*>(row)[i];
+        return __uint_as_float((uint32_t)h << 16);
+    } else {
+        return reinterpret_cast<const float*>(row)[i];
+    }
+}
+
+// Row pointer; returns nullptr for rows skipped by tree verification.
+__device__ __forceinline__ const char* row_pointer(const RowSource& s, int64_t r, int64_t row_bytes)
+{
+    if (r < s.rows0) {
+        if (s.num_nodes) {
+            const int64_t req = r / s.rows_per_req;
+            if (r - req * s.rows_per_req >= (int64_t)s.num_nodes[req]) return nullptr;
+        }
+        return s.src0 + r * row_bytes;
+    }
+    return s.src1 + (r - s.rows0) * row_bytes;
+}
+
+// Split of a row into a scalar head (up to the first 16-byte boundary), whole
+// 16-byte vectors, and a scalar tail.
+struct RowGeom { int64_t head, nvec, tail_beg; };
+
+template <bool BF16>
+__device__ __forceinline__ RowGeom row_geom(const char* row, int64_t N)
+{
+    constexpr int ESZ = Vec<BF16>::ESZ, EPV = Vec<BF16>::EPV;
+    int64_t head = (int64_t)(((16u - ((uintptr_t)row & 15u)) & 15u) / ESZ);
+    if (head > N) head = N;
+    const int64_t nvec = (N - head) / EPV;
+    return { head, nvec, head + nvec * EPV };
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// ---- double-precision exp for the dense path ---------------------------------
+// exp(d / T) for d <= 0: y = d * log2(e) / T = n/64 + f with |f| <= 1/128;
+// 2^(n/64) from a 64-entry table of 2^(j/64) (one copy per wave in LDS) and 2^f
+// from the Taylor series of exp(f ln 2) to degree 5 (truncation < 4e-17).
+__device__ __forceinline__ void fill_exp2_table(double* tab, int lane)
+{
+    tab[lane] = exp2((double)lane * (1.0 / 64.0));
+    wave_sync();
+}
+
+struct DenseExp {
+    double c;              // log2(e) / T
+    const double* tab;     // 64 entries, 2^(j/64)
+    __device__ __forceinline__ double operator()(double d) const
+    {
+        double y = d * c;
+        y = fmax(y, -1100.0);
+        const double kf = rint(y * 64.0);
+        const double f = fma(kf, -1.0 / 64.0, y);
+        const int ki = (int)kf;
+        const double t = f * 0.69314718055994530942;
+        const double p = fma(fma(fma(fma(fma(t, 1.0 / 120.0, 1.0 / 24.0), t, 1.0 / 6.0), t, 0.5), t, 1.0), t, 1.0);
+        return ldexp(tab[ki & 63] * p, ki >> 6);
+    }
+};
+
+}  // namespace uno

@@ -1,0 +1,119 @@
+// uno_internal.h -- kernel launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace uno {
+
+// Where logit row r lives.  Rows [0, rows0) are src0[r], rows [rows0, rows)
+// are src1[r - rows0].  When num_nodes is set (tree verification), row r of
+// src0 belongs to request r / rows_per_req and is skipped when its index in
+// the request is >= num_nodes[request].
+struct RowSource {
+    const char* src0;
+    int64_t rows0;
+    const char* src1;
+    const int32_t* num_nodes;
+    int32_t rows_per_req;
+};
+
+struct FilterParams {
+    float temperature;
+    float top_p;
+    int32_t k;        // effective top-k (1 when greedy)
+    int32_t greedy;   // temperature == 0
+    int32_t topp_on;  // top_p < 1
+};
+
+// Compact per-row supports in filter order.
+struct SparseOut {
+    int32_t* ids;      // [rows][cap]
+    double* probs;     // [rows][cap]
+    int32_t* count;    // [rows]; -1 invalid row
+    double* stats;     // [rows][2] (m, S) or nullptr
+    int32_t cap;
+};
+
+// Per-chunk statistics of dense rows: m_c = chunk max, s_c = sum over the
+// chunk of exp((z - m_c)/T), n_c = finite logits in the chunk.
+struct DenseChunks {
+    float* cmax;       // [rows][nchunks]
+    double* csum;      // [rows][nchunks]
+    int32_t* ccount;   // [rows][nchunks]
+    int32_t nchunks;
+};
+
+constexpr int kDenseChunk = 2048;          // elements per dense chunk
+constexpr int kMergeCap = 4096;            // candidates one merge workgroup holds
+
+inline int32_t dense_nchunks(int64_t vocab) { return (int32_t)((vocab + kDenseChunk - 1) / kDenseChunk); }
+
+// Segments per row for the top-k stream (rows * S workgroups).
+int topk_segments(int64_t rows, int64_t vocab, int k);
+
+size_t align_up(size_t x, size_t a);
+
+// ---- launchers (return hipGetLastError() after the launch) ----------------
+hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
+                              const FilterParams& fp, const SparseOut& out, int S,
+                              uint32_t* part_key, int32_t* part_id, int32_t* part_n,
+                              hipStream_t stream);
+
+hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
+                               float temperature, const DenseChunks& dc, hipStream_t stream);
+
+hipError_t launch_dense_row_stats(int64_t rows, float temperature, const DenseChunks& dc,
+                                  int32_t* out_count, double* out_stats, hipStream_t stream);
+
+struct LinearOut {
+    int32_t* tokens;
+    int32_t* accept_len;
+    int32_t* proposals;
+    uint32_t* flags;
+};
+
+hipError_t launch_linear_sparse(int32_t batch, int32_t B, const SparseOut& sup, uint64_t seed,
+                                uint64_t offset, const uint32_t* request_ids, const LinearOut& o,
+                                hipStream_t stream);
+
+// Scratch of the dense linear path.
+struct DenseScratch {
+    float* row_m;      // [rows]
+    double* row_S;     // [rows]
+    int32_t* jstar;    // [batch]
+    int32_t* y;        // [batch][B]
+    uint32_t* flags;   // [batch]
+    double* resid;     // [batch][nchunks]
+};
+
+hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, int64_t vocab,
+                               bool bf16, float temperature, const DenseChunks& dc,
+                               const DenseScratch& sc, uint64_t seed, uint64_t offset,
+                               const uint32_t* request_ids, const LinearOut& o, hipStream_t stream);
+
+struct TreeOut {
+    int32_t* node_token;
+    int32_t* node_parent;
+    int32_t* node_depth;
+    double* node_score;
+    int32_t* num_nodes;
+};
+
+hipError_t launch_tree_build(int32_t batch, int32_t B, int32_t K, int32_t V, const SparseOut& sup,
+                             const TreeOut& o, hipStream_t stream);
+
+struct WalkOut {
+    int32_t* tokens;
+    int32_t* path;
+    int32_t* accept_len;
+    uint32_t* flags;
+};
+
+hipError_t launch_tree_walk(int32_t batch, int32_t B, int32_t V, const SparseOut& sup,
+                            uint64_t seed, uint64_t offset, const uint32_t* request_ids,
+                            const int32_t* node_token, const int32_t* node_parent,
+                            const int32_t* num_nodes, const WalkOut& o, hipStream_t stream);
+
+}  // namespace uno

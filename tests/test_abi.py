@@ -1,0 +1,164 @@
+"""C ABI checks that need no GPU: every declared symbol is exported, status
+strings, workspace sizing, and every invalid argument is rejected on the host
+before anything is launched (all calls here fail validation, so no HIP call
+is made)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import lossless_draft_verify_amd as uno
+from lossless_draft_verify_amd import build as hip_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uno.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+F32, BF16 = 0, 1
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p(0x10002)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hip_build.LIB):
+        hip_build.build()
+    return uno.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*|size_t)\s+(uno_\w+)\s*\(", text, re.M)))
+
+
+def sp(T=1.0, k=50, p=0.95):
+    return ctypes.byref(uno.Sampling(T, k, p))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) >= {"uno_filter", "uno_sample_linear", "uno_build_tree", "uno_verify_tree",
+                          "uno_workspace_bytes", "uno_status_string", "uno_last_hip_error",
+                          "uno_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", hip_build.LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(uno_\w+)$", out, re.M))
+    for n in names:
+        assert n in exported, n
+        getattr(lib, n)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.uno_status_string(OK) == b"ok"
+    for s in (INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert lib.uno_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.uno_status_string(12345) == b"unknown status"
+    assert b"gfx950" in lib.uno_version()
+    assert lib.uno_last_hip_error() == 0
+
+
+def _ws(lib, op, batch, B, K, V, vocab, dtype, s):
+    n = ctypes.c_size_t(0)
+    st = lib.uno_workspace_bytes(op, batch, B, K, V, vocab, dtype, s, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes(lib):
+    N = 151936
+    # linear 8/1/8 b64 sparse: supports only (k = 50) for 1088 rows, no segment partials
+    st, n = _ws(lib, uno.OP_SAMPLE_LINEAR, 64, 8, 1, 8, N, F32, sp())
+    assert st == OK and n >= 1088 * 50 * (4 + 8) + 1088 * 4
+    # dense linear: chunk statistics for every row dominate
+    st, nd = _ws(lib, uno.OP_SAMPLE_LINEAR, 256, 16, 1, 16, N, BF16, sp(0.7, 0, 1.0))
+    nch = math.ceil(N / 2048)
+    assert st == OK and nd >= 256 * 33 * nch * (4 + 8 + 4)
+    # few rows -> segmented rows need partial lists
+    st, nt = _ws(lib, uno.OP_BUILD_TREE, 1, 16, 32, 32, N, F32, sp())
+    assert st == OK and nt > 16 * 50 * 12
+    st, nv = _ws(lib, uno.OP_VERIFY_TREE, 1, 16, 1, 32, N, F32, sp())
+    assert st == OK and nv > 33 * 50 * 12
+    # filter with many rows needs nothing beyond the caller's outputs
+    st, nf = _ws(lib, uno.OP_FILTER, 4096, 0, 0, 0, N, F32, sp())
+    assert st == OK and nf == 0
+    st, _ = _ws(lib, 9, 1, 1, 1, 1, N, F32, sp())
+    assert st == INVALID
+    assert lib.uno_workspace_bytes(0, 1, 1, 1, 1, N, F32, sp(), None) == INVALID
+
+
+@pytest.mark.parametrize("T,k,p,expect", [
+    (-1.0, 50, 0.95, INVALID), (float("nan"), 50, 0.95, INVALID), (float("inf"), 50, 0.95, INVALID),
+    (1.0, 50, 0.0, INVALID), (1.0, 50, 1.5, INVALID), (1.0, 50, float("nan"), INVALID),
+    (1.0, 0, 0.9, UNSUPPORTED), (1.0, 257, 1.0, UNSUPPORTED), (1.0, 300, 0.95, UNSUPPORTED),
+])
+def test_sampling_parameter_checks(lib, T, k, p, expect):
+    st, _ = _ws(lib, uno.OP_SAMPLE_LINEAR, 2, 4, 1, 4, 1000, F32, sp(T, k, p))
+    assert st == expect
+    ids = ctypes.c_void_p(0x20000)
+    assert lib.uno_filter(FAKE, F32, 4, 1000, sp(T, k, p), 256, ids, ids, ids, ids, None, 0, None) == expect
+
+
+def test_filter_argument_checks(lib):
+    out = ctypes.c_void_p(0x20000)
+    f = lib.uno_filter
+    assert f(FAKE, 2, 4, 1000, sp(), 64, out, out, out, out, None, 0, None) == UNSUPPORTED
+    assert f(FAKE, F32, -1, 1000, sp(), 64, out, out, out, out, None, 0, None) == INVALID
+    assert f(FAKE, F32, 4, 0, sp(), 64, out, out, out, out, None, 0, None) == INVALID
+    assert f(FAKE, F32, 4, 1 << 31, sp(), 64, out, out, out, out, None, 0, None) == INVALID
+    assert f(FAKE, F32, 4, 1000, None, 64, out, out, out, out, None, 0, None) == INVALID
+    assert f(FAKE, F32, 4, 1000, sp(), 49, out, out, out, out, None, 0, None) == INVALID   # cap < k
+    assert f(None, F32, 4, 1000, sp(), 64, out, out, out, out, None, 0, None) == INVALID
+    assert f(FAKE, F32, 4, 1000, sp(), 64, None, out, out, out, None, 0, None) == INVALID
+    assert f(FAKE, F32, 4, 1000, sp(), 64, out, out, None, out, None, 0, None) == INVALID
+    assert f(FAKE_ODD, F32, 4, 1000, sp(), 64, out, out, out, out, None, 0, None) == INVALID
+    # dense mode needs stats and a workspace
+    assert f(FAKE, F32, 4, 1000, sp(1.0, 0, 1.0), 0, None, None, out, None, None, 0, None) == INVALID
+    assert f(FAKE, F32, 4, 1000, sp(1.0, 0, 1.0), 0, None, None, out, out, None, 0, None) == WORKSPACE
+    # zero rows is a no-op
+    assert f(None, F32, 0, 1000, sp(), 0, None, None, None, None, None, 0, None) == OK
+
+
+def test_linear_argument_checks(lib):
+    f = lib.uno_sample_linear
+    o = ctypes.c_void_p(0x30000)
+    args = lambda batch=2, B=4, vocab=1000, d=FAKE, t=FAKE, s=None, dt=F32, ws=None, wsn=0, tok=o, acc=o: \
+        f(d, t, dt, batch, B, vocab, s or sp(), 1, 0, None, tok, acc, None, None, ws, wsn, None)
+    assert args(B=0) == INVALID
+    assert args(B=129) == INVALID
+    assert args(batch=-1) == INVALID
+    assert args(dt=7) == UNSUPPORTED
+    assert args(d=None) == INVALID
+    assert args(tok=None) == INVALID
+    assert args(acc=None) == INVALID
+    assert args(d=FAKE_ODD) == INVALID
+    assert args() == WORKSPACE                                       # sparse supports need ws
+    assert args(s=sp(1.0, 0, 1.0)) == WORKSPACE                      # dense chunk stats need ws
+    assert args(ws=ctypes.c_void_p(0x40001), wsn=1 << 30) == WORKSPACE   # misaligned
+    assert args(ws=ctypes.c_void_p(0x40000), wsn=16) == WORKSPACE        # too small
+    assert args(s=sp(1.0, 0, 0.5)) == UNSUPPORTED
+    assert args(batch=0, d=None, t=None, tok=None, acc=None) == OK
+
+
+def test_tree_argument_checks(lib):
+    o = ctypes.c_void_p(0x30000)
+    bt = lambda B=4, K=4, V=8, s=None, d=FAKE: lib.uno_build_tree(
+        d, F32, 2, B, K, V, 1000, s or sp(), o, o, o, None, o, None, 0, None)
+    assert bt(V=3) == INVALID              # V < B
+    assert bt(V=129, B=4, K=1) == INVALID  # V > 128
+    assert bt(K=0) == INVALID
+    assert bt(K=300, V=8) == INVALID       # V * K > 2048
+    assert bt(B=0) == INVALID
+    assert bt(s=sp(1.0, 0, 1.0)) == UNSUPPORTED     # dense tree sampling not built
+    assert bt(d=None) == INVALID
+    assert bt() == WORKSPACE
+    assert bt(K=256, V=8) == WORKSPACE     # V * K == 2048 is allowed
+    vt = lambda B=4, V=8, s=None: lib.uno_verify_tree(
+        FAKE, F32, 2, B, V, 1000, s or sp(), 1, 0, None, o, o, o, o, o, o, None, None, 0, None)
+    assert vt(V=3) == INVALID
+    assert vt(V=200) == INVALID
+    assert vt(s=sp(0.5, 0, 1.0)) == UNSUPPORTED
+    assert vt() == WORKSPACE
+    # greedy decoding is a sparse (k = 1) mode
+    assert vt(s=sp(0.0, 0, 1.0)) == WORKSPACE

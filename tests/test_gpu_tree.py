@@ -1,0 +1,125 @@
+"""GPU parity of uno_build_tree and uno_verify_tree against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import lossless_draft_verify_amd as uno
+import oracle
+from lossless_draft_verify_amd import synth
+from gpu_util import Tally, device, np_of, say
+from stats_util import chisq_pvalue
+
+pytestmark = pytest.mark.gpu
+
+TREE_KEYS = ("node_token", "node_parent", "node_depth", "num_nodes")
+
+
+def _build_parity(draft, K, V, T, k, p, label):
+    g = uno.build_tree(draft, K, V, T, k, p)
+    torch.cuda.synchronize()
+    o = oracle.build_tree(synth.as_float32_numpy(draft), K, V, T, k, p)
+    for key in TREE_KEYS:
+        gk = np_of(g[key])
+        bad = np.any(gk.reshape(gk.shape[0], -1) != o[key].reshape(gk.shape[0], -1), axis=1)
+        # a pop order may only differ where two scores are within rounding of each other
+        assert not np.any(bad & (o["min_gap"] >= 1e-12)), (label, key, np.flatnonzero(bad)[:4])
+    # scores are products of filtered probabilities, each within an ulp or two of
+    # the reference (the device and host exp may differ in the last bit)
+    np.testing.assert_allclose(np_of(g["node_score"]), o["node_score"], rtol=1e-12, atol=0)
+    return g, o
+
+
+def _verify_parity(target, B, tree, T, k, p, seed, offset, tally, label, request_ids=None):
+    dev = target.device
+    tk = torch.from_numpy(tree["node_token"]).to(dev)
+    pa = torch.from_numpy(tree["node_parent"]).to(dev)
+    nn = torch.from_numpy(tree["num_nodes"]).to(dev)
+    g = uno.verify_tree(target, B, tk, pa, nn, T, k, p, seed, offset, request_ids=request_ids)
+    torch.cuda.synchronize()
+    rid = None if request_ids is None else np.asarray(request_ids, dtype=np.uint32)
+    o = oracle.verify_tree(synth.as_float32_numpy(target), B, tree["node_token"], tree["node_parent"],
+                           tree["num_nodes"], T, k, p, seed=seed, offset=offset, request_ids=rid)
+    gg = {key: np_of(g[key]) for key in ("tokens", "path", "accept_len")}
+    tally.compare(gg, o, ("tokens", "path", "accept_len"), label)
+    return gg
+
+
+def _tree_cycles(w, cycles, batch=None, label=None):
+    dev = device()
+    tally = Tally()
+    acc = []
+    for c in range(cycles):
+        draft, R = synth.tree_inputs(w, cycle=c, device=dev, batch=batch)
+        _, o = _build_parity(draft, w.K, w.V, w.temperature, w.top_k, w.top_p, f"{w.name} build {c}")
+        # the walk checks against the oracle's own tree, so its inputs never come from the HIP path
+        tgt = synth.tree_target_rows(R, torch.from_numpy(o["node_depth"]), torch.from_numpy(o["num_nodes"]), w.V)
+        gg = _verify_parity(tgt, w.B, o, w.temperature, w.top_k, w.top_p, w.seed, c, tally,
+                            f"{w.name} verify {c}")
+        acc.append(gg["accept_len"])
+    tally.check_rate()
+    a = np.concatenate(acc)
+    say(f"{label or w.name}: {tally.total} request-cycles, excused {tally.excused}, mean accept_len "
+        f"{a.mean():.3f}, TPF {oracle.tpf(a):.3f}")
+
+
+def test_tree_16_32_32_full_size():
+    _tree_cycles(synth.WORKLOADS["tree_16_32_32"], 6)
+
+
+def test_tree_8_16_8_reduced_batch():
+    _tree_cycles(synth.WORKLOADS["tree_8_16_8"], 3, batch=8, label="tree_8_16_8 b8")
+
+
+def test_tree_8_16_8_full_size():
+    _tree_cycles(synth.WORKLOADS["tree_8_16_8"], 1, label="tree_8_16_8 b64")
+
+
+@pytest.mark.parametrize("B,K,V,T,k,p", [(3, 3, 10, 1.0, 5, 1.0),
+                                         (4, 1, 4, 1.0, 50, 0.95), (2, 8, 16, 0.5, 8, 1.0),
+                                         (5, 16, 128, 1.0, 16, 1.0), (6, 4, 20, 0.0, 0, 1.0),
+                                         (8, 256, 8, 1.0, 256, 1.0)])
+def test_tree_shapes_small_vocab(B, K, V, T, k, p):
+    dev = device()
+    rng = np.random.default_rng(B * 100 + K)
+    batch, N = 12, 301
+    d = (rng.standard_normal((batch, B, N)) * 2).astype(np.float32)
+    draft = torch.from_numpy(d).to(dev)
+    _, o = _build_parity(draft, K, V, T, k, p, f"shape B{B} K{K} V{V}")
+    tgt = torch.from_numpy((rng.standard_normal((batch, V + 1, N)) * 2).astype(np.float32)).to(dev)
+    t = Tally()
+    rid = np.arange(batch, dtype=np.uint32) * 7919
+    for c in range(3):
+        _verify_parity(tgt, B, o, T, k, p, 17, c, t, f"walk B{B} K{K} V{V}", request_ids=rid)
+    t.check_rate()
+
+
+def test_tree_ties_in_bf16():
+    # coarse logits give exact probability ties between siblings and across depths
+    dev = device()
+    rng = np.random.default_rng(41)
+    batch, B, N = 16, 4, 500
+    d = np.round(rng.standard_normal((batch, B, N)) * 2) / 2
+    draft = torch.from_numpy(d.astype(np.float32)).to(dev).to(torch.bfloat16)
+    _build_parity(draft, 6, 24, 1.0, 10, 1.0, "bf16 ties")
+
+
+def test_walk_is_lossless_small_vocab():
+    dev = device()
+    rng = np.random.default_rng(42)
+    B, K, V, N, n = 3, 3, 7, 9, 100_000
+    d = (rng.standard_normal((1, B, N)) * 1.2).astype(np.float32)
+    tree = oracle.build_tree(d, K, V, 1.0, 0, 1.0)
+    target_rows = (rng.standard_normal((V + 1, N)) * 1.2).astype(np.float32)
+    tgt = torch.from_numpy(target_rows).to(dev).expand(n, V + 1, N).contiguous()
+    rep = lambda a: torch.from_numpy(np.ascontiguousarray(np.tile(a, (n, 1)))).to(dev)
+    g = uno.verify_tree(tgt, B, rep(tree["node_token"]), rep(tree["node_parent"]),
+                        torch.full((n,), int(tree["num_nodes"][0]), dtype=torch.int32, device=dev),
+                        1.0, 5, 1.0, 77, 0)
+    torch.cuda.synchronize()
+    P = oracle.filter_rows(target_rows, 1.0, 5, 1.0)["dense"]
+    tok, path = np_of(g["tokens"]), np_of(g["path"])
+    for node in range(int(tree["num_nodes"][0])):
+        for dd in range(B + 1):
+            sel = path[:, dd] == node
+            if sel.sum() > 3000:
+                assert chisq_pvalue(tok[sel, dd], P[node]) > 1e-4, (node, dd)
