@@ -1,0 +1,294 @@
+"""Benchmark of the UNO decode-cycle sampling path on one MI355X.
+
+A step is one full cycle of the hot path over one batch of synthetic logits
+already resident in HBM: for the linear workloads one uno_sample_linear call
+(filter every draft and target row, proposals, acceptance, residual / bonus);
+for the tree workloads one uno_build_tree plus one uno_verify_tree call.
+Inputs rotate over a pool of distinct cycles (> 1.5 GB) so the 256 MB
+Infinity Cache cannot serve repeated steps.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified vocab rows/sec + achieved HBM GB/s (vocab 151936, linear 8/1/8 b64)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+DOMINANT = "topk_stream_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_stream_kernel_linear_8_1_8_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="linear_8_1_8")
+    ap.add_argument("--pool", type=int, default=3, help="distinct input cycles rotated through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("filter_kernels.hip", "uno_device.h", "uno_internal.h"):
+        with open(os.path.join(ROOT, "lossless_draft_verify_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry():
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sampling path has no multi-GPU component in this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lossless_draft_verify_amd as uno
+    from lossless_draft_verify_amd import synth
+    from lossless_draft_verify_amd import build as hip_build
+
+    if not os.path.exists(hip_build.LIB):
+        hip_build.build()
+    uno.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    stream = torch.cuda.current_stream()
+
+    # ---- input pool -------------------------------------------------------------
+    pool = []
+    t0 = time.time()
+    for c in range(args.pool):
+        if w.mode == "linear":
+            # draft and target rows in one buffer, so uno_filter can replay the
+            # exact filter launch of the step over the same rows
+            draft, target = synth.linear_inputs(w, cycle=c, device=dev)
+            allrows = torch.empty((w.batch * (2 * w.B + 1), w.vocab), dtype=draft.dtype, device=dev)
+            nd = w.batch * w.B
+            allrows[:nd] = draft.view(nd, w.vocab)
+            allrows[nd:] = target.view(-1, w.vocab)
+            del draft, target
+            d = allrows[:nd].view(w.batch, w.B, w.vocab)
+            t = allrows[nd:].view(w.batch, w.B + 1, w.vocab)
+            pool.append(dict(all=allrows, draft=d, target=t))
+        else:
+            draft, R = synth.tree_inputs(w, cycle=c, device=dev)
+            tree = uno.build_tree(draft, w.K, w.V, w.temperature, w.top_k, w.top_p)
+            tgt = synth.tree_target_rows(R, tree["node_depth"], tree["num_nodes"], w.V)
+            del R
+            pool.append(dict(draft=draft, target=tgt))
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: pool of {args.pool} cycles ready in {time.time() - t0:.1f}s "
+        f"({w.bytes_per_cycle / 1e6:.1f} MB per cycle)")
+
+    # ---- step: direct C-ABI calls with pre-built arguments -------------------------
+    import ctypes
+    lib = uno.load_library()
+    dt = 0 if w.dtype == "f32" else 1
+    sp = uno.Sampling(w.temperature, w.top_k, w.top_p)
+    spr = ctypes.byref(sp)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+    def wsbuf(op, K, V):
+        n = uno.workspace_bytes(op, w.batch, w.B, K, V, w.vocab, dt, w.temperature, w.top_k, w.top_p)
+        if n == 0:
+            return None, 0
+        t = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        a = (t.data_ptr() + 255) // 256 * 256
+        return (t, ctypes.c_void_p(a)), t.numel() - (a - t.data_ptr())
+
+    if w.mode == "linear":
+        tokens = torch.empty((w.batch, w.B + 1), dtype=torch.int32, device=dev)
+        acc = torch.empty(w.batch, dtype=torch.int32, device=dev)
+        prop = torch.empty((w.batch, w.B), dtype=torch.int32, device=dev)
+        flags = torch.empty(w.batch, dtype=torch.int32, device=dev)
+        ws, wsn = wsbuf(uno.OP_SAMPLE_LINEAR, 1, w.B)
+        ptrs = [(P(p["draft"]), P(p["target"])) for p in pool]
+
+        def step(i):
+            d, t = ptrs[i % len(ptrs)]
+            st = lib.uno_sample_linear(d, t, dt, w.batch, w.B, w.vocab, spr, w.seed, i, None, P(tokens), P(acc),
+                                       P(prop), P(flags), ws[1] if ws else None, wsn, sptr)
+            if st != 0:
+                raise uno.UnoError(st, "uno_sample_linear")
+            return acc
+    else:
+        ntok = torch.empty((w.batch, w.V + 1), dtype=torch.int32, device=dev)
+        npar = torch.empty_like(ntok)
+        ndep = torch.empty_like(ntok)
+        nnum = torch.empty(w.batch, dtype=torch.int32, device=dev)
+        tokens = torch.empty((w.batch, w.B + 1), dtype=torch.int32, device=dev)
+        path = torch.empty_like(tokens)
+        acc = torch.empty(w.batch, dtype=torch.int32, device=dev)
+        flags = torch.empty(w.batch, dtype=torch.int32, device=dev)
+        wsb, wsbn = wsbuf(uno.OP_BUILD_TREE, w.K, w.V)
+        wsv, wsvn = wsbuf(uno.OP_VERIFY_TREE, 1, w.V)
+        ptrs = [(P(p["draft"]), P(p["target"])) for p in pool]
+
+        def step(i):
+            d, t = ptrs[i % len(ptrs)]
+            st = lib.uno_build_tree(d, dt, w.batch, w.B, w.K, w.V, w.vocab, spr, P(ntok), P(npar), P(ndep), None,
+                                    P(nnum), wsb[1] if wsb else None, wsbn, sptr)
+            if st != 0:
+                raise uno.UnoError(st, "uno_build_tree")
+            st = lib.uno_verify_tree(t, dt, w.batch, w.B, w.V, w.vocab, spr, w.seed, i, None, P(ntok), P(npar),
+                                     P(nnum), P(tokens), P(path), P(acc), P(flags), wsv[1] if wsv else None,
+                                     wsvn, sptr)
+            if st != 0:
+                raise uno.UnoError(st, "uno_verify_tree")
+            return acc
+
+    # warm-up steps also give the tokens-per-forward figure (outside the timed region)
+    acc_total = 0
+    for i in range(args.warmup):
+        acc_total += int(step(i).sum().item())
+    tpf = acc_total / (2.0 * w.batch * max(args.warmup, 1))
+    torch.cuda.synchronize()
+
+    # ---- timed steps --------------------------------------------------------------
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1e3 * wall / args.steps
+    rows_per_s = w.rows_per_cycle * args.steps / wall
+    gbs = w.bytes_per_cycle * args.steps / wall / 1e9
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events {ev_ms / args.steps * 1e3:.1f} us), "
+        f"{rows_per_s / 1e6:.2f} M rows/s, {gbs:.0f} GB/s algorithmic, TPF {tpf:.3f} (warm-up steps)")
+
+    # ---- dominant kernel: the same filter launch, timed alone with HIP events ------
+    roofline = None
+    if w.mode == "linear" and w.top_k > 0:
+        ids = torch.empty((pool[0]["all"].shape[0], w.top_k), dtype=torch.int32, device=dev)
+        probs = torch.empty((pool[0]["all"].shape[0], w.top_k), dtype=torch.float64, device=dev)
+        cnt = torch.empty(pool[0]["all"].shape[0], dtype=torch.int32, device=dev)
+        nrows = pool[0]["all"].shape[0]
+        n_f = max(50, min(args.steps, 500))
+
+        def filt(i):
+            a = pool[i % len(pool)]["all"]
+            st = lib.uno_filter(ctypes.c_void_p(a.data_ptr()), dt, nrows, w.vocab, ctypes.byref(sp), w.top_k,
+                                ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(probs.data_ptr()),
+                                ctypes.c_void_p(cnt.data_ptr()), None, None, 0,
+                                ctypes.c_void_p(stream.cuda_stream))
+            assert st == 0, st
+        for i in range(10):
+            filt(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(n_f):
+            filt(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        k_us = ev0.elapsed_time(ev1) * 1e3 / n_f
+        alg_bytes = nrows * w.vocab * w.elem_bytes
+        achieved = alg_bytes / (k_us * 1e-6) / 1e9
+        traffic = traffic_entry()
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": DOMINANT, "kernel_us": round(k_us, 2), "bytes_per_launch": alg_bytes}
+        log(f"[bench] {DOMINANT}: {k_us:.1f} us/launch over {n_f} launches -> {achieved:.0f} GB/s "
+            f"({100 * achieved / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload ----------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        p = pool[0]
+        n_req = 0
+        rows = 0
+        t0 = time.perf_counter()
+        if w.mode == "linear":
+            dnp = synth.as_float32_numpy(p["draft"])
+            tnp = synth.as_float32_numpy(p["target"])
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < args.cpu_seconds and n_req < w.batch * 8:
+                lo = n_req % w.batch
+                hi = min(lo + 16, w.batch)
+                oracle.linear(dnp[lo:hi], tnp[lo:hi], w.temperature, w.top_k, w.top_p, w.seed, 0,
+                              request_ids=np.arange(lo, hi, dtype=np.uint32))
+                n_req += hi - lo
+                rows += (hi - lo) * (2 * w.B + 1)
+        else:
+            dnp = synth.as_float32_numpy(p["draft"])
+            tnp = synth.as_float32_numpy(p["target"])
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < args.cpu_seconds and n_req < w.batch * 8:
+                lo = n_req % w.batch
+                hi = min(lo + 16, w.batch)
+                tr = oracle.build_tree(dnp[lo:hi], w.K, w.V, w.temperature, w.top_k, w.top_p)
+                oracle.verify_tree(tnp[lo:hi], w.B, tr["node_token"], tr["node_parent"], tr["num_nodes"],
+                                   w.temperature, w.top_k, w.top_p, w.seed, 0,
+                                   request_ids=np.arange(lo, hi, dtype=np.uint32))
+                n_req += hi - lo
+                rows += (hi - lo) * (w.B + w.V + 1)
+        el = time.perf_counter() - t0
+        cpu = {"value": round(rows / el, 1), "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{n_req} request-cycles ({rows} rows) of {w.name}, {el:.1f} s"}
+        log(f"[bench] oracle: {rows / el:.0f} rows/s on {oracle.num_threads()} threads ({n_req} requests)")
+
+    res = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "B": w.B, "K": w.K, "V": w.V or w.B,
+                   "vocab": w.vocab, "logits": w.dtype, "temperature": w.temperature, "top_k": w.top_k,
+                   "top_p": w.top_p, "rows_per_step": w.rows_per_cycle, "bytes_per_step": w.bytes_per_cycle,
+                   "pool_cycles": args.pool},
+        "hbm_gbs_algorithmic": round(gbs, 1),
+        "tpf": round(tpf, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,8 +21,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kCap = 1024;      // candidate entries per wave
-constexpr int kUnroll = 8;      // 16-byte vectors in flight per lane
+constexpr int kCap = 768;       // candidate entries per wave
+constexpr int kPerIter = 16;    // logits per lane per streaming iteration
 constexpr int kMaxK = 256;      // UNO_MAX_TOP_K
 
 // kk-th largest value (1-based) among entries i < cnt with pred(i), by an
@@ -206,13 +206,28 @@ __device__ void finalize_row(const uint32_t* sk, const int32_t* sid, int n, cons
 }
 
 // ---- top-k stream ------------------------------------------------------------
+// Number of set bits of `c` (< 64) over the wave, and over the lanes below this one.
+__device__ __forceinline__ uint32_t wave_count_prefix(uint32_t c, uint32_t* total)
+{
+    uint32_t tot = 0, excl = 0;
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+        const uint64_t m = __ballot((c >> b) & 1u);
+        tot += (uint32_t)__popcll(m) << b;
+        excl += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+    }
+    *total = tot;
+    return excl;
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void topk_stream_kernel(
+__global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     RowSource src, int64_t rows, int64_t N, FilterParams fp, SparseOut out, int S,
     uint32_t* part_key, int32_t* part_id, int32_t* part_n)
 {
     using V = Vec<BF16>;
     constexpr int EPV = V::EPV, ESZ = V::ESZ;
+    constexpr int U = kPerIter / EPV;                  // 16-byte vectors per lane per iteration
     __shared__ uint32_t s_key[kWaves][kCap];
     __shared__ int32_t s_id[kWaves][kCap];
     __shared__ uint32_t s_hist[kWaves][256];
@@ -237,10 +252,11 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
     uint32_t* hist = s_hist[w];
     const int k = fp.k;
     int cnt = 0;
-    // Admission threshold: thr_key exactly (keys, strict >); thr is its float
-    // value, used only by the skip test of the fast path.
+    // Admission: key(z) > thr_key.  thr is the float of thr_key; for logits
+    // `z > thr` (an ordered compare, false for NaN) is the same test.  It starts
+    // at -inf, passed in as an argument so the compare is never constant-folded.
     uint32_t thr_key = kKeyNegInf;
-    float thr = -INFINITY;
+    float thr = fp.thr_init;
 
     auto compact = [&]() __attribute__((always_inline)) {
         uint32_t T;
@@ -265,11 +281,12 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
     if (seg == 0 && w == 0 && g.head > 0) scalar_part(0, g.head);
 
     const typename V::T* body = reinterpret_cast<const typename V::T*>(row + g.head * ESZ);
-    // slow path of one iteration: some lane holds a logit above the threshold.
-    // Vectors are re-read (cache hits) so x[] below is only indexed by constants.
-    auto slow_path = [&](int64_t v0) __attribute__((always_inline)) {
+    // Fallback for an iteration whose candidates cannot all fit the buffer even
+    // after a cut (only while the threshold is still low): vector by vector,
+    // re-reading each vector (a cache hit), with a cut whenever the buffer fills.
+    auto reload_path = [&](int64_t v0) __attribute__((always_inline)) {
 #pragma unroll 1
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t vbase = v0 + u * kWave;
             if (vbase >= we) break;
             const int64_t vl = vbase + lane;
@@ -291,32 +308,68 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
             }
         }
     };
-    constexpr int64_t kStep = (int64_t)kUnroll * kWave;
-    int64_t v0 = wb;
-    for (; v0 + kStep <= we; v0 += kStep) {          // whole iterations: unguarded loads
-        typename V::T x[kUnroll];
+    auto admit_mask = [&](const typename V::T (&x)[U]) __attribute__((always_inline)) {
+        uint32_t mask = 0;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) x[u] = body[v0 + u * kWave + lane];
-        float mx = -INFINITY;
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, V::get(x[u], e));
-        if (__ballot(mx > thr) != 0ull) slow_path(v0);
-    }
-    if (v0 < we) {                                     // last partial iteration
-        typename V::T x[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t v = v0 + u * kWave + lane;
-            x[u] = (v < we) ? body[v] : V::neg_inf();
+            for (int e = 0; e < EPV; ++e) mask |= (V::get(x[u], e) > thr ? 1u : 0u) << (u * EPV + e);
+        return mask;
+    };
+    // One iteration: U vectors per lane (vector v0 + u*64 + lane), already in x.
+    auto process = [&](const typename V::T (&x)[U], int64_t v0) __attribute__((always_inline)) {
+        uint32_t mask = admit_mask(x);
+        uint32_t total;
+        uint32_t excl = wave_count_prefix(__popc(mask), &total);
+        if (total == 0) return;
+        if (cnt + (int)total > kCap) {
+            compact();
+            mask = admit_mask(x);
+            excl = wave_count_prefix(__popc(mask), &total);
+            if (cnt + (int)total > kCap) { reload_path(v0); return; }
         }
-        float mx = -INFINITY;
+        int pos = cnt + (int)excl;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, V::get(x[u], e));
-        if (__ballot(mx > thr) != 0ull) slow_path(v0);
+            for (int e = 0; e < EPV; ++e)
+                if (mask & (1u << (u * EPV + e))) {
+                    bk[pos] = float_key(V::get(x[u], e));
+                    bi[pos] = (int32_t)(g.head + (v0 + u * kWave + lane) * EPV + e);
+                    ++pos;
+                }
+        cnt += (int)total;
+    };
+
+    // whole iterations with the next iteration's loads in flight
+    constexpr int64_t kStep = (int64_t)U * kWave;
+    const int64_t nfull = (we - wb) / kStep;
+    typename V::T xc[U], xn[U];
+    if (nfull > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) xc[u] = body[wb + u * kWave + lane];
+    }
+    for (int64_t it = 0; it < nfull; ++it) {
+        const int64_t v0 = wb + it * kStep;
+        // unconditional prefetch (the last iteration re-reads its own vectors), so
+        // the number of loads in flight is the same on every path
+        const int64_t vn = (it + 1 < nfull) ? v0 + kStep : v0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) xn[u] = body[vn + u * kWave + lane];
+        process(xc, v0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) xc[u] = xn[u];
+    }
+    {   // last partial iteration
+        const int64_t v0 = wb + nfull * kStep;
+        if (v0 < we) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t v = v0 + u * kWave + lane;
+                xc[u] = (v < we) ? body[v] : V::neg_inf();
+            }
+            process(xc, v0);
+        }
     }
 
     if (seg == S - 1 && w == kWaves - 1 && g.tail_beg < N) scalar_part(g.tail_beg, N - g.tail_beg);

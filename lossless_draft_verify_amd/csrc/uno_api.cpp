@@ -138,6 +138,7 @@ FilterParams filter_params(const uno_sampling_t* sp, const Mode& m)
     fp.k = m.k;
     fp.greedy = m.greedy ? 1 : 0;
     fp.topp_on = m.topp_on ? 1 : 0;
+    fp.thr_init = -INFINITY;
     return fp;
 }
 

@@ -25,6 +25,7 @@ struct FilterParams {
     int32_t k;        // effective top-k (1 when greedy)
     int32_t greedy;   // temperature == 0
     int32_t topp_on;  // top_p < 1
+    float thr_init;   // -inf: initial admission threshold of the top-k stream
 };
 
 // Compact per-row supports in filter order.
