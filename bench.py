@@ -201,12 +201,15 @@ def main():
         cnt = torch.empty(pool[0]["all"].shape[0], dtype=torch.int32, device=dev)
         nrows = pool[0]["all"].shape[0]
         n_f = max(50, min(args.steps, 500))
+        fws_n = uno.workspace_bytes(uno.OP_FILTER, nrows, 0, 0, 0, w.vocab, dt, w.temperature, w.top_k, w.top_p)
+        fws = torch.empty(fws_n + 256, dtype=torch.uint8, device=dev)
+        fws_p = ctypes.c_void_p((fws.data_ptr() + 255) // 256 * 256) if fws_n else None
 
         def filt(i):
             a = pool[i % len(pool)]["all"]
             st = lib.uno_filter(ctypes.c_void_p(a.data_ptr()), dt, nrows, w.vocab, ctypes.byref(sp), w.top_k,
                                 ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(probs.data_ptr()),
-                                ctypes.c_void_p(cnt.data_ptr()), None, None, 0,
+                                ctypes.c_void_p(cnt.data_ptr()), None, fws_p, fws_n,
                                 ctypes.c_void_p(stream.cuda_stream))
             assert st == 0, st
         for i in range(10):

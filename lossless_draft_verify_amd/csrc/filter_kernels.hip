@@ -21,137 +21,215 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kCap = 768;       // candidate entries per wave
+constexpr int kCap = 768;       // candidate entries per wave (12 per lane)
+constexpr int kCapE = kCap / 64;
 constexpr int kPerIter = 16;    // logits per lane per streaming iteration
 constexpr int kMaxK = 256;      // UNO_MAX_TOP_K
 
-// kk-th largest value (1-based) among entries i < cnt with pred(i), by an
-// 8-bit radix select over a 256-bin LDS histogram.  Requires at least kk such
-// entries.  On return *kk_left is the rank of the k-th element among the
-// entries equal to the returned value.
-template <typename GetV, typename Pred>
-__device__ uint32_t wave_kth_largest(int cnt, int kk, GetV getv, Pred pred, uint32_t* hist,
-                                     int lane, int* kk_left)
+// ---- candidate buffers and register-resident lists ----------------------------
+// A streaming candidate is (raw float bits of the logit, token id); keys are
+// formed only when a list is loaded into registers.
+using Cand = uint2;
+
+// Entry j*64 + lane of a wave's list lives in kv[j] / iv[j].  Key 0 pads unused
+// slots; it ranks below every admitted key (admitted keys exceed the key of -inf).
+template <int E>
+struct RegList {
+    uint32_t kv[E];
+    int32_t iv[E];
+};
+
+// Loads entries [0, cnt) of buf (which holds at least E*64 entries; slots past
+// cnt are read but padded).
+template <int E>
+__device__ __forceinline__ void reg_load(RegList<E>& L, const Cand* buf, int cnt, int lane)
+{
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const int i = j * kWave + lane;
+        const bool in = i < cnt;
+        const Cand c = buf[i];
+        L.kv[j] = in ? float_key(__uint_as_float(c.x)) : 0u;
+        L.iv[j] = in ? (int32_t)c.y : 0x7FFFFFFF;
+    }
+}
+
+// Wave-wide number of entries with key >= t (t >= 1: padding never counts).
+template <int E>
+__device__ __forceinline__ int reg_count_ge(const RegList<E>& L, uint32_t t)
+{
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) c += __popcll(__ballot(L.kv[j] >= t));
+    return c;
+}
+
+// Largest t whose bits below min_bit are zero with count(key >= t) >= k
+// (requires k <= count of entries): the k-th largest key, truncated.
+template <int E>
+__device__ __forceinline__ uint32_t reg_kth_key(const RegList<E>& L, int k, int min_bit)
 {
     uint32_t prefix = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        const uint32_t hmask = (shift == 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
-        for (int b = lane; b < 256; b += kWave) hist[b] = 0u;
-        wave_sync();
-        for (int i = lane; i < cnt; i += kWave) {
-            if (!pred(i)) continue;
-            const uint32_t v = getv(i);
-            if ((v & hmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
-        }
-        wave_sync();
-        // lane l owns bins 255-4l .. 252-4l, so lane order walks the bins downward
-        const int b0 = 255 - 4 * lane;
-        const uint32_t c0 = hist[b0], c1 = hist[b0 - 1], c2 = hist[b0 - 2], c3 = hist[b0 - 3];
-        const uint32_t lsum = c0 + c1 + c2 + c3;
-        const uint32_t incl = wave_incl_scan_u32(lsum, lane);
-        const uint32_t excl = incl - lsum;
-        const uint32_t need = (uint32_t)kk;
-        int found = -1;
-        uint32_t before = 0;
-        if (excl < need && incl >= need) {
-            uint32_t a = excl;
-            if (a + c0 >= need) { found = b0; before = a; }
-            else {
-                a += c0;
-                if (a + c1 >= need) { found = b0 - 1; before = a; }
-                else {
-                    a += c1;
-                    if (a + c2 >= need) { found = b0 - 2; before = a; }
-                    else { a += c2; found = b0 - 3; before = a; }
-                }
-            }
-        }
-        const uint64_t bal = __ballot(found >= 0);
-        const int src = bal ? wave_first_lane(bal) : 0;
-        const int bin = __shfl(found, src, kWave);
-        const uint32_t bef = __shfl(before, src, kWave);
-        prefix |= (uint32_t)(bin & 255) << shift;
-        kk -= (int)bef;
-        wave_sync();
+    for (int b = 31; b >= min_bit; --b) {
+        const uint32_t cand = prefix | (1u << b);
+        if (reg_count_ge(L, cand) >= k) prefix = cand;
     }
-    *kk_left = kk;
     return prefix;
 }
 
-// Cut the wave's candidate buffer to the exact top-k by (key desc, id asc).
-// Returns the new count; when the old count was >= k, *kth is the key of the
-// k-th entry and *full is set.
-__device__ int wave_topk_exact(uint32_t* key, int32_t* id, int cnt, int k, uint32_t* hist,
-                               int lane, uint32_t* kth, bool* full)
+// Write the entries with keep(kv, iv) compactly to buf (as candidates);
+// returns their number.  keep must reject key 0 (padding).
+template <int E, typename Keep>
+__device__ __forceinline__ int reg_store_if(const RegList<E>& L, Keep keep, Cand* buf)
 {
-    *full = false;
-    if (cnt < k) return cnt;
-    int kk;
-    const uint32_t T = wave_kth_largest(
-        cnt, k, [&](int i) { return key[i]; }, [](int) { return true; }, hist, lane, &kk);
-    uint32_t eq = 0;
-    for (int i = lane; i < cnt; i += kWave) eq += (key[i] == T) ? 1u : 0u;
-    eq = wave_sum_u32(eq);
-    int32_t idcut = 0x7FFFFFFF;
-    if ((int)eq > kk) {
-        int kk2;
-        const uint32_t v = wave_kth_largest(
-            cnt, kk, [&](int i) { return ~(uint32_t)id[i]; }, [&](int i) { return key[i] == T; },
-            hist, lane, &kk2);
-        idcut = (int32_t)~v;
-    }
     int out = 0;
-    for (int base = 0; base < cnt; base += kWave) {
-        const int i = base + lane;
-        uint32_t kv = 0;
-        int32_t iv = 0;
-        bool keep = false;
-        if (i < cnt) {
-            kv = key[i];
-            iv = id[i];
-            keep = (kv > T) || (kv == T && iv <= idcut);
-        }
-        const uint64_t m = __ballot(keep);
-        wave_sync();
-        if (keep) {
-            const int pos = out + __popcll(m & lanes_below(lane));
-            key[pos] = kv;
-            id[pos] = iv;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const bool kp = keep(L.kv[j], L.iv[j]);
+        const uint64_t m = __ballot(kp);
+        if (kp) {
+            const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)out));
+            buf[pos] = make_uint2(__float_as_uint(key_float(L.kv[j])), (uint32_t)L.iv[j]);
         }
         out += __popcll(m);
-        wave_sync();
     }
-    *kth = T;
-    *full = true;
     return out;
 }
 
-// Sort n entries by (key desc, id asc) into okey/oid (rank by counting).
-__device__ void wave_sort_desc(const uint32_t* key, const int32_t* id, int n, uint32_t* okey,
-                               int32_t* oid, int lane)
+// Exact top-k by (key desc, id asc) of the >= k entries in L, written to buf
+// (unordered); *kth receives the k-th key.
+template <int E>
+__device__ __forceinline__ int reg_select_exact(const RegList<E>& L, int k, Cand* buf, uint32_t* kth)
 {
-    for (int i = lane; i < n; i += kWave) {
-        const uint32_t ki = key[i];
-        const int32_t ii = id[i];
-        int r = 0;
-        for (int j = 0; j < n; ++j) {
-            const uint32_t kj = key[j];
-            const int32_t ij = id[j];
-            r += (kj > ki || (kj == ki && ij < ii)) ? 1 : 0;
+    const uint32_t T = reg_kth_key(L, k, 0);
+    const int ge = reg_count_ge(L, T);
+    const int gt = reg_count_ge(L, T + 1u);
+    const int need = k - gt;              // entries with key == T to keep, smallest ids first
+    uint32_t idcut = 0x7FFFFFFFu;
+    if (ge - gt > need) {
+        // need-th smallest id among the entries with key == T, bit by bit
+        uint32_t x = 0;
+        for (int b = 30; b >= 0; --b) {
+            const uint32_t y = x | ((1u << b) - 1u);
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < E; ++j) c += __popcll(__ballot(L.kv[j] == T && (uint32_t)L.iv[j] <= y));
+            if (c < need) x |= 1u << b;
         }
-        okey[r] = ki;
-        oid[r] = ii;
+        idcut = x;
     }
-    wave_sync();
+    *kth = T;
+    return reg_store_if(L, [&](uint32_t kv, int32_t iv) {
+        return kv > T || (kv == T && (uint32_t)iv <= idcut);
+    }, buf);
 }
 
-// Softmax over the sorted top-k set, top-p cut, renormalisation; writes the
-// row's support.  Same operation order as the filter definition: normaliser
-// summed in filter order, pi = e / S, cumulative pi in filter order, kept
-// probabilities pi / (kept mass) when top-p is on.
-__device__ void finalize_row(const uint32_t* sk, const int32_t* sid, int n, const FilterParams& fp,
-                             double* scratch, const SparseOut& out, int64_t r, int lane)
+// Cut of a wave's candidate list (cnt >= k entries in buf, cnt <= E*64): keep
+// every entry whose key lies in or above the 16-bit key bin holding the k-th
+// largest key (at least k stay), or exactly the top-k when more than `limit`
+// would.  Returns the new count; *lo receives a key that every kept entry
+// reaches and that at least k kept entries reach (the bin's lower edge, or
+// the k-th key).  While streaming, admitting only keys above *lo loses
+// nothing: the stream visits ids in increasing order, so a later logit whose
+// key does not exceed *lo ranks below at least k kept entries.
+template <int E>
+__device__ __forceinline__ int wave_cut(Cand* buf, int cnt, int k, int limit, int lane, uint32_t* lo)
 {
+    RegList<E> L;
+    reg_load(L, buf, cnt, lane);
+    wave_sync();
+    const uint32_t b = reg_kth_key(L, k, 16);
+    int c;
+    if (reg_count_ge(L, b) > limit) {
+        c = reg_select_exact(L, k, buf, lo);
+    } else {
+        c = reg_store_if(L, [&](uint32_t kv, int32_t) { return kv >= b; }, buf);
+        *lo = b;
+    }
+    wave_sync();
+    return c;
+}
+
+// k-th largest of one key per lane (k <= 64), by bitwise search over ballots.
+__device__ __forceinline__ uint32_t wave_kth_largest_of_lanes(uint32_t v, int k)
+{
+    uint32_t prefix = 0;
+#pragma unroll 1
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = prefix | (1u << b);
+        if (__popcll(__ballot(v >= cand)) >= k) prefix = cand;
+    }
+    return prefix;
+}
+
+// Float threshold equivalent to "key > t" for every non-NaN logit.  Key
+// 0x7FFFFFFF (the key of -0, which float_key folds onto +0) maps to the
+// largest negative float instead.
+__device__ __forceinline__ float thr_float(uint32_t t)
+{
+    return key_float(t == 0x7FFFFFFFu ? 0x7FFFFFFEu : t);
+}
+
+// Filter-order position key: larger means earlier (key desc, then id asc).
+__device__ __forceinline__ uint64_t order_key(uint32_t key, int32_t id)
+{
+    return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)id);
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v)
+{
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) {
+        const uint64_t o = __shfl_xor(v, d, kWave);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+// Block-wide ranking of n candidates (cand[i] = (key, id) in LDS, distinct
+// ids): the entry at filter-order position r < k goes to sk/sid[r].  Returns
+// min(n, k).
+__device__ __forceinline__ int block_rank_topk(const uint2* cand, int n, int k, uint32_t* sk, int32_t* sid,
+                                               int tid, int nthreads)
+{
+    for (int g = tid; g < n; g += nthreads) {
+        const uint2 c = cand[g];
+        const uint64_t p = order_key(c.x, (int32_t)c.y);
+        int rank = 0;
+        int j = 0;
+        for (; j + 4 <= n; j += 4) {
+            const uint2 a0 = cand[j], a1 = cand[j + 1], a2 = cand[j + 2], a3 = cand[j + 3];
+            rank += (order_key(a0.x, (int32_t)a0.y) > p) + (order_key(a1.x, (int32_t)a1.y) > p) +
+                    (order_key(a2.x, (int32_t)a2.y) > p) + (order_key(a3.x, (int32_t)a3.y) > p);
+        }
+        for (; j < n; ++j) rank += (order_key(cand[j].x, (int32_t)cand[j].y) > p);
+        if (rank < k) {
+            sk[rank] = c.x;
+            sid[rank] = (int32_t)c.y;
+        }
+    }
+    return n < k ? n : k;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Softmax over the sorted top-k set, top-p cut, renormalisation (one wave);
+// writes the row's support.  Same operation order as the filter definition:
+// normaliser summed in filter order, pi = e / S, cumulative pi in filter
+// order, kept probabilities pi / (kept mass) when top-p is on.  Entry
+// q*64 + lane is held by this lane in registers; the sums run in order with
+// readlane.
+__device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* sid, int n, const FilterParams fp,
+                                             const SparseOut out, int64_t r, int lane)
+{
+    constexpr int Q = kMaxK / kWave;
     int32_t* oid = out.ids + r * out.cap;
     double* op = out.probs + r * out.cap;
     int n_out;
@@ -166,29 +244,41 @@ __device__ void finalize_row(const uint32_t* sk, const int32_t* sid, int n, cons
     } else {
         m = (double)key_float(sk[0]);
         const double Td = (double)fp.temperature;
-        for (int i = lane; i < n; i += kWave) scratch[i] = exp(((double)key_float(sk[i]) - m) / Td);
-        wave_sync();
+        double e[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int i = q * kWave + lane;
+            e[q] = (i < n) ? exp(((double)key_float(sk[i]) - m) / Td) : 0.0;
+        }
         S = 0.0;
-        for (int i = 0; i < n; ++i) S += scratch[i];
-        wave_sync();
-        for (int i = lane; i < n; i += kWave) scratch[i] = scratch[i] / S;
-        wave_sync();
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int lim = n - q * kWave;
+            for (int l = 0; l < kWave && l < lim; ++l) S += readlane_f64(e[q], l);
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q) e[q] = e[q] / S;
         int n_keep = n;
         double c = 0.0;
         if (fp.topp_on) {
             const double p = (double)fp.top_p;
             n_keep = 0;
-            for (int i = 0; i < n; ++i) {
-                if (i > 0 && c >= p) break;
-                c += scratch[i];
-                ++n_keep;
+            bool stop = false;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int lim = n - q * kWave;
+                for (int l = 0; l < kWave && l < lim && !stop; ++l) {
+                    if (n_keep > 0 && c >= p) { stop = true; break; }
+                    c += readlane_f64(e[q], l);
+                    ++n_keep;
+                }
             }
         }
         int npos = 0;
-        for (int base = 0; base < n_keep; base += kWave) {
-            const int i = base + lane;
-            double v = 0.0;
-            if (i < n_keep) v = fp.topp_on ? scratch[i] / c : scratch[i];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int i = q * kWave + lane;
+            const double v = fp.topp_on ? e[q] / c : e[q];
             const bool pos = (i < n_keep) && v > 0.0;
             npos += __popcll(__ballot(pos));
             if (pos) { oid[i] = sid[i]; op[i] = v; }
@@ -206,20 +296,12 @@ __device__ void finalize_row(const uint32_t* sk, const int32_t* sid, int n, cons
 }
 
 // ---- top-k stream ------------------------------------------------------------
-// Number of set bits of `c` (< 64) over the wave, and over the lanes below this one.
-__device__ __forceinline__ uint32_t wave_count_prefix(uint32_t c, uint32_t* total)
-{
-    uint32_t tot = 0, excl = 0;
-#pragma unroll
-    for (int b = 0; b < 6; ++b) {
-        const uint64_t m = __ballot((c >> b) & 1u);
-        tot += (uint32_t)__popcll(m) << b;
-        excl += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
-    }
-    *total = tot;
-    return excl;
-}
-
+// Block (r, seg): four waves stream quarters of segment seg of row r, each
+// keeping candidates in its own LDS buffer behind a rising admission
+// threshold; then every wave cuts its buffer to its exact top-k, the four
+// lists are pruned by the best per-wave k-th entry and ranked together.  With
+// one segment the block also finalises the row; otherwise it writes the
+// segment's sorted top-k for topk_merge_kernel.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     RowSource src, int64_t rows, int64_t N, FilterParams fp, SparseOut out, int S,
@@ -228,11 +310,13 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     using V = Vec<BF16>;
     constexpr int EPV = V::EPV, ESZ = V::ESZ;
     constexpr int U = kPerIter / EPV;                  // 16-byte vectors per lane per iteration
-    __shared__ uint32_t s_key[kWaves][kCap];
-    __shared__ int32_t s_id[kWaves][kCap];
-    __shared__ uint32_t s_hist[kWaves][256];
-    __shared__ int s_cnt[kWaves];
-    __shared__ double s_scratch[kMaxK];
+    // a streaming cut must leave room for one whole vector of candidates per lane
+    constexpr int kCutLimit = (kCap - kWave * EPV < kCap / 2) ? kCap - kWave * EPV : kCap / 2;
+    __shared__ Cand s_buf[kWaves * kCap];
+    __shared__ uint32_t s_sk[kMaxK];
+    __shared__ int32_t s_sid[kMaxK];
+    __shared__ uint64_t s_pk[kWaves];
+    __shared__ int s_ns[kWaves];
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -241,39 +325,42 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     const char* row = row_pointer(src, r, N * ESZ);
     if (row == nullptr) {
         if (S == 1 && threadIdx.x == 0) out.count[r] = -1;
+        if (S > 1 && threadIdx.x == 0) part_n[r * S + seg] = -1;
         return;
     }
     const RowGeom g = row_geom<BF16>(row, N);
     const int64_t vb = g.nvec * seg / S, ve = g.nvec * (seg + 1) / S;
     const int64_t wb = vb + (ve - vb) * w / kWaves, we = vb + (ve - vb) * (w + 1) / kWaves;
 
-    uint32_t* bk = s_key[w];
-    int32_t* bi = s_id[w];
-    uint32_t* hist = s_hist[w];
+    Cand* buf = s_buf + w * kCap;
     const int k = fp.k;
     int cnt = 0;
-    // Admission: key(z) > thr_key.  thr is the float of thr_key; for logits
-    // `z > thr` (an ordered compare, false for NaN) is the same test.  It starts
-    // at -inf, passed in as an argument so the compare is never constant-folded.
+    // Admission: key(z) > thr_key.  thr is the float with the same meaning for
+    // logits (an ordered compare, false for NaN); it starts at -inf, passed in
+    // as an argument so the compare is never constant-folded.
     uint32_t thr_key = kKeyNegInf;
     float thr = fp.thr_init;
 
     auto compact = [&]() __attribute__((always_inline)) {
-        uint32_t T;
-        bool full;
-        cnt = wave_topk_exact(bk, bi, cnt, k, hist, lane, &T, &full);
-        if (full) { thr_key = T; thr = key_float(T); }
+        if (cnt < k) return;
+        uint32_t t;
+        cnt = __builtin_amdgcn_readfirstlane(wave_cut<kCapE>(buf, cnt, k, kCutLimit, lane, &t));
+        t = __builtin_amdgcn_readfirstlane(t);
+        if (t > thr_key) { thr_key = t; thr = thr_float(t); }
     };
     auto scalar_part = [&](int64_t beg, int64_t n) __attribute__((always_inline)) {   // n <= 64, ids increase with lane
         if (cnt > kCap - kWave) compact();
+        float v = 0.0f;
         uint32_t key = 0;
-        if (lane < n) key = float_key(load_scalar<BF16>(row, beg + lane));
+        if (lane < n) {
+            v = load_scalar<BF16>(row, beg + lane);
+            key = float_key(v);
+        }
         const bool pass = key_admits(key, thr_key);
         const uint64_t m = __ballot(pass);
         if (pass) {
             const int pos = cnt + __popcll(m & lanes_below(lane));
-            bk[pos] = key;
-            bi[pos] = (int32_t)(beg + lane);
+            buf[pos] = make_uint2(__float_as_uint(v), (uint32_t)(beg + lane));
         }
         cnt += __popcll(m);
     };
@@ -292,53 +379,65 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
             const int64_t vl = vbase + lane;
             const typename V::T xv = (vl < we) ? body[vl] : V::neg_inf();
             if (cnt > kCap - kWave * EPV) compact();
+            const uint32_t id0 = (uint32_t)(g.head + vl * EPV);
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
-                const uint32_t key = float_key(V::get(xv, e));
-                const bool pass = key_admits(key, thr_key);
+                const float z = V::get(xv, e);
+                const bool pass = z > thr;
                 const uint64_t m = __ballot(pass);
                 if (m) {
                     if (pass) {
-                        const int pos = cnt + __popcll(m & lanes_below(lane));
-                        bk[pos] = key;
-                        bi[pos] = (int32_t)(g.head + vl * EPV + e);
+                        const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)cnt));
+                        buf[pos] = make_uint2(__float_as_uint(z), id0 + e);
                     }
                     cnt += __popcll(m);
                 }
             }
         }
     };
-    auto admit_mask = [&](const typename V::T (&x)[U]) __attribute__((always_inline)) {
-        uint32_t mask = 0;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) mask |= (V::get(x[u], e) > thr ? 1u : 0u) << (u * EPV + e);
-        return mask;
-    };
-    // One iteration: U vectors per lane (vector v0 + u*64 + lane), already in x.
+    // One iteration: U vectors per lane (vector v0 + u*64 + lane), already in
+    // x.  Each logit's test is one compare; its result is both the lane's
+    // predicate and, as a wave mask in scalar registers, the source of counts,
+    // skips and write positions.
     auto process = [&](const typename V::T (&x)[U], int64_t v0) __attribute__((always_inline)) {
-        uint32_t mask = admit_mask(x);
-        uint32_t total;
-        uint32_t excl = wave_count_prefix(__popc(mask), &total);
-        if (total == 0) return;
-        if (cnt + (int)total > kCap) {
-            compact();
-            mask = admit_mask(x);
-            excl = wave_count_prefix(__popc(mask), &total);
-            if (cnt + (int)total > kCap) { reload_path(v0); return; }
+        bool pass[kPerIter];
+        uint64_t m[kPerIter];
+        uint64_t any = 0;
+#pragma unroll
+        for (int i = 0; i < kPerIter; ++i) {
+            pass[i] = V::get(x[i / EPV], i % EPV) > thr;
+            m[i] = __ballot(pass[i]);
+            any |= m[i];
         }
-        int pos = cnt + (int)excl;
+        if (any == 0) return;
+        int total = 0;
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int i = 0; i < kPerIter; ++i) total += __popcll(m[i]);
+        if (cnt + total > kCap) {
+            compact();
+            total = 0;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e)
-                if (mask & (1u << (u * EPV + e))) {
-                    bk[pos] = float_key(V::get(x[u], e));
-                    bi[pos] = (int32_t)(g.head + (v0 + u * kWave + lane) * EPV + e);
-                    ++pos;
+            for (int i = 0; i < kPerIter; ++i) {
+                pass[i] = V::get(x[i / EPV], i % EPV) > thr;
+                m[i] = __ballot(pass[i]);
+                total += __popcll(m[i]);
+            }
+            if (cnt + total > kCap) { reload_path(v0); return; }
+        }
+        const uint32_t id0 = (uint32_t)(g.head + (v0 + lane) * EPV);
+#pragma unroll
+        for (int i = 0; i < kPerIter; ++i) {
+            if (m[i]) {
+                if (pass[i]) {
+                    const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[i] >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m[i], (uint32_t)cnt));
+                    buf[pos] = make_uint2(__float_as_uint(V::get(x[i / EPV], i % EPV)),
+                                          id0 + (uint32_t)((i / EPV) * kWave * EPV + (i % EPV)));
                 }
-        cnt += (int)total;
+                cnt += __popcll(m[i]);
+            }
+        }
     };
 
     // whole iterations with the next iteration's loads in flight
@@ -348,6 +447,19 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     if (nfull > 0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) xc[u] = body[wb + u * kWave + lane];
+        if (cnt == 0 && k <= kWave) {
+            // Seed the threshold from the first iteration: the k-th largest lane
+            // maximum has at least k logits at or above it, all admitted below.
+            float mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, V::get(xc[u], e));
+            uint32_t km = float_key(mx);
+            km = (km <= kKeyPosInf && km > kKeyNegInf) ? km : kKeyNegInf;
+            const uint32_t t0 = wave_kth_largest_of_lanes(km, k);
+            if (t0 > kKeyNegInf + 1u) { thr_key = t0 - 1u; thr = thr_float(thr_key); }
+        }
     }
     for (int64_t it = 0; it < nfull; ++it) {
         const int64_t v0 = wb + it * kStep;
@@ -374,75 +486,125 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
 
     if (seg == S - 1 && w == kWaves - 1 && g.tail_beg < N) scalar_part(g.tail_beg, N - g.tail_beg);
 
-    if (cnt > k) compact();
-    if (lane == 0) s_cnt[w] = cnt;
-    __syncthreads();
-    if (w != 0) return;
-
-    int tot = cnt;
-    for (int ow = 1; ow < kWaves; ++ow) {
-        const int c = s_cnt[ow];
-        for (int i = lane; i < c; i += kWave) {
-            bk[tot + i] = s_key[ow][i];
-            bi[tot + i] = s_id[ow][i];
-        }
-        tot += c;
+    // Cut this wave's list to at most min(k + 64, 256) entries that include its
+    // top-k; every kept entry and at least k of them reach key `lo`, so the
+    // block's k-th entry lies at or above (lo, any id) and entries below the
+    // largest such bound of any wave are out.
+    uint64_t bound = 0;
+    if (cnt >= k) {
+        const int lim = (k + kWave < kMaxK) ? k + kWave : kMaxK;
+        uint32_t lo;
+        if (cnt <= kMaxK)
+            cnt = __builtin_amdgcn_readfirstlane(wave_cut<kMaxK / kWave>(buf, cnt, k, lim, lane, &lo));
+        else
+            cnt = __builtin_amdgcn_readfirstlane(wave_cut<kCapE>(buf, cnt, k, lim, lane, &lo));
+        bound = (uint64_t)__builtin_amdgcn_readfirstlane(lo) << 32;
     }
-    wave_sync();
-    cnt = tot;
-    if (cnt > k) compact();
-
+    RegList<kMaxK / kWave> F;
+    reg_load(F, buf, cnt, lane);
+    if (lane == 0) s_pk[w] = bound;
+    __syncthreads();
+    uint64_t pstar = 0;
+#pragma unroll
+    for (int o = 0; o < kWaves; ++o) pstar = s_pk[o] > pstar ? s_pk[o] : pstar;
+    bool keep[kMaxK / kWave];
+    int ns = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxK / kWave; ++q) {
+        keep[q] = (q * kWave + lane < cnt) && order_key(F.kv[q], F.iv[q]) >= pstar;
+        ns += __popcll(__ballot(keep[q]));
+    }
+    if (lane == 0) s_ns[w] = ns;
+    __syncthreads();
+    int off = 0, n_all = 0;
+#pragma unroll
+    for (int o = 0; o < kWaves; ++o) {
+        off += (o < w) ? s_ns[o] : 0;
+        n_all += s_ns[o];
+    }
+    // survivors of every wave as (key, id), contiguous at the front of s_buf
+#pragma unroll
+    for (int q = 0; q < kMaxK / kWave; ++q) {
+        const uint64_t mq = __ballot(keep[q]);
+        if (keep[q]) {
+            const int pos = off + __popcll(mq & lanes_below(lane));
+            s_buf[pos] = make_uint2(F.kv[q], (uint32_t)F.iv[q]);
+        }
+        off += __popcll(mq);
+    }
+    __syncthreads();
+    const int n = block_rank_topk(s_buf, n_all, k, s_sk, s_sid, threadIdx.x, kThreads);
+    __syncthreads();
     if (S == 1) {
-        wave_sort_desc(bk, bi, cnt, s_key[1], s_id[1], lane);
-        finalize_row(s_key[1], s_id[1], cnt, fp, s_scratch, out, r, lane);
+        if (w == 0) finalize_row(s_sk, s_sid, n, fp, out, r, lane);
     } else {
         const int64_t base = (r * S + seg) * (int64_t)k;
-        for (int i = lane; i < cnt; i += kWave) {
-            part_key[base + i] = bk[i];
-            part_id[base + i] = bi[i];
+        for (int i = threadIdx.x; i < n; i += kThreads) {
+            part_key[base + i] = s_sk[i];
+            part_id[base + i] = s_sid[i];
         }
-        if (lane == 0) part_n[r * S + seg] = cnt;
+        if (threadIdx.x == 0) part_n[r * S + seg] = n;
     }
 }
 
-// One wave per row: merge the S segment lists into the row's top-k and finalize.
-__global__ __launch_bounds__(kWave) void topk_merge_kernel(
+// One workgroup per row: the S segment lists (each sorted, at most k entries)
+// are pruned by the best full list's k-th entry, ranked together and finalised.
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     RowSource src, int64_t rows, FilterParams fp, SparseOut out, int S,
     const uint32_t* part_key, const int32_t* part_id, const int32_t* part_n)
 {
-    __shared__ uint32_t s_key[kMergeCap];
-    __shared__ int32_t s_id[kMergeCap];
-    __shared__ uint32_t s_hist[256];
-    __shared__ uint32_t s_skey[kMaxK];
+    __shared__ uint2 s_cand[kMergeCap];
+    __shared__ uint32_t s_sk[kMaxK];
     __shared__ int32_t s_sid[kMaxK];
-    __shared__ double s_scratch[kMaxK];
+    __shared__ uint64_t s_pstar;
+    __shared__ int s_n;
 
     const int lane = lane_id();
     const int64_t r = blockIdx.x;
     if (r >= rows) return;
     if (row_pointer(src, r, 1) == nullptr) {
-        if (lane == 0) out.count[r] = -1;
+        if (threadIdx.x == 0) out.count[r] = -1;
         return;
     }
     const int k = fp.k;
-    int cnt = 0;
-    for (int seg = 0; seg < S; ++seg) {
-        const int c = part_n[r * S + seg];
-        const int64_t base = (r * S + seg) * (int64_t)k;
-        for (int i = lane; i < c; i += kWave) {
-            s_key[cnt + i] = part_key[base + i];
-            s_id[cnt + i] = part_id[base + i];
+    if (threadIdx.x == 0) {
+        uint64_t p = 0;
+        for (int s = 0; s < S; ++s) {
+            const int64_t base = (r * S + s) * (int64_t)k;
+            if (part_n[r * S + s] == k) {
+                const uint64_t q = order_key(part_key[base + k - 1], part_id[base + k - 1]);
+                p = q > p ? q : p;
+            }
         }
-        cnt += c;
+        s_pstar = p;
+        s_n = 0;
     }
-    wave_sync();
-    if (cnt > k) {
-        uint32_t T;
-        bool full;
-        cnt = wave_topk_exact(s_key, s_id, cnt, k, s_hist, lane, &T, &full);
+    __syncthreads();
+    const uint64_t pstar = s_pstar;
+    for (int s = 0; s < S; ++s) {
+        const int64_t base = (r * S + s) * (int64_t)k;
+        const int ns = part_n[r * S + s];
+        for (int i0 = 0; i0 < ns; i0 += kThreads) {
+            const int i = i0 + (int)threadIdx.x;
+            uint32_t kk = 0;
+            int32_t ii = 0;
+            bool keep = false;
+            if (i < ns) {
+                kk = part_key[base + i];
+                ii = part_id[base + i];
+                keep = order_key(kk, ii) >= pstar;
+            }
+            const uint64_t m = __ballot(keep);
+            int pos0 = 0;
+            if (lane == 0 && m) pos0 = atomicAdd(&s_n, __popcll(m));
+            pos0 = __shfl(pos0, 0, kWave);
+            if (keep) s_cand[pos0 + __popcll(m & lanes_below(lane))] = make_uint2(kk, (uint32_t)ii);
+        }
     }
-    wave_sort_desc(s_key, s_id, cnt, s_skey, s_sid, lane);
-    finalize_row(s_skey, s_sid, cnt, fp, s_scratch, out, r, lane);
+    __syncthreads();
+    const int n = block_rank_topk(s_cand, s_n, k, s_sk, s_sid, threadIdx.x, kThreads);
+    __syncthreads();
+    if (threadIdx.x < kWave) finalize_row(s_sk, s_sid, n, fp, out, r, lane);
 }
 
 // ---- dense chunk statistics --------------------------------------------------
@@ -548,9 +710,10 @@ __global__ void dense_row_stats_kernel(int64_t rows, double inv_T, DenseChunks d
 
 int topk_segments(int64_t rows, int64_t vocab, int k)
 {
-    // Aim for >= 1024 workgroups (4 per CU) while keeping segments >= 4096
-    // logits and the merged candidate list within one merge workgroup.
-    int64_t S = (1024 + rows - 1) / rows;
+    // About 4096 workgroups (16 per CU, several rounds) balance the stream
+    // better than one workgroup per row; segments keep >= 4096 logits and the
+    // merged candidate list fits one merge workgroup.
+    int64_t S = (4096 + rows - 1) / rows;
     const int64_t by_len = vocab / 4096;
     if (S > by_len) S = by_len;
     const int64_t by_merge = kMergeCap / (k > 0 ? k : 1);
@@ -577,7 +740,7 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
                                                                  part_id, part_n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
-    topk_merge_kernel<<<dim3((unsigned)rows), kWave, 0, stream>>>(src, rows, fp, out, S, part_key,
+    topk_merge_kernel<<<dim3((unsigned)rows), kThreads, 0, stream>>>(src, rows, fp, out, S, part_key,
                                                                    part_id, part_n);
     return hipGetLastError();
 }

@@ -1,6 +1,6 @@
 // uno_api.cpp -- C ABI of the UNO sampling library: argument checks, workspace
 // layout and kernel launches.  Every check runs on the host before any launch.
-#include "../../include/uno.h"
+#include "uno.h"
 #include "uno_internal.h"
 
 #include <math.h>

@@ -139,8 +139,8 @@ template <bool BF16> struct Vec;
 template <> struct Vec<false> {
     using T = float4;
     static constexpr int EPV = 4, ESZ = 4;
-    __device__ static T neg_inf() { return make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY); }
-    __device__ static float get(const T& v, int e)
+    __device__ __forceinline__ static T neg_inf() { return make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY); }
+    __device__ __forceinline__ static float get(const T& v, int e)
     {
         return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
     }
@@ -148,8 +148,8 @@ template <> struct Vec<false> {
 template <> struct Vec<true> {
     using T = uint4;
     static constexpr int EPV = 8, ESZ = 2;
-    __device__ static T neg_inf() { return make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u); }
-    __device__ static float get(const T& v, int e)
+    __device__ __forceinline__ static T neg_inf() { return make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u); }
+    __device__ __forceinline__ static float get(const T& v, int e)
     {
         const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
         return (e & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -168,7 +168,7 @@ __device__ __forceinline__ float load_scalar(const char* row, int64_t i)
 }
 
 // Row pointer; returns nullptr for rows skipped by tree verification.
-__device__ __forceinline__ const char* row_pointer(const RowSource& s, int64_t r, int64_t row_bytes)
+__device__ __forceinline__ const char* row_pointer(const RowSource s, int64_t r, int64_t row_bytes)
 {
     if (r < s.rows0) {
         if (s.num_nodes) {
