@@ -171,42 +171,57 @@ __device__ __forceinline__ float thr_float(uint32_t t)
     return key_float(t == 0x7FFFFFFFu ? 0x7FFFFFFEu : t);
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) {
+        const uint32_t o = __shfl_xor(v, d, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
 // Filter-order position key: larger means earlier (key desc, then id asc).
 __device__ __forceinline__ uint64_t order_key(uint32_t key, int32_t id)
 {
     return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)id);
 }
 
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v)
+// Block-wide ranking of the candidates held in L lists (list o: lst[o*stride ..
+// o*stride + cnt[o]) in LDS, entries (key, id), distinct ids): the entry at
+// filter-order position r < k goes to sk/sid[r], and, when se is given, its
+// softmax numerator exp((z - m) / T) to se[r] (m: the largest key's logit).
+// Returns min(total, k).
+template <int L>
+__device__ __forceinline__ int block_rank_topk(const uint2* lst, int stride, const int* cnt, int k, uint32_t* sk,
+                                               int32_t* sid, double* se, double m, double Td, int tid,
+                                               int nthreads)
 {
+    int n = 0;
 #pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) {
-        const uint64_t o = __shfl_xor(v, d, kWave);
-        v = o < v ? o : v;
-    }
-    return v;
-}
-
-// Block-wide ranking of n candidates (cand[i] = (key, id) in LDS, distinct
-// ids): the entry at filter-order position r < k goes to sk/sid[r].  Returns
-// min(n, k).
-__device__ __forceinline__ int block_rank_topk(const uint2* cand, int n, int k, uint32_t* sk, int32_t* sid,
-                                               int tid, int nthreads)
-{
+    for (int o = 0; o < L; ++o) n += cnt[o];
     for (int g = tid; g < n; g += nthreads) {
-        const uint2 c = cand[g];
+        int o = 0, i = g;
+        while (i >= cnt[o]) { i -= cnt[o]; ++o; }
+        const uint2 c = lst[o * stride + i];
         const uint64_t p = order_key(c.x, (int32_t)c.y);
         int rank = 0;
-        int j = 0;
-        for (; j + 4 <= n; j += 4) {
-            const uint2 a0 = cand[j], a1 = cand[j + 1], a2 = cand[j + 2], a3 = cand[j + 3];
-            rank += (order_key(a0.x, (int32_t)a0.y) > p) + (order_key(a1.x, (int32_t)a1.y) > p) +
-                    (order_key(a2.x, (int32_t)a2.y) > p) + (order_key(a3.x, (int32_t)a3.y) > p);
+#pragma unroll
+        for (int o2 = 0; o2 < L; ++o2) {
+            const uint2* a = lst + o2 * stride;
+            const int m = cnt[o2];
+            int j = 0;
+            for (; j + 4 <= m; j += 4) {
+                const uint2 a0 = a[j], a1 = a[j + 1], a2 = a[j + 2], a3 = a[j + 3];
+                rank += (order_key(a0.x, (int32_t)a0.y) > p) + (order_key(a1.x, (int32_t)a1.y) > p) +
+                        (order_key(a2.x, (int32_t)a2.y) > p) + (order_key(a3.x, (int32_t)a3.y) > p);
+            }
+            for (; j < m; ++j) rank += (order_key(a[j].x, (int32_t)a[j].y) > p);
         }
-        for (; j < n; ++j) rank += (order_key(cand[j].x, (int32_t)cand[j].y) > p);
         if (rank < k) {
             sk[rank] = c.x;
             sid[rank] = (int32_t)c.y;
+            if (se) se[rank] = exp(((double)key_float(c.x) - m) / Td);
         }
     }
     return n < k ? n : k;
@@ -223,11 +238,11 @@ __device__ __forceinline__ double readlane_f64(double v, int l)
 // Softmax over the sorted top-k set, top-p cut, renormalisation (one wave);
 // writes the row's support.  Same operation order as the filter definition:
 // normaliser summed in filter order, pi = e / S, cumulative pi in filter
-// order, kept probabilities pi / (kept mass) when top-p is on.  Entry
-// q*64 + lane is held by this lane in registers; the sums run in order with
-// readlane.
-__device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* sid, int n, const FilterParams fp,
-                                             const SparseOut out, int64_t r, int lane)
+// order, kept probabilities pi / (kept mass) when top-p is on.  se holds the
+// numerators e in filter order.  Entry q*64 + lane is held by this lane in
+// registers; the sums run in order with readlane.
+__device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* sid, const double* se, int n,
+                                             const FilterParams fp, const SparseOut out, int64_t r, int lane)
 {
     constexpr int Q = kMaxK / kWave;
     int32_t* oid = out.ids + r * out.cap;
@@ -243,21 +258,23 @@ __device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* 
         if (lane == 0) { oid[0] = sid[0]; op[0] = 1.0; }
     } else {
         m = (double)key_float(sk[0]);
-        const double Td = (double)fp.temperature;
         double e[Q];
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int i = q * kWave + lane;
-            e[q] = (i < n) ? exp(((double)key_float(sk[i]) - m) / Td) : 0.0;
+            e[q] = 0.0;
+            if (q * kWave < n && i < n) e[q] = se[i];
         }
         S = 0.0;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int lim = n - q * kWave;
-            for (int l = 0; l < kWave && l < lim; ++l) S += readlane_f64(e[q], l);
+            if (lim > 0)
+                for (int l = 0; l < kWave && l < lim; ++l) S += readlane_f64(e[q], l);
         }
 #pragma unroll
-        for (int q = 0; q < Q; ++q) e[q] = e[q] / S;
+        for (int q = 0; q < Q; ++q)
+            if (q * kWave < n) e[q] = e[q] / S;
         int n_keep = n;
         double c = 0.0;
         if (fp.topp_on) {
@@ -267,6 +284,7 @@ __device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* 
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
                 const int lim = n - q * kWave;
+                if (lim <= 0 || stop) break;
                 for (int l = 0; l < kWave && l < lim && !stop; ++l) {
                     if (n_keep > 0 && c >= p) { stop = true; break; }
                     c += readlane_f64(e[q], l);
@@ -277,6 +295,7 @@ __device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* 
         int npos = 0;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
+            if (q * kWave >= n_keep) break;
             const int i = q * kWave + lane;
             const double v = fp.topp_on ? e[q] / c : e[q];
             const bool pos = (i < n_keep) && v > 0.0;
@@ -315,7 +334,9 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     __shared__ Cand s_buf[kWaves * kCap];
     __shared__ uint32_t s_sk[kMaxK];
     __shared__ int32_t s_sid[kMaxK];
-    __shared__ uint64_t s_pk[kWaves];
+    __shared__ double s_e[kMaxK];
+    __shared__ uint32_t s_b[kWaves];
+    __shared__ uint32_t s_mx[kWaves];
     __shared__ int s_ns[kWaves];
 
     const int lane = lane_id();
@@ -486,57 +507,64 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
 
     if (seg == S - 1 && w == kWaves - 1 && g.tail_beg < N) scalar_part(g.tail_beg, N - g.tail_beg);
 
-    // Cut this wave's list to at most min(k + 64, 256) entries that include its
-    // top-k; every kept entry and at least k of them reach key `lo`, so the
-    // block's k-th entry lies at or above (lo, any id) and entries below the
-    // largest such bound of any wave are out.
-    uint64_t bound = 0;
-    if (cnt >= k) {
-        const int lim = (k + kWave < kMaxK) ? k + kWave : kMaxK;
-        uint32_t lo;
-        if (cnt <= kMaxK)
-            cnt = __builtin_amdgcn_readfirstlane(wave_cut<kMaxK / kWave>(buf, cnt, k, lim, lane, &lo));
-        else
-            cnt = __builtin_amdgcn_readfirstlane(wave_cut<kCapE>(buf, cnt, k, lim, lane, &lo));
-        bound = (uint64_t)__builtin_amdgcn_readfirstlane(lo) << 32;
-    }
-    RegList<kMaxK / kWave> F;
-    reg_load(F, buf, cnt, lane);
-    if (lane == 0) s_pk[w] = bound;
-    __syncthreads();
-    uint64_t pstar = 0;
-#pragma unroll
-    for (int o = 0; o < kWaves; ++o) pstar = s_pk[o] > pstar ? s_pk[o] : pstar;
-    bool keep[kMaxK / kWave];
-    int ns = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxK / kWave; ++q) {
-        keep[q] = (q * kWave + lane < cnt) && order_key(F.kv[q], F.iv[q]) >= pstar;
-        ns += __popcll(__ballot(keep[q]));
-    }
-    if (lane == 0) s_ns[w] = ns;
-    __syncthreads();
-    int off = 0, n_all = 0;
-#pragma unroll
-    for (int o = 0; o < kWaves; ++o) {
-        off += (o < w) ? s_ns[o] : 0;
-        n_all += s_ns[o];
-    }
-    // survivors of every wave as (key, id), contiguous at the front of s_buf
-#pragma unroll
-    for (int q = 0; q < kMaxK / kWave; ++q) {
-        const uint64_t mq = __ballot(keep[q]);
-        if (keep[q]) {
-            const int pos = off + __popcll(mq & lanes_below(lane));
-            s_buf[pos] = make_uint2(F.kv[q], (uint32_t)F.iv[q]);
+    // Bound: with quota q = ceil(k/4), each wave's q-th largest key (truncated
+    // to its 16-bit bin) has q entries at or above it, so the smallest of the
+    // four has at least k; the block's k-th entry lies at or above it.  Without
+    // q entries in every wave there is no bound (B = 0).
+    const int quota = (k + kWaves - 1) / kWaves;
+    uint32_t b = 0;
+    if (cnt >= quota) {
+        if (cnt <= kMaxK) {
+            RegList<kMaxK / kWave> L;
+            reg_load(L, buf, cnt, lane);
+            b = reg_kth_key(L, quota, 16);
+        } else {
+            RegList<kCapE> L;
+            reg_load(L, buf, cnt, lane);
+            b = reg_kth_key(L, quota, 16);
         }
-        off += __popcll(mq);
     }
+    if (lane == 0) s_b[w] = b;
     __syncthreads();
-    const int n = block_rank_topk(s_buf, n_all, k, s_sk, s_sid, threadIdx.x, kThreads);
+    uint32_t B = s_b[0];
+#pragma unroll
+    for (int o = 1; o < kWaves; ++o) B = s_b[o] < B ? s_b[o] : B;
+    // this wave's entries with key >= B, compacted in place as (key, id)
+    int ns = 0;
+    uint32_t mx = 0;
+    for (int j = 0; j < cnt; j += kWave) {
+        const int i = j + lane;
+        uint2 c = make_uint2(0u, 0u);
+        bool keep = false;
+        if (i < cnt) {
+            c = buf[i];
+            c.x = float_key(__uint_as_float(c.x));
+            keep = c.x >= B;
+            mx = c.x > mx ? c.x : mx;
+        }
+        const uint64_t mk = __ballot(keep);
+        if (keep)
+            buf[(int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, (uint32_t)ns))] = c;
+        ns += __popcll(mk);
+    }
+    mx = wave_max_u32(mx);
+    if (lane == 0) { s_ns[w] = ns; s_mx[w] = mx; }
+    __syncthreads();
+    // softmax numerators are formed during the rank when this block finalises
+    uint32_t top = s_mx[0];
+#pragma unroll
+    for (int o = 1; o < kWaves; ++o) top = s_mx[o] > top ? s_mx[o] : top;
+    const bool want_e = (S == 1) && !fp.greedy;
+    // The rank and the one-wave finalisation start at a different wave in each
+    // block, so co-resident blocks spread these short serial phases over the
+    // four SIMDs instead of stacking them on one.
+    const int rot = (int)(blockIdx.x & (kWaves - 1));
+    const int trot = (int)((threadIdx.x + rot * kWave) & (kThreads - 1));
+    const int n = block_rank_topk<kWaves>(s_buf, kCap, s_ns, k, s_sk, s_sid, want_e ? s_e : nullptr,
+                                          (double)key_float(top), (double)fp.temperature, trot, kThreads);
     __syncthreads();
     if (S == 1) {
-        if (w == 0) finalize_row(s_sk, s_sid, n, fp, out, r, lane);
+        if (w == rot) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane);
     } else {
         const int64_t base = (r * S + seg) * (int64_t)k;
         for (int i = threadIdx.x; i < n; i += kThreads) {
@@ -556,7 +584,9 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     __shared__ uint2 s_cand[kMergeCap];
     __shared__ uint32_t s_sk[kMaxK];
     __shared__ int32_t s_sid[kMaxK];
+    __shared__ double s_e[kMaxK];
     __shared__ uint64_t s_pstar;
+    __shared__ uint32_t s_top;
     __shared__ int s_n;
 
     const int lane = lane_id();
@@ -569,14 +599,18 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     const int k = fp.k;
     if (threadIdx.x == 0) {
         uint64_t p = 0;
+        uint32_t top = 0;
         for (int s = 0; s < S; ++s) {
             const int64_t base = (r * S + s) * (int64_t)k;
-            if (part_n[r * S + s] == k) {
+            const int ns = part_n[r * S + s];
+            if (ns > 0) top = part_key[base] > top ? part_key[base] : top;   // lists are sorted
+            if (ns == k) {
                 const uint64_t q = order_key(part_key[base + k - 1], part_id[base + k - 1]);
                 p = q > p ? q : p;
             }
         }
         s_pstar = p;
+        s_top = top;
         s_n = 0;
     }
     __syncthreads();
@@ -602,9 +636,10 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
         }
     }
     __syncthreads();
-    const int n = block_rank_topk(s_cand, s_n, k, s_sk, s_sid, threadIdx.x, kThreads);
+    const int n = block_rank_topk<1>(s_cand, 0, &s_n, k, s_sk, s_sid, fp.greedy ? nullptr : s_e,
+                                     (double)key_float(s_top), (double)fp.temperature, threadIdx.x, kThreads);
     __syncthreads();
-    if (threadIdx.x < kWave) finalize_row(s_sk, s_sid, n, fp, out, r, lane);
+    if (threadIdx.x < kWave) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane);
 }
 
 // ---- dense chunk statistics --------------------------------------------------
