@@ -227,14 +227,6 @@ __device__ __forceinline__ int block_rank_topk(const uint2* lst, int stride, con
     return n < k ? n : k;
 }
 
-__device__ __forceinline__ double readlane_f64(double v, int l)
-{
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
 // Softmax over the sorted top-k set, top-p cut, renormalisation (one wave);
 // writes the row's support.  Same operation order as the filter definition:
 // normaliser summed in filter order, pi = e / S, cumulative pi in filter
@@ -391,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     const typename V::T* body = reinterpret_cast<const typename V::T*>(row + g.head * ESZ);
     // Fallback for an iteration whose candidates cannot all fit the buffer even
     // after a cut (only while the threshold is still low): vector by vector,
-    // re-reading each vector (a cache hit), with a cut whenever the buffer fills.
+    // re-reading each vector, with a cut whenever the buffer fills.
     auto reload_path = [&](int64_t v0) __attribute__((always_inline)) {
 #pragma unroll 1
         for (int u = 0; u < U; ++u) {
@@ -467,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     typename V::T xc[U], xn[U];
     if (nfull > 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) xc[u] = body[wb + u * kWave + lane];
+        for (int u = 0; u < U; ++u) xc[u] = V::load_stream(body + wb + u * kWave + lane);
         if (cnt == 0 && k <= kWave) {
             // Seed the threshold from the first iteration: the k-th largest lane
             // maximum has at least k logits at or above it, all admitted below.
@@ -488,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
         // the number of loads in flight is the same on every path
         const int64_t vn = (it + 1 < nfull) ? v0 + kStep : v0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) xn[u] = body[vn + u * kWave + lane];
+        for (int u = 0; u < U; ++u) xn[u] = V::load_stream(body + vn + u * kWave + lane);
         process(xc, v0);
 #pragma unroll
         for (int u = 0; u < U; ++u) xc[u] = xn[u];
@@ -499,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t v = v0 + u * kWave + lane;
-                xc[u] = (v < we) ? body[v] : V::neg_inf();
+                xc[u] = (v < we) ? V::load_stream(body + v) : V::neg_inf();
             }
             process(xc, v0);
         }
@@ -672,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
         const typename V::T* p = reinterpret_cast<const typename V::T*>(row + beg * ESZ);
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            const typename V::T v = p[j * kWave + lane];
+            const typename V::T v = V::load_stream(p + j * kWave + lane);
 #pragma unroll
             for (int e = 0; e < EPV; ++e) x[j * EPV + e] = V::get(v, e);
         }
@@ -745,10 +737,12 @@ __global__ void dense_row_stats_kernel(int64_t rows, double inv_T, DenseChunks d
 
 int topk_segments(int64_t rows, int64_t vocab, int k)
 {
-    // About 4096 workgroups (16 per CU, several rounds) balance the stream
-    // better than one workgroup per row; segments keep >= 4096 logits and the
-    // merged candidate list fits one merge workgroup.
-    int64_t S = (4096 + rows - 1) / rows;
+    // Enough workgroups for one full round over the chip (about 1024: four per
+    // CU, all resident at once) and no more: every segment pays a serial
+    // epilogue, which only overlaps other work when the round is not full.
+    // Segments keep >= 4096 logits and the merged candidate list fits one merge
+    // workgroup.
+    int64_t S = (1024 + rows - 1) / rows;
     const int64_t by_len = vocab / 4096;
     if (S > by_len) S = by_len;
     const int64_t by_merge = kMergeCap / (k > 0 ? k : 1);

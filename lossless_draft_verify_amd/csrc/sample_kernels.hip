@@ -8,10 +8,11 @@
 // constraints fix both acceptance thresholds at 1.0.
 //
 // Sampling from a distribution is an inverse CDF in ascending token-id order.
-// Sparse supports (<= 256 ids) are sorted by id in LDS and scanned
-// sequentially in double precision, which reproduces the reference arithmetic
-// exactly.  Dense rows are located chunk by chunk from per-chunk statistics and
-// finished inside one 2048-logit chunk.
+// A sparse support (<= 256 ids) is held by one wave in registers, put in id
+// order through LDS, and its cumulative sum is taken in that order in double
+// precision (the same additions, in the same order, as a sequential scan over
+// the dense vector, whose zeros add nothing).  Dense rows are located chunk by
+// chunk from per-chunk statistics and finished inside one 2048-logit chunk.
 #include "uno_device.h"
 #include "uno_internal.h"
 
@@ -27,37 +28,104 @@ constexpr int kMaxNodes = 129;          // V + 1 with V <= 128
 constexpr int kFrontierCap = 192;       // >= V + 2, three slots per lane
 
 // ---- sparse helpers ------------------------------------------------------------
-// Copy a support (filter order) into LDS sorted by token id.
-__device__ void stage_sorted_by_id(const int32_t* ids_in, const double* p_in, int n, int32_t* raw,
-                                   int32_t* out_id, double* out_p, int lane)
+constexpr int kQ = kMaxK / kWave;      // support entries per lane
+
+// A support held by one wave: entry q*64 + lane in id[q] / w[q].
+struct WaveRow {
+    int32_t id[kQ];
+    double w[kQ];
+};
+
+// Load n <= 256 entries (unordered); slots past n hold id INT32_MAX, weight 0.
+__device__ __forceinline__ void wave_load_support(const int32_t* ids, const double* p, int n, WaveRow& R, int lane)
 {
-    for (int i = lane; i < n; i += kWave) raw[i] = ids_in[i];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        const int i = q * kWave + lane;
+        R.id[q] = 0x7FFFFFFF;
+        R.w[q] = 0.0;
+        if (q * kWave < n && i < n) { R.id[q] = ids[i]; R.w[q] = p[i]; }
+    }
+}
+
+// Reorder the n entries of R by ascending id (ids distinct), through the
+// wave's LDS scratch (s_key, s_id: kMaxK ints; s_w: kMaxK doubles).
+__device__ __forceinline__ void wave_sort_by_id(WaveRow& R, int n, int32_t* s_key, int32_t* s_id, double* s_w,
+                                                int lane)
+{
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        const int i = q * kWave + lane;
+        if (q * kWave < n && i < n) s_key[i] = R.id[q];
+    }
     wave_sync();
-    for (int i = lane; i < n; i += kWave) {
-        const int32_t me = raw[i];
-        int r = 0;
-        for (int j = 0; j < n; ++j) r += (raw[j] < me) ? 1 : 0;
-        out_id[r] = me;
-        out_p[r] = p_in[i];
+    int rank[kQ] = {};
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {
+        const int32_t a0 = s_key[j], a1 = s_key[j + 1], a2 = s_key[j + 2], a3 = s_key[j + 3];
+#pragma unroll
+        for (int q = 0; q < kQ; ++q)
+            rank[q] += (a0 < R.id[q]) + (a1 < R.id[q]) + (a2 < R.id[q]) + (a3 < R.id[q]);
+    }
+    for (; j < n; ++j) {
+        const int32_t a = s_key[j];
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) rank[q] += (a < R.id[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        const int i = q * kWave + lane;
+        if (q * kWave < n && i < n) { s_id[rank[q]] = R.id[q]; s_w[rank[q]] = R.w[q]; }
+    }
+    wave_sync();
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        const int i = q * kWave + lane;
+        if (q * kWave < n && i < n) { R.id[q] = s_id[i]; R.w[q] = s_w[i]; }
     }
     wave_sync();
 }
 
-// Inverse CDF over an id-sorted list (all lanes run it identically).
-__device__ int32_t sample_sorted(const int32_t* ids, const double* w, int n, double u, double* wpick)
+// Inverse CDF over the n id-ordered entries of R with uniform u: the first
+// entry whose inclusive cumulative weight exceeds u * W (W the total); when
+// rounding leaves none, the last entry with positive weight.  Returns its id
+// (-1 when W is not positive) and its weight in *wpick.
+__device__ __forceinline__ int32_t wave_sample_sorted(const WaveRow& R, int n, double u, double* wpick, int lane)
 {
-    double W = 0.0;
-    for (int i = 0; i < n; ++i) W += w[i];
-    *wpick = 0.0;
-    if (!(W > 0.0)) return -1;
-    const double t = u * W;
     double c = 0.0;
-    for (int i = 0; i < n; ++i) {
-        c += w[i];
-        if (c > t) { *wpick = w[i]; return ids[i]; }
+    double cv[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        cv[q] = 0.0;
+        const int lim = n - q * kWave;
+        if (lim > 0)
+            for (int l = 0; l < kWave && l < lim; ++l) {
+                c += readlane_f64(R.w[q], l);
+                cv[q] = (lane == l) ? c : cv[q];
+            }
     }
-    for (int i = n - 1; i >= 0; --i)
-        if (w[i] > 0.0) { *wpick = w[i]; return ids[i]; }
+    *wpick = 0.0;
+    if (!(c > 0.0)) return -1;
+    const double t = u * c;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        if (q * kWave >= n) break;
+        const uint64_t m = __ballot(q * kWave + lane < n && cv[q] > t);
+        if (m) {
+            const int src = wave_first_lane(m);
+            *wpick = __shfl(R.w[q], src, kWave);
+            return __shfl(R.id[q], src, kWave);
+        }
+    }
+#pragma unroll
+    for (int q = kQ - 1; q >= 0; --q) {
+        const uint64_t m = __ballot(q * kWave + lane < n && R.w[q] > 0.0);
+        if (m) {
+            const int src = 63 - __clzll((long long)m);
+            *wpick = __shfl(R.w[q], src, kWave);
+            return __shfl(R.id[q], src, kWave);
+        }
+    }
     return -1;
 }
 
@@ -77,17 +145,26 @@ __device__ double lookup_prob(const int32_t* ids, const double* p, int n, int32_
     return 0.0;
 }
 
+// Per-wave LDS scratch for sorting one support.
+struct SortScratch {
+    int32_t key[kMaxK];
+    int32_t id[kMaxK];
+    double w[kMaxK];
+};
+
 // ---- linear, sparse supports -----------------------------------------------------
-constexpr int kLinThreads = 256;
-constexpr int kLinWaves = kLinThreads / kWave;
+// One workgroup per request, one wave per block position: propose y_j ~ q_j and
+// test it against p_j; then one wave takes the first rejection j* and draws the
+// last token from the residual max(0, p_j* - q_j*) (or p_j* when it has no
+// mass), or from the bonus row p_B when every proposal was accepted.
+constexpr int kLinWaves = 8;
+constexpr int kLinThreads = kLinWaves * kWave;
 
 __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     int32_t batch, int32_t B, SparseOut sup, uint64_t seed, uint64_t offset,
     const uint32_t* req_ids, LinearOut o)
 {
-    __shared__ int32_t s_raw[kLinWaves][kMaxK];
-    __shared__ int32_t s_sid[kLinWaves][kMaxK];
-    __shared__ double s_sp[kLinWaves][kMaxK];
+    __shared__ SortScratch s_sort[kLinWaves];
     __shared__ int32_t s_y[kMaxLinearB];
     __shared__ int32_t s_acc[kMaxLinearB];
     __shared__ uint32_t s_flags;
@@ -110,8 +187,10 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
         int32_t y = -1;
         double qy = 0.0;
         if (nq > 0) {
-            stage_sorted_by_id(sup.ids + qr * cap, sup.probs + qr * cap, nq, s_raw[w], s_sid[w], s_sp[w], lane);
-            y = sample_sorted(s_sid[w], s_sp[w], nq, d.u[0], &qy);
+            WaveRow R;
+            wave_load_support(sup.ids + qr * cap, sup.probs + qr * cap, nq, R, lane);
+            wave_sort_by_id(R, nq, s_sort[w].key, s_sort[w].id, s_sort[w].w, lane);
+            y = wave_sample_sorted(R, nq, d.u[0], &qy, lane);
         } else {
             flags |= 1u;
         }
@@ -128,7 +207,6 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
             s_acc[j] = acc;
             if (o.proposals) o.proposals[(int64_t)b * B + j] = y;
         }
-        wave_sync();
     }
     if (flags && lane == 0) atomicOr(&s_flags, flags);
     __syncthreads();
@@ -144,46 +222,40 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     int32_t fin = -1;
     double dummy;
     uint32_t fl = 0;
-    if (jstar < B) {
-        const int64_t pr = pbase + jstar, qr = qbase + jstar;
-        const int np = sup.count[pr], nq = sup.count[qr];
-        if (np > 0) {
-            stage_sorted_by_id(sup.ids + pr * cap, sup.probs + pr * cap, np, s_raw[0], s_sid[0], s_sp[0], lane);
-            // draft support, unordered, for lookups
-            const int nqq = nq > 0 ? nq : 0;
-            for (int i = lane; i < nqq; i += kWave) {
-                s_raw[2][i] = sup.ids[qr * cap + i];
-                s_sp[2][i] = sup.probs[qr * cap + i];
-            }
+    const int64_t pr = (jstar < B) ? pbase + jstar : pbase + B;
+    const int np = sup.count[pr];
+    if (np > 0) {
+        WaveRow P;
+        wave_load_support(sup.ids + pr * cap, sup.probs + pr * cap, np, P, lane);
+        wave_sort_by_id(P, np, s_sort[0].key, s_sort[0].id, s_sort[0].w, lane);
+        if (jstar < B) {
+            // residual max(0, p - q) over p's support (ids outside it have zero
+            // residual); q's weights found by id through LDS
+            const int64_t qr = qbase + jstar;
+            const int nq = sup.count[qr] > 0 ? sup.count[qr] : 0;
+            int32_t* qid = s_sort[1].id;
+            double* qw = s_sort[1].w;
+            for (int i = lane; i < nq; i += kWave) { qid[i] = sup.ids[qr * cap + i]; qw[i] = sup.probs[qr * cap + i]; }
             wave_sync();
-            // residual max(0, p - q) over p's support in id order; ids outside p's
-            // support have zero residual
-            for (int i = lane; i < np; i += kWave) {
-                const int32_t id = s_sid[0][i];
+            WaveRow Rz = P;
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+                if (q * kWave >= np) break;
                 double qv = 0.0;
-                for (int j = 0; j < nqq; ++j)
-                    if (s_raw[2][j] == id) { qv = s_sp[2][j]; break; }
-                const double dlt = s_sp[0][i] - qv;
-                s_sp[1][i] = dlt > 0.0 ? dlt : 0.0;
+                for (int i = 0; i < nq; ++i) qv = (qid[i] == P.id[q]) ? qw[i] : qv;
+                const double dlt = P.w[q] - qv;
+                Rz.w[q] = dlt > 0.0 ? dlt : 0.0;
             }
-            wave_sync();
-            fin = sample_sorted(s_sid[0], s_sp[1], np, d.u[2], &dummy);
+            fin = wave_sample_sorted(Rz, np, d.u[2], &dummy, lane);
             if (fin < 0) {
                 fl |= 2u;
-                fin = sample_sorted(s_sid[0], s_sp[0], np, d.u[2], &dummy);
+                fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane);
             }
         } else {
-            fl |= 1u;
+            fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane);
         }
     } else {
-        const int64_t pr = pbase + B;
-        const int np = sup.count[pr];
-        if (np > 0) {
-            stage_sorted_by_id(sup.ids + pr * cap, sup.probs + pr * cap, np, s_raw[0], s_sid[0], s_sp[0], lane);
-            fin = sample_sorted(s_sid[0], s_sp[0], np, d.u[2], &dummy);
-        } else {
-            fl |= 1u;
-        }
+        fl |= 1u;
     }
     int32_t* tok = o.tokens + (int64_t)b * (B + 1);
     for (int j = lane; j <= B; j += kWave) tok[j] = (j < jstar) ? s_y[j] : (j == jstar ? fin : -1);
@@ -303,7 +375,7 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_
 }
 
 // ---- tree walk (one workgroup per request) ---------------------------------------
-constexpr int kWalkThreads = 256;
+constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / kWave;
 
 __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
@@ -311,9 +383,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     const uint32_t* req_ids, const int32_t* node_token, const int32_t* node_parent,
     const int32_t* num_nodes, WalkOut o)
 {
-    __shared__ int32_t s_raw[kWalkWaves][kMaxK];
-    __shared__ int32_t s_sid[kWalkWaves][kMaxK];
-    __shared__ double s_sp[kWalkWaves][kMaxK];
+    __shared__ SortScratch s_sort[kWalkWaves];
     __shared__ int32_t s_dep[kMaxNodes], s_t[kMaxNodes], s_tok[kMaxNodes], s_par[kMaxNodes];
 
     const int lane = lane_id();
@@ -342,9 +412,11 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
         const int cnt = sup.count[row];
         if (dep >= 0 && dep <= B && cnt > 0) {
             const Draw d = uno_draw(seed, req, (uint32_t)dep, offset);
-            stage_sorted_by_id(sup.ids + row * cap, sup.probs + row * cap, cnt, s_raw[w], s_sid[w], s_sp[w], lane);
+            WaveRow R;
+            wave_load_support(sup.ids + row * cap, sup.probs + row * cap, cnt, R, lane);
+            wave_sort_by_id(R, cnt, s_sort[w].key, s_sort[w].id, s_sort[w].w, lane);
             double dummy;
-            t = sample_sorted(s_sid[w], s_sp[w], cnt, d.u[2], &dummy);
+            t = wave_sample_sorted(R, cnt, d.u[2], &dummy, lane);
         }
         if (lane == 0) s_t[n] = t;
         wave_sync();
@@ -392,7 +464,7 @@ __device__ __forceinline__ void load_chunk(const char* row, int64_t N, int64_t c
         const typename V::T* p = reinterpret_cast<const typename V::T*>(row + beg * ESZ);
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            const typename V::T v = p[j * kWave + lane];
+            const typename V::T v = V::load_stream(p + j * kWave + lane);
 #pragma unroll
             for (int e = 0; e < EPV; ++e) x[j * EPV + e] = V::get(v, e);
         }

@@ -134,11 +134,29 @@ __device__ __forceinline__ float wave_max_f32(float v)
 
 __device__ __forceinline__ int wave_first_lane(uint64_t mask) { return __ffsll((long long)mask) - 1; }
 
+// Lane l's value of a double (l uniform).
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // ---- logit rows --------------------------------------------------------------
 template <bool BF16> struct Vec;
+// load_stream: a 16-byte load marked non-temporal (the logits are read once;
+// keeping them out of the caches' normal replacement lets the stream run
+// closer to the HBM rate).
 template <> struct Vec<false> {
     using T = float4;
     static constexpr int EPV = 4, ESZ = 4;
+    __device__ __forceinline__ static T load_stream(const T* p)
+    {
+        typedef float v4 __attribute__((ext_vector_type(4)));
+        const v4 r = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+        return make_float4(r.x, r.y, r.z, r.w);
+    }
     __device__ __forceinline__ static T neg_inf() { return make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY); }
     __device__ __forceinline__ static float get(const T& v, int e)
     {
@@ -148,6 +166,12 @@ template <> struct Vec<false> {
 template <> struct Vec<true> {
     using T = uint4;
     static constexpr int EPV = 8, ESZ = 2;
+    __device__ __forceinline__ static T load_stream(const T* p)
+    {
+        typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+        const v4 r = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+        return make_uint4(r.x, r.y, r.z, r.w);
+    }
     __device__ __forceinline__ static T neg_inf() { return make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u); }
     __device__ __forceinline__ static float get(const T& v, int e)
     {
