@@ -568,7 +568,8 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
 }
 
 // One workgroup per row: the S segment lists (each sorted, at most k entries)
-// are pruned by the best full list's k-th entry, ranked together and finalised.
+// are pruned by the best full list's k-th entry, ranked together and
+// finalised.  Every global read is spread over the workgroup.
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     RowSource src, int64_t rows, FilterParams fp, SparseOut out, int S,
     const uint32_t* part_key, const int32_t* part_id, const int32_t* part_n)
@@ -577,11 +578,13 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     __shared__ uint32_t s_sk[kMaxK];
     __shared__ int32_t s_sid[kMaxK];
     __shared__ double s_e[kMaxK];
-    __shared__ uint64_t s_pstar;
-    __shared__ uint32_t s_top;
+    __shared__ int s_segn[kMaxSegments];
+    __shared__ uint64_t s_wp[kWaves];
+    __shared__ uint32_t s_wt[kWaves];
     __shared__ int s_n;
 
     const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r = blockIdx.x;
     if (r >= rows) return;
     if (row_pointer(src, r, 1) == nullptr) {
@@ -589,47 +592,59 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
         return;
     }
     const int k = fp.k;
-    if (threadIdx.x == 0) {
-        uint64_t p = 0;
-        uint32_t top = 0;
-        for (int s = 0; s < S; ++s) {
-            const int64_t base = (r * S + s) * (int64_t)k;
-            const int ns = part_n[r * S + s];
-            if (ns > 0) top = part_key[base] > top ? part_key[base] : top;   // lists are sorted
-            if (ns == k) {
-                const uint64_t q = order_key(part_key[base + k - 1], part_id[base + k - 1]);
-                p = q > p ? q : p;
-            }
+    // per segment: its count, the bound from its k-th entry, its first key
+    uint64_t p = 0;
+    uint32_t top = 0;
+    for (int sg = threadIdx.x; sg < S; sg += kThreads) {
+        const int64_t base = (r * S + sg) * (int64_t)k;
+        const int ns = part_n[r * S + sg];
+        s_segn[sg] = ns;
+        if (ns > 0) top = part_key[base] > top ? part_key[base] : top;    // lists are sorted
+        if (ns == k) {
+            const uint64_t q = order_key(part_key[base + k - 1], part_id[base + k - 1]);
+            p = q > p ? q : p;
         }
-        s_pstar = p;
-        s_top = top;
-        s_n = 0;
     }
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) {
+        const uint64_t po = __shfl_xor(p, d, kWave);
+        const uint32_t to = __shfl_xor(top, d, kWave);
+        p = po > p ? po : p;
+        top = to > top ? to : top;
+    }
+    if (lane == 0) { s_wp[w] = p; s_wt[w] = top; }
+    if (threadIdx.x == 0) s_n = 0;
     __syncthreads();
-    const uint64_t pstar = s_pstar;
-    for (int s = 0; s < S; ++s) {
-        const int64_t base = (r * S + s) * (int64_t)k;
-        const int ns = part_n[r * S + s];
-        for (int i0 = 0; i0 < ns; i0 += kThreads) {
-            const int i = i0 + (int)threadIdx.x;
-            uint32_t kk = 0;
-            int32_t ii = 0;
-            bool keep = false;
-            if (i < ns) {
-                kk = part_key[base + i];
-                ii = part_id[base + i];
-                keep = order_key(kk, ii) >= pstar;
-            }
-            const uint64_t m = __ballot(keep);
-            int pos0 = 0;
-            if (lane == 0 && m) pos0 = atomicAdd(&s_n, __popcll(m));
-            pos0 = __shfl(pos0, 0, kWave);
-            if (keep) s_cand[pos0 + __popcll(m & lanes_below(lane))] = make_uint2(kk, (uint32_t)ii);
+    uint64_t pstar = 0;
+    top = 0;
+#pragma unroll
+    for (int o = 0; o < kWaves; ++o) {
+        pstar = s_wp[o] > pstar ? s_wp[o] : pstar;
+        top = s_wt[o] > top ? s_wt[o] : top;
+    }
+    // candidates at or above the bound, gathered from all segments at once
+    const int total = S * k;
+    for (int g0 = 0; g0 < total; g0 += kThreads) {
+        const int g = g0 + (int)threadIdx.x;
+        const int sg = g / k, i = g - sg * k;
+        uint32_t kk = 0;
+        int32_t ii = 0;
+        bool keep = false;
+        if (g < total && i < s_segn[sg]) {
+            const int64_t base = (r * S + sg) * (int64_t)k;
+            kk = part_key[base + i];
+            ii = part_id[base + i];
+            keep = order_key(kk, ii) >= pstar;
         }
+        const uint64_t m = __ballot(keep);
+        int pos0 = 0;
+        if (lane == 0 && m) pos0 = atomicAdd(&s_n, __popcll(m));
+        pos0 = __shfl(pos0, 0, kWave);
+        if (keep) s_cand[pos0 + __popcll(m & lanes_below(lane))] = make_uint2(kk, (uint32_t)ii);
     }
     __syncthreads();
     const int n = block_rank_topk<1>(s_cand, 0, &s_n, k, s_sk, s_sid, fp.greedy ? nullptr : s_e,
-                                     (double)key_float(s_top), (double)fp.temperature, threadIdx.x, kThreads);
+                                     (double)key_float(top), (double)fp.temperature, threadIdx.x, kThreads);
     __syncthreads();
     if (threadIdx.x < kWave) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane);
 }
@@ -643,32 +658,74 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
     constexpr int EPV = V::EPV, ESZ = V::ESZ;
     constexpr int PER_LANE = kDenseChunk / kWave;          // 32 logits per lane
     constexpr int NV = PER_LANE / EPV;                      // vectors per lane
-    __shared__ double s_exp2[kWaves][64];
+    __shared__ double s_exp2[kExp2Entries];
+    load_exp2_table(s_exp2);
+    __syncthreads();
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    fill_exp2_table(s_exp2[w], lane);
     const int64_t r = blockIdx.x;
-    const int64_t c = (int64_t)blockIdx.y * kWaves + w;
-    if (c >= dc.nchunks) return;
+    const int nc = dc.nchunks;
     const char* row = row_pointer(src, r, N * ESZ);
-    const int64_t slot = r * dc.nchunks + c;
     if (row == nullptr) {
-        if (lane == 0) { dc.cmax[slot] = -INFINITY; dc.csum[slot] = 0.0; dc.ccount[slot] = 0; }
+        for (int c = w; c < nc; c += kWaves)
+            if (lane == 0) {
+                const int64_t slot = r * nc + c;
+                dc.cmax[slot] = -INFINITY; dc.csum[slot] = 0.0; dc.ccount[slot] = 0;
+            }
         return;
     }
-    const int64_t beg = c * kDenseChunk;
-    const int64_t n = (N - beg < kDenseChunk) ? (N - beg) : kDenseChunk;
-    float x[PER_LANE];
-    const bool vec_ok = (n == kDenseChunk) && ((((uintptr_t)(row + beg * ESZ)) & 15u) == 0);
-    if (vec_ok) {
-        const typename V::T* p = reinterpret_cast<const typename V::T*>(row + beg * ESZ);
+    const DenseExp ex{ log2e_over_T, s_exp2 };
+    // whole chunks of a 16-byte aligned row are loaded as vectors (other waves
+    // of the CU cover the load latency: the pass is bound by its fp64 work)
+    const bool aligned = (((uintptr_t)row) & 15u) == 0;
+    const int nvec_chunks = aligned ? (int)(N / kDenseChunk) : 0;
+    auto load_vec = [&](int c, typename V::T (&v)[NV]) __attribute__((always_inline)) {
+        const typename V::T* p = reinterpret_cast<const typename V::T*>(row + (int64_t)c * kDenseChunk * ESZ);
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const typename V::T v = V::load_stream(p + j * kWave + lane);
+        for (int j = 0; j < NV; ++j) v[j] = V::load_stream(p + j * kWave + lane);
+    };
+    // statistics of one chunk held as x[PER_LANE] (element (j*64 + lane)*EPV + e at x[j*EPV + e])
+    auto chunk_stats = [&](int c, const float (&x)[PER_LANE]) __attribute__((always_inline)) {
+        float mx = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) x[j * EPV + e] = V::get(v, e);
+        for (int i = 0; i < PER_LANE; ++i) mx = fmaxf(mx, x[i]);
+        mx = wave_max_f32(mx);
+        double s = 0.0;
+        uint32_t cntf = 0;
+        if (mx > -INFINITY && mx < INFINITY) {
+            const double md = (double)mx;
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                // NaN and -inf reach the exp's lower clamp, whose term (2^-1000)
+                // vanishes next to the chunk maximum's 1
+                cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
+                s += ex((double)x[i] - md);
+            }
         }
-    } else {
+        s = wave_sum_f64(s);
+        if (lane == 0) {
+            const int64_t slot = r * nc + c;
+            dc.cmax[slot] = mx;
+            dc.csum[slot] = (mx < INFINITY) ? s : NAN;
+            dc.ccount[slot] = (int32_t)cntf;
+        }
+    };
+    int c = w;
+    for (; c < nvec_chunks; c += kWaves) {
+        typename V::T cur[NV];
+        load_vec(c, cur);
+        float x[PER_LANE];
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) x[j * EPV + e] = V::get(cur[j], e);
+        chunk_stats(c, x);
+    }
+    // remaining chunks (ragged tail, or a row off 16-byte alignment) element by element
+    for (; c < nc; c += kWaves) {
+        const int64_t beg = (int64_t)c * kDenseChunk;
+        const int64_t n = (N - beg < kDenseChunk) ? (N - beg) : kDenseChunk;
+        float x[PER_LANE];
 #pragma unroll
         for (int j = 0; j < NV; ++j)
 #pragma unroll
@@ -676,29 +733,7 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
                 const int64_t i = (int64_t)(j * kWave + lane) * EPV + e;
                 x[j * EPV + e] = (i < n) ? load_scalar<BF16>(row, beg + i) : -INFINITY;
             }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) mx = fmaxf(mx, x[i]);
-    mx = wave_max_f32(mx);
-    double s = 0.0;
-    uint32_t cntf = 0;
-    if (mx > -INFINITY && mx < INFINITY) {
-        const DenseExp ex{ log2e_over_T, s_exp2[w] };
-        const double md = (double)mx;
-#pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) {
-            const bool fin = finite_f32(x[i]);
-            cntf += fin ? 1u : 0u;
-            s += fin ? ex((double)x[i] - md) : 0.0;
-        }
-    }
-    s = wave_sum_f64(s);
-    cntf = wave_sum_u32(cntf);
-    if (lane == 0) {
-        dc.cmax[slot] = mx;
-        dc.csum[slot] = (mx < INFINITY) ? s : NAN;
-        dc.ccount[slot] = (int32_t)cntf;
+        chunk_stats(c, x);
     }
 }
 
@@ -740,14 +775,14 @@ int topk_segments(int64_t rows, int64_t vocab, int k)
     // Enough workgroups for one full round over the chip (about 1024: four per
     // CU, all resident at once) and no more: every segment pays a serial
     // epilogue, which only overlaps other work when the round is not full.
-    // Segments keep >= 4096 logits and the merged candidate list fits one merge
-    // workgroup.
+    // Segments keep >= 16384 logits (each wave streams several iterations) and
+    // the merged candidate list fits one merge workgroup.
     int64_t S = (1024 + rows - 1) / rows;
-    const int64_t by_len = vocab / 4096;
+    const int64_t by_len = vocab / 16384;
     if (S > by_len) S = by_len;
     const int64_t by_merge = kMergeCap / (k > 0 ? k : 1);
     if (S > by_merge) S = by_merge;
-    if (S > 64) S = 64;
+    if (S > kMaxSegments) S = kMaxSegments;
     if (S < 1) S = 1;
     return (int)S;
 }
@@ -779,7 +814,7 @@ hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab
 {
     if (rows == 0) return hipSuccess;
     const double c = 1.4426950408889634074 / (double)temperature;
-    dim3 grid((unsigned)rows, (unsigned)((dc.nchunks + kWaves - 1) / kWaves));
+    dim3 grid((unsigned)rows);
     if (bf16)
         dense_chunk_kernel<true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, dc);
     else

@@ -153,20 +153,36 @@ struct SortScratch {
 };
 
 // ---- linear, sparse supports -----------------------------------------------------
-// One workgroup per request, one wave per block position: propose y_j ~ q_j and
-// test it against p_j; then one wave takes the first rejection j* and draws the
-// last token from the residual max(0, p_j* - q_j*) (or p_j* when it has no
-// mass), or from the bonus row p_B when every proposal was accepted.
-constexpr int kLinWaves = 8;
+// One workgroup per request.  Each wave takes block positions j (and the
+// bonus position B): it proposes y_j ~ q_j, tests it against p_j and, when the
+// proposal is rejected, already draws the last token that a first rejection
+// at j would emit -- from the residual max(0, p_j - q_j), or from p_j when the
+// residual has no mass; at position B it draws the bonus token from p_B.  The
+// first rejection j* then only selects among these draws.
+constexpr int kLinWaves = 16;
 constexpr int kLinThreads = kLinWaves * kWave;
+
+// Weight of token `id` in an id-sorted list in LDS (0 when absent).
+__device__ __forceinline__ double sorted_lookup(const int32_t* ids, const double* w, int n, int32_t id)
+{
+    int lo = 0, hi = n;                 // first index with ids[index] >= id
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (ids[mid] < id) lo = mid + 1; else hi = mid;
+    }
+    return (lo < n && ids[lo] == id) ? w[lo] : 0.0;
+}
 
 __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     int32_t batch, int32_t B, SparseOut sup, uint64_t seed, uint64_t offset,
     const uint32_t* req_ids, LinearOut o)
 {
-    __shared__ SortScratch s_sort[kLinWaves];
+    __shared__ SortScratch s_q[kLinWaves];
+    __shared__ SortScratch s_p[kLinWaves];
     __shared__ int32_t s_y[kMaxLinearB];
     __shared__ int32_t s_acc[kMaxLinearB];
+    __shared__ int32_t s_fin[kMaxLinearB + 1];
+    __shared__ uint32_t s_ffl[kMaxLinearB + 1];
     __shared__ uint32_t s_flags;
 
     const int lane = lane_id();
@@ -180,31 +196,73 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     __syncthreads();
 
     uint32_t flags = 0;
-    for (int j = w; j < B; j += kLinWaves) {
+    for (int j = w; j <= B; j += kLinWaves) {
         const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
-        const int64_t qr = qbase + j, pr = pbase + j;
+        const int64_t pr = pbase + j;
+        const int np = sup.count[pr];
+        WaveRow P;                       // p_j, loaded up front
+        if (np > 0) wave_load_support(sup.ids + pr * cap, sup.probs + pr * cap, np, P, lane);
+        int32_t fin = -1;
+        uint32_t ffl = 0;
+        if (j == B) {                    // bonus draw
+            double dummy;
+            if (np > 0) {
+                wave_sort_by_id(P, np, s_p[w].key, s_p[w].id, s_p[w].w, lane);
+                fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane);
+            } else {
+                ffl = 1u;
+            }
+            if (lane == 0) { s_fin[j] = fin; s_ffl[j] = ffl; }
+            continue;
+        }
+        const int64_t qr = qbase + j;
         const int nq = sup.count[qr];
         int32_t y = -1;
         double qy = 0.0;
         if (nq > 0) {
-            WaveRow R;
-            wave_load_support(sup.ids + qr * cap, sup.probs + qr * cap, nq, R, lane);
-            wave_sort_by_id(R, nq, s_sort[w].key, s_sort[w].id, s_sort[w].w, lane);
-            y = wave_sample_sorted(R, nq, d.u[0], &qy, lane);
+            WaveRow Q;
+            wave_load_support(sup.ids + qr * cap, sup.probs + qr * cap, nq, Q, lane);
+            wave_sort_by_id(Q, nq, s_q[w].key, s_q[w].id, s_q[w].w, lane);   // q stays id-sorted in s_q
+            y = wave_sample_sorted(Q, nq, d.u[0], &qy, lane);
         } else {
             flags |= 1u;
         }
         int acc = 0;
         if (y >= 0) {
-            const int np = sup.count[pr];
             double py = 0.0;
             if (np > 0) py = lookup_prob(sup.ids + pr * cap, sup.probs + pr * cap, np, y, lane);
             else flags |= 1u;
             acc = (d.u[1] * qy < py) ? 1 : 0;
         }
+        if (!acc) {
+            // the last token if j is the first rejection: residual max(0, p - q)
+            // over p's support (ids outside it have zero residual)
+            double dummy;
+            if (np > 0) {
+                wave_sort_by_id(P, np, s_p[w].key, s_p[w].id, s_p[w].w, lane);
+                const int nqq = nq > 0 ? nq : 0;
+                WaveRow Rz = P;
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) {
+                    if (q * kWave >= np) break;
+                    const double qv = (q * kWave + lane < np) ? sorted_lookup(s_q[w].id, s_q[w].w, nqq, P.id[q]) : 0.0;
+                    const double dlt = P.w[q] - qv;
+                    Rz.w[q] = dlt > 0.0 ? dlt : 0.0;
+                }
+                fin = wave_sample_sorted(Rz, np, d.u[2], &dummy, lane);
+                if (fin < 0) {
+                    ffl = 2u;
+                    fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane);
+                }
+            } else {
+                ffl = 1u;
+            }
+        }
         if (lane == 0) {
             s_y[j] = y;
             s_acc[j] = acc;
+            s_fin[j] = fin;
+            s_ffl[j] = ffl;
             if (o.proposals) o.proposals[(int64_t)b * B + j] = y;
         }
     }
@@ -218,50 +276,12 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
         const uint64_t m = __ballot(j < B && s_acc[j] == 0);
         if (m) { jstar = base + wave_first_lane(m); break; }
     }
-    const Draw d = uno_draw(seed, req, (uint32_t)jstar, offset);
-    int32_t fin = -1;
-    double dummy;
-    uint32_t fl = 0;
-    const int64_t pr = (jstar < B) ? pbase + jstar : pbase + B;
-    const int np = sup.count[pr];
-    if (np > 0) {
-        WaveRow P;
-        wave_load_support(sup.ids + pr * cap, sup.probs + pr * cap, np, P, lane);
-        wave_sort_by_id(P, np, s_sort[0].key, s_sort[0].id, s_sort[0].w, lane);
-        if (jstar < B) {
-            // residual max(0, p - q) over p's support (ids outside it have zero
-            // residual); q's weights found by id through LDS
-            const int64_t qr = qbase + jstar;
-            const int nq = sup.count[qr] > 0 ? sup.count[qr] : 0;
-            int32_t* qid = s_sort[1].id;
-            double* qw = s_sort[1].w;
-            for (int i = lane; i < nq; i += kWave) { qid[i] = sup.ids[qr * cap + i]; qw[i] = sup.probs[qr * cap + i]; }
-            wave_sync();
-            WaveRow Rz = P;
-#pragma unroll
-            for (int q = 0; q < kQ; ++q) {
-                if (q * kWave >= np) break;
-                double qv = 0.0;
-                for (int i = 0; i < nq; ++i) qv = (qid[i] == P.id[q]) ? qw[i] : qv;
-                const double dlt = P.w[q] - qv;
-                Rz.w[q] = dlt > 0.0 ? dlt : 0.0;
-            }
-            fin = wave_sample_sorted(Rz, np, d.u[2], &dummy, lane);
-            if (fin < 0) {
-                fl |= 2u;
-                fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane);
-            }
-        } else {
-            fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane);
-        }
-    } else {
-        fl |= 1u;
-    }
+    const int32_t fin = s_fin[jstar];
     int32_t* tok = o.tokens + (int64_t)b * (B + 1);
     for (int j = lane; j <= B; j += kWave) tok[j] = (j < jstar) ? s_y[j] : (j == jstar ? fin : -1);
     if (lane == 0) {
         o.accept_len[b] = jstar + 1;
-        if (o.flags) o.flags[b] = s_flags | fl;
+        if (o.flags) o.flags[b] = s_flags | s_ffl[jstar];
     }
 }
 
@@ -654,14 +674,15 @@ __global__ __launch_bounds__(kDenseThreads) void dense_propose_kernel(
     uint64_t seed, uint64_t offset, const uint32_t* req_ids, float* row_m, double* row_S,
     int32_t* jstar_out, int32_t* y_out, uint32_t* flag_out, LinearOut o)
 {
-    __shared__ double s_exp2[kDenseWaves][64];
+    __shared__ double s_exp2[kExp2Entries];
     __shared__ int32_t s_acc[kMaxLinearB];
     __shared__ uint32_t s_flags;
+    load_exp2_table(s_exp2);
+    __syncthreads();
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int b = blockIdx.x;
-    fill_exp2_table(s_exp2[w], lane);
-    const DenseExp ex{ log2e_over_T, s_exp2[w] };
+    const DenseExp ex{ log2e_over_T, s_exp2 };
     const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
     const int nc = dc.nchunks;
     const int64_t row_bytes = N * Vec<BF16>::ESZ;
@@ -725,15 +746,16 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, int32_t nc,
     const float* row_m, const double* row_S, const int32_t* jstar_in, double* resid)
 {
-    __shared__ double s_exp2[kDenseWaves][64];
+    __shared__ double s_exp2[kExp2Entries];
+    load_exp2_table(s_exp2);
+    __syncthreads();
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int b = blockIdx.x;
     const int c = blockIdx.y * kDenseWaves + w;
     const int js = jstar_in[b];
     if (js >= B || c >= nc) return;
-    fill_exp2_table(s_exp2[w], lane);
-    const DenseExp ex{ log2e_over_T, s_exp2[w] };
+    const DenseExp ex{ log2e_over_T, s_exp2 };
     const int64_t qr = linear_row(batch, B, b, js), pr = linear_row(batch, B, b, B + js);
     const double Sp = row_S[pr], Sq = row_S[qr];
     double total = 0.0;
@@ -764,10 +786,11 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
     const int32_t* jstar_in, const int32_t* y_in, const uint32_t* flag_in, const double* resid,
     LinearOut o)
 {
-    __shared__ double s_exp2[64];
+    __shared__ double s_exp2[kExp2Entries];
+    load_exp2_table(s_exp2);
+    __syncthreads();
     const int lane = lane_id();
     const int b = blockIdx.x;
-    fill_exp2_table(s_exp2, lane);
     const DenseExp ex{ log2e_over_T, s_exp2 };
     const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
     const int nc = dc.nchunks;

@@ -226,28 +226,41 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
 }
 
 // ---- double-precision exp for the dense path ---------------------------------
-// exp(d / T) for d <= 0: y = d * log2(e) / T = n/64 + f with |f| <= 1/128;
-// 2^(n/64) from a 64-entry table of 2^(j/64) (one copy per wave in LDS) and 2^f
-// from the Taylor series of exp(f ln 2) to degree 5 (truncation < 4e-17).
-__device__ __forceinline__ void fill_exp2_table(double* tab, int lane)
+// Table-driven exponential (P. T. P. Tang, "Table-driven implementation of the
+// exponential function in IEEE floating-point arithmetic", ACM TOMS 15(2),
+// 1989).  exp(d / T) = 2^y with y = d * log2(e) / T <= 0.  y = k/2048 + r with
+// k the integer nearest 2048*y, read from the low bits of fma(d, c, 1.5*2^41)
+// (whose ulp is 2^-11), and r = fma(d, c, -k/2048) rounded once, |r| <= 2^-12;
+// then 2^y = 2^(k>>11) * 2^((k&2047)/2048) * 2^r, the middle factor from a
+// 2048-entry table of nearest doubles and 2^r from the Taylor series of
+// exp(r ln 2) to degree 3 (truncation below 4e-17).  d is clamped so that
+// y >= -1000 (NaN and -inf land on the clamp as well).
+constexpr int kExp2Entries = 2048;
+static __constant__ double kExp2Table[kExp2Entries] = {
+#include "exp2_table.inc"
+};
+
+// Copy the table into LDS (tab: kExp2Entries doubles); the caller synchronises.
+__device__ __forceinline__ void load_exp2_table(double* tab)
 {
-    tab[lane] = exp2((double)lane * (1.0 / 64.0));
-    wave_sync();
+    for (int i = (int)threadIdx.x; i < kExp2Entries; i += (int)blockDim.x) tab[i] = kExp2Table[i];
 }
 
 struct DenseExp {
     double c;              // log2(e) / T
-    const double* tab;     // 64 entries, 2^(j/64)
+    const double* tab;     // LDS copy of kExp2Table
     __device__ __forceinline__ double operator()(double d) const
     {
-        double y = d * c;
-        y = fmax(y, -1100.0);
-        const double kf = rint(y * 64.0);
-        const double f = fma(kf, -1.0 / 64.0, y);
-        const int ki = (int)kf;
-        const double t = f * 0.69314718055994530942;
-        const double p = fma(fma(fma(fma(fma(t, 1.0 / 120.0, 1.0 / 24.0), t, 1.0 / 6.0), t, 0.5), t, 1.0), t, 1.0);
-        return ldexp(tab[ki & 63] * p, ki >> 6);
+        constexpr double kC1 = 0.69314718055994530942;     // ln 2
+        constexpr double kC2 = 0.24022650695910071233;     // (ln 2)^2 / 2
+        constexpr double kC3 = 0.055504108664821579953;    // (ln 2)^3 / 6
+        constexpr double kMagic = 0x1.8p41;
+        d = fmax(d, -1000.0 / c);
+        const double t = fma(d, c, kMagic);
+        const double r = fma(d, c, -(t - kMagic));
+        const int32_t k = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(t);
+        const double p = fma(fma(fma(r, kC3, kC2), r, kC1), r, 1.0);
+        return ldexp(tab[k & (kExp2Entries - 1)] * p, k >> 11);
     }
 };
 

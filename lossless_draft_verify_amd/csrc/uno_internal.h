@@ -48,6 +48,7 @@ struct DenseChunks {
 
 constexpr int kDenseChunk = 2048;          // elements per dense chunk
 constexpr int kMergeCap = 4096;            // candidates one merge workgroup holds
+constexpr int kMaxSegments = 64;           // segments per row of the top-k stream
 
 inline int32_t dense_nchunks(int64_t vocab) { return (int32_t)((vocab + kDenseChunk - 1) / kDenseChunk); }
 
