@@ -40,12 +40,15 @@ def parse():
     ap.add_argument("--pool", type=int, default=3, help="distinct input cycles rotated through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic-probe", type=int, default=0, metavar="N",
+                    help="only run N launches of the timed filter kernel and N plain device copies "
+                         "of the same byte count (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
     return ap.parse_args()
 
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("filter_kernels.hip", "uno_device.h", "uno_internal.h"):
+    for f in ("filter_kernels.hip", "uno_device.h", "uno_internal.h", "exp2_table.inc"):
         with open(os.path.join(ROOT, "lossless_draft_verify_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -62,6 +65,35 @@ def traffic_entry():
     if t.get("source_hash") != source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def traffic_probe(args, w, lib, pool, dt, sp, stream, dev):
+    """The dominant kernel alone (the same uno_filter launch the bench times) and a
+    plain device-to-device copy of the same number of bytes, N times each; the
+    copy calibrates the HBM byte counters."""
+    import ctypes
+    import torch
+    import lossless_draft_verify_amd as uno
+    a = pool[0]["all"]
+    nrows = a.shape[0]
+    ids = torch.empty((nrows, w.top_k), dtype=torch.int32, device=dev)
+    probs = torch.empty((nrows, w.top_k), dtype=torch.float64, device=dev)
+    cnt = torch.empty(nrows, dtype=torch.int32, device=dev)
+    fws_n = uno.workspace_bytes(uno.OP_FILTER, nrows, 0, 0, 0, w.vocab, dt, w.temperature, w.top_k, w.top_p)
+    fws = torch.empty(fws_n + 256, dtype=torch.uint8, device=dev)
+    fws_p = ctypes.c_void_p((fws.data_ptr() + 255) // 256 * 256) if fws_n else None
+    src = pool[1 % len(pool)]["all"]
+    dst = torch.empty_like(src)
+    for i in range(args.traffic_probe):
+        st = lib.uno_filter(ctypes.c_void_p(pool[i % len(pool)]["all"].data_ptr()), dt, nrows, w.vocab,
+                            ctypes.byref(sp), w.top_k, ctypes.c_void_p(ids.data_ptr()),
+                            ctypes.c_void_p(probs.data_ptr()), ctypes.c_void_p(cnt.data_ptr()), None, fws_p,
+                            fws_n, ctypes.c_void_p(stream.cuda_stream))
+        assert st == 0, st
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] traffic probe: {args.traffic_probe} x uno_filter ({nrows} rows) + {args.traffic_probe} x copy "
+        f"of {src.numel() * src.element_size()} bytes")
 
 
 def main():
@@ -167,6 +199,10 @@ def main():
             if st != 0:
                 raise uno.UnoError(st, "uno_verify_tree")
             return acc
+
+    if args.traffic_probe:
+        traffic_probe(args, w, lib, pool, dt, sp, stream, dev)
+        return
 
     # warm-up steps also give the tokens-per-forward figure (outside the timed region)
     acc_total = 0
