@@ -231,12 +231,13 @@ __device__ __forceinline__ int block_rank_topk(const uint2* lst, int stride, con
 // writes the row's support.  Same operation order as the filter definition:
 // normaliser summed in filter order, pi = e / S, cumulative pi in filter
 // order, kept probabilities pi / (kept mass) when top-p is on.  se holds the
-// numerators e in filter order.  Entry q*64 + lane is held by this lane in
-// registers; the sums run in order with readlane.
-__device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* sid, const double* se, int n,
-                                             const FilterParams fp, const SparseOut out, int64_t r, int lane)
+// numerators e in filter order (LDS, overwritten with pi); s_cx receives the
+// cumulative sums (n + 1 entries).  The two in-order sums run in one lane over
+// LDS -- one add per step -- and everything else across the wave.
+__device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* sid, double* se, int n,
+                                             const FilterParams fp, const SparseOut out, int64_t r, int lane,
+                                             double* s_scal, double* s_cx)
 {
-    constexpr int Q = kMaxK / kWave;
     int32_t* oid = out.ids + r * out.cap;
     double* op = out.probs + r * out.cap;
     int n_out;
@@ -250,46 +251,44 @@ __device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* 
         if (lane == 0) { oid[0] = sid[0]; op[0] = 1.0; }
     } else {
         m = (double)key_float(sk[0]);
-        double e[Q];
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int i = q * kWave + lane;
-            e[q] = 0.0;
-            if (q * kWave < n && i < n) e[q] = se[i];
+        if (lane == 0) {
+            double acc = 0.0;
+#pragma unroll 8
+            for (int i = 0; i < n; ++i) acc += se[i];
+            s_scal[0] = acc;
         }
-        S = 0.0;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int lim = n - q * kWave;
-            if (lim > 0)
-                for (int l = 0; l < kWave && l < lim; ++l) S += readlane_f64(e[q], l);
-        }
-#pragma unroll
-        for (int q = 0; q < Q; ++q)
-            if (q * kWave < n) e[q] = e[q] / S;
+        wave_sync();
+        S = s_scal[0];
+        for (int i = lane; i < n; i += kWave) se[i] = se[i] / S;
+        wave_sync();
         int n_keep = n;
-        double c = 0.0;
+        double c = 1.0;
         if (fp.topp_on) {
+            // exclusive cumulative pi in filter order (one lane), then the kept
+            // prefix: i == 0 or cumulative < top_p (non-decreasing, so a prefix)
+            if (lane == 0) {
+                double acc = 0.0;
+#pragma unroll 8
+                for (int i = 0; i < n; ++i) {
+                    s_cx[i] = acc;
+                    acc += se[i];
+                }
+                s_cx[n] = acc;
+            }
+            wave_sync();
             const double p = (double)fp.top_p;
             n_keep = 0;
-            bool stop = false;
-#pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                const int lim = n - q * kWave;
-                if (lim <= 0 || stop) break;
-                for (int l = 0; l < kWave && l < lim && !stop; ++l) {
-                    if (n_keep > 0 && c >= p) { stop = true; break; }
-                    c += readlane_f64(e[q], l);
-                    ++n_keep;
-                }
+            for (int base = 0; base < n; base += kWave) {
+                const int i = base + lane;
+                n_keep += __popcll(__ballot(i < n && (i == 0 || s_cx[i] < p)));
             }
+            c = s_cx[n_keep];
         }
         int npos = 0;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            if (q * kWave >= n_keep) break;
-            const int i = q * kWave + lane;
-            const double v = fp.topp_on ? e[q] / c : e[q];
+        for (int base = 0; base < n_keep; base += kWave) {
+            const int i = base + lane;
+            double v = 0.0;
+            if (i < n_keep) v = fp.topp_on ? se[i] / c : se[i];
             const bool pos = (i < n_keep) && v > 0.0;
             npos += __popcll(__ballot(pos));
             if (pos) { oid[i] = sid[i]; op[i] = v; }
@@ -327,6 +326,8 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     __shared__ uint32_t s_sk[kMaxK];
     __shared__ int32_t s_sid[kMaxK];
     __shared__ double s_e[kMaxK];
+    __shared__ double s_cx[kMaxK + 1];
+    __shared__ double s_scal[1];
     __shared__ uint32_t s_b[kWaves];
     __shared__ uint32_t s_mx[kWaves];
     __shared__ int s_ns[kWaves];
@@ -499,21 +500,23 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
 
     if (seg == S - 1 && w == kWaves - 1 && g.tail_beg < N) scalar_part(g.tail_beg, N - g.tail_beg);
 
-    // Bound: with quota q = ceil(k/4), each wave's q-th largest key (truncated
-    // to its 16-bit bin) has q entries at or above it, so the smallest of the
-    // four has at least k; the block's k-th entry lies at or above it.  Without
-    // q entries in every wave there is no bound (B = 0).
+    // Bound: with quota q = ceil(k/4), the q-th largest of this wave's lane
+    // maxima (truncated to its 16-bit key bin) has q entries at or above it, so
+    // the smallest of the four waves' bounds has at least k: the block's k-th
+    // entry lies at or above it.  Without q entries in every wave there is no
+    // bound (B = 0).
     const int quota = (k + kWaves - 1) / kWaves;
+    uint32_t lmax = 0;
+    for (int j = lane; j < cnt; j += kWave) {
+        const uint32_t kj = float_key(__uint_as_float(buf[j].x));
+        lmax = kj > lmax ? kj : lmax;
+    }
     uint32_t b = 0;
     if (cnt >= quota) {
-        if (cnt <= kMaxK) {
-            RegList<kMaxK / kWave> L;
-            reg_load(L, buf, cnt, lane);
-            b = reg_kth_key(L, quota, 16);
-        } else {
-            RegList<kCapE> L;
-            reg_load(L, buf, cnt, lane);
-            b = reg_kth_key(L, quota, 16);
+        // largest 16-bit prefix t with at least quota lane maxima >= t
+        for (int bit = 31; bit >= 16; --bit) {
+            const uint32_t cand = b | (1u << bit);
+            if (__popcll(__ballot(lmax >= cand)) >= quota) b = cand;
         }
     }
     if (lane == 0) s_b[w] = b;
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
                                           (double)key_float(top), (double)fp.temperature, trot, kThreads);
     __syncthreads();
     if (S == 1) {
-        if (w == rot) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane);
+        if (w == rot) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane, s_scal, s_cx);
     } else {
         const int64_t base = (r * S + seg) * (int64_t)k;
         for (int i = threadIdx.x; i < n; i += kThreads) {
@@ -578,8 +581,11 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     __shared__ uint32_t s_sk[kMaxK];
     __shared__ int32_t s_sid[kMaxK];
     __shared__ double s_e[kMaxK];
+    __shared__ double s_cx[kMaxK + 1];
+    __shared__ double s_scal[1];
     __shared__ int s_segn[kMaxSegments];
     __shared__ uint64_t s_wp[kWaves];
+    __shared__ uint64_t s_wq[kWaves];
     __shared__ uint32_t s_wt[kWaves];
     __shared__ int s_n;
 
@@ -592,8 +598,11 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
         return;
     }
     const int k = fp.k;
-    // per segment: its count, the bound from its k-th entry, its first key
-    uint64_t p = 0;
+    // Per segment: its count, its first key, and two lower bounds on the row's
+    // k-th entry -- the k-th entry of a full list, and (quota q = ceil(k/S)) the
+    // smallest of the lists' q-th entries, valid when every list holds q.
+    const int quota = (k + S - 1) / S;
+    uint64_t p = 0, pq = ~0ull;
     uint32_t top = 0;
     for (int sg = threadIdx.x; sg < S; sg += kThreads) {
         const int64_t base = (r * S + sg) * (int64_t)k;
@@ -604,24 +613,30 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
             const uint64_t q = order_key(part_key[base + k - 1], part_id[base + k - 1]);
             p = q > p ? q : p;
         }
+        const uint64_t qq = (ns >= quota) ? order_key(part_key[base + quota - 1], part_id[base + quota - 1]) : 0ull;
+        pq = qq < pq ? qq : pq;
     }
 #pragma unroll
     for (int d = kWave / 2; d >= 1; d >>= 1) {
         const uint64_t po = __shfl_xor(p, d, kWave);
+        const uint64_t qo = __shfl_xor(pq, d, kWave);
         const uint32_t to = __shfl_xor(top, d, kWave);
         p = po > p ? po : p;
+        pq = qo < pq ? qo : pq;
         top = to > top ? to : top;
     }
-    if (lane == 0) { s_wp[w] = p; s_wt[w] = top; }
+    if (lane == 0) { s_wp[w] = p; s_wq[w] = pq; s_wt[w] = top; }
     if (threadIdx.x == 0) s_n = 0;
     __syncthreads();
-    uint64_t pstar = 0;
+    uint64_t pstar = 0, pquota = ~0ull;
     top = 0;
 #pragma unroll
     for (int o = 0; o < kWaves; ++o) {
         pstar = s_wp[o] > pstar ? s_wp[o] : pstar;
+        pquota = s_wq[o] < pquota ? s_wq[o] : pquota;
         top = s_wt[o] > top ? s_wt[o] : top;
     }
+    pstar = pquota > pstar ? pquota : pstar;
     // candidates at or above the bound, gathered from all segments at once
     const int total = S * k;
     for (int g0 = 0; g0 < total; g0 += kThreads) {
@@ -646,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     const int n = block_rank_topk<1>(s_cand, 0, &s_n, k, s_sk, s_sid, fp.greedy ? nullptr : s_e,
                                      (double)key_float(top), (double)fp.temperature, threadIdx.x, kThreads);
     __syncthreads();
-    if (threadIdx.x < kWave) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane);
+    if (threadIdx.x < kWave) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane, s_scal, s_cx);
 }
 
 // ---- dense chunk statistics --------------------------------------------------

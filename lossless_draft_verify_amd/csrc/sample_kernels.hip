@@ -25,7 +25,7 @@ namespace {
 constexpr int kMaxK = 256;
 constexpr int kMaxLinearB = 128;
 constexpr int kMaxNodes = 129;          // V + 1 with V <= 128
-constexpr int kFrontierCap = 192;       // >= V + 2, three slots per lane
+constexpr int kMaxTreeVK = 2048;        // V * K limit the C ABI enforces
 
 // ---- sparse helpers ------------------------------------------------------------
 constexpr int kQ = kMaxK / kWave;      // support entries per lane
@@ -286,28 +286,35 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
 }
 
 // ---- tree build (one wave per request) ------------------------------------------
-struct FrontierEntry {
-    double score;
-    int32_t depth, parent, rank;
+// Best-first expansion with lazily pushed siblings: a popped node pushes its
+// next sibling and its first child.  Siblings come in non-increasing score
+// (candidate order), so the frontier always holds the best unexpanded entry.
+// The candidate table (first K ids and probabilities of each depth's filtered
+// row) is staged in LDS once; the frontier is an unordered set in registers
+// (entry q*64 + lane in slot q of this lane), and each pop is a wave argmax.
+constexpr int kFrontierSlots = 5;       // 320 entries >= 2V + 1 with V <= 128
+
+// Order of frontier entries: larger score first, then smaller depth, parent,
+// candidate rank.  Scores are non-negative doubles, so their bit patterns
+// order as integers; (depth, parent, rank) pack into 27 bits, smaller first.
+struct FrontKey {
+    uint64_t sbits;     // score bits; 0 with tie = ~0u marks an empty slot
+    uint32_t tie;       // depth << 20 | parent << 12 | rank
 };
 
-__device__ __forceinline__ bool fr_better(double sa, int da, int pa, int ra, double sb, int db, int pb,
-                                          int rb)
+__device__ __forceinline__ bool fk_better(const FrontKey& a, const FrontKey& b)
 {
-    if (sa != sb) return sa > sb;
-    if (da != db) return da < db;
-    if (pa != pb) return pa < pb;
-    return ra < rb;
+    return a.sbits != b.sbits ? a.sbits > b.sbits : a.tie < b.tie;
 }
 
 __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_t B, int32_t K, int32_t V,
                                                            SparseOut sup, TreeOut o)
 {
-    __shared__ double f_score[kFrontierCap];
-    __shared__ int32_t f_depth[kFrontierCap], f_parent[kFrontierCap], f_rank[kFrontierCap];
+    __shared__ int32_t c_id[kMaxTreeVK];       // depth d, rank r at d*K + r (B*K <= V*K <= 2048)
+    __shared__ double c_p[kMaxTreeVK];
+    __shared__ int32_t s_cn[kMaxNodes];
     __shared__ double n_score[kMaxNodes];
     __shared__ int32_t n_tok[kMaxNodes], n_par[kMaxNodes], n_dep[kMaxNodes];
-    __shared__ int32_t s_cn[kMaxNodes];
 
     const int lane = lane_id();
     const int b = blockIdx.x;
@@ -319,68 +326,70 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_
     }
     if (lane == 0) { n_score[0] = 1.0; n_tok[0] = -1; n_par[0] = -1; n_dep[0] = 0; }
     wave_sync();
+    for (int i = lane; i < B * K; i += kWave) {
+        const int d = i / K, r = i - d * K;
+        if (r < s_cn[d]) {
+            c_id[i] = sup.ids[(rbase + d) * cap + r];
+            c_p[i] = sup.probs[(rbase + d) * cap + r];
+        }
+    }
+    wave_sync();
 
-    auto qprob = [&](int d, int r) { return sup.probs[(rbase + d) * cap + r]; };
-    int fs = 0;
-    auto insert = [&](double s, int dd, int pp, int rr) {
-        int pos = 0;
-        for (int base = 0; base < fs; base += kWave) {
-            const int i = base + lane;
-            const bool bt = i < fs && fr_better(f_score[i], f_depth[i], f_parent[i], f_rank[i], s, dd, pp, rr);
-            pos += __popcll(__ballot(bt));
-        }
-        double rs[3];
-        int rd[3], rp[3], rk[3];
+    double fsc[kFrontierSlots];
+    FrontKey fk[kFrontierSlots];
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int i = q * kWave + lane;
-            if (i >= pos && i < fs) { rs[q] = f_score[i]; rd[q] = f_depth[i]; rp[q] = f_parent[i]; rk[q] = f_rank[i]; }
-        }
-        wave_sync();
+    for (int q = 0; q < kFrontierSlots; ++q) { fsc[q] = 0.0; fk[q] = FrontKey{ 0ull, ~0u }; }
+    int nf = 0;                                        // slots handed out (uniform)
+    auto push = [&](double sc, int d, int par, int rk) __attribute__((always_inline)) {
+        const int qs = nf >> 6, ls = nf & (kWave - 1);
+        const FrontKey key{ (uint64_t)__double_as_longlong(sc), ((uint32_t)d << 20) | ((uint32_t)par << 12) | (uint32_t)rk };
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int i = q * kWave + lane;
-            if (i >= pos && i < fs && i + 1 < kFrontierCap) {
-                f_score[i + 1] = rs[q]; f_depth[i + 1] = rd[q]; f_parent[i + 1] = rp[q]; f_rank[i + 1] = rk[q];
-            }
-        }
-        if (lane == 0) { f_score[pos] = s; f_depth[pos] = dd; f_parent[pos] = pp; f_rank[pos] = rr; }
-        wave_sync();
-        ++fs;
-    };
-    auto pop = [&](FrontierEntry& e) {
-        e.score = f_score[0]; e.depth = f_depth[0]; e.parent = f_parent[0]; e.rank = f_rank[0];
-        double rs[3];
-        int rd[3], rp[3], rk[3];
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int i = q * kWave + lane + 1;
-            if (i < fs) { rs[q] = f_score[i]; rd[q] = f_depth[i]; rp[q] = f_parent[i]; rk[q] = f_rank[i]; }
-        }
-        wave_sync();
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int i = q * kWave + lane + 1;
-            if (i < fs) { f_score[i - 1] = rs[q]; f_depth[i - 1] = rd[q]; f_parent[i - 1] = rp[q]; f_rank[i - 1] = rk[q]; }
-        }
-        wave_sync();
-        --fs;
+        for (int q = 0; q < kFrontierSlots; ++q)
+            if (q == qs && lane == ls) { fsc[q] = sc; fk[q] = key; }
+        ++nf;
     };
 
-    // Best-first expansion with lazily pushed siblings: a popped node pushes its
-    // next sibling and its first child.  Siblings come in non-increasing score
-    // (candidate order), so the frontier always holds the best unexpanded entry.
-    if (B > 0 && s_cn[0] > 0) insert(1.0 * qprob(0, 0), 1, 0, 0);
+    if (B > 0 && s_cn[0] > 0) push(1.0 * c_p[0], 1, 0, 0);
     int num = 1;
-    while (num <= V && fs > 0) {
-        FrontierEntry e;
-        pop(e);
-        const int32_t tok = sup.ids[(rbase + e.depth - 1) * cap + e.rank];
-        if (lane == 0) { n_score[num] = e.score; n_tok[num] = tok; n_par[num] = e.parent; n_dep[num] = e.depth; }
+    int live = nf;
+    while (num <= V && live > 0) {
+        // this lane's best slot, then the wave's best entry
+        FrontKey best = fk[0];
+        int bq = 0;
+#pragma unroll
+        for (int q = 1; q < kFrontierSlots; ++q)
+            if (fk_better(fk[q], best)) { best = fk[q]; bq = q; }
+        FrontKey w = best;
+#pragma unroll
+        for (int dd = kWave / 2; dd >= 1; dd >>= 1) {
+            FrontKey o2;
+            o2.sbits = (uint64_t)__shfl_xor((long long)w.sbits, dd, kWave);
+            o2.tie = (uint32_t)__shfl_xor((int)w.tie, dd, kWave);
+            if (fk_better(o2, w)) w = o2;
+        }
+        // the owner of the winning entry frees its slot
+        const bool mine = best.sbits == w.sbits && best.tie == w.tie;
+#pragma unroll
+        for (int q = 0; q < kFrontierSlots; ++q)
+            if (mine && q == bq) fk[q] = FrontKey{ 0ull, ~0u };
+        --live;
+        const double score = __longlong_as_double((long long)w.sbits);
+        const int depth = (int)(w.tie >> 20), parent = (int)((w.tie >> 12) & 0xFFu), rank = (int)(w.tie & 0xFFFu);
+        if (lane == 0) {
+            n_score[num] = score;
+            n_tok[num] = c_id[(depth - 1) * K + rank];
+            n_par[num] = parent;
+            n_dep[num] = depth;
+        }
         wave_sync();
-        if (e.rank + 1 < s_cn[e.depth - 1])
-            insert(n_score[e.parent] * qprob(e.depth - 1, e.rank + 1), e.depth, e.parent, e.rank + 1);
-        if (e.depth < B && s_cn[e.depth] > 0) insert(e.score * qprob(e.depth, 0), e.depth + 1, num, 0);
+        if (rank + 1 < s_cn[depth - 1]) {
+            push(n_score[parent] * c_p[(depth - 1) * K + rank + 1], depth, parent, rank + 1);
+            ++live;
+        }
+        if (depth < B && s_cn[depth] > 0) {
+            push(score * c_p[depth * K], depth + 1, num, 0);
+            ++live;
+        }
         ++num;
     }
     const int64_t ob = (int64_t)b * (V + 1);
@@ -425,21 +434,39 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     }
     __syncthreads();
     // every node's sample, drawn with the uniform of its depth
-    for (int n = w; n < nn; n += kWalkWaves) {
+    // the next node's support is loaded while this one is sampled
+    auto node_live = [&](int n, int* cnt) __attribute__((always_inline)) {
         const int dep = s_dep[n];
+        *cnt = sup.count[ob + n];
+        return dep >= 0 && dep <= B && *cnt > 0;
+    };
+    WaveRow R;
+    int cnt = 0;
+    bool live = false;
+    if (w < nn) {
+        live = node_live(w, &cnt);
+        if (live) wave_load_support(sup.ids + (ob + w) * cap, sup.probs + (ob + w) * cap, cnt, R, lane);
+    }
+    for (int n = w; n < nn; n += kWalkWaves) {
+        const int nx = n + kWalkWaves;
+        WaveRow Rn;
+        int cntn = 0;
+        bool liven = false;
+        if (nx < nn) {
+            liven = node_live(nx, &cntn);
+            if (liven) wave_load_support(sup.ids + (ob + nx) * cap, sup.probs + (ob + nx) * cap, cntn, Rn, lane);
+        }
         int32_t t = -1;
-        const int64_t row = ob + n;
-        const int cnt = sup.count[row];
-        if (dep >= 0 && dep <= B && cnt > 0) {
-            const Draw d = uno_draw(seed, req, (uint32_t)dep, offset);
-            WaveRow R;
-            wave_load_support(sup.ids + row * cap, sup.probs + row * cap, cnt, R, lane);
+        if (live) {
+            const Draw d = uno_draw(seed, req, (uint32_t)s_dep[n], offset);
             wave_sort_by_id(R, cnt, s_sort[w].key, s_sort[w].id, s_sort[w].w, lane);
             double dummy;
             t = wave_sample_sorted(R, cnt, d.u[2], &dummy, lane);
         }
         if (lane == 0) s_t[n] = t;
-        wave_sync();
+        R = Rn;
+        cnt = cntn;
+        live = liven;
     }
     __syncthreads();
     if (threadIdx.x != 0) return;
