@@ -89,60 +89,72 @@ __device__ __forceinline__ void wave_sort_by_id(WaveRow& R, int n, int32_t* s_ke
 // Inverse CDF over the n id-ordered entries of R with uniform u: the first
 // entry whose inclusive cumulative weight exceeds u * W (W the total); when
 // rounding leaves none, the last entry with positive weight.  Returns its id
-// (-1 when W is not positive) and its weight in *wpick.
-__device__ __forceinline__ int32_t wave_sample_sorted(const WaveRow& R, int n, double u, double* wpick, int lane)
+// (-1 when W is not positive) and its weight in *wpick.  The cumulative sums
+// are taken in id order by one lane over cum (LDS, n doubles), one add per
+// step; the pick is a ballot.
+__device__ __forceinline__ int32_t wave_sample_sorted(const WaveRow& R, int n, double u, double* wpick, int lane,
+                                                      double* cum)
 {
-    double c = 0.0;
-    double cv[kQ];
+    *wpick = 0.0;
+    if (n <= 0) return -1;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-        cv[q] = 0.0;
-        const int lim = n - q * kWave;
-        if (lim > 0)
-            for (int l = 0; l < kWave && l < lim; ++l) {
-                c += readlane_f64(R.w[q], l);
-                cv[q] = (lane == l) ? c : cv[q];
-            }
+        const int i = q * kWave + lane;
+        if (q * kWave < n && i < n) cum[i] = R.w[q];
     }
-    *wpick = 0.0;
-    if (!(c > 0.0)) return -1;
-    const double t = u * c;
+    wave_sync();
+    if (lane == 0) {
+        double acc = 0.0;
+#pragma unroll 8
+        for (int i = 0; i < n; ++i) {
+            acc += cum[i];
+            cum[i] = acc;
+        }
+    }
+    wave_sync();
+    const double W = cum[n - 1];
+    int32_t pick = -1;
+    if (W > 0.0) {
+        const double t = u * W;
+        bool found = false;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            if (q * kWave >= n || found) break;
+            const uint64_t m = __ballot(q * kWave + lane < n && cum[q * kWave + lane] > t);
+            if (m) {
+                const int src = wave_first_lane(m);
+                *wpick = __shfl(R.w[q], src, kWave);
+                pick = __shfl(R.id[q], src, kWave);
+                found = true;
+            }
+        }
+#pragma unroll
+        for (int q = kQ - 1; q >= 0; --q) {
+            if (found) break;
+            const uint64_t m = __ballot(q * kWave + lane < n && R.w[q] > 0.0);
+            if (m) {
+                const int src = 63 - __clzll((long long)m);
+                *wpick = __shfl(R.w[q], src, kWave);
+                pick = __shfl(R.id[q], src, kWave);
+                found = true;
+            }
+        }
+    }
+    wave_sync();             // cum is reused by the caller
+    return pick;
+}
+
+// Weight of token y in a wave's register support (0 when absent).
+__device__ __forceinline__ double reg_lookup(const WaveRow& R, int n, int32_t y, int lane)
+{
+    double v = 0.0;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
         if (q * kWave >= n) break;
-        const uint64_t m = __ballot(q * kWave + lane < n && cv[q] > t);
-        if (m) {
-            const int src = wave_first_lane(m);
-            *wpick = __shfl(R.w[q], src, kWave);
-            return __shfl(R.id[q], src, kWave);
-        }
+        const uint64_t m = __ballot(q * kWave + lane < n && R.id[q] == y);
+        if (m) v = __shfl(R.w[q], wave_first_lane(m), kWave);
     }
-#pragma unroll
-    for (int q = kQ - 1; q >= 0; --q) {
-        const uint64_t m = __ballot(q * kWave + lane < n && R.w[q] > 0.0);
-        if (m) {
-            const int src = 63 - __clzll((long long)m);
-            *wpick = __shfl(R.w[q], src, kWave);
-            return __shfl(R.id[q], src, kWave);
-        }
-    }
-    return -1;
-}
-
-// Probability of token y in an unordered support (0 when absent).
-__device__ double lookup_prob(const int32_t* ids, const double* p, int n, int32_t y, int lane)
-{
-    for (int base = 0; base < n; base += kWave) {
-        const int i = base + lane;
-        const bool hit = (i < n) && ids[i] == y;
-        const uint64_t m = __ballot(hit);
-        if (m) {
-            const int src = wave_first_lane(m);
-            const double pv = hit ? p[i] : 0.0;
-            return __shfl(pv, src, kWave);
-        }
-    }
-    return 0.0;
+    return v;
 }
 
 // Per-wave LDS scratch for sorting one support.
@@ -150,6 +162,7 @@ struct SortScratch {
     int32_t key[kMaxK];
     int32_t id[kMaxK];
     double w[kMaxK];
+    double cum[kMaxK];
 };
 
 // ---- linear, sparse supports -----------------------------------------------------
@@ -159,7 +172,7 @@ struct SortScratch {
 // at j would emit -- from the residual max(0, p_j - q_j), or from p_j when the
 // residual has no mass; at position B it draws the bonus token from p_B.  The
 // first rejection j* then only selects among these draws.
-constexpr int kLinWaves = 16;
+constexpr int kLinWaves = 9;     // B = 8 positions and the bonus in one round
 constexpr int kLinThreads = kLinWaves * kWave;
 
 // Weight of token `id` in an id-sorted list in LDS (0 when absent).
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     int32_t batch, int32_t B, SparseOut sup, uint64_t seed, uint64_t offset,
     const uint32_t* req_ids, LinearOut o)
 {
-    __shared__ SortScratch s_q[kLinWaves];
+    __shared__ SortScratch s_q[kLinWaves];     // q_j, left id-sorted for the residual
     __shared__ SortScratch s_p[kLinWaves];
     __shared__ int32_t s_y[kMaxLinearB];
     __shared__ int32_t s_acc[kMaxLinearB];
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
             double dummy;
             if (np > 0) {
                 wave_sort_by_id(P, np, s_p[w].key, s_p[w].id, s_p[w].w, lane);
-                fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane);
+                fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane, s_p[w].cum);
             } else {
                 ffl = 1u;
             }
@@ -223,14 +236,14 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
             WaveRow Q;
             wave_load_support(sup.ids + qr * cap, sup.probs + qr * cap, nq, Q, lane);
             wave_sort_by_id(Q, nq, s_q[w].key, s_q[w].id, s_q[w].w, lane);   // q stays id-sorted in s_q
-            y = wave_sample_sorted(Q, nq, d.u[0], &qy, lane);
+            y = wave_sample_sorted(Q, nq, d.u[0], &qy, lane, s_q[w].cum);
         } else {
             flags |= 1u;
         }
         int acc = 0;
         if (y >= 0) {
             double py = 0.0;
-            if (np > 0) py = lookup_prob(sup.ids + pr * cap, sup.probs + pr * cap, np, y, lane);
+            if (np > 0) py = reg_lookup(P, np, y, lane);
             else flags |= 1u;
             acc = (d.u[1] * qy < py) ? 1 : 0;
         }
@@ -249,10 +262,10 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
                     const double dlt = P.w[q] - qv;
                     Rz.w[q] = dlt > 0.0 ? dlt : 0.0;
                 }
-                fin = wave_sample_sorted(Rz, np, d.u[2], &dummy, lane);
+                fin = wave_sample_sorted(Rz, np, d.u[2], &dummy, lane, s_p[w].cum);
                 if (fin < 0) {
                     ffl = 2u;
-                    fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane);
+                    fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane, s_p[w].cum);
                 }
             } else {
                 ffl = 1u;
@@ -292,8 +305,6 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
 // The candidate table (first K ids and probabilities of each depth's filtered
 // row) is staged in LDS once; the frontier is an unordered set in registers
 // (entry q*64 + lane in slot q of this lane), and each pop is a wave argmax.
-constexpr int kFrontierSlots = 5;       // 320 entries >= 2V + 1 with V <= 128
-
 // Order of frontier entries: larger score first, then smaller depth, parent,
 // candidate rank.  Scores are non-negative doubles, so their bit patterns
 // order as integers; (depth, parent, rank) pack into 27 bits, smaller first.
@@ -307,6 +318,53 @@ __device__ __forceinline__ bool fk_better(const FrontKey& a, const FrontKey& b)
     return a.sbits != b.sbits ? a.sbits > b.sbits : a.tie < b.tie;
 }
 
+// Partner lane's key through a DPP lane permutation (CTRL: DPP control word).
+template <int CTRL>
+__device__ __forceinline__ FrontKey fk_dpp(const FrontKey& a)
+{
+    FrontKey o;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)a.sbits, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(a.sbits >> 32), CTRL, 0xF, 0xF, false);
+    o.sbits = ((uint64_t)hi << 32) | lo;
+    o.tie = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.tie, CTRL, 0xF, 0xF, false);
+    return o;
+}
+
+__device__ __forceinline__ FrontKey fk_readlane(const FrontKey& a, int l)
+{
+    FrontKey o;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.sbits, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.sbits >> 32), l);
+    o.sbits = ((uint64_t)hi << 32) | lo;
+    o.tie = (uint32_t)__builtin_amdgcn_readlane((int)a.tie, l);
+    return o;
+}
+
+// Best key of the wave: within each 16-lane row by DPP (swap neighbours, swap
+// pairs, mirror halves, mirror the row), then across the four rows.
+__device__ __forceinline__ FrontKey fk_wave_best(FrontKey w)
+{
+    FrontKey o = fk_dpp<0xB1>(w);      // quad_perm [1,0,3,2]
+    if (fk_better(o, w)) w = o;
+    o = fk_dpp<0x4E>(w);               // quad_perm [2,3,0,1]
+    if (fk_better(o, w)) w = o;
+    o = fk_dpp<0x141>(w);              // row_half_mirror
+    if (fk_better(o, w)) w = o;
+    o = fk_dpp<0x140>(w);              // row_mirror
+    if (fk_better(o, w)) w = o;
+    FrontKey best = fk_readlane(w, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const FrontKey c = fk_readlane(w, 16 * r);
+        if (fk_better(c, best)) best = c;
+    }
+    return best;
+}
+
+// FS frontier slots per lane: at most 1 + V entries are ever live, since a
+// popped entry's slot takes its next sibling and only first children need new
+// slots (FS = ceil((V + 1) / 64)).
+template <int FS>
 __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_t B, int32_t K, int32_t V,
                                                            SparseOut sup, TreeOut o)
 {
@@ -335,42 +393,35 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_
     }
     wave_sync();
 
-    double fsc[kFrontierSlots];
-    FrontKey fk[kFrontierSlots];
+    FrontKey fk[FS];
 #pragma unroll
-    for (int q = 0; q < kFrontierSlots; ++q) { fsc[q] = 0.0; fk[q] = FrontKey{ 0ull, ~0u }; }
-    int nf = 0;                                        // slots handed out (uniform)
-    auto push = [&](double sc, int d, int par, int rk) __attribute__((always_inline)) {
-        const int qs = nf >> 6, ls = nf & (kWave - 1);
+    for (int q = 0; q < FS; ++q) fk[q] = FrontKey{ 0ull, ~0u };
+    auto put = [&](int slot, double sc, int d, int par, int rk) __attribute__((always_inline)) {
+        const int qs = slot >> 6, ls = slot & (kWave - 1);
         const FrontKey key{ (uint64_t)__double_as_longlong(sc), ((uint32_t)d << 20) | ((uint32_t)par << 12) | (uint32_t)rk };
 #pragma unroll
-        for (int q = 0; q < kFrontierSlots; ++q)
-            if (q == qs && lane == ls) { fsc[q] = sc; fk[q] = key; }
-        ++nf;
+        for (int q = 0; q < FS; ++q)
+            if (q == qs && lane == ls) fk[q] = key;
     };
 
-    if (B > 0 && s_cn[0] > 0) push(1.0 * c_p[0], 1, 0, 0);
+    int nf = 0;                                        // slots handed out (uniform)
+    int live = 0;
+    if (B > 0 && s_cn[0] > 0) { put(nf++, 1.0 * c_p[0], 1, 0, 0); ++live; }
     int num = 1;
-    int live = nf;
     while (num <= V && live > 0) {
         // this lane's best slot, then the wave's best entry
         FrontKey best = fk[0];
         int bq = 0;
 #pragma unroll
-        for (int q = 1; q < kFrontierSlots; ++q)
+        for (int q = 1; q < FS; ++q)
             if (fk_better(fk[q], best)) { best = fk[q]; bq = q; }
-        FrontKey w = best;
-#pragma unroll
-        for (int dd = kWave / 2; dd >= 1; dd >>= 1) {
-            FrontKey o2;
-            o2.sbits = (uint64_t)__shfl_xor((long long)w.sbits, dd, kWave);
-            o2.tie = (uint32_t)__shfl_xor((int)w.tie, dd, kWave);
-            if (fk_better(o2, w)) w = o2;
-        }
-        // the owner of the winning entry frees its slot
+        const FrontKey w = fk_wave_best(best);
+        // the owner of the winning entry frees its slot, which the sibling reuses
         const bool mine = best.sbits == w.sbits && best.tie == w.tie;
+        const int wl = wave_first_lane(__ballot(mine));
+        const int wslot = __builtin_amdgcn_readlane(bq, wl) * kWave + wl;
 #pragma unroll
-        for (int q = 0; q < kFrontierSlots; ++q)
+        for (int q = 0; q < FS; ++q)
             if (mine && q == bq) fk[q] = FrontKey{ 0ull, ~0u };
         --live;
         const double score = __longlong_as_double((long long)w.sbits);
@@ -383,11 +434,11 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_
         }
         wave_sync();
         if (rank + 1 < s_cn[depth - 1]) {
-            push(n_score[parent] * c_p[(depth - 1) * K + rank + 1], depth, parent, rank + 1);
+            put(wslot, n_score[parent] * c_p[(depth - 1) * K + rank + 1], depth, parent, rank + 1);
             ++live;
         }
         if (depth < B && s_cn[depth] > 0) {
-            push(score * c_p[depth * K], depth + 1, num, 0);
+            put(nf++, score * c_p[depth * K], depth + 1, num, 0);
             ++live;
         }
         ++num;
@@ -461,7 +512,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
             const Draw d = uno_draw(seed, req, (uint32_t)s_dep[n], offset);
             wave_sort_by_id(R, cnt, s_sort[w].key, s_sort[w].id, s_sort[w].w, lane);
             double dummy;
-            t = wave_sample_sorted(R, cnt, d.u[2], &dummy, lane);
+            t = wave_sample_sorted(R, cnt, d.u[2], &dummy, lane, s_sort[w].cum);
         }
         if (lane == 0) s_t[n] = t;
         R = Rn;
@@ -469,27 +520,32 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
         live = liven;
     }
     __syncthreads();
-    if (threadIdx.x != 0) return;
+    if (w != 0) return;
+    // the walk itself: one wave, each step finds the matching child by ballot
     int32_t* tok = o.tokens + (int64_t)b * (B + 1);
     int32_t* pth = o.path + (int64_t)b * (B + 1);
     int n = 0, d = 0;
     uint32_t fl = 0;
     for (;;) {
         const int32_t t = s_t[n];
-        tok[d] = t;
-        pth[d] = n;
+        if (lane == 0) { tok[d] = t; pth[d] = n; }
         if (t < 0) fl |= 1u;
         int child = -1;
         if (t >= 0 && d < B)
-            for (int c = 1; c < nn; ++c)
-                if (s_par[c] == n && s_tok[c] == t) { child = c; break; }
+            for (int base = 1; base < nn && child < 0; base += kWave) {
+                const int c = base + lane;
+                const uint64_t m = __ballot(c < nn && s_par[c] == n && s_tok[c] == t);
+                if (m) child = base + wave_first_lane(m);
+            }
         if (child < 0) break;
         n = child;
         ++d;
     }
-    for (int j = d + 1; j <= B; ++j) { tok[j] = -1; pth[j] = -1; }
-    o.accept_len[b] = d + 1;
-    if (o.flags) o.flags[b] = fl;
+    for (int j = d + 1 + lane; j <= B; j += kWave) { tok[j] = -1; pth[j] = -1; }
+    if (lane == 0) {
+        o.accept_len[b] = d + 1;
+        if (o.flags) o.flags[b] = fl;
+    }
 }
 
 // ---- dense linear ------------------------------------------------------------------
@@ -922,7 +978,13 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
 hipError_t launch_tree_build(int32_t batch, int32_t B, int32_t K, int32_t V, const SparseOut& sup,
                              const TreeOut& o, hipStream_t stream)
 {
-    tree_build_kernel<<<dim3((unsigned)batch), kWave, 0, stream>>>(batch, B, K, V, sup, o);
+    // live frontier entries <= 1 + V
+    if (V + 1 <= kWave)
+        tree_build_kernel<1><<<dim3((unsigned)batch), kWave, 0, stream>>>(batch, B, K, V, sup, o);
+    else if (V + 1 <= 2 * kWave)
+        tree_build_kernel<2><<<dim3((unsigned)batch), kWave, 0, stream>>>(batch, B, K, V, sup, o);
+    else
+        tree_build_kernel<3><<<dim3((unsigned)batch), kWave, 0, stream>>>(batch, B, K, V, sup, o);
     return hipGetLastError();
 }
 
