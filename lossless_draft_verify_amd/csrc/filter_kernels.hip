@@ -667,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
 // ---- dense chunk statistics --------------------------------------------------
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
-    RowSource src, int64_t rows, int64_t N, double log2e_over_T, DenseChunks dc)
+    RowSource src, int64_t rows, int64_t N, double log2e_over_T, int64_t exact_rows, DenseChunks dc)
 {
     using V = Vec<BF16>;
     constexpr int EPV = V::EPV, ESZ = V::ESZ;
@@ -699,25 +699,16 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
 #pragma unroll
         for (int j = 0; j < NV; ++j) v[j] = V::load_stream(p + j * kWave + lane);
     };
-    // statistics of one chunk held as x[PER_LANE] (element (j*64 + lane)*EPV + e at x[j*EPV + e])
+    // statistics of one chunk held as x[PER_LANE] (element (j*64 + lane)*EPV + e
+    // at x[j*EPV + e]); rows from exact_rows on take the fast sums
+    const bool exact = r < exact_rows;
+    const float log2e_over_T32 = (float)log2e_over_T;
     auto chunk_stats = [&](int c, const float (&x)[PER_LANE]) __attribute__((always_inline)) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) mx = fmaxf(mx, x[i]);
-        mx = wave_max_f32(mx);
-        double s = 0.0;
-        uint32_t cntf = 0;
-        if (mx > -INFINITY && mx < INFINITY) {
-            const double md = (double)mx;
-#pragma unroll
-            for (int i = 0; i < PER_LANE; ++i) {
-                // NaN and -inf reach the exp's lower clamp, whose term (2^-1000)
-                // vanishes next to the chunk maximum's 1
-                cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
-                s += ex((double)x[i] - md);
-            }
-        }
-        s = wave_sum_f64(s);
+        float mx;
+        double s;
+        uint32_t cntf;
+        if (exact) chunk_stats_exact(x, ex, &mx, &s, &cntf);
+        else chunk_stats_fast(x, log2e_over_T32, &mx, &s, &cntf);
         if (lane == 0) {
             const int64_t slot = r * nc + c;
             dc.cmax[slot] = mx;
@@ -825,15 +816,15 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
 }
 
 hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
-                               float temperature, const DenseChunks& dc, hipStream_t stream)
+                               float temperature, const DenseChunks& dc, int64_t exact_rows, hipStream_t stream)
 {
     if (rows == 0) return hipSuccess;
     const double c = 1.4426950408889634074 / (double)temperature;
     dim3 grid((unsigned)rows);
     if (bf16)
-        dense_chunk_kernel<true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, dc);
+        dense_chunk_kernel<true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
     else
-        dense_chunk_kernel<false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, dc);
+        dense_chunk_kernel<false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
     return hipGetLastError();
 }
 

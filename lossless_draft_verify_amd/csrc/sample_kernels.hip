@@ -823,12 +823,47 @@ __global__ __launch_bounds__(kDenseThreads) void dense_propose_kernel(
     }
 }
 
+// Exact chunk statistics of the target row each request draws its last token
+// from (p_j* after a rejection, the bonus row p_B otherwise).  The chunk pass
+// gave target rows fast sums, which only enter acceptance ratios.
+template <bool BF16>
+__global__ __launch_bounds__(kDenseThreads) void dense_exact_row_kernel(
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
+    const int32_t* jstar_in)
+{
+    __shared__ double s_exp2[kExp2Entries];
+    load_exp2_table(s_exp2);
+    __syncthreads();
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int b = blockIdx.x;
+    const int nc = dc.nchunks;
+    const int c = blockIdx.y * kDenseWaves + w;
+    if (c >= nc) return;
+    const int js = jstar_in[b];
+    const int64_t pr = linear_row(batch, B, b, B + (js < B ? js : B));
+    const DenseExp ex{ log2e_over_T, s_exp2 };
+    float x[kPerLane];
+    load_chunk<BF16>(row_pointer(src, pr, N * Vec<BF16>::ESZ), N, c, x, lane);
+    float mx;
+    double sum;
+    uint32_t cntf;
+    chunk_stats_exact(x, ex, &mx, &sum, &cntf);
+    if (lane == 0) {
+        const int64_t slot = pr * nc + c;
+        dc.cmax[slot] = mx;
+        dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
+        dc.ccount[slot] = (int32_t)cntf;
+    }
+}
+
 // Residual mass per chunk for requests that rejected a proposal.
 template <bool BF16>
 __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
-    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, int32_t nc,
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
     const float* row_m, const double* row_S, const int32_t* jstar_in, double* resid)
 {
+    const int nc = dc.nchunks;
     __shared__ double s_exp2[kExp2Entries];
     load_exp2_table(s_exp2);
     __syncthreads();
@@ -840,7 +875,10 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
     if (js >= B || c >= nc) return;
     const DenseExp ex{ log2e_over_T, s_exp2 };
     const int64_t qr = linear_row(batch, B, b, js), pr = linear_row(batch, B, b, B + js);
-    const double Sp = row_S[pr], Sq = row_S[qr];
+    float mpf;
+    double Sp;
+    dense_row_stat(dc.cmax + pr * nc, dc.csum + pr * nc, nc, ex, lane, &mpf, &Sp);   // exact chunks
+    const double Sq = row_S[qr];
     double total = 0.0;
     if (Sp > 0.0) {
         const int64_t row_bytes = N * Vec<BF16>::ESZ;
@@ -848,7 +886,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
         float xp[kPerLane], xq[kPerLane];
         load_chunk<BF16>(row_pointer(src, pr, row_bytes), N, c, xp, lane);
         if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
-        const double mp = (double)row_m[pr], mq = (double)row_m[qr];
+        const double mp = (double)mpf, mq = (double)row_m[qr];
         const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
         auto wf = [&](int i) {
             const double pv = finite_f32(xp[i]) ? ex((double)xp[i] - mp) * iSp : 0.0;
@@ -884,8 +922,9 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
     int32_t fin = -1;
     const int64_t pr = linear_row(batch, B, b, B + js);
     const char* prow = row_pointer(src, pr, row_bytes);
-    const float mp = row_m[pr];
-    const double Sp = row_S[pr];
+    float mp;
+    double Sp;
+    dense_row_stat(dc.cmax + pr * nc, dc.csum + pr * nc, nc, ex, lane, &mp, &Sp);   // exact chunks
     if (!(Sp > 0.0)) {
         fl |= 1u;
     } else if (js < B) {
@@ -957,8 +996,9 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
         dense_propose_kernel<true><<<dim3((unsigned)batch), kDenseThreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
             sc.flags, o);
+        dense_exact_row_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar);
         dense_residual_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(
-            src, batch, B, vocab, c, dc.nchunks, sc.row_m, sc.row_S, sc.jstar, sc.resid);
+            src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid);
         dense_finish_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
             sc.flags, sc.resid, o);
@@ -966,8 +1006,9 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
         dense_propose_kernel<false><<<dim3((unsigned)batch), kDenseThreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
             sc.flags, o);
+        dense_exact_row_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar);
         dense_residual_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(
-            src, batch, B, vocab, c, dc.nchunks, sc.row_m, sc.row_S, sc.jstar, sc.resid);
+            src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid);
         dense_finish_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
             sc.flags, sc.resid, o);

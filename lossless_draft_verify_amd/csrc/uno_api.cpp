@@ -255,7 +255,7 @@ int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab, c
         return hip_status(launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, m), out, sw.S,
                                              sw.part_key, sw.part_id, sw.part_n, stream));
     }
-    hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, stream);
+    hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
     if (e == hipSuccess) e = launch_dense_row_stats(rows, sp->temperature, dc, out_count, out_stats, stream);
     return hip_status(e);
 }
@@ -294,7 +294,10 @@ int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int3
                                sw.part_id, sw.part_n, stream);
         if (e == hipSuccess) e = launch_linear_sparse(batch, B, sw.sup, seed, offset, request_ids, o, stream);
     } else {
-        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, stream);
+        // draft rows are sampled from (exact sums); target rows enter only
+        // acceptance ratios, except the one each request draws its last token
+        // from, which the dense linear path recomputes exactly
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, (int64_t)batch * B, stream);
         if (e == hipSuccess)
             e = launch_linear_dense(src, batch, B, vocab, bf16, sp->temperature, dc, ds, seed, offset,
                                     request_ids, o, stream);

@@ -264,4 +264,63 @@ struct DenseExp {
     }
 };
 
+// ---- per-chunk statistics of dense rows ----------------------------------------
+// x: one chunk held by a wave (entry i of each lane; NaN and -inf allowed).
+// Outputs are wave-uniform: the chunk max m, the fp64 sum of exp((z - m)/T)
+// over the chunk and the number of finite logits.  With no finite logit the
+// sum is 0; with +inf the max is +inf (the caller marks the row invalid).
+
+// Exact: every term from DenseExp.
+template <int PER_LANE>
+__device__ __forceinline__ void chunk_stats_exact(const float (&x)[PER_LANE], const DenseExp& ex, float* m_out,
+                                                  double* s_out, uint32_t* cnt_out)
+{
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) mx = fmaxf(mx, x[i]);
+    mx = wave_max_f32(mx);
+    double s = 0.0;
+    uint32_t cntf = 0;
+    if (mx > -INFINITY && mx < INFINITY) {
+        const double md = (double)mx;
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            // NaN and -inf reach the exp's lower clamp, whose term (2^-1000)
+            // vanishes next to the chunk maximum's 1
+            cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
+            s += ex((double)x[i] - md);
+        }
+    }
+    *m_out = mx;
+    *s_out = wave_sum_f64(s);
+    *cnt_out = cntf;
+}
+
+// Fast: terms from the fp32 exponential (relative error near 1e-7), summed in
+// fp64.  Good enough for a normaliser that only enters a probability ratio;
+// never used where a CDF is inverted.
+template <int PER_LANE>
+__device__ __forceinline__ void chunk_stats_fast(const float (&x)[PER_LANE], float log2e_over_T, float* m_out,
+                                                 double* s_out, uint32_t* cnt_out)
+{
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) mx = fmaxf(mx, x[i]);
+    mx = wave_max_f32(mx);
+    double s = 0.0;
+    uint32_t cntf = 0;
+    if (mx > -INFINITY && mx < INFINITY) {
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
+            // fmaxf maps NaN to the large negative bound; its term is 0
+            const float y = (fmaxf(x[i], -3.0e38f) - mx) * log2e_over_T;
+            s += (double)__builtin_amdgcn_exp2f(fmaxf(y, -200.0f));
+        }
+    }
+    *m_out = mx;
+    *s_out = wave_sum_f64(s);
+    *cnt_out = cntf;
+}
+
 }  // namespace uno
