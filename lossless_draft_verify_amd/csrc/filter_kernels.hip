@@ -645,11 +645,11 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
         uint32_t kk = 0;
         int32_t ii = 0;
         bool keep = false;
-        if (g < total && i < s_segn[sg]) {
+        if (g < total) {
             const int64_t base = (r * S + sg) * (int64_t)k;
             kk = part_key[base + i];
             ii = part_id[base + i];
-            keep = order_key(kk, ii) >= pstar;
+            keep = i < s_segn[sg] && order_key(kk, ii) >= pstar;
         }
         const uint64_t m = __ballot(keep);
         int pos0 = 0;

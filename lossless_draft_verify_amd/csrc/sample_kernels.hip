@@ -36,15 +36,21 @@ struct WaveRow {
     double w[kQ];
 };
 
-// Load n <= 256 entries (unordered); slots past n hold id INT32_MAX, weight 0.
-__device__ __forceinline__ void wave_load_support(const int32_t* ids, const double* p, int n, WaveRow& R, int lane)
+// Load the n <= cap <= 256 entries of a support (unordered); slots past n hold
+// id INT32_MAX, weight 0.
+__device__ __forceinline__ void wave_load_support(const int32_t* ids, const double* p, int n, int cap, WaveRow& R,
+                                                  int lane)
 {
+    // every slot below cap is read (the filter pads supports to cap), so the
+    // loads do not wait for the count
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
         const int i = q * kWave + lane;
-        R.id[q] = 0x7FFFFFFF;
-        R.w[q] = 0.0;
-        if (q * kWave < n && i < n) { R.id[q] = ids[i]; R.w[q] = p[i]; }
+        int32_t id = 0x7FFFFFFF;
+        double w = 0.0;
+        if (q * kWave < cap && i < cap) { id = ids[i]; w = p[i]; }
+        R.id[q] = (i < n) ? id : 0x7FFFFFFF;
+        R.w[q] = (i < n) ? w : 0.0;
     }
 }
 
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
         const int64_t pr = pbase + j;
         const int np = sup.count[pr];
         WaveRow P;                       // p_j, loaded up front
-        if (np > 0) wave_load_support(sup.ids + pr * cap, sup.probs + pr * cap, np, P, lane);
+        wave_load_support(sup.ids + pr * cap, sup.probs + pr * cap, np, cap, P, lane);
         int32_t fin = -1;
         uint32_t ffl = 0;
         if (j == B) {                    // bonus draw
@@ -232,9 +238,9 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
         const int nq = sup.count[qr];
         int32_t y = -1;
         double qy = 0.0;
+        WaveRow Q;
+        wave_load_support(sup.ids + qr * cap, sup.probs + qr * cap, nq, cap, Q, lane);
         if (nq > 0) {
-            WaveRow Q;
-            wave_load_support(sup.ids + qr * cap, sup.probs + qr * cap, nq, Q, lane);
             wave_sort_by_id(Q, nq, s_q[w].key, s_q[w].id, s_q[w].w, lane);   // q stays id-sorted in s_q
             y = wave_sample_sorted(Q, nq, d.u[0], &qy, lane, s_q[w].cum);
         } else {
@@ -383,10 +389,12 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_
         s_cn[d] = n > 0 ? (n < K ? n : K) : 0;
     }
     if (lane == 0) { n_score[0] = 1.0; n_tok[0] = -1; n_par[0] = -1; n_dep[0] = 0; }
-    wave_sync();
+    // the candidate table is read whole (supports are padded to cap), together
+    // with the counts above; entries past a count are never used
+    const int kk = K < cap ? K : cap;
     for (int i = lane; i < B * K; i += kWave) {
         const int d = i / K, r = i - d * K;
-        if (r < s_cn[d]) {
+        if (r < kk) {
             c_id[i] = sup.ids[(rbase + d) * cap + r];
             c_p[i] = sup.probs[(rbase + d) * cap + r];
         }
@@ -465,6 +473,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
 {
     __shared__ SortScratch s_sort[kWalkWaves];
     __shared__ int32_t s_dep[kMaxNodes], s_t[kMaxNodes], s_tok[kMaxNodes], s_par[kMaxNodes];
+    __shared__ int32_t s_anc[2][kMaxNodes], s_dist[2][kMaxNodes];
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -474,15 +483,31 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     int nn = num_nodes[b];
     nn = nn < 1 ? 1 : (nn > V + 1 ? V + 1 : nn);
     const int64_t ob = (int64_t)b * (V + 1);
-    if (threadIdx.x == 0) {
-        s_dep[0] = 0; s_tok[0] = -1; s_par[0] = -1;
-        for (int n = 1; n < nn; ++n) {
-            const int p = node_parent[ob + n];
-            s_par[n] = p;
-            s_tok[n] = node_token[ob + n];
-            s_dep[n] = (p >= 0 && p < n && s_dep[p] >= 0) ? s_dep[p] + 1 : -1;
-        }
+    // node arrays (all V + 1 slots, read at once), then depths by pointer
+    // jumping: (anc, dist) climbs towards the root in doubling steps; -1 marks
+    // the root reached, -2 a broken parent link (depth -1)
+    const int t = (int)threadIdx.x;
+    int anc = -2, dist = 0;
+    if (t <= V) {
+        const int p = node_parent[ob + t];
+        const int tk = node_token[ob + t];
+        if (t == 0) { anc = -1; s_par[0] = -1; s_tok[0] = -1; }
+        else if (t < nn) { anc = (p >= 0 && p < t) ? p : -2; dist = 1; s_par[t] = p; s_tok[t] = tk; }
+        s_anc[0][t] = anc;
+        s_dist[0][t] = dist;
     }
+    __syncthreads();
+    for (int it = 0; it < 8; ++it) {
+        const int cur = it & 1;
+        if (t < nn && anc >= 0) {
+            const int a = s_anc[cur][anc];
+            dist += s_dist[cur][anc];
+            anc = a;
+        }
+        if (t < nn) { s_anc[cur ^ 1][t] = anc; s_dist[cur ^ 1][t] = dist; }
+        __syncthreads();
+    }
+    if (t < nn) s_dep[t] = (anc == -1) ? dist : -1;
     __syncthreads();
     // every node's sample, drawn with the uniform of its depth
     // the next node's support is loaded while this one is sampled
@@ -496,7 +521,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     bool live = false;
     if (w < nn) {
         live = node_live(w, &cnt);
-        if (live) wave_load_support(sup.ids + (ob + w) * cap, sup.probs + (ob + w) * cap, cnt, R, lane);
+        wave_load_support(sup.ids + (ob + w) * cap, sup.probs + (ob + w) * cap, live ? cnt : 0, cap, R, lane);
     }
     for (int n = w; n < nn; n += kWalkWaves) {
         const int nx = n + kWalkWaves;
@@ -505,7 +530,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
         bool liven = false;
         if (nx < nn) {
             liven = node_live(nx, &cntn);
-            if (liven) wave_load_support(sup.ids + (ob + nx) * cap, sup.probs + (ob + nx) * cap, cntn, Rn, lane);
+            wave_load_support(sup.ids + (ob + nx) * cap, sup.probs + (ob + nx) * cap, liven ? cntn : 0, cap, Rn, lane);
         }
         int32_t t = -1;
         if (live) {
