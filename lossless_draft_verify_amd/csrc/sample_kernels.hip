@@ -308,89 +308,75 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
 // Best-first expansion with lazily pushed siblings: a popped node pushes its
 // next sibling and its first child.  Siblings come in non-increasing score
 // (candidate order), so the frontier always holds the best unexpanded entry.
-// The candidate table (first K ids and probabilities of each depth's filtered
-// row) is staged in LDS once; the frontier is an unordered set in registers
-// (entry q*64 + lane in slot q of this lane), and each pop is a wave argmax.
 // Order of frontier entries: larger score first, then smaller depth, parent,
 // candidate rank.  Scores are non-negative doubles, so their bit patterns
-// order as integers; (depth, parent, rank) pack into 27 bits, smaller first.
-struct FrontKey {
-    uint64_t sbits;     // score bits; 0 with tie = ~0u marks an empty slot
-    uint32_t tie;       // depth << 20 | parent << 12 | rank
-};
+// order as integers; (depth, parent, rank) pack into one word, smaller first.
+//
+// Everything a pop touches lives in registers, spread over the lanes: entry
+// (or node, or depth) i sits in lane i % 64 of slot i / 64.  The frontier is
+// an unordered set; each pop is a wave maximum of the score's high word, and
+// only lanes that tie on it go on to the low word and then the tie word.  The
+// only memory access of a pop is the next sibling's probability, from the
+// candidate table (first K ids and probabilities of each depth's filtered
+// row) staged in LDS.
 
-__device__ __forceinline__ bool fk_better(const FrontKey& a, const FrontKey& b)
+__device__ __forceinline__ uint32_t tree_tie(int depth, int parent, int rank)
 {
-    return a.sbits != b.sbits ? a.sbits > b.sbits : a.tie < b.tie;
+    return ((uint32_t)depth << 20) | ((uint32_t)parent << 12) | (uint32_t)rank;
 }
 
-// Partner lane's key through a DPP lane permutation (CTRL: DPP control word).
-template <int CTRL>
-__device__ __forceinline__ FrontKey fk_dpp(const FrontKey& a)
+// Lane (i % 64) of slot (i / 64), i uniform.
+template <int N>
+__device__ __forceinline__ int slot_get_i32(const int (&a)[N], int i)
 {
-    FrontKey o;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)a.sbits, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(a.sbits >> 32), CTRL, 0xF, 0xF, false);
-    o.sbits = ((uint64_t)hi << 32) | lo;
-    o.tie = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.tie, CTRL, 0xF, 0xF, false);
-    return o;
-}
-
-__device__ __forceinline__ FrontKey fk_readlane(const FrontKey& a, int l)
-{
-    FrontKey o;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.sbits, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.sbits >> 32), l);
-    o.sbits = ((uint64_t)hi << 32) | lo;
-    o.tie = (uint32_t)__builtin_amdgcn_readlane((int)a.tie, l);
-    return o;
-}
-
-// Best key of the wave: within each 16-lane row by DPP (swap neighbours, swap
-// pairs, mirror halves, mirror the row), then across the four rows.
-__device__ __forceinline__ FrontKey fk_wave_best(FrontKey w)
-{
-    FrontKey o = fk_dpp<0xB1>(w);      // quad_perm [1,0,3,2]
-    if (fk_better(o, w)) w = o;
-    o = fk_dpp<0x4E>(w);               // quad_perm [2,3,0,1]
-    if (fk_better(o, w)) w = o;
-    o = fk_dpp<0x141>(w);              // row_half_mirror
-    if (fk_better(o, w)) w = o;
-    o = fk_dpp<0x140>(w);              // row_mirror
-    if (fk_better(o, w)) w = o;
-    FrontKey best = fk_readlane(w, 0);
+    int r = 0;
 #pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        const FrontKey c = fk_readlane(w, 16 * r);
-        if (fk_better(c, best)) best = c;
-    }
-    return best;
+    for (int q = 0; q < N; ++q)
+        if ((i >> 6) == q) r = __builtin_amdgcn_readlane(a[q], i & (kWave - 1));
+    return r;
 }
 
-// FS frontier slots per lane: at most 1 + V entries are ever live, since a
-// popped entry's slot takes its next sibling and only first children need new
-// slots (FS = ceil((V + 1) / 64)).
+template <int N>
+__device__ __forceinline__ double slot_get_f64(const double (&a)[N], int i)
+{
+    double r = 0.0;
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+        if ((i >> 6) == q) r = readlane_f64(a[q], i & (kWave - 1));
+    return r;
+}
+
+// FS register slots per lane for the frontier and for the node records: at
+// most 1 + V entries are ever live, since a popped entry's slot takes its next
+// sibling and only first children need new slots (FS = ceil((V + 1) / 64)).
 template <int FS>
 __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_t B, int32_t K, int32_t V,
                                                            SparseOut sup, TreeOut o)
 {
     __shared__ int32_t c_id[kMaxTreeVK];       // depth d, rank r at d*K + r (B*K <= V*K <= 2048)
     __shared__ double c_p[kMaxTreeVK];
-    __shared__ int32_t s_cn[kMaxNodes];
-    __shared__ double n_score[kMaxNodes];
-    __shared__ int32_t n_tok[kMaxNodes], n_par[kMaxNodes], n_dep[kMaxNodes];
 
     const int lane = lane_id();
     const int b = blockIdx.x;
     const int cap = sup.cap;
     const int64_t rbase = (int64_t)b * B;
-    for (int d = lane; d < B; d += kWave) {
-        const int n = sup.count[rbase + d];
-        s_cn[d] = n > 0 ? (n < K ? n : K) : 0;
+    // per depth (B <= 128): candidate count (at most K) and first probability
+    int cn[2];
+    double p0[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int d = s * kWave + lane;
+        int n = 0;
+        double f = 0.0;
+        if (d < B) {
+            n = sup.count[rbase + d];
+            f = sup.probs[(rbase + d) * cap];
+        }
+        cn[s] = n > 0 ? (n < K ? n : K) : 0;
+        p0[s] = f;
     }
-    if (lane == 0) { n_score[0] = 1.0; n_tok[0] = -1; n_par[0] = -1; n_dep[0] = 0; }
-    // the candidate table is read whole (supports are padded to cap), together
-    // with the counts above; entries past a count are never used
+    // the candidate table is read whole (supports are padded to cap); entries
+    // past a count are never used
     const int kk = K < cap ? K : cap;
     for (int i = lane; i < B * K; i += kWave) {
         const int d = i / K, r = i - d * K;
@@ -401,63 +387,88 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_
     }
     wave_sync();
 
-    FrontKey fk[FS];
+    uint64_t fs[FS];                                   // frontier: score bits (0 = empty)
+    uint32_t ft[FS];                                   // frontier: tie word (~0 = empty)
+    double ns[FS];                                     // node records: score
+    uint32_t nt[FS];                                   // node records: tie word of the entry
 #pragma unroll
-    for (int q = 0; q < FS; ++q) fk[q] = FrontKey{ 0ull, ~0u };
-    auto put = [&](int slot, double sc, int d, int par, int rk) __attribute__((always_inline)) {
+    for (int q = 0; q < FS; ++q) { fs[q] = 0ull; ft[q] = ~0u; ns[q] = 0.0; nt[q] = 0u; }
+    if (lane == 0) ns[0] = 1.0;
+    auto put = [&](int slot, double sc, uint32_t tie) __attribute__((always_inline)) {
         const int qs = slot >> 6, ls = slot & (kWave - 1);
-        const FrontKey key{ (uint64_t)__double_as_longlong(sc), ((uint32_t)d << 20) | ((uint32_t)par << 12) | (uint32_t)rk };
 #pragma unroll
         for (int q = 0; q < FS; ++q)
-            if (q == qs && lane == ls) fk[q] = key;
+            if (q == qs && lane == ls) { fs[q] = (uint64_t)__double_as_longlong(sc); ft[q] = tie; }
     };
 
     int nf = 0;                                        // slots handed out (uniform)
     int live = 0;
-    if (B > 0 && s_cn[0] > 0) { put(nf++, 1.0 * c_p[0], 1, 0, 0); ++live; }
+    if (__builtin_amdgcn_readlane(cn[0], 0) > 0) { put(nf++, 1.0 * readlane_f64(p0[0], 0), tree_tie(1, 0, 0)); ++live; }
     int num = 1;
     while (num <= V && live > 0) {
-        // this lane's best slot, then the wave's best entry
-        FrontKey best = fk[0];
+        // this lane's best slot
+        uint64_t bs = fs[0];
+        uint32_t bt = ft[0];
         int bq = 0;
 #pragma unroll
         for (int q = 1; q < FS; ++q)
-            if (fk_better(fk[q], best)) { best = fk[q]; bq = q; }
-        const FrontKey w = fk_wave_best(best);
+            if (fs[q] > bs || (fs[q] == bs && ft[q] < bt)) { bs = fs[q]; bt = ft[q]; bq = q; }
+        // the wave's best: high score word, then (on ties) low word, tie word
+        const uint32_t bh = (uint32_t)(bs >> 32), bl = (uint32_t)bs;
+        const uint32_t hm = wave_ext_u32<true>(bh);
+        uint64_t hit = __ballot(bh == hm);
+        if (__popcll(hit) > 1) {
+            const uint32_t lm = wave_ext_u32<true>(bh == hm ? bl : 0u);
+            const bool c = bh == hm && bl == lm;
+            hit = __ballot(c);
+            if (__popcll(hit) > 1) {
+                const uint32_t tm = wave_ext_u32<false>(c ? bt : ~0u);
+                hit = __ballot(c && bt == tm);
+            }
+        }
+        const int wl = wave_first_lane(hit);
+        const uint32_t tie = (uint32_t)__builtin_amdgcn_readlane((int)bt, wl);
+        const int wq = __builtin_amdgcn_readlane(bq, wl);
+        const double score = __longlong_as_double(
+            (long long)(((uint64_t)hm << 32) | (uint32_t)__builtin_amdgcn_readlane((int)bl, wl)));
         // the owner of the winning entry frees its slot, which the sibling reuses
-        const bool mine = best.sbits == w.sbits && best.tie == w.tie;
-        const int wl = wave_first_lane(__ballot(mine));
-        const int wslot = __builtin_amdgcn_readlane(bq, wl) * kWave + wl;
 #pragma unroll
         for (int q = 0; q < FS; ++q)
-            if (mine && q == bq) fk[q] = FrontKey{ 0ull, ~0u };
+            if (lane == wl && q == wq) { fs[q] = 0ull; ft[q] = ~0u; }
         --live;
-        const double score = __longlong_as_double((long long)w.sbits);
-        const int depth = (int)(w.tie >> 20), parent = (int)((w.tie >> 12) & 0xFFu), rank = (int)(w.tie & 0xFFFu);
-        if (lane == 0) {
-            n_score[num] = score;
-            n_tok[num] = c_id[(depth - 1) * K + rank];
-            n_par[num] = parent;
-            n_dep[num] = depth;
-        }
-        wave_sync();
-        if (rank + 1 < s_cn[depth - 1]) {
-            put(wslot, n_score[parent] * c_p[(depth - 1) * K + rank + 1], depth, parent, rank + 1);
+        const int depth = (int)(tie >> 20), parent = (int)((tie >> 12) & 0xFFu), rank = (int)(tie & 0xFFFu);
+        int si = (depth - 1) * K + rank + 1;
+        si = si < kMaxTreeVK ? si : kMaxTreeVK - 1;
+        const double sp = c_p[si];
+#pragma unroll
+        for (int q = 0; q < FS; ++q)
+            if (q == (num >> 6) && lane == (num & (kWave - 1))) { ns[q] = score; nt[q] = tie; }
+        if (rank + 1 < slot_get_i32(cn, depth - 1)) {
+            put(wq * kWave + wl, slot_get_f64(ns, parent) * sp, tree_tie(depth, parent, rank + 1));
             ++live;
         }
-        if (depth < B && s_cn[depth] > 0) {
-            put(nf++, score * c_p[depth * K], depth + 1, num, 0);
+        if (depth < B && slot_get_i32(cn, depth) > 0) {
+            put(nf++, score * slot_get_f64(p0, depth), tree_tie(depth + 1, num, 0));
             ++live;
         }
         ++num;
     }
     const int64_t ob = (int64_t)b * (V + 1);
-    for (int n = lane; n <= V; n += kWave) {
+#pragma unroll
+    for (int q = 0; q < FS; ++q) {
+        const int n = q * kWave + lane;
         const bool used = n < num;
-        o.node_token[ob + n] = used ? n_tok[n] : -1;
-        o.node_parent[ob + n] = used ? n_par[n] : -1;
-        o.node_depth[ob + n] = used ? n_dep[n] : -1;
-        if (o.node_score) o.node_score[ob + n] = used ? n_score[n] : 0.0;
+        const uint32_t t = nt[q];
+        const int depth = (int)(t >> 20), parent = (int)((t >> 12) & 0xFFu), rank = (int)(t & 0xFFFu);
+        int tok = -1, par = -1, dep = -1;
+        if (n == 0) { dep = 0; }
+        else if (used) { tok = c_id[(depth - 1) * K + rank]; par = parent; dep = depth; }
+        if (n <= V) {
+            o.node_token[ob + n] = tok;
+            o.node_parent[ob + n] = par;
+            o.node_depth[ob + n] = dep;
+            if (o.node_score) o.node_score[ob + n] = used ? ns[q] : 0.0;
+        }
     }
     if (lane == 0) o.num_nodes[b] = num;
 }

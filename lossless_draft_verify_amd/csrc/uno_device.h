@@ -134,6 +134,26 @@ __device__ __forceinline__ float wave_max_f32(float v)
 
 __device__ __forceinline__ int wave_first_lane(uint64_t mask) { return __ffsll((long long)mask) - 1; }
 
+// Wave-wide maximum / minimum of a u32, returned to every lane: within each
+// 16-lane row by DPP (swap neighbours, swap pairs, mirror halves, mirror the
+// row), then lane 15 of each row into the next row and lane 31 into rows 2-3,
+// which leaves the result in lane 63.  (The in-row steps have a source for
+// every lane, so their old value is never used and they fuse into one DPP op.)
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v)
+{
+    auto pick = [](uint32_t a, uint32_t b) __attribute__((always_inline)) {
+        return MAX ? (a > b ? a : b) : (a < b ? a : b);
+    };
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
 // Lane l's value of a double (l uniform).
 __device__ __forceinline__ double readlane_f64(double v, int l)
 {
