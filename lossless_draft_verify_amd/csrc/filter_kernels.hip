@@ -25,6 +25,7 @@ constexpr int kCap = 768;       // candidate entries per wave (12 per lane)
 constexpr int kCapE = kCap / 64;
 constexpr int kPerIter = 16;    // logits per lane per streaming iteration
 constexpr int kMaxK = 256;      // UNO_MAX_TOP_K
+constexpr int64_t kSegmentTarget = 1024;   // workgroups the top-k stream aims for (four per CU)
 
 // ---- candidate buffers and register-resident lists ----------------------------
 // A streaming candidate is (raw float bits of the logit, token id); keys are
@@ -334,8 +335,10 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t r = blockIdx.x;
-    const int seg = blockIdx.y;
+    // segments of one row are consecutive workgroups, so they run together
+    // and the dispatcher hands the next row's segments to whichever CUs free up
+    const int64_t r = blockIdx.x / S;
+    const int seg = (int)(blockIdx.x - r * S);
     const char* row = row_pointer(src, r, N * ESZ);
     if (row == nullptr) {
         if (S == 1 && threadIdx.x == 0) out.count[r] = -1;
@@ -778,12 +781,13 @@ __global__ void dense_row_stats_kernel(int64_t rows, double inv_T, DenseChunks d
 
 int topk_segments(int64_t rows, int64_t vocab, int k)
 {
-    // Enough workgroups for one full round over the chip (about 1024: four per
-    // CU, all resident at once) and no more: every segment pays a serial
-    // epilogue, which only overlaps other work when the round is not full.
-    // Segments keep >= 16384 logits (each wave streams several iterations) and
-    // the merged candidate list fits one merge workgroup.
-    int64_t S = (1024 + rows - 1) / rows;
+    // About kSegmentTarget workgroups: one full round over the chip, all
+    // resident at once.  More segments would balance CUs that stream at
+    // different rates, but each segment pays a serial epilogue and a split row
+    // a merge, which cost more than the balance gains on 151936-logit rows.
+    // A segment keeps >= 16384 logits (each wave streams several iterations)
+    // and the merged candidate list fits one merge workgroup.
+    int64_t S = (kSegmentTarget + rows - 1) / rows;
     const int64_t by_len = vocab / 16384;
     if (S > by_len) S = by_len;
     const int64_t by_merge = kMergeCap / (k > 0 ? k : 1);
@@ -801,7 +805,7 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
                               hipStream_t stream)
 {
     if (rows == 0) return hipSuccess;
-    dim3 grid((unsigned)rows, (unsigned)S);
+    dim3 grid((unsigned)(rows * S));
     if (bf16)
         topk_stream_kernel<true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
                                                                 part_id, part_n);
