@@ -480,11 +480,14 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     }
     for (int64_t it = 0; it < nfull; ++it) {
         const int64_t v0 = wb + it * kStep;
-        // unconditional prefetch (the last iteration re-reads its own vectors), so
-        // the number of loads in flight is the same on every path
-        const int64_t vn = (it + 1 < nfull) ? v0 + kStep : v0;
+        // unconditional prefetch, so the number of loads in flight is the same
+        // on every path; the last iteration's only keeps that shape (4-byte
+        // rows: one of its own vectors per u for every lane, a few cache lines
+        // instead of a re-read; 2-byte rows measured faster re-reading)
+        const bool more = it + 1 < nfull;
+        const typename V::T* pn = body + (more ? v0 + kStep : v0) + ((more || BF16) ? lane : 0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) xn[u] = V::load_stream(body + vn + u * kWave + lane);
+        for (int u = 0; u < U; ++u) xn[u] = V::load_stream(pn + u * kWave);
         process(xc, v0);
 #pragma unroll
         for (int u = 0; u < U; ++u) xc[u] = xn[u];

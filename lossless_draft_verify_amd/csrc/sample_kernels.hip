@@ -67,16 +67,25 @@ __device__ __forceinline__ void wave_sort_by_id(WaveRow& R, int n, int32_t* s_ke
     wave_sync();
     int rank[kQ] = {};
     int j = 0;
-    for (; j + 4 <= n; j += 4) {
-        const int32_t a0 = s_key[j], a1 = s_key[j + 1], a2 = s_key[j + 2], a3 = s_key[j + 3];
+    if (n <= kWave) {
+        // one entry per lane: only slot 0 holds entries
+        for (; j + 4 <= n; j += 4) {
+            const int32_t a0 = s_key[j], a1 = s_key[j + 1], a2 = s_key[j + 2], a3 = s_key[j + 3];
+            rank[0] += (a0 < R.id[0]) + (a1 < R.id[0]) + (a2 < R.id[0]) + (a3 < R.id[0]);
+        }
+        for (; j < n; ++j) rank[0] += (s_key[j] < R.id[0]);
+    } else {
+        for (; j + 4 <= n; j += 4) {
+            const int32_t a0 = s_key[j], a1 = s_key[j + 1], a2 = s_key[j + 2], a3 = s_key[j + 3];
 #pragma unroll
-        for (int q = 0; q < kQ; ++q)
-            rank[q] += (a0 < R.id[q]) + (a1 < R.id[q]) + (a2 < R.id[q]) + (a3 < R.id[q]);
-    }
-    for (; j < n; ++j) {
-        const int32_t a = s_key[j];
+            for (int q = 0; q < kQ; ++q)
+                rank[q] += (a0 < R.id[q]) + (a1 < R.id[q]) + (a2 < R.id[q]) + (a3 < R.id[q]);
+        }
+        for (; j < n; ++j) {
+            const int32_t a = s_key[j];
 #pragma unroll
-        for (int q = 0; q < kQ; ++q) rank[q] += (a < R.id[q]);
+            for (int q = 0; q < kQ; ++q) rank[q] += (a < R.id[q]);
+        }
     }
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
@@ -129,8 +138,8 @@ __device__ __forceinline__ int32_t wave_sample_sorted(const WaveRow& R, int n, d
             const uint64_t m = __ballot(q * kWave + lane < n && cum[q * kWave + lane] > t);
             if (m) {
                 const int src = wave_first_lane(m);
-                *wpick = __shfl(R.w[q], src, kWave);
-                pick = __shfl(R.id[q], src, kWave);
+                *wpick = readlane_f64(R.w[q], src);
+                pick = __builtin_amdgcn_readlane(R.id[q], src);
                 found = true;
             }
         }
@@ -140,8 +149,8 @@ __device__ __forceinline__ int32_t wave_sample_sorted(const WaveRow& R, int n, d
             const uint64_t m = __ballot(q * kWave + lane < n && R.w[q] > 0.0);
             if (m) {
                 const int src = 63 - __clzll((long long)m);
-                *wpick = __shfl(R.w[q], src, kWave);
-                pick = __shfl(R.id[q], src, kWave);
+                *wpick = readlane_f64(R.w[q], src);
+                pick = __builtin_amdgcn_readlane(R.id[q], src);
                 found = true;
             }
         }
@@ -158,7 +167,7 @@ __device__ __forceinline__ double reg_lookup(const WaveRow& R, int n, int32_t y,
     for (int q = 0; q < kQ; ++q) {
         if (q * kWave >= n) break;
         const uint64_t m = __ballot(q * kWave + lane < n && R.id[q] == y);
-        if (m) v = __shfl(R.w[q], wave_first_lane(m), kWave);
+        if (m) v = readlane_f64(R.w[q], wave_first_lane(m));
     }
     return v;
 }
