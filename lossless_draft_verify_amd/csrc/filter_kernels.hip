@@ -192,15 +192,46 @@ __device__ __forceinline__ uint64_t order_key(uint32_t key, int32_t id)
 // o*stride + cnt[o]) in LDS, entries (key, id), distinct ids): the entry at
 // filter-order position r < k goes to sk/sid[r], and, when se is given, its
 // softmax numerator exp((z - m) / T) to se[r] (m: the largest key's logit).
-// Returns min(total, k).
+// Returns min(total, k).  Every thread calls it.  With at most kOkCap
+// candidates (the usual case) their order keys are first gathered into ok (LDS
+// scratch of kOkCap words, free during the rank) and each rank is a count over
+// that one array; otherwise every comparison reads the lists.
+constexpr int kOkCap = kMaxK + 1;
 template <int L>
 __device__ __forceinline__ int block_rank_topk(const uint2* lst, int stride, const int* cnt, int k, uint32_t* sk,
                                                int32_t* sid, double* se, double m, double Td, int tid,
-                                               int nthreads)
+                                               int nthreads, uint64_t* ok)
 {
     int n = 0;
 #pragma unroll
     for (int o = 0; o < L; ++o) n += cnt[o];
+    auto place = [&](uint64_t p, int rank) __attribute__((always_inline)) {
+        if (rank < k) {
+            const uint32_t key = (uint32_t)(p >> 32);
+            sk[rank] = key;
+            sid[rank] = (int32_t)~(uint32_t)p;
+            if (se) se[rank] = exp(((double)key_float(key) - m) / Td);
+        }
+    };
+    if (n <= kOkCap) {
+        for (int g = tid; g < n; g += nthreads) {
+            int o = 0, i = g;
+            while (i >= cnt[o]) { i -= cnt[o]; ++o; }
+            const uint2 c = lst[o * stride + i];
+            ok[g] = order_key(c.x, (int32_t)c.y);
+        }
+        __syncthreads();
+        for (int g = tid; g < n; g += nthreads) {
+            const uint64_t p = ok[g];
+            int rank = 0;
+            int j = 0;
+            for (; j + 4 <= n; j += 4)
+                rank += (ok[j] > p) + (ok[j + 1] > p) + (ok[j + 2] > p) + (ok[j + 3] > p);
+            for (; j < n; ++j) rank += (ok[j] > p);
+            place(p, rank);
+        }
+        return n < k ? n : k;
+    }
     for (int g = tid; g < n; g += nthreads) {
         int o = 0, i = g;
         while (i >= cnt[o]) { i -= cnt[o]; ++o; }
@@ -210,20 +241,16 @@ __device__ __forceinline__ int block_rank_topk(const uint2* lst, int stride, con
 #pragma unroll
         for (int o2 = 0; o2 < L; ++o2) {
             const uint2* a = lst + o2 * stride;
-            const int m = cnt[o2];
+            const int mo = cnt[o2];
             int j = 0;
-            for (; j + 4 <= m; j += 4) {
+            for (; j + 4 <= mo; j += 4) {
                 const uint2 a0 = a[j], a1 = a[j + 1], a2 = a[j + 2], a3 = a[j + 3];
                 rank += (order_key(a0.x, (int32_t)a0.y) > p) + (order_key(a1.x, (int32_t)a1.y) > p) +
                         (order_key(a2.x, (int32_t)a2.y) > p) + (order_key(a3.x, (int32_t)a3.y) > p);
             }
-            for (; j < m; ++j) rank += (order_key(a[j].x, (int32_t)a[j].y) > p);
+            for (; j < mo; ++j) rank += (order_key(a[j].x, (int32_t)a[j].y) > p);
         }
-        if (rank < k) {
-            sk[rank] = c.x;
-            sid[rank] = (int32_t)c.y;
-            if (se) se[rank] = exp(((double)key_float(c.x) - m) / Td);
-        }
+        place(p, rank);
     }
     return n < k ? n : k;
 }
@@ -562,7 +589,8 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     const int rot = (int)(blockIdx.x & (kWaves - 1));
     const int trot = (int)((threadIdx.x + rot * kWave) & (kThreads - 1));
     const int n = block_rank_topk<kWaves>(s_buf, kCap, s_ns, k, s_sk, s_sid, want_e ? s_e : nullptr,
-                                          (double)key_float(top), (double)fp.temperature, trot, kThreads);
+                                          (double)key_float(top), (double)fp.temperature, trot, kThreads,
+                                          reinterpret_cast<uint64_t*>(s_cx));
     __syncthreads();
     if (S == 1) {
         if (w == rot) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane, s_scal, s_cx);
@@ -665,7 +693,8 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     }
     __syncthreads();
     const int n = block_rank_topk<1>(s_cand, 0, &s_n, k, s_sk, s_sid, fp.greedy ? nullptr : s_e,
-                                     (double)key_float(top), (double)fp.temperature, threadIdx.x, kThreads);
+                                     (double)key_float(top), (double)fp.temperature, threadIdx.x, kThreads,
+                                     reinterpret_cast<uint64_t*>(s_cx));
     __syncthreads();
     if (threadIdx.x < kWave) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane, s_scal, s_cx);
 }
