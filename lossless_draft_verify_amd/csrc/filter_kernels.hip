@@ -700,7 +700,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
 }
 
 // ---- dense chunk statistics --------------------------------------------------
-template <bool BF16>
+template <bool BF16, bool COUNT>
 __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
     RowSource src, int64_t rows, int64_t N, double log2e_over_T, int64_t exact_rows, DenseChunks dc)
 {
@@ -709,72 +709,113 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
     constexpr int PER_LANE = kDenseChunk / kWave;          // 32 logits per lane
     constexpr int NV = PER_LANE / EPV;                      // vectors per lane
     __shared__ double s_exp2[kExp2Entries];
-    load_exp2_table(s_exp2);
-    __syncthreads();
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r = blockIdx.x;
     const int nc = dc.nchunks;
+    // rows below exact_rows take the exact (fp64-bound) sums, the rest the fast
+    // ones, which need no table
+    const bool exact = r < exact_rows;
+    if (exact) load_exp2_table(s_exp2);
+    __syncthreads();
     const char* row = row_pointer(src, r, N * ESZ);
     if (row == nullptr) {
         for (int c = w; c < nc; c += kWaves)
             if (lane == 0) {
                 const int64_t slot = r * nc + c;
-                dc.cmax[slot] = -INFINITY; dc.csum[slot] = 0.0; dc.ccount[slot] = 0;
+                dc.cmax[slot] = -INFINITY; dc.csum[slot] = 0.0;
+                if (COUNT) dc.ccount[slot] = 0;
             }
         return;
     }
     const DenseExp ex{ log2e_over_T, s_exp2 };
-    // whole chunks of a 16-byte aligned row are loaded as vectors (other waves
-    // of the CU cover the load latency: the pass is bound by its fp64 work)
+    // whole chunks of a 16-byte aligned row are loaded as vectors, the next
+    // chunk of this wave while the current one is summed
     const bool aligned = (((uintptr_t)row) & 15u) == 0;
     const int nvec_chunks = aligned ? (int)(N / kDenseChunk) : 0;
-    auto load_vec = [&](int c, typename V::T (&v)[NV]) __attribute__((always_inline)) {
-        const typename V::T* p = reinterpret_cast<const typename V::T*>(row + (int64_t)c * kDenseChunk * ESZ);
+    // vectors of chunk c (all lanes read one vector per j when `shape` only:
+    // a load that keeps the pipeline's shape at its end)
+    auto load_vec = [&](int c, typename V::T (&v)[NV], bool shape) __attribute__((always_inline)) {
+        const typename V::T* p = reinterpret_cast<const typename V::T*>(row + (int64_t)c * kDenseChunk * ESZ) +
+                                 (shape ? 0 : lane);
 #pragma unroll
-        for (int j = 0; j < NV; ++j) v[j] = V::load_stream(p + j * kWave + lane);
+        for (int j = 0; j < NV; ++j) v[j] = V::load_stream(p + j * kWave);
     };
     // statistics of one chunk held as x[PER_LANE] (element (j*64 + lane)*EPV + e
-    // at x[j*EPV + e]); rows from exact_rows on take the fast sums
-    const bool exact = r < exact_rows;
+    // at x[j*EPV + e])
     const float log2e_over_T32 = (float)log2e_over_T;
     auto chunk_stats = [&](int c, const float (&x)[PER_LANE]) __attribute__((always_inline)) {
         float mx;
         double s;
         uint32_t cntf;
-        if (exact) chunk_stats_exact(x, ex, &mx, &s, &cntf);
-        else chunk_stats_fast(x, log2e_over_T32, &mx, &s, &cntf);
+        if (exact) chunk_stats_exact<COUNT>(x, ex, &mx, &s, &cntf);
+        else chunk_stats_fast<COUNT>(x, log2e_over_T32, &mx, &s, &cntf);
         if (lane == 0) {
             const int64_t slot = r * nc + c;
             dc.cmax[slot] = mx;
             dc.csum[slot] = (mx < INFINITY) ? s : NAN;
-            dc.ccount[slot] = (int32_t)cntf;
+            if (COUNT) dc.ccount[slot] = (int32_t)cntf;
         }
     };
     int c = w;
-    for (; c < nvec_chunks; c += kWaves) {
-        typename V::T cur[NV];
-        load_vec(c, cur);
-        float x[PER_LANE];
+    if (c < nvec_chunks) {
+        typename V::T cur[NV], nxt[NV];
+        load_vec(c, cur, false);
+        for (;;) {
+            const int cn = c + kWaves;
+            const bool more = cn < nvec_chunks;
+            load_vec(more ? cn : c, nxt, !more);
+            float x[PER_LANE];
 #pragma unroll
-        for (int j = 0; j < NV; ++j)
+            for (int j = 0; j < NV; ++j)
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) x[j * EPV + e] = V::get(cur[j], e);
-        chunk_stats(c, x);
+                for (int e = 0; e < EPV; ++e) x[j * EPV + e] = V::get(cur[j], e);
+            chunk_stats(c, x);
+            c = cn;
+            if (!more) break;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) cur[j] = nxt[j];
+        }
     }
-    // remaining chunks (ragged tail, or a row off 16-byte alignment) element by element
+    // remaining chunks (ragged tail, or a row off 16-byte alignment) element by
+    // element, element i of the chunk in lane i % 64: one pass for the maximum,
+    // one (reloading) for the count and the sum, in loops that keep this rare
+    // path from setting the kernel's register count
     for (; c < nc; c += kWaves) {
         const int64_t beg = (int64_t)c * kDenseChunk;
-        const int64_t n = (N - beg < kDenseChunk) ? (N - beg) : kDenseChunk;
-        float x[PER_LANE];
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const int64_t i = (int64_t)(j * kWave + lane) * EPV + e;
-                x[j * EPV + e] = (i < n) ? load_scalar<BF16>(row, beg + i) : -INFINITY;
+        const int n = (int)((N - beg < kDenseChunk) ? (N - beg) : kDenseChunk);
+        const char* base = row + beg * ESZ;
+        float mx = -INFINITY;
+#pragma unroll 1
+        for (int i = lane; i < n; i += kWave) mx = fmaxf(mx, load_scalar<BF16>(base, i));
+        mx = wave_max_f32(mx);
+        double sum = 0.0;
+        uint32_t cntf = 0;
+        if (mx > -INFINITY && mx < INFINITY) {
+            const double md = (double)mx;
+#pragma unroll 1
+            for (int i0 = 0; i0 < n; i0 += kWave) {
+                const int i = i0 + lane;
+                const float v = i < n ? load_scalar<BF16>(base, i) : -INFINITY;
+                if (COUNT) cntf += (uint32_t)__popcll(__ballot(finite_f32(v)));
+                if (i < n) {
+                    // as in the whole-chunk sums: NaN and -inf add a vanishing term
+                    if (exact) {
+                        sum += ex((double)v - md);
+                    } else {
+                        const float y = (fmaxf(v, -3.0e38f) - mx) * log2e_over_T32;
+                        sum += (double)__builtin_amdgcn_exp2f(fmaxf(y, -200.0f));
+                    }
+                }
             }
-        chunk_stats(c, x);
+        }
+        sum = wave_sum_f64(sum);
+        if (lane == 0) {
+            const int64_t slot = r * nc + c;
+            dc.cmax[slot] = mx;
+            dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
+            if (COUNT) dc.ccount[slot] = (int32_t)cntf;
+        }
     }
 }
 
@@ -857,10 +898,15 @@ hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab
     if (rows == 0) return hipSuccess;
     const double c = 1.4426950408889634074 / (double)temperature;
     dim3 grid((unsigned)rows);
-    if (bf16)
-        dense_chunk_kernel<true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
+    const bool counts = dc.ccount != nullptr;
+    if (bf16 && counts)
+        dense_chunk_kernel<true, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
+    else if (bf16)
+        dense_chunk_kernel<true, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
+    else if (counts)
+        dense_chunk_kernel<false, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
     else
-        dense_chunk_kernel<false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
+        dense_chunk_kernel<false, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
     return hipGetLastError();
 }
 

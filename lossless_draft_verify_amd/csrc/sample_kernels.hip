@@ -893,12 +893,12 @@ __global__ __launch_bounds__(kDenseThreads) void dense_exact_row_kernel(
     float mx;
     double sum;
     uint32_t cntf;
-    chunk_stats_exact(x, ex, &mx, &sum, &cntf);
+    chunk_stats_exact<true>(x, ex, &mx, &sum, &cntf);
     if (lane == 0) {
         const int64_t slot = pr * nc + c;
         dc.cmax[slot] = mx;
         dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
-        dc.ccount[slot] = (int32_t)cntf;
+        if (dc.ccount) dc.ccount[slot] = (int32_t)cntf;
     }
 }
 

@@ -94,13 +94,15 @@ void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool ow
     }
 }
 
-DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab)
+// Chunk statistics; the finite counts only for uno_filter, whose dense mode
+// reports each row's support size (the samplers never read them).
+DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts)
 {
     DenseChunks dc;
     dc.nchunks = dense_nchunks(vocab);
     dc.cmax = cv.take<float>((size_t)rows * dc.nchunks);
     dc.csum = cv.take<double>((size_t)rows * dc.nchunks);
-    dc.ccount = cv.take<int32_t>((size_t)rows * dc.nchunks);
+    dc.ccount = counts ? cv.take<int32_t>((size_t)rows * dc.nchunks) : nullptr;
     return dc;
 }
 
@@ -160,7 +162,7 @@ int layout_filter(int64_t rows, int64_t vocab, int32_t dtype, const uno_sampling
     if (st) return st;
     if (rows == 0) return UNO_OK;
     if (m->sparse) carve_sparse(cv, rows, vocab, *m, false, sw);
-    else *dc = carve_chunks(cv, rows, vocab);
+    else *dc = carve_chunks(cv, rows, vocab, true);
     return UNO_OK;
 }
 
@@ -177,7 +179,7 @@ int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const 
     if (m->sparse) {
         carve_sparse(cv, rows, vocab, *m, true, sw);
     } else {
-        *dc = carve_chunks(cv, rows, vocab);
+        *dc = carve_chunks(cv, rows, vocab, false);
         *ds = carve_dense_scratch(cv, rows, (int32_t)batch, B, dc->nchunks);
     }
     return UNO_OK;

@@ -290,8 +290,11 @@ struct DenseExp {
 // over the chunk and the number of finite logits.  With no finite logit the
 // sum is 0; with +inf the max is +inf (the caller marks the row invalid).
 
+// The finite count costs a compare and a ballot per logit, so it is taken
+// only when COUNT is set (*cnt_out is 0 otherwise).
+
 // Exact: every term from DenseExp.
-template <int PER_LANE>
+template <bool COUNT, int PER_LANE>
 __device__ __forceinline__ void chunk_stats_exact(const float (&x)[PER_LANE], const DenseExp& ex, float* m_out,
                                                   double* s_out, uint32_t* cnt_out)
 {
@@ -299,27 +302,34 @@ __device__ __forceinline__ void chunk_stats_exact(const float (&x)[PER_LANE], co
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) mx = fmaxf(mx, x[i]);
     mx = wave_max_f32(mx);
-    double s = 0.0;
+    double s0 = 0.0, s1 = 0.0;
     uint32_t cntf = 0;
     if (mx > -INFINITY && mx < INFINITY) {
         const double md = (double)mx;
+        // groups of eight exps (two sums) bound how many are in flight, and
+        // with them the registers
 #pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) {
-            // NaN and -inf reach the exp's lower clamp, whose term (2^-1000)
-            // vanishes next to the chunk maximum's 1
-            cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
-            s += ex((double)x[i] - md);
+        for (int g = 0; g < PER_LANE; g += 8) {
+#pragma unroll
+            for (int i = g; i < g + 8; ++i) {
+                // NaN and -inf reach the exp's lower clamp, whose term (2^-1000)
+                // vanishes next to the chunk maximum's 1
+                if (COUNT) cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
+                const double e = ex((double)x[i] - md);
+                if (i & 1) s1 += e; else s0 += e;
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     *m_out = mx;
-    *s_out = wave_sum_f64(s);
+    *s_out = wave_sum_f64(s0 + s1);
     *cnt_out = cntf;
 }
 
 // Fast: terms from the fp32 exponential (relative error near 1e-7), summed in
 // fp64.  Good enough for a normaliser that only enters a probability ratio;
 // never used where a CDF is inverted.
-template <int PER_LANE>
+template <bool COUNT, int PER_LANE>
 __device__ __forceinline__ void chunk_stats_fast(const float (&x)[PER_LANE], float log2e_over_T, float* m_out,
                                                  double* s_out, uint32_t* cnt_out)
 {
@@ -332,7 +342,7 @@ __device__ __forceinline__ void chunk_stats_fast(const float (&x)[PER_LANE], flo
     if (mx > -INFINITY && mx < INFINITY) {
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i) {
-            cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
+            if (COUNT) cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
             // fmaxf maps NaN to the large negative bound; its term is 0
             const float y = (fmaxf(x[i], -3.0e38f) - mx) * log2e_over_T;
             s += (double)__builtin_amdgcn_exp2f(fmaxf(y, -200.0f));

@@ -42,7 +42,7 @@ struct SparseOut {
 struct DenseChunks {
     float* cmax;       // [rows][nchunks]
     double* csum;      // [rows][nchunks]
-    int32_t* ccount;   // [rows][nchunks]
+    int32_t* ccount;   // [rows][nchunks], or nullptr when no caller needs the counts
     int32_t nchunks;
 };
 

@@ -71,10 +71,14 @@ def test_workspace_sizes(lib):
     # linear 8/1/8 b64 sparse: supports only (k = 50) for 1088 rows, no segment partials
     st, n = _ws(lib, uno.OP_SAMPLE_LINEAR, 64, 8, 1, 8, N, F32, sp())
     assert st == OK and n >= 1088 * 50 * (4 + 8) + 1088 * 4
-    # dense linear: chunk statistics for every row dominate
+    # dense linear: chunk statistics (max and sum, no finite counts: the
+    # samplers never read them) for every row dominate
     st, nd = _ws(lib, uno.OP_SAMPLE_LINEAR, 256, 16, 1, 16, N, BF16, sp(0.7, 0, 1.0))
     nch = math.ceil(N / 2048)
-    assert st == OK and nd >= 256 * 33 * nch * (4 + 8 + 4)
+    assert st == OK and nd >= 256 * 33 * nch * (4 + 8)
+    # dense filter: the counts too (each row's support size)
+    st, ndf = _ws(lib, uno.OP_FILTER, 1000, 0, 0, 0, N, BF16, sp(0.7, 0, 1.0))
+    assert st == OK and ndf >= 1000 * nch * (4 + 8 + 4)
     # few rows -> segmented rows need partial lists
     st, nt = _ws(lib, uno.OP_BUILD_TREE, 1, 16, 32, 32, N, F32, sp())
     assert st == OK and nt > 16 * 50 * 12
