@@ -260,12 +260,16 @@ __device__ __forceinline__ int block_rank_topk(const uint2* lst, int stride, con
 // normaliser summed in filter order, pi = e / S, cumulative pi in filter
 // order, kept probabilities pi / (kept mass) when top-p is on.  se holds the
 // numerators e in filter order (LDS, overwritten with pi); s_cx receives the
-// cumulative sums (n + 1 entries).  The two in-order sums run in one lane over
+// cumulative sums (n + 1 entries).  The in-order sums run in one lane over
 // LDS -- one add per step -- and everything else across the wave.
-__device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* sid, double* se, int n,
+// With out.cum the support is written in ascending id order with its
+// inclusive cumulative sums in that order (sk, whose keys are consumed by
+// then, serves as the id scratch).
+__device__ __forceinline__ void finalize_row(uint32_t* sk, const int32_t* sid, double* se, int n,
                                              const FilterParams fp, const SparseOut out, int64_t r, int lane,
                                              double* s_scal, double* s_cx)
 {
+    double* oc = out.cum ? out.cum + r * out.cap : nullptr;
     int32_t* oid = out.ids + r * out.cap;
     double* op = out.probs + r * out.cap;
     int n_out;
@@ -276,7 +280,11 @@ __device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* 
         n_out = 1;
         m = (double)key_float(sk[0]);
         S = 1.0;
-        if (lane == 0) { oid[0] = sid[0]; op[0] = 1.0; }
+        if (lane == 0) {
+            oid[0] = sid[0];
+            op[0] = 1.0;
+            if (oc) oc[0] = 1.0;
+        }
     } else {
         m = (double)key_float(sk[0]);
         if (lane == 0) {
@@ -312,6 +320,7 @@ __device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* 
             }
             c = s_cx[n_keep];
         }
+        // the kept entries with positive probability: a prefix in filter order
         int npos = 0;
         for (int base = 0; base < n_keep; base += kWave) {
             const int i = base + lane;
@@ -319,13 +328,51 @@ __device__ __forceinline__ void finalize_row(const uint32_t* sk, const int32_t* 
             if (i < n_keep) v = fp.topp_on ? se[i] / c : se[i];
             const bool pos = (i < n_keep) && v > 0.0;
             npos += __popcll(__ballot(pos));
-            if (pos) { oid[i] = sid[i]; op[i] = v; }
+            if (!oc) {
+                if (pos) { oid[i] = sid[i]; op[i] = v; }
+            } else if (i < n_keep) {
+                se[i] = v;
+            }
+        }
+        if (oc) {
+            // id order: an entry's position counts the smaller ids among the kept
+            int32_t* s_id = reinterpret_cast<int32_t*>(sk);
+            wave_sync();
+            for (int base = 0; base < npos; base += kWave) {
+                const int i = base + lane;
+                if (i < npos) {
+                    const int32_t id = sid[i];
+                    int rank = 0;
+                    int j = 0;
+                    for (; j + 4 <= npos; j += 4)
+                        rank += (sid[j] < id) + (sid[j + 1] < id) + (sid[j + 2] < id) + (sid[j + 3] < id);
+                    for (; j < npos; ++j) rank += (sid[j] < id);
+                    s_cx[rank] = se[i];
+                    s_id[rank] = id;
+                }
+            }
+            wave_sync();
+            if (lane == 0) {
+                double acc = 0.0;
+#pragma unroll 8
+                for (int j = 0; j < npos; ++j) {
+                    acc += s_cx[j];
+                    se[j] = acc;
+                }
+            }
+            wave_sync();
+            for (int j = lane; j < npos; j += kWave) {
+                oid[j] = s_id[j];
+                op[j] = s_cx[j];
+                oc[j] = se[j];
+            }
         }
         n_out = npos;
     }
     for (int i = (n_out > 0 ? n_out : 0) + lane; i < out.cap; i += kWave) {
         oid[i] = -1;
         op[i] = 0.0;
+        if (oc) oc[i] = 0.0;
     }
     if (lane == 0) {
         out.count[r] = n_out;

@@ -34,12 +34,13 @@ constexpr int kQ = kMaxK / kWave;      // support entries per lane
 struct WaveRow {
     int32_t id[kQ];
     double w[kQ];
+    double c[kQ];      // inclusive cumulative sums in id order (supports that carry them)
 };
 
 // Load the n <= cap <= 256 entries of a support (unordered); slots past n hold
 // id INT32_MAX, weight 0.
-__device__ __forceinline__ void wave_load_support(const int32_t* ids, const double* p, int n, int cap, WaveRow& R,
-                                                  int lane)
+__device__ __forceinline__ void wave_load_support(const int32_t* ids, const double* p, const double* cum, int n,
+                                                  int cap, WaveRow& R, int lane)
 {
     // every slot below cap is read (the filter pads supports to cap), so the
     // loads do not wait for the count
@@ -47,58 +48,16 @@ __device__ __forceinline__ void wave_load_support(const int32_t* ids, const doub
     for (int q = 0; q < kQ; ++q) {
         const int i = q * kWave + lane;
         int32_t id = 0x7FFFFFFF;
-        double w = 0.0;
-        if (q * kWave < cap && i < cap) { id = ids[i]; w = p[i]; }
+        double w = 0.0, c = 0.0;
+        if (q * kWave < cap && i < cap) {
+            id = ids[i];
+            w = p[i];
+            if (cum) c = cum[i];
+        }
         R.id[q] = (i < n) ? id : 0x7FFFFFFF;
         R.w[q] = (i < n) ? w : 0.0;
+        R.c[q] = (i < n) ? c : 0.0;
     }
-}
-
-// Reorder the n entries of R by ascending id (ids distinct), through the
-// wave's LDS scratch (s_key, s_id: kMaxK ints; s_w: kMaxK doubles).
-__device__ __forceinline__ void wave_sort_by_id(WaveRow& R, int n, int32_t* s_key, int32_t* s_id, double* s_w,
-                                                int lane)
-{
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-        const int i = q * kWave + lane;
-        if (q * kWave < n && i < n) s_key[i] = R.id[q];
-    }
-    wave_sync();
-    int rank[kQ] = {};
-    int j = 0;
-    if (n <= kWave) {
-        // one entry per lane: only slot 0 holds entries
-        for (; j + 4 <= n; j += 4) {
-            const int32_t a0 = s_key[j], a1 = s_key[j + 1], a2 = s_key[j + 2], a3 = s_key[j + 3];
-            rank[0] += (a0 < R.id[0]) + (a1 < R.id[0]) + (a2 < R.id[0]) + (a3 < R.id[0]);
-        }
-        for (; j < n; ++j) rank[0] += (s_key[j] < R.id[0]);
-    } else {
-        for (; j + 4 <= n; j += 4) {
-            const int32_t a0 = s_key[j], a1 = s_key[j + 1], a2 = s_key[j + 2], a3 = s_key[j + 3];
-#pragma unroll
-            for (int q = 0; q < kQ; ++q)
-                rank[q] += (a0 < R.id[q]) + (a1 < R.id[q]) + (a2 < R.id[q]) + (a3 < R.id[q]);
-        }
-        for (; j < n; ++j) {
-            const int32_t a = s_key[j];
-#pragma unroll
-            for (int q = 0; q < kQ; ++q) rank[q] += (a < R.id[q]);
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-        const int i = q * kWave + lane;
-        if (q * kWave < n && i < n) { s_id[rank[q]] = R.id[q]; s_w[rank[q]] = R.w[q]; }
-    }
-    wave_sync();
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-        const int i = q * kWave + lane;
-        if (q * kWave < n && i < n) { R.id[q] = s_id[i]; R.w[q] = s_w[i]; }
-    }
-    wave_sync();
 }
 
 // Inverse CDF over the n id-ordered entries of R with uniform u: the first
@@ -159,6 +118,48 @@ __device__ __forceinline__ int32_t wave_sample_sorted(const WaveRow& R, int n, d
     return pick;
 }
 
+// Inverse CDF over the n id-ordered entries of R whose inclusive cumulative
+// sums R.c came with the support (the filter takes them in id order, one add
+// per step, exactly as wave_sample_sorted would): the same rule, with the
+// pick a ballot and W the last sum.
+__device__ __forceinline__ int32_t wave_sample_cum(const WaveRow& R, int n, double u, double* wpick, int lane)
+{
+    *wpick = 0.0;
+    if (n <= 0) return -1;
+    double W = 0.0;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+        if (((n - 1) >> 6) == q) W = readlane_f64(R.c[q], (n - 1) & (kWave - 1));
+    int32_t pick = -1;
+    if (W > 0.0) {
+        const double t = u * W;
+        bool found = false;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            if (q * kWave >= n || found) break;
+            const uint64_t m = __ballot(q * kWave + lane < n && R.c[q] > t);
+            if (m) {
+                const int src = wave_first_lane(m);
+                *wpick = readlane_f64(R.w[q], src);
+                pick = __builtin_amdgcn_readlane(R.id[q], src);
+                found = true;
+            }
+        }
+#pragma unroll
+        for (int q = kQ - 1; q >= 0; --q) {
+            if (found) break;
+            const uint64_t m = __ballot(q * kWave + lane < n && R.w[q] > 0.0);
+            if (m) {
+                const int src = 63 - __clzll((long long)m);
+                *wpick = readlane_f64(R.w[q], src);
+                pick = __builtin_amdgcn_readlane(R.id[q], src);
+                found = true;
+            }
+        }
+    }
+    return pick;
+}
+
 // Weight of token y in a wave's register support (0 when absent).
 __device__ __forceinline__ double reg_lookup(const WaveRow& R, int n, int32_t y, int lane)
 {
@@ -174,7 +175,6 @@ __device__ __forceinline__ double reg_lookup(const WaveRow& R, int n, int32_t y,
 
 // Per-wave LDS scratch for sorting one support.
 struct SortScratch {
-    int32_t key[kMaxK];
     int32_t id[kMaxK];
     double w[kMaxK];
     double cum[kMaxK];
@@ -205,8 +205,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     int32_t batch, int32_t B, SparseOut sup, uint64_t seed, uint64_t offset,
     const uint32_t* req_ids, LinearOut o)
 {
-    __shared__ SortScratch s_q[kLinWaves];     // q_j, left id-sorted for the residual
-    __shared__ SortScratch s_p[kLinWaves];
+    __shared__ SortScratch s_q[kLinWaves];     // q_j in id order for the residual's lookups; its cumulative sums
     __shared__ int32_t s_y[kMaxLinearB];
     __shared__ int32_t s_acc[kMaxLinearB];
     __shared__ int32_t s_fin[kMaxLinearB + 1];
@@ -228,18 +227,14 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
         const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
         const int64_t pr = pbase + j;
         const int np = sup.count[pr];
-        WaveRow P;                       // p_j, loaded up front
-        wave_load_support(sup.ids + pr * cap, sup.probs + pr * cap, np, cap, P, lane);
+        WaveRow P;                       // p_j (id order, with its cumulative sums), loaded up front
+        wave_load_support(sup.ids + pr * cap, sup.probs + pr * cap, sup.cum + pr * cap, np, cap, P, lane);
         int32_t fin = -1;
         uint32_t ffl = 0;
         if (j == B) {                    // bonus draw
             double dummy;
-            if (np > 0) {
-                wave_sort_by_id(P, np, s_p[w].key, s_p[w].id, s_p[w].w, lane);
-                fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane, s_p[w].cum);
-            } else {
-                ffl = 1u;
-            }
+            if (np > 0) fin = wave_sample_cum(P, np, d.u[2], &dummy, lane);
+            else ffl = 1u;
             if (lane == 0) { s_fin[j] = fin; s_ffl[j] = ffl; }
             continue;
         }
@@ -248,13 +243,9 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
         int32_t y = -1;
         double qy = 0.0;
         WaveRow Q;
-        wave_load_support(sup.ids + qr * cap, sup.probs + qr * cap, nq, cap, Q, lane);
-        if (nq > 0) {
-            wave_sort_by_id(Q, nq, s_q[w].key, s_q[w].id, s_q[w].w, lane);   // q stays id-sorted in s_q
-            y = wave_sample_sorted(Q, nq, d.u[0], &qy, lane, s_q[w].cum);
-        } else {
-            flags |= 1u;
-        }
+        wave_load_support(sup.ids + qr * cap, sup.probs + qr * cap, sup.cum + qr * cap, nq, cap, Q, lane);
+        if (nq > 0) y = wave_sample_cum(Q, nq, d.u[0], &qy, lane);
+        else flags |= 1u;
         int acc = 0;
         if (y >= 0) {
             double py = 0.0;
@@ -267,8 +258,14 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
             // over p's support (ids outside it have zero residual)
             double dummy;
             if (np > 0) {
-                wave_sort_by_id(P, np, s_p[w].key, s_p[w].id, s_p[w].w, lane);
+                // q's entries in LDS (already in id order) for the lookups
                 const int nqq = nq > 0 ? nq : 0;
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) {
+                    const int i = q * kWave + lane;
+                    if (q * kWave < nqq && i < nqq) { s_q[w].id[i] = Q.id[q]; s_q[w].w[i] = Q.w[q]; }
+                }
+                wave_sync();
                 WaveRow Rz = P;
 #pragma unroll
                 for (int q = 0; q < kQ; ++q) {
@@ -277,10 +274,10 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
                     const double dlt = P.w[q] - qv;
                     Rz.w[q] = dlt > 0.0 ? dlt : 0.0;
                 }
-                fin = wave_sample_sorted(Rz, np, d.u[2], &dummy, lane, s_p[w].cum);
+                fin = wave_sample_sorted(Rz, np, d.u[2], &dummy, lane, s_q[w].cum);
                 if (fin < 0) {
                     ffl = 2u;
-                    fin = wave_sample_sorted(P, np, d.u[2], &dummy, lane, s_p[w].cum);
+                    fin = wave_sample_cum(P, np, d.u[2], &dummy, lane);
                 }
             } else {
                 ffl = 1u;
@@ -491,7 +488,6 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     const uint32_t* req_ids, const int32_t* node_token, const int32_t* node_parent,
     const int32_t* num_nodes, WalkOut o)
 {
-    __shared__ SortScratch s_sort[kWalkWaves];
     __shared__ int32_t s_dep[kMaxNodes], s_t[kMaxNodes], s_tok[kMaxNodes], s_par[kMaxNodes];
     __shared__ int32_t s_anc[2][kMaxNodes], s_dist[2][kMaxNodes];
 
@@ -541,7 +537,8 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     bool live = false;
     if (w < nn) {
         live = node_live(w, &cnt);
-        wave_load_support(sup.ids + (ob + w) * cap, sup.probs + (ob + w) * cap, live ? cnt : 0, cap, R, lane);
+        wave_load_support(sup.ids + (ob + w) * cap, sup.probs + (ob + w) * cap, sup.cum + (ob + w) * cap,
+                          live ? cnt : 0, cap, R, lane);
     }
     for (int n = w; n < nn; n += kWalkWaves) {
         const int nx = n + kWalkWaves;
@@ -550,14 +547,14 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
         bool liven = false;
         if (nx < nn) {
             liven = node_live(nx, &cntn);
-            wave_load_support(sup.ids + (ob + nx) * cap, sup.probs + (ob + nx) * cap, liven ? cntn : 0, cap, Rn, lane);
+            wave_load_support(sup.ids + (ob + nx) * cap, sup.probs + (ob + nx) * cap, sup.cum + (ob + nx) * cap,
+                              liven ? cntn : 0, cap, Rn, lane);
         }
         int32_t t = -1;
         if (live) {
             const Draw d = uno_draw(seed, req, (uint32_t)s_dep[n], offset);
-            wave_sort_by_id(R, cnt, s_sort[w].key, s_sort[w].id, s_sort[w].w, lane);
             double dummy;
-            t = wave_sample_sorted(R, cnt, d.u[2], &dummy, lane, s_sort[w].cum);
+            t = wave_sample_cum(R, cnt, d.u[2], &dummy, lane);
         }
         if (lane == 0) s_t[n] = t;
         R = Rn;
@@ -1025,6 +1022,7 @@ hipError_t launch_linear_sparse(int32_t batch, int32_t B, const SparseOut& sup, 
                                 uint64_t offset, const uint32_t* request_ids, const LinearOut& o,
                                 hipStream_t stream)
 {
+    if (sup.cum == nullptr) return hipErrorInvalidValue;     // needs id-ordered supports
     linear_sparse_kernel<<<dim3((unsigned)batch), kLinThreads, 0, stream>>>(batch, B, sup, seed, offset,
                                                                            request_ids, o);
     return hipGetLastError();
@@ -1079,6 +1077,7 @@ hipError_t launch_tree_walk(int32_t batch, int32_t B, int32_t V, const SparseOut
                             const int32_t* node_parent, const int32_t* num_nodes, const WalkOut& o,
                             hipStream_t stream)
 {
+    if (sup.cum == nullptr) return hipErrorInvalidValue;     // needs id-ordered supports
     tree_walk_kernel<<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
         batch, B, V, sup, seed, offset, request_ids, node_token, node_parent, num_nodes, o);
     return hipGetLastError();

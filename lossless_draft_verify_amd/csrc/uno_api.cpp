@@ -73,8 +73,10 @@ struct SparseWs {
     int32_t* part_n;
 };
 
-// Supports (when own_supports) and segment partials for `rows` sparse rows.
-void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool own_supports, SparseWs* w)
+// Supports (when own_supports; in id order with cumulative sums when id_order)
+// and segment partials for `rows` sparse rows.
+void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool own_supports, bool id_order,
+                  SparseWs* w)
 {
     w->S = topk_segments(rows, vocab, m.k);
     if (own_supports) {
@@ -83,6 +85,7 @@ void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool ow
         w->sup.probs = cv.take<double>((size_t)rows * m.k);
         w->sup.count = cv.take<int32_t>((size_t)rows);
         w->sup.stats = nullptr;
+        w->sup.cum = id_order ? cv.take<double>((size_t)rows * m.k) : nullptr;
     }
     w->part_key = nullptr;
     w->part_id = nullptr;
@@ -161,7 +164,7 @@ int layout_filter(int64_t rows, int64_t vocab, int32_t dtype, const uno_sampling
     st = check_sampling(sp, vocab, m);
     if (st) return st;
     if (rows == 0) return UNO_OK;
-    if (m->sparse) carve_sparse(cv, rows, vocab, *m, false, sw);
+    if (m->sparse) carve_sparse(cv, rows, vocab, *m, false, false, sw);
     else *dc = carve_chunks(cv, rows, vocab, true);
     return UNO_OK;
 }
@@ -177,7 +180,7 @@ int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const 
     if (batch == 0) return UNO_OK;
     const int64_t rows = batch * (2 * (int64_t)B + 1);
     if (m->sparse) {
-        carve_sparse(cv, rows, vocab, *m, true, sw);
+        carve_sparse(cv, rows, vocab, *m, true, true, sw);
     } else {
         *dc = carve_chunks(cv, rows, vocab, false);
         *ds = carve_dense_scratch(cv, rows, (int32_t)batch, B, dc->nchunks);
@@ -198,7 +201,8 @@ int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int6
     if (!m->sparse) return UNO_ERR_UNSUPPORTED;      // dense tree sampling is not built
     if (batch == 0) return UNO_OK;
     const int64_t rows = batch * (op == UNO_OP_BUILD_TREE ? (int64_t)B : (int64_t)V + 1);
-    carve_sparse(cv, rows, vocab, *m, true, sw);
+    // the build reads its candidates in filter order, the walk samples in id order
+    carve_sparse(cv, rows, vocab, *m, true, op == UNO_OP_VERIFY_TREE, sw);
     return UNO_OK;
 }
 

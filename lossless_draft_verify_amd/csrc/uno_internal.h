@@ -35,6 +35,10 @@ struct SparseOut {
     int32_t* count;    // [rows]; -1 invalid row
     double* stats;     // [rows][2] (m, S) or nullptr
     int32_t cap;
+    // nullptr: ids/probs in filter order.  Otherwise [rows][cap]: the support
+    // is stored in ascending id order, with its inclusive cumulative sums taken
+    // in that order (the samplers' inverse CDF, computed once per row).
+    double* cum;
 };
 
 // Per-chunk statistics of dense rows: m_c = chunk max, s_c = sum over the
