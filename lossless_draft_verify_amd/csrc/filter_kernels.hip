@@ -760,6 +760,10 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r = blockIdx.x;
     const int nc = dc.nchunks;
+    // a row's chunks are dealt over gridDim.y workgroups (more than one when
+    // there are few rows), round robin over all their waves
+    const int c0 = (int)blockIdx.y * kWaves + w;
+    const int cstep = (int)gridDim.y * kWaves;
     // rows below exact_rows take the exact (fp64-bound) sums, the rest the fast
     // ones, which need no table
     const bool exact = r < exact_rows;
@@ -767,7 +771,7 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
     __syncthreads();
     const char* row = row_pointer(src, r, N * ESZ);
     if (row == nullptr) {
-        for (int c = w; c < nc; c += kWaves)
+        for (int c = c0; c < nc; c += cstep)
             if (lane == 0) {
                 const int64_t slot = r * nc + c;
                 dc.cmax[slot] = -INFINITY; dc.csum[slot] = 0.0;
@@ -804,12 +808,12 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
             if (COUNT) dc.ccount[slot] = (int32_t)cntf;
         }
     };
-    int c = w;
+    int c = c0;
     if (c < nvec_chunks) {
         typename V::T cur[NV], nxt[NV];
         load_vec(c, cur, false);
         for (;;) {
-            const int cn = c + kWaves;
+            const int cn = c + cstep;
             const bool more = cn < nvec_chunks;
             load_vec(more ? cn : c, nxt, !more);
             float x[PER_LANE];
@@ -828,7 +832,7 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
     // element, element i of the chunk in lane i % 64: one pass for the maximum,
     // one (reloading) for the count and the sum, in loops that keep this rare
     // path from setting the kernel's register count
-    for (; c < nc; c += kWaves) {
+    for (; c < nc; c += cstep) {
         const int64_t beg = (int64_t)c * kDenseChunk;
         const int n = (int)((N - beg < kDenseChunk) ? (N - beg) : kDenseChunk);
         const char* base = row + beg * ESZ;
@@ -944,7 +948,13 @@ hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab
 {
     if (rows == 0) return hipSuccess;
     const double c = 1.4426950408889634074 / (double)temperature;
-    dim3 grid((unsigned)rows);
+    // about two rounds of workgroups over the chip at least: few rows are
+    // split over several workgroups each (at most one chunk per wave)
+    const int64_t per_row_max = (dc.nchunks + kWaves - 1) / kWaves;
+    int64_t g = (2048 + rows - 1) / rows;
+    if (g > per_row_max) g = per_row_max;
+    if (g < 1) g = 1;
+    dim3 grid((unsigned)rows, (unsigned)g);
     const bool counts = dc.ccount != nullptr;
     if (bf16 && counts)
         dense_chunk_kernel<true, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);

@@ -483,13 +483,81 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / kWave;
 
+// LDS copy of one request's tree and every node's depth.  Node arrays are read
+// at once (all V + 1 slots); depths come from pointer jumping: (anc, dist)
+// climbs towards the root in doubling steps; -1 marks the root reached, -2 a
+// broken parent link (depth -1).  Called by all kWalkThreads threads.
+struct TreeLds {
+    int32_t dep[kMaxNodes], tok[kMaxNodes], par[kMaxNodes];
+    int32_t anc[2][kMaxNodes], dist[2][kMaxNodes];
+};
+
+__device__ __forceinline__ void tree_depths(const int32_t* node_token, const int32_t* node_parent, int64_t ob,
+                                            int nn, int V, TreeLds& L)
+{
+    const int t = (int)threadIdx.x;
+    int anc = -2, dist = 0;
+    if (t <= V) {
+        const int p = node_parent[ob + t];
+        const int tk = node_token[ob + t];
+        if (t == 0) { anc = -1; L.par[0] = -1; L.tok[0] = -1; }
+        else if (t < nn) { anc = (p >= 0 && p < t) ? p : -2; dist = 1; L.par[t] = p; L.tok[t] = tk; }
+        L.anc[0][t] = anc;
+        L.dist[0][t] = dist;
+    }
+    __syncthreads();
+    for (int it = 0; it < 8; ++it) {
+        const int cur = it & 1;
+        if (t < nn && anc >= 0) {
+            const int a = L.anc[cur][anc];
+            dist += L.dist[cur][anc];
+            anc = a;
+        }
+        if (t < nn) { L.anc[cur ^ 1][t] = anc; L.dist[cur ^ 1][t] = dist; }
+        __syncthreads();
+    }
+    if (t < nn) L.dep[t] = (anc == -1) ? dist : -1;
+    __syncthreads();
+}
+
+// The walk itself from every node's sample s_t (one wave): emit the node's
+// sample, then move to the child carrying that token, found by ballot.
+__device__ __forceinline__ void follow_path(int b, int B, int nn, const int32_t* s_t, const TreeLds& L,
+                                            const WalkOut& o, int lane)
+{
+    int32_t* tok = o.tokens + (int64_t)b * (B + 1);
+    int32_t* pth = o.path + (int64_t)b * (B + 1);
+    int n = 0, d = 0;
+    uint32_t fl = 0;
+    for (;;) {
+        const int32_t t = s_t[n];
+        if (lane == 0) { tok[d] = t; pth[d] = n; }
+        if (t < 0) fl |= 1u;
+        int child = -1;
+        if (t >= 0 && d < B)
+            for (int base = 1; base < nn && child < 0; base += kWave) {
+                const int c = base + lane;
+                const uint64_t m = __ballot(c < nn && L.par[c] == n && L.tok[c] == t);
+                if (m) child = base + wave_first_lane(m);
+            }
+        if (child < 0) break;
+        n = child;
+        ++d;
+    }
+    for (int j = d + 1 + lane; j <= B; j += kWave) { tok[j] = -1; pth[j] = -1; }
+    if (lane == 0) {
+        o.accept_len[b] = d + 1;
+        if (o.flags) o.flags[b] = fl;
+    }
+}
+
 __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     int32_t batch, int32_t B, int32_t V, SparseOut sup, uint64_t seed, uint64_t offset,
     const uint32_t* req_ids, const int32_t* node_token, const int32_t* node_parent,
     const int32_t* num_nodes, WalkOut o)
 {
-    __shared__ int32_t s_dep[kMaxNodes], s_t[kMaxNodes], s_tok[kMaxNodes], s_par[kMaxNodes];
-    __shared__ int32_t s_anc[2][kMaxNodes], s_dist[2][kMaxNodes];
+    __shared__ TreeLds L;
+    __shared__ int32_t s_t[kMaxNodes];
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -499,36 +567,11 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     int nn = num_nodes[b];
     nn = nn < 1 ? 1 : (nn > V + 1 ? V + 1 : nn);
     const int64_t ob = (int64_t)b * (V + 1);
-    // node arrays (all V + 1 slots, read at once), then depths by pointer
-    // jumping: (anc, dist) climbs towards the root in doubling steps; -1 marks
-    // the root reached, -2 a broken parent link (depth -1)
-    const int t = (int)threadIdx.x;
-    int anc = -2, dist = 0;
-    if (t <= V) {
-        const int p = node_parent[ob + t];
-        const int tk = node_token[ob + t];
-        if (t == 0) { anc = -1; s_par[0] = -1; s_tok[0] = -1; }
-        else if (t < nn) { anc = (p >= 0 && p < t) ? p : -2; dist = 1; s_par[t] = p; s_tok[t] = tk; }
-        s_anc[0][t] = anc;
-        s_dist[0][t] = dist;
-    }
-    __syncthreads();
-    for (int it = 0; it < 8; ++it) {
-        const int cur = it & 1;
-        if (t < nn && anc >= 0) {
-            const int a = s_anc[cur][anc];
-            dist += s_dist[cur][anc];
-            anc = a;
-        }
-        if (t < nn) { s_anc[cur ^ 1][t] = anc; s_dist[cur ^ 1][t] = dist; }
-        __syncthreads();
-    }
-    if (t < nn) s_dep[t] = (anc == -1) ? dist : -1;
-    __syncthreads();
+    tree_depths(node_token, node_parent, ob, nn, V, L);
     // every node's sample, drawn with the uniform of its depth
     // the next node's support is loaded while this one is sampled
     auto node_live = [&](int n, int* cnt) __attribute__((always_inline)) {
-        const int dep = s_dep[n];
+        const int dep = L.dep[n];
         *cnt = sup.count[ob + n];
         return dep >= 0 && dep <= B && *cnt > 0;
     };
@@ -552,7 +595,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
         }
         int32_t t = -1;
         if (live) {
-            const Draw d = uno_draw(seed, req, (uint32_t)s_dep[n], offset);
+            const Draw d = uno_draw(seed, req, (uint32_t)L.dep[n], offset);
             double dummy;
             t = wave_sample_cum(R, cnt, d.u[2], &dummy, lane);
         }
@@ -562,32 +605,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
         live = liven;
     }
     __syncthreads();
-    if (w != 0) return;
-    // the walk itself: one wave, each step finds the matching child by ballot
-    int32_t* tok = o.tokens + (int64_t)b * (B + 1);
-    int32_t* pth = o.path + (int64_t)b * (B + 1);
-    int n = 0, d = 0;
-    uint32_t fl = 0;
-    for (;;) {
-        const int32_t t = s_t[n];
-        if (lane == 0) { tok[d] = t; pth[d] = n; }
-        if (t < 0) fl |= 1u;
-        int child = -1;
-        if (t >= 0 && d < B)
-            for (int base = 1; base < nn && child < 0; base += kWave) {
-                const int c = base + lane;
-                const uint64_t m = __ballot(c < nn && s_par[c] == n && s_tok[c] == t);
-                if (m) child = base + wave_first_lane(m);
-            }
-        if (child < 0) break;
-        n = child;
-        ++d;
-    }
-    for (int j = d + 1 + lane; j <= B; j += kWave) { tok[j] = -1; pth[j] = -1; }
-    if (lane == 0) {
-        o.accept_len[b] = d + 1;
-        if (o.flags) o.flags[b] = fl;
-    }
+    if (w == 0) follow_path(b, B, nn, s_t, L, o, lane);
 }
 
 // ---- dense linear ------------------------------------------------------------------
@@ -1016,6 +1034,79 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
     }
 }
 
+// ---- dense tree (full-vocabulary filters) ------------------------------------------
+// Target-sampled walk over node rows whose filter keeps the whole vocabulary:
+// each live node's token is drawn from its row's exact chunk statistics (one
+// wave per node, the uniform of the node's depth), then wave 0 follows the
+// path as in the sparse walk.
+template <bool BF16>
+__global__ __launch_bounds__(kWalkThreads) void dense_walk_kernel(
+    RowSource src, int32_t batch, int32_t B, int32_t V, int64_t N, double log2e_over_T, DenseChunks dc,
+    uint64_t seed, uint64_t offset, const uint32_t* req_ids, const int32_t* node_token,
+    const int32_t* node_parent, const int32_t* num_nodes, WalkOut o)
+{
+    __shared__ double s_exp2[kExp2Entries];
+    __shared__ TreeLds L;
+    __shared__ int32_t s_t[kMaxNodes];
+    load_exp2_table(s_exp2);
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int b = blockIdx.x;
+    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+    int nn = num_nodes[b];
+    nn = nn < 1 ? 1 : (nn > V + 1 ? V + 1 : nn);
+    const int64_t ob = (int64_t)b * (V + 1);
+    tree_depths(node_token, node_parent, ob, nn, V, L);      // its barriers also publish the table
+    const DenseExp ex{ log2e_over_T, s_exp2 };
+    const int nc = dc.nchunks;
+    const int64_t row_bytes = N * Vec<BF16>::ESZ;
+    for (int n = w; n < nn; n += kWalkWaves) {
+        const int dep = L.dep[n];
+        int32_t t = -1;
+        if (dep >= 0 && dep <= B) {
+            const int64_t r = ob + n;
+            const float* cm = dc.cmax + r * nc;
+            const double* cs = dc.csum + r * nc;
+            float m;
+            double S;
+            if (dense_row_stat(cm, cs, nc, ex, lane, &m, &S)) {
+                const Draw d = uno_draw(seed, req, (uint32_t)dep, offset);
+                t = dense_sample_row<BF16>(row_pointer(src, r, row_bytes), N, cm, cs, nc, m, S, d.u[2], ex, lane);
+            }
+        }
+        if (lane == 0) s_t[n] = t;
+    }
+    __syncthreads();
+    if (w == 0) follow_path(b, B, nn, s_t, L, o, lane);
+}
+
+// Tree build over full-vocabulary filters: the top-K supports come normalised
+// over their K ids; this rescales them to the full softmax, whose normaliser
+// the exact chunk statistics give (one wave per row).
+__global__ __launch_bounds__(kDenseThreads) void dense_support_scale_kernel(int64_t rows, double inv_T,
+                                                                           DenseChunks dc, SparseOut sup)
+{
+    const int lane = lane_id();
+    const int64_t r = (int64_t)blockIdx.x * kDenseWaves + threadIdx.x / kWave;
+    if (r >= rows) return;
+    const int n = sup.count[r];
+    if (n <= 0) return;
+    const int nc = dc.nchunks;
+    const float* cm = dc.cmax + r * nc;
+    const double* cs = dc.csum + r * nc;
+    float m = -INFINITY;
+    for (int c = lane; c < nc; c += kWave) m = fmaxf(m, cm[c]);
+    m = wave_max_f32(m);
+    double S = 0.0;
+    for (int c = lane; c < nc; c += kWave)
+        if (cm[c] > -INFINITY) S += cs[c] * exp(((double)cm[c] - (double)m) * inv_T);
+    S = wave_sum_f64(S);
+    const double scale = sup.stats[2 * r + 1] / S;
+    double* p = sup.probs + r * sup.cap;
+    for (int i = lane; i < n; i += kWave) p[i] *= scale;
+    if (lane == 0) sup.stats[2 * r + 1] = S;
+}
+
 }  // namespace
 
 hipError_t launch_linear_sparse(int32_t batch, int32_t B, const SparseOut& sup, uint64_t seed,
@@ -1080,6 +1171,31 @@ hipError_t launch_tree_walk(int32_t batch, int32_t B, int32_t V, const SparseOut
     if (sup.cum == nullptr) return hipErrorInvalidValue;     // needs id-ordered supports
     tree_walk_kernel<<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
         batch, B, V, sup, seed, offset, request_ids, node_token, node_parent, num_nodes, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_walk_dense(const RowSource& src, int32_t batch, int32_t B, int32_t V, int64_t vocab,
+                                  bool bf16, float temperature, const DenseChunks& dc, uint64_t seed,
+                                  uint64_t offset, const uint32_t* request_ids, const int32_t* node_token,
+                                  const int32_t* node_parent, const int32_t* num_nodes, const WalkOut& o,
+                                  hipStream_t stream)
+{
+    const double c = 1.4426950408889634074 / (double)temperature;
+    if (bf16)
+        dense_walk_kernel<true><<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
+            src, batch, B, V, vocab, c, dc, seed, offset, request_ids, node_token, node_parent, num_nodes, o);
+    else
+        dense_walk_kernel<false><<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
+            src, batch, B, V, vocab, c, dc, seed, offset, request_ids, node_token, node_parent, num_nodes, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_support_scale(int64_t rows, float temperature, const DenseChunks& dc,
+                                      const SparseOut& sup, hipStream_t stream)
+{
+    if (sup.stats == nullptr) return hipErrorInvalidValue;
+    dense_support_scale_kernel<<<dim3((unsigned)((rows + kDenseWaves - 1) / kDenseWaves)), kDenseThreads, 0,
+                                 stream>>>(rows, 1.0 / (double)temperature, dc, sup);
     return hipGetLastError();
 }
 

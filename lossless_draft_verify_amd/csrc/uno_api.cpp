@@ -189,20 +189,32 @@ int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const 
 }
 
 int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int64_t vocab, int32_t dtype,
-                const uno_sampling_t* sp, Carve& cv, Mode* m, SparseWs* sw)
+                const uno_sampling_t* sp, Carve& cv, Mode* m, SparseWs* sw, DenseChunks* dc)
 {
     int st = check_common(dtype, vocab);
     if (st) return st;
     if (batch < 0 || batch * ((int64_t)V + 1) > 0x7FFFFFFF) return UNO_ERR_INVALID_ARG;
-    st = check_tree_shape(B, K, V, op == UNO_OP_BUILD_TREE);
+    const bool build = op == UNO_OP_BUILD_TREE;
+    st = check_tree_shape(B, K, V, build);
     if (st) return st;
     st = check_sampling(sp, vocab, m);
     if (st) return st;
-    if (!m->sparse) return UNO_ERR_UNSUPPORTED;      // dense tree sampling is not built
+    // a full-vocabulary build selects its K candidates with the top-k path
+    if (!m->sparse && build && K > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
     if (batch == 0) return UNO_OK;
-    const int64_t rows = batch * (op == UNO_OP_BUILD_TREE ? (int64_t)B : (int64_t)V + 1);
-    // the build reads its candidates in filter order, the walk samples in id order
-    carve_sparse(cv, rows, vocab, *m, true, op == UNO_OP_VERIFY_TREE, sw);
+    const int64_t rows = batch * (build ? (int64_t)B : (int64_t)V + 1);
+    if (m->sparse) {
+        // the build reads its candidates in filter order, the walk samples in id order
+        carve_sparse(cv, rows, vocab, *m, true, !build, sw);
+    } else if (build) {
+        Mode mk = *m;
+        mk.k = K;
+        carve_sparse(cv, rows, vocab, mk, true, false, sw);
+        sw->sup.stats = cv.take<double>((size_t)rows * 2);
+        *dc = carve_chunks(cv, rows, vocab, false);
+    } else {
+        *dc = carve_chunks(cv, rows, vocab, false);
+    }
     return UNO_OK;
 }
 
@@ -224,7 +236,7 @@ int uno_workspace_bytes(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K,
     case UNO_OP_FILTER: st = layout_filter(batch_or_rows, vocab, dtype, sp, cv, &m, &sw, &dc); break;
     case UNO_OP_SAMPLE_LINEAR: st = layout_linear(batch_or_rows, B, vocab, dtype, sp, cv, &m, &sw, &dc, &ds); break;
     case UNO_OP_BUILD_TREE:
-    case UNO_OP_VERIFY_TREE: st = layout_tree(op, batch_or_rows, B, K, V, vocab, dtype, sp, cv, &m, &sw); break;
+    case UNO_OP_VERIFY_TREE: st = layout_tree(op, batch_or_rows, B, K, V, vocab, dtype, sp, cv, &m, &sw, &dc); break;
     default: return UNO_ERR_INVALID_ARG;
     }
     if (st) return st;
@@ -319,7 +331,8 @@ int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, i
     Carve sizing{ nullptr };
     Mode m;
     SparseWs sw;
-    int st = layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sp, sizing, &m, &sw);
+    DenseChunks dc;
+    int st = layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sp, sizing, &m, &sw, &dc);
     if (st) return st;
     if (batch == 0) return UNO_OK;
     if (draft == nullptr || node_token == nullptr || node_parent == nullptr || node_depth == nullptr ||
@@ -328,12 +341,26 @@ int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, i
     st = check_ws(ws, ws_bytes, sizing.used);
     if (st) return st;
     Carve cv{ static_cast<char*>(ws) };
-    layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sp, cv, &m, &sw);
+    layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sp, cv, &m, &sw, &dc);
 
     const int64_t rows = (int64_t)batch * B;
+    const bool bf16 = dtype == UNO_BF16;
     RowSource src{ static_cast<const char*>(draft), rows, nullptr, nullptr, 1 };
-    hipError_t e = launch_topk_filter(src, rows, vocab, dtype == UNO_BF16, filter_params(sp, m), sw.sup, sw.S,
-                                      sw.part_key, sw.part_id, sw.part_n, stream);
+    hipError_t e;
+    if (m.sparse) {
+        e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, m), sw.sup, sw.S, sw.part_key,
+                               sw.part_id, sw.part_n, stream);
+    } else {
+        // full-vocabulary filter: exact row normalisers, the K best ids, then
+        // their probabilities under the full softmax
+        Mode mk = m;
+        mk.k = K;
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
+        if (e == hipSuccess)
+            e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, mk), sw.sup, sw.S, sw.part_key,
+                                   sw.part_id, sw.part_n, stream);
+        if (e == hipSuccess) e = launch_dense_support_scale(rows, sp->temperature, dc, sw.sup, stream);
+    }
     if (e == hipSuccess) {
         TreeOut o{ node_token, node_parent, node_depth, node_score, num_nodes };
         e = launch_tree_build(batch, B, K, V, sw.sup, o, stream);
@@ -350,7 +377,8 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
     Carve sizing{ nullptr };
     Mode m;
     SparseWs sw;
-    int st = layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sp, sizing, &m, &sw);
+    DenseChunks dc;
+    int st = layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sp, sizing, &m, &sw, &dc);
     if (st) return st;
     if (batch == 0) return UNO_OK;
     if (target == nullptr || node_token == nullptr || node_parent == nullptr || num_nodes == nullptr ||
@@ -360,16 +388,25 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
     st = check_ws(ws, ws_bytes, sizing.used);
     if (st) return st;
     Carve cv{ static_cast<char*>(ws) };
-    layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sp, cv, &m, &sw);
+    layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sp, cv, &m, &sw, &dc);
 
     const int64_t rows = (int64_t)batch * (V + 1);
+    const bool bf16 = dtype == UNO_BF16;
     RowSource src{ static_cast<const char*>(target), rows, nullptr, num_nodes, V + 1 };
-    hipError_t e = launch_topk_filter(src, rows, vocab, dtype == UNO_BF16, filter_params(sp, m), sw.sup, sw.S,
-                                      sw.part_key, sw.part_id, sw.part_n, stream);
-    if (e == hipSuccess) {
-        WalkOut o{ out_tokens, out_path, out_accept_len, out_flags };
-        e = launch_tree_walk(batch, B, V, sw.sup, seed, offset, request_ids, node_token, node_parent, num_nodes,
-                             o, stream);
+    WalkOut o{ out_tokens, out_path, out_accept_len, out_flags };
+    hipError_t e;
+    if (m.sparse) {
+        e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, m), sw.sup, sw.S, sw.part_key,
+                               sw.part_id, sw.part_n, stream);
+        if (e == hipSuccess)
+            e = launch_tree_walk(batch, B, V, sw.sup, seed, offset, request_ids, node_token, node_parent,
+                                 num_nodes, o, stream);
+    } else {
+        // every node row a walk may sample gets exact chunk statistics
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
+        if (e == hipSuccess)
+            e = launch_tree_walk_dense(src, batch, B, V, vocab, bf16, sp->temperature, dc, seed, offset,
+                                       request_ids, node_token, node_parent, num_nodes, o, stream);
     }
     return hip_status(e);
 }

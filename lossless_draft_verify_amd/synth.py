@@ -86,6 +86,15 @@ WORKLOADS = {
                             dtype="bf16", slope=1.0, sigma=_const(0.4, 8), temperature=1.0,
                             top_k=50, top_p=0.95, seed=123, cycles=500,
                             note="Tree 8/16/8, 64 requests"),
+    # the tree shapes with filters that keep the whole vocabulary (dense tree mode)
+    "tree_dense_16_32_32": Workload("tree_dense_16_32_32", "tree", batch=1, B=16, K=32, V=32,
+                                    vocab=VOCAB_QWEN3, dtype="f32", slope=1.2, sigma=_const(0.3, 16),
+                                    temperature=1.0, top_k=0, top_p=1.0, seed=42, cycles=2000,
+                                    note="Tree 16/32/32, one request, full-softmax filters"),
+    "tree_dense_8_16_8": Workload("tree_dense_8_16_8", "tree", batch=64, B=8, K=16, V=8,
+                                  vocab=VOCAB_QWEN3, dtype="bf16", slope=1.0, sigma=_const(0.4, 8),
+                                  temperature=1.0, top_k=0, top_p=1.0, seed=123, cycles=500,
+                                  note="Tree 8/16/8, 64 requests, full-softmax filters"),
 }
 
 

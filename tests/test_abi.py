@@ -84,6 +84,12 @@ def test_workspace_sizes(lib):
     assert st == OK and nt > 16 * 50 * 12
     st, nv = _ws(lib, uno.OP_VERIFY_TREE, 1, 16, 1, 32, N, F32, sp())
     assert st == OK and nv > 33 * 50 * 12
+    # dense tree: exact chunk statistics of every row; the build also keeps
+    # K-entry supports with their row statistics
+    st, nbd = _ws(lib, uno.OP_BUILD_TREE, 1, 16, 32, 32, N, F32, sp(1.0, 0, 1.0))
+    assert st == OK and nbd >= 16 * nch * (4 + 8) + 16 * 32 * (4 + 8) + 16 * 16
+    st, nvd = _ws(lib, uno.OP_VERIFY_TREE, 1, 16, 1, 32, N, F32, sp(1.0, 0, 1.0))
+    assert st == OK and nvd >= 33 * nch * (4 + 8)
     # filter with many rows needs nothing beyond the caller's outputs
     st, nf = _ws(lib, uno.OP_FILTER, 4096, 0, 0, 0, N, F32, sp())
     assert st == OK and nf == 0
@@ -154,7 +160,10 @@ def test_tree_argument_checks(lib):
     assert bt(K=0) == INVALID
     assert bt(K=300, V=8) == INVALID       # V * K > 2048
     assert bt(B=0) == INVALID
-    assert bt(s=sp(1.0, 0, 1.0)) == UNSUPPORTED     # dense tree sampling not built
+    # full-vocabulary filters: the build picks its K candidates with the top-k path
+    assert bt(s=sp(1.0, 0, 1.0)) == WORKSPACE
+    assert bt(s=sp(1.0, 0, 1.0), K=257, V=4) == UNSUPPORTED
+    assert bt(s=sp(1.0, 0, 0.9)) == UNSUPPORTED     # full-vocabulary nucleus
     assert bt(d=None) == INVALID
     assert bt() == WORKSPACE
     assert bt(K=256, V=8) == WORKSPACE     # V * K == 2048 is allowed
@@ -162,7 +171,8 @@ def test_tree_argument_checks(lib):
         FAKE, F32, 2, B, V, 1000, s or sp(), 1, 0, None, o, o, o, o, o, o, None, None, 0, None)
     assert vt(V=3) == INVALID
     assert vt(V=200) == INVALID
-    assert vt(s=sp(0.5, 0, 1.0)) == UNSUPPORTED
+    assert vt(s=sp(0.5, 0, 1.0)) == WORKSPACE        # dense walk
+    assert vt(s=sp(0.5, 0, 0.9)) == UNSUPPORTED       # full-vocabulary nucleus
     assert vt() == WORKSPACE
     # greedy decoding is a sparse (k = 1) mode
     assert vt(s=sp(0.0, 0, 1.0)) == WORKSPACE

@@ -14,18 +14,72 @@ pytestmark = pytest.mark.gpu
 TREE_KEYS = ("node_token", "node_parent", "node_depth", "num_nodes")
 
 
+def _tree_paths(tok, par, num):
+    """Token path (root to node) of every non-root node."""
+    out = {}
+    for n in range(1, int(num)):
+        seq, q = [], n
+        while q > 0:
+            seq.append(int(tok[q]))
+            q = int(par[q])
+        out[n] = tuple(reversed(seq))
+    return out
+
+
+def _check_tied_tree(g, o, f, b, B, label):
+    """A tree that differs from the oracle's is valid when only the order of
+    scores equal in exact arithmetic differs: every node's score is the product
+    of the filtered probabilities on its path, nodes come in best-first order,
+    and the node sets differ only by entries tied with the last one kept."""
+    num = int(o["num_nodes"][b])
+    assert int(g["num_nodes"][b]) == num, (label, b)
+
+    def path_score(path):
+        s = 1.0
+        for d, t in enumerate(path):
+            ids = list(f["ids"][b * B + d])
+            assert t in ids, (label, b, d, t)
+            s *= f["probs"][b * B + d][ids.index(t)]
+        return s
+
+    gp = _tree_paths(g["node_token"][b], g["node_parent"][b], num)
+    op = _tree_paths(o["node_token"][b], o["node_parent"][b], num)
+    for n, path in gp.items():
+        assert int(g["node_depth"][b][n]) == len(path), (label, b, n)
+        s = path_score(path)
+        assert abs(g["node_score"][b][n] - s) <= 1e-12 * s, (label, b, n)
+    sc = g["node_score"][b][1:num]
+    assert np.all(sc[1:] <= sc[:-1] * (1 + 1e-12)), (label, b)
+    lowest = min(o["node_score"][b][1:num]) if num > 1 else 1.0
+    for path in set(gp.values()) ^ set(op.values()):
+        assert abs(path_score(path) - lowest) <= 1e-12 * lowest, (label, b, path)
+
+
 def _build_parity(draft, K, V, T, k, p, label):
     g = uno.build_tree(draft, K, V, T, k, p)
     torch.cuda.synchronize()
-    o = oracle.build_tree(synth.as_float32_numpy(draft), K, V, T, k, p)
+    dh = synth.as_float32_numpy(draft)
+    o = oracle.build_tree(dh, K, V, T, k, p)
+    batch, B, N = dh.shape
+    G = {key: np_of(g[key]) for key in TREE_KEYS + ("node_score",)}
+    bad = np.zeros(batch, dtype=bool)
     for key in TREE_KEYS:
-        gk = np_of(g[key])
-        bad = np.any(gk.reshape(gk.shape[0], -1) != o[key].reshape(gk.shape[0], -1), axis=1)
-        # a pop order may only differ where two scores are within rounding of each other
-        assert not np.any(bad & (o["min_gap"] >= 1e-12)), (label, key, np.flatnonzero(bad)[:4])
+        bad |= np.any(G[key].reshape(batch, -1) != o[key].reshape(batch, -1), axis=1)
+    full_vocab = T > 0 and (k <= 0 or k >= N) and p >= 1.0 and N > uno.MAX_TOP_K
+    if full_vocab:
+        # full-softmax normalisers are summed in another order on the device, so
+        # scores equal in exact arithmetic may round apart and pop in either order
+        f = oracle.filter_rows(dh.reshape(batch * B, N), T, 0, 1.0, cap=K, dense=False)
+        for b in np.flatnonzero(bad):
+            _check_tied_tree(G, o, f, int(b), B, label)
+        same = ~bad
+        np.testing.assert_allclose(G["node_score"][same], o["node_score"][same], rtol=1e-12, atol=0)
+        return g, o
+    # a pop order may only differ where two scores are within rounding of each other
+    assert not np.any(bad & (o["min_gap"] >= 1e-12)), (label, np.flatnonzero(bad)[:4])
     # scores are products of filtered probabilities, each within an ulp or two of
     # the reference (the device and host exp may differ in the last bit)
-    np.testing.assert_allclose(np_of(g["node_score"]), o["node_score"], rtol=1e-12, atol=0)
+    np.testing.assert_allclose(G["node_score"], o["node_score"], rtol=1e-12, atol=0)
     return g, o
 
 
@@ -123,3 +177,82 @@ def test_walk_is_lossless_small_vocab():
             sel = path[:, dd] == node
             if sel.sum() > 3000:
                 assert chisq_pvalue(tok[sel, dd], P[node]) > 1e-4, (node, dd)
+
+
+# ---- full-vocabulary filters (dense tree mode) ----------------------------------------
+
+def test_dense_tree_16_32_32_full_size():
+    _tree_cycles(synth.WORKLOADS["tree_dense_16_32_32"], 4)
+
+
+def test_dense_tree_8_16_8_reduced_batch():
+    _tree_cycles(synth.WORKLOADS["tree_dense_8_16_8"], 2, batch=8, label="tree_dense_8_16_8 b8")
+
+
+@pytest.mark.parametrize("B,K,V,T,N,bf16", [(3, 3, 10, 1.0, 5000, False), (2, 8, 16, 0.5, 4099, True),
+                                            (5, 16, 128, 1.0, 3 * 2048, False), (4, 256, 8, 1.0, 700, False),
+                                            (6, 4, 20, 2.0, 257, True)])
+def test_dense_tree_shapes(B, K, V, T, N, bf16):
+    # several chunks and a ragged tail, K up to the top-k limit, V up to 128
+    dev = device()
+    rng = np.random.default_rng(B * 1000 + K + N)
+    batch = 10
+    d = torch.from_numpy((rng.standard_normal((batch, B, N)) * 2).astype(np.float32)).to(dev)
+    tg = torch.from_numpy((rng.standard_normal((batch, V + 1, N)) * 2).astype(np.float32)).to(dev)
+    if bf16:
+        d, tg = d.to(torch.bfloat16), tg.to(torch.bfloat16)
+    label = f"dense B{B} K{K} V{V} N{N}"
+    _, o = _build_parity(d, K, V, T, 0, 1.0, label)
+    t = Tally()
+    rid = np.arange(batch, dtype=np.uint32) * 7919 + 3
+    for c in range(3):
+        _verify_parity(tg, B, o, T, 0, 1.0, 23, c, t, label, request_ids=rid)
+    t.check_rate()
+
+
+def test_dense_walk_invalid_rows_and_unread_rows():
+    # a live node row with no finite logit stops the walk with -1 (flagged);
+    # rows at or past num_nodes hold +inf and must not be read
+    dev = device()
+    rng = np.random.default_rng(5)
+    batch, B, K, V, N = 6, 3, 4, 12, 3000
+    d = (rng.standard_normal((batch, B, N)) * 1.5).astype(np.float32)
+    tree = oracle.build_tree(d, K, V, 1.0, 0, 1.0)
+    tree["num_nodes"] = np.minimum(tree["num_nodes"], 7).astype(np.int32)
+    tg = (rng.standard_normal((batch, V + 1, N)) * 1.5).astype(np.float32)
+    tg[:, 7:, :] = np.inf
+    tg[1, 0, :] = -np.inf                     # request 1: the root row is empty
+    tg[2, :, :5] = np.nan                     # NaN logits count as -inf
+    tg[3, 0, 100] = np.inf                    # request 3: the root row is invalid
+    g = _verify_parity(torch.from_numpy(tg).to(dev), B, tree, 1.0, 0, 1.0, 9, 4, Tally(), "dense invalid")
+    assert g["tokens"][1, 0] == -1 and g["accept_len"][1] == 1
+    assert g["tokens"][3, 0] == -1 and g["accept_len"][3] == 1
+
+
+def test_dense_walk_is_lossless():
+    # vocabulary above the top-k limit, so the full-softmax path runs
+    dev = device()
+    rng = np.random.default_rng(43)
+    B, K, V, N, n = 3, 3, 7, 300, 60_000
+    # peaked rows, and node rows equal to the draft row of their depth, so that
+    # walks often follow a child and reach the deeper nodes
+    R = (rng.standard_normal((B + 1, N)) * 3.0).astype(np.float32)
+    tree = oracle.build_tree(R[None, :B], K, V, 1.0, 0, 1.0)
+    dep = np.maximum(tree["node_depth"][0], 0)
+    target_rows = np.ascontiguousarray(R[dep])
+    tgt = torch.from_numpy(target_rows).to(dev).expand(n, V + 1, N).contiguous()
+    rep = lambda a: torch.from_numpy(np.ascontiguousarray(np.tile(a, (n, 1)))).to(dev)
+    g = uno.verify_tree(tgt, B, rep(tree["node_token"]), rep(tree["node_parent"]),
+                        torch.full((n,), int(tree["num_nodes"][0]), dtype=torch.int32, device=dev),
+                        1.0, 0, 1.0, 78, 0)
+    torch.cuda.synchronize()
+    P = oracle.filter_rows(target_rows, 1.0, 0, 1.0)["dense"]
+    tok, path = np_of(g["tokens"]), np_of(g["path"])
+    checked = 0
+    for node in range(int(tree["num_nodes"][0])):
+        for dd in range(B + 1):
+            sel = path[:, dd] == node
+            if sel.sum() > 3000:
+                assert chisq_pvalue(tok[sel, dd], P[node]) > 1e-4, (node, dd)
+                checked += 1
+    assert checked >= 2
