@@ -25,6 +25,11 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
+# Filter orders: top-k, renormalise, then top-p (the default), or joint (the
+# top-p cut taken on the full-vocabulary softmax, within the top-k set).
+ORDER_TOPK_FIRST = 0
+ORDER_JOINT = 1
+
 
 def build(force: bool = False) -> str:
     """Compile ``uno_oracle.c`` into ``liboracle.so`` (gcc, -O2, OpenMP)."""
@@ -51,17 +56,17 @@ def _load():
         lib.oracle_philox4x32_10.restype = None
         lib.oracle_uniform.argtypes = [u64, u32, u32, u64, ctypes.c_int]
         lib.oracle_uniform.restype = f64
-        lib.oracle_filter.argtypes = [P, i64, i64, f64, i32, f64, P, P, P, P, i32, P, P]
+        lib.oracle_filter.argtypes = [P, i64, i64, f64, i32, f64, i32, P, P, P, P, i32, P, P]
         lib.oracle_filter.restype = ctypes.c_int
         lib.oracle_sample.argtypes = [P, i64, f64, P]
         lib.oracle_sample.restype = i32
-        lib.oracle_linear.argtypes = [P, P, i32, i32, i64, i64, i64, f64, i32, f64, u64, u64, P,
+        lib.oracle_linear.argtypes = [P, P, i32, i32, i64, i64, i64, f64, i32, f64, i32, u64, u64, P,
                                       P, P, P, P]
         lib.oracle_linear.restype = None
-        lib.oracle_build_tree.argtypes = [P, i32, i32, i32, i32, i64, i64, f64, i32, f64,
+        lib.oracle_build_tree.argtypes = [P, i32, i32, i32, i32, i64, i64, f64, i32, f64, i32,
                                           P, P, P, P, P, P]
         lib.oracle_build_tree.restype = None
-        lib.oracle_verify_tree.argtypes = [P, i32, i32, i32, i64, i64, f64, i32, f64, u64, u64, P,
+        lib.oracle_verify_tree.argtypes = [P, i32, i32, i32, i64, i64, f64, i32, f64, i32, u64, u64, P,
                                            P, P, P, P, P, P, P]
         lib.oracle_verify_tree.restype = None
         lib.oracle_tpf.argtypes = [P, i64]
@@ -104,7 +109,7 @@ def uniform(seed, req, pos, offset, lane):
     return float(_load().oracle_uniform(seed, req, pos, offset, lane))
 
 
-def filter_rows(z, temperature, top_k, top_p, cap=None, dense=True):
+def filter_rows(z, temperature, top_k, top_p, cap=None, dense=True, order=ORDER_TOPK_FIRST):
     """Filter each row of ``z`` [rows, N].
 
     Returns dict(dense [rows,N] f64 or None, ids [rows,cap], probs [rows,cap]
@@ -122,7 +127,7 @@ def filter_rows(z, temperature, top_k, top_p, cap=None, dense=True):
     n = np.zeros(rows, dtype=np.int32)
     stats = np.zeros((rows, 2), dtype=np.float64)
     margin = np.zeros(rows, dtype=np.float64)
-    rc = lib.oracle_filter(_ptr(z), rows, N, _param(temperature), int(top_k), _param(top_p),
+    rc = lib.oracle_filter(_ptr(z), rows, N, _param(temperature), int(top_k), _param(top_p), int(order),
                            _ptr(d), _ptr(ids), _ptr(probs), _ptr(n), cap, _ptr(stats), _ptr(margin))
     if rc != 0:
         raise MemoryError("oracle_filter: allocation failed")
@@ -146,7 +151,7 @@ def _req_ids(request_ids, batch):
 
 
 def linear(draft, target, temperature, top_k, top_p, seed, offset, request_ids=None,
-           batch=None):
+           batch=None, order=ORDER_TOPK_FIRST):
     """One linear UNO cycle per request.
 
     draft [batch, B, N] and target [batch, B+1, N]; with ``batch`` given and
@@ -170,12 +175,12 @@ def linear(draft, target, temperature, top_k, top_p, seed, offset, request_ids=N
     mg = np.zeros(batch, dtype=np.float64)
     rid = _req_ids(request_ids, batch)
     lib.oracle_linear(_ptr(draft), _ptr(target), batch, B, N, ds, ts, _param(temperature),
-                      int(top_k), _param(top_p), int(seed), int(offset), _ptr(rid),
+                      int(top_k), _param(top_p), int(order), int(seed), int(offset), _ptr(rid),
                       _ptr(tokens), _ptr(acc), _ptr(prop), _ptr(mg))
     return dict(tokens=tokens, accept_len=acc, proposals=prop, margin=mg)
 
 
-def build_tree(draft, K, V, temperature, top_k, top_p):
+def build_tree(draft, K, V, temperature, top_k, top_p, order=ORDER_TOPK_FIRST):
     """Best-first candidate tree per request from draft [batch, B, N]."""
     lib = _load()
     draft = _f32(draft)
@@ -187,14 +192,14 @@ def build_tree(draft, K, V, temperature, top_k, top_p):
     nn = np.zeros(batch, dtype=np.int32)
     gap = np.zeros(batch, dtype=np.float64)
     lib.oracle_build_tree(_ptr(draft), batch, B, int(K), int(V), N, B * N, _param(temperature),
-                          int(top_k), _param(top_p), _ptr(tok), _ptr(par), _ptr(dep), _ptr(sc),
+                          int(top_k), _param(top_p), int(order), _ptr(tok), _ptr(par), _ptr(dep), _ptr(sc),
                           _ptr(nn), _ptr(gap))
     return dict(node_token=tok, node_parent=par, node_depth=dep, node_score=sc, num_nodes=nn,
                 min_gap=gap)
 
 
 def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_k, top_p,
-                seed, offset, request_ids=None, batch=None):
+                seed, offset, request_ids=None, batch=None, order=ORDER_TOPK_FIRST):
     """Target-sampled tree walk per request over target [batch, V+1, N].
 
     With ``batch`` given and a 2-D target [V+1, N] plus one tree ([V+1], [V+1],
@@ -222,7 +227,7 @@ def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_
     mg = np.zeros(batch, dtype=np.float64)
     rid = _req_ids(request_ids, batch)
     lib.oracle_verify_tree(_ptr(target), batch, int(B), V, N, stride, _param(temperature),
-                           int(top_k), _param(top_p), int(seed), int(offset), _ptr(rid),
+                           int(top_k), _param(top_p), int(order), int(seed), int(offset), _ptr(rid),
                            _ptr(tk), _ptr(pa), _ptr(nn), _ptr(tokens), _ptr(path), _ptr(acc),
                            _ptr(mg))
     return dict(tokens=tokens, path=path, accept_len=acc, margin=mg)

@@ -86,6 +86,14 @@ double oracle_uniform(uint64_t seed, uint32_t req, uint32_t pos, uint64_t offset
  * rule keeps an id while the exclusive cumulative sum (in filter order) is
  * below top_p, and always keeps the first; NaN logits count as -inf; a row
  * holding +inf, or no finite logit, is invalid (empty support).              */
+/* Joint order ([PR] review thread: the regular sampler's joint filtering takes
+ * top-p from the full softmax): keep an id when it is in the top-k set and the
+ * exclusive cumulative full-vocabulary probability before it (filter order)
+ * is below top_p (the first id always), then renormalise over the kept ids.
+ * It differs from the default order only when both top-k and top-p are on.   */
+#define ORACLE_ORDER_TOPK_FIRST 0
+#define ORACLE_ORDER_JOINT 1
+
 typedef struct { double v; int32_t id; } vid_t;
 
 static int cmp_filter_order(const void* a, const void* b)
@@ -121,7 +129,8 @@ static void row_free(row_t* r)
     free(r->p); free(r->ids); free(r->sp); free(r->pairs);
 }
 
-static void filter_row(const float* z, int64_t N, double T, int32_t top_k, double top_p, row_t* r)
+static void filter_row(const float* z, int64_t N, double T, int32_t top_k, double top_p, int32_t order,
+                       row_t* r)
 {
     memset(r->p, 0, sizeof(double) * (size_t)N);
     r->n = 0; r->m = NAN; r->S = NAN; r->margin = INFINITY;
@@ -173,11 +182,22 @@ static void filter_row(const float* z, int64_t N, double T, int32_t top_k, doubl
     }
 
     const int64_t k_eff = topk_on ? (n_use < top_k ? n_use : top_k) : n_use;
-    /* softmax over the top-k set; normaliser summed in filter order */
     double S = 0.0;
-    for (int64_t j = 0; j < k_eff; ++j) {
-        r->sp[j] = exp((r->pairs[j].v - m) / T);
-        S += r->sp[j];
+    if (order == ORACLE_ORDER_JOINT && topk_on && topp_on) {
+        /* joint order: the top-p cut reads the softmax over the whole
+         * vocabulary (normaliser summed in id order), restricted to the
+         * top-k set */
+        for (int64_t i = 0; i < N; ++i) {
+            if (isnan(z[i]) || !(z[i] > -INFINITY)) continue;
+            S += exp(((double)z[i] - m) / T);
+        }
+        for (int64_t j = 0; j < k_eff; ++j) r->sp[j] = exp((r->pairs[j].v - m) / T);
+    } else {
+        /* softmax over the top-k set; normaliser summed in filter order */
+        for (int64_t j = 0; j < k_eff; ++j) {
+            r->sp[j] = exp((r->pairs[j].v - m) / T);
+            S += r->sp[j];
+        }
     }
     r->S = S;
     for (int64_t j = 0; j < k_eff; ++j) r->sp[j] = r->sp[j] / S;      /* pi_j */
@@ -241,7 +261,7 @@ static inline void fmin_into(double* acc, double v) { if (v < *acc) *acc = v; }
 /* ------------------------------------------------------------------------ */
 /* Filter many rows (test aid).  Support written in filter order.             */
 int oracle_filter(const float* z, int64_t rows, int64_t N, double T, int32_t top_k, double top_p,
-                  double* dense, int32_t* sup_ids, double* sup_p, int32_t* sup_n, int32_t cap,
+                  int32_t order, double* dense, int32_t* sup_ids, double* sup_p, int32_t* sup_n, int32_t cap,
                   double* stats, double* margin)
 {
     int err = 0;
@@ -256,7 +276,7 @@ int oracle_filter(const float* z, int64_t rows, int64_t N, double T, int32_t top
         #pragma omp for schedule(dynamic)
         for (int64_t i = 0; i < rows; ++i) {
             if (!ok) continue;
-            filter_row(z + i * N, N, T, top_k, top_p, &r);
+            filter_row(z + i * N, N, T, top_k, top_p, order, &r);
             if (dense) memcpy(dense + i * N, r.p, sizeof(double) * (size_t)N);
             if (sup_n) sup_n[i] = r.n;
             for (int32_t j = 0; j < r.n && j < cap; ++j) {
@@ -297,7 +317,7 @@ int32_t oracle_sample(const double* w, int64_t N, double u, double* margin)
  * a zero stride shares one block of rows between all requests.              */
 void oracle_linear(const float* draft, const float* target, int32_t batch, int32_t B, int64_t N,
                    int64_t draft_req_stride, int64_t target_req_stride,
-                   double T, int32_t top_k, double top_p, uint64_t seed, uint64_t offset,
+                   double T, int32_t top_k, double top_p, int32_t order, uint64_t seed, uint64_t offset,
                    const uint32_t* request_ids,
                    int32_t* tokens, int32_t* accept_len, int32_t* proposals, double* min_margin)
 {
@@ -316,9 +336,9 @@ void oracle_linear(const float* draft, const float* target, int32_t batch, int32
             double mg = INFINITY, m1;
             if (!(shared_done && draft_req_stride == 0 && target_req_stride == 0)) {
                 for (int32_t j = 0; j < B; ++j)
-                    filter_row(draft + (int64_t)b * draft_req_stride + (int64_t)j * N, N, T, top_k, top_p, &q[j]);
+                    filter_row(draft + (int64_t)b * draft_req_stride + (int64_t)j * N, N, T, top_k, top_p, order, &q[j]);
                 for (int32_t j = 0; j <= B; ++j)
-                    filter_row(target + (int64_t)b * target_req_stride + (int64_t)j * N, N, T, top_k, top_p, &p[j]);
+                    filter_row(target + (int64_t)b * target_req_stride + (int64_t)j * N, N, T, top_k, top_p, order, &p[j]);
                 shared_done = 1;
             }
             for (int32_t j = 0; j < B; ++j) fmin_into(&mg, q[j].margin);
@@ -404,7 +424,7 @@ static int fr_better(const fr_t* a, const fr_t* b)
 }
 
 void oracle_build_tree(const float* draft, int32_t batch, int32_t B, int32_t K, int32_t V, int64_t N,
-                       int64_t req_stride, double T, int32_t top_k, double top_p,
+                       int64_t req_stride, double T, int32_t top_k, double top_p, int32_t order,
                        int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
                        double* node_score, int32_t* num_nodes, double* min_gap)
 {
@@ -418,7 +438,7 @@ void oracle_build_tree(const float* draft, int32_t batch, int32_t B, int32_t K, 
         #pragma omp for schedule(dynamic)
         for (int32_t b = 0; b < batch; ++b) {
             for (int32_t d = 0; d < B; ++d)
-                filter_row(draft + (int64_t)b * req_stride + (int64_t)d * N, N, T, top_k, top_p, &q[d]);
+                filter_row(draft + (int64_t)b * req_stride + (int64_t)d * N, N, T, top_k, top_p, order, &q[d]);
             int32_t cn[B > 0 ? B : 1];
             for (int32_t d = 0; d < B; ++d) cn[d] = q[d].n > 0 ? (q[d].n < K ? q[d].n : K) : 0;
 
@@ -472,7 +492,7 @@ void oracle_build_tree(const float* draft, int32_t batch, int32_t B, int32_t K, 
  * (row 0: the root).  Rows past num_nodes are never read.
  * tokens/path = emitted tokens / visited nodes, then -1; accept_len = #emitted. */
 void oracle_verify_tree(const float* target, int32_t batch, int32_t B, int32_t V, int64_t N,
-                        int64_t req_stride, double T, int32_t top_k, double top_p,
+                        int64_t req_stride, double T, int32_t top_k, double top_p, int32_t order,
                         uint64_t seed, uint64_t offset, const uint32_t* request_ids,
                         const int32_t* node_token, const int32_t* node_parent, const int32_t* num_nodes,
                         int32_t* tokens, int32_t* path, int32_t* accept_len, double* min_margin)
@@ -493,7 +513,7 @@ void oracle_verify_tree(const float* target, int32_t batch, int32_t B, int32_t V
             double mg = INFINITY, m1;
             int32_t n = 0, d = 0;
             for (;;) {
-                filter_row(target + (int64_t)b * req_stride + (int64_t)n * N, N, T, top_k, top_p, &r);
+                filter_row(target + (int64_t)b * req_stride + (int64_t)n * N, N, T, top_k, top_p, order, &r);
                 fmin_into(&mg, r.margin);
                 double u[4];
                 draw4(seed, req, (uint32_t)d, offset, u);

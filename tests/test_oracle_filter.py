@@ -170,3 +170,64 @@ def test_stats_match_definition():
         T = np.float64(np.float32(0.7))
         ref = np.exp((z[i].astype(np.float64) - m) / T).sum()
         assert abs(S - ref) / ref < 1e-13
+
+
+# ---- joint filter order: the top-p cut on the full-vocabulary softmax ------------------
+
+def test_hand_example_joint_keeps_more_than_topk_first():
+    # weights 1, 4, 2, 1, 8 (sum 16); top-3 = ids 4, 1, 2 (weights 8, 4, 2).
+    # Top-k first, top-p 0.8: pi = [8,4,2]/14; cumsum before id 2 is 12/14 >= 0.8 -> {4, 1}.
+    # Joint, top-p 0.8: full-softmax pi = [8,4,2]/16; before id 2 it is 12/16 < 0.8 -> keep;
+    # the top-k set ends there -> {4, 1, 2} renormalised: [8,4,2]/14.
+    ids, p = _support(oracle.filter_rows(Z, 1.0, 3, 0.8))
+    assert ids == [4, 1]
+    np.testing.assert_allclose(p, [8 / 12, 4 / 12], rtol=RT)
+    r = oracle.filter_rows(Z, 1.0, 3, 0.8, order=oracle.ORDER_JOINT)
+    ids, p = _support(r)
+    assert ids == [4, 1, 2]
+    np.testing.assert_allclose(p, [8 / 14, 4 / 14, 2 / 14], rtol=RT)
+    # the statistics report the full-vocabulary normaliser (weights relative to the max 8)
+    np.testing.assert_allclose(r["stats"][0], [math.log(8.0), 16 / 8], rtol=RT)
+    # top-p 0.7: 12/16 >= 0.7 stops the joint cut before id 2 as well
+    ids, p = _support(oracle.filter_rows(Z, 1.0, 3, 0.7, order=oracle.ORDER_JOINT))
+    assert ids == [4, 1]
+    np.testing.assert_allclose(p, [8 / 12, 4 / 12], rtol=RT)
+
+
+@pytest.mark.parametrize("T,k,p", [(1.0, 20, 1.0), (0.7, 0, 0.9), (1.3, 1, 0.5), (0.0, 10, 0.9),
+                                   (1.0, 400, 0.9)])
+def test_joint_equals_topk_first_when_one_filter_is_off(T, k, p):
+    # with top-p off, top-k off (k 0 or >= vocab), k = 1 or greedy there is only one reading
+    rng = np.random.default_rng(11)
+    z = (rng.standard_normal((6, 300)) * 2).astype(np.float32)
+    a = oracle.filter_rows(z, T, k, p)
+    b = oracle.filter_rows(z, T, k, p, order=oracle.ORDER_JOINT)
+    for key in ("n", "ids", "probs"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_joint_is_the_smallest_prefix_reaching_top_p():
+    # brute force on small rows: over the top-k order, the joint support is the
+    # shortest prefix whose full-softmax mass (scipy) reaches top_p, capped at k;
+    # the default order's support is never larger
+    rng = np.random.default_rng(12)
+    N, checked = 40, 0
+    for trial in range(300):
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        k = int(rng.integers(2, 30))
+        p = float(rng.uniform(0.2, 0.99))
+        z = (rng.standard_normal(N) * 2).astype(np.float32)
+        order = sorted(range(N), key=lambda i: (-float(z[i]), i))
+        full = softmax(z.astype(np.float64) / float(np.float32(T)))    # parameters are float32
+        mass = np.cumsum(full[order])
+        if np.any(np.abs(mass[:k] - p) < 1e-9):
+            continue
+        L = next((n + 1 for n in range(k) if mass[n] >= p), k)
+        r = oracle.filter_rows(z, T, k, p, order=oracle.ORDER_JOINT)
+        ids, pr = _support(r)
+        assert ids == order[:L], (trial, ids, order[:L])
+        np.testing.assert_allclose(pr, full[order[:L]] / full[order[:L]].sum(), rtol=1e-12)
+        ids_default, _ = _support(oracle.filter_rows(z, T, k, p))
+        assert ids[:len(ids_default)] == ids_default and len(ids_default) <= L
+        checked += 1
+    assert checked > 250
