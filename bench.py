@@ -79,7 +79,8 @@ def traffic_probe(args, w, lib, pool, dt, sp, stream, dev):
     ids = torch.empty((nrows, w.top_k), dtype=torch.int32, device=dev)
     probs = torch.empty((nrows, w.top_k), dtype=torch.float64, device=dev)
     cnt = torch.empty(nrows, dtype=torch.int32, device=dev)
-    fws_n = uno.workspace_bytes(uno.OP_FILTER, nrows, 0, 0, 0, w.vocab, dt, w.temperature, w.top_k, w.top_p)
+    fws_n = uno.workspace_bytes(uno.OP_FILTER, nrows, 0, 0, 0, w.vocab, dt, w.temperature, w.top_k, w.top_p,
+                               w.order)
     fws = torch.empty(fws_n + 256, dtype=torch.uint8, device=dev)
     fws_p = ctypes.c_void_p((fws.data_ptr() + 255) // 256 * 256) if fws_n else None
     src = pool[1 % len(pool)]["all"]
@@ -134,7 +135,7 @@ def main():
             pool.append(dict(all=allrows, draft=d, target=t))
         else:
             draft, R = synth.tree_inputs(w, cycle=c, device=dev)
-            tree = uno.build_tree(draft, w.K, w.V, w.temperature, w.top_k, w.top_p)
+            tree = uno.build_tree(draft, w.K, w.V, w.temperature, w.top_k, w.top_p, order=w.order)
             tgt = synth.tree_target_rows(R, tree["node_depth"], tree["num_nodes"], w.V)
             del R
             pool.append(dict(draft=draft, target=tgt))
@@ -146,13 +147,13 @@ def main():
     import ctypes
     lib = uno.load_library()
     dt = 0 if w.dtype == "f32" else 1
-    sp = uno.Sampling(w.temperature, w.top_k, w.top_p)
+    sp = uno.Sampling(w.temperature, w.top_k, w.top_p, w.order)
     spr = ctypes.byref(sp)
     sptr = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
     def wsbuf(op, K, V):
-        n = uno.workspace_bytes(op, w.batch, w.B, K, V, w.vocab, dt, w.temperature, w.top_k, w.top_p)
+        n = uno.workspace_bytes(op, w.batch, w.B, K, V, w.vocab, dt, w.temperature, w.top_k, w.top_p, w.order)
         if n == 0:
             return None, 0
         t = torch.empty(n + 256, dtype=torch.uint8, device=dev)
@@ -231,13 +232,14 @@ def main():
 
     # ---- dominant kernel: the same filter launch, timed alone with HIP events ------
     roofline = None
-    if w.mode == "linear" and w.top_k > 0:
+    if w.mode == "linear" and w.top_k > 0 and w.order == uno.ORDER_TOPK_FIRST:
         ids = torch.empty((pool[0]["all"].shape[0], w.top_k), dtype=torch.int32, device=dev)
         probs = torch.empty((pool[0]["all"].shape[0], w.top_k), dtype=torch.float64, device=dev)
         cnt = torch.empty(pool[0]["all"].shape[0], dtype=torch.int32, device=dev)
         nrows = pool[0]["all"].shape[0]
         n_f = max(50, min(args.steps, 500))
-        fws_n = uno.workspace_bytes(uno.OP_FILTER, nrows, 0, 0, 0, w.vocab, dt, w.temperature, w.top_k, w.top_p)
+        fws_n = uno.workspace_bytes(uno.OP_FILTER, nrows, 0, 0, 0, w.vocab, dt, w.temperature, w.top_k, w.top_p,
+                               w.order)
         fws = torch.empty(fws_n + 256, dtype=torch.uint8, device=dev)
         fws_p = ctypes.c_void_p((fws.data_ptr() + 255) // 256 * 256) if fws_n else None
 
@@ -283,7 +285,7 @@ def main():
                 lo = n_req % w.batch
                 hi = min(lo + 16, w.batch)
                 oracle.linear(dnp[lo:hi], tnp[lo:hi], w.temperature, w.top_k, w.top_p, w.seed, 0,
-                              request_ids=np.arange(lo, hi, dtype=np.uint32))
+                              request_ids=np.arange(lo, hi, dtype=np.uint32), order=w.order)
                 n_req += hi - lo
                 rows += (hi - lo) * (2 * w.B + 1)
         else:
@@ -293,10 +295,10 @@ def main():
             while time.perf_counter() - t0 < args.cpu_seconds and n_req < w.batch * 8:
                 lo = n_req % w.batch
                 hi = min(lo + 16, w.batch)
-                tr = oracle.build_tree(dnp[lo:hi], w.K, w.V, w.temperature, w.top_k, w.top_p)
+                tr = oracle.build_tree(dnp[lo:hi], w.K, w.V, w.temperature, w.top_k, w.top_p, order=w.order)
                 oracle.verify_tree(tnp[lo:hi], w.B, tr["node_token"], tr["node_parent"], tr["num_nodes"],
                                    w.temperature, w.top_k, w.top_p, w.seed, 0,
-                                   request_ids=np.arange(lo, hi, dtype=np.uint32))
+                                   request_ids=np.arange(lo, hi, dtype=np.uint32), order=w.order)
                 n_req += hi - lo
                 rows += (hi - lo) * (w.B + w.V + 1)
         el = time.perf_counter() - t0

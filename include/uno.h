@@ -29,6 +29,10 @@
  *    exclusive cumulative probability is below top_p (the first id is always
  *    kept), then renormalise over the kept ids.  NaN logits count as -inf; a
  *    row holding +inf, or no finite logit, is invalid (empty support).
+ *    With order == UNO_ORDER_JOINT (the regular sampler's joint filtering the
+ *    same review thread describes) the top-p cut reads the softmax over the
+ *    whole vocabulary instead, within the top-k set; the kept ids are then
+ *    renormalised.  The orders differ only when top-k and top-p are both on.
  *  - Random numbers: Philox4x32-10 (Salmon et al., SC'11) with counter
  *    (request id, position, offset lo, offset hi) and key (seed lo, seed hi);
  *    word 0 draws proposals, word 1 the acceptance test, word 2 the residual /
@@ -71,10 +75,16 @@ typedef enum {
     UNO_OP_VERIFY_TREE = 3
 } uno_op_t;
 
+typedef enum {
+    UNO_ORDER_TOPK_FIRST = 0,   /* top-k, renormalise, then top-p (default)       */
+    UNO_ORDER_JOINT = 1         /* top-p on the full softmax, within the top-k set */
+} uno_order_t;
+
 typedef struct uno_sampling {
     float temperature;   /* >= 0; 0 = greedy                                  */
     int32_t top_k;       /* <= 0 or >= vocab: off                              */
     float top_p;         /* (0, 1]; 1 = off                                    */
+    int32_t order;       /* uno_order_t; anything else is UNO_ERR_INVALID_ARG   */
 } uno_sampling_t;
 
 /* Largest top_k the sparse (top-k) path accepts.  Larger finite top_k returns

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "UnoError", "Sampling", "library_path", "load_library", "workspace_bytes", "filter_rows",
     "sample_linear", "build_tree", "verify_tree", "OP_FILTER", "OP_SAMPLE_LINEAR",
-    "OP_BUILD_TREE", "OP_VERIFY_TREE", "MAX_TOP_K",
+    "OP_BUILD_TREE", "OP_VERIFY_TREE", "MAX_TOP_K", "ORDER_TOPK_FIRST", "ORDER_JOINT",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,6 +27,7 @@ _lib = None
 
 OP_FILTER, OP_SAMPLE_LINEAR, OP_BUILD_TREE, OP_VERIFY_TREE = 0, 1, 2, 3
 MAX_TOP_K = 256
+ORDER_TOPK_FIRST, ORDER_JOINT = 0, 1     # uno_order_t
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
            -3: "workspace missing, too small or misaligned", -4: "HIP launch failure"}
 
@@ -39,7 +40,7 @@ class UnoError(RuntimeError):
 
 class Sampling(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
-                ("top_p", ctypes.c_float)]
+                ("top_p", ctypes.c_float), ("order", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -98,14 +99,15 @@ def _check(status: int, where: str):
         raise UnoError(status, where)
 
 
-def _sp(temperature, top_k, top_p) -> Sampling:
-    return Sampling(float(temperature), int(top_k), float(top_p))
+def _sp(temperature, top_k, top_p, order=ORDER_TOPK_FIRST) -> Sampling:
+    return Sampling(float(temperature), int(top_k), float(top_p), int(order))
 
 
-def workspace_bytes(op, batch_or_rows, B, K, V, vocab, dtype_code, temperature, top_k, top_p) -> int:
+def workspace_bytes(op, batch_or_rows, B, K, V, vocab, dtype_code, temperature, top_k, top_p,
+                    order=ORDER_TOPK_FIRST) -> int:
     lib = load_library()
     out = ctypes.c_size_t(0)
-    sp = _sp(temperature, top_k, top_p)
+    sp = _sp(temperature, top_k, top_p, order)
     _check(lib.uno_workspace_bytes(op, batch_or_rows, B, K, V, vocab, dtype_code, ctypes.byref(sp),
                                    ctypes.byref(out)), "uno_workspace_bytes")
     return int(out.value)
@@ -137,7 +139,8 @@ def _as_u32_ids(request_ids, batch, device):
     return r.contiguous()
 
 
-def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, stream=None):
+def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, stream=None,
+                order=ORDER_TOPK_FIRST):
     """uno_filter over logits [rows, vocab].  Returns dict of device tensors:
     ids/probs [rows, cap] (sparse modes), count [rows], stats [rows, 2]."""
     lib = load_library()
@@ -150,14 +153,14 @@ def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, str
     sparse = greedy or topk_on or vocab <= MAX_TOP_K
     k_eff = 1 if greedy else (int(top_k) if topk_on else (vocab if sparse else 0))
     cap = (k_eff if sparse else 0) if cap is None else int(cap)
-    nb = workspace_bytes(OP_FILTER, rows, 0, 0, 0, vocab, dt, temperature, top_k, top_p)
+    nb = workspace_bytes(OP_FILTER, rows, 0, 0, 0, vocab, dt, temperature, top_k, top_p, order)
     ws = _workspace(nb, dev, workspace)
     wsp, wsn = _aligned_ptr(ws)
     ids = torch.empty((rows, max(cap, 1)), dtype=torch.int32, device=dev) if sparse else None
     probs = torch.empty((rows, max(cap, 1)), dtype=torch.float64, device=dev) if sparse else None
     count = torch.empty(rows, dtype=torch.int32, device=dev)
     stats = torch.empty((rows, 2), dtype=torch.float64, device=dev)
-    sp = _sp(temperature, top_k, top_p)
+    sp = _sp(temperature, top_k, top_p, order)
     _check(lib.uno_filter(_ptr(logits), dt, rows, vocab, ctypes.byref(sp), cap, _ptr(ids),
                           _ptr(probs), _ptr(count), _ptr(stats), wsp, wsn, _stream(stream)),
            "uno_filter")
@@ -165,7 +168,7 @@ def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, str
 
 
 def sample_linear(draft, target, temperature, top_k, top_p, seed, offset, request_ids=None,
-                  out=None, workspace=None, stream=None):
+                  out=None, workspace=None, stream=None, order=ORDER_TOPK_FIRST):
     """uno_sample_linear: draft [batch, B, vocab], target [batch, B+1, vocab]."""
     lib = load_library()
     assert draft.is_cuda and target.is_cuda and draft.dtype == target.dtype
@@ -180,11 +183,11 @@ def sample_linear(draft, target, temperature, top_k, top_p, seed, offset, reques
                    proposals=torch.empty((batch, B), dtype=torch.int32, device=dev),
                    flags=torch.empty(batch, dtype=torch.int32, device=dev))
     if workspace is None:
-        nb = workspace_bytes(OP_SAMPLE_LINEAR, batch, B, 1, B, vocab, dt, temperature, top_k, top_p)
+        nb = workspace_bytes(OP_SAMPLE_LINEAR, batch, B, 1, B, vocab, dt, temperature, top_k, top_p, order)
         workspace = _workspace(nb, dev, None)
     wsp, wsn = _aligned_ptr(workspace)
     rid = _as_u32_ids(request_ids, batch, dev)
-    sp = _sp(temperature, top_k, top_p)
+    sp = _sp(temperature, top_k, top_p, order)
     _check(lib.uno_sample_linear(_ptr(draft), _ptr(target), dt, batch, B, vocab, ctypes.byref(sp),
                                  int(seed), int(offset), _ptr(rid), _ptr(out["tokens"]),
                                  _ptr(out["accept_len"]), _ptr(out.get("proposals")),
@@ -194,7 +197,8 @@ def sample_linear(draft, target, temperature, top_k, top_p, seed, offset, reques
     return out
 
 
-def build_tree(draft, K, V, temperature, top_k, top_p, out=None, workspace=None, stream=None):
+def build_tree(draft, K, V, temperature, top_k, top_p, out=None, workspace=None, stream=None,
+               order=ORDER_TOPK_FIRST):
     """uno_build_tree: draft [batch, B, vocab] -> node arrays [batch, V+1], num_nodes [batch]."""
     lib = load_library()
     assert draft.is_cuda and draft.is_contiguous()
@@ -208,10 +212,10 @@ def build_tree(draft, K, V, temperature, top_k, top_p, out=None, workspace=None,
                    node_score=torch.empty((batch, V + 1), dtype=torch.float64, device=dev),
                    num_nodes=torch.empty(batch, dtype=torch.int32, device=dev))
     if workspace is None:
-        nb = workspace_bytes(OP_BUILD_TREE, batch, B, K, V, vocab, dt, temperature, top_k, top_p)
+        nb = workspace_bytes(OP_BUILD_TREE, batch, B, K, V, vocab, dt, temperature, top_k, top_p, order)
         workspace = _workspace(nb, dev, None)
     wsp, wsn = _aligned_ptr(workspace)
-    sp = _sp(temperature, top_k, top_p)
+    sp = _sp(temperature, top_k, top_p, order)
     _check(lib.uno_build_tree(_ptr(draft), dt, batch, B, int(K), int(V), vocab, ctypes.byref(sp),
                               _ptr(out["node_token"]), _ptr(out["node_parent"]),
                               _ptr(out["node_depth"]), _ptr(out.get("node_score")),
@@ -221,7 +225,7 @@ def build_tree(draft, K, V, temperature, top_k, top_p, out=None, workspace=None,
 
 
 def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_k, top_p, seed,
-                offset, request_ids=None, out=None, workspace=None, stream=None):
+                offset, request_ids=None, out=None, workspace=None, stream=None, order=ORDER_TOPK_FIRST):
     """uno_verify_tree: target [batch, V+1, vocab] and a tree from build_tree."""
     lib = load_library()
     assert target.is_cuda and target.is_contiguous()
@@ -238,11 +242,11 @@ def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_
                    accept_len=torch.empty(batch, dtype=torch.int32, device=dev),
                    flags=torch.empty(batch, dtype=torch.int32, device=dev))
     if workspace is None:
-        nb = workspace_bytes(OP_VERIFY_TREE, batch, B, 1, V, vocab, dt, temperature, top_k, top_p)
+        nb = workspace_bytes(OP_VERIFY_TREE, batch, B, 1, V, vocab, dt, temperature, top_k, top_p, order)
         workspace = _workspace(nb, dev, None)
     wsp, wsn = _aligned_ptr(workspace)
     rid = _as_u32_ids(request_ids, batch, dev)
-    sp = _sp(temperature, top_k, top_p)
+    sp = _sp(temperature, top_k, top_p, order)
     _check(lib.uno_verify_tree(_ptr(target), dt, batch, int(B), V, vocab, ctypes.byref(sp),
                                int(seed), int(offset), _ptr(rid), _ptr(node_token),
                                _ptr(node_parent), _ptr(num_nodes), _ptr(out["tokens"]),

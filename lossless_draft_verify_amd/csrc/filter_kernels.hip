@@ -287,14 +287,26 @@ __device__ __forceinline__ void finalize_row(uint32_t* sk, const int32_t* sid, d
         }
     } else {
         m = (double)key_float(sk[0]);
-        if (lane == 0) {
-            double acc = 0.0;
+        if (fp.full_cmax) {
+            // joint order: pi takes the full-vocabulary normaliser, combined from
+            // the row's exact chunk sums (each relative to its chunk maximum)
+            const float* cm = fp.full_cmax + r * fp.full_nc;
+            const double* cs = fp.full_csum + r * fp.full_nc;
+            const double T = (double)fp.temperature;
+            double part = 0.0;
+            for (int c = lane; c < fp.full_nc; c += kWave)
+                if (cm[c] > -INFINITY) part += cs[c] * exp(((double)cm[c] - m) / T);
+            S = wave_sum_f64(part);
+        } else {
+            if (lane == 0) {
+                double acc = 0.0;
 #pragma unroll 8
-            for (int i = 0; i < n; ++i) acc += se[i];
-            s_scal[0] = acc;
+                for (int i = 0; i < n; ++i) acc += se[i];
+                s_scal[0] = acc;
+            }
+            wave_sync();
+            S = s_scal[0];
         }
-        wave_sync();
-        S = s_scal[0];
         for (int i = lane; i < n; i += kWave) se[i] = se[i] / S;
         wave_sync();
         int n_keep = n;

@@ -20,6 +20,7 @@ struct Mode {
     bool topk_on;
     bool topp_on;
     bool sparse;     // support from a top-k selection (greedy: k = 1)
+    bool joint;      // joint order with both top-k and top-p on (sparse only)
     int32_t k;       // effective k on the sparse path
 };
 
@@ -29,12 +30,15 @@ int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
     const float T = sp->temperature, p = sp->top_p;
     if (!(T >= 0.0f) || !isfinite(T)) return UNO_ERR_INVALID_ARG;       // temperature >= 0
     if (!(p > 0.0f && p <= 1.0f)) return UNO_ERR_INVALID_ARG;           // top_p in (0, 1]
+    if (sp->order != UNO_ORDER_TOPK_FIRST && sp->order != UNO_ORDER_JOINT) return UNO_ERR_INVALID_ARG;
     m->greedy = (T == 0.0f);
     m->topk_on = sp->top_k > 0 && (int64_t)sp->top_k < vocab;
     m->topp_on = p < 1.0f;
     // a vocabulary of at most UNO_MAX_TOP_K ids is filtered whole by the top-k path
     m->sparse = m->greedy || m->topk_on || vocab <= UNO_MAX_TOP_K;
     m->k = m->greedy ? 1 : (m->topk_on ? sp->top_k : (int32_t)vocab);
+    // the orders differ only when top-k and top-p both act on a sampled row
+    m->joint = sp->order == UNO_ORDER_JOINT && !m->greedy && m->topk_on && m->topp_on;
     if (m->sparse && m->k > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
     if (!m->sparse && m->topp_on) return UNO_ERR_UNSUPPORTED;           // full-vocabulary nucleus
     if (!m->sparse && vocab > (int64_t)65535 * 4 * kDenseChunk) return UNO_ERR_UNSUPPORTED;
@@ -71,10 +75,14 @@ struct SparseWs {
     uint32_t* part_key;
     int32_t* part_id;
     int32_t* part_n;
+    DenseChunks full;    // joint order: exact chunk statistics of the rows
 };
 
-// Supports (when own_supports; in id order with cumulative sums when id_order)
-// and segment partials for `rows` sparse rows.
+DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts);
+
+// Supports (when own_supports; in id order with cumulative sums when id_order),
+// segment partials and, in the joint order, chunk statistics for `rows` sparse
+// rows.
 void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool own_supports, bool id_order,
                   SparseWs* w)
 {
@@ -95,6 +103,8 @@ void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool ow
         w->part_id = cv.take<int32_t>((size_t)rows * w->S * m.k);
         w->part_n = cv.take<int32_t>((size_t)rows * w->S);
     }
+    w->full = DenseChunks{};
+    if (m.joint) w->full = carve_chunks(cv, rows, vocab, false);
 }
 
 // Chunk statistics; the finite counts only for uno_filter, whose dense mode
@@ -144,7 +154,27 @@ FilterParams filter_params(const uno_sampling_t* sp, const Mode& m)
     fp.greedy = m.greedy ? 1 : 0;
     fp.topp_on = m.topp_on ? 1 : 0;
     fp.thr_init = -INFINITY;
+    fp.full_cmax = nullptr;
+    fp.full_csum = nullptr;
+    fp.full_nc = 0;
     return fp;
+}
+
+// The sparse filter of `rows` rows into `out`; the joint order first takes
+// exact chunk statistics of the same rows for the full-softmax normaliser.
+hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
+                                const uno_sampling_t* sp, const Mode& m, const SparseWs& sw,
+                                const SparseOut& out, hipStream_t stream)
+{
+    FilterParams fp = filter_params(sp, m);
+    if (m.joint) {
+        const hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, sw.full, rows, stream);
+        if (e != hipSuccess) return e;
+        fp.full_cmax = sw.full.cmax;
+        fp.full_csum = sw.full.csum;
+        fp.full_nc = sw.full.nchunks;
+    }
+    return launch_topk_filter(src, rows, vocab, bf16, fp, out, sw.S, sw.part_key, sw.part_id, sw.part_n, stream);
 }
 
 int check_tree_shape(int32_t B, int32_t K, int32_t V, bool need_k)
@@ -270,8 +300,7 @@ int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab, c
     const bool bf16 = dtype == UNO_BF16;
     if (m.sparse) {
         SparseOut out{ out_ids, out_probs, out_count, out_stats, cap };
-        return hip_status(launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, m), out, sw.S,
-                                             sw.part_key, sw.part_id, sw.part_n, stream));
+        return hip_status(launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, out, stream));
     }
     hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
     if (e == hipSuccess) e = launch_dense_row_stats(rows, sp->temperature, dc, out_count, out_stats, stream);
@@ -308,8 +337,7 @@ int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int3
     LinearOut o{ out_tokens, out_accept_len, out_proposals, out_flags };
     hipError_t e;
     if (m.sparse) {
-        e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, m), sw.sup, sw.S, sw.part_key,
-                               sw.part_id, sw.part_n, stream);
+        e = launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, sw.sup, stream);
         if (e == hipSuccess) e = launch_linear_sparse(batch, B, sw.sup, seed, offset, request_ids, o, stream);
     } else {
         // draft rows are sampled from (exact sums); target rows enter only
@@ -348,8 +376,7 @@ int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, i
     RowSource src{ static_cast<const char*>(draft), rows, nullptr, nullptr, 1 };
     hipError_t e;
     if (m.sparse) {
-        e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, m), sw.sup, sw.S, sw.part_key,
-                               sw.part_id, sw.part_n, stream);
+        e = launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, sw.sup, stream);
     } else {
         // full-vocabulary filter: exact row normalisers, the K best ids, then
         // their probabilities under the full softmax
@@ -396,8 +423,7 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
     WalkOut o{ out_tokens, out_path, out_accept_len, out_flags };
     hipError_t e;
     if (m.sparse) {
-        e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, m), sw.sup, sw.S, sw.part_key,
-                               sw.part_id, sw.part_n, stream);
+        e = launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, sw.sup, stream);
         if (e == hipSuccess)
             e = launch_tree_walk(batch, B, V, sw.sup, seed, offset, request_ids, node_token, node_parent,
                                  num_nodes, o, stream);

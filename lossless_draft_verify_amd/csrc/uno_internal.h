@@ -26,6 +26,11 @@ struct FilterParams {
     int32_t greedy;   // temperature == 0
     int32_t topp_on;  // top_p < 1
     float thr_init;   // -inf: initial admission threshold of the top-k stream
+    // joint order: exact chunk statistics of the same rows, whose full-softmax
+    // normaliser the top-p cut reads (null in the default order)
+    const float* full_cmax;
+    const double* full_csum;
+    int32_t full_nc;
 };
 
 // Compact per-row supports in filter order.

@@ -34,8 +34,8 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:int|const char\*|size_t)\s+(uno_\w+)\s*\(", text, re.M)))
 
 
-def sp(T=1.0, k=50, p=0.95):
-    return ctypes.byref(uno.Sampling(T, k, p))
+def sp(T=1.0, k=50, p=0.95, order=0):
+    return ctypes.byref(uno.Sampling(T, k, p, order))
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -90,6 +90,14 @@ def test_workspace_sizes(lib):
     assert st == OK and nbd >= 16 * nch * (4 + 8) + 16 * 32 * (4 + 8) + 16 * 16
     st, nvd = _ws(lib, uno.OP_VERIFY_TREE, 1, 16, 1, 32, N, F32, sp(1.0, 0, 1.0))
     assert st == OK and nvd >= 33 * nch * (4 + 8)
+    # joint order: exact chunk statistics of every filtered row on top of the supports
+    st, nj = _ws(lib, uno.OP_SAMPLE_LINEAR, 64, 8, 1, 8, N, F32, sp(order=uno.ORDER_JOINT))
+    assert st == OK and nj >= n + 1088 * nch * (4 + 8)
+    st, nfj = _ws(lib, uno.OP_FILTER, 4096, 0, 0, 0, N, F32, sp(order=uno.ORDER_JOINT))
+    assert st == OK and nfj >= 4096 * nch * (4 + 8)
+    # ... which the orders share when only one filter is on
+    st, n1 = _ws(lib, uno.OP_SAMPLE_LINEAR, 64, 8, 1, 8, N, F32, sp(1.0, 50, 1.0, uno.ORDER_JOINT))
+    assert st == OK and n1 == _ws(lib, uno.OP_SAMPLE_LINEAR, 64, 8, 1, 8, N, F32, sp(1.0, 50, 1.0))[1]
     # filter with many rows needs nothing beyond the caller's outputs
     st, nf = _ws(lib, uno.OP_FILTER, 4096, 0, 0, 0, N, F32, sp())
     assert st == OK and nf == 0
@@ -176,3 +184,14 @@ def test_tree_argument_checks(lib):
     assert vt() == WORKSPACE
     # greedy decoding is a sparse (k = 1) mode
     assert vt(s=sp(0.0, 0, 1.0)) == WORKSPACE
+
+
+@pytest.mark.parametrize("order", [-1, 2, 7])
+def test_unknown_filter_order_is_rejected(lib, order):
+    o = ctypes.c_void_p(0x30000)
+    n = ctypes.c_size_t(0)
+    assert lib.uno_workspace_bytes(uno.OP_FILTER, 4, 0, 0, 0, 1000, F32, sp(order=order),
+                                   ctypes.byref(n)) == INVALID
+    assert lib.uno_filter(FAKE, F32, 4, 1000, sp(order=order), 64, o, o, o, o, None, 0, None) == INVALID
+    assert lib.uno_sample_linear(FAKE, FAKE, F32, 2, 4, 1000, sp(order=order), 1, 0, None, o, o, None,
+                                 None, None, 0, None) == INVALID

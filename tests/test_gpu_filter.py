@@ -14,14 +14,14 @@ def _rows(rng, rows, N, scale=2.0):
     return (rng.standard_normal((rows, N)) * scale).astype(np.float32)
 
 
-def _check_sparse(z32, dtype, T, k, p, label):
+def _check_sparse(z32, dtype, T, k, p, label, order=uno.ORDER_TOPK_FIRST):
     dev = device()
     zt = torch.from_numpy(z32).to(dev).to(dtype).contiguous()
     zh = zt.float().cpu().numpy()                     # exact values the GPU sees
-    g = uno.filter_rows(zt, T, k, p)
+    g = uno.filter_rows(zt, T, k, p, order=order)
     torch.cuda.synchronize()
     cap = g["ids"].shape[1]
-    o = oracle.filter_rows(zh, T, k, p, cap=cap, dense=False)
+    o = oracle.filter_rows(zh, T, k, p, cap=cap, dense=False, order=order)
     gn, gi, gp = np_of(g["count"]), np_of(g["ids"]), np_of(g["probs"])
     # rows whose top-p cut sits within rounding of the threshold may cut differently
     near = o["margin"] < 1e-9
@@ -39,6 +39,13 @@ def _check_sparse(z32, dtype, T, k, p, label):
         worst = max(worst, float(rel.max()))
     assert worst <= 1e-5, (label, worst)          # parity bar on filtered probabilities
     assert worst <= 1e-12, (label, worst)         # same fp64 operations; only exp may differ by an ulp
+    if order == uno.ORDER_JOINT and T > 0:
+        # the statistics carry the full-vocabulary normaliser, summed in another
+        # order: within the error bound of a recursive sum of N positive terms
+        ok = o["n"] > 0
+        gs = np_of(g["stats"])
+        assert np.array_equal(gs[ok, 0], o["stats"][ok, 0]), label
+        np.testing.assert_allclose(gs[ok, 1], o["stats"][ok, 1], rtol=2 * zh.shape[1] * 2.0**-53, atol=0)
     say(f"{label}: rows {zh.shape[0]} max rel err {worst:.2e} near-cut rows {int(near.sum())}")
 
 
@@ -137,3 +144,36 @@ def test_filter_is_deterministic():
     torch.cuda.synchronize()
     for key in ("ids", "probs", "count"):
         assert torch.equal(a[key], b[key])
+
+
+# ---- joint filter order: the top-p cut on the full-vocabulary softmax ------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("T,k,p", [(1.0, 50, 0.95), (0.7, 20, 0.8), (1.3, 256, 0.9), (1.0, 7, 0.5),
+                                   (0.0, 50, 0.9), (1.0, 50, 1.0)])
+def test_joint_order_ragged_vocab(dtype, T, k, p):
+    rng = np.random.default_rng(300 + k)
+    z = _rows(rng, 1100, 1003)
+    _check_sparse(z, dtype, T, k, p, f"joint ragged {dtype} T{T} k{k} p{p}", order=uno.ORDER_JOINT)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows", [6, 1040])
+def test_joint_order_full_vocab(dtype, rows):
+    # 6 rows: segments and the merge kernel; 1040 rows: one workgroup per row
+    rng = np.random.default_rng(9)
+    N = 151936
+    rank = np.argsort(rng.random((rows, N)), axis=1).astype(np.float32)
+    z = (-1.2 * np.log1p(rank) + rng.standard_normal((rows, N))).astype(np.float32)
+    _check_sparse(z, dtype, 1.0, 50, 0.95, f"joint full-vocab {rows} rows {dtype}", order=uno.ORDER_JOINT)
+
+
+def test_joint_order_keeps_at_least_the_default_support():
+    dev = device()
+    rng = np.random.default_rng(13)
+    z = torch.from_numpy(_rows(rng, 500, 4000)).to(dev)
+    a = uno.filter_rows(z, 1.0, 40, 0.9)
+    b = uno.filter_rows(z, 1.0, 40, 0.9, order=uno.ORDER_JOINT)
+    torch.cuda.synchronize()
+    na, nb = np_of(a["count"]), np_of(b["count"])
+    assert np.all(nb >= na) and np.all(nb <= 40) and np.any(nb > na)

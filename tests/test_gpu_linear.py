@@ -12,12 +12,13 @@ from stats_util import chisq_pvalue
 pytestmark = pytest.mark.gpu
 
 
-def _run(draft, target, T, k, p, seed, offset, request_ids=None, tally=None, label=""):
-    g = uno.sample_linear(draft, target, T, k, p, seed, offset, request_ids=request_ids)
+def _run(draft, target, T, k, p, seed, offset, request_ids=None, tally=None, label="",
+         order=uno.ORDER_TOPK_FIRST):
+    g = uno.sample_linear(draft, target, T, k, p, seed, offset, request_ids=request_ids, order=order)
     torch.cuda.synchronize()
     rid = None if request_ids is None else np.asarray(request_ids, dtype=np.uint32)
     o = oracle.linear(synth.as_float32_numpy(draft), synth.as_float32_numpy(target), T, k, p,
-                      seed=seed, offset=offset, request_ids=rid)
+                      seed=seed, offset=offset, request_ids=rid, order=order)
     gg = dict(tokens=np_of(g["tokens"]), accept_len=np_of(g["accept_len"]),
               proposals=np_of(g["proposals"]))
     t = tally or Tally()
@@ -25,14 +26,14 @@ def _run(draft, target, T, k, p, seed, offset, request_ids=None, tally=None, lab
     return gg, o
 
 
-def _cycles(w, n, batch=None, label=None):
+def _cycles(w, n, batch=None, label=None, order=uno.ORDER_TOPK_FIRST):
     dev = device()
     tally = Tally()
     acc = []
     for c in range(n):
         draft, target = synth.linear_inputs(w, cycle=c, device=dev, batch=batch)
         gg, o = _run(draft, target, w.temperature, w.top_k, w.top_p, w.seed, c, tally=tally,
-                     label=f"{label or w.name} cycle {c}")
+                     label=f"{label or w.name} cycle {c}", order=order)
         acc.append(gg["accept_len"])
     tally.check_rate()
     a = np.concatenate(acc)
@@ -138,3 +139,25 @@ def test_linear_is_deterministic():
     torch.cuda.synchronize()
     for key in ("tokens", "accept_len", "proposals"):
         assert torch.equal(a[key], b[key])
+
+
+def test_linear_8_1_8_joint_order():
+    # the headline workload with the joint filter order (full batch, two cycles)
+    _cycles(synth.WORKLOADS["linear_8_1_8"], 2, label="linear_8_1_8 joint", order=uno.ORDER_JOINT)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("T,k,p", [(1.0, 20, 0.8), (0.7, 256, 0.95)])
+def test_joint_order_small_vocab(dtype, T, k, p):
+    dev = device()
+    rng = np.random.default_rng(33)
+    batch, B, N = 24, 5, 3001
+    R = rng.standard_normal((batch, B + 1, N)).astype(np.float32) * 2
+    d = (R[:, :B] + 0.5 * rng.standard_normal((batch, B, N))).astype(np.float32)
+    draft = torch.from_numpy(d).to(dev).to(dtype).contiguous()
+    target = torch.from_numpy(R).to(dev).to(dtype).contiguous()
+    t = Tally()
+    for c in range(3):
+        _run(draft, target, T, k, p, 5, c, tally=t, label=f"joint {dtype} T{T} k{k} p{p}",
+             order=uno.ORDER_JOINT)
+    t.check_rate()

@@ -256,3 +256,32 @@ def test_dense_walk_is_lossless():
                 assert chisq_pvalue(tok[sel, dd], P[node]) > 1e-4, (node, dd)
                 checked += 1
     assert checked >= 2
+
+
+
+def test_tree_joint_order():
+    # tree 8/16/8 rows (reduced batch) with the joint filter order for build and walk
+    dev = device()
+    w = synth.WORKLOADS["tree_8_16_8"]
+    t = Tally()
+    for c in range(2):
+        draft, R = synth.tree_inputs(w, cycle=c, device=dev, batch=8)
+        g = uno.build_tree(draft, w.K, w.V, w.temperature, w.top_k, w.top_p, order=uno.ORDER_JOINT)
+        torch.cuda.synchronize()
+        o = oracle.build_tree(synth.as_float32_numpy(draft), w.K, w.V, w.temperature, w.top_k, w.top_p,
+                              order=oracle.ORDER_JOINT)
+        for key in TREE_KEYS:
+            bad = np.any(np_of(g[key]).reshape(8, -1) != o[key].reshape(8, -1), axis=1)
+            assert not np.any(bad & (o["min_gap"] >= 1e-12)), (key, c)
+        tgt = synth.tree_target_rows(R, torch.from_numpy(o["node_depth"]), torch.from_numpy(o["num_nodes"]), w.V)
+        dv = tgt.device
+        gv = uno.verify_tree(tgt, w.B, torch.from_numpy(o["node_token"]).to(dv),
+                             torch.from_numpy(o["node_parent"]).to(dv), torch.from_numpy(o["num_nodes"]).to(dv),
+                             w.temperature, w.top_k, w.top_p, w.seed, c, order=uno.ORDER_JOINT)
+        torch.cuda.synchronize()
+        ov = oracle.verify_tree(synth.as_float32_numpy(tgt), w.B, o["node_token"], o["node_parent"],
+                                o["num_nodes"], w.temperature, w.top_k, w.top_p, seed=w.seed, offset=c,
+                                order=oracle.ORDER_JOINT)
+        t.compare({k: np_of(gv[k]) for k in ("tokens", "path", "accept_len")}, ov,
+                  ("tokens", "path", "accept_len"), f"tree joint {c}")
+    t.check_rate()
