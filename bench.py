@@ -101,7 +101,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the sampling path has no multi-GPU component in this build).", file=sys.stderr)
+              "(the sampling path runs on one GPU; requests shard across GPUs with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
     UNO_OK = 0,
     UNO_ERR_INVALID_ARG = -1,   /* a size, pointer or parameter is out of range      */
-    UNO_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement        */
+    UNO_ERR_UNSUPPORTED = -2,   /* valid request the library does not implement      */
     UNO_ERR_WORKSPACE = -3,     /* ws is NULL, too small or misaligned                 */
     UNO_ERR_HIP = -4            /* a HIP launch failed (see uno_last_hip_error)        */
 } uno_status_t;
