@@ -231,3 +231,27 @@ def test_joint_is_the_smallest_prefix_reaching_top_p():
         assert ids[:len(ids_default)] == ids_default and len(ids_default) <= L
         checked += 1
     assert checked > 250
+
+
+def test_full_vocabulary_nucleus_is_the_smallest_prefix():
+    # top-k off, top-p on: brute force over the whole row (scipy softmax, stable
+    # sort): the support is the shortest (z desc, id asc) prefix whose mass reaches
+    # top_p, ties at the cut going to the smaller ids; coarse values make ties common
+    rng = np.random.default_rng(21)
+    checked = 0
+    for trial in range(120):
+        N = int(rng.integers(300, 3000))
+        T = float(np.float32(rng.choice([0.6, 1.0, 1.5])))
+        p = float(np.float32(rng.uniform(0.3, 0.99)))
+        z = (np.round(rng.standard_normal(N) * 8) / 4).astype(np.float32)
+        order = sorted(range(N), key=lambda i: (-float(z[i]), i))
+        full = softmax(z.astype(np.float64) / T)
+        mass = np.cumsum(full[order])
+        if np.any(np.abs(mass - p) < 1e-9):
+            continue
+        L = int(np.argmax(mass >= p)) + 1
+        ids, pr = _support(oracle.filter_rows(z, T, 0, p))
+        assert ids == order[:L], trial
+        np.testing.assert_allclose(pr, full[order[:L]] / full[order[:L]].sum(), rtol=1e-12)
+        checked += 1
+    assert checked > 100
