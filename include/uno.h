@@ -110,15 +110,16 @@ int uno_workspace_bytes(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K,
  *   support hold -1 / 0.  out_count[rows] = support size, -1 for an invalid row.
  *   cap must be >= the effective top-k (1 when temperature == 0, vocab when
  *   top-k is off on a small vocabulary).
- * Dense mode (top-k off, top_p == 1, temperature > 0, vocab > UNO_MAX_TOP_K): the
- *   support is the whole
- *   vocabulary; out_ids / out_probs are not written (may be NULL) and
- *   out_count[r] = number of finite logits (-1: invalid row).
- * out_stats [rows][2] (nullable in sparse modes, required in dense mode):
+ * Dense modes (top-k off, temperature > 0, vocab > UNO_MAX_TOP_K): out_ids /
+ *   out_probs are not written (may be NULL).
+ *   - top_p == 1: the support is the whole vocabulary; out_count[r] = number
+ *     of finite logits (-1: invalid row).
+ *   - top_p < 1 (full-vocabulary nucleus): the support is the shortest prefix
+ *     of the filter order whose softmax mass reaches top_p; out_count[r] = its
+ *     size (-1: invalid row).
+ * out_stats [rows][2] (nullable in sparse modes, required in dense modes):
  *   (m, S) such that the probability before any top-p renormalisation is
- *   exp((z - m) / T) / S; m is the row maximum.
- * Top-k off with top_p < 1 on a vocabulary above UNO_MAX_TOP_K (full-vocabulary
- * nucleus) returns UNO_ERR_UNSUPPORTED. */
+ *   exp((z - m) / T) / S; m is the row maximum. */
 int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab,
                const uno_sampling_t* sp, int32_t cap,
                int32_t* out_ids, double* out_probs, int32_t* out_count, double* out_stats,
@@ -139,9 +140,8 @@ int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab,
  *   out_flags [batch] (nullable): bit 0 = an invalid row was met, bit 1 = the
  *     residual had no mass
  *   request_ids [batch] (nullable device pointer): Philox request ids
- * Sparse (top-k on, greedy, or vocab <= UNO_MAX_TOP_K) and dense (top-k off,
- * top_p == 1) filters are supported; top-k off with top_p < 1 on a larger
- * vocabulary returns UNO_ERR_UNSUPPORTED. */
+ * Sparse (top-k on, greedy, or vocab <= UNO_MAX_TOP_K) and dense (top-k off:
+ * the whole vocabulary, or its nucleus when top_p < 1) filters are supported. */
 int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int32_t batch,
                       int32_t B, int64_t vocab, const uno_sampling_t* sp, uint64_t seed,
                       uint64_t offset, const uint32_t* request_ids,
@@ -159,7 +159,8 @@ int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int3
  *   node_token / node_parent / node_depth [batch][V+1] (unused slots: -1)
  *   node_score [batch][V+1] (nullable; unused slots 0)
  *   num_nodes [batch]: nodes including the root (< V+1 when candidates run out)
- * Requires 1 <= K, B <= V <= 128 and V * K <= 2048.  A filter that keeps the
+ * Requires 1 <= K, B <= V <= 128 and V * K <= 2048; a full-vocabulary nucleus
+ * (top-k off, top_p < 1) returns UNO_ERR_UNSUPPORTED.  A filter that keeps the
  * whole vocabulary (top-k off, top_p == 1, temperature > 0) takes the K most
  * likely ids of the full softmax, with their full-softmax probabilities, and
  * needs K <= UNO_MAX_TOP_K (else UNO_ERR_UNSUPPORTED). */
@@ -180,7 +181,8 @@ int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, i
  * child of n whose token is t, else stop.
  *   out_tokens [batch][B+1], out_path [batch][B+1] (visited nodes), -1 padded
  *   out_accept_len [batch] in [1, B+1]; out_flags as in uno_sample_linear.
- * Requires B <= V <= 128.  With a filter that keeps the whole vocabulary
+ * Requires B <= V <= 128; a full-vocabulary nucleus (top-k off, top_p < 1)
+ * returns UNO_ERR_UNSUPPORTED.  With a filter that keeps the whole vocabulary
  * (top-k off, top_p == 1, temperature > 0) each node's token is drawn from the
  * full softmax of its row: the fallback the PR names for tree verification
  * when sparse target sampling does not apply (PR #37667, Modifications). */

@@ -183,10 +183,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 }
 
 // Filter-order position key: larger means earlier (key desc, then id asc).
-__device__ __forceinline__ uint64_t order_key(uint32_t key, int32_t id)
-{
-    return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)id);
-}
 
 // Block-wide ranking of the candidates held in L lists (list o: lst[o*stride ..
 // o*stride + cnt[o]) in LDS, entries (key, id), distinct ids): the entry at

@@ -769,10 +769,30 @@ __device__ double chunk_total(WeightF wf, int lane)
     return run;
 }
 
-// Sample a dense filtered row p = exp((z - m)/T) / S with uniform u.
+// Support test of a dense row: finite, and at or above the row's keep
+// threshold (0 keeps every finite logit).
+__device__ __forceinline__ bool dense_keeps(uint64_t thr, float x, int64_t id)
+{
+    return finite_f32(x) && order_key(float_key(x), (int32_t)id) >= thr;
+}
+
+// Id of entry i of chunk c as load_chunk lays it out in this lane.
+template <int EPV>
+__device__ __forceinline__ int64_t chunk_elem_id(int64_t c, int i, int lane)
+{
+    return c * kDenseChunk + (int64_t)((i / EPV) * kWave + lane) * EPV + i % EPV;
+}
+
+__device__ __forceinline__ uint64_t row_keep(const DenseChunks& dc, int64_t r)
+{
+    return dc.keep ? dc.keep[r] : 0ull;
+}
+
+// Sample a dense filtered row p = exp((z - m)/T) / S (over the logits the keep
+// threshold admits) with uniform u.
 template <bool BF16>
 __device__ int32_t dense_sample_row(const char* row, int64_t N, const float* cm, const double* cs, int nc,
-                                    float m, double S, double u, const DenseExp& ex, int lane)
+                                    float m, double S, double u, const DenseExp& ex, int lane, uint64_t thr)
 {
     auto term = [&](int c) { return chunk_term(cm, cs, c, m, ex); };
     const double t = u * S;
@@ -789,7 +809,8 @@ __device__ int32_t dense_sample_row(const char* row, int64_t N, const float* cm,
     float x[kPerLane];
     load_chunk<BF16>(row, N, c, x, lane);
     const double mc = (double)cm[c];
-    auto wf = [&](int i) { return finite_f32(x[i]) ? ex((double)x[i] - mc) : 0.0; };
+    constexpr int EPV = Vec<BF16>::EPV;
+    auto wf = [&](int i) { return dense_keeps(thr, x[i], chunk_elem_id<EPV>(c, i, lane)) ? ex((double)x[i] - mc) : 0.0; };
     const int l = pick_in_chunk<Vec<BF16>::EPV>(wf, tau, lane);
     return l < 0 ? -1 : (int32_t)(c * (int64_t)kDenseChunk + l);
 }
@@ -851,7 +872,8 @@ __global__ __launch_bounds__(kDenseThreads) void dense_propose_kernel(
         int32_t y = -1;
         int acc = 0;
         if (Sq > 0.0) {
-            y = dense_sample_row<BF16>(qrow, N, dc.cmax + qr * nc, dc.csum + qr * nc, nc, mq, Sq, d.u[0], ex, lane);
+            y = dense_sample_row<BF16>(qrow, N, dc.cmax + qr * nc, dc.csum + qr * nc, nc, mq, Sq, d.u[0], ex, lane,
+                                       row_keep(dc, qr));
         } else {
             flags |= 1u;
         }
@@ -860,7 +882,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_propose_kernel(
             double py = 0.0;
             if (Sp > 0.0) {
                 const float zp = load_one<BF16>(prow, y);
-                if (finite_f32(zp)) py = ex((double)zp - (double)mp) / Sp;
+                if (dense_keeps(row_keep(dc, pr), zp, y)) py = ex((double)zp - (double)mp) / Sp;
             } else {
                 flags |= 1u;
             }
@@ -948,13 +970,16 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
         if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
         const double mp = (double)mpf, mq = (double)row_m[qr];
         const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
+        const uint64_t tp = row_keep(dc, pr), tq = row_keep(dc, qr);
+        constexpr int EPV = Vec<BF16>::EPV;
         auto wf = [&](int i) {
-            const double pv = finite_f32(xp[i]) ? ex((double)xp[i] - mp) * iSp : 0.0;
-            const double qv = (q_ok && finite_f32(xq[i])) ? ex((double)xq[i] - mq) * iSq : 0.0;
+            const int64_t id = chunk_elem_id<EPV>(c, i, lane);
+            const double pv = dense_keeps(tp, xp[i], id) ? ex((double)xp[i] - mp) * iSp : 0.0;
+            const double qv = (q_ok && dense_keeps(tq, xq[i], id)) ? ex((double)xq[i] - mq) * iSq : 0.0;
             const double dl = pv - qv;
             return dl > 0.0 ? dl : 0.0;
         };
-        total = chunk_total<Vec<BF16>::EPV>(wf, lane);
+        total = chunk_total<EPV>(wf, lane);
     }
     if (lane == 0) resid[(int64_t)b * nc + c] = total;
 }
@@ -1010,27 +1035,217 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
             if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
             const double mpd = (double)mp, mq = (double)row_m[qr];
             const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
+            const uint64_t tp = row_keep(dc, pr), tq = row_keep(dc, qr);
+            constexpr int EPV = Vec<BF16>::EPV;
             auto wf = [&](int i) {
-                const double pv = finite_f32(xp[i]) ? ex((double)xp[i] - mpd) * iSp : 0.0;
-                const double qv = (q_ok && finite_f32(xq[i])) ? ex((double)xq[i] - mq) * iSq : 0.0;
+                const int64_t id = chunk_elem_id<EPV>(c, i, lane);
+                const double pv = dense_keeps(tp, xp[i], id) ? ex((double)xp[i] - mpd) * iSp : 0.0;
+                const double qv = (q_ok && dense_keeps(tq, xq[i], id)) ? ex((double)xq[i] - mq) * iSq : 0.0;
                 const double dl = pv - qv;
                 return dl > 0.0 ? dl : 0.0;
             };
-            const int l = pick_in_chunk<Vec<BF16>::EPV>(wf, tau, lane);
+            const int l = pick_in_chunk<EPV>(wf, tau, lane);
             fin = l < 0 ? -1 : (int32_t)(c * (int64_t)kDenseChunk + l);
         } else {
             fl |= 2u;
         }
         if (fin < 0)
-            fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp, d.u[2], ex, lane);
+            fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp, d.u[2], ex, lane,
+                                         row_keep(dc, pr));
     } else {
-        fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp, d.u[2], ex, lane);
+        fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp, d.u[2], ex, lane,
+                                     row_keep(dc, pr));
     }
     int32_t* tok = o.tokens + (int64_t)b * (B + 1);
     for (int j = lane; j <= B; j += kWave) tok[j] = (j < js) ? y_in[(int64_t)b * B + j] : (j == js ? fin : -1);
     if (lane == 0) {
         o.accept_len[b] = js + 1;
         if (o.flags) o.flags[b] = fl;
+    }
+}
+
+// ---- full-vocabulary nucleus (top-p without top-k) -------------------------------
+// The support is the shortest prefix of the filter order (z desc, id asc) whose
+// mass reaches top_p (the first logit always kept).  One workgroup per row
+// finds the cut by a mass-weighted radix select over the 32-bit order keys of
+// the logits -- 11, 11, then 10 bits, one pass over the row per digit, each
+// digit's bins holding the exact fp64 mass exp((z - m)/T) of their logits --
+// and the number of tied logits at the cut from the mass left; the cut among
+// the ties (smaller ids first) comes from an ordered count over ids.  The
+// row's keep threshold is the order key of its last kept logit; the chunk
+// sums are then rewritten over the support.
+constexpr int kNucThreads = 256;
+constexpr int kNucWaves = kNucThreads / kWave;
+constexpr int kNucBins = 2048;
+
+template <bool BF16>
+__global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int64_t N, double log2e_over_T,
+                                                              double top_p, DenseChunks dc, int32_t* out_count,
+                                                              double* out_stats)
+{
+    __shared__ double s_exp2[kExp2Entries];
+    __shared__ double s_mass[kNucBins];
+    __shared__ uint32_t s_cnt[kNucBins];
+    __shared__ double s_row[2];              // S, mass above the cut's bin
+    __shared__ float s_m;
+    __shared__ int64_t s_cab;                // logits above the cut's bin
+    __shared__ int s_bin;
+    __shared__ int64_t s_wc[kNucWaves];
+    __shared__ int32_t s_idlim;
+    constexpr int EPV = Vec<BF16>::EPV;
+    load_exp2_table(s_exp2);
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t r = blockIdx.x;
+    const int nc = dc.nchunks;
+    const float* cm = dc.cmax + r * nc;
+    double* cs = dc.csum + r * nc;
+    const char* row = row_pointer(src, r, N * Vec<BF16>::ESZ);
+    const DenseExp ex{ log2e_over_T, s_exp2 };
+    __syncthreads();
+    if (w == 0) {
+        float m = NAN;
+        double S = -1.0;
+        const bool ok = row != nullptr && dense_row_stat(cm, cs, nc, ex, lane, &m, &S);
+        if (lane == 0) { s_row[0] = ok ? S : -1.0; s_m = m; }
+    }
+    __syncthreads();
+    const double S = s_row[0];
+    const float m = s_m;
+    if (!(S > 0.0)) {                        // invalid or absent row: an empty support
+        if (threadIdx.x == 0) {
+            dc.keep[r] = ~0ull;
+            if (out_count) out_count[r] = -1;
+            if (out_stats) { out_stats[2 * r] = NAN; out_stats[2 * r + 1] = NAN; }
+        }
+        return;
+    }
+    const double target = top_p * S;
+    uint32_t prefix = 0;
+    int pbits = 0;
+    double A = 0.0;
+    int64_t cab = 0;
+    for (int level = 0; level < 3; ++level) {
+        const int bits = level < 2 ? 11 : 10;
+        const int nb = 1 << bits;
+        const int shift = 32 - pbits - bits;
+        for (int b = (int)threadIdx.x; b < nb; b += kNucThreads) { s_mass[b] = 0.0; s_cnt[b] = 0u; }
+        __syncthreads();
+        for (int64_t i = threadIdx.x; i < N; i += kNucThreads) {
+            const float v = load_scalar<BF16>(row, i);
+            if (!finite_f32(v)) continue;
+            const uint32_t key = float_key(v);
+            if (pbits > 0 && (key >> (32 - pbits)) != prefix) continue;
+            const int bin = (int)((key >> shift) & (uint32_t)(nb - 1));
+            atomicAdd(&s_mass[bin], ex((double)v - (double)m));
+            atomicAdd(&s_cnt[bin], 1u);
+        }
+        __syncthreads();
+        if (w == 0) {
+            // bins from the top down: the first non-empty bin whose inclusive
+            // mass reaches the target holds the last kept logit
+            double run = A, crun = (double)cab;
+            int found = -1, last = -1;
+            double fa = 0.0, fc = 0.0, la = 0.0, lc = 0.0;
+            for (int top = nb - 1; top >= 0 && found < 0; top -= kWave) {
+                const int b = top - lane;
+                const double mb = b >= 0 ? s_mass[b] : 0.0;
+                const double cb = b >= 0 ? (double)s_cnt[b] : 0.0;
+                const double incl = wave_incl_scan_f64(mb, lane);
+                const double cincl = wave_incl_scan_f64(cb, lane);
+                const uint64_t hit = __ballot(cb > 0.0 && run + incl >= target);
+                if (hit) {
+                    const int l = wave_first_lane(hit);
+                    found = top - l;
+                    fa = run + __shfl(incl - mb, l, kWave);
+                    fc = crun + __shfl(cincl - cb, l, kWave);
+                } else {
+                    const uint64_t nz = __ballot(cb > 0.0);
+                    if (nz) {
+                        const int l = 63 - __clzll((long long)nz);
+                        last = top - l;
+                        la = run + __shfl(incl - mb, l, kWave);
+                        lc = crun + __shfl(cincl - cb, l, kWave);
+                    }
+                    run += __shfl(incl, kWave - 1, kWave);
+                    crun += __shfl(cincl, kWave - 1, kWave);
+                }
+            }
+            if (found < 0) { found = last; fa = la; fc = lc; }   // target past the summed mass: keep all
+            if (lane == 0) { s_bin = found; s_row[1] = fa; s_cab = (int64_t)fc; }
+        }
+        __syncthreads();
+        prefix = (prefix << bits) | (uint32_t)s_bin;
+        pbits += bits;
+        A = s_row[1];
+        cab = s_cab;
+    }
+    // ties at the cut: keep the j-th (by id) while the mass before it is below
+    // the target
+    const uint32_t tau = prefix;
+    const int64_t ctau = (int64_t)s_cnt[s_bin];
+    const double etau = ex((double)key_float(tau) - (double)m);
+    int64_t t = ctau;
+    if (etau > 0.0) {
+        const double x = ceil((target - A) / etau);
+        t = x < 1.0 ? 1 : (x < (double)ctau ? (int64_t)x : ctau);
+    }
+    // the t-th tie in id order: each wave counts its quarter of the ids, then
+    // the wave holding it finds it
+    const int64_t q0 = N * w / kNucWaves, q1 = N * (w + 1) / kNucWaves;
+    int64_t cw = 0;
+    for (int64_t base = q0; base < q1; base += kWave) {
+        const int64_t i = base + lane;
+        bool mt = false;
+        if (i < q1) {
+            const float v = load_scalar<BF16>(row, i);
+            mt = finite_f32(v) && float_key(v) == tau;
+        }
+        cw += __popcll(__ballot(mt));
+    }
+    if (lane == 0) s_wc[w] = cw;
+    __syncthreads();
+    int64_t before = 0;
+    for (int o = 0; o < w; ++o) before += s_wc[o];
+    if (t > before && t <= before + cw) {
+        int64_t need = t - before;
+        for (int64_t base = q0; base < q1; base += kWave) {
+            const int64_t i = base + lane;
+            bool mt = false;
+            if (i < q1) {
+                const float v = load_scalar<BF16>(row, i);
+                mt = finite_f32(v) && float_key(v) == tau;
+            }
+            const uint64_t mk = __ballot(mt);
+            const int pc = __popcll(mk);
+            if (need <= pc) {
+                const uint64_t at = __ballot(mt && __popcll(mk & lanes_below(lane)) + 1 == need);
+                if (lane == 0) s_idlim = (int32_t)(base + wave_first_lane(at));
+                break;
+            }
+            need -= pc;
+        }
+    }
+    __syncthreads();
+    const uint64_t thr = order_key(tau, s_idlim);
+    // chunk sums over the support, relative to each chunk's (unchanged) maximum
+    for (int c = w; c < nc; c += kNucWaves) {
+        double sum = 0.0;
+        if (cm[c] > -INFINITY) {
+            float x[kPerLane];
+            load_chunk<BF16>(row, N, c, x, lane);
+            const double mc = (double)cm[c];
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i)
+                if (dense_keeps(thr, x[i], chunk_elem_id<EPV>(c, i, lane))) sum += ex((double)x[i] - mc);
+        }
+        sum = wave_sum_f64(sum);
+        if (lane == 0) cs[c] = sum;
+    }
+    if (threadIdx.x == 0) {
+        dc.keep[r] = thr;
+        if (out_count) out_count[r] = (int32_t)(cab + t);
+        if (out_stats) { out_stats[2 * r] = (double)m; out_stats[2 * r + 1] = S; }
     }
 }
 
@@ -1071,7 +1286,8 @@ __global__ __launch_bounds__(kWalkThreads) void dense_walk_kernel(
             double S;
             if (dense_row_stat(cm, cs, nc, ex, lane, &m, &S)) {
                 const Draw d = uno_draw(seed, req, (uint32_t)dep, offset);
-                t = dense_sample_row<BF16>(row_pointer(src, r, row_bytes), N, cm, cs, nc, m, S, d.u[2], ex, lane);
+                t = dense_sample_row<BF16>(row_pointer(src, r, row_bytes), N, cm, cs, nc, m, S, d.u[2], ex, lane,
+                                           row_keep(dc, r));
             }
         }
         if (lane == 0) s_t[n] = t;
@@ -1122,7 +1338,8 @@ hipError_t launch_linear_sparse(int32_t batch, int32_t B, const SparseOut& sup, 
 hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, int64_t vocab,
                                bool bf16, float temperature, const DenseChunks& dc,
                                const DenseScratch& sc, uint64_t seed, uint64_t offset,
-                               const uint32_t* request_ids, const LinearOut& o, hipStream_t stream)
+                               const uint32_t* request_ids, const LinearOut& o, bool exact_all,
+                               hipStream_t stream)
 {
     const double c = 1.4426950408889634074 / (double)temperature;
     const dim3 rgrid((unsigned)batch, (unsigned)((dc.nchunks + kDenseWaves - 1) / kDenseWaves));
@@ -1130,7 +1347,8 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
         dense_propose_kernel<true><<<dim3((unsigned)batch), kDenseThreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
             sc.flags, o);
-        dense_exact_row_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar);
+        if (!exact_all)
+            dense_exact_row_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar);
         dense_residual_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid);
         dense_finish_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
@@ -1140,7 +1358,8 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
         dense_propose_kernel<false><<<dim3((unsigned)batch), kDenseThreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
             sc.flags, o);
-        dense_exact_row_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar);
+        if (!exact_all)
+            dense_exact_row_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar);
         dense_residual_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid);
         dense_finish_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
@@ -1196,6 +1415,22 @@ hipError_t launch_dense_support_scale(int64_t rows, float temperature, const Den
     if (sup.stats == nullptr) return hipErrorInvalidValue;
     dense_support_scale_kernel<<<dim3((unsigned)((rows + kDenseWaves - 1) / kDenseWaves)), kDenseThreads, 0,
                                  stream>>>(rows, 1.0 / (double)temperature, dc, sup);
+    return hipGetLastError();
+}
+
+hipError_t launch_nucleus(const RowSource& src, int64_t rows, int64_t vocab, bool bf16, float temperature,
+                          float top_p, const DenseChunks& dc, int32_t* out_count, double* out_stats,
+                          hipStream_t stream)
+{
+    if (rows == 0) return hipSuccess;
+    if (dc.keep == nullptr) return hipErrorInvalidValue;
+    const double c = 1.4426950408889634074 / (double)temperature;
+    if (bf16)
+        nucleus_kernel<true><<<dim3((unsigned)rows), kNucThreads, 0, stream>>>(src, vocab, c, (double)top_p, dc,
+                                                                             out_count, out_stats);
+    else
+        nucleus_kernel<false><<<dim3((unsigned)rows), kNucThreads, 0, stream>>>(src, vocab, c, (double)top_p, dc,
+                                                                              out_count, out_stats);
     return hipGetLastError();
 }
 

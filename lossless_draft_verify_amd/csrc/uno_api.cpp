@@ -21,6 +21,7 @@ struct Mode {
     bool topp_on;
     bool sparse;     // support from a top-k selection (greedy: k = 1)
     bool joint;      // joint order with both top-k and top-p on (sparse only)
+    bool nucleus;    // top-p without top-k over a full vocabulary (dense only)
     int32_t k;       // effective k on the sparse path
 };
 
@@ -40,7 +41,7 @@ int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
     // the orders differ only when top-k and top-p both act on a sampled row
     m->joint = sp->order == UNO_ORDER_JOINT && !m->greedy && m->topk_on && m->topp_on;
     if (m->sparse && m->k > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
-    if (!m->sparse && m->topp_on) return UNO_ERR_UNSUPPORTED;           // full-vocabulary nucleus
+    m->nucleus = !m->sparse && m->topp_on;
     if (!m->sparse && vocab > (int64_t)65535 * 4 * kDenseChunk) return UNO_ERR_UNSUPPORTED;
     return UNO_OK;
 }
@@ -78,7 +79,7 @@ struct SparseWs {
     DenseChunks full;    // joint order: exact chunk statistics of the rows
 };
 
-DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts);
+DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bool keep);
 
 // Supports (when own_supports; in id order with cumulative sums when id_order),
 // segment partials and, in the joint order, chunk statistics for `rows` sparse
@@ -104,18 +105,19 @@ void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool ow
         w->part_n = cv.take<int32_t>((size_t)rows * w->S);
     }
     w->full = DenseChunks{};
-    if (m.joint) w->full = carve_chunks(cv, rows, vocab, false);
+    if (m.joint) w->full = carve_chunks(cv, rows, vocab, false, false);
 }
 
 // Chunk statistics; the finite counts only for uno_filter, whose dense mode
 // reports each row's support size (the samplers never read them).
-DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts)
+DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bool keep)
 {
     DenseChunks dc;
     dc.nchunks = dense_nchunks(vocab);
     dc.cmax = cv.take<float>((size_t)rows * dc.nchunks);
     dc.csum = cv.take<double>((size_t)rows * dc.nchunks);
     dc.ccount = counts ? cv.take<int32_t>((size_t)rows * dc.nchunks) : nullptr;
+    dc.keep = keep ? cv.take<uint64_t>((size_t)rows) : nullptr;
     return dc;
 }
 
@@ -195,7 +197,8 @@ int layout_filter(int64_t rows, int64_t vocab, int32_t dtype, const uno_sampling
     if (st) return st;
     if (rows == 0) return UNO_OK;
     if (m->sparse) carve_sparse(cv, rows, vocab, *m, false, false, sw);
-    else *dc = carve_chunks(cv, rows, vocab, true);
+    else if (m->nucleus) *dc = carve_chunks(cv, rows, vocab, false, true);   // counts come from the nucleus
+    else *dc = carve_chunks(cv, rows, vocab, true, false);
     return UNO_OK;
 }
 
@@ -212,7 +215,7 @@ int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const 
     if (m->sparse) {
         carve_sparse(cv, rows, vocab, *m, true, true, sw);
     } else {
-        *dc = carve_chunks(cv, rows, vocab, false);
+        *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
         *ds = carve_dense_scratch(cv, rows, (int32_t)batch, B, dc->nchunks);
     }
     return UNO_OK;
@@ -231,6 +234,7 @@ int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int6
     if (st) return st;
     // a full-vocabulary build selects its K candidates with the top-k path
     if (!m->sparse && build && K > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
+    if (m->nucleus) return UNO_ERR_UNSUPPORTED;      // the tree paths take no nucleus
     if (batch == 0) return UNO_OK;
     const int64_t rows = batch * (build ? (int64_t)B : (int64_t)V + 1);
     if (m->sparse) {
@@ -241,9 +245,9 @@ int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int6
         mk.k = K;
         carve_sparse(cv, rows, vocab, mk, true, false, sw);
         sw->sup.stats = cv.take<double>((size_t)rows * 2);
-        *dc = carve_chunks(cv, rows, vocab, false);
+        *dc = carve_chunks(cv, rows, vocab, false, false);
     } else {
-        *dc = carve_chunks(cv, rows, vocab, false);
+        *dc = carve_chunks(cv, rows, vocab, false, false);
     }
     return UNO_OK;
 }
@@ -303,7 +307,12 @@ int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab, c
         return hip_status(launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, out, stream));
     }
     hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
-    if (e == hipSuccess) e = launch_dense_row_stats(rows, sp->temperature, dc, out_count, out_stats, stream);
+    if (e == hipSuccess) {
+        if (m.nucleus)
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, out_count, out_stats, stream);
+        else
+            e = launch_dense_row_stats(rows, sp->temperature, dc, out_count, out_stats, stream);
+    }
     return hip_status(e);
 }
 
@@ -343,10 +352,14 @@ int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int3
         // draft rows are sampled from (exact sums); target rows enter only
         // acceptance ratios, except the one each request draws its last token
         // from, which the dense linear path recomputes exactly
-        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, (int64_t)batch * B, stream);
+        // (the nucleus needs exact sums on every row)
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, m.nucleus ? rows : (int64_t)batch * B,
+                                stream);
+        if (e == hipSuccess && m.nucleus)
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream);
         if (e == hipSuccess)
             e = launch_linear_dense(src, batch, B, vocab, bf16, sp->temperature, dc, ds, seed, offset,
-                                    request_ids, o, stream);
+                                    request_ids, o, m.nucleus, stream);
     }
     return hip_status(e);
 }

@@ -38,6 +38,13 @@ __device__ __forceinline__ float key_float(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
+// 64-bit order key of (logit key, id): larger keys first, then smaller ids --
+// the filter order (z desc, id asc) as one unsigned compare.
+__device__ __forceinline__ uint64_t order_key(uint32_t key, int32_t id)
+{
+    return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)id);
+}
+
 constexpr uint32_t kKeyPosInf = 0xFF800000u;   // float_key(+inf)
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // float_key(-inf)
 

@@ -53,6 +53,10 @@ struct DenseChunks {
     double* csum;      // [rows][nchunks]
     int32_t* ccount;   // [rows][nchunks], or nullptr when no caller needs the counts
     int32_t nchunks;
+    // [rows] keep thresholds of a full-vocabulary nucleus, or nullptr: logit i of
+    // row r is in the support iff order_key(float_key(z_i), i) >= keep[r] (the
+    // chunk sums are then sums over the support)
+    uint64_t* keep;
 };
 
 constexpr int kDenseChunk = 2048;          // elements per dense chunk
@@ -100,10 +104,21 @@ struct DenseScratch {
     double* resid;     // [batch][nchunks]
 };
 
+// With exact_all every row's chunk sums are already exact (the nucleus needs
+// them); otherwise target rows have fast sums and the row each request draws
+// its last token from is recomputed exactly.
 hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, int64_t vocab,
                                bool bf16, float temperature, const DenseChunks& dc,
                                const DenseScratch& sc, uint64_t seed, uint64_t offset,
-                               const uint32_t* request_ids, const LinearOut& o, hipStream_t stream);
+                               const uint32_t* request_ids, const LinearOut& o, bool exact_all,
+                               hipStream_t stream);
+
+// Full-vocabulary nucleus (top-p without top-k) of `rows` rows with exact chunk
+// statistics in dc: writes dc.keep, rewrites dc.csum to sums over each row's
+// support, and (when non-null) the support sizes and (m, S) statistics.
+hipError_t launch_nucleus(const RowSource& src, int64_t rows, int64_t vocab, bool bf16, float temperature,
+                          float top_p, const DenseChunks& dc, int32_t* out_count, double* out_stats,
+                          hipStream_t stream);
 
 struct TreeOut {
     int32_t* node_token;

@@ -81,6 +81,12 @@ WORKLOADS = {
                                    sigma=tuple(0.3 + 0.1 * j for j in range(8)), temperature=1.0,
                                    top_k=50, top_p=0.95, seed=42, cycles=1000, order=1,
                                    note="Linear 8/1/8, 64 requests, joint top-k 50 / top-p 0.95"),
+    # the headline shape with top-k off: a full-vocabulary nucleus at top-p 0.95
+    "linear_8_1_8_nucleus": Workload("linear_8_1_8_nucleus", "linear", batch=64, B=8, vocab=VOCAB_QWEN3,
+                                     dtype="f32", slope=1.2,
+                                     sigma=tuple(0.3 + 0.1 * j for j in range(8)), temperature=1.0,
+                                     top_k=0, top_p=0.95, seed=42, cycles=1000,
+                                     note="Linear 8/1/8, 64 requests, top-p 0.95 over the full vocabulary"),
     "linear_dense": Workload("linear_dense", "linear", batch=256, B=16, vocab=VOCAB_QWEN3,
                              dtype="bf16", slope=1.0, sigma=_const(0.5, 16), temperature=0.7,
                              top_k=0, top_p=1.0, seed=7, cycles=200,

@@ -98,6 +98,11 @@ def test_workspace_sizes(lib):
     # ... which the orders share when only one filter is on
     st, n1 = _ws(lib, uno.OP_SAMPLE_LINEAR, 64, 8, 1, 8, N, F32, sp(1.0, 50, 1.0, uno.ORDER_JOINT))
     assert st == OK and n1 == _ws(lib, uno.OP_SAMPLE_LINEAR, 64, 8, 1, 8, N, F32, sp(1.0, 50, 1.0))[1]
+    # nucleus: chunk statistics and a keep threshold per row
+    st, nn = _ws(lib, uno.OP_SAMPLE_LINEAR, 256, 16, 1, 16, N, BF16, sp(0.7, 0, 0.9))
+    assert st == OK and nn >= nd + 256 * 33 * 8
+    st, nfn = _ws(lib, uno.OP_FILTER, 1000, 0, 0, 0, N, BF16, sp(0.7, 0, 0.9))
+    assert st == OK and nfn >= 1000 * (nch * (4 + 8) + 8)
     # filter with many rows needs nothing beyond the caller's outputs
     st, nf = _ws(lib, uno.OP_FILTER, 4096, 0, 0, 0, N, F32, sp())
     assert st == OK and nf == 0
@@ -109,7 +114,7 @@ def test_workspace_sizes(lib):
 @pytest.mark.parametrize("T,k,p,expect", [
     (-1.0, 50, 0.95, INVALID), (float("nan"), 50, 0.95, INVALID), (float("inf"), 50, 0.95, INVALID),
     (1.0, 50, 0.0, INVALID), (1.0, 50, 1.5, INVALID), (1.0, 50, float("nan"), INVALID),
-    (1.0, 0, 0.9, UNSUPPORTED), (1.0, 257, 1.0, UNSUPPORTED), (1.0, 300, 0.95, UNSUPPORTED),
+    (1.0, 257, 1.0, UNSUPPORTED), (1.0, 300, 0.95, UNSUPPORTED),
 ])
 def test_sampling_parameter_checks(lib, T, k, p, expect):
     st, _ = _ws(lib, uno.OP_SAMPLE_LINEAR, 2, 4, 1, 4, 1000, F32, sp(T, k, p))
@@ -134,6 +139,9 @@ def test_filter_argument_checks(lib):
     # dense mode needs stats and a workspace
     assert f(FAKE, F32, 4, 1000, sp(1.0, 0, 1.0), 0, None, None, out, None, None, 0, None) == INVALID
     assert f(FAKE, F32, 4, 1000, sp(1.0, 0, 1.0), 0, None, None, out, out, None, 0, None) == WORKSPACE
+    # the full-vocabulary nucleus (top-k off, top_p < 1) is a dense mode too
+    assert f(FAKE, F32, 4, 1000, sp(1.0, 0, 0.9), 0, None, None, out, None, None, 0, None) == INVALID
+    assert f(FAKE, F32, 4, 1000, sp(1.0, 0, 0.9), 0, None, None, out, out, None, 0, None) == WORKSPACE
     # zero rows is a no-op
     assert f(None, F32, 0, 1000, sp(), 0, None, None, None, None, None, 0, None) == OK
 
@@ -155,7 +163,7 @@ def test_linear_argument_checks(lib):
     assert args(s=sp(1.0, 0, 1.0)) == WORKSPACE                      # dense chunk stats need ws
     assert args(ws=ctypes.c_void_p(0x40001), wsn=1 << 30) == WORKSPACE   # misaligned
     assert args(ws=ctypes.c_void_p(0x40000), wsn=16) == WORKSPACE        # too small
-    assert args(s=sp(1.0, 0, 0.5)) == UNSUPPORTED
+    assert args(s=sp(1.0, 0, 0.5)) == WORKSPACE                      # the full-vocabulary nucleus too
     assert args(batch=0, d=None, t=None, tok=None, acc=None) == OK
 
 

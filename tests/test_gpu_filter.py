@@ -177,3 +177,38 @@ def test_joint_order_keeps_at_least_the_default_support():
     torch.cuda.synchronize()
     na, nb = np_of(a["count"]), np_of(b["count"])
     assert np.all(nb >= na) and np.all(nb <= 40) and np.any(nb > na)
+
+
+# ---- full-vocabulary nucleus (top-p without top-k) ---------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("N,T,p", [(1003, 1.0, 0.9), (3001, 0.7, 0.5), (5000, 1.5, 0.99), (151936, 1.0, 0.95)])
+def test_nucleus_support_size_and_stats(dtype, N, T, p):
+    dev = device()
+    rng = np.random.default_rng(N + int(100 * p))
+    rows = 12 if N > 100000 else 40
+    z = _rows(rng, rows, N, scale=3.0)
+    rank = np.argsort(rng.random((4, N)), axis=1).astype(np.float32)
+    z[:4] = -1.2 * np.log1p(rank) + rng.standard_normal((4, N)).astype(np.float32)   # long tails
+    z[4] = np.round(z[4] * 2) / 2                  # coarse values: ties at the cut
+    z[5, ::3] = np.nan                             # NaN counts as -inf
+    z[6, ::2] = -np.inf
+    z[7] = 0.25                                    # one value everywhere: the cut falls inside a tie
+    z[8, 17] = np.inf                              # invalid row
+    z[9] = -np.inf                                 # invalid row
+    zt = torch.from_numpy(z).to(dev).to(dtype).contiguous()
+    zh = zt.float().cpu().numpy()
+    g = uno.filter_rows(zt, T, 0, p)
+    torch.cuda.synchronize()
+    o = oracle.filter_rows(zh, T, 0, p, cap=1, dense=False)
+    gc, gs = np_of(g["count"]), np_of(g["stats"])
+    near = o["margin"] < 1e-9
+    for r in range(rows):
+        if o["n"][r] < 0:
+            assert gc[r] == -1, r
+            continue
+        if not near[r]:
+            assert gc[r] == o["n"][r], (r, gc[r], o["n"][r])
+        assert gs[r, 0] == o["stats"][r, 0], r
+        assert abs(gs[r, 1] - o["stats"][r, 1]) <= 2 * N * 2.0**-53 * o["stats"][r, 1], r
+    say(f"nucleus {dtype} N={N} T={T} p={p}: sizes {sorted(gc.tolist())[-3:]}, near-cut rows {int(near.sum())}")

@@ -161,3 +161,35 @@ def test_joint_order_small_vocab(dtype, T, k, p):
         _run(draft, target, T, k, p, 5, c, tally=t, label=f"joint {dtype} T{T} k{k} p{p}",
              order=uno.ORDER_JOINT)
     t.check_rate()
+
+
+# ---- full-vocabulary nucleus (top-p without top-k) ---------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("T,p", [(1.0, 0.9), (0.7, 0.5), (1.3, 0.99)])
+def test_nucleus_small_vocab(dtype, T, p):
+    dev = device()
+    rng = np.random.default_rng(34)
+    batch, B, N = 24, 5, 3001
+    R = rng.standard_normal((batch, B + 1, N)).astype(np.float32) * 2
+    d = (R[:, :B] + 0.5 * rng.standard_normal((batch, B, N))).astype(np.float32)
+    draft = torch.from_numpy(d).to(dev).to(dtype).contiguous()
+    target = torch.from_numpy(R).to(dev).to(dtype).contiguous()
+    t = Tally()
+    for c in range(3):
+        _run(draft, target, T, 0, p, 8, c, tally=t, label=f"nucleus {dtype} T{T} p{p}")
+    t.check_rate()
+
+
+def test_linear_8_1_8_nucleus_reduced_batch():
+    # the headline rows with top-k off and top-p 0.95 (a nucleus of thousands of ids)
+    dev = device()
+    w = synth.WORKLOADS["linear_8_1_8"]
+    t = Tally()
+    acc = []
+    for c in range(2):
+        draft, target = synth.linear_inputs(w, cycle=c, device=dev, batch=8)
+        gg, _ = _run(draft, target, w.temperature, 0, w.top_p, w.seed, c, tally=t, label=f"L818 nucleus {c}")
+        acc.append(gg["accept_len"])
+    t.check_rate()
+    say(f"linear_8_1_8 nucleus b8: mean accept_len {np.concatenate(acc).mean():.3f}, excused {t.excused}")
