@@ -159,11 +159,10 @@ int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int3
  *   node_token / node_parent / node_depth [batch][V+1] (unused slots: -1)
  *   node_score [batch][V+1] (nullable; unused slots 0)
  *   num_nodes [batch]: nodes including the root (< V+1 when candidates run out)
- * Requires 1 <= K, B <= V <= 128 and V * K <= 2048; a full-vocabulary nucleus
- * (top-k off, top_p < 1) returns UNO_ERR_UNSUPPORTED.  A filter that keeps the
- * whole vocabulary (top-k off, top_p == 1, temperature > 0) takes the K most
- * likely ids of the full softmax, with their full-softmax probabilities, and
- * needs K <= UNO_MAX_TOP_K (else UNO_ERR_UNSUPPORTED). */
+ * Requires 1 <= K, B <= V <= 128 and V * K <= 2048.  Without top-k
+ * (temperature > 0) the candidates are the K most likely ids of the full
+ * softmax -- of its nucleus when top_p < 1, renormalised over it -- and K must
+ * be <= UNO_MAX_TOP_K (else UNO_ERR_UNSUPPORTED). */
 int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, int32_t K,
                    int32_t V, int64_t vocab, const uno_sampling_t* sp,
                    int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
@@ -181,11 +180,10 @@ int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, i
  * child of n whose token is t, else stop.
  *   out_tokens [batch][B+1], out_path [batch][B+1] (visited nodes), -1 padded
  *   out_accept_len [batch] in [1, B+1]; out_flags as in uno_sample_linear.
- * Requires B <= V <= 128; a full-vocabulary nucleus (top-k off, top_p < 1)
- * returns UNO_ERR_UNSUPPORTED.  With a filter that keeps the whole vocabulary
- * (top-k off, top_p == 1, temperature > 0) each node's token is drawn from the
- * full softmax of its row: the fallback the PR names for tree verification
- * when sparse target sampling does not apply (PR #37667, Modifications). */
+ * Requires B <= V <= 128.  Without top-k (temperature > 0) each node's token
+ * is drawn from the full softmax of its row (its nucleus when top_p < 1): the
+ * fallback the PR names for tree verification when sparse target sampling does
+ * not apply (PR #37667, Modifications). */
 int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B, int32_t V,
                     int64_t vocab, const uno_sampling_t* sp, uint64_t seed, uint64_t offset,
                     const uint32_t* request_ids, const int32_t* node_token,

@@ -1300,13 +1300,19 @@ __global__ __launch_bounds__(kWalkThreads) void dense_walk_kernel(
 // over their K ids; this rescales them to the full softmax, whose normaliser
 // the exact chunk statistics give (one wave per row).
 __global__ __launch_bounds__(kDenseThreads) void dense_support_scale_kernel(int64_t rows, double inv_T,
-                                                                           DenseChunks dc, SparseOut sup)
+                                                                           DenseChunks dc, const int32_t* limit,
+                                                                           SparseOut sup)
 {
     const int lane = lane_id();
     const int64_t r = (int64_t)blockIdx.x * kDenseWaves + threadIdx.x / kWave;
     if (r >= rows) return;
-    const int n = sup.count[r];
+    int n = sup.count[r];
     if (n <= 0) return;
+    if (limit && limit[r] < n) {
+        // the nucleus ends inside the top K: both are prefixes of the filter order
+        n = limit[r];
+        if (lane == 0) sup.count[r] = n;
+    }
     const int nc = dc.nchunks;
     const float* cm = dc.cmax + r * nc;
     const double* cs = dc.csum + r * nc;
@@ -1410,11 +1416,11 @@ hipError_t launch_tree_walk_dense(const RowSource& src, int32_t batch, int32_t B
 }
 
 hipError_t launch_dense_support_scale(int64_t rows, float temperature, const DenseChunks& dc,
-                                      const SparseOut& sup, hipStream_t stream)
+                                      const int32_t* limit, const SparseOut& sup, hipStream_t stream)
 {
     if (sup.stats == nullptr) return hipErrorInvalidValue;
     dense_support_scale_kernel<<<dim3((unsigned)((rows + kDenseWaves - 1) / kDenseWaves)), kDenseThreads, 0,
-                                 stream>>>(rows, 1.0 / (double)temperature, dc, sup);
+                                 stream>>>(rows, 1.0 / (double)temperature, dc, limit, sup);
     return hipGetLastError();
 }
 

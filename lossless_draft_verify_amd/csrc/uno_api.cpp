@@ -77,6 +77,7 @@ struct SparseWs {
     int32_t* part_id;
     int32_t* part_n;
     DenseChunks full;    // joint order: exact chunk statistics of the rows
+    int32_t* nucleus_n;  // dense tree build with a nucleus: support sizes
 };
 
 DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bool keep);
@@ -104,6 +105,7 @@ void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool ow
         w->part_id = cv.take<int32_t>((size_t)rows * w->S * m.k);
         w->part_n = cv.take<int32_t>((size_t)rows * w->S);
     }
+    w->nucleus_n = nullptr;
     w->full = DenseChunks{};
     if (m.joint) w->full = carve_chunks(cv, rows, vocab, false, false);
 }
@@ -234,7 +236,6 @@ int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int6
     if (st) return st;
     // a full-vocabulary build selects its K candidates with the top-k path
     if (!m->sparse && build && K > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
-    if (m->nucleus) return UNO_ERR_UNSUPPORTED;      // the tree paths take no nucleus
     if (batch == 0) return UNO_OK;
     const int64_t rows = batch * (build ? (int64_t)B : (int64_t)V + 1);
     if (m->sparse) {
@@ -245,9 +246,10 @@ int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int6
         mk.k = K;
         carve_sparse(cv, rows, vocab, mk, true, false, sw);
         sw->sup.stats = cv.take<double>((size_t)rows * 2);
-        *dc = carve_chunks(cv, rows, vocab, false, false);
+        *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
+        sw->nucleus_n = m->nucleus ? cv.take<int32_t>((size_t)rows) : nullptr;
     } else {
-        *dc = carve_chunks(cv, rows, vocab, false, false);
+        *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
     }
     return UNO_OK;
 }
@@ -391,15 +393,20 @@ int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, i
     if (m.sparse) {
         e = launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, sw.sup, stream);
     } else {
-        // full-vocabulary filter: exact row normalisers, the K best ids, then
-        // their probabilities under the full softmax
+        // full-vocabulary filter: exact row normalisers (over the nucleus when
+        // top-p is on), the K best ids, then their probabilities under the
+        // full softmax (renormalised over the nucleus)
         Mode mk = m;
         mk.k = K;
+        mk.topp_on = false;
         e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
+        if (e == hipSuccess && m.nucleus)
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, sw.nucleus_n, nullptr, stream);
         if (e == hipSuccess)
             e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, mk), sw.sup, sw.S, sw.part_key,
                                    sw.part_id, sw.part_n, stream);
-        if (e == hipSuccess) e = launch_dense_support_scale(rows, sp->temperature, dc, sw.sup, stream);
+        if (e == hipSuccess)
+            e = launch_dense_support_scale(rows, sp->temperature, dc, sw.nucleus_n, sw.sup, stream);
     }
     if (e == hipSuccess) {
         TreeOut o{ node_token, node_parent, node_depth, node_score, num_nodes };
@@ -441,8 +448,11 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
             e = launch_tree_walk(batch, B, V, sw.sup, seed, offset, request_ids, node_token, node_parent,
                                  num_nodes, o, stream);
     } else {
-        // every node row a walk may sample gets exact chunk statistics
+        // every node row a walk may sample gets exact chunk statistics (and
+        // its nucleus when top-p is on)
         e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
+        if (e == hipSuccess && m.nucleus)
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream);
         if (e == hipSuccess)
             e = launch_tree_walk_dense(src, batch, B, V, vocab, bf16, sp->temperature, dc, seed, offset,
                                        request_ids, node_token, node_parent, num_nodes, o, stream);

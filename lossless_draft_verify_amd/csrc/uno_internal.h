@@ -143,12 +143,13 @@ hipError_t launch_tree_walk(int32_t batch, int32_t B, int32_t V, const SparseOut
                             const int32_t* node_token, const int32_t* node_parent,
                             const int32_t* num_nodes, const WalkOut& o, hipStream_t stream);
 
-// Dense tree mode (filters that keep the whole vocabulary).  The build takes
-// the top-K supports and rescales them to the full softmax (sup.stats holds
-// the top-K normaliser on entry, the full one on exit); the walk samples node
-// rows from exact chunk statistics.
+// Dense tree mode (filters without top-k).  The build takes the top-K supports
+// and rescales them to the full softmax, or to the nucleus when the chunk sums
+// are over a nucleus (sup.stats holds the top-K normaliser on entry, the new
+// one on exit); `limit` (nullable) caps each row's count at its nucleus size.
+// The walk samples node rows from exact chunk statistics.
 hipError_t launch_dense_support_scale(int64_t rows, float temperature, const DenseChunks& dc,
-                                      const SparseOut& sup, hipStream_t stream);
+                                      const int32_t* limit, const SparseOut& sup, hipStream_t stream);
 
 hipError_t launch_tree_walk_dense(const RowSource& src, int32_t batch, int32_t B, int32_t V, int64_t vocab,
                                   bool bf16, float temperature, const DenseChunks& dc, uint64_t seed,

@@ -179,7 +179,7 @@ def test_tree_argument_checks(lib):
     # full-vocabulary filters: the build picks its K candidates with the top-k path
     assert bt(s=sp(1.0, 0, 1.0)) == WORKSPACE
     assert bt(s=sp(1.0, 0, 1.0), K=257, V=4) == UNSUPPORTED
-    assert bt(s=sp(1.0, 0, 0.9)) == UNSUPPORTED     # full-vocabulary nucleus
+    assert bt(s=sp(1.0, 0, 0.9)) == WORKSPACE       # full-vocabulary nucleus
     assert bt(d=None) == INVALID
     assert bt() == WORKSPACE
     assert bt(K=256, V=8) == WORKSPACE     # V * K == 2048 is allowed
@@ -188,7 +188,7 @@ def test_tree_argument_checks(lib):
     assert vt(V=3) == INVALID
     assert vt(V=200) == INVALID
     assert vt(s=sp(0.5, 0, 1.0)) == WORKSPACE        # dense walk
-    assert vt(s=sp(0.5, 0, 0.9)) == UNSUPPORTED       # full-vocabulary nucleus
+    assert vt(s=sp(0.5, 0, 0.9)) == WORKSPACE         # full-vocabulary nucleus
     assert vt() == WORKSPACE
     # greedy decoding is a sparse (k = 1) mode
     assert vt(s=sp(0.0, 0, 1.0)) == WORKSPACE

@@ -1,4 +1,6 @@
 """GPU parity of uno_build_tree and uno_verify_tree against the oracle."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -65,11 +67,12 @@ def _build_parity(draft, K, V, T, k, p, label):
     bad = np.zeros(batch, dtype=bool)
     for key in TREE_KEYS:
         bad |= np.any(G[key].reshape(batch, -1) != o[key].reshape(batch, -1), axis=1)
-    full_vocab = T > 0 and (k <= 0 or k >= N) and p >= 1.0 and N > uno.MAX_TOP_K
+    full_vocab = T > 0 and (k <= 0 or k >= N) and N > uno.MAX_TOP_K
     if full_vocab:
-        # full-softmax normalisers are summed in another order on the device, so
-        # scores equal in exact arithmetic may round apart and pop in either order
-        f = oracle.filter_rows(dh.reshape(batch * B, N), T, 0, 1.0, cap=K, dense=False)
+        # full-softmax (or nucleus) normalisers are summed in another order on the
+        # device, so scores equal in exact arithmetic may round apart and pop in
+        # either order
+        f = oracle.filter_rows(dh.reshape(batch * B, N), T, 0, p, cap=K, dense=False)
         for b in np.flatnonzero(bad):
             _check_tied_tree(G, o, f, int(b), B, label)
         same = ~bad
@@ -285,3 +288,29 @@ def test_tree_joint_order():
         t.compare({k: np_of(gv[k]) for k in ("tokens", "path", "accept_len")}, ov,
                   ("tokens", "path", "accept_len"), f"tree joint {c}")
     t.check_rate()
+
+
+@pytest.mark.parametrize("B,K,V,T,p,N,bf16", [(3, 3, 10, 1.0, 0.9, 5000, False), (2, 8, 16, 0.5, 0.5, 4099, True),
+                                              (4, 64, 8, 1.0, 0.3, 700, False), (5, 16, 128, 1.0, 0.95, 3 * 2048, True)])
+def test_dense_tree_nucleus_shapes(B, K, V, T, p, N, bf16):
+    # top-k off, top-p on: candidates from each draft row's nucleus (fewer than K
+    # when the nucleus is small), node tokens from each target row's nucleus
+    dev = device()
+    rng = np.random.default_rng(B * 7 + K + N)
+    batch = 10
+    d = torch.from_numpy((rng.standard_normal((batch, B, N)) * 2.5).astype(np.float32)).to(dev)
+    tg = torch.from_numpy((rng.standard_normal((batch, V + 1, N)) * 2.5).astype(np.float32)).to(dev)
+    if bf16:
+        d, tg = d.to(torch.bfloat16), tg.to(torch.bfloat16)
+    label = f"nucleus tree B{B} K{K} V{V} p{p} N{N}"
+    _, o = _build_parity(d, K, V, T, 0, p, label)
+    t = Tally()
+    rid = np.arange(batch, dtype=np.uint32) * 31 + 5
+    for c in range(3):
+        _verify_parity(tg, B, o, T, 0, p, 29, c, t, label, request_ids=rid)
+    t.check_rate()
+
+
+def test_dense_tree_16_32_32_nucleus_full_size():
+    w = dataclasses.replace(synth.WORKLOADS["tree_dense_16_32_32"], top_p=0.95, name="tree 16/32/32 nucleus")
+    _tree_cycles(w, 3)
