@@ -1067,13 +1067,16 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
 // ---- full-vocabulary nucleus (top-p without top-k) -------------------------------
 // The support is the shortest prefix of the filter order (z desc, id asc) whose
 // mass reaches top_p (the first logit always kept).  One workgroup per row
-// finds the cut by a mass-weighted radix select over the 32-bit order keys of
-// the logits -- 11, 11, then 10 bits, one pass over the row per digit, each
-// digit's bins holding the exact fp64 mass exp((z - m)/T) of their logits --
-// and the number of tied logits at the cut from the mass left; the cut among
-// the ties (smaller ids first) comes from an ordered count over ids.  The
-// row's keep threshold is the order key of its last kept logit; the chunk
-// sums are then rewritten over the support.
+// finds the cut by a mass-weighted select over the 32-bit order keys of the
+// logits: a key range known to hold the cut is split into up to 2048 equal
+// bins, one pass over the row accumulates each bin's logit count and exact
+// fp64 mass exp((z - m)/T), and the bin where the mass counted from the top
+// reaches top_p * S becomes the next range, until one key is left.  The
+// first range starts at the value below which all logits together hold less
+// than (1 - top_p) / 2 of the mass.  The number of tied logits kept at the cut
+// follows from the mass left; which ties (smaller ids first) from an ordered
+// count over ids.  The row's keep threshold is the order key of its last kept
+// logit; the chunk sums are then rewritten over the support.
 constexpr int kNucThreads = 256;
 constexpr int kNucWaves = kNucThreads / kWave;
 constexpr int kNucBins = 2048;
@@ -1121,24 +1124,32 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
         return;
     }
     const double target = top_p * S;
-    uint32_t prefix = 0;
-    int pbits = 0;
-    double A = 0.0;
-    int64_t cab = 0;
-    for (int level = 0; level < 3; ++level) {
-        const int bits = level < 2 ? 11 : 10;
-        const int nb = 1 << bits;
-        const int shift = 32 - pbits - bits;
+    // logits below z_lo weigh less than (1 - p) S / (2N) each, (1 - p) S / 2 in all
+    const double T = 1.0 / (log2e_over_T * 0.69314718055994530942);
+    const double z_lo = (double)m + T * log((1.0 - top_p) * S / (2.0 * (double)N));
+    uint32_t lo = float_key(z_lo > -3.0e38 ? (float)z_lo : -3.0e38f);
+    uint32_t hi = float_key(m) + 1u;         // keys in [lo, hi)
+    lo = lo < hi - 1u ? lo : hi - 1u;
+    double A = 0.0;                          // mass at or above hi
+    int64_t cab = 0;                         // logits at or above hi
+    do {
+        const uint32_t width = hi - lo;
+        const int nb = width < (uint32_t)kNucBins ? (int)width : kNucBins;
         for (int b = (int)threadIdx.x; b < nb; b += kNucThreads) { s_mass[b] = 0.0; s_cnt[b] = 0u; }
         __syncthreads();
-        for (int64_t i = threadIdx.x; i < N; i += kNucThreads) {
-            const float v = load_scalar<BF16>(row, i);
-            if (!finite_f32(v)) continue;
-            const uint32_t key = float_key(v);
-            if (pbits > 0 && (key >> (32 - pbits)) != prefix) continue;
-            const int bin = (int)((key >> shift) & (uint32_t)(nb - 1));
-            atomicAdd(&s_mass[bin], ex((double)v - (double)m));
-            atomicAdd(&s_cnt[bin], 1u);
+        for (int c = w; c < nc; c += kNucWaves) {
+            if (!(cm[c] > -INFINITY) || float_key(cm[c]) < lo) continue;     // nothing in range
+            float x[kPerLane];
+            load_chunk<BF16>(row, N, c, x, lane);
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) {
+                if (!finite_f32(x[i])) continue;
+                const uint32_t key = float_key(x[i]);
+                if (key < lo || key >= hi) continue;
+                const int bin = (int)((uint64_t)(key - lo) * (uint64_t)nb / width);
+                atomicAdd(&s_mass[bin], ex((double)x[i] - (double)m));
+                atomicAdd(&s_cnt[bin], 1u);
+            }
         }
         __syncthreads();
         if (w == 0) {
@@ -1175,14 +1186,18 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
             if (lane == 0) { s_bin = found; s_row[1] = fa; s_cab = (int64_t)fc; }
         }
         __syncthreads();
-        prefix = (prefix << bits) | (uint32_t)s_bin;
-        pbits += bits;
+        // bin b holds the keys k with floor((k - lo) * nb / width) == b
+        const uint64_t fb = (uint64_t)s_bin;
+        const uint32_t nlo = lo + (uint32_t)((fb * width + (uint64_t)nb - 1) / (uint64_t)nb);
+        const uint32_t nhi = lo + (uint32_t)(((fb + 1) * width + (uint64_t)nb - 1) / (uint64_t)nb);
+        lo = nlo;
+        hi = nhi;
         A = s_row[1];
         cab = s_cab;
-    }
+    } while (hi - lo > 1u);
     // ties at the cut: keep the j-th (by id) while the mass before it is below
     // the target
-    const uint32_t tau = prefix;
+    const uint32_t tau = lo;
     const int64_t ctau = (int64_t)s_cnt[s_bin];
     const double etau = ex((double)key_float(tau) - (double)m);
     int64_t t = ctau;
@@ -1190,18 +1205,27 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
         const double x = ceil((target - A) / etau);
         t = x < 1.0 ? 1 : (x < (double)ctau ? (int64_t)x : ctau);
     }
-    // the t-th tie in id order: each wave counts its quarter of the ids, then
-    // the wave holding it finds it
-    const int64_t q0 = N * w / kNucWaves, q1 = N * (w + 1) / kNucWaves;
-    int64_t cw = 0;
-    for (int64_t base = q0; base < q1; base += kWave) {
-        const int64_t i = base + lane;
-        bool mt = false;
-        if (i < q1) {
-            const float v = load_scalar<BF16>(row, i);
-            mt = finite_f32(v) && float_key(v) == tau;
+    // the t-th tie in id order: each wave counts the ties in its run of whole
+    // chunks, then the wave holding the t-th finds it chunk by chunk, and in
+    // its chunk vector by vector (ids rise with the vector, the lane, then the
+    // element)
+    const int c0 = (int)((int64_t)nc * w / kNucWaves), c1 = (int)((int64_t)nc * (w + 1) / kNucWaves);
+    auto chunk_ties = [&](int c, float (&x)[kPerLane]) __attribute__((always_inline)) {
+        int n = 0;
+        if (cm[c] > -INFINITY && float_key(cm[c]) >= tau) {
+            load_chunk<BF16>(row, N, c, x, lane);
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) n += (finite_f32(x[i]) && float_key(x[i]) == tau) ? 1 : 0;
+        } else {
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) x[i] = -INFINITY;
         }
-        cw += __popcll(__ballot(mt));
+        return (int64_t)wave_sum_f64((double)n);
+    };
+    int64_t cw = 0;
+    for (int c = c0; c < c1; ++c) {
+        float x[kPerLane];
+        cw += chunk_ties(c, x);
     }
     if (lane == 0) s_wc[w] = cw;
     __syncthreads();
@@ -1209,21 +1233,35 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
     for (int o = 0; o < w; ++o) before += s_wc[o];
     if (t > before && t <= before + cw) {
         int64_t need = t - before;
-        for (int64_t base = q0; base < q1; base += kWave) {
-            const int64_t i = base + lane;
-            bool mt = false;
-            if (i < q1) {
-                const float v = load_scalar<BF16>(row, i);
-                mt = finite_f32(v) && float_key(v) == tau;
+        for (int c = c0; c < c1; ++c) {
+            float x[kPerLane];
+            const int64_t n = chunk_ties(c, x);
+            if (need > n) { need -= n; continue; }
+            constexpr int NVEC = kPerLane / EPV;
+#pragma unroll
+            for (int j = 0; j < NVEC; ++j) {
+                int nl = 0;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) nl += (finite_f32(x[j * EPV + e]) && float_key(x[j * EPV + e]) == tau) ? 1 : 0;
+                const double incl = wave_incl_scan_f64((double)nl, lane);
+                const double tot = __shfl(incl, kWave - 1, kWave);
+                if ((double)need <= tot) {
+                    const uint64_t at = __ballot((double)need <= incl && (double)need > incl - (double)nl);
+                    const int l = wave_first_lane(at);
+                    if (lane == l) {
+                        int64_t k = need - (int64_t)(incl - (double)nl);      // k-th tie of this lane's vector
+                        for (int e = 0; e < EPV; ++e) {
+                            if (finite_f32(x[j * EPV + e]) && float_key(x[j * EPV + e]) == tau && --k == 0) {
+                                s_idlim = (int32_t)(c * (int64_t)kDenseChunk + (int64_t)(j * kWave + lane) * EPV + e);
+                                break;
+                            }
+                        }
+                    }
+                    break;
+                }
+                need -= (int64_t)tot;
             }
-            const uint64_t mk = __ballot(mt);
-            const int pc = __popcll(mk);
-            if (need <= pc) {
-                const uint64_t at = __ballot(mt && __popcll(mk & lanes_below(lane)) + 1 == need);
-                if (lane == 0) s_idlim = (int32_t)(base + wave_first_lane(at));
-                break;
-            }
-            need -= pc;
+            break;
         }
     }
     __syncthreads();
