@@ -1124,33 +1124,63 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
         return;
     }
     const double target = top_p * S;
+    // chunks c = w, w + kNucWaves, ... handed to body(c, x) with the next
+    // chunk's loads in flight (past the last chunk the prefetch re-reads the
+    // current one, so every iteration has the same loads in flight)
+    auto each_chunk = [&](auto body) __attribute__((always_inline)) {
+        int c = w;
+        if (c >= nc) return;
+        float xc[kPerLane], xn[kPerLane];
+        load_chunk<BF16>(row, N, c, xc, lane);
+        for (;;) {
+            const int cn = c + kNucWaves;
+            load_chunk<BF16>(row, N, cn < nc ? cn : c, xn, lane);
+            body(c, xc);
+            if (cn >= nc) break;
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) xc[i] = xn[i];
+            c = cn;
+        }
+    };
     // logits below z_lo weigh less than (1 - p) S / (2N) each, (1 - p) S / 2 in all
     const double T = 1.0 / (log2e_over_T * 0.69314718055994530942);
     const double z_lo = (double)m + T * log((1.0 - top_p) * S / (2.0 * (double)N));
-    uint32_t lo = float_key(z_lo > -3.0e38 ? (float)z_lo : -3.0e38f);
-    uint32_t hi = float_key(m) + 1u;         // keys in [lo, hi)
-    lo = lo < hi - 1u ? lo : hi - 1u;
-    double A = 0.0;                          // mass at or above hi
-    int64_t cab = 0;                         // logits at or above hi
+    // First level: equal value bins over [vlo, m], so the logits near the cut
+    // spread over the bins (equal key bins would stack whole octaves into a
+    // few); later levels: equal key bins within the chosen value bin.
+    const float vlo_f = (float)(z_lo > -3.0e38 ? (z_lo < (double)m ? z_lo : (double)m) : -3.0e38);
+    const double vlo = (double)vlo_f;
+    const double vscale = (vlo < (double)m) ? (double)kNucBins / ((double)m - vlo) : 0.0;
+    auto vbin = [&](float z) __attribute__((always_inline)) {     // z >= vlo
+        const int b = (int)floor(((double)z - vlo) * vscale);
+        return b < kNucBins - 1 ? b : kNucBins - 1;
+    };
+    int b0 = -1;                             // the chosen value bin
+    uint32_t lo = 0, hi = 0;                 // later levels: keys in [lo, hi)
+    double A = 0.0;                          // mass above the current range
+    int64_t cab = 0;                         // logits above the current range
     do {
+        const bool first = b0 < 0;
         const uint32_t width = hi - lo;
-        const int nb = width < (uint32_t)kNucBins ? (int)width : kNucBins;
+        const int nb = first ? kNucBins : (width < (uint32_t)kNucBins ? (int)width : kNucBins);
         for (int b = (int)threadIdx.x; b < nb; b += kNucThreads) { s_mass[b] = 0.0; s_cnt[b] = 0u; }
         __syncthreads();
-        for (int c = w; c < nc; c += kNucWaves) {
-            if (!(cm[c] > -INFINITY) || float_key(cm[c]) < lo) continue;     // nothing in range
-            float x[kPerLane];
-            load_chunk<BF16>(row, N, c, x, lane);
+        each_chunk([&](int, const float (&x)[kPerLane]) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < kPerLane; ++i) {
-                if (!finite_f32(x[i])) continue;
-                const uint32_t key = float_key(x[i]);
-                if (key < lo || key >= hi) continue;
-                const int bin = (int)((uint64_t)(key - lo) * (uint64_t)nb / width);
+                if (!finite_f32(x[i]) || !(x[i] >= vlo_f)) continue;
+                int bin;
+                if (first) {
+                    bin = vbin(x[i]);
+                } else {
+                    const uint32_t key = float_key(x[i]);
+                    if (key < lo || key >= hi || vbin(x[i]) != b0) continue;
+                    bin = (int)((uint64_t)(key - lo) * (uint64_t)nb / width);
+                }
                 atomicAdd(&s_mass[bin], ex((double)x[i] - (double)m));
                 atomicAdd(&s_cnt[bin], 1u);
             }
-        }
+        });
         __syncthreads();
         if (w == 0) {
             // bins from the top down: the first non-empty bin whose inclusive
@@ -1186,12 +1216,23 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
             if (lane == 0) { s_bin = found; s_row[1] = fa; s_cab = (int64_t)fc; }
         }
         __syncthreads();
-        // bin b holds the keys k with floor((k - lo) * nb / width) == b
-        const uint64_t fb = (uint64_t)s_bin;
-        const uint32_t nlo = lo + (uint32_t)((fb * width + (uint64_t)nb - 1) / (uint64_t)nb);
-        const uint32_t nhi = lo + (uint32_t)(((fb + 1) * width + (uint64_t)nb - 1) / (uint64_t)nb);
-        lo = nlo;
-        hi = nhi;
+        if (first) {
+            // the keys of the value bin's logits, with a few keys' margin for
+            // the rounding of the bin index (the bin test itself stays exact)
+            b0 = s_bin;
+            const float za = (float)(vlo + (double)b0 / vscale);
+            const float zb = (float)(vlo + (double)(b0 + 1) / vscale);
+            const uint32_t ka = float_key(za), kb = float_key(zb);
+            lo = ka > 8u ? ka - 8u : 0u;
+            hi = kb < 0xFFFFFFF0u ? kb + 9u : 0xFFFFFFF8u;
+        } else {
+            // bin b holds the keys k with floor((k - lo) * nb / width) == b
+            const uint64_t fb = (uint64_t)s_bin;
+            const uint32_t nlo = lo + (uint32_t)((fb * width + (uint64_t)nb - 1) / (uint64_t)nb);
+            const uint32_t nhi = lo + (uint32_t)(((fb + 1) * width + (uint64_t)nb - 1) / (uint64_t)nb);
+            lo = nlo;
+            hi = nhi;
+        }
         A = s_row[1];
         cab = s_cab;
     } while (hi - lo > 1u);
@@ -1222,16 +1263,21 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
         }
         return (int64_t)wave_sum_f64((double)n);
     };
+    // (all ties kept -- always so without ties -- needs no search: the
+    // largest id keeps every logit of key tau)
+    const bool search = t < ctau;
+    if (threadIdx.x == 0) s_idlim = 0x7FFFFFFF;
     int64_t cw = 0;
-    for (int c = c0; c < c1; ++c) {
-        float x[kPerLane];
-        cw += chunk_ties(c, x);
-    }
+    if (search)
+        for (int c = c0; c < c1; ++c) {
+            float x[kPerLane];
+            cw += chunk_ties(c, x);
+        }
     if (lane == 0) s_wc[w] = cw;
     __syncthreads();
     int64_t before = 0;
     for (int o = 0; o < w; ++o) before += s_wc[o];
-    if (t > before && t <= before + cw) {
+    if (search && t > before && t <= before + cw) {
         int64_t need = t - before;
         for (int c = c0; c < c1; ++c) {
             float x[kPerLane];
@@ -1267,19 +1313,18 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
     __syncthreads();
     const uint64_t thr = order_key(tau, s_idlim);
     // chunk sums over the support, relative to each chunk's (unchanged) maximum
-    for (int c = w; c < nc; c += kNucWaves) {
+    each_chunk([&](int c, const float (&x)[kPerLane]) __attribute__((always_inline)) {
         double sum = 0.0;
-        if (cm[c] > -INFINITY) {
-            float x[kPerLane];
-            load_chunk<BF16>(row, N, c, x, lane);
-            const double mc = (double)cm[c];
+        const float mcf = cm[c];
+        if (mcf > -INFINITY) {
+            const double mc = (double)mcf;
 #pragma unroll
             for (int i = 0; i < kPerLane; ++i)
                 if (dense_keeps(thr, x[i], chunk_elem_id<EPV>(c, i, lane))) sum += ex((double)x[i] - mc);
         }
         sum = wave_sum_f64(sum);
         if (lane == 0) cs[c] = sum;
-    }
+    });
     if (threadIdx.x == 0) {
         dc.keep[r] = thr;
         if (out_count) out_count[r] = (int32_t)(cab + t);
