@@ -69,6 +69,8 @@ def _load():
         lib.oracle_verify_tree.argtypes = [P, i32, i32, i32, i64, i64, f64, i32, f64, i32, u64, u64, P,
                                            P, P, P, P, P, P, P]
         lib.oracle_verify_tree.restype = None
+        lib.oracle_tree_attention.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f64, P, P]
+        lib.oracle_tree_attention.restype = None
         lib.oracle_tpf.argtypes = [P, i64]
         lib.oracle_tpf.restype = f64
         lib.oracle_num_threads.argtypes = []
@@ -236,3 +238,25 @@ def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_
 def tpf(accept_len):
     a = np.ascontiguousarray(accept_len, dtype=np.int32).ravel()
     return float(_load().oracle_tpf(_ptr(a), a.shape[0]))
+
+
+def tree_attention(q, k, v, o_prefix, lse_prefix, node_parent, num_nodes, scale):
+    """Tree-suffix attention merged with the prefix state, per request.
+
+    q, o_prefix [batch, n, Hq, D]; k, v [batch, n, Hkv, D]; lse_prefix [batch, n, Hq];
+    node_parent [batch, n]; num_nodes [batch].  Returns dict(o [batch, n, Hq, D],
+    lse [batch, n, Hq]) in float64 (rows at or past num_nodes are zero)."""
+    lib = _load()
+    q, k, v, op = _f32(q), _f32(k), _f32(v), _f32(o_prefix)
+    lp = _f32(lse_prefix)
+    batch, n, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (batch, n, Hkv, D) and v.shape == k.shape and op.shape == q.shape
+    assert lp.shape == (batch, n, Hq) and Hq % Hkv == 0
+    par = np.ascontiguousarray(node_parent, dtype=np.int32)
+    nn = np.ascontiguousarray(num_nodes, dtype=np.int32)
+    o = np.zeros((batch, n, Hq, D), dtype=np.float64)
+    lse = np.zeros((batch, n, Hq), dtype=np.float64)
+    lib.oracle_tree_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(op), _ptr(lp), _ptr(par), _ptr(nn),
+                              batch, n, Hq, Hkv, D, float(scale), _ptr(o), _ptr(lse))
+    return dict(o=o, lse=lse)

@@ -537,6 +537,79 @@ void oracle_verify_tree(const float* target, int32_t batch, int32_t B, int32_t V
 }
 
 /* ------------------------------------------------------------------------ */
+/* Tree-suffix attention merged with the prefix attention.  [PR]
+ * "Modifications": an UNO-only fused kernel for tree-suffix attention and LSE
+ * merge, with the FlashAttention + state-merge path as fallback; "Changes to
+ * shared SGLang infrastructure": the fused merge serves UNO tree verification
+ * (cascade attention: the shared prefix once, the V-node tree suffix apart).
+ * Reading: each request's n = V + 1 verify tokens are the tree's nodes (node 0
+ * the root); the query of node i attends, among the suffix keys, to node i and
+ * its ancestors.  With scores s_j = scale * q_i . k_j over those nodes,
+ *   lse_s = log sum_j exp(s_j),  o_s = sum_j exp(s_j - lse_s) v_j,
+ * and the prefix state (o_p, lse_p) of the same query (its attention over the
+ * shared context, computed elsewhere):
+ *   lse = log(exp(lse_p) + exp(lse_s)),
+ *   o   = exp(lse_p - lse) o_p + exp(lse_s - lse) o_s,
+ * i.e. softmax attention over the prefix keys and the visible suffix keys
+ * together.  lse_p = -inf means an empty prefix.  Query head h reads key/value
+ * head h / (Hq / Hkv).  Layout: token t = b * n + i; q, o_p, o [t][Hq][D],
+ * k, v [t][Hkv][D], lse_p, lse [t][Hq].  Nodes at or past num_nodes[b] are not
+ * read or written.                                                            */
+void oracle_tree_attention(const float* q, const float* k, const float* v, const float* o_p,
+                           const float* lse_p, const int32_t* node_parent, const int32_t* num_nodes,
+                           int32_t batch, int32_t n, int32_t Hq, int32_t Hkv, int32_t D, double scale,
+                           double* o, double* lse)
+{
+    const int32_t G = Hq / Hkv;
+    #pragma omp parallel for schedule(dynamic)
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t nn = num_nodes[b] < n ? num_nodes[b] : n;
+        const int32_t* par = node_parent + (int64_t)b * n;
+        double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        char* vis = (char*)malloc((size_t)(n > 0 ? n : 1));
+        for (int32_t i = 0; i < nn; ++i) {
+            /* node i and its ancestors */
+            memset(vis, 0, (size_t)n);
+            for (int32_t a = i, steps = 0; a >= 0 && a < nn && steps <= n; a = par[a], ++steps) vis[a] = 1;
+            const int64_t t = (int64_t)b * n + i;
+            for (int32_t h = 0; h < Hq; ++h) {
+                const int32_t hk = h / G;
+                const float* qi = q + (t * Hq + h) * D;
+                double mx = -INFINITY;
+                for (int32_t j = 0; j < nn; ++j) {
+                    if (!vis[j]) continue;
+                    const float* kj = k + (((int64_t)b * n + j) * Hkv + hk) * D;
+                    double d = 0.0;
+                    for (int32_t e = 0; e < D; ++e) d += (double)qi[e] * (double)kj[e];
+                    s[j] = scale * d;
+                    if (s[j] > mx) mx = s[j];
+                }
+                double sum = 0.0;
+                for (int32_t j = 0; j < nn; ++j)
+                    if (vis[j]) sum += exp(s[j] - mx);
+                const double ls = mx + log(sum);
+                const double lp = (double)lse_p[t * Hq + h];
+                const double l = (lp == -INFINITY) ? ls : (lp > ls ? lp + log1p(exp(ls - lp))
+                                                                   : ls + log1p(exp(lp - ls)));
+                const double wp = (lp == -INFINITY) ? 0.0 : exp(lp - l);
+                const double ws = exp(ls - l);
+                double* oi = o + (t * Hq + h) * D;
+                const float* pi = o_p + (t * Hq + h) * D;
+                for (int32_t e = 0; e < D; ++e) {
+                    double acc = 0.0;
+                    for (int32_t j = 0; j < nn; ++j)
+                        if (vis[j]) acc += exp(s[j] - ls) * (double)v[(((int64_t)b * n + j) * Hkv + hk) * D + e];
+                    oi[e] = wp * (double)pi[e] + ws * acc;
+                }
+                lse[t * Hq + h] = l;
+            }
+        }
+        free(s);
+        free(vis);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Tokens per forward.  [Blog] "TPF 统计口径" and [PR] "Validation": each UNO
  * cycle runs two target forwards, so TPF = emitted tokens / (2 * cycles).   */
 double oracle_tpf(const int32_t* accept_len, int64_t n_request_cycles)
