@@ -11,6 +11,7 @@
  *   uno_sample_linear  linear mode: proposals, rejection, residual / bonus
  *   uno_build_tree     tree mode: top-K candidates per position -> V-node tree
  *   uno_verify_tree    tree mode: target-sampled walk of the candidate tree
+ *   uno_tree_attention tree mode: tree-suffix attention merged with the prefix state
  *
  * Conventions shared by every entry point
  *  - Pointers named logits / draft / target / out_* / node_* / request_ids /
@@ -192,6 +193,31 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
                     uint32_t* out_flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
+/* Tree-suffix attention merged with the prefix attention state.  (PR #37667,
+ * Modifications: an UNO-only fused kernel for tree-suffix attention and LSE
+ * merge; Changes to shared SGLang infrastructure: it serves UNO tree
+ * verification, where cascade attention takes the shared prefix once.)
+ * The n verify tokens of request b (token t = b * n + i) are the nodes of its
+ * tree (node 0 the root; node_parent as uno_build_tree writes it, parents
+ * before children).  The query of node i, head h, attends to the suffix keys
+ * of node i and its ancestors (key/value head h / (Hq / Hkv)) with scores
+ * scale * q.k, giving (o_s, lse_s); with the same query's prefix state
+ * (o_p, lse_p) -- its attention over the shared context, computed elsewhere --
+ *   out_lse = log(exp(lse_p) + exp(lse_s)),
+ *   out = exp(lse_p - out_lse) o_p + exp(lse_s - out_lse) o_s,
+ * i.e. softmax attention over the prefix keys and the visible suffix keys.
+ *   q, o_prefix, out [batch * n][Hq][D], k, v [batch * n][Hkv][D]: bf16
+ *   lse_prefix, out_lse [batch * n][Hq]: fp32, natural log (-inf: no prefix)
+ *   node_parent [batch][n]; num_nodes [batch] (nullable: n for every request)
+ * Tokens at or past num_nodes[b] are neither read nor written.  Scores,
+ * softmax and sums run in fp32.  No workspace.
+ * Requires dtype UNO_BF16 and D == 128 (else UNO_ERR_UNSUPPORTED),
+ * 1 <= n <= UNO_MAX_TREE_NODES + 1, Hq % Hkv == 0 and scale > 0. */
+int uno_tree_attention(const void* q, const void* k, const void* v, const void* o_prefix,
+                       const float* lse_prefix, const int32_t* node_parent, const int32_t* num_nodes,
+                       int32_t dtype, int32_t batch, int32_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                       float scale, void* out, float* out_lse, hipStream_t stream);
+
 const char* uno_status_string(int status);
 
 /* hipError_t of the last failed launch on this host thread (0 if none). */

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "UnoError", "Sampling", "library_path", "load_library", "workspace_bytes", "filter_rows",
-    "sample_linear", "build_tree", "verify_tree", "OP_FILTER", "OP_SAMPLE_LINEAR",
+    "sample_linear", "build_tree", "verify_tree", "tree_attention", "OP_FILTER", "OP_SAMPLE_LINEAR",
     "OP_BUILD_TREE", "OP_VERIFY_TREE", "MAX_TOP_K", "ORDER_TOPK_FIRST", "ORDER_JOINT",
 ]
 
@@ -67,8 +67,10 @@ def load_library():
                                        ctypes.c_size_t, P]
         lib.uno_verify_tree.argtypes = [P, i32, i32, i32, i32, i64, SP, u64, u64, P, P, P, P, P, P,
                                         P, P, P, ctypes.c_size_t, P]
+        lib.uno_tree_attention.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                           P, P, P]
         for f in ("uno_workspace_bytes", "uno_filter", "uno_sample_linear", "uno_build_tree",
-                  "uno_verify_tree", "uno_last_hip_error"):
+                  "uno_verify_tree", "uno_tree_attention", "uno_last_hip_error"):
             getattr(lib, f).restype = ctypes.c_int
         lib.uno_status_string.argtypes = [ctypes.c_int]
         lib.uno_status_string.restype = ctypes.c_char_p
@@ -253,4 +255,26 @@ def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_
                                _ptr(out["path"]), _ptr(out["accept_len"]), _ptr(out.get("flags")),
                                wsp, wsn, _stream(stream)), "uno_verify_tree")
     out["workspace"] = workspace
+    return out
+
+
+def tree_attention(q, k, v, o_prefix, lse_prefix, node_parent, num_nodes, scale, out=None, stream=None):
+    """uno_tree_attention: q, o_prefix [batch, n, Hq, D], k, v [batch, n, Hkv, D] (bf16),
+    lse_prefix [batch, n, Hq] (fp32), node_parent [batch, n], num_nodes [batch] or None.
+    Returns dict(o [batch, n, Hq, D] bf16, lse [batch, n, Hq] fp32)."""
+    lib = load_library()
+    batch, n, Hq, D = q.shape
+    Hkv = k.shape[2]
+    for t in (q, k, v, o_prefix):
+        assert t.is_cuda and t.is_contiguous() and t.dtype == torch.bfloat16
+    assert k.shape == (batch, n, Hkv, D) and v.shape == k.shape and o_prefix.shape == q.shape
+    assert lse_prefix.dtype == torch.float32 and lse_prefix.shape == (batch, n, Hq) and lse_prefix.is_contiguous()
+    assert node_parent.dtype == torch.int32 and node_parent.shape == (batch, n) and node_parent.is_contiguous()
+    if num_nodes is not None:
+        assert num_nodes.dtype == torch.int32 and num_nodes.shape == (batch,)
+    if out is None:
+        out = dict(o=torch.empty_like(q), lse=torch.empty_like(lse_prefix))
+    _check(lib.uno_tree_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o_prefix), _ptr(lse_prefix), _ptr(node_parent),
+                                  _ptr(num_nodes), 1, batch, n, Hq, Hkv, D, float(scale), _ptr(out["o"]),
+                                  _ptr(out["lse"]), _stream(stream)), "uno_tree_attention")
     return out

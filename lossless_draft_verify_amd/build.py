@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libuno.so")
-SOURCES = ["uno_api.cpp", "filter_kernels.hip", "sample_kernels.hip"]
+SOURCES = ["uno_api.cpp", "filter_kernels.hip", "sample_kernels.hip", "attention_kernels.hip"]
 HEADERS = ["uno_device.h", "uno_internal.h", "exp2_table.inc", os.path.join("..", "..", "include", "uno.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -460,6 +460,25 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
     return hip_status(e);
 }
 
+int uno_tree_attention(const void* q, const void* k, const void* v, const void* o_prefix, const float* lse_prefix,
+                       const int32_t* node_parent, const int32_t* num_nodes, int32_t dtype, int32_t batch,
+                       int32_t n, int32_t Hq, int32_t Hkv, int32_t D, float scale, void* out, float* out_lse,
+                       hipStream_t stream)
+{
+    if (dtype != UNO_BF16 || D != 128) return UNO_ERR_UNSUPPORTED;
+    if (batch < 0 || n < 1 || n > UNO_MAX_TREE_NODES + 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+        Hkv > 65535 || !(scale > 0.0f) || !isfinite(scale))
+        return UNO_ERR_INVALID_ARG;
+    if (batch == 0) return UNO_OK;
+    if (q == nullptr || k == nullptr || v == nullptr || o_prefix == nullptr || lse_prefix == nullptr ||
+        node_parent == nullptr || out == nullptr || out_lse == nullptr)
+        return UNO_ERR_INVALID_ARG;
+    return hip_status(launch_tree_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                            static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o_prefix),
+                                            lse_prefix, node_parent, num_nodes, batch, n, Hq, Hkv, scale,
+                                            static_cast<uint16_t*>(out), out_lse, stream));
+}
+
 const char* uno_status_string(int status)
 {
     switch (status) {

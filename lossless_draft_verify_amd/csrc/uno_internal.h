@@ -157,4 +157,11 @@ hipError_t launch_tree_walk_dense(const RowSource& src, int32_t batch, int32_t B
                                   const int32_t* node_parent, const int32_t* num_nodes, const WalkOut& o,
                                   hipStream_t stream);
 
+// Tree-suffix attention merged with the prefix state (head dimension 128,
+// bf16 tensors, fp32 log-sum-exps); one workgroup per (request, kv head).
+hipError_t launch_tree_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o_prefix,
+                                 const float* lse_prefix, const int32_t* node_parent, const int32_t* num_nodes,
+                                 int32_t batch, int32_t n, int32_t Hq, int32_t Hkv, float scale, uint16_t* out,
+                                 float* out_lse, hipStream_t stream);
+
 }  // namespace uno

@@ -203,3 +203,19 @@ def test_unknown_filter_order_is_rejected(lib, order):
     assert lib.uno_filter(FAKE, F32, 4, 1000, sp(order=order), 64, o, o, o, o, None, 0, None) == INVALID
     assert lib.uno_sample_linear(FAKE, FAKE, F32, 2, 4, 1000, sp(order=order), 1, 0, None, o, o, None,
                                  None, None, 0, None) == INVALID
+
+
+def test_tree_attention_argument_checks(lib):
+    P = ctypes.c_void_p(0x50000)
+    f = lambda dt=BF16, batch=2, n=9, Hq=32, Hkv=8, D=128, scale=0.088, q=P, out=P: lib.uno_tree_attention(
+        q, P, P, P, P, P, None, dt, batch, n, Hq, Hkv, D, ctypes.c_float(scale), out, P, None)
+    assert f(dt=F32) == UNSUPPORTED
+    assert f(D=64) == UNSUPPORTED
+    assert f(n=0) == INVALID
+    assert f(n=131) == INVALID                # more than V + 1 nodes
+    assert f(Hq=30) == INVALID                # Hq % Hkv != 0
+    assert f(scale=0.0) == INVALID
+    assert f(scale=float("nan")) == INVALID
+    assert f(q=None) == INVALID
+    assert f(out=None) == INVALID
+    assert f(batch=0, q=None, out=None) == OK
