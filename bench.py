@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import math
 import json
 import os
 import sys
@@ -97,6 +98,70 @@ def traffic_probe(args, w, lib, pool, dt, sp, stream, dev):
         f"of {src.numel() * src.element_size()} bytes")
 
 
+def bench_tree_attention(args, uno, synth, dev):
+    """uno_tree_attention at a tree workload's verify shape: K timed calls."""
+    import torch
+    a = synth.ATTENTION_WORKLOADS[args.workload]
+    batch, n, Hq, Hkv, D = a["batch"], a["n"], a["Hq"], a["Hkv"], a["D"]
+    q, k, v, op, lp, par = synth.attention_inputs(batch, n, Hq, Hkv, D, a["seed"], device=dev)
+    scale = float(1.0 / math.sqrt(D))
+    out = dict(o=torch.empty_like(q), lse=torch.empty_like(lp))
+    stream = torch.cuda.current_stream()
+    uno.tree_attention(q, k, v, op, lp, par, None, scale, out=out)      # argument checks once
+    # then direct C-ABI calls with pre-built arguments
+    import ctypes
+    lib = uno.load_library()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    cargs = (P(q), P(k), P(v), P(op), P(lp), P(par), None, 1, batch, n, Hq, Hkv, D, ctypes.c_float(scale),
+             P(out["o"]), P(out["lse"]), ctypes.c_void_p(stream.cuda_stream))
+    call = lib.uno_tree_attention
+    for _ in range(args.warmup):
+        assert call(*cargs) == 0
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call(*cargs)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    T = batch * n
+    # one read of q, k, v, o_prefix, lse_prefix and the parents, one write of o and lse
+    nbytes = 2 * T * (3 * Hq + 2 * Hkv) * D + 8 * T * Hq + 4 * T
+    achieved = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] {args.workload}: {us:.2f} us/call (events), {T} verify tokens, {nbytes / 1e6:.1f} MB, "
+        f"{achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        f = lambda t: t.float().cpu().numpy()
+        qs, ks, vs, os_, ls, ps = (f(t) if t.dtype != torch.int32 else t.cpu().numpy() for t in (q, k, v, op, lp, par))
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            oracle.tree_attention(qs, ks, vs, os_, ls, ps, [n] * batch, scale)
+            reps += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(reps * T / el, 1), "unit": "verify tokens/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"{reps} calls of {args.workload} ({T} tokens each), {el:.1f} s"}
+    res = {
+        "metric": "verify tokens/s (tree-suffix attention merged with the prefix state)",
+        "value": round(T / (us * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": batch, "verify_tokens": n, "heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "tree_attention_kernel",
+                     "kernel_us": round(us, 3), "bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 4),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -114,6 +179,9 @@ def main():
     uno.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.workload in synth.ATTENTION_WORKLOADS:
+        bench_tree_attention(args, uno, synth, dev)
+        return
     w = synth.WORKLOADS[args.workload]
     stream = torch.cuda.current_stream()
 

@@ -212,7 +212,8 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
  * Tokens at or past num_nodes[b] are neither read nor written.  Scores,
  * softmax and sums run in fp32.  No workspace.
  * Requires dtype UNO_BF16 and D == 128 (else UNO_ERR_UNSUPPORTED),
- * 1 <= n <= UNO_MAX_TREE_NODES + 1, Hq % Hkv == 0 and scale > 0. */
+ * 1 <= n <= UNO_MAX_TREE_NODES + 1, Hq % Hkv == 0, scale > 0, and k, v
+ * 16-byte aligned. */
 int uno_tree_attention(const void* q, const void* k, const void* v, const void* o_prefix,
                        const float* lse_prefix, const int32_t* node_parent, const int32_t* num_nodes,
                        int32_t dtype, int32_t batch, int32_t n, int32_t Hq, int32_t Hkv, int32_t D,

@@ -473,6 +473,8 @@ int uno_tree_attention(const void* q, const void* k, const void* v, const void* 
     if (q == nullptr || k == nullptr || v == nullptr || o_prefix == nullptr || lse_prefix == nullptr ||
         node_parent == nullptr || out == nullptr || out_lse == nullptr)
         return UNO_ERR_INVALID_ARG;
+    if (!aligned(k, 16) || !aligned(v, 16))          // staged 16 bytes at a time
+        return UNO_ERR_INVALID_ARG;
     return hip_status(launch_tree_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                             static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o_prefix),
                                             lse_prefix, node_parent, num_nodes, batch, n, Hq, Hkv, scale,

@@ -161,3 +161,27 @@ def tree_target_rows(R: torch.Tensor, node_depth: torch.Tensor, num_nodes: torch
 def as_float32_numpy(t: torch.Tensor):
     """Exact float32 view of f32/bf16 logits for the host side."""
     return t.detach().to("cpu").to(torch.float32).contiguous().numpy()
+
+
+# Tree-suffix attention inputs at the tree workloads' verify shapes (Qwen3-8B
+# attention: 32 query heads, 8 key/value heads, head dimension 128).
+ATTENTION_WORKLOADS = {
+    "tree_attention_8_16_8": dict(batch=64, n=9, Hq=32, Hkv=8, D=128, seed=123),
+    "tree_attention_16_32_32": dict(batch=1, n=33, Hq=32, Hkv=8, D=128, seed=42),
+}
+
+
+def attention_inputs(batch: int, n: int, Hq: int, Hkv: int, D: int, seed: int, device="cpu"):
+    """q, k, v, o_prefix (bf16), lse_prefix (fp32), node_parent (int32, parents
+    before children) for `batch` requests of n verify tokens each."""
+    g = _generator(seed, 0, device)
+    q = torch.randn(batch, n, Hq, D, generator=g, device=device).to(torch.bfloat16)
+    k = torch.randn(batch, n, Hkv, D, generator=g, device=device).to(torch.bfloat16)
+    v = torch.randn(batch, n, Hkv, D, generator=g, device=device).to(torch.bfloat16)
+    o_prefix = torch.randn(batch, n, Hq, D, generator=g, device=device).to(torch.bfloat16)
+    lse_prefix = 3.0 * torch.randn(batch, n, Hq, generator=g, device=device)
+    u = torch.rand(batch, n, generator=g, device=device)
+    idx = torch.arange(n, device=device).view(1, n)
+    parent = torch.floor(u * idx).to(torch.int32)           # uniform over the earlier nodes
+    parent[:, 0] = -1
+    return q, k, v, o_prefix, lse_prefix.contiguous(), parent.contiguous()

@@ -219,3 +219,6 @@ def test_tree_attention_argument_checks(lib):
     assert f(q=None) == INVALID
     assert f(out=None) == INVALID
     assert f(batch=0, q=None, out=None) == OK
+    odd = ctypes.c_void_p(0x50008)            # k and v must be 16-byte aligned
+    assert lib.uno_tree_attention(P, odd, P, P, P, P, None, BF16, 2, 9, 32, 8, 128, ctypes.c_float(0.1), P, P,
+                                  None) == INVALID
