@@ -8,11 +8,13 @@
 // constraints fix both acceptance thresholds at 1.0.
 //
 // Sampling from a distribution is an inverse CDF in ascending token-id order.
-// A sparse support (<= 256 ids) is held by one wave in registers, put in id
-// order through LDS, and its cumulative sum is taken in that order in double
-// precision (the same additions, in the same order, as a sequential scan over
-// the dense vector, whose zeros add nothing).  Dense rows are located chunk by
-// chunk from per-chunk statistics and finished inside one 2048-logit chunk.
+// A sparse support (<= 256 ids) arrives in id order with its cumulative sums,
+// taken in that order in double precision by the filter (the same additions,
+// in the same order, as a sequential scan over the dense vector, whose zeros
+// add nothing); one wave holds it in registers and picks by ballot.  Dense
+// rows are located chunk by chunk from per-chunk statistics and finished
+// inside one 2048-logit chunk; a full-vocabulary nucleus restricts every
+// weight to the logits at or above the row's keep threshold.
 #include "uno_device.h"
 #include "uno_internal.h"
 
@@ -173,8 +175,8 @@ __device__ __forceinline__ double reg_lookup(const WaveRow& R, int n, int32_t y,
     return v;
 }
 
-// Per-wave LDS scratch for sorting one support.
-struct SortScratch {
+// Per-wave LDS copy of one id-ordered support (ids, weights, cumulative sums).
+struct SupportScratch {
     int32_t id[kMaxK];
     double w[kMaxK];
     double cum[kMaxK];
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     int32_t batch, int32_t B, SparseOut sup, uint64_t seed, uint64_t offset,
     const uint32_t* req_ids, LinearOut o)
 {
-    __shared__ SortScratch s_q[kLinWaves];     // q_j in id order for the residual's lookups; its cumulative sums
+    __shared__ SupportScratch s_q[kLinWaves];     // q_j in id order for the residual's lookups; its cumulative sums
     __shared__ int32_t s_y[kMaxLinearB];
     __shared__ int32_t s_acc[kMaxLinearB];
     __shared__ int32_t s_fin[kMaxLinearB + 1];
