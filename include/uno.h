@@ -193,6 +193,41 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
                     uint32_t* out_flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
+/* Per-request sampling parameters.  Each *_ex entry point is its namesake with
+ * `sp` an array of n_sp sets: n_sp == 1 is the namesake; n_sp == batch (rows
+ * for uno_filter_ex) gives request b (row r) the set sp[b] (sp[r]), so greedy
+ * and stochastic requests with their own temperature, top-k, top-p and order
+ * share one call.  With n_sp > 1 every set must take the top-k path
+ * (temperature == 0, top-k on with top_k <= UNO_MAX_TOP_K, or a vocabulary of
+ * at most UNO_MAX_TOP_K), and the joint-order sets must share one temperature;
+ * else UNO_ERR_UNSUPPORTED.  Supports are sized for the largest k (cap for
+ * uno_filter_ex).  The sets are copied to the workspace on `stream` (host
+ * memory; the call returns once they are staged).  Workspace sizes come from
+ * uno_workspace_bytes_ex with the same sets. */
+int uno_workspace_bytes_ex(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K, int32_t V,
+                           int64_t vocab, int32_t dtype, const uno_sampling_t* sp, int32_t n_sp,
+                           size_t* out_bytes);
+int uno_filter_ex(const void* logits, int32_t dtype, int64_t rows, int64_t vocab,
+                  const uno_sampling_t* sp, int32_t n_sp, int32_t cap,
+                  int32_t* out_ids, double* out_probs, int32_t* out_count, double* out_stats,
+                  void* ws, size_t ws_bytes, hipStream_t stream);
+int uno_sample_linear_ex(const void* draft, const void* target, int32_t dtype, int32_t batch,
+                         int32_t B, int64_t vocab, const uno_sampling_t* sp, int32_t n_sp,
+                         uint64_t seed, uint64_t offset, const uint32_t* request_ids,
+                         int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_proposals,
+                         uint32_t* out_flags, void* ws, size_t ws_bytes, hipStream_t stream);
+int uno_build_tree_ex(const void* draft, int32_t dtype, int32_t batch, int32_t B, int32_t K,
+                      int32_t V, int64_t vocab, const uno_sampling_t* sp, int32_t n_sp,
+                      int32_t* node_token, int32_t* node_parent, int32_t* node_depth,
+                      double* node_score, int32_t* num_nodes,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+int uno_verify_tree_ex(const void* target, int32_t dtype, int32_t batch, int32_t B, int32_t V,
+                       int64_t vocab, const uno_sampling_t* sp, int32_t n_sp, uint64_t seed,
+                       uint64_t offset, const uint32_t* request_ids,
+                       const int32_t* node_token, const int32_t* node_parent, const int32_t* num_nodes,
+                       int32_t* out_tokens, int32_t* out_path, int32_t* out_accept_len,
+                       uint32_t* out_flags, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Tree-suffix attention merged with the prefix attention state.  (PR #37667,
  * Modifications: an UNO-only fused kernel for tree-suffix attention and LSE
  * merge; Changes to shared SGLang infrastructure: it serves UNO tree

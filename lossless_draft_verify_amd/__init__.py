@@ -12,6 +12,7 @@ import ctypes
 import os
 import threading
 
+import numpy as np
 import torch
 
 __all__ = [
@@ -67,10 +68,19 @@ def load_library():
                                        ctypes.c_size_t, P]
         lib.uno_verify_tree.argtypes = [P, i32, i32, i32, i32, i64, SP, u64, u64, P, P, P, P, P, P,
                                         P, P, P, ctypes.c_size_t, P]
+        lib.uno_workspace_bytes_ex.argtypes = [i32, i64, i32, i32, i32, i64, i32, SP, i32, sz]
+        lib.uno_filter_ex.argtypes = [P, i32, i64, i64, SP, i32, i32, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.uno_sample_linear_ex.argtypes = [P, P, i32, i32, i32, i64, SP, i32, u64, u64, P, P, P, P, P, P,
+                                             ctypes.c_size_t, P]
+        lib.uno_build_tree_ex.argtypes = [P, i32, i32, i32, i32, i32, i64, SP, i32, P, P, P, P, P, P,
+                                          ctypes.c_size_t, P]
+        lib.uno_verify_tree_ex.argtypes = [P, i32, i32, i32, i32, i64, SP, i32, u64, u64, P, P, P, P, P, P,
+                                           P, P, P, ctypes.c_size_t, P]
         lib.uno_tree_attention.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                            P, P, P]
         for f in ("uno_workspace_bytes", "uno_filter", "uno_sample_linear", "uno_build_tree",
-                  "uno_verify_tree", "uno_tree_attention", "uno_last_hip_error"):
+                  "uno_verify_tree", "uno_tree_attention", "uno_last_hip_error", "uno_workspace_bytes_ex",
+                  "uno_filter_ex", "uno_sample_linear_ex", "uno_build_tree_ex", "uno_verify_tree_ex"):
             getattr(lib, f).restype = ctypes.c_int
         lib.uno_status_string.argtypes = [ctypes.c_int]
         lib.uno_status_string.restype = ctypes.c_char_p
@@ -105,13 +115,23 @@ def _sp(temperature, top_k, top_p, order=ORDER_TOPK_FIRST) -> Sampling:
     return Sampling(float(temperature), int(top_k), float(top_p), int(order))
 
 
+def _sp_set(n, temperature, top_k, top_p, order):
+    """(array of Sampling, count): one set when every parameter is a scalar,
+    else one per request (or row), each parameter broadcast to n."""
+    vals = [np.asarray(x.cpu() if isinstance(x, torch.Tensor) else x) for x in (temperature, top_k, top_p, order)]
+    if all(v.ndim == 0 for v in vals):
+        return (Sampling * 1)(_sp(*[v.item() for v in vals])), 1
+    T, K, P, O = (np.broadcast_to(v, (n,)) for v in vals)
+    return (Sampling * n)(*[Sampling(float(T[i]), int(K[i]), float(P[i]), int(O[i])) for i in range(n)]), n
+
+
 def workspace_bytes(op, batch_or_rows, B, K, V, vocab, dtype_code, temperature, top_k, top_p,
                     order=ORDER_TOPK_FIRST) -> int:
     lib = load_library()
     out = ctypes.c_size_t(0)
-    sp = _sp(temperature, top_k, top_p, order)
-    _check(lib.uno_workspace_bytes(op, batch_or_rows, B, K, V, vocab, dtype_code, ctypes.byref(sp),
-                                   ctypes.byref(out)), "uno_workspace_bytes")
+    sps, n = _sp_set(batch_or_rows, temperature, top_k, top_p, order)
+    _check(lib.uno_workspace_bytes_ex(op, batch_or_rows, B, K, V, vocab, dtype_code, sps, n, ctypes.byref(out)),
+           "uno_workspace_bytes_ex")
     return int(out.value)
 
 
@@ -150,10 +170,14 @@ def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, str
     rows, vocab = logits.shape
     dt = _dtype_code(logits)
     dev = logits.device
-    greedy = float(temperature) == 0.0
-    topk_on = 0 < int(top_k) < vocab
-    sparse = greedy or topk_on or vocab <= MAX_TOP_K
-    k_eff = 1 if greedy else (int(top_k) if topk_on else (vocab if sparse else 0))
+    sps, nsp = _sp_set(rows, temperature, top_k, top_p, order)
+    sparse, k_eff = True, 1
+    for i in range(nsp):
+        greedy = sps[i].temperature == 0.0
+        topk_on = 0 < sps[i].top_k < vocab
+        sp_i = greedy or topk_on or vocab <= MAX_TOP_K
+        sparse = sparse and sp_i
+        k_eff = max(k_eff, 1 if greedy else (sps[i].top_k if topk_on else (vocab if sp_i else 0)))
     cap = (k_eff if sparse else 0) if cap is None else int(cap)
     nb = workspace_bytes(OP_FILTER, rows, 0, 0, 0, vocab, dt, temperature, top_k, top_p, order)
     ws = _workspace(nb, dev, workspace)
@@ -162,10 +186,9 @@ def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, str
     probs = torch.empty((rows, max(cap, 1)), dtype=torch.float64, device=dev) if sparse else None
     count = torch.empty(rows, dtype=torch.int32, device=dev)
     stats = torch.empty((rows, 2), dtype=torch.float64, device=dev)
-    sp = _sp(temperature, top_k, top_p, order)
-    _check(lib.uno_filter(_ptr(logits), dt, rows, vocab, ctypes.byref(sp), cap, _ptr(ids),
-                          _ptr(probs), _ptr(count), _ptr(stats), wsp, wsn, _stream(stream)),
-           "uno_filter")
+    _check(lib.uno_filter_ex(_ptr(logits), dt, rows, vocab, sps, nsp, cap, _ptr(ids),
+                             _ptr(probs), _ptr(count), _ptr(stats), wsp, wsn, _stream(stream)),
+           "uno_filter_ex")
     return dict(ids=ids, probs=probs, count=count, stats=stats, workspace=ws)
 
 
@@ -189,12 +212,12 @@ def sample_linear(draft, target, temperature, top_k, top_p, seed, offset, reques
         workspace = _workspace(nb, dev, None)
     wsp, wsn = _aligned_ptr(workspace)
     rid = _as_u32_ids(request_ids, batch, dev)
-    sp = _sp(temperature, top_k, top_p, order)
-    _check(lib.uno_sample_linear(_ptr(draft), _ptr(target), dt, batch, B, vocab, ctypes.byref(sp),
+    sps, nsp = _sp_set(batch, temperature, top_k, top_p, order)
+    _check(lib.uno_sample_linear_ex(_ptr(draft), _ptr(target), dt, batch, B, vocab, sps, nsp,
                                  int(seed), int(offset), _ptr(rid), _ptr(out["tokens"]),
                                  _ptr(out["accept_len"]), _ptr(out.get("proposals")),
                                  _ptr(out.get("flags")), wsp, wsn, _stream(stream)),
-           "uno_sample_linear")
+           "uno_sample_linear_ex")
     out["workspace"] = workspace
     return out
 
@@ -217,11 +240,11 @@ def build_tree(draft, K, V, temperature, top_k, top_p, out=None, workspace=None,
         nb = workspace_bytes(OP_BUILD_TREE, batch, B, K, V, vocab, dt, temperature, top_k, top_p, order)
         workspace = _workspace(nb, dev, None)
     wsp, wsn = _aligned_ptr(workspace)
-    sp = _sp(temperature, top_k, top_p, order)
-    _check(lib.uno_build_tree(_ptr(draft), dt, batch, B, int(K), int(V), vocab, ctypes.byref(sp),
+    sps, nsp = _sp_set(batch, temperature, top_k, top_p, order)
+    _check(lib.uno_build_tree_ex(_ptr(draft), dt, batch, B, int(K), int(V), vocab, sps, nsp,
                               _ptr(out["node_token"]), _ptr(out["node_parent"]),
                               _ptr(out["node_depth"]), _ptr(out.get("node_score")),
-                              _ptr(out["num_nodes"]), wsp, wsn, _stream(stream)), "uno_build_tree")
+                              _ptr(out["num_nodes"]), wsp, wsn, _stream(stream)), "uno_build_tree_ex")
     out["workspace"] = workspace
     return out
 
@@ -248,12 +271,12 @@ def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_
         workspace = _workspace(nb, dev, None)
     wsp, wsn = _aligned_ptr(workspace)
     rid = _as_u32_ids(request_ids, batch, dev)
-    sp = _sp(temperature, top_k, top_p, order)
-    _check(lib.uno_verify_tree(_ptr(target), dt, batch, int(B), V, vocab, ctypes.byref(sp),
+    sps, nsp = _sp_set(batch, temperature, top_k, top_p, order)
+    _check(lib.uno_verify_tree_ex(_ptr(target), dt, batch, int(B), V, vocab, sps, nsp,
                                int(seed), int(offset), _ptr(rid), _ptr(node_token),
                                _ptr(node_parent), _ptr(num_nodes), _ptr(out["tokens"]),
                                _ptr(out["path"]), _ptr(out["accept_len"]), _ptr(out.get("flags")),
-                               wsp, wsn, _stream(stream)), "uno_verify_tree")
+                               wsp, wsn, _stream(stream)), "uno_verify_tree_ex")
     out["workspace"] = workspace
     return out
 

@@ -397,8 +397,8 @@ __device__ __forceinline__ void finalize_row(uint32_t* sk, const int32_t* sid, d
 // segment's sorted top-k for topk_merge_kernel.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
-    RowSource src, int64_t rows, int64_t N, FilterParams fp, SparseOut out, int S,
-    uint32_t* part_key, int32_t* part_id, int32_t* part_n)
+    RowSource src, int64_t rows, int64_t N, FilterParams fp_all, SparseOut out, int S,
+    uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap, const FilterParams* rowp)
 {
     using V = Vec<BF16>;
     constexpr int EPV = V::EPV, ESZ = V::ESZ;
@@ -421,6 +421,7 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     // and the dispatcher hands the next row's segments to whichever CUs free up
     const int64_t r = blockIdx.x / S;
     const int seg = (int)(blockIdx.x - r * S);
+    const FilterParams fp = rowp ? rowp[r] : fp_all;              // per-row parameters when given
     const char* row = row_pointer(src, r, N * ESZ);
     if (row == nullptr) {
         if (S == 1 && threadIdx.x == 0) out.count[r] = -1;
@@ -650,7 +651,7 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     if (S == 1) {
         if (w == rot) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane, s_scal, s_cx);
     } else {
-        const int64_t base = (r * S + seg) * (int64_t)k;
+        const int64_t base = (r * S + seg) * (int64_t)part_cap;
         for (int i = threadIdx.x; i < n; i += kThreads) {
             part_key[base + i] = s_sk[i];
             part_id[base + i] = s_sid[i];
@@ -663,8 +664,9 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
 // are pruned by the best full list's k-th entry, ranked together and
 // finalised.  Every global read is spread over the workgroup.
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
-    RowSource src, int64_t rows, FilterParams fp, SparseOut out, int S,
-    const uint32_t* part_key, const int32_t* part_id, const int32_t* part_n)
+    RowSource src, int64_t rows, FilterParams fp_all, SparseOut out, int S,
+    const uint32_t* part_key, const int32_t* part_id, const int32_t* part_n, int part_cap,
+    const FilterParams* rowp)
 {
     __shared__ uint2 s_cand[kMergeCap];
     __shared__ uint32_t s_sk[kMaxK];
@@ -686,6 +688,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
         if (threadIdx.x == 0) out.count[r] = -1;
         return;
     }
+    const FilterParams fp = rowp ? rowp[r] : fp_all;
     const int k = fp.k;
     // Per segment: its count, its first key, and two lower bounds on the row's
     // k-th entry -- the k-th entry of a full list, and (quota q = ceil(k/S)) the
@@ -694,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     uint64_t p = 0, pq = ~0ull;
     uint32_t top = 0;
     for (int sg = threadIdx.x; sg < S; sg += kThreads) {
-        const int64_t base = (r * S + sg) * (int64_t)k;
+        const int64_t base = (r * S + sg) * (int64_t)part_cap;
         const int ns = part_n[r * S + sg];
         s_segn[sg] = ns;
         if (ns > 0) top = part_key[base] > top ? part_key[base] : top;    // lists are sorted
@@ -735,7 +738,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
         int32_t ii = 0;
         bool keep = false;
         if (g < total) {
-            const int64_t base = (r * S + sg) * (int64_t)k;
+            const int64_t base = (r * S + sg) * (int64_t)part_cap;
             kk = part_key[base + i];
             ii = part_id[base + i];
             keep = i < s_segn[sg] && order_key(kk, ii) >= pstar;
@@ -933,21 +936,21 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                               const FilterParams& fp, const SparseOut& out, int S,
-                              uint32_t* part_key, int32_t* part_id, int32_t* part_n,
-                              hipStream_t stream)
+                              uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap,
+                              const FilterParams* rowp, hipStream_t stream)
 {
     if (rows == 0) return hipSuccess;
     dim3 grid((unsigned)(rows * S));
     if (bf16)
         topk_stream_kernel<true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
-                                                                part_id, part_n);
+                                                                part_id, part_n, part_cap, rowp);
     else
         topk_stream_kernel<false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
-                                                                 part_id, part_n);
+                                                                 part_id, part_n, part_cap, rowp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     topk_merge_kernel<<<dim3((unsigned)rows), kThreads, 0, stream>>>(src, rows, fp, out, S, part_key,
-                                                                   part_id, part_n);
+                                                                   part_id, part_n, part_cap, rowp);
     return hipGetLastError();
 }
 

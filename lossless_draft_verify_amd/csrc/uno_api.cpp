@@ -6,6 +6,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <vector>
+
 using namespace uno;
 
 namespace {
@@ -22,7 +24,9 @@ struct Mode {
     bool sparse;     // support from a top-k selection (greedy: k = 1)
     bool joint;      // joint order with both top-k and top-p on (sparse only)
     bool nucleus;    // top-p without top-k over a full vocabulary (dense only)
+    bool per_request;// one parameter set per request (sparse only; k is the largest)
     int32_t k;       // effective k on the sparse path
+    float joint_T;   // temperature of the joint-order chunk statistics
 };
 
 int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
@@ -42,9 +46,64 @@ int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
     m->joint = sp->order == UNO_ORDER_JOINT && !m->greedy && m->topk_on && m->topp_on;
     if (m->sparse && m->k > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
     m->nucleus = !m->sparse && m->topp_on;
+    m->per_request = false;
+    m->joint_T = T;
     if (!m->sparse && vocab > (int64_t)65535 * 4 * kDenseChunk) return UNO_ERR_UNSUPPORTED;
     return UNO_OK;
 }
+
+// Sampling parameters of a call: one set for every row, or one per request.
+struct SpSet {
+    const uno_sampling_t* sp;
+    int64_t n;
+};
+
+// One set: its mode.  One per request (n == requests): every set must take the
+// top-k path (greedy, top-k on, or a small vocabulary); the combined mode has
+// the largest k and carries the joint-order statistics when any set needs them
+// (one chunk pass, so the joint-order sets must share their temperature).
+int check_set(const SpSet& s, int64_t requests, int64_t vocab, Mode* m)
+{
+    if (s.sp == nullptr) return UNO_ERR_INVALID_ARG;
+    if (s.n == 1) return check_sampling(s.sp, vocab, m);
+    if (s.n != requests || s.n < 1) return UNO_ERR_INVALID_ARG;
+    Mode all{};
+    all.sparse = true;
+    all.per_request = true;
+    all.greedy = true;
+    all.k = 1;
+    for (int64_t i = 0; i < s.n; ++i) {
+        Mode mi;
+        const int st = check_sampling(&s.sp[i], vocab, &mi);
+        if (st) return st;
+        if (!mi.sparse) return UNO_ERR_UNSUPPORTED;     // per-request parameters take the top-k path only
+        all.greedy = all.greedy && mi.greedy;
+        all.topk_on = all.topk_on || mi.topk_on;
+        all.topp_on = all.topp_on || mi.topp_on;
+        if (mi.joint) {
+            if (all.joint && mi.joint_T != all.joint_T) return UNO_ERR_UNSUPPORTED;
+            all.joint = true;
+            all.joint_T = mi.joint_T;
+        }
+        all.k = mi.k > all.k ? mi.k : all.k;
+    }
+    *m = all;
+    return UNO_OK;
+}
+
+// Request of row r for each entry point's row layout.
+struct RowMap {
+    int kind;          // 0: one row per request, 1: linear (draft rows, then target rows), 2: rows_per_req rows each
+    int64_t batch;
+    int32_t B;
+    int32_t rows_per_req;
+    int64_t req(int64_t r) const
+    {
+        if (kind == 0) return r;
+        if (kind == 1) return r < batch * B ? r / B : (r - batch * B) / (B + 1);
+        return r / rows_per_req;
+    }
+};
 
 int check_common(int32_t dtype, int64_t vocab)
 {
@@ -78,6 +137,8 @@ struct SparseWs {
     int32_t* part_n;
     DenseChunks full;    // joint order: exact chunk statistics of the rows
     int32_t* nucleus_n;  // dense tree build with a nucleus: support sizes
+    FilterParams* rowp;  // per-request parameters: one set per row
+    int part_cap;        // entries per segment list (the largest k)
 };
 
 DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bool keep);
@@ -89,6 +150,7 @@ void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool ow
                   SparseWs* w)
 {
     w->S = topk_segments(rows, vocab, m.k);
+    w->part_cap = m.k;
     if (own_supports) {
         w->sup.cap = m.k;
         w->sup.ids = cv.take<int32_t>((size_t)rows * m.k);
@@ -108,6 +170,7 @@ void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool ow
     w->nucleus_n = nullptr;
     w->full = DenseChunks{};
     if (m.joint) w->full = carve_chunks(cv, rows, vocab, false, false);
+    w->rowp = m.per_request ? cv.take<FilterParams>((size_t)rows) : nullptr;
 }
 
 // Chunk statistics; the finite counts only for uno_filter, whose dense mode
@@ -166,19 +229,39 @@ FilterParams filter_params(const uno_sampling_t* sp, const Mode& m)
 
 // The sparse filter of `rows` rows into `out`; the joint order first takes
 // exact chunk statistics of the same rows for the full-softmax normaliser.
+// With per-request parameters each row's set is copied to the workspace.
 hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
-                                const uno_sampling_t* sp, const Mode& m, const SparseWs& sw,
+                                const SpSet& sps, const RowMap& map, const Mode& m, const SparseWs& sw,
                                 const SparseOut& out, hipStream_t stream)
 {
-    FilterParams fp = filter_params(sp, m);
+    FilterParams fp = filter_params(sps.sp, m);
     if (m.joint) {
-        const hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, sw.full, rows, stream);
+        const hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, m.joint_T, sw.full, rows, stream);
         if (e != hipSuccess) return e;
         fp.full_cmax = sw.full.cmax;
         fp.full_csum = sw.full.csum;
         fp.full_nc = sw.full.nchunks;
     }
-    return launch_topk_filter(src, rows, vocab, bf16, fp, out, sw.S, sw.part_key, sw.part_id, sw.part_n, stream);
+    if (m.per_request) {
+        std::vector<FilterParams> host((size_t)rows);
+        for (int64_t r = 0; r < rows; ++r) {
+            const uno_sampling_t* s = &sps.sp[map.req(r)];
+            Mode mi;
+            check_sampling(s, vocab, &mi);
+            host[(size_t)r] = filter_params(s, mi);
+            if (mi.joint) {
+                host[(size_t)r].full_cmax = sw.full.cmax;
+                host[(size_t)r].full_csum = sw.full.csum;
+                host[(size_t)r].full_nc = sw.full.nchunks;
+            }
+        }
+        // from pageable memory: the call returns once the data is staged
+        const hipError_t e = hipMemcpyAsync(sw.rowp, host.data(), host.size() * sizeof(FilterParams),
+                                            hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_topk_filter(src, rows, vocab, bf16, fp, out, sw.S, sw.part_key, sw.part_id, sw.part_n,
+                              sw.part_cap, sw.rowp, stream);
 }
 
 int check_tree_shape(int32_t B, int32_t K, int32_t V, bool need_k)
@@ -189,13 +272,13 @@ int check_tree_shape(int32_t B, int32_t K, int32_t V, bool need_k)
 }
 
 // ---- per-op layout (shared by the size query and the calls) ---------------------
-int layout_filter(int64_t rows, int64_t vocab, int32_t dtype, const uno_sampling_t* sp, Carve& cv,
+int layout_filter(int64_t rows, int64_t vocab, int32_t dtype, const SpSet& sps, Carve& cv,
                   Mode* m, SparseWs* sw, DenseChunks* dc)
 {
     int st = check_common(dtype, vocab);
     if (st) return st;
     if (rows < 0 || rows > 0x7FFFFFFF) return UNO_ERR_INVALID_ARG;
-    st = check_sampling(sp, vocab, m);
+    st = check_set(sps, rows, vocab, m);
     if (st) return st;
     if (rows == 0) return UNO_OK;
     if (m->sparse) carve_sparse(cv, rows, vocab, *m, false, false, sw);
@@ -204,13 +287,13 @@ int layout_filter(int64_t rows, int64_t vocab, int32_t dtype, const uno_sampling
     return UNO_OK;
 }
 
-int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const uno_sampling_t* sp,
+int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const SpSet& sps,
                   Carve& cv, Mode* m, SparseWs* sw, DenseChunks* dc, DenseScratch* ds)
 {
     int st = check_common(dtype, vocab);
     if (st) return st;
     if (batch < 0 || B < 1 || B > 128 || batch * (2 * (int64_t)B + 1) > 0x7FFFFFFF) return UNO_ERR_INVALID_ARG;
-    st = check_sampling(sp, vocab, m);
+    st = check_set(sps, batch, vocab, m);
     if (st) return st;
     if (batch == 0) return UNO_OK;
     const int64_t rows = batch * (2 * (int64_t)B + 1);
@@ -224,7 +307,7 @@ int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const 
 }
 
 int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int64_t vocab, int32_t dtype,
-                const uno_sampling_t* sp, Carve& cv, Mode* m, SparseWs* sw, DenseChunks* dc)
+                const SpSet& sps, Carve& cv, Mode* m, SparseWs* sw, DenseChunks* dc)
 {
     int st = check_common(dtype, vocab);
     if (st) return st;
@@ -232,7 +315,7 @@ int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int6
     const bool build = op == UNO_OP_BUILD_TREE;
     st = check_tree_shape(B, K, V, build);
     if (st) return st;
-    st = check_sampling(sp, vocab, m);
+    st = check_set(sps, batch, vocab, m);
     if (st) return st;
     // a full-vocabulary build selects its K candidates with the top-k path
     if (!m->sparse && build && K > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
@@ -258,9 +341,10 @@ int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int6
 
 extern "C" {
 
-int uno_workspace_bytes(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K, int32_t V, int64_t vocab,
-                        int32_t dtype, const uno_sampling_t* sp, size_t* out_bytes)
+int uno_workspace_bytes_ex(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K, int32_t V, int64_t vocab,
+                           int32_t dtype, const uno_sampling_t* sp, int32_t n_sp, size_t* out_bytes)
 {
+    const SpSet sps{ sp, n_sp };
     if (out_bytes == nullptr) return UNO_ERR_INVALID_ARG;
     Carve cv{ nullptr };
     Mode m;
@@ -269,10 +353,10 @@ int uno_workspace_bytes(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K,
     DenseScratch ds;
     int st;
     switch (op) {
-    case UNO_OP_FILTER: st = layout_filter(batch_or_rows, vocab, dtype, sp, cv, &m, &sw, &dc); break;
-    case UNO_OP_SAMPLE_LINEAR: st = layout_linear(batch_or_rows, B, vocab, dtype, sp, cv, &m, &sw, &dc, &ds); break;
+    case UNO_OP_FILTER: st = layout_filter(batch_or_rows, vocab, dtype, sps, cv, &m, &sw, &dc); break;
+    case UNO_OP_SAMPLE_LINEAR: st = layout_linear(batch_or_rows, B, vocab, dtype, sps, cv, &m, &sw, &dc, &ds); break;
     case UNO_OP_BUILD_TREE:
-    case UNO_OP_VERIFY_TREE: st = layout_tree(op, batch_or_rows, B, K, V, vocab, dtype, sp, cv, &m, &sw, &dc); break;
+    case UNO_OP_VERIFY_TREE: st = layout_tree(op, batch_or_rows, B, K, V, vocab, dtype, sps, cv, &m, &sw, &dc); break;
     default: return UNO_ERR_INVALID_ARG;
     }
     if (st) return st;
@@ -280,15 +364,17 @@ int uno_workspace_bytes(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K,
     return UNO_OK;
 }
 
-int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab, const uno_sampling_t* sp,
-               int32_t cap, int32_t* out_ids, double* out_probs, int32_t* out_count, double* out_stats,
-               void* ws, size_t ws_bytes, hipStream_t stream)
+int uno_filter_ex(const void* logits, int32_t dtype, int64_t rows, int64_t vocab, const uno_sampling_t* sp,
+                  int32_t n_sp, int32_t cap, int32_t* out_ids, double* out_probs, int32_t* out_count,
+                  double* out_stats, void* ws, size_t ws_bytes, hipStream_t stream)
 {
+    const SpSet sps{ sp, n_sp };
+    const RowMap map{ 0, rows, 0, 1 };
     Carve sizing{ nullptr };
     Mode m;
     SparseWs sw;
     DenseChunks dc;
-    int st = layout_filter(rows, vocab, dtype, sp, sizing, &m, &sw, &dc);
+    int st = layout_filter(rows, vocab, dtype, sps, sizing, &m, &sw, &dc);
     if (st) return st;
     if (rows == 0) return UNO_OK;
     if (logits == nullptr || out_count == nullptr || !aligned(logits, elem_size(dtype))) return UNO_ERR_INVALID_ARG;
@@ -300,13 +386,13 @@ int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab, c
     st = check_ws(ws, ws_bytes, sizing.used);
     if (st) return st;
     Carve cv{ static_cast<char*>(ws) };
-    layout_filter(rows, vocab, dtype, sp, cv, &m, &sw, &dc);
+    layout_filter(rows, vocab, dtype, sps, cv, &m, &sw, &dc);
 
     RowSource src{ static_cast<const char*>(logits), rows, nullptr, nullptr, 1 };
     const bool bf16 = dtype == UNO_BF16;
     if (m.sparse) {
         SparseOut out{ out_ids, out_probs, out_count, out_stats, cap };
-        return hip_status(launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, out, stream));
+        return hip_status(launch_sparse_filter(src, rows, vocab, bf16, sps, map, m, sw, out, stream));
     }
     hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
     if (e == hipSuccess) {
@@ -318,18 +404,20 @@ int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab, c
     return hip_status(e);
 }
 
-int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int32_t batch, int32_t B,
-                      int64_t vocab, const uno_sampling_t* sp, uint64_t seed, uint64_t offset,
-                      const uint32_t* request_ids, int32_t* out_tokens, int32_t* out_accept_len,
-                      int32_t* out_proposals, uint32_t* out_flags, void* ws, size_t ws_bytes,
-                      hipStream_t stream)
+int uno_sample_linear_ex(const void* draft, const void* target, int32_t dtype, int32_t batch, int32_t B,
+                         int64_t vocab, const uno_sampling_t* sp, int32_t n_sp, uint64_t seed, uint64_t offset,
+                         const uint32_t* request_ids, int32_t* out_tokens, int32_t* out_accept_len,
+                         int32_t* out_proposals, uint32_t* out_flags, void* ws, size_t ws_bytes,
+                         hipStream_t stream)
 {
+    const SpSet sps{ sp, n_sp };
+    const RowMap map{ 1, batch, B, 1 };
     Carve sizing{ nullptr };
     Mode m;
     SparseWs sw;
     DenseChunks dc;
     DenseScratch ds;
-    int st = layout_linear(batch, B, vocab, dtype, sp, sizing, &m, &sw, &dc, &ds);
+    int st = layout_linear(batch, B, vocab, dtype, sps, sizing, &m, &sw, &dc, &ds);
     if (st) return st;
     if (batch == 0) return UNO_OK;
     const size_t es = elem_size(dtype);
@@ -339,7 +427,7 @@ int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int3
     st = check_ws(ws, ws_bytes, sizing.used);
     if (st) return st;
     Carve cv{ static_cast<char*>(ws) };
-    layout_linear(batch, B, vocab, dtype, sp, cv, &m, &sw, &dc, &ds);
+    layout_linear(batch, B, vocab, dtype, sps, cv, &m, &sw, &dc, &ds);
 
     const int64_t rows = (int64_t)batch * (2 * B + 1);
     RowSource src{ static_cast<const char*>(draft), (int64_t)batch * B, static_cast<const char*>(target),
@@ -348,7 +436,7 @@ int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int3
     LinearOut o{ out_tokens, out_accept_len, out_proposals, out_flags };
     hipError_t e;
     if (m.sparse) {
-        e = launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, sw.sup, stream);
+        e = launch_sparse_filter(src, rows, vocab, bf16, sps, map, m, sw, sw.sup, stream);
         if (e == hipSuccess) e = launch_linear_sparse(batch, B, sw.sup, seed, offset, request_ids, o, stream);
     } else {
         // draft rows are sampled from (exact sums); target rows enter only
@@ -366,16 +454,18 @@ int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int3
     return hip_status(e);
 }
 
-int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, int32_t K, int32_t V,
-                   int64_t vocab, const uno_sampling_t* sp, int32_t* node_token, int32_t* node_parent,
-                   int32_t* node_depth, double* node_score, int32_t* num_nodes, void* ws, size_t ws_bytes,
-                   hipStream_t stream)
+int uno_build_tree_ex(const void* draft, int32_t dtype, int32_t batch, int32_t B, int32_t K, int32_t V,
+                      int64_t vocab, const uno_sampling_t* sp, int32_t n_sp, int32_t* node_token,
+                      int32_t* node_parent, int32_t* node_depth, double* node_score, int32_t* num_nodes, void* ws,
+                      size_t ws_bytes, hipStream_t stream)
 {
+    const SpSet sps{ sp, n_sp };
+    const RowMap map{ 2, batch, B, B };
     Carve sizing{ nullptr };
     Mode m;
     SparseWs sw;
     DenseChunks dc;
-    int st = layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sp, sizing, &m, &sw, &dc);
+    int st = layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sps, sizing, &m, &sw, &dc);
     if (st) return st;
     if (batch == 0) return UNO_OK;
     if (draft == nullptr || node_token == nullptr || node_parent == nullptr || node_depth == nullptr ||
@@ -384,14 +474,14 @@ int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, i
     st = check_ws(ws, ws_bytes, sizing.used);
     if (st) return st;
     Carve cv{ static_cast<char*>(ws) };
-    layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sp, cv, &m, &sw, &dc);
+    layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sps, cv, &m, &sw, &dc);
 
     const int64_t rows = (int64_t)batch * B;
     const bool bf16 = dtype == UNO_BF16;
     RowSource src{ static_cast<const char*>(draft), rows, nullptr, nullptr, 1 };
     hipError_t e;
     if (m.sparse) {
-        e = launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, sw.sup, stream);
+        e = launch_sparse_filter(src, rows, vocab, bf16, sps, map, m, sw, sw.sup, stream);
     } else {
         // full-vocabulary filter: exact row normalisers (over the nucleus when
         // top-p is on), the K best ids, then their probabilities under the
@@ -404,7 +494,7 @@ int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, i
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, sw.nucleus_n, nullptr, stream);
         if (e == hipSuccess)
             e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, mk), sw.sup, sw.S, sw.part_key,
-                                   sw.part_id, sw.part_n, stream);
+                                   sw.part_id, sw.part_n, sw.part_cap, nullptr, stream);
         if (e == hipSuccess)
             e = launch_dense_support_scale(rows, sp->temperature, dc, sw.nucleus_n, sw.sup, stream);
     }
@@ -415,17 +505,19 @@ int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, i
     return hip_status(e);
 }
 
-int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B, int32_t V, int64_t vocab,
-                    const uno_sampling_t* sp, uint64_t seed, uint64_t offset, const uint32_t* request_ids,
-                    const int32_t* node_token, const int32_t* node_parent, const int32_t* num_nodes,
-                    int32_t* out_tokens, int32_t* out_path, int32_t* out_accept_len, uint32_t* out_flags,
-                    void* ws, size_t ws_bytes, hipStream_t stream)
+int uno_verify_tree_ex(const void* target, int32_t dtype, int32_t batch, int32_t B, int32_t V, int64_t vocab,
+                       const uno_sampling_t* sp, int32_t n_sp, uint64_t seed, uint64_t offset,
+                       const uint32_t* request_ids, const int32_t* node_token, const int32_t* node_parent,
+                       const int32_t* num_nodes, int32_t* out_tokens, int32_t* out_path, int32_t* out_accept_len,
+                       uint32_t* out_flags, void* ws, size_t ws_bytes, hipStream_t stream)
 {
+    const SpSet sps{ sp, n_sp };
+    const RowMap map{ 2, batch, B, V + 1 };
     Carve sizing{ nullptr };
     Mode m;
     SparseWs sw;
     DenseChunks dc;
-    int st = layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sp, sizing, &m, &sw, &dc);
+    int st = layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sps, sizing, &m, &sw, &dc);
     if (st) return st;
     if (batch == 0) return UNO_OK;
     if (target == nullptr || node_token == nullptr || node_parent == nullptr || num_nodes == nullptr ||
@@ -435,7 +527,7 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
     st = check_ws(ws, ws_bytes, sizing.used);
     if (st) return st;
     Carve cv{ static_cast<char*>(ws) };
-    layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sp, cv, &m, &sw, &dc);
+    layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sps, cv, &m, &sw, &dc);
 
     const int64_t rows = (int64_t)batch * (V + 1);
     const bool bf16 = dtype == UNO_BF16;
@@ -443,7 +535,7 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
     WalkOut o{ out_tokens, out_path, out_accept_len, out_flags };
     hipError_t e;
     if (m.sparse) {
-        e = launch_sparse_filter(src, rows, vocab, bf16, sp, m, sw, sw.sup, stream);
+        e = launch_sparse_filter(src, rows, vocab, bf16, sps, map, m, sw, sw.sup, stream);
         if (e == hipSuccess)
             e = launch_tree_walk(batch, B, V, sw.sup, seed, offset, request_ids, node_token, node_parent,
                                  num_nodes, o, stream);
@@ -458,6 +550,51 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
                                        request_ids, node_token, node_parent, num_nodes, o, stream);
     }
     return hip_status(e);
+}
+
+// ---- one parameter set for every row -------------------------------------------
+int uno_workspace_bytes(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K, int32_t V, int64_t vocab,
+                        int32_t dtype, const uno_sampling_t* sp, size_t* out_bytes)
+{
+    return uno_workspace_bytes_ex(op, batch_or_rows, B, K, V, vocab, dtype, sp, 1, out_bytes);
+}
+
+int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab, const uno_sampling_t* sp,
+               int32_t cap, int32_t* out_ids, double* out_probs, int32_t* out_count, double* out_stats,
+               void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return uno_filter_ex(logits, dtype, rows, vocab, sp, 1, cap, out_ids, out_probs, out_count, out_stats, ws,
+                         ws_bytes, stream);
+}
+
+int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int32_t batch, int32_t B,
+                      int64_t vocab, const uno_sampling_t* sp, uint64_t seed, uint64_t offset,
+                      const uint32_t* request_ids, int32_t* out_tokens, int32_t* out_accept_len,
+                      int32_t* out_proposals, uint32_t* out_flags, void* ws, size_t ws_bytes,
+                      hipStream_t stream)
+{
+    return uno_sample_linear_ex(draft, target, dtype, batch, B, vocab, sp, 1, seed, offset, request_ids, out_tokens,
+                                out_accept_len, out_proposals, out_flags, ws, ws_bytes, stream);
+}
+
+int uno_build_tree(const void* draft, int32_t dtype, int32_t batch, int32_t B, int32_t K, int32_t V,
+                   int64_t vocab, const uno_sampling_t* sp, int32_t* node_token, int32_t* node_parent,
+                   int32_t* node_depth, double* node_score, int32_t* num_nodes, void* ws, size_t ws_bytes,
+                   hipStream_t stream)
+{
+    return uno_build_tree_ex(draft, dtype, batch, B, K, V, vocab, sp, 1, node_token, node_parent, node_depth,
+                             node_score, num_nodes, ws, ws_bytes, stream);
+}
+
+int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B, int32_t V, int64_t vocab,
+                    const uno_sampling_t* sp, uint64_t seed, uint64_t offset, const uint32_t* request_ids,
+                    const int32_t* node_token, const int32_t* node_parent, const int32_t* num_nodes,
+                    int32_t* out_tokens, int32_t* out_path, int32_t* out_accept_len, uint32_t* out_flags,
+                    void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    return uno_verify_tree_ex(target, dtype, batch, B, V, vocab, sp, 1, seed, offset, request_ids, node_token,
+                              node_parent, num_nodes, out_tokens, out_path, out_accept_len, out_flags, ws, ws_bytes,
+                              stream);
 }
 
 int uno_tree_attention(const void* q, const void* k, const void* v, const void* o_prefix, const float* lse_prefix,

@@ -71,10 +71,13 @@ int topk_segments(int64_t rows, int64_t vocab, int k);
 size_t align_up(size_t x, size_t a);
 
 // ---- launchers (return hipGetLastError() after the launch) ----------------
+// Segment lists hold part_cap entries each; rowp (nullable): per-row
+// parameters replacing fp (k at most part_cap, the k the segments were chosen
+// for)
 hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                               const FilterParams& fp, const SparseOut& out, int S,
-                              uint32_t* part_key, int32_t* part_id, int32_t* part_n,
-                              hipStream_t stream);
+                              uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap,
+                              const FilterParams* rowp, hipStream_t stream);
 
 // Rows below exact_rows get exact (fp64 exp) chunk sums; the rest fast ones.
 hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,

@@ -222,3 +222,30 @@ def test_tree_attention_argument_checks(lib):
     odd = ctypes.c_void_p(0x50008)            # k and v must be 16-byte aligned
     assert lib.uno_tree_attention(P, odd, P, P, P, P, None, BF16, 2, 9, 32, 8, 128, ctypes.c_float(0.1), P, P,
                                   None) == INVALID
+
+
+def _sp_array(*sets):
+    arr = (uno.Sampling * len(sets))(*[uno.Sampling(*s) for s in sets])
+    return arr, len(sets)
+
+
+def test_per_request_parameter_checks(lib):
+    N = 151936
+    n = ctypes.c_size_t(0)
+    ws = lambda op, batch, sets: (lib.uno_workspace_bytes_ex(op, batch, 8, 16, 8, N, F32, sets[0], sets[1],
+                                                             ctypes.byref(n)), n.value)
+    mixed = _sp_array((0.0, 0, 1.0, 0), (1.0, 50, 0.95, 0), (0.7, 20, 1.0, 1), (1.3, 256, 0.9, 0))
+    st, nmix = ws(uno.OP_SAMPLE_LINEAR, 4, mixed)
+    assert st == OK
+    # supports sized for the largest k (256), plus one parameter set per row
+    assert nmix >= 4 * 17 * 256 * 12 + 4 * 17 * 40
+    assert ws(uno.OP_SAMPLE_LINEAR, 3, mixed)[0] == INVALID            # one set per request
+    dense = _sp_array((1.0, 50, 0.95, 0), (1.0, 0, 1.0, 0))
+    assert ws(uno.OP_SAMPLE_LINEAR, 2, dense)[0] == UNSUPPORTED        # top-k off: not per request
+    joint_t = _sp_array((1.0, 50, 0.9, 1), (0.5, 50, 0.9, 1))
+    assert ws(uno.OP_SAMPLE_LINEAR, 2, joint_t)[0] == UNSUPPORTED      # joint sets with two temperatures
+    bad = _sp_array((1.0, 50, 0.95, 0), (-1.0, 50, 0.95, 0))
+    assert ws(uno.OP_SAMPLE_LINEAR, 2, bad)[0] == INVALID
+    assert ws(uno.OP_BUILD_TREE, 4, mixed)[0] == OK
+    assert ws(uno.OP_VERIFY_TREE, 4, mixed)[0] == OK
+    assert ws(uno.OP_FILTER, 4, mixed)[0] == OK

@@ -1,0 +1,98 @@
+"""GPU parity of per-request sampling parameters (the *_ex entry points):
+greedy and stochastic requests with their own temperature, top-k, top-p and
+filter order in one call, each checked against the oracle run with its own set."""
+import numpy as np
+import pytest
+import torch
+
+import lossless_draft_verify_amd as uno
+import oracle
+from lossless_draft_verify_amd import synth
+from gpu_util import Tally, device, np_of, say
+
+pytestmark = pytest.mark.gpu
+
+# (temperature, top_k, top_p, order): greedy, the pages' 50 / 0.95, no top-p, a
+# large k, a tiny k, the joint order (all joint sets at temperature 1)
+SETS = [(0.0, 0, 1.0, 0), (1.0, 50, 0.95, 0), (0.7, 20, 1.0, 0), (1.3, 256, 0.9, 0), (1.0, 3, 0.5, 0),
+        (1.0, 50, 0.9, 1), (0.5, 8, 0.8, 0), (1.0, 100, 0.99, 1)]
+
+
+def _params(n):
+    s = [SETS[i % len(SETS)] for i in range(n)]
+    return [np.array([x[j] for x in s]) for j in range(4)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,N", [(64, 3001), (24, 151936)])
+def test_filter_per_row_parameters(dtype, rows, N):
+    # 3001 logits: one workgroup per row; 151936: rows split into segments whose
+    # lists (sized for the largest k) the merge reads with each row's own k
+    dev = device()
+    rng = np.random.default_rng(50)
+    z = torch.from_numpy((rng.standard_normal((rows, N)) * 2).astype(np.float32)).to(dev).to(dtype)
+    T, K, P, O = _params(rows)
+    g = uno.filter_rows(z, T, K, P, order=O)
+    torch.cuda.synchronize()
+    zh = z.float().cpu().numpy()
+    gn, gi, gp = np_of(g["count"]), np_of(g["ids"]), np_of(g["probs"])
+    for r in range(rows):
+        o = oracle.filter_rows(zh[r:r + 1], T[r], K[r], P[r], cap=gi.shape[1], dense=False, order=int(O[r]))
+        if o["margin"][0] < 1e-9:
+            continue
+        n = int(o["n"][0])
+        assert gn[r] == n, (r, gn[r], n)
+        assert np.array_equal(gi[r, :n], o["ids"][0, :n]), r
+        np.testing.assert_allclose(gp[r, :n], o["probs"][0, :n], rtol=1e-12, atol=0)
+
+
+def test_linear_per_request_parameters():
+    dev = device()
+    w = synth.WORKLOADS["linear_8_1_8"]
+    batch = 16
+    T, K, P, O = _params(batch)
+    t = Tally()
+    for c in range(2):
+        draft, target = synth.linear_inputs(w, cycle=c, device=dev, batch=batch)
+        g = uno.sample_linear(draft, target, T, K, P, w.seed, c, order=O)
+        torch.cuda.synchronize()
+        d, tg = synth.as_float32_numpy(draft), synth.as_float32_numpy(target)
+        gg = {k: np_of(g[k]) for k in ("tokens", "accept_len", "proposals")}
+        for b in range(batch):
+            o = oracle.linear(d[b:b + 1], tg[b:b + 1], T[b], K[b], P[b], w.seed, c,
+                              request_ids=np.array([b], np.uint32), order=int(O[b]))
+            t.compare({k: v[b:b + 1] for k, v in gg.items()}, o, ("tokens", "accept_len", "proposals"),
+                      f"per-request linear cycle {c} request {b}")
+    t.check_rate()
+    say(f"per-request linear: {t.total} request-cycles, excused {t.excused}")
+
+
+def test_tree_per_request_parameters():
+    dev = device()
+    w = synth.WORKLOADS["tree_8_16_8"]
+    batch = 8
+    T, K, P, O = _params(batch)
+    draft, R = synth.tree_inputs(w, cycle=0, device=dev, batch=batch)
+    g = uno.build_tree(draft, w.K, w.V, T, K, P, order=O)
+    torch.cuda.synchronize()
+    d = synth.as_float32_numpy(draft)
+    trees = [oracle.build_tree(d[b:b + 1], w.K, w.V, T[b], K[b], P[b], order=int(O[b])) for b in range(batch)]
+    for b, o in enumerate(trees):
+        for key in ("node_token", "node_parent", "node_depth", "num_nodes"):
+            same = np.array_equal(np_of(g[key])[b], o[key][0])
+            assert same or o["min_gap"][0] < 1e-12, (b, key)
+    node_depth = torch.from_numpy(np.stack([o["node_depth"][0] for o in trees]))
+    num_nodes = torch.from_numpy(np.array([o["num_nodes"][0] for o in trees], np.int32))
+    tgt = synth.tree_target_rows(R, node_depth, num_nodes, w.V)
+    tk = torch.from_numpy(np.stack([o["node_token"][0] for o in trees])).to(dev)
+    pa = torch.from_numpy(np.stack([o["node_parent"][0] for o in trees])).to(dev)
+    gv = uno.verify_tree(tgt, w.B, tk, pa, num_nodes.to(dev), T, K, P, w.seed, 3, order=O)
+    torch.cuda.synchronize()
+    th = synth.as_float32_numpy(tgt)
+    t = Tally()
+    for b in range(batch):
+        o = oracle.verify_tree(th[b:b + 1], w.B, np_of(tk)[b:b + 1], np_of(pa)[b:b + 1], np_of(num_nodes)[b:b + 1],
+                               T[b], K[b], P[b], w.seed, 3, request_ids=np.array([b], np.uint32), order=int(O[b]))
+        t.compare({k: np_of(gv[k])[b:b + 1] for k in ("tokens", "path", "accept_len")}, o,
+                  ("tokens", "path", "accept_len"), f"per-request walk {b}")
+    t.check_rate()
