@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import math
+import numpy as np
 import json
 import os
 import sys
@@ -88,7 +89,7 @@ def traffic_probe(args, w, lib, pool, dt, sp, stream, dev):
     dst = torch.empty_like(src)
     for i in range(args.traffic_probe):
         st = lib.uno_filter(ctypes.c_void_p(pool[i % len(pool)]["all"].data_ptr()), dt, nrows, w.vocab,
-                            ctypes.byref(sp), w.top_k, ctypes.c_void_p(ids.data_ptr()),
+                            sp, w.top_k, ctypes.c_void_p(ids.data_ptr()),
                             ctypes.c_void_p(probs.data_ptr()), ctypes.c_void_p(cnt.data_ptr()), None, fws_p,
                             fws_n, ctypes.c_void_p(stream.cuda_stream))
         assert st == 0, st
@@ -215,13 +216,17 @@ def main():
     import ctypes
     lib = uno.load_library()
     dt = 0 if w.dtype == "f32" else 1
-    sp = uno.Sampling(w.temperature, w.top_k, w.top_p, w.order)
-    spr = ctypes.byref(sp)
+    # one parameter set, or one per request (the mixed workload)
+    sets = [w.request_params(b) for b in range(w.batch)] if w.mixed else [w.request_params(0)]
+    sp = (uno.Sampling * len(sets))(*[uno.Sampling(*x) for x in sets])
+    spr, nsp = sp, len(sets)
+    cols = [np.array([x[j] for x in sets]) for j in range(4)] if w.mixed else \
+        [w.temperature, w.top_k, w.top_p, w.order]
     sptr = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
     def wsbuf(op, K, V):
-        n = uno.workspace_bytes(op, w.batch, w.B, K, V, w.vocab, dt, w.temperature, w.top_k, w.top_p, w.order)
+        n = uno.workspace_bytes(op, w.batch, w.B, K, V, w.vocab, dt, *cols)
         if n == 0:
             return None, 0
         t = torch.empty(n + 256, dtype=torch.uint8, device=dev)
@@ -238,7 +243,7 @@ def main():
 
         def step(i):
             d, t = ptrs[i % len(ptrs)]
-            st = lib.uno_sample_linear(d, t, dt, w.batch, w.B, w.vocab, spr, w.seed, i, None, P(tokens), P(acc),
+            st = lib.uno_sample_linear_ex(d, t, dt, w.batch, w.B, w.vocab, spr, nsp, w.seed, i, None, P(tokens), P(acc),
                                        P(prop), P(flags), ws[1] if ws else None, wsn, sptr)
             if st != 0:
                 raise uno.UnoError(st, "uno_sample_linear")
@@ -258,11 +263,11 @@ def main():
 
         def step(i):
             d, t = ptrs[i % len(ptrs)]
-            st = lib.uno_build_tree(d, dt, w.batch, w.B, w.K, w.V, w.vocab, spr, P(ntok), P(npar), P(ndep), None,
+            st = lib.uno_build_tree_ex(d, dt, w.batch, w.B, w.K, w.V, w.vocab, spr, nsp, P(ntok), P(npar), P(ndep), None,
                                     P(nnum), wsb[1] if wsb else None, wsbn, sptr)
             if st != 0:
                 raise uno.UnoError(st, "uno_build_tree")
-            st = lib.uno_verify_tree(t, dt, w.batch, w.B, w.V, w.vocab, spr, w.seed, i, None, P(ntok), P(npar),
+            st = lib.uno_verify_tree_ex(t, dt, w.batch, w.B, w.V, w.vocab, spr, nsp, w.seed, i, None, P(ntok), P(npar),
                                      P(nnum), P(tokens), P(path), P(acc), P(flags), wsv[1] if wsv else None,
                                      wsvn, sptr)
             if st != 0:
@@ -300,7 +305,7 @@ def main():
 
     # ---- dominant kernel: the same filter launch, timed alone with HIP events ------
     roofline = None
-    if w.mode == "linear" and w.top_k > 0 and w.order == uno.ORDER_TOPK_FIRST:
+    if w.mode == "linear" and w.top_k > 0 and w.order == uno.ORDER_TOPK_FIRST and not w.mixed:
         ids = torch.empty((pool[0]["all"].shape[0], w.top_k), dtype=torch.int32, device=dev)
         probs = torch.empty((pool[0]["all"].shape[0], w.top_k), dtype=torch.float64, device=dev)
         cnt = torch.empty(pool[0]["all"].shape[0], dtype=torch.int32, device=dev)
@@ -313,7 +318,7 @@ def main():
 
         def filt(i):
             a = pool[i % len(pool)]["all"]
-            st = lib.uno_filter(ctypes.c_void_p(a.data_ptr()), dt, nrows, w.vocab, ctypes.byref(sp), w.top_k,
+            st = lib.uno_filter(ctypes.c_void_p(a.data_ptr()), dt, nrows, w.vocab, sp, w.top_k,
                                 ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(probs.data_ptr()),
                                 ctypes.c_void_p(cnt.data_ptr()), None, fws_p, fws_n,
                                 ctypes.c_void_p(stream.cuda_stream))
@@ -339,7 +344,6 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample of the same workload ----------
     cpu = None
     if not args.no_cpu_baseline:
-        import numpy as np
         import oracle
         p = pool[0]
         n_req = 0
@@ -352,8 +356,14 @@ def main():
             while time.perf_counter() - t0 < args.cpu_seconds and n_req < w.batch * 8:
                 lo = n_req % w.batch
                 hi = min(lo + 16, w.batch)
-                oracle.linear(dnp[lo:hi], tnp[lo:hi], w.temperature, w.top_k, w.top_p, w.seed, 0,
-                              request_ids=np.arange(lo, hi, dtype=np.uint32), order=w.order)
+                if w.mixed:
+                    for b in range(lo, hi):
+                        T, k, p_, o = w.request_params(b)
+                        oracle.linear(dnp[b:b + 1], tnp[b:b + 1], T, k, p_, w.seed, 0,
+                                      request_ids=np.array([b], dtype=np.uint32), order=o)
+                else:
+                    oracle.linear(dnp[lo:hi], tnp[lo:hi], w.temperature, w.top_k, w.top_p, w.seed, 0,
+                                  request_ids=np.arange(lo, hi, dtype=np.uint32), order=w.order)
                 n_req += hi - lo
                 rows += (hi - lo) * (2 * w.B + 1)
         else:
@@ -390,7 +400,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "B": w.B, "K": w.K, "V": w.V or w.B,
                    "vocab": w.vocab, "logits": w.dtype, "temperature": w.temperature, "top_k": w.top_k,
                    "top_p": w.top_p, "rows_per_step": w.rows_per_cycle, "bytes_per_step": w.bytes_per_cycle,
-                   "pool_cycles": args.pool},
+                   "pool_cycles": args.pool,
+                   **({"per_request": [list(x) for x in synth.MIXED_SETS]} if w.mixed else {})},
         "hbm_gbs_algorithmic": round(gbs, 1),
         "tpf": round(tpf, 4),
         "roofline": roofline,

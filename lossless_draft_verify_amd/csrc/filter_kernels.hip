@@ -589,19 +589,26 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
 
     if (seg == S - 1 && w == kWaves - 1 && g.tail_beg < N) scalar_part(g.tail_beg, N - g.tail_beg);
 
-    // Bound: with quota q = ceil(k/4), the q-th largest of this wave's lane
-    // maxima (truncated to its 16-bit key bin) has q entries at or above it, so
-    // the smallest of the four waves' bounds has at least k: the block's k-th
-    // entry lies at or above it.  Without q entries in every wave there is no
-    // bound (B = 0).
+    // Bound: with quota q = ceil(k/4), each wave finds a key b with at least q
+    // of its entries at or above it, so the smallest of the four waves' bounds
+    // has at least k: the block's k-th entry lies at or above it.  Without q
+    // entries in every wave there is no bound (B = 0).  For small q, b is the
+    // q-th largest of the lane maxima (truncated to its 16-bit key bin); a
+    // larger q would push that down to the smallest lane maximum, and the
+    // block would rank several times k entries, so there b is the wave's own
+    // q-th largest key (truncated to 24 bits).
     const int quota = (k + kWaves - 1) / kWaves;
-    uint32_t lmax = 0;
-    for (int j = lane; j < cnt; j += kWave) {
-        const uint32_t kj = float_key(__uint_as_float(buf[j].x));
-        lmax = kj > lmax ? kj : lmax;
-    }
     uint32_t b = 0;
-    if (cnt >= quota) {
+    if (cnt >= quota && quota > kWave / 2) {
+        RegList<kCapE> L;
+        reg_load(L, buf, cnt, lane);
+        b = reg_kth_key(L, quota, 8);
+    } else if (cnt >= quota) {
+        uint32_t lmax = 0;
+        for (int j = lane; j < cnt; j += kWave) {
+            const uint32_t kj = float_key(__uint_as_float(buf[j].x));
+            lmax = kj > lmax ? kj : lmax;
+        }
         // largest 16-bit prefix t with at least quota lane maxima >= t
         for (int bit = 31; bit >= 16; --bit) {
             const uint32_t cand = b | (1u << bit);

@@ -40,7 +40,14 @@ class Workload:
     K: int = 1
     V: int = 0
     order: int = 0       # filter order: 0 top-k first, 1 joint
+    mixed: bool = False  # request b takes MIXED_SETS[b % len] instead of the scalars above
     note: str = field(default="", compare=False)
+
+    def request_params(self, b: int):
+        """(temperature, top_k, top_p, order) of request b."""
+        if self.mixed:
+            return MIXED_SETS[b % len(MIXED_SETS)]
+        return (self.temperature, self.top_k, self.top_p, self.order)
 
     @property
     def rows_per_cycle(self) -> int:
@@ -66,6 +73,11 @@ def _const(v, n):
     return tuple(float(v) for _ in range(n))
 
 
+# Per-request parameter sets of the mixed workload: greedy, the pages' top-k 50 /
+# top-p 0.95, no top-p, a large k, a tiny k and the joint order.
+MIXED_SETS = [(0.0, 0, 1.0, 0), (1.0, 50, 0.95, 0), (0.7, 20, 1.0, 0), (1.3, 256, 0.9, 0), (1.0, 3, 0.5, 0),
+              (1.0, 50, 0.9, 1), (0.5, 8, 0.8, 0), (1.0, 100, 0.99, 1)]
+
 WORKLOADS = {
     "tiny": Workload("tiny", "linear", batch=2, B=4, vocab=1000, dtype="f32", slope=1.0,
                      sigma=_const(0.5, 4), temperature=1.0, top_k=0, top_p=1.0, seed=42,
@@ -81,6 +93,12 @@ WORKLOADS = {
                                    sigma=tuple(0.3 + 0.1 * j for j in range(8)), temperature=1.0,
                                    top_k=50, top_p=0.95, seed=42, cycles=1000, order=1,
                                    note="Linear 8/1/8, 64 requests, joint top-k 50 / top-p 0.95"),
+    # the headline shape with one parameter set per request (MIXED_SETS)
+    "linear_8_1_8_mixed": Workload("linear_8_1_8_mixed", "linear", batch=64, B=8, vocab=VOCAB_QWEN3,
+                                   dtype="f32", slope=1.2,
+                                   sigma=tuple(0.3 + 0.1 * j for j in range(8)), temperature=1.0,
+                                   top_k=50, top_p=0.95, seed=42, cycles=1000, mixed=True,
+                                   note="Linear 8/1/8, 64 requests, per-request parameters"),
     # the headline shape with top-k off: a full-vocabulary nucleus at top-p 0.95
     "linear_8_1_8_nucleus": Workload("linear_8_1_8_nucleus", "linear", batch=64, B=8, vocab=VOCAB_QWEN3,
                                      dtype="f32", slope=1.2,

@@ -51,7 +51,7 @@ def _check_sparse(z32, dtype, T, k, p, label, order=uno.ORDER_TOPK_FIRST):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("T,k,p", [(1.0, 50, 0.95), (0.7, 50, 1.0), (1.0, 1, 1.0), (0.0, 0, 1.0),
-                                   (1.3, 256, 0.9), (1.0, 7, 0.5)])
+                                   (1.3, 256, 0.9), (1.0, 7, 0.5), (1.0, 128, 0.97), (1.0, 129, 0.97)])
 def test_sparse_many_rows_ragged_vocab(dtype, T, k, p):
     # 1100 rows of a 1003-logit vocabulary: one workgroup per row, rows that start
     # off 16-byte boundaries (scalar head and tail), several tiles per row
