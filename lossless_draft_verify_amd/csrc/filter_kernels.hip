@@ -767,7 +767,8 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
 // ---- dense chunk statistics --------------------------------------------------
 template <bool BF16, bool COUNT>
 __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
-    RowSource src, int64_t rows, int64_t N, double log2e_over_T, int64_t exact_rows, DenseChunks dc)
+    RowSource src, int64_t rows, int64_t N, double log2e_over_T, int64_t exact_rows, DenseChunks dc,
+    const FilterParams* rowp)
 {
     using V = Vec<BF16>;
     constexpr int EPV = V::EPV, ESZ = V::ESZ;
@@ -777,6 +778,9 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r = blockIdx.x;
+    // with per-row parameters only the rows that read full-softmax statistics
+    // (the joint order) need them
+    if (rowp != nullptr && rowp[r].full_cmax == nullptr) return;
     const int nc = dc.nchunks;
     // a row's chunks are dealt over gridDim.y workgroups (more than one when
     // there are few rows), round robin over all their waves
@@ -962,7 +966,8 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
 }
 
 hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
-                               float temperature, const DenseChunks& dc, int64_t exact_rows, hipStream_t stream)
+                               float temperature, const DenseChunks& dc, int64_t exact_rows, hipStream_t stream,
+                               const FilterParams* rowp)
 {
     if (rows == 0) return hipSuccess;
     const double c = 1.4426950408889634074 / (double)temperature;
@@ -975,13 +980,13 @@ hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab
     dim3 grid((unsigned)rows, (unsigned)g);
     const bool counts = dc.ccount != nullptr;
     if (bf16 && counts)
-        dense_chunk_kernel<true, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
+        dense_chunk_kernel<true, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp);
     else if (bf16)
-        dense_chunk_kernel<true, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
+        dense_chunk_kernel<true, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp);
     else if (counts)
-        dense_chunk_kernel<false, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
+        dense_chunk_kernel<false, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp);
     else
-        dense_chunk_kernel<false, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc);
+        dense_chunk_kernel<false, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp);
     return hipGetLastError();
 }
 

@@ -229,19 +229,13 @@ FilterParams filter_params(const uno_sampling_t* sp, const Mode& m)
 
 // The sparse filter of `rows` rows into `out`; the joint order first takes
 // exact chunk statistics of the same rows for the full-softmax normaliser.
-// With per-request parameters each row's set is copied to the workspace.
+// With per-request parameters each row's set is copied to the workspace, and
+// only the joint rows' statistics are taken.
 hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                                 const SpSet& sps, const RowMap& map, const Mode& m, const SparseWs& sw,
                                 const SparseOut& out, hipStream_t stream)
 {
     FilterParams fp = filter_params(sps.sp, m);
-    if (m.joint) {
-        const hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, m.joint_T, sw.full, rows, stream);
-        if (e != hipSuccess) return e;
-        fp.full_cmax = sw.full.cmax;
-        fp.full_csum = sw.full.csum;
-        fp.full_nc = sw.full.nchunks;
-    }
     if (m.per_request) {
         std::vector<FilterParams> host((size_t)rows);
         for (int64_t r = 0; r < rows; ++r) {
@@ -259,6 +253,15 @@ hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t voca
         const hipError_t e = hipMemcpyAsync(sw.rowp, host.data(), host.size() * sizeof(FilterParams),
                                             hipMemcpyHostToDevice, stream);
         if (e != hipSuccess) return e;
+    }
+    if (m.joint) {
+        // with per-row parameters only the joint rows' statistics are taken
+        const hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, m.joint_T, sw.full, rows, stream,
+                                                 m.per_request ? sw.rowp : nullptr);
+        if (e != hipSuccess) return e;
+        fp.full_cmax = sw.full.cmax;
+        fp.full_csum = sw.full.csum;
+        fp.full_nc = sw.full.nchunks;
     }
     return launch_topk_filter(src, rows, vocab, bf16, fp, out, sw.S, sw.part_key, sw.part_id, sw.part_n,
                               sw.part_cap, sw.rowp, stream);

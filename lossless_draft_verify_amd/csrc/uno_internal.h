@@ -80,8 +80,11 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
                               const FilterParams* rowp, hipStream_t stream);
 
 // Rows below exact_rows get exact (fp64 exp) chunk sums; the rest fast ones.
+// rowp (nullable, device): per-row parameters; rows whose entry has no
+// full_cmax are skipped (nothing read or written).
 hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
-                               float temperature, const DenseChunks& dc, int64_t exact_rows, hipStream_t stream);
+                               float temperature, const DenseChunks& dc, int64_t exact_rows, hipStream_t stream,
+                               const FilterParams* rowp = nullptr);
 
 hipError_t launch_dense_row_stats(int64_t rows, float temperature, const DenseChunks& dc,
                                   int32_t* out_count, double* out_stats, hipStream_t stream);
