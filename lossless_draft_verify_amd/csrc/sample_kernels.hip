@@ -1079,9 +1079,14 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
 // follows from the mass left; which ties (smaller ids first) from an ordered
 // count over ids.  The row's keep threshold is the order key of its last kept
 // logit; the chunk sums are then rewritten over the support.
+// When the first level's chosen bin holds few logits, one more pass instead
+// collects them (as order keys) together with the chunk sums above the bin;
+// the collected logits are ranked in LDS and the cut is the first whose
+// inclusive mass, counted from the top in the filter order, reaches the target.
 constexpr int kNucThreads = 256;
 constexpr int kNucWaves = kNucThreads / kWave;
 constexpr int kNucBins = 2048;
+constexpr int kNucCand = kNucBins / 2 / kNucWaves;   // collected logits per wave (in s_cnt)
 
 template <bool BF16>
 __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int64_t N, double log2e_over_T,
@@ -1161,7 +1166,7 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
     uint32_t lo = 0, hi = 0;                 // later levels: keys in [lo, hi)
     double A = 0.0;                          // mass above the current range
     int64_t cab = 0;                         // logits above the current range
-    do {
+    auto level = [&]() __attribute__((always_inline)) {
         const bool first = b0 < 0;
         const uint32_t width = hi - lo;
         const int nb = first ? kNucBins : (width < (uint32_t)kNucBins ? (int)width : kNucBins);
@@ -1237,7 +1242,122 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_kernel(RowSource src, int
         }
         A = s_row[1];
         cab = s_cab;
-    } while (hi - lo > 1u);
+    };
+    level();
+    // ---- one-pass finish when the chosen value bin holds few logits ----------
+    const uint32_t n_b0 = s_cnt[b0];
+    __syncthreads();                          // s_cnt is reused below
+    if (n_b0 <= (uint32_t)(kNucCand * kNucWaves) && nc <= kNucWaves * kWave) {
+        // Candidates: this wave's logits of bin b0 as order keys (hi, lo words
+        // in s_cnt), appended chunk by chunk, so each chunk's run is
+        // contiguous; lane q holds the run bounds and the sum above the bin
+        // of the wave's q-th chunk (chunks w, w + kNucWaves, ...).
+        uint32_t* cl = s_cnt + 2 * kNucCand * w;
+        int ncl = 0;
+        int run_b = 0, run_e = 0;
+        double above = 0.0;
+        each_chunk([&](int c, const float (&x)[kPerLane]) __attribute__((always_inline)) {
+            const int q = (c - w) / kNucWaves;
+            const int start = ncl;
+            double sum = 0.0;
+            const float mcf = cm[c];
+            if (mcf > -INFINITY) {
+                const double mc = (double)mcf;
+#pragma unroll
+                for (int i = 0; i < kPerLane; ++i) {
+                    const float z = x[i];
+                    const int vb = (finite_f32(z) && z >= vlo_f) ? vbin(z) : -1;
+                    if (vb > b0) sum += ex((double)z - mc);
+                    const bool cand = vb == b0;
+                    const uint64_t mk = __ballot(cand);
+                    if (mk) {
+                        const int pos = ncl + __popcll(mk & lanes_below(lane));
+                        if (cand && pos < kNucCand) {
+                            const uint64_t ok = order_key(float_key(z), (int32_t)chunk_elem_id<EPV>(c, i, lane));
+                            cl[2 * pos] = (uint32_t)(ok >> 32);
+                            cl[2 * pos + 1] = (uint32_t)ok;
+                        }
+                        ncl += __popcll(mk);
+                    }
+                }
+            }
+            sum = wave_sum_f64(sum);
+            if (lane == q) { run_b = start; run_e = ncl; above = sum; }
+        });
+        if (lane == 0) s_wc[w] = ncl;
+        __syncthreads();
+        int64_t ntot = 0;
+        bool fits = true;
+#pragma unroll
+        for (int o = 0; o < kNucWaves; ++o) {
+            ntot += s_wc[o];
+            fits = fits && s_wc[o] <= kNucCand;
+        }
+        if (fits && ntot == (int64_t)n_b0 && ntot > 0) {
+            // rank every candidate over the four lists; sorted masses go to
+            // s_mass[0, half), sorted keys (bit patterns) to s_mass[half, ...)
+            constexpr int half = kNucBins / 2;
+            for (int g = (int)threadIdx.x; g < (int)ntot; g += kNucThreads) {
+                int o = 0, i = g;
+                while (i >= s_wc[o]) { i -= (int)s_wc[o]; ++o; }
+                const uint32_t* lo_list = s_cnt + 2 * kNucCand * o;
+                const uint64_t pk = ((uint64_t)lo_list[2 * i] << 32) | lo_list[2 * i + 1];
+                int rank = 0;
+                for (int o2 = 0; o2 < kNucWaves; ++o2) {
+                    const uint32_t* l2 = s_cnt + 2 * kNucCand * o2;
+                    const int n2 = (int)s_wc[o2];
+                    for (int j = 0; j < n2; ++j) rank += ((((uint64_t)l2[2 * j] << 32) | l2[2 * j + 1]) > pk) ? 1 : 0;
+                }
+                s_mass[rank] = ex((double)key_float((uint32_t)(pk >> 32)) - (double)m);
+                s_mass[half + rank] = __longlong_as_double((long long)pk);
+            }
+            __syncthreads();
+            if (w == 0) {
+                // first sorted candidate whose inclusive mass from the top
+                // reaches the target (all of them when rounding leaves the
+                // target unreached)
+                double run = A;
+                int jcut = -1;
+                for (int top = 0; top < (int)ntot && jcut < 0; top += kWave) {
+                    const int j = top + lane;
+                    const double e = j < (int)ntot ? s_mass[j] : 0.0;
+                    const double incl = wave_incl_scan_f64(e, lane);
+                    const uint64_t hit = __ballot(j < (int)ntot && run + incl >= target);
+                    if (hit) jcut = top + wave_first_lane(hit);
+                    run += __shfl(incl, kWave - 1, kWave);
+                }
+                if (jcut < 0) jcut = (int)ntot - 1;
+                if (lane == 0) s_bin = jcut;
+            }
+            __syncthreads();
+            const int jcut = s_bin;
+            const uint64_t thr = (uint64_t)__double_as_longlong(s_mass[half + jcut]);
+            // chunk sums over the support: the sum above the bin plus the
+            // run's kept candidates
+            for (int c = w; c < nc; c += kNucWaves) {
+                const int q = (c - w) / kNucWaves;
+                const int b = __shfl(run_b, q, kWave), e = __shfl(run_e, q, kWave);
+                const double ab = __shfl(above, q, kWave);
+                const float mcf = cm[c];
+                double add = 0.0;
+                if (mcf > -INFINITY)
+                    for (int i = b + lane; i < e; i += kWave) {
+                        const uint64_t pk = ((uint64_t)cl[2 * i] << 32) | cl[2 * i + 1];
+                        if (pk >= thr) add += ex((double)key_float((uint32_t)(pk >> 32)) - (double)mcf);
+                    }
+                add = wave_sum_f64(add);
+                if (lane == 0) cs[c] = ab + add;
+            }
+            if (threadIdx.x == 0) {
+                dc.keep[r] = thr;
+                if (out_count) out_count[r] = (int32_t)(cab + jcut + 1);
+                if (out_stats) { out_stats[2 * r] = (double)m; out_stats[2 * r + 1] = S; }
+            }
+            return;
+        }
+        __syncthreads();                      // the later levels reset s_mass and s_cnt
+    }
+    while (hi - lo > 1u) level();
     // ties at the cut: keep the j-th (by id) while the mass before it is below
     // the target
     const uint32_t tau = lo;
