@@ -96,3 +96,25 @@ def test_tree_per_request_parameters():
         t.compare({k: np_of(gv[k])[b:b + 1] for k in ("tokens", "path", "accept_len")}, o,
                   ("tokens", "path", "accept_len"), f"per-request walk {b}")
     t.check_rate()
+
+
+def test_linear_8_1_8_mixed_full_size():
+    # the bench's mixed workload: the headline shape (64 requests, 151936 fp32
+    # logits) with one parameter set per request, every request checked
+    dev = device()
+    w = synth.WORKLOADS["linear_8_1_8_mixed"]
+    sets = [w.request_params(b) for b in range(w.batch)]
+    T, K, P, O = (np.array([s[j] for s in sets]) for j in range(4))
+    draft, target = synth.linear_inputs(w, cycle=0, device=dev)
+    g = uno.sample_linear(draft, target, T, K, P, w.seed, 0, order=O)
+    torch.cuda.synchronize()
+    d, tg = synth.as_float32_numpy(draft), synth.as_float32_numpy(target)
+    gg = {k: np_of(g[k]) for k in ("tokens", "accept_len", "proposals")}
+    t = Tally()
+    for b in range(w.batch):
+        o = oracle.linear(d[b:b + 1], tg[b:b + 1], T[b], K[b], P[b], w.seed, 0,
+                          request_ids=np.array([b], np.uint32), order=int(O[b]))
+        t.compare({k: v[b:b + 1] for k, v in gg.items()}, o, ("tokens", "accept_len", "proposals"),
+                  f"mixed linear_8_1_8 request {b}")
+    t.check_rate()
+    say(f"linear_8_1_8_mixed: {t.total} requests, excused {t.excused}, mean accept_len {gg['accept_len'].mean():.3f}")
