@@ -922,22 +922,23 @@ __global__ __launch_bounds__(kDenseThreads) void dense_exact_row_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int b = blockIdx.x;
     const int nc = dc.nchunks;
-    const int c = blockIdx.y * kDenseWaves + w;
-    if (c >= nc) return;
     const int js = jstar_in[b];
     const int64_t pr = linear_row(batch, B, b, B + (js < B ? js : B));
     const DenseExp ex{ log2e_over_T, s_exp2 };
-    float x[kPerLane];
-    load_chunk<BF16>(row_pointer(src, pr, N * Vec<BF16>::ESZ), N, c, x, lane);
-    float mx;
-    double sum;
-    uint32_t cntf;
-    chunk_stats_exact<true>(x, ex, &mx, &sum, &cntf);
-    if (lane == 0) {
-        const int64_t slot = pr * nc + c;
-        dc.cmax[slot] = mx;
-        dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
-        if (dc.ccount) dc.ccount[slot] = (int32_t)cntf;
+    // the row's chunks dealt over gridDim.y workgroups, round robin over their waves
+    for (int c = blockIdx.y * kDenseWaves + w; c < nc; c += gridDim.y * kDenseWaves) {
+        float x[kPerLane];
+        load_chunk<BF16>(row_pointer(src, pr, N * Vec<BF16>::ESZ), N, c, x, lane);
+        float mx;
+        double sum;
+        uint32_t cntf;
+        chunk_stats_exact<true>(x, ex, &mx, &sum, &cntf);
+        if (lane == 0) {
+            const int64_t slot = pr * nc + c;
+            dc.cmax[slot] = mx;
+            dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
+            if (dc.ccount) dc.ccount[slot] = (int32_t)cntf;
+        }
     }
 }
 
@@ -954,36 +955,39 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int b = blockIdx.x;
-    const int c = blockIdx.y * kDenseWaves + w;
+    const int c0 = blockIdx.y * kDenseWaves + w;
     const int js = jstar_in[b];
-    if (js >= B || c >= nc) return;
+    if (js >= B || c0 >= nc) return;
     const DenseExp ex{ log2e_over_T, s_exp2 };
     const int64_t qr = linear_row(batch, B, b, js), pr = linear_row(batch, B, b, B + js);
     float mpf;
     double Sp;
     dense_row_stat(dc.cmax + pr * nc, dc.csum + pr * nc, nc, ex, lane, &mpf, &Sp);   // exact chunks
     const double Sq = row_S[qr];
-    double total = 0.0;
-    if (Sp > 0.0) {
-        const int64_t row_bytes = N * Vec<BF16>::ESZ;
-        const bool q_ok = Sq > 0.0;
-        float xp[kPerLane], xq[kPerLane];
-        load_chunk<BF16>(row_pointer(src, pr, row_bytes), N, c, xp, lane);
-        if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
-        const double mp = (double)mpf, mq = (double)row_m[qr];
-        const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
-        const uint64_t tp = row_keep(dc, pr), tq = row_keep(dc, qr);
-        constexpr int EPV = Vec<BF16>::EPV;
-        auto wf = [&](int i) {
-            const int64_t id = chunk_elem_id<EPV>(c, i, lane);
-            const double pv = dense_keeps(tp, xp[i], id) ? ex((double)xp[i] - mp) * iSp : 0.0;
-            const double qv = (q_ok && dense_keeps(tq, xq[i], id)) ? ex((double)xq[i] - mq) * iSq : 0.0;
-            const double dl = pv - qv;
-            return dl > 0.0 ? dl : 0.0;
-        };
-        total = chunk_total<EPV>(wf, lane);
+    // the request's chunks dealt over gridDim.y workgroups, round robin over their waves
+    for (int c = c0; c < nc; c += gridDim.y * kDenseWaves) {
+        double total = 0.0;
+        if (Sp > 0.0) {
+            const int64_t row_bytes = N * Vec<BF16>::ESZ;
+            const bool q_ok = Sq > 0.0;
+            float xp[kPerLane], xq[kPerLane];
+            load_chunk<BF16>(row_pointer(src, pr, row_bytes), N, c, xp, lane);
+            if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
+            const double mp = (double)mpf, mq = (double)row_m[qr];
+            const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
+            const uint64_t tp = row_keep(dc, pr), tq = row_keep(dc, qr);
+            constexpr int EPV = Vec<BF16>::EPV;
+            auto wf = [&](int i) {
+                const int64_t id = chunk_elem_id<EPV>(c, i, lane);
+                const double pv = dense_keeps(tp, xp[i], id) ? ex((double)xp[i] - mp) * iSp : 0.0;
+                const double qv = (q_ok && dense_keeps(tq, xq[i], id)) ? ex((double)xq[i] - mq) * iSq : 0.0;
+                const double dl = pv - qv;
+                return dl > 0.0 ? dl : 0.0;
+            };
+            total = chunk_total<EPV>(wf, lane);
+        }
+        if (lane == 0) resid[(int64_t)b * nc + c] = total;
     }
-    if (lane == 0) resid[(int64_t)b * nc + c] = total;
 }
 
 // Residual (or bonus) sample and the cycle's outputs.
@@ -1548,7 +1552,12 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
                                hipStream_t stream)
 {
     const double c = 1.4426950408889634074 / (double)temperature;
-    const dim3 rgrid((unsigned)batch, (unsigned)((dc.nchunks + kDenseWaves - 1) / kDenseWaves));
+    // about 2048 workgroups: with many requests each wave takes several chunks,
+    // so fewer workgroups load the exponential table
+    const int per_req = (dc.nchunks + kDenseWaves - 1) / kDenseWaves;
+    const int want = (2048 + batch - 1) / batch;
+    const int gy = per_req < want ? per_req : want;
+    const dim3 rgrid((unsigned)batch, (unsigned)gy);
     if (bf16) {
         dense_propose_kernel<true><<<dim3((unsigned)batch), kDenseThreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
