@@ -612,6 +612,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
 
 // ---- dense linear ------------------------------------------------------------------
 constexpr int kDenseThreads = 256;
+constexpr int kProposeMaxThreads = 1024;   // dense_propose_kernel: up to one wave per proposal
 constexpr int kDenseWaves = kDenseThreads / kWave;
 constexpr int kPerLane = kDenseChunk / kWave;   // 32 logits per lane per chunk
 
@@ -835,7 +836,7 @@ __device__ __forceinline__ float load_one(const char* row, int64_t i)
 
 // Row stats of every row, proposals, acceptance and the first rejection.
 template <bool BF16>
-__global__ __launch_bounds__(kDenseThreads) void dense_propose_kernel(
+__global__ __launch_bounds__(kProposeMaxThreads) void dense_propose_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
     uint64_t seed, uint64_t offset, const uint32_t* req_ids, float* row_m, double* row_S,
     int32_t* jstar_out, int32_t* y_out, uint32_t* flag_out, LinearOut o)
@@ -854,7 +855,8 @@ __global__ __launch_bounds__(kDenseThreads) void dense_propose_kernel(
     const int64_t row_bytes = N * Vec<BF16>::ESZ;
     if (threadIdx.x == 0) s_flags = 0;
 
-    for (int i = w; i < 2 * B + 1; i += kDenseWaves) {
+    const int nw = (int)(blockDim.x / kWave);   // one wave per proposal, up to 16
+    for (int i = w; i < 2 * B + 1; i += nw) {
         const int64_t r = linear_row(batch, B, b, i);
         float m;
         double S;
@@ -864,7 +866,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_propose_kernel(
     __syncthreads();
 
     uint32_t flags = 0;
-    for (int j = w; j < B; j += kDenseWaves) {
+    for (int j = w; j < B; j += nw) {
         const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
         const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
         const float mq = row_m[qr], mp = row_m[pr];
@@ -1558,8 +1560,11 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
     const int want = (2048 + batch - 1) / batch;
     const int gy = per_req < want ? per_req : want;
     const dim3 rgrid((unsigned)batch, (unsigned)gy);
+    // the proposals of a request run side by side: one wave each (4 to 16 waves)
+    const int pw = B < kDenseWaves ? kDenseWaves : (B > kProposeMaxThreads / kWave ? kProposeMaxThreads / kWave : B);
+    const unsigned pthreads = (unsigned)(pw * kWave);
     if (bf16) {
-        dense_propose_kernel<true><<<dim3((unsigned)batch), kDenseThreads, 0, stream>>>(
+        dense_propose_kernel<true><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
             sc.flags, o);
         if (!exact_all)
@@ -1570,7 +1575,7 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
             sc.flags, sc.resid, o);
     } else {
-        dense_propose_kernel<false><<<dim3((unsigned)batch), kDenseThreads, 0, stream>>>(
+        dense_propose_kernel<false><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
             sc.flags, o);
         if (!exact_all)
