@@ -263,7 +263,8 @@ __device__ __forceinline__ int block_rank_topk(const uint2* lst, int stride, con
 // then, serves as the id scratch).
 __device__ __forceinline__ void finalize_row(uint32_t* sk, const int32_t* sid, double* se, int n,
                                              const FilterParams fp, const SparseOut out, int64_t r, int lane,
-                                             double* s_scal, double* s_cx)
+                                             double* s_scal, double* s_cx, bool have_full = false,
+                                             double s_full = 0.0)
 {
     double* oc = out.cum ? out.cum + r * out.cap : nullptr;
     int32_t* oid = out.ids + r * out.cap;
@@ -283,7 +284,10 @@ __device__ __forceinline__ void finalize_row(uint32_t* sk, const int32_t* sid, d
         }
     } else {
         m = (double)key_float(sk[0]);
-        if (fp.full_cmax) {
+        if (have_full) {
+            // joint order, summed by the stream itself (relative to the row maximum)
+            S = s_full;
+        } else if (fp.full_cmax) {
             // joint order: pi takes the full-vocabulary normaliser, combined from
             // the row's exact chunk sums (each relative to its chunk maximum)
             const float* cm = fp.full_cmax + r * fp.full_nc;
@@ -395,8 +399,8 @@ __device__ __forceinline__ void finalize_row(uint32_t* sk, const int32_t* sid, d
 // lists are pruned by the best per-wave k-th entry and ranked together.  With
 // one segment the block also finalises the row; otherwise it writes the
 // segment's sorted top-k for topk_merge_kernel.
-template <bool BF16>
-__global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
+template <bool BF16, bool JOINT>
+__global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     RowSource src, int64_t rows, int64_t N, FilterParams fp_all, SparseOut out, int S,
     uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap, const FilterParams* rowp)
 {
@@ -414,6 +418,13 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     __shared__ uint32_t s_b[kWaves];
     __shared__ uint32_t s_mx[kWaves];
     __shared__ int s_ns[kWaves];
+    __shared__ uint32_t s_jm[kWaves];
+    __shared__ double s_js[kWaves];
+    __shared__ double s_exp2[JOINT ? kExp2Entries : 1];
+    if constexpr (JOINT) {
+        load_exp2_table(s_exp2);
+        __syncthreads();
+    }
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -440,6 +451,19 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     // as an argument so the compare is never constant-folded.
     uint32_t thr_key = kKeyNegInf;
     float thr = fp.thr_init;
+    // Joint order in one pass (JOINT, whole rows): each lane keeps the running
+    // maximum jm of the finite logits it streams and the sum js of
+    // exp((z - jm)/T) over them, rescaled when jm rises.
+    const bool jrow = JOINT && fp.joint && !fp.greedy;
+    const DenseExp jex{ jrow ? 1.4426950408889634074 / (double)fp.temperature : 1.0, s_exp2 };
+    float jm = -INFINITY;
+    double js = 0.0;
+    auto joint_raise = [&](float mx) __attribute__((always_inline)) {
+        if (mx > jm) {
+            js = (jm > -INFINITY) ? js * jex((double)jm - (double)mx) : 0.0;
+            jm = mx;
+        }
+    };
 
     auto compact = [&]() __attribute__((always_inline)) {
         if (cnt < k) return;
@@ -455,6 +479,12 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
         if (lane < n) {
             v = load_scalar<BF16>(row, beg + lane);
             key = float_key(v);
+        }
+        if constexpr (JOINT) {
+            if (jrow && lane < n && finite_f32(v)) {
+                joint_raise(v);
+                js += jex((double)v - (double)jm);
+            }
         }
         const bool pass = key_admits(key, thr_key);
         const uint64_t m = __ballot(pass);
@@ -501,6 +531,24 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
     // predicate and, as a wave mask in scalar registers, the source of counts,
     // skips and write positions.
     auto process = [&](const typename V::T (&x)[U], int64_t v0) __attribute__((always_inline)) {
+        if constexpr (JOINT) {
+            if (jrow) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < kPerIter; ++i) {
+                    const float z = V::get(x[i / EPV], i % EPV);
+                    if (finite_f32(z)) mx = fmaxf(mx, z);
+                }
+                joint_raise(mx);
+                double acc = 0.0;
+#pragma unroll
+                for (int i = 0; i < kPerIter; ++i) {
+                    const float z = V::get(x[i / EPV], i % EPV);
+                    if (finite_f32(z)) acc += jex((double)z - (double)jm);
+                }
+                js += acc;
+            }
+        }
         bool pass[kPerIter];
         uint64_t m[kPerIter];
         uint64_t any = 0;
@@ -615,6 +663,15 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
             if (__popcll(__ballot(lmax >= cand)) >= quota) b = cand;
         }
     }
+    if constexpr (JOINT) {
+        if (jrow) {    // the wave's maximum and sum relative to it
+            const uint32_t kw = wave_max_u32(float_key(jm));
+            const float mw = key_float(kw);
+            double part = (jm > -INFINITY) ? js * jex((double)jm - (double)mw) : 0.0;
+            part = wave_sum_f64(part);
+            if (lane == 0) { s_jm[w] = kw; s_js[w] = part; }
+        }
+    }
     if (lane == 0) s_b[w] = b;
     __syncthreads();
     uint32_t B = s_b[0];
@@ -656,7 +713,21 @@ __global__ __launch_bounds__(kThreads, 5) void topk_stream_kernel(
                                           reinterpret_cast<uint64_t*>(s_cx));
     __syncthreads();
     if (S == 1) {
-        if (w == rot) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane, s_scal, s_cx);
+        if (w == rot) {
+            double s_full = 0.0;
+            if constexpr (JOINT) {
+                if (jrow) {    // the row's full normaliser relative to its maximum
+                    uint32_t km = s_jm[0];
+#pragma unroll
+                    for (int o = 1; o < kWaves; ++o) km = s_jm[o] > km ? s_jm[o] : km;
+                    const double mr = (double)key_float(km);
+#pragma unroll
+                    for (int o = 0; o < kWaves; ++o)
+                        if (s_jm[o] > kKeyNegInf) s_full += s_js[o] * jex((double)key_float(s_jm[o]) - mr);
+                }
+            }
+            finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane, s_scal, s_cx, jrow, s_full);
+        }
     } else {
         const int64_t base = (r * S + seg) * (int64_t)part_cap;
         for (int i = threadIdx.x; i < n; i += kThreads) {
@@ -948,16 +1019,26 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                               const FilterParams& fp, const SparseOut& out, int S,
                               uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap,
-                              const FilterParams* rowp, hipStream_t stream)
+                              const FilterParams* rowp, bool joint_sums, hipStream_t stream)
 {
     if (rows == 0) return hipSuccess;
+    if (joint_sums && S != 1) return hipErrorInvalidValue;
     dim3 grid((unsigned)(rows * S));
-    if (bf16)
-        topk_stream_kernel<true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
-                                                                part_id, part_n, part_cap, rowp);
-    else
-        topk_stream_kernel<false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
-                                                                 part_id, part_n, part_cap, rowp);
+    if (joint_sums) {
+        if (bf16)
+            topk_stream_kernel<true, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
+                                                                          part_id, part_n, part_cap, rowp);
+        else
+            topk_stream_kernel<false, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
+                                                                           part_id, part_n, part_cap, rowp);
+    } else {
+        if (bf16)
+            topk_stream_kernel<true, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
+                                                                           part_id, part_n, part_cap, rowp);
+        else
+            topk_stream_kernel<false, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
+                                                                            part_id, part_n, part_cap, rowp);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     topk_merge_kernel<<<dim3((unsigned)rows), kThreads, 0, stream>>>(src, rows, fp, out, S, part_key,

@@ -224,18 +224,24 @@ FilterParams filter_params(const uno_sampling_t* sp, const Mode& m)
     fp.full_cmax = nullptr;
     fp.full_csum = nullptr;
     fp.full_nc = 0;
+    fp.joint = 0;
     return fp;
 }
 
-// The sparse filter of `rows` rows into `out`; the joint order first takes
-// exact chunk statistics of the same rows for the full-softmax normaliser.
-// With per-request parameters each row's set is copied to the workspace, and
-// only the joint rows' statistics are taken.
+// The sparse filter of `rows` rows into `out`.  The joint order needs each
+// row's full-softmax normaliser: with one set for whole rows (one segment
+// each) the top-k stream sums it while it streams; otherwise exact chunk
+// statistics of the rows come first.  With per-request parameters each row's
+// set is copied to the workspace, and only the joint rows' statistics are
+// taken.
 hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                                 const SpSet& sps, const RowMap& map, const Mode& m, const SparseWs& sw,
                                 const SparseOut& out, hipStream_t stream)
 {
     FilterParams fp = filter_params(sps.sp, m);
+    // (per-request sets keep the chunk pass, over their joint rows only: the
+    // summing stream runs at lower occupancy for every row of its launch)
+    const bool joint_sums = m.joint && sw.S == 1 && !m.per_request;
     if (m.per_request) {
         std::vector<FilterParams> host((size_t)rows);
         for (int64_t r = 0; r < rows; ++r) {
@@ -254,7 +260,9 @@ hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t voca
                                             hipMemcpyHostToDevice, stream);
         if (e != hipSuccess) return e;
     }
-    if (m.joint) {
+    if (joint_sums) {
+        fp.joint = 1;
+    } else if (m.joint) {
         // with per-row parameters only the joint rows' statistics are taken
         const hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, m.joint_T, sw.full, rows, stream,
                                                  m.per_request ? sw.rowp : nullptr);
@@ -264,7 +272,7 @@ hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t voca
         fp.full_nc = sw.full.nchunks;
     }
     return launch_topk_filter(src, rows, vocab, bf16, fp, out, sw.S, sw.part_key, sw.part_id, sw.part_n,
-                              sw.part_cap, sw.rowp, stream);
+                              sw.part_cap, sw.rowp, joint_sums, stream);
 }
 
 int check_tree_shape(int32_t B, int32_t K, int32_t V, bool need_k)
@@ -497,7 +505,7 @@ int uno_build_tree_ex(const void* draft, int32_t dtype, int32_t batch, int32_t B
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, sw.nucleus_n, nullptr, stream);
         if (e == hipSuccess)
             e = launch_topk_filter(src, rows, vocab, bf16, filter_params(sp, mk), sw.sup, sw.S, sw.part_key,
-                                   sw.part_id, sw.part_n, sw.part_cap, nullptr, stream);
+                                   sw.part_id, sw.part_n, sw.part_cap, nullptr, false, stream);
         if (e == hipSuccess)
             e = launch_dense_support_scale(rows, sp->temperature, dc, sw.nucleus_n, sw.sup, stream);
     }

@@ -27,10 +27,13 @@ struct FilterParams {
     int32_t topp_on;  // top_p < 1
     float thr_init;   // -inf: initial admission threshold of the top-k stream
     // joint order: exact chunk statistics of the same rows, whose full-softmax
-    // normaliser the top-p cut reads (null in the default order)
+    // normaliser the top-p cut reads (null in the default order) ...
     const float* full_cmax;
     const double* full_csum;
     int32_t full_nc;
+    // ... or, with joint set, the top-k stream sums the normaliser itself
+    // (whole rows only, launched with joint_sums)
+    int32_t joint;
 };
 
 // Compact per-row supports in filter order.
@@ -73,11 +76,12 @@ size_t align_up(size_t x, size_t a);
 // ---- launchers (return hipGetLastError() after the launch) ----------------
 // Segment lists hold part_cap entries each; rowp (nullable): per-row
 // parameters replacing fp (k at most part_cap, the k the segments were chosen
-// for)
+// for).  joint_sums (S == 1 only): the stream also sums each joint row's
+// full-softmax normaliser.
 hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                               const FilterParams& fp, const SparseOut& out, int S,
                               uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap,
-                              const FilterParams* rowp, hipStream_t stream);
+                              const FilterParams* rowp, bool joint_sums, hipStream_t stream);
 
 // Rows below exact_rows get exact (fp64 exp) chunk sums; the rest fast ones.
 // rowp (nullable, device): per-row parameters; rows whose entry has no
