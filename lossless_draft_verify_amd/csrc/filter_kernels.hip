@@ -1016,6 +1016,25 @@ int topk_segments(int64_t rows, int64_t vocab, int k)
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+__global__ __launch_bounds__(kThreads) void expand_params_kernel(ParamArgs a, int64_t first, int n, RowMap map,
+                                                                int64_t rows, FilterParams* out)
+{
+    for (int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x; r < rows; r += (int64_t)gridDim.x * kThreads) {
+        const int64_t q = map.req(r) - first;
+        if (q >= 0 && q < n) out[r] = a.p[q];
+    }
+}
+
+hipError_t launch_expand_params(const ParamArgs& a, int64_t first, int n, const RowMap& map, int64_t rows,
+                                FilterParams* out, hipStream_t stream)
+{
+    if (rows == 0 || n <= 0) return hipSuccess;
+    const int64_t blocks = (rows + kThreads - 1) / kThreads;
+    expand_params_kernel<<<dim3((unsigned)(blocks < 1024 ? blocks : 1024)), kThreads, 0, stream>>>(a, first, n, map,
+                                                                                                  rows, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                               const FilterParams& fp, const SparseOut& out, int S,
                               uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap,

@@ -92,19 +92,6 @@ int check_set(const SpSet& s, int64_t requests, int64_t vocab, Mode* m)
 }
 
 // Request of row r for each entry point's row layout.
-struct RowMap {
-    int kind;          // 0: one row per request, 1: linear (draft rows, then target rows), 2: rows_per_req rows each
-    int64_t batch;
-    int32_t B;
-    int32_t rows_per_req;
-    int64_t req(int64_t r) const
-    {
-        if (kind == 0) return r;
-        if (kind == 1) return r < batch * B ? r / B : (r - batch * B) / (B + 1);
-        return r / rows_per_req;
-    }
-};
-
 int check_common(int32_t dtype, int64_t vocab)
 {
     if (dtype != UNO_F32 && dtype != UNO_BF16) return UNO_ERR_UNSUPPORTED;
@@ -242,7 +229,27 @@ hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t voca
     // (per-request sets keep the chunk pass, over their joint rows only: the
     // summing stream runs at lower occupancy for every row of its launch)
     const bool joint_sums = m.joint && sw.S == 1 && !m.per_request;
-    if (m.per_request) {
+    if (m.per_request && sps.n <= 4 * kParamSlots) {
+        // few sets: each set's parameters ride in the arguments of a small
+        // kernel that writes them to its requests' rows (no host copy)
+        for (int64_t first = 0; first < sps.n; first += kParamSlots) {
+            ParamArgs a;
+            const int n = (int)(sps.n - first < kParamSlots ? sps.n - first : kParamSlots);
+            for (int i = 0; i < n; ++i) {
+                const uno_sampling_t* s = &sps.sp[first + i];
+                Mode mi;
+                check_sampling(s, vocab, &mi);
+                a.p[i] = filter_params(s, mi);
+                if (mi.joint) {
+                    a.p[i].full_cmax = sw.full.cmax;
+                    a.p[i].full_csum = sw.full.csum;
+                    a.p[i].full_nc = sw.full.nchunks;
+                }
+            }
+            const hipError_t e = launch_expand_params(a, first, n, map, rows, sw.rowp, stream);
+            if (e != hipSuccess) return e;
+        }
+    } else if (m.per_request) {
         std::vector<FilterParams> host((size_t)rows);
         for (int64_t r = 0; r < rows; ++r) {
             const uno_sampling_t* s = &sps.sp[map.req(r)];

@@ -62,6 +62,27 @@ struct DenseChunks {
     uint64_t* keep;
 };
 
+// Request of row r: kind 0 one row per request, 1 linear (batch*B draft rows,
+// then B+1 target rows per request), 2 rows_per_req consecutive rows each.
+struct RowMap {
+    int kind;
+    int64_t batch;
+    int32_t B;
+    int32_t rows_per_req;
+    __host__ __device__ int64_t req(int64_t r) const
+    {
+        if (kind == 0) return r;
+        if (kind == 1) return r < batch * B ? r / B : (r - batch * B) / (B + 1);
+        return r / rows_per_req;
+    }
+};
+
+// Per-request filter parameters passed by value to launch_expand_params.
+constexpr int kParamSlots = 32;
+struct ParamArgs {
+    FilterParams p[kParamSlots];
+};
+
 constexpr int kDenseChunk = 2048;          // elements per dense chunk
 constexpr int kMergeCap = 4096;            // candidates one merge workgroup holds
 constexpr int kMaxSegments = 64;           // segments per row of the top-k stream
@@ -82,6 +103,11 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
                               const FilterParams& fp, const SparseOut& out, int S,
                               uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap,
                               const FilterParams* rowp, bool joint_sums, hipStream_t stream);
+
+// out[r] = a.p[map.req(r) - first] for the rows whose request lies in
+// [first, first + n), n <= kParamSlots.
+hipError_t launch_expand_params(const ParamArgs& a, int64_t first, int n, const RowMap& map, int64_t rows,
+                                FilterParams* out, hipStream_t stream);
 
 // Rows below exact_rows get exact (fp64 exp) chunk sums; the rest fast ones.
 // rowp (nullable, device): per-row parameters; rows whose entry has no

@@ -24,10 +24,11 @@ def _params(n):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("rows,N", [(64, 3001), (24, 151936)])
+@pytest.mark.parametrize("rows,N", [(64, 3001), (24, 151936), (300, 1003)])
 def test_filter_per_row_parameters(dtype, rows, N):
     # 3001 logits: one workgroup per row; 151936: rows split into segments whose
-    # lists (sized for the largest k) the merge reads with each row's own k
+    # lists (sized for the largest k) the merge reads with each row's own k;
+    # 300 rows: more sets than the kernel arguments carry (the staged copy)
     dev = device()
     rng = np.random.default_rng(50)
     z = torch.from_numpy((rng.standard_normal((rows, N)) * 2).astype(np.float32)).to(dev).to(dtype)
