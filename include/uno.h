@@ -201,8 +201,10 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
  * (temperature == 0, top-k on with top_k <= UNO_MAX_TOP_K, or a vocabulary of
  * at most UNO_MAX_TOP_K), and the joint-order sets must share one temperature;
  * else UNO_ERR_UNSUPPORTED.  Supports are sized for the largest k (cap for
- * uno_filter_ex).  The sets are copied to the workspace on `stream` (host
- * memory; the call returns once they are staged).  Workspace sizes come from
+ * uno_filter_ex).  `sp` is host memory, read during the call: the sets are
+ * written to the workspace on `stream` (up to 128 through kernel arguments,
+ * more by a copy staged before the call returns), so the caller may reuse the
+ * array once the call returns.  Workspace sizes come from
  * uno_workspace_bytes_ex with the same sets. */
 int uno_workspace_bytes_ex(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K, int32_t V,
                            int64_t vocab, int32_t dtype, const uno_sampling_t* sp, int32_t n_sp,
