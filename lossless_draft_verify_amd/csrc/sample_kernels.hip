@@ -1160,7 +1160,8 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
     const double vlo = (double)vlo_f;
     const double vscale = (vlo < (double)m) ? (double)kNucBins / ((double)m - vlo) : 0.0;
     auto vbin = [&](float z) __attribute__((always_inline)) {     // z >= vlo
-        const int b = (int)floor(((double)z - vlo) * vscale);
+        // the product is >= 0 and at most about kNucBins: truncation is the floor
+        const int b = (int)(((double)z - vlo) * vscale);
         return b < kNucBins - 1 ? b : kNucBins - 1;
     };
     int b0 = -1;                             // the chosen value bin
