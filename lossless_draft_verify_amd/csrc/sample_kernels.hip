@@ -1109,6 +1109,7 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
     __shared__ int64_t s_cab;                // logits above the cut's bin
     __shared__ int s_bin;
     __shared__ int64_t s_wc[kNucWaves];
+    __shared__ int64_t s_nab[kNucWaves];
     __shared__ int32_t s_idlim;
     constexpr int EPV = Vec<BF16>::EPV;
     load_exp2_table(s_exp2);
@@ -1168,8 +1169,13 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
     uint32_t lo = 0, hi = 0;                 // later levels: keys in [lo, hi)
     double A = 0.0;                          // mass above the current range
     int64_t cab = 0;                         // logits above the current range
+    // With the one-pass finish available, the first level keeps masses only:
+    // the finish counts the logits above the chosen bin itself (a non-empty
+    // bin is one of positive mass, every finite logit weighing at least 2^-1000).
+    const bool one_pass = nc <= kNucWaves * kWave;
     auto level = [&]() __attribute__((always_inline)) {
         const bool first = b0 < 0;
+        const bool counts = !(first && one_pass);
         const uint32_t width = hi - lo;
         const int nb = first ? kNucBins : (width < (uint32_t)kNucBins ? (int)width : kNucBins);
         for (int b = (int)threadIdx.x; b < nb; b += kNucThreads) { s_mass[b] = 0.0; s_cnt[b] = 0u; }
@@ -1187,7 +1193,7 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
                     bin = (int)((uint64_t)(key - lo) * (uint64_t)nb / width);
                 }
                 atomicAdd(&s_mass[bin], ex((double)x[i] - (double)m));
-                atomicAdd(&s_cnt[bin], 1u);
+                if (counts) atomicAdd(&s_cnt[bin], 1u);
             }
         });
         __syncthreads();
@@ -1200,17 +1206,18 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
             for (int top = nb - 1; top >= 0 && found < 0; top -= kWave) {
                 const int b = top - lane;
                 const double mb = b >= 0 ? s_mass[b] : 0.0;
-                const double cb = b >= 0 ? (double)s_cnt[b] : 0.0;
+                const double cb = (b >= 0 && counts) ? (double)s_cnt[b] : 0.0;
+                const bool filled = counts ? cb > 0.0 : mb > 0.0;
                 const double incl = wave_incl_scan_f64(mb, lane);
                 const double cincl = wave_incl_scan_f64(cb, lane);
-                const uint64_t hit = __ballot(cb > 0.0 && run + incl >= target);
+                const uint64_t hit = __ballot(filled && run + incl >= target);
                 if (hit) {
                     const int l = wave_first_lane(hit);
                     found = top - l;
                     fa = run + __shfl(incl - mb, l, kWave);
                     fc = crun + __shfl(cincl - cb, l, kWave);
                 } else {
-                    const uint64_t nz = __ballot(cb > 0.0);
+                    const uint64_t nz = __ballot(filled);
                     if (nz) {
                         const int l = 63 - __clzll((long long)nz);
                         last = top - l;
@@ -1247,15 +1254,14 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
     };
     level();
     // ---- one-pass finish when the chosen value bin holds few logits ----------
-    const uint32_t n_b0 = s_cnt[b0];
-    __syncthreads();                          // s_cnt is reused below
-    if (n_b0 <= (uint32_t)(kNucCand * kNucWaves) && nc <= kNucWaves * kWave) {
+    if (one_pass) {
         // Candidates: this wave's logits of bin b0 as order keys (hi, lo words
         // in s_cnt), appended chunk by chunk, so each chunk's run is
         // contiguous; lane q holds the run bounds and the sum above the bin
         // of the wave's q-th chunk (chunks w, w + kNucWaves, ...).
         uint32_t* cl = s_cnt + 2 * kNucCand * w;
         int ncl = 0;
+        int64_t nab = 0;                      // this wave's logits above the bin
         int run_b = 0, run_e = 0;
         double above = 0.0;
         each_chunk([&](int c, const float (&x)[kPerLane]) __attribute__((always_inline)) {
@@ -1270,6 +1276,7 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
                     const float z = x[i];
                     const int vb = (finite_f32(z) && z >= vlo_f) ? vbin(z) : -1;
                     if (vb > b0) sum += ex((double)z - mc);
+                    nab += __popcll(__ballot(vb > b0));
                     const bool cand = vb == b0;
                     const uint64_t mk = __ballot(cand);
                     if (mk) {
@@ -1286,16 +1293,18 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
             sum = wave_sum_f64(sum);
             if (lane == q) { run_b = start; run_e = ncl; above = sum; }
         });
-        if (lane == 0) s_wc[w] = ncl;
+        if (lane == 0) { s_wc[w] = ncl; s_nab[w] = nab; }
         __syncthreads();
         int64_t ntot = 0;
         bool fits = true;
+        cab = 0;
 #pragma unroll
         for (int o = 0; o < kNucWaves; ++o) {
             ntot += s_wc[o];
             fits = fits && s_wc[o] <= kNucCand;
+            cab += s_nab[o];
         }
-        if (fits && ntot == (int64_t)n_b0 && ntot > 0) {
+        if (fits && ntot > 0) {
             // rank every candidate over the four lists; sorted masses go to
             // s_mass[0, half), sorted keys (bit patterns) to s_mass[half, ...)
             constexpr int half = kNucBins / 2;

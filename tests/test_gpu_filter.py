@@ -182,8 +182,11 @@ def test_joint_order_keeps_at_least_the_default_support():
 # ---- full-vocabulary nucleus (top-p without top-k) ---------------------------------------
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("N,T,p", [(1003, 1.0, 0.9), (3001, 0.7, 0.5), (5000, 1.5, 0.99), (151936, 1.0, 0.95)])
+@pytest.mark.parametrize("N,T,p", [(1003, 1.0, 0.9), (3001, 0.7, 0.5), (5000, 1.5, 0.99), (151936, 1.0, 0.95),
+                                   (600000, 1.0, 0.9)])
 def test_nucleus_support_size_and_stats(dtype, N, T, p):
+    # (600000 logits: more chunks than the one-pass finish tracks, so the
+    # first level counts too and the key-bin levels finish every row)
     dev = device()
     rng = np.random.default_rng(N + int(100 * p))
     rows = 12 if N > 100000 else 40
