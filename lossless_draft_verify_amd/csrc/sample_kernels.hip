@@ -1160,10 +1160,24 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
     const float vlo_f = (float)(z_lo > -3.0e38 ? (z_lo < (double)m ? z_lo : (double)m) : -3.0e38);
     const double vlo = (double)vlo_f;
     const double vscale = (vlo < (double)m) ? (double)kNucBins / ((double)m - vlo) : 0.0;
-    auto vbin = [&](float z) __attribute__((always_inline)) {     // z >= vlo
-        // the product is >= 0 and at most about kNucBins: truncation is the floor
-        const int b = (int)(((double)z - vlo) * vscale);
-        return b < kNucBins - 1 ? b : kNucBins - 1;
+    const float vscale_f = (float)(vscale < 3.0e38 ? vscale : 3.0e38);
+    // The value bin of a logit z >= vlo, in fp32: monotone in z (a difference
+    // with a constant, a positive scale, a clamp and a truncation of a
+    // non-negative number), which is all the levels rely on.
+    auto vbin = [&](float z) __attribute__((always_inline)) {
+        return (int)fminf((z - vlo_f) * vscale_f, (float)(kNucBins - 1));
+    };
+    // Smallest key in [ka, kb] whose logit's value bin reaches tb (kb + 1 when
+    // none does): the keys of bin tb are [first_key(tb), first_key(tb + 1)).
+    const uint32_t kvlo = float_key(vlo_f), kvm = float_key(m);
+    auto first_key = [&](int tb) __attribute__((always_inline)) {
+        uint32_t a = kvlo, b = kvm + 1u;
+        while (a < b) {
+            const uint32_t mid = a + (b - a) / 2u;
+            if (vbin(key_float(mid)) >= tb) b = mid;
+            else a = mid + 1u;
+        }
+        return a;
     };
     int b0 = -1;                             // the chosen value bin
     uint32_t lo = 0, hi = 0;                 // later levels: keys in [lo, hi)
@@ -1189,7 +1203,7 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
                     bin = vbin(x[i]);
                 } else {
                     const uint32_t key = float_key(x[i]);
-                    if (key < lo || key >= hi || vbin(x[i]) != b0) continue;
+                    if (key < lo || key >= hi) continue;
                     bin = (int)((uint64_t)(key - lo) * (uint64_t)nb / width);
                 }
                 atomicAdd(&s_mass[bin], ex((double)x[i] - (double)m));
@@ -1233,14 +1247,10 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
         }
         __syncthreads();
         if (first) {
-            // the keys of the value bin's logits, with a few keys' margin for
-            // the rounding of the bin index (the bin test itself stays exact)
+            // exactly the keys of the value bin's logits
             b0 = s_bin;
-            const float za = (float)(vlo + (double)b0 / vscale);
-            const float zb = (float)(vlo + (double)(b0 + 1) / vscale);
-            const uint32_t ka = float_key(za), kb = float_key(zb);
-            lo = ka > 8u ? ka - 8u : 0u;
-            hi = kb < 0xFFFFFFF0u ? kb + 9u : 0xFFFFFFF8u;
+            lo = first_key(b0);
+            hi = first_key(b0 + 1);
         } else {
             // bin b holds the keys k with floor((k - lo) * nb / width) == b
             const uint64_t fb = (uint64_t)s_bin;
