@@ -60,13 +60,13 @@ def _load():
         lib.oracle_filter.restype = ctypes.c_int
         lib.oracle_sample.argtypes = [P, i64, f64, P]
         lib.oracle_sample.restype = i32
-        lib.oracle_linear.argtypes = [P, P, i32, i32, i64, i64, i64, f64, i32, f64, i32, u64, u64, P,
+        lib.oracle_linear.argtypes = [P, P, i32, i32, i64, i64, i64, f64, i32, f64, i32, u64, u64, P, P,
                                       P, P, P, P]
         lib.oracle_linear.restype = None
         lib.oracle_build_tree.argtypes = [P, i32, i32, i32, i32, i64, i64, f64, i32, f64, i32,
                                           P, P, P, P, P, P]
         lib.oracle_build_tree.restype = None
-        lib.oracle_verify_tree.argtypes = [P, i32, i32, i32, i64, i64, f64, i32, f64, i32, u64, u64, P,
+        lib.oracle_verify_tree.argtypes = [P, i32, i32, i32, i64, i64, f64, i32, f64, i32, u64, u64, P, P,
                                            P, P, P, P, P, P, P]
         lib.oracle_verify_tree.restype = None
         lib.oracle_tree_attention.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f64, P, P]
@@ -152,12 +152,21 @@ def _req_ids(request_ids, batch):
     return r
 
 
+def _offsets(offsets, batch):
+    if offsets is None:
+        return None
+    r = np.ascontiguousarray(offsets, dtype=np.uint64)
+    assert r.shape == (batch,)
+    return r
+
+
 def linear(draft, target, temperature, top_k, top_p, seed, offset, request_ids=None,
-           batch=None, order=ORDER_TOPK_FIRST):
+           batch=None, order=ORDER_TOPK_FIRST, offsets=None):
     """One linear UNO cycle per request.
 
     draft [batch, B, N] and target [batch, B+1, N]; with ``batch`` given and
     2-D inputs ([B, N], [B+1, N]) all requests share the same rows.
+    ``offsets`` [batch] (optional): request b's cycle index instead of ``offset``.
     Returns dict(tokens [batch, B+1], accept_len [batch], proposals [batch, B],
     margin [batch])."""
     lib = _load()
@@ -176,8 +185,9 @@ def linear(draft, target, temperature, top_k, top_p, seed, offset, request_ids=N
     prop = np.zeros((batch, B), dtype=np.int32)
     mg = np.zeros(batch, dtype=np.float64)
     rid = _req_ids(request_ids, batch)
+    offs = _offsets(offsets, batch)
     lib.oracle_linear(_ptr(draft), _ptr(target), batch, B, N, ds, ts, _param(temperature),
-                      int(top_k), _param(top_p), int(order), int(seed), int(offset), _ptr(rid),
+                      int(top_k), _param(top_p), int(order), int(seed), int(offset), _ptr(rid), _ptr(offs),
                       _ptr(tokens), _ptr(acc), _ptr(prop), _ptr(mg))
     return dict(tokens=tokens, accept_len=acc, proposals=prop, margin=mg)
 
@@ -201,11 +211,12 @@ def build_tree(draft, K, V, temperature, top_k, top_p, order=ORDER_TOPK_FIRST):
 
 
 def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_k, top_p,
-                seed, offset, request_ids=None, batch=None, order=ORDER_TOPK_FIRST):
+                seed, offset, request_ids=None, batch=None, order=ORDER_TOPK_FIRST, offsets=None):
     """Target-sampled tree walk per request over target [batch, V+1, N].
 
     With ``batch`` given and a 2-D target [V+1, N] plus one tree ([V+1], [V+1],
-    scalar), every request shares those rows and that tree."""
+    scalar), every request shares those rows and that tree.  ``offsets``
+    [batch] (optional): request b's cycle index instead of ``offset``."""
     lib = _load()
     target = _f32(target)
     if target.ndim == 2:
@@ -228,8 +239,9 @@ def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_
     acc = np.zeros(batch, dtype=np.int32)
     mg = np.zeros(batch, dtype=np.float64)
     rid = _req_ids(request_ids, batch)
+    offs = _offsets(offsets, batch)
     lib.oracle_verify_tree(_ptr(target), batch, int(B), V, N, stride, _param(temperature),
-                           int(top_k), _param(top_p), int(order), int(seed), int(offset), _ptr(rid),
+                           int(top_k), _param(top_p), int(order), int(seed), int(offset), _ptr(rid), _ptr(offs),
                            _ptr(tk), _ptr(pa), _ptr(nn), _ptr(tokens), _ptr(path), _ptr(acc),
                            _ptr(mg))
     return dict(tokens=tokens, path=path, accept_len=acc, margin=mg)

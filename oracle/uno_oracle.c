@@ -312,13 +312,16 @@ int32_t oracle_sample(const double* w, int64_t N, double u, double* margin)
  *   j* = B: final ~ p_B (word 2 of position B).
  * Draft row j is judged by target row j; target row B is the bonus row.
  * tokens = y_0 .. y_{j*-1}, final, then -1; accept_len = j* + 1.
- * All B proposals are reported (positions past j* included).
+ * All B proposals are reported (positions past j* included), so the margin
+ * covers every proposal's draw as well as the decisions up to j*.
  * Layout: draft + b*draft_req_stride + j*N, target + b*target_req_stride + j*N;
- * a zero stride shares one block of rows between all requests.              */
+ * a zero stride shares one block of rows between all requests.
+ * offsets (nullable): request b takes the decode-cycle index offsets[b]
+ * instead of `offset` (independent cycles side by side in one call).       */
 void oracle_linear(const float* draft, const float* target, int32_t batch, int32_t B, int64_t N,
                    int64_t draft_req_stride, int64_t target_req_stride,
                    double T, int32_t top_k, double top_p, int32_t order, uint64_t seed, uint64_t offset,
-                   const uint32_t* request_ids,
+                   const uint32_t* request_ids, const uint64_t* offsets,
                    int32_t* tokens, int32_t* accept_len, int32_t* proposals, double* min_margin)
 {
     #pragma omp parallel
@@ -333,6 +336,7 @@ void oracle_linear(const float* draft, const float* target, int32_t batch, int32
         #pragma omp for schedule(dynamic)
         for (int32_t b = 0; b < batch; ++b) {
             const uint32_t req = request_ids ? request_ids[b] : (uint32_t)b;
+            const uint64_t cyc = offsets ? offsets[b] : offset;
             double mg = INFINITY, m1;
             if (!(shared_done && draft_req_stride == 0 && target_req_stride == 0)) {
                 for (int32_t j = 0; j < B; ++j)
@@ -351,17 +355,17 @@ void oracle_linear(const float* draft, const float* target, int32_t batch, int32
             double ym[B > 0 ? B : 1];
             for (int32_t j = 0; j < B; ++j) {
                 double u[4];
-                draw4(seed, req, (uint32_t)j, offset, u);
+                draw4(seed, req, (uint32_t)j, cyc, u);
                 ym[j] = INFINITY;
                 y[j] = (q[j].n > 0) ? sample_weights(q[j].p, N, u[0], &ym[j]) : -1;
                 if (proposals) proposals[(int64_t)b * B + j] = y[j];
+                fmin_into(&mg, ym[j]);
             }
 
             int32_t jstar = B;
             for (int32_t j = 0; j < B; ++j) {
                 double u[4];
-                draw4(seed, req, (uint32_t)j, offset, u);
-                fmin_into(&mg, ym[j]);
+                draw4(seed, req, (uint32_t)j, cyc, u);
                 int accept = 0;
                 if (y[j] >= 0) {
                     const double qy = q[j].p[y[j]];
@@ -374,7 +378,7 @@ void oracle_linear(const float* draft, const float* target, int32_t batch, int32
             }
 
             double u[4];
-            draw4(seed, req, (uint32_t)jstar, offset, u);
+            draw4(seed, req, (uint32_t)jstar, cyc, u);
             int32_t final_tok = -1;
             if (jstar < B) {
                 for (int64_t i = 0; i < N; ++i) {
@@ -490,10 +494,11 @@ void oracle_build_tree(const float* draft, int32_t batch, int32_t B, int32_t K, 
  * the child of n whose token is t if there is one (and d < B), else stop.
  * Target row n of a request is the distribution that follows node n's prefix
  * (row 0: the root).  Rows past num_nodes are never read.
- * tokens/path = emitted tokens / visited nodes, then -1; accept_len = #emitted. */
+ * tokens/path = emitted tokens / visited nodes, then -1; accept_len = #emitted.
+ * offsets (nullable): request b takes the cycle index offsets[b].            */
 void oracle_verify_tree(const float* target, int32_t batch, int32_t B, int32_t V, int64_t N,
                         int64_t req_stride, double T, int32_t top_k, double top_p, int32_t order,
-                        uint64_t seed, uint64_t offset, const uint32_t* request_ids,
+                        uint64_t seed, uint64_t offset, const uint32_t* request_ids, const uint64_t* offsets,
                         const int32_t* node_token, const int32_t* node_parent, const int32_t* num_nodes,
                         int32_t* tokens, int32_t* path, int32_t* accept_len, double* min_margin)
 {
@@ -504,6 +509,7 @@ void oracle_verify_tree(const float* target, int32_t batch, int32_t B, int32_t V
         #pragma omp for schedule(dynamic)
         for (int32_t b = 0; b < batch; ++b) {
             const uint32_t req = request_ids ? request_ids[b] : (uint32_t)b;
+            const uint64_t cyc = offsets ? offsets[b] : offset;
             const int32_t* tk = node_token + (int64_t)b * (V + 1);
             const int32_t* pa = node_parent + (int64_t)b * (V + 1);
             const int32_t nn = num_nodes[b];
@@ -516,7 +522,7 @@ void oracle_verify_tree(const float* target, int32_t batch, int32_t B, int32_t V
                 filter_row(target + (int64_t)b * req_stride + (int64_t)n * N, N, T, top_k, top_p, order, &r);
                 fmin_into(&mg, r.margin);
                 double u[4];
-                draw4(seed, req, (uint32_t)d, offset, u);
+                draw4(seed, req, (uint32_t)d, cyc, u);
                 int32_t t = -1;
                 if (r.n > 0) { t = sample_weights(r.p, N, u[2], &m1); fmin_into(&mg, m1); }
                 tok[d] = t;
