@@ -401,7 +401,7 @@ def main():
                    "vocab": w.vocab, "logits": w.dtype, "temperature": w.temperature, "top_k": w.top_k,
                    "top_p": w.top_p, "rows_per_step": w.rows_per_cycle, "bytes_per_step": w.bytes_per_cycle,
                    "pool_cycles": args.pool,
-                   **({"per_request": [list(x) for x in synth.MIXED_SETS]} if w.mixed else {})},
+                   **({"per_request": [list(x) for x in w.sets]} if w.mixed else {})},
         "hbm_gbs_algorithmic": round(gbs, 1),
         "tpf": round(tpf, 4),
         "roofline": roofline,

@@ -140,7 +140,8 @@ int uno_filter(const void* logits, int32_t dtype, int64_t rows, int64_t vocab,
  *   out_proposals [batch][B] (nullable): every y_j (-1 if q_j is invalid)
  *   out_flags [batch] (nullable): bit 0 = an invalid row was met, bit 1 = the
  *     residual had no mass
- *   request_ids [batch] (nullable device pointer): Philox request ids
+ *   request_ids [batch] (nullable device pointer): Philox request ids, uint32
+ *     (they fill the counter's first 32-bit word)
  * Sparse (top-k on, greedy, or vocab <= UNO_MAX_TOP_K) and dense (top-k off:
  * the whole vocabulary, or its nucleus when top_p < 1) filters are supported. */
 int uno_sample_linear(const void* draft, const void* target, int32_t dtype, int32_t batch,
@@ -192,20 +193,27 @@ int uno_verify_tree(const void* target, int32_t dtype, int32_t batch, int32_t B,
                     int32_t* out_tokens, int32_t* out_path, int32_t* out_accept_len,
                     uint32_t* out_flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Static description of a status code. */
 /* Per-request sampling parameters.  Each *_ex entry point is its namesake with
  * `sp` an array of n_sp sets: n_sp == 1 is the namesake; n_sp == batch (rows
- * for uno_filter_ex) gives request b (row r) the set sp[b] (sp[r]), so greedy
- * and stochastic requests with their own temperature, top-k, top-p and order
- * share one call.  With n_sp > 1 every set must take the top-k path
- * (temperature == 0, top-k on with top_k <= UNO_MAX_TOP_K, or a vocabulary of
- * at most UNO_MAX_TOP_K), and the joint-order sets must share one temperature;
- * else UNO_ERR_UNSUPPORTED.  Supports are sized for the largest k (cap for
- * uno_filter_ex).  `sp` is host memory, read during the call: the sets are
- * written to the workspace on `stream` (up to 128 through kernel arguments,
- * more by a copy staged before the call returns), so the caller may reuse the
- * array once the call returns.  Workspace sizes come from
- * uno_workspace_bytes_ex with the same sets. */
+ * for uno_filter_ex) gives request b (row r) the set sp[b] (sp[r]), so requests
+ * with their own temperature, top-k, top-p and order share one call (SGLang
+ * PR #37667, Changes to shared SGLang infrastructure: verification takes each
+ * request's sampling parameters; run_math_eval walk-through,
+ * "run_math_eval 全参数详解").  Each set keeps its own path:
+ *   - the top-k path (temperature == 0, top-k on with top_k <= UNO_MAX_TOP_K,
+ *     or a vocabulary of at most UNO_MAX_TOP_K), in either filter order --
+ *     a joint-order set at its own temperature;
+ *   - the full-vocabulary path (top-k off, temperature > 0): the full softmax
+ *     when top_p == 1, its nucleus when top_p < 1.
+ * Top-k supports are sized for the largest k among the top-k sets (cap for
+ * uno_filter_ex).  uno_filter_ex: the rows of full-vocabulary sets receive
+ * out_count and out_stats only (their out_ids / out_probs rows hold -1 / 0),
+ * and out_stats is required when any set is full-vocabulary.
+ * uno_build_tree_ex: K <= UNO_MAX_TOP_K when any set is full-vocabulary.
+ * `sp` is host memory, read during the call: the sets reach the workspace
+ * through the arguments of small kernels launched on `stream` (64 sets per
+ * launch), so the caller may reuse the array once the call returns.
+ * Workspace sizes come from uno_workspace_bytes_ex with the same sets. */
 int uno_workspace_bytes_ex(int32_t op, int64_t batch_or_rows, int32_t B, int32_t K, int32_t V,
                            int64_t vocab, int32_t dtype, const uno_sampling_t* sp, int32_t n_sp,
                            size_t* out_bytes);
@@ -256,6 +264,7 @@ int uno_tree_attention(const void* q, const void* k, const void* v, const void* 
                        int32_t dtype, int32_t batch, int32_t n, int32_t Hq, int32_t Hkv, int32_t D,
                        float scale, void* out, float* out_lse, hipStream_t stream);
 
+/* Static description of a status code. */
 const char* uno_status_string(int status);
 
 /* hipError_t of the last failed launch on this host thread (0 if none). */

@@ -8,6 +8,7 @@ raises -- there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -106,6 +107,14 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which a call allocates its outputs, workspace and temporaries
+    and converts its arguments: the call's own stream, so the caching allocator
+    orders their reuse after the kernels that read them.  The caller orders the
+    inputs it passes against that stream."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _check(status: int, where: str):
     if status != 0:
         raise UnoError(status, where)
@@ -161,7 +170,7 @@ def _as_u32_ids(request_ids, batch, device):
     return r.contiguous()
 
 
-def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, stream=None,
+def _filter_rows_impl(logits, temperature, top_k, top_p, cap=None, workspace=None, stream=None,
                 order=ORDER_TOPK_FIRST):
     """uno_filter over logits [rows, vocab].  Returns dict of device tensors:
     ids/probs [rows, cap] (sparse modes), count [rows], stats [rows, 2]."""
@@ -171,13 +180,15 @@ def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, str
     dt = _dtype_code(logits)
     dev = logits.device
     sps, nsp = _sp_set(rows, temperature, top_k, top_p, order)
-    sparse, k_eff = True, 1
+    # rows on the top-k path get supports of the largest k among them; rows
+    # over the full vocabulary report only their count and statistics
+    sparse, k_eff = False, 1
     for i in range(nsp):
         greedy = sps[i].temperature == 0.0
         topk_on = 0 < sps[i].top_k < vocab
-        sp_i = greedy or topk_on or vocab <= MAX_TOP_K
-        sparse = sparse and sp_i
-        k_eff = max(k_eff, 1 if greedy else (sps[i].top_k if topk_on else (vocab if sp_i else 0)))
+        if greedy or topk_on or vocab <= MAX_TOP_K:
+            sparse = True
+            k_eff = max(k_eff, 1 if greedy else (sps[i].top_k if topk_on else vocab))
     cap = (k_eff if sparse else 0) if cap is None else int(cap)
     nb = workspace_bytes(OP_FILTER, rows, 0, 0, 0, vocab, dt, temperature, top_k, top_p, order)
     ws = _workspace(nb, dev, workspace)
@@ -192,7 +203,7 @@ def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, str
     return dict(ids=ids, probs=probs, count=count, stats=stats, workspace=ws)
 
 
-def sample_linear(draft, target, temperature, top_k, top_p, seed, offset, request_ids=None,
+def _sample_linear_impl(draft, target, temperature, top_k, top_p, seed, offset, request_ids=None,
                   out=None, workspace=None, stream=None, order=ORDER_TOPK_FIRST):
     """uno_sample_linear: draft [batch, B, vocab], target [batch, B+1, vocab]."""
     lib = load_library()
@@ -222,7 +233,7 @@ def sample_linear(draft, target, temperature, top_k, top_p, seed, offset, reques
     return out
 
 
-def build_tree(draft, K, V, temperature, top_k, top_p, out=None, workspace=None, stream=None,
+def _build_tree_impl(draft, K, V, temperature, top_k, top_p, out=None, workspace=None, stream=None,
                order=ORDER_TOPK_FIRST):
     """uno_build_tree: draft [batch, B, vocab] -> node arrays [batch, V+1], num_nodes [batch]."""
     lib = load_library()
@@ -249,7 +260,7 @@ def build_tree(draft, K, V, temperature, top_k, top_p, out=None, workspace=None,
     return out
 
 
-def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_k, top_p, seed,
+def _verify_tree_impl(target, B, node_token, node_parent, num_nodes, temperature, top_k, top_p, seed,
                 offset, request_ids=None, out=None, workspace=None, stream=None, order=ORDER_TOPK_FIRST):
     """uno_verify_tree: target [batch, V+1, vocab] and a tree from build_tree."""
     lib = load_library()
@@ -281,7 +292,7 @@ def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_
     return out
 
 
-def tree_attention(q, k, v, o_prefix, lse_prefix, node_parent, num_nodes, scale, out=None, stream=None):
+def _tree_attention_impl(q, k, v, o_prefix, lse_prefix, node_parent, num_nodes, scale, out=None, stream=None):
     """uno_tree_attention: q, o_prefix [batch, n, Hq, D], k, v [batch, n, Hkv, D] (bf16),
     lse_prefix [batch, n, Hq] (fp32), node_parent [batch, n], num_nodes [batch] or None.
     Returns dict(o [batch, n, Hq, D] bf16, lse [batch, n, Hq] fp32)."""
@@ -301,3 +312,42 @@ def tree_attention(q, k, v, o_prefix, lse_prefix, node_parent, num_nodes, scale,
                                   _ptr(num_nodes), 1, batch, n, Hq, Hkv, D, float(scale), _ptr(out["o"]),
                                   _ptr(out["lse"]), _stream(stream)), "uno_tree_attention")
     return out
+
+
+def filter_rows(logits, temperature, top_k, top_p, cap=None, workspace=None, stream=None,
+                order=ORDER_TOPK_FIRST):
+    """uno_filter over logits [rows, vocab].  Returns dict of device tensors:
+    ids/probs [rows, cap] (sparse modes), count [rows], stats [rows, 2]."""
+    with _on(stream):
+        return _filter_rows_impl(logits, temperature, top_k, top_p, cap, workspace, stream, order)
+
+
+def sample_linear(draft, target, temperature, top_k, top_p, seed, offset, request_ids=None,
+                  out=None, workspace=None, stream=None, order=ORDER_TOPK_FIRST):
+    """uno_sample_linear: draft [batch, B, vocab], target [batch, B+1, vocab]."""
+    with _on(stream):
+        return _sample_linear_impl(draft, target, temperature, top_k, top_p, seed, offset, request_ids, out,
+                                   workspace, stream, order)
+
+
+def build_tree(draft, K, V, temperature, top_k, top_p, out=None, workspace=None, stream=None,
+               order=ORDER_TOPK_FIRST):
+    """uno_build_tree: draft [batch, B, vocab] -> node arrays [batch, V+1], num_nodes [batch]."""
+    with _on(stream):
+        return _build_tree_impl(draft, K, V, temperature, top_k, top_p, out, workspace, stream, order)
+
+
+def verify_tree(target, B, node_token, node_parent, num_nodes, temperature, top_k, top_p, seed,
+                offset, request_ids=None, out=None, workspace=None, stream=None, order=ORDER_TOPK_FIRST):
+    """uno_verify_tree: target [batch, V+1, vocab] and a tree from build_tree."""
+    with _on(stream):
+        return _verify_tree_impl(target, B, node_token, node_parent, num_nodes, temperature, top_k, top_p, seed,
+                                 offset, request_ids, out, workspace, stream, order)
+
+
+def tree_attention(q, k, v, o_prefix, lse_prefix, node_parent, num_nodes, scale, out=None, stream=None):
+    """uno_tree_attention: q, o_prefix [batch, n, Hq, D], k, v [batch, n, Hkv, D] (bf16),
+    lse_prefix [batch, n, Hq] (fp32), node_parent [batch, n], num_nodes [batch] or None.
+    Returns dict(o [batch, n, Hq, D] bf16, lse [batch, n, Hq] fp32)."""
+    with _on(stream):
+        return _tree_attention_impl(q, k, v, o_prefix, lse_prefix, node_parent, num_nodes, scale, out, stream)

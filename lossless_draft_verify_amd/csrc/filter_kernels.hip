@@ -392,6 +392,17 @@ __device__ __forceinline__ void finalize_row(uint32_t* sk, const int32_t* sid, d
     }
 }
 
+// A row the top-k path leaves to the dense kernels: its support slots hold
+// -1 / 0 (its count and statistics come from the dense kernels).
+__device__ __forceinline__ void pad_skipped_row(const SparseOut& out, int64_t r)
+{
+    for (int i = threadIdx.x; i < out.cap; i += blockDim.x) {
+        out.ids[r * out.cap + i] = -1;
+        out.probs[r * out.cap + i] = 0.0;
+        if (out.cum) out.cum[r * out.cap + i] = 0.0;
+    }
+}
+
 // ---- top-k stream ------------------------------------------------------------
 // Block (r, seg): four waves stream quarters of segment seg of row r, each
 // keeping candidates in its own LDS buffer behind a rising admission
@@ -433,6 +444,10 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     const int64_t r = blockIdx.x / S;
     const int seg = (int)(blockIdx.x - r * S);
     const FilterParams fp = rowp ? rowp[r] : fp_all;              // per-row parameters when given
+    if (fp.skip_topk) {
+        if (S == 1) pad_skipped_row(out, r);
+        return;
+    }
     const char* row = row_pointer(src, r, N * ESZ);
     if (row == nullptr) {
         if (S == 1 && threadIdx.x == 0) out.count[r] = -1;
@@ -762,11 +777,15 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r = blockIdx.x;
     if (r >= rows) return;
+    const FilterParams fp = rowp ? rowp[r] : fp_all;
+    if (fp.skip_topk) {
+        pad_skipped_row(out, r);
+        return;
+    }
     if (row_pointer(src, r, 1) == nullptr) {
         if (threadIdx.x == 0) out.count[r] = -1;
         return;
     }
-    const FilterParams fp = rowp ? rowp[r] : fp_all;
     const int k = fp.k;
     // Per segment: its count, its first key, and two lower bounds on the row's
     // k-th entry -- the k-th entry of a full list, and (quota q = ceil(k/S)) the
@@ -839,7 +858,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
 template <bool BF16, bool COUNT>
 __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
     RowSource src, int64_t rows, int64_t N, double log2e_over_T, int64_t exact_rows, DenseChunks dc,
-    const FilterParams* rowp)
+    const FilterParams* rowp, int select)
 {
     using V = Vec<BF16>;
     constexpr int EPV = V::EPV, ESZ = V::ESZ;
@@ -849,17 +868,23 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r = blockIdx.x;
-    // with per-row parameters only the rows that read full-softmax statistics
-    // (the joint order) need them
-    if (rowp != nullptr && rowp[r].full_cmax == nullptr) return;
+    // rows below exact_rows take the exact (fp64-bound) sums, the rest the fast
+    // ones, which need no table
+    bool exact = r < exact_rows;
+    if (rowp != nullptr) {
+        // per-row parameters: only the rows the pass is for, each at its own
+        // temperature; joint-order and nucleus rows are cut on these sums
+        const float* fc = rowp[r].full_cmax;
+        const int32_t dn = rowp[r].dense;
+        if (select == kChunkJointRows ? fc == nullptr : dn == kRowTopK) return;
+        log2e_over_T = 1.4426950408889634074 / (double)rowp[r].temperature;
+        exact = exact || fc != nullptr || dn == kRowNucleus;
+    }
     const int nc = dc.nchunks;
     // a row's chunks are dealt over gridDim.y workgroups (more than one when
     // there are few rows), round robin over all their waves
     const int c0 = (int)blockIdx.y * kWaves + w;
     const int cstep = (int)gridDim.y * kWaves;
-    // rows below exact_rows take the exact (fp64-bound) sums, the rest the fast
-    // ones, which need no table
-    const bool exact = r < exact_rows;
     if (exact) load_exp2_table(s_exp2);
     __syncthreads();
     const char* row = row_pointer(src, r, N * ESZ);
@@ -965,10 +990,14 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
 
 // Row maximum and normaliser from the chunk statistics (uno_filter, dense mode).
 __global__ void dense_row_stats_kernel(int64_t rows, double inv_T, DenseChunks dc, int32_t* out_count,
-                                       double* out_stats)
+                                       double* out_stats, const FilterParams* rowp)
 {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= rows) return;
+    if (rowp != nullptr) {
+        if (rowp[r].dense != kRowFull) return;
+        inv_T = 1.0 / (double)rowp[r].temperature;
+    }
     const float* cm = dc.cmax + r * dc.nchunks;
     const double* cs = dc.csum + r * dc.nchunks;
     const int32_t* cc = dc.ccount + r * dc.nchunks;
@@ -1016,22 +1045,31 @@ int topk_segments(int64_t rows, int64_t vocab, int k)
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__global__ __launch_bounds__(kThreads) void expand_params_kernel(ParamArgs a, int64_t first, int n, RowMap map,
-                                                                int64_t rows, FilterParams* out)
+// One workgroup per request of the launch: request first + blockIdx.x gets the
+// set a.p[blockIdx.x] on each of its rows (the row layout of map).
+__global__ __launch_bounds__(kThreads) void expand_params_kernel(ParamArgs a, int64_t first, RowMap map,
+                                                                FilterParams* out)
 {
-    for (int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x; r < rows; r += (int64_t)gridDim.x * kThreads) {
-        const int64_t q = map.req(r) - first;
-        if (q >= 0 && q < n) out[r] = a.p[q];
+    const int64_t q = first + blockIdx.x;
+    const FilterParams p = a.p[blockIdx.x];
+    if (map.kind == 0) {
+        if (threadIdx.x == 0) out[q] = p;
+    } else if (map.kind == 1) {
+        const int n = 2 * map.B + 1;
+        for (int j = threadIdx.x; j < n; j += kThreads) {
+            const int64_t row = j < map.B ? q * map.B + j : map.batch * map.B + q * (map.B + 1) + (j - map.B);
+            out[row] = p;
+        }
+    } else {
+        for (int j = threadIdx.x; j < map.rows_per_req; j += kThreads) out[q * map.rows_per_req + j] = p;
     }
 }
 
-hipError_t launch_expand_params(const ParamArgs& a, int64_t first, int n, const RowMap& map, int64_t rows,
-                                FilterParams* out, hipStream_t stream)
+hipError_t launch_expand_params(const ParamArgs& a, int64_t first, int n, const RowMap& map, FilterParams* out,
+                                hipStream_t stream)
 {
-    if (rows == 0 || n <= 0) return hipSuccess;
-    const int64_t blocks = (rows + kThreads - 1) / kThreads;
-    expand_params_kernel<<<dim3((unsigned)(blocks < 1024 ? blocks : 1024)), kThreads, 0, stream>>>(a, first, n, map,
-                                                                                                  rows, out);
+    if (n <= 0) return hipSuccess;
+    expand_params_kernel<<<dim3((unsigned)n), kThreads, 0, stream>>>(a, first, map, out);
     return hipGetLastError();
 }
 
@@ -1067,7 +1105,7 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
 
 hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                                float temperature, const DenseChunks& dc, int64_t exact_rows, hipStream_t stream,
-                               const FilterParams* rowp)
+                               const FilterParams* rowp, int select)
 {
     if (rows == 0) return hipSuccess;
     const double c = 1.4426950408889634074 / (double)temperature;
@@ -1080,23 +1118,28 @@ hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab
     dim3 grid((unsigned)rows, (unsigned)g);
     const bool counts = dc.ccount != nullptr;
     if (bf16 && counts)
-        dense_chunk_kernel<true, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp);
+        dense_chunk_kernel<true, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp,
+                                                                       select);
     else if (bf16)
-        dense_chunk_kernel<true, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp);
+        dense_chunk_kernel<true, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp,
+                                                                        select);
     else if (counts)
-        dense_chunk_kernel<false, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp);
+        dense_chunk_kernel<false, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp,
+                                                                        select);
     else
-        dense_chunk_kernel<false, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp);
+        dense_chunk_kernel<false, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, c, exact_rows, dc, rowp,
+                                                                         select);
     return hipGetLastError();
 }
 
 hipError_t launch_dense_row_stats(int64_t rows, float temperature, const DenseChunks& dc,
-                                  int32_t* out_count, double* out_stats, hipStream_t stream)
+                                  int32_t* out_count, double* out_stats, hipStream_t stream,
+                                  const FilterParams* rowp)
 {
     if (rows == 0) return hipSuccess;
     const unsigned blocks = (unsigned)((rows + 255) / 256);
     dense_row_stats_kernel<<<blocks, 256, 0, stream>>>(rows, 1.0 / (double)temperature, dc, out_count,
-                                                       out_stats);
+                                                       out_stats, rowp);
     return hipGetLastError();
 }
 

@@ -205,7 +205,7 @@ __device__ __forceinline__ double sorted_lookup(const int32_t* ids, const double
 
 __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     int32_t batch, int32_t B, SparseOut sup, uint64_t seed, uint64_t offset,
-    const uint32_t* req_ids, LinearOut o)
+    const uint32_t* req_ids, LinearOut o, const FilterParams* rowp)
 {
     __shared__ SupportScratch s_q[kLinWaves];     // q_j in id order for the residual's lookups; its cumulative sums
     __shared__ int32_t s_y[kMaxLinearB];
@@ -217,6 +217,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int b = blockIdx.x;
+    if (rowp && rowp[(int64_t)b * B].skip_topk) return;      // a request of the dense samplers
     const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
     const int64_t qbase = (int64_t)b * B;
     const int64_t pbase = (int64_t)batch * B + (int64_t)b * (B + 1);
@@ -556,7 +557,7 @@ __device__ __forceinline__ void follow_path(int b, int B, int nn, const int32_t*
 __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     int32_t batch, int32_t B, int32_t V, SparseOut sup, uint64_t seed, uint64_t offset,
     const uint32_t* req_ids, const int32_t* node_token, const int32_t* node_parent,
-    const int32_t* num_nodes, WalkOut o)
+    const int32_t* num_nodes, WalkOut o, const FilterParams* rowp)
 {
     __shared__ TreeLds L;
     __shared__ int32_t s_t[kMaxNodes];
@@ -564,6 +565,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int b = blockIdx.x;
+    if (rowp && rowp[(int64_t)b * (V + 1)].skip_topk) return;   // a request of the dense walk
     const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
     const int cap = sup.cap;
     int nn = num_nodes[b];
@@ -839,11 +841,16 @@ template <bool BF16>
 __global__ __launch_bounds__(kProposeMaxThreads) void dense_propose_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
     uint64_t seed, uint64_t offset, const uint32_t* req_ids, float* row_m, double* row_S,
-    int32_t* jstar_out, int32_t* y_out, uint32_t* flag_out, LinearOut o)
+    int32_t* jstar_out, int32_t* y_out, uint32_t* flag_out, LinearOut o, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
     __shared__ int32_t s_acc[kMaxLinearB];
     __shared__ uint32_t s_flags;
+    if (rowp) {                              // per-request parameters: the request's own temperature
+        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
+        if (f.dense == kRowTopK) return;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
@@ -915,9 +922,14 @@ __global__ __launch_bounds__(kProposeMaxThreads) void dense_propose_kernel(
 template <bool BF16>
 __global__ __launch_bounds__(kDenseThreads) void dense_exact_row_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
-    const int32_t* jstar_in)
+    const int32_t* jstar_in, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
+    if (rowp) {                              // a nucleus request's rows are exact already
+        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
+        if (f.dense != kRowFull) return;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
@@ -948,10 +960,15 @@ __global__ __launch_bounds__(kDenseThreads) void dense_exact_row_kernel(
 template <bool BF16>
 __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
-    const float* row_m, const double* row_S, const int32_t* jstar_in, double* resid)
+    const float* row_m, const double* row_S, const int32_t* jstar_in, double* resid, const FilterParams* rowp)
 {
     const int nc = dc.nchunks;
     __shared__ double s_exp2[kExp2Entries];
+    if (rowp) {
+        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
+        if (f.dense == kRowTopK) return;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
@@ -998,9 +1015,14 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
     uint64_t seed, uint64_t offset, const uint32_t* req_ids, const float* row_m, const double* row_S,
     const int32_t* jstar_in, const int32_t* y_in, const uint32_t* flag_in, const double* resid,
-    LinearOut o)
+    LinearOut o, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
+    if (rowp) {
+        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
+        if (f.dense == kRowTopK) return;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
@@ -1099,7 +1121,7 @@ constexpr int kNucCand = kNucBins / 2 / kNucWaves;   // collected logits per wav
 template <bool BF16>
 __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, int64_t N, double log2e_over_T,
                                                               double top_p, DenseChunks dc, int32_t* out_count,
-                                                              double* out_stats)
+                                                              double* out_stats, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
     __shared__ double s_mass[kNucBins];
@@ -1112,10 +1134,21 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
     __shared__ int64_t s_nab[kNucWaves];
     __shared__ int32_t s_idlim;
     constexpr int EPV = Vec<BF16>::EPV;
+    const int64_t r = blockIdx.x;
+    if (rowp) {
+        // per-row parameters: a full-softmax row keeps the whole vocabulary,
+        // a top-k row is not this kernel's
+        const FilterParams& f = rowp[r];
+        if (f.dense != kRowNucleus) {
+            if (f.dense == kRowFull && threadIdx.x == 0) dc.keep[r] = 0ull;
+            return;
+        }
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+        top_p = (double)f.top_p;
+    }
     load_exp2_table(s_exp2);
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t r = blockIdx.x;
     const int nc = dc.nchunks;
     const float* cm = dc.cmax + r * nc;
     double* cs = dc.csum + r * nc;
@@ -1377,6 +1410,10 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
             return;
         }
         __syncthreads();                      // the later levels reset s_mass and s_cnt
+        // The first level counted nothing (masses only), and s_cnt now holds
+        // the waves' lists: at least one counting level must run, even when
+        // the chosen bin is a single key (a level of width 1 counts its ties).
+        level();
     }
     while (hi - lo > 1u) level();
     // ties at the cut: keep the j-th (by id) while the mass before it is below
@@ -1484,11 +1521,16 @@ template <bool BF16>
 __global__ __launch_bounds__(kWalkThreads) void dense_walk_kernel(
     RowSource src, int32_t batch, int32_t B, int32_t V, int64_t N, double log2e_over_T, DenseChunks dc,
     uint64_t seed, uint64_t offset, const uint32_t* req_ids, const int32_t* node_token,
-    const int32_t* node_parent, const int32_t* num_nodes, WalkOut o)
+    const int32_t* node_parent, const int32_t* num_nodes, WalkOut o, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
     __shared__ TreeLds L;
     __shared__ int32_t s_t[kMaxNodes];
+    if (rowp) {
+        const FilterParams& f = rowp[(int64_t)blockIdx.x * (V + 1)];
+        if (f.dense == kRowTopK) return;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
     load_exp2_table(s_exp2);
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -1527,11 +1569,16 @@ __global__ __launch_bounds__(kWalkThreads) void dense_walk_kernel(
 // the exact chunk statistics give (one wave per row).
 __global__ __launch_bounds__(kDenseThreads) void dense_support_scale_kernel(int64_t rows, double inv_T,
                                                                            DenseChunks dc, const int32_t* limit,
-                                                                           SparseOut sup)
+                                                                           SparseOut sup, const FilterParams* rowp)
 {
     const int lane = lane_id();
     const int64_t r = (int64_t)blockIdx.x * kDenseWaves + threadIdx.x / kWave;
     if (r >= rows) return;
+    if (rowp) {                              // per-row parameters: the full-vocabulary rows only
+        if (rowp[r].dense == kRowTopK) return;
+        if (rowp[r].dense != kRowNucleus) limit = nullptr;
+        inv_T = 1.0 / (double)rowp[r].temperature;
+    }
     int n = sup.count[r];
     if (n <= 0) return;
     if (limit && limit[r] < n) {
@@ -1559,11 +1606,11 @@ __global__ __launch_bounds__(kDenseThreads) void dense_support_scale_kernel(int6
 
 hipError_t launch_linear_sparse(int32_t batch, int32_t B, const SparseOut& sup, uint64_t seed,
                                 uint64_t offset, const uint32_t* request_ids, const LinearOut& o,
-                                hipStream_t stream)
+                                hipStream_t stream, const FilterParams* rowp)
 {
     if (sup.cum == nullptr) return hipErrorInvalidValue;     // needs id-ordered supports
     linear_sparse_kernel<<<dim3((unsigned)batch), kLinThreads, 0, stream>>>(batch, B, sup, seed, offset,
-                                                                           request_ids, o);
+                                                                           request_ids, o, rowp);
     return hipGetLastError();
 }
 
@@ -1571,7 +1618,7 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
                                bool bf16, float temperature, const DenseChunks& dc,
                                const DenseScratch& sc, uint64_t seed, uint64_t offset,
                                const uint32_t* request_ids, const LinearOut& o, bool exact_all,
-                               hipStream_t stream)
+                               hipStream_t stream, const FilterParams* rowp)
 {
     const double c = 1.4426950408889634074 / (double)temperature;
     // about 2048 workgroups: with many requests each wave takes several chunks,
@@ -1586,25 +1633,27 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
     if (bf16) {
         dense_propose_kernel<true><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
-            sc.flags, o);
+            sc.flags, o, rowp);
         if (!exact_all)
-            dense_exact_row_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar);
+            dense_exact_row_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
+                                                                              rowp);
         dense_residual_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(
-            src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid);
+            src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid, rowp);
         dense_finish_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
-            sc.flags, sc.resid, o);
+            sc.flags, sc.resid, o, rowp);
     } else {
         dense_propose_kernel<false><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
-            sc.flags, o);
+            sc.flags, o, rowp);
         if (!exact_all)
-            dense_exact_row_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar);
+            dense_exact_row_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc,
+                                                                               sc.jstar, rowp);
         dense_residual_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(
-            src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid);
+            src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid, rowp);
         dense_finish_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
-            sc.flags, sc.resid, o);
+            sc.flags, sc.resid, o, rowp);
     }
     return hipGetLastError();
 }
@@ -1625,11 +1674,11 @@ hipError_t launch_tree_build(int32_t batch, int32_t B, int32_t K, int32_t V, con
 hipError_t launch_tree_walk(int32_t batch, int32_t B, int32_t V, const SparseOut& sup, uint64_t seed,
                             uint64_t offset, const uint32_t* request_ids, const int32_t* node_token,
                             const int32_t* node_parent, const int32_t* num_nodes, const WalkOut& o,
-                            hipStream_t stream)
+                            hipStream_t stream, const FilterParams* rowp)
 {
     if (sup.cum == nullptr) return hipErrorInvalidValue;     // needs id-ordered supports
     tree_walk_kernel<<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
-        batch, B, V, sup, seed, offset, request_ids, node_token, node_parent, num_nodes, o);
+        batch, B, V, sup, seed, offset, request_ids, node_token, node_parent, num_nodes, o, rowp);
     return hipGetLastError();
 }
 
@@ -1637,40 +1686,43 @@ hipError_t launch_tree_walk_dense(const RowSource& src, int32_t batch, int32_t B
                                   bool bf16, float temperature, const DenseChunks& dc, uint64_t seed,
                                   uint64_t offset, const uint32_t* request_ids, const int32_t* node_token,
                                   const int32_t* node_parent, const int32_t* num_nodes, const WalkOut& o,
-                                  hipStream_t stream)
+                                  hipStream_t stream, const FilterParams* rowp)
 {
     const double c = 1.4426950408889634074 / (double)temperature;
     if (bf16)
         dense_walk_kernel<true><<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
-            src, batch, B, V, vocab, c, dc, seed, offset, request_ids, node_token, node_parent, num_nodes, o);
+            src, batch, B, V, vocab, c, dc, seed, offset, request_ids, node_token, node_parent, num_nodes, o,
+            rowp);
     else
         dense_walk_kernel<false><<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
-            src, batch, B, V, vocab, c, dc, seed, offset, request_ids, node_token, node_parent, num_nodes, o);
+            src, batch, B, V, vocab, c, dc, seed, offset, request_ids, node_token, node_parent, num_nodes, o,
+            rowp);
     return hipGetLastError();
 }
 
 hipError_t launch_dense_support_scale(int64_t rows, float temperature, const DenseChunks& dc,
-                                      const int32_t* limit, const SparseOut& sup, hipStream_t stream)
+                                      const int32_t* limit, const SparseOut& sup, hipStream_t stream,
+                                      const FilterParams* rowp)
 {
     if (sup.stats == nullptr) return hipErrorInvalidValue;
     dense_support_scale_kernel<<<dim3((unsigned)((rows + kDenseWaves - 1) / kDenseWaves)), kDenseThreads, 0,
-                                 stream>>>(rows, 1.0 / (double)temperature, dc, limit, sup);
+                                 stream>>>(rows, 1.0 / (double)temperature, dc, limit, sup, rowp);
     return hipGetLastError();
 }
 
 hipError_t launch_nucleus(const RowSource& src, int64_t rows, int64_t vocab, bool bf16, float temperature,
                           float top_p, const DenseChunks& dc, int32_t* out_count, double* out_stats,
-                          hipStream_t stream)
+                          hipStream_t stream, const FilterParams* rowp)
 {
     if (rows == 0) return hipSuccess;
     if (dc.keep == nullptr) return hipErrorInvalidValue;
     const double c = 1.4426950408889634074 / (double)temperature;
     if (bf16)
         nucleus_kernel<true><<<dim3((unsigned)rows), kNucThreads, 0, stream>>>(src, vocab, c, (double)top_p, dc,
-                                                                             out_count, out_stats);
+                                                                             out_count, out_stats, rowp);
     else
         nucleus_kernel<false><<<dim3((unsigned)rows), kNucThreads, 0, stream>>>(src, vocab, c, (double)top_p, dc,
-                                                                              out_count, out_stats);
+                                                                              out_count, out_stats, rowp);
     return hipGetLastError();
 }
 

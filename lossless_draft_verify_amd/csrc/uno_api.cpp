@@ -6,8 +6,6 @@
 #include <math.h>
 #include <string.h>
 
-#include <vector>
-
 using namespace uno;
 
 namespace {
@@ -16,17 +14,22 @@ thread_local int g_last_hip_error = 0;
 
 constexpr size_t kAlign = 256;
 
-// Sampling mode of a parameter set.
+// Sampling mode of a call: of its one parameter set, or of all its per-request
+// sets together.
 struct Mode {
-    bool greedy;
+    bool greedy;     // every set is greedy
     bool topk_on;
     bool topp_on;
-    bool sparse;     // support from a top-k selection (greedy: k = 1)
-    bool joint;      // joint order with both top-k and top-p on (sparse only)
-    bool nucleus;    // top-p without top-k over a full vocabulary (dense only)
-    bool per_request;// one parameter set per request (sparse only; k is the largest)
-    int32_t k;       // effective k on the sparse path
-    float joint_T;   // temperature of the joint-order chunk statistics
+    bool sparse;     // every row takes the top-k path (greedy: k = 1)
+    bool joint;      // some set is in the joint order with top-k and top-p on (a top-k set)
+    bool nucleus;    // one set: top-p without top-k over a full vocabulary
+    bool per_request;// one parameter set per request (or per row for the filter)
+    bool any_sparse; // some set takes the top-k path
+    bool any_dense;  // some set takes a full-vocabulary path (full softmax or nucleus)
+    bool any_full;   // some set is a full softmax (top-k and top-p off)
+    bool any_nucleus;// some set is a nucleus
+    int32_t k;       // largest effective k over the top-k sets (1 when there is none)
+    float joint_T;   // one set in the joint order: its temperature
 };
 
 int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
@@ -47,6 +50,10 @@ int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
     if (m->sparse && m->k > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
     m->nucleus = !m->sparse && m->topp_on;
     m->per_request = false;
+    m->any_sparse = m->sparse;
+    m->any_dense = !m->sparse;
+    m->any_nucleus = m->nucleus;
+    m->any_full = !m->sparse && !m->nucleus;
     m->joint_T = T;
     if (!m->sparse && vocab > (int64_t)65535 * 4 * kDenseChunk) return UNO_ERR_UNSUPPORTED;
     return UNO_OK;
@@ -58,10 +65,10 @@ struct SpSet {
     int64_t n;
 };
 
-// One set: its mode.  One per request (n == requests): every set must take the
-// top-k path (greedy, top-k on, or a small vocabulary); the combined mode has
-// the largest k and carries the joint-order statistics when any set needs them
-// (one chunk pass, so the joint-order sets must share their temperature).
+// One set: its mode.  One per request (n == requests): each set is checked
+// alone and keeps its own path -- top-k, full softmax or nucleus -- and its
+// own temperature; the combined mode says which paths the call runs, and its
+// k is the largest k of the top-k sets (the stride of their supports).
 int check_set(const SpSet& s, int64_t requests, int64_t vocab, Mode* m)
 {
     if (s.sp == nullptr) return UNO_ERR_INVALID_ARG;
@@ -76,22 +83,24 @@ int check_set(const SpSet& s, int64_t requests, int64_t vocab, Mode* m)
         Mode mi;
         const int st = check_sampling(&s.sp[i], vocab, &mi);
         if (st) return st;
-        if (!mi.sparse) return UNO_ERR_UNSUPPORTED;     // per-request parameters take the top-k path only
         all.greedy = all.greedy && mi.greedy;
         all.topk_on = all.topk_on || mi.topk_on;
         all.topp_on = all.topp_on || mi.topp_on;
-        if (mi.joint) {
-            if (all.joint && mi.joint_T != all.joint_T) return UNO_ERR_UNSUPPORTED;
-            all.joint = true;
-            all.joint_T = mi.joint_T;
+        all.joint = all.joint || mi.joint;
+        if (mi.sparse) {
+            all.any_sparse = true;
+            all.k = mi.k > all.k ? mi.k : all.k;
+        } else {
+            all.sparse = false;
+            all.any_dense = true;
+            all.any_nucleus = all.any_nucleus || mi.nucleus;
+            all.any_full = all.any_full || !mi.nucleus;
         }
-        all.k = mi.k > all.k ? mi.k : all.k;
     }
     *m = all;
     return UNO_OK;
 }
 
-// Request of row r for each entry point's row layout.
 int check_common(int32_t dtype, int64_t vocab)
 {
     if (dtype != UNO_F32 && dtype != UNO_BF16) return UNO_ERR_UNSUPPORTED;
@@ -123,16 +132,17 @@ struct SparseWs {
     int32_t* part_id;
     int32_t* part_n;
     DenseChunks full;    // joint order: exact chunk statistics of the rows
-    int32_t* nucleus_n;  // dense tree build with a nucleus: support sizes
+    int32_t* nucleus_n;  // tree build with nucleus rows: support sizes
     FilterParams* rowp;  // per-request parameters: one set per row
     int part_cap;        // entries per segment list (the largest k)
 };
 
 DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bool keep);
 
-// Supports (when own_supports; in id order with cumulative sums when id_order),
-// segment partials and, in the joint order, chunk statistics for `rows` sparse
-// rows.
+// Supports (when own_supports; in id order with cumulative sums when id_order)
+// and segment partials for `rows` top-k rows with supports of m.k entries;
+// with one set in the joint order, that order's chunk statistics too (per
+// request, the joint rows share the call's chunk statistics instead).
 void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool own_supports, bool id_order,
                   SparseWs* w)
 {
@@ -155,9 +165,10 @@ void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool ow
         w->part_n = cv.take<int32_t>((size_t)rows * w->S);
     }
     w->nucleus_n = nullptr;
-    w->full = DenseChunks{};
-    if (m.joint) w->full = carve_chunks(cv, rows, vocab, false, false);
-    w->rowp = m.per_request ? cv.take<FilterParams>((size_t)rows) : nullptr;
+    if (!m.per_request) {
+        w->full = DenseChunks{};
+        if (m.joint) w->full = carve_chunks(cv, rows, vocab, false, false);
+    }
 }
 
 // Chunk statistics; the finite counts only for uno_filter, whose dense mode
@@ -183,6 +194,19 @@ DenseScratch carve_dense_scratch(Carve& cv, int64_t rows, int32_t batch, int32_t
     s.flags = cv.take<uint32_t>((size_t)batch);
     s.resid = cv.take<double>((size_t)batch * nchunks);
     return s;
+}
+
+// Per-request sets: the row table, and one chunk-statistics array that the
+// joint-order rows and the full-vocabulary rows share (a row is one or the
+// other).
+void carve_per_request(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool counts, SparseWs* sw,
+                       DenseChunks* dc)
+{
+    sw->rowp = cv.take<FilterParams>((size_t)rows);
+    if (m.any_dense || m.joint) {
+        *dc = carve_chunks(cv, rows, vocab, counts, m.any_nucleus);
+        if (m.joint) sw->full = *dc;
+    }
 }
 
 int check_ws(void* ws, size_t ws_bytes, size_t need)
@@ -212,67 +236,64 @@ FilterParams filter_params(const uno_sampling_t* sp, const Mode& m)
     fp.full_csum = nullptr;
     fp.full_nc = 0;
     fp.joint = 0;
+    fp.dense = m.sparse ? kRowTopK : (m.nucleus ? kRowNucleus : kRowFull);
+    fp.skip_topk = m.sparse ? 0 : 1;
     return fp;
 }
 
-// The sparse filter of `rows` rows into `out`.  The joint order needs each
-// row's full-softmax normaliser: with one set for whole rows (one segment
-// each) the top-k stream sums it while it streams; otherwise exact chunk
-// statistics of the rows come first.  With per-request parameters each row's
-// set is copied to the workspace, and only the joint rows' statistics are
-// taken.
+// Per-request sets to the row table (sw.rowp), on the stream: each set rides
+// in the arguments of a small kernel that writes it to its request's rows
+// (kParamSlots sets per launch), so the host array is not read after the call
+// returns.  Joint-order rows point at the call's chunk statistics; with
+// build_K > 0 (tree build) the full-vocabulary rows take the top-k stream with
+// k = build_K and no top-p (their candidates are the K most likely ids, the
+// probabilities rescaled to the full softmax or the nucleus afterwards).
+hipError_t expand_row_params(const SpSet& sps, int64_t vocab, const RowMap& map, const SparseWs& sw,
+                             int32_t build_K, hipStream_t stream)
+{
+    for (int64_t first = 0; first < sps.n; first += kParamSlots) {
+        ParamArgs a;
+        const int n = (int)(sps.n - first < kParamSlots ? sps.n - first : kParamSlots);
+        for (int i = 0; i < n; ++i) {
+            const uno_sampling_t* s = &sps.sp[first + i];
+            Mode mi;
+            check_sampling(s, vocab, &mi);
+            a.p[i] = filter_params(s, mi);
+            if (mi.joint) {
+                a.p[i].full_cmax = sw.full.cmax;
+                a.p[i].full_csum = sw.full.csum;
+                a.p[i].full_nc = sw.full.nchunks;
+            }
+            if (build_K > 0 && !mi.sparse) {
+                a.p[i].k = build_K;
+                a.p[i].topp_on = 0;
+                a.p[i].skip_topk = 0;
+            }
+        }
+        const hipError_t e = launch_expand_params(a, first, n, map, sw.rowp, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// The top-k filter of `rows` rows into `out` (rows of full-vocabulary sets
+// skipped when per-request).  The joint order needs each row's full-softmax
+// normaliser: with one set for whole rows (one segment each) the top-k stream
+// sums it while it streams; otherwise exact chunk statistics of the joint rows
+// come first (per request: each at its own temperature).
 hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
-                                const SpSet& sps, const RowMap& map, const Mode& m, const SparseWs& sw,
+                                const SpSet& sps, const Mode& m, const SparseWs& sw,
                                 const SparseOut& out, hipStream_t stream)
 {
     FilterParams fp = filter_params(sps.sp, m);
     // (per-request sets keep the chunk pass, over their joint rows only: the
     // summing stream runs at lower occupancy for every row of its launch)
     const bool joint_sums = m.joint && sw.S == 1 && !m.per_request;
-    if (m.per_request && sps.n <= 4 * kParamSlots) {
-        // few sets: each set's parameters ride in the arguments of a small
-        // kernel that writes them to its requests' rows (no host copy)
-        for (int64_t first = 0; first < sps.n; first += kParamSlots) {
-            ParamArgs a;
-            const int n = (int)(sps.n - first < kParamSlots ? sps.n - first : kParamSlots);
-            for (int i = 0; i < n; ++i) {
-                const uno_sampling_t* s = &sps.sp[first + i];
-                Mode mi;
-                check_sampling(s, vocab, &mi);
-                a.p[i] = filter_params(s, mi);
-                if (mi.joint) {
-                    a.p[i].full_cmax = sw.full.cmax;
-                    a.p[i].full_csum = sw.full.csum;
-                    a.p[i].full_nc = sw.full.nchunks;
-                }
-            }
-            const hipError_t e = launch_expand_params(a, first, n, map, rows, sw.rowp, stream);
-            if (e != hipSuccess) return e;
-        }
-    } else if (m.per_request) {
-        std::vector<FilterParams> host((size_t)rows);
-        for (int64_t r = 0; r < rows; ++r) {
-            const uno_sampling_t* s = &sps.sp[map.req(r)];
-            Mode mi;
-            check_sampling(s, vocab, &mi);
-            host[(size_t)r] = filter_params(s, mi);
-            if (mi.joint) {
-                host[(size_t)r].full_cmax = sw.full.cmax;
-                host[(size_t)r].full_csum = sw.full.csum;
-                host[(size_t)r].full_nc = sw.full.nchunks;
-            }
-        }
-        // from pageable memory: the call returns once the data is staged
-        const hipError_t e = hipMemcpyAsync(sw.rowp, host.data(), host.size() * sizeof(FilterParams),
-                                            hipMemcpyHostToDevice, stream);
-        if (e != hipSuccess) return e;
-    }
     if (joint_sums) {
         fp.joint = 1;
     } else if (m.joint) {
-        // with per-row parameters only the joint rows' statistics are taken
         const hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, m.joint_T, sw.full, rows, stream,
-                                                 m.per_request ? sw.rowp : nullptr);
+                                                 m.per_request ? sw.rowp : nullptr, kChunkJointRows);
         if (e != hipSuccess) return e;
         fp.full_cmax = sw.full.cmax;
         fp.full_csum = sw.full.csum;
@@ -299,9 +320,17 @@ int layout_filter(int64_t rows, int64_t vocab, int32_t dtype, const SpSet& sps, 
     st = check_set(sps, rows, vocab, m);
     if (st) return st;
     if (rows == 0) return UNO_OK;
-    if (m->sparse) carve_sparse(cv, rows, vocab, *m, false, false, sw);
-    else if (m->nucleus) *dc = carve_chunks(cv, rows, vocab, false, true);   // counts come from the nucleus
-    else *dc = carve_chunks(cv, rows, vocab, true, false);
+    if (m->per_request) {
+        // counts: a full-softmax row reports its number of finite logits
+        carve_per_request(cv, rows, vocab, *m, m->any_full, sw, dc);
+        if (m->any_sparse) carve_sparse(cv, rows, vocab, *m, false, false, sw);
+    } else if (m->sparse) {
+        carve_sparse(cv, rows, vocab, *m, false, false, sw);
+    } else if (m->nucleus) {
+        *dc = carve_chunks(cv, rows, vocab, false, true);   // counts come from the nucleus
+    } else {
+        *dc = carve_chunks(cv, rows, vocab, true, false);
+    }
     return UNO_OK;
 }
 
@@ -315,10 +344,10 @@ int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const 
     if (st) return st;
     if (batch == 0) return UNO_OK;
     const int64_t rows = batch * (2 * (int64_t)B + 1);
-    if (m->sparse) {
-        carve_sparse(cv, rows, vocab, *m, true, true, sw);
-    } else {
-        *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
+    if (m->per_request) carve_per_request(cv, rows, vocab, *m, false, sw, dc);
+    if (m->any_sparse) carve_sparse(cv, rows, vocab, *m, true, true, sw);
+    if (m->any_dense) {
+        if (!m->per_request) *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
         *ds = carve_dense_scratch(cv, rows, (int32_t)batch, B, dc->nchunks);
     }
     return UNO_OK;
@@ -336,21 +365,25 @@ int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int6
     st = check_set(sps, batch, vocab, m);
     if (st) return st;
     // a full-vocabulary build selects its K candidates with the top-k path
-    if (!m->sparse && build && K > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
+    if (m->any_dense && build && K > UNO_MAX_TOP_K) return UNO_ERR_UNSUPPORTED;
     if (batch == 0) return UNO_OK;
     const int64_t rows = batch * (build ? (int64_t)B : (int64_t)V + 1);
-    if (m->sparse) {
-        // the build reads its candidates in filter order, the walk samples in id order
-        carve_sparse(cv, rows, vocab, *m, true, !build, sw);
-    } else if (build) {
+    if (m->per_request) carve_per_request(cv, rows, vocab, *m, false, sw, dc);
+    if (build) {
+        // every row's candidates in filter order: the top-k rows with their own
+        // k, the full-vocabulary rows with k = K (rescaled afterwards)
         Mode mk = *m;
-        mk.k = K;
+        if (m->any_dense) mk.k = (m->any_sparse && m->k > K) ? m->k : K;
         carve_sparse(cv, rows, vocab, mk, true, false, sw);
-        sw->sup.stats = cv.take<double>((size_t)rows * 2);
-        *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
-        sw->nucleus_n = m->nucleus ? cv.take<int32_t>((size_t)rows) : nullptr;
+        if (m->any_dense) {
+            sw->sup.stats = cv.take<double>((size_t)rows * 2);
+            if (!m->per_request) *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
+            sw->nucleus_n = m->any_nucleus ? cv.take<int32_t>((size_t)rows) : nullptr;
+        }
     } else {
-        *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
+        // the walk samples top-k rows in id order
+        if (m->any_sparse) carve_sparse(cv, rows, vocab, *m, true, true, sw);
+        if (m->any_dense && !m->per_request) *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
     }
     return UNO_OK;
 }
@@ -366,9 +399,9 @@ int uno_workspace_bytes_ex(int32_t op, int64_t batch_or_rows, int32_t B, int32_t
     if (out_bytes == nullptr) return UNO_ERR_INVALID_ARG;
     Carve cv{ nullptr };
     Mode m;
-    SparseWs sw;
-    DenseChunks dc;
-    DenseScratch ds;
+    SparseWs sw{};
+    DenseChunks dc{};
+    DenseScratch ds{};
     int st;
     switch (op) {
     case UNO_OP_FILTER: st = layout_filter(batch_or_rows, vocab, dtype, sps, cv, &m, &sw, &dc); break;
@@ -390,17 +423,14 @@ int uno_filter_ex(const void* logits, int32_t dtype, int64_t rows, int64_t vocab
     const RowMap map{ 0, rows, 0, 1 };
     Carve sizing{ nullptr };
     Mode m;
-    SparseWs sw;
-    DenseChunks dc;
+    SparseWs sw{};
+    DenseChunks dc{};
     int st = layout_filter(rows, vocab, dtype, sps, sizing, &m, &sw, &dc);
     if (st) return st;
     if (rows == 0) return UNO_OK;
     if (logits == nullptr || out_count == nullptr || !aligned(logits, elem_size(dtype))) return UNO_ERR_INVALID_ARG;
-    if (m.sparse) {
-        if (out_ids == nullptr || out_probs == nullptr || cap < m.k) return UNO_ERR_INVALID_ARG;
-    } else if (out_stats == nullptr) {
-        return UNO_ERR_INVALID_ARG;
-    }
+    if (m.any_sparse && (out_ids == nullptr || out_probs == nullptr || cap < m.k)) return UNO_ERR_INVALID_ARG;
+    if (m.any_dense && out_stats == nullptr) return UNO_ERR_INVALID_ARG;
     st = check_ws(ws, ws_bytes, sizing.used);
     if (st) return st;
     Carve cv{ static_cast<char*>(ws) };
@@ -408,16 +438,20 @@ int uno_filter_ex(const void* logits, int32_t dtype, int64_t rows, int64_t vocab
 
     RowSource src{ static_cast<const char*>(logits), rows, nullptr, nullptr, 1 };
     const bool bf16 = dtype == UNO_BF16;
-    if (m.sparse) {
-        SparseOut out{ out_ids, out_probs, out_count, out_stats, cap };
-        return hip_status(launch_sparse_filter(src, rows, vocab, bf16, sps, map, m, sw, out, stream));
+    const FilterParams* rowp = m.per_request ? sw.rowp : nullptr;
+    hipError_t e = hipSuccess;
+    if (m.per_request) e = expand_row_params(sps, vocab, map, sw, 0, stream);
+    if (e == hipSuccess && m.any_sparse) {
+        SparseOut out{ out_ids, out_probs, out_count, out_stats, cap, nullptr };
+        e = launch_sparse_filter(src, rows, vocab, bf16, sps, m, sw, out, stream);
     }
-    hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
-    if (e == hipSuccess) {
-        if (m.nucleus)
-            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, out_count, out_stats, stream);
-        else
-            e = launch_dense_row_stats(rows, sp->temperature, dc, out_count, out_stats, stream);
+    if (e == hipSuccess && m.any_dense) {
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream, rowp, kChunkDenseRows);
+        if (e == hipSuccess && m.any_nucleus)
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, out_count, out_stats, stream,
+                               rowp);
+        if (e == hipSuccess && m.any_full)
+            e = launch_dense_row_stats(rows, sp->temperature, dc, out_count, out_stats, stream, rowp);
     }
     return hip_status(e);
 }
@@ -432,9 +466,9 @@ int uno_sample_linear_ex(const void* draft, const void* target, int32_t dtype, i
     const RowMap map{ 1, batch, B, 1 };
     Carve sizing{ nullptr };
     Mode m;
-    SparseWs sw;
-    DenseChunks dc;
-    DenseScratch ds;
+    SparseWs sw{};
+    DenseChunks dc{};
+    DenseScratch ds{};
     int st = layout_linear(batch, B, vocab, dtype, sps, sizing, &m, &sw, &dc, &ds);
     if (st) return st;
     if (batch == 0) return UNO_OK;
@@ -451,23 +485,28 @@ int uno_sample_linear_ex(const void* draft, const void* target, int32_t dtype, i
     RowSource src{ static_cast<const char*>(draft), (int64_t)batch * B, static_cast<const char*>(target),
                    nullptr, 1 };
     const bool bf16 = dtype == UNO_BF16;
+    const FilterParams* rowp = m.per_request ? sw.rowp : nullptr;
     LinearOut o{ out_tokens, out_accept_len, out_proposals, out_flags };
-    hipError_t e;
-    if (m.sparse) {
-        e = launch_sparse_filter(src, rows, vocab, bf16, sps, map, m, sw, sw.sup, stream);
-        if (e == hipSuccess) e = launch_linear_sparse(batch, B, sw.sup, seed, offset, request_ids, o, stream);
-    } else {
+    hipError_t e = hipSuccess;
+    if (m.per_request) e = expand_row_params(sps, vocab, map, sw, 0, stream);
+    if (e == hipSuccess && m.any_sparse) {
+        e = launch_sparse_filter(src, rows, vocab, bf16, sps, m, sw, sw.sup, stream);
+        if (e == hipSuccess) e = launch_linear_sparse(batch, B, sw.sup, seed, offset, request_ids, o, stream, rowp);
+    }
+    if (e == hipSuccess && m.any_dense) {
         // draft rows are sampled from (exact sums); target rows enter only
         // acceptance ratios, except the one each request draws its last token
-        // from, which the dense linear path recomputes exactly
-        // (the nucleus needs exact sums on every row)
-        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, m.nucleus ? rows : (int64_t)batch * B,
-                                stream);
-        if (e == hipSuccess && m.nucleus)
-            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream);
+        // from, which the dense linear path recomputes exactly (a nucleus
+        // needs exact sums on every row: one set, all rows; per request, the
+        // chunk pass makes the nucleus rows exact itself)
+        const bool exact_all = !m.per_request && m.nucleus;
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, exact_all ? rows : (int64_t)batch * B,
+                                stream, rowp, kChunkDenseRows);
+        if (e == hipSuccess && m.any_nucleus)
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream, rowp);
         if (e == hipSuccess)
             e = launch_linear_dense(src, batch, B, vocab, bf16, sp->temperature, dc, ds, seed, offset,
-                                    request_ids, o, m.nucleus, stream);
+                                    request_ids, o, exact_all, stream, rowp);
     }
     return hip_status(e);
 }
@@ -481,8 +520,8 @@ int uno_build_tree_ex(const void* draft, int32_t dtype, int32_t batch, int32_t B
     const RowMap map{ 2, batch, B, B };
     Carve sizing{ nullptr };
     Mode m;
-    SparseWs sw;
-    DenseChunks dc;
+    SparseWs sw{};
+    DenseChunks dc{};
     int st = layout_tree(UNO_OP_BUILD_TREE, batch, B, K, V, vocab, dtype, sps, sizing, &m, &sw, &dc);
     if (st) return st;
     if (batch == 0) return UNO_OK;
@@ -497,9 +536,24 @@ int uno_build_tree_ex(const void* draft, int32_t dtype, int32_t batch, int32_t B
     const int64_t rows = (int64_t)batch * B;
     const bool bf16 = dtype == UNO_BF16;
     RowSource src{ static_cast<const char*>(draft), rows, nullptr, nullptr, 1 };
-    hipError_t e;
-    if (m.sparse) {
-        e = launch_sparse_filter(src, rows, vocab, bf16, sps, map, m, sw, sw.sup, stream);
+    hipError_t e = hipSuccess;
+    if (m.per_request) {
+        // each row with its own set; the full-vocabulary rows: exact row
+        // normalisers (over the nucleus when top-p is on) first, then the K
+        // best ids by the same stream as the top-k rows, then their
+        // probabilities under the full softmax (renormalised over the nucleus)
+        e = expand_row_params(sps, vocab, map, sw, K, stream);
+        if (e == hipSuccess && m.any_dense)
+            e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream, sw.rowp,
+                                    kChunkDenseRows);
+        if (e == hipSuccess && m.any_nucleus)
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, sw.nucleus_n, nullptr, stream,
+                               sw.rowp);
+        if (e == hipSuccess) e = launch_sparse_filter(src, rows, vocab, bf16, sps, m, sw, sw.sup, stream);
+        if (e == hipSuccess && m.any_dense)
+            e = launch_dense_support_scale(rows, sp->temperature, dc, sw.nucleus_n, sw.sup, stream, sw.rowp);
+    } else if (m.sparse) {
+        e = launch_sparse_filter(src, rows, vocab, bf16, sps, m, sw, sw.sup, stream);
     } else {
         // full-vocabulary filter: exact row normalisers (over the nucleus when
         // top-p is on), the K best ids, then their probabilities under the
@@ -507,6 +561,7 @@ int uno_build_tree_ex(const void* draft, int32_t dtype, int32_t batch, int32_t B
         Mode mk = m;
         mk.k = K;
         mk.topp_on = false;
+        mk.sparse = true;     // the K best ids come from the top-k stream
         e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
         if (e == hipSuccess && m.nucleus)
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, sw.nucleus_n, nullptr, stream);
@@ -533,8 +588,8 @@ int uno_verify_tree_ex(const void* target, int32_t dtype, int32_t batch, int32_t
     const RowMap map{ 2, batch, B, V + 1 };
     Carve sizing{ nullptr };
     Mode m;
-    SparseWs sw;
-    DenseChunks dc;
+    SparseWs sw{};
+    DenseChunks dc{};
     int st = layout_tree(UNO_OP_VERIFY_TREE, batch, B, 1, V, vocab, dtype, sps, sizing, &m, &sw, &dc);
     if (st) return st;
     if (batch == 0) return UNO_OK;
@@ -550,22 +605,25 @@ int uno_verify_tree_ex(const void* target, int32_t dtype, int32_t batch, int32_t
     const int64_t rows = (int64_t)batch * (V + 1);
     const bool bf16 = dtype == UNO_BF16;
     RowSource src{ static_cast<const char*>(target), rows, nullptr, num_nodes, V + 1 };
+    const FilterParams* rowp = m.per_request ? sw.rowp : nullptr;
     WalkOut o{ out_tokens, out_path, out_accept_len, out_flags };
-    hipError_t e;
-    if (m.sparse) {
-        e = launch_sparse_filter(src, rows, vocab, bf16, sps, map, m, sw, sw.sup, stream);
+    hipError_t e = hipSuccess;
+    if (m.per_request) e = expand_row_params(sps, vocab, map, sw, 0, stream);
+    if (e == hipSuccess && m.any_sparse) {
+        e = launch_sparse_filter(src, rows, vocab, bf16, sps, m, sw, sw.sup, stream);
         if (e == hipSuccess)
             e = launch_tree_walk(batch, B, V, sw.sup, seed, offset, request_ids, node_token, node_parent,
-                                 num_nodes, o, stream);
-    } else {
+                                 num_nodes, o, stream, rowp);
+    }
+    if (e == hipSuccess && m.any_dense) {
         // every node row a walk may sample gets exact chunk statistics (and
         // its nucleus when top-p is on)
-        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream);
-        if (e == hipSuccess && m.nucleus)
-            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream);
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream, rowp, kChunkDenseRows);
+        if (e == hipSuccess && m.any_nucleus)
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream, rowp);
         if (e == hipSuccess)
             e = launch_tree_walk_dense(src, batch, B, V, vocab, bf16, sp->temperature, dc, seed, offset,
-                                       request_ids, node_token, node_parent, num_nodes, o, stream);
+                                       request_ids, node_token, node_parent, num_nodes, o, stream, rowp);
     }
     return hip_status(e);
 }

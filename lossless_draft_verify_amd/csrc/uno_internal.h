@@ -19,6 +19,11 @@ struct RowSource {
     int32_t rows_per_req;
 };
 
+// How a row is filtered (FilterParams::dense).
+constexpr int32_t kRowTopK = 0;      // top-k path (greedy, top-k on, or a small vocabulary)
+constexpr int32_t kRowFull = 1;      // full softmax (top-k off, top-p off)
+constexpr int32_t kRowNucleus = 2;   // full-vocabulary nucleus (top-k off, top-p on)
+
 struct FilterParams {
     float temperature;
     float top_p;
@@ -34,6 +39,12 @@ struct FilterParams {
     // ... or, with joint set, the top-k stream sums the normaliser itself
     // (whole rows only, launched with joint_sums)
     int32_t joint;
+    // kRowTopK / kRowFull / kRowNucleus: the dense kernels take the rows (and
+    // the requests) that are not kRowTopK, the top-k samplers the others
+    int32_t dense;
+    // the top-k stream and merge leave this row alone (a full-vocabulary row of
+    // a call that samples it with the dense kernels)
+    int32_t skip_topk;
 };
 
 // Compact per-row supports in filter order.
@@ -77,8 +88,9 @@ struct RowMap {
     }
 };
 
-// Per-request filter parameters passed by value to launch_expand_params.
-constexpr int kParamSlots = 32;
+// Per-request filter parameters passed by value to launch_expand_params
+// (64 sets: about 3 KB of kernel arguments).
+constexpr int kParamSlots = 64;
 struct ParamArgs {
     FilterParams p[kParamSlots];
 };
@@ -104,20 +116,27 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
                               uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap,
                               const FilterParams* rowp, bool joint_sums, hipStream_t stream);
 
-// out[r] = a.p[map.req(r) - first] for the rows whose request lies in
-// [first, first + n), n <= kParamSlots.
-hipError_t launch_expand_params(const ParamArgs& a, int64_t first, int n, const RowMap& map, int64_t rows,
-                                FilterParams* out, hipStream_t stream);
+// out[r] = a.p[map.req(r) - first] for every row r whose request lies in
+// [first, first + n), n <= kParamSlots (only those rows are written).
+hipError_t launch_expand_params(const ParamArgs& a, int64_t first, int n, const RowMap& map, FilterParams* out,
+                                hipStream_t stream);
+
+// Which rows a chunk pass with per-row parameters takes.
+constexpr int kChunkJointRows = 1;   // rows whose set is in the joint order (full_cmax set)
+constexpr int kChunkDenseRows = 2;   // rows whose set is not kRowTopK
 
 // Rows below exact_rows get exact (fp64 exp) chunk sums; the rest fast ones.
-// rowp (nullable, device): per-row parameters; rows whose entry has no
-// full_cmax are skipped (nothing read or written).
+// rowp (nullable, device): per-row parameters; the pass then takes only the
+// rows `select` names (nothing read or written for the others), each at its
+// own temperature, and joint-order and nucleus rows always get exact sums.
 hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                                float temperature, const DenseChunks& dc, int64_t exact_rows, hipStream_t stream,
-                               const FilterParams* rowp = nullptr);
+                               const FilterParams* rowp = nullptr, int select = 0);
 
+// rowp (nullable): per-row temperatures; only the kRowFull rows are written.
 hipError_t launch_dense_row_stats(int64_t rows, float temperature, const DenseChunks& dc,
-                                  int32_t* out_count, double* out_stats, hipStream_t stream);
+                                  int32_t* out_count, double* out_stats, hipStream_t stream,
+                                  const FilterParams* rowp = nullptr);
 
 struct LinearOut {
     int32_t* tokens;
@@ -126,9 +145,11 @@ struct LinearOut {
     uint32_t* flags;
 };
 
+// rowp (nullable): per-row parameters; requests whose rows skip the top-k
+// stream are left to the dense samplers.
 hipError_t launch_linear_sparse(int32_t batch, int32_t B, const SparseOut& sup, uint64_t seed,
                                 uint64_t offset, const uint32_t* request_ids, const LinearOut& o,
-                                hipStream_t stream);
+                                hipStream_t stream, const FilterParams* rowp = nullptr);
 
 // Scratch of the dense linear path.
 struct DenseScratch {
@@ -142,19 +163,24 @@ struct DenseScratch {
 
 // With exact_all every row's chunk sums are already exact (the nucleus needs
 // them); otherwise target rows have fast sums and the row each request draws
-// its last token from is recomputed exactly.
+// its last token from is recomputed exactly.  rowp (nullable): per-row
+// parameters; only the requests whose rows are not kRowTopK are sampled, each
+// at its own temperature (a nucleus request's target rows are exact already).
 hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, int64_t vocab,
                                bool bf16, float temperature, const DenseChunks& dc,
                                const DenseScratch& sc, uint64_t seed, uint64_t offset,
                                const uint32_t* request_ids, const LinearOut& o, bool exact_all,
-                               hipStream_t stream);
+                               hipStream_t stream, const FilterParams* rowp = nullptr);
 
 // Full-vocabulary nucleus (top-p without top-k) of `rows` rows with exact chunk
 // statistics in dc: writes dc.keep, rewrites dc.csum to sums over each row's
 // support, and (when non-null) the support sizes and (m, S) statistics.
+// rowp (nullable): per-row parameters; kRowNucleus rows are cut at their own
+// temperature and top_p, kRowFull rows get keep = 0 (the whole vocabulary),
+// kRowTopK rows are left alone.
 hipError_t launch_nucleus(const RowSource& src, int64_t rows, int64_t vocab, bool bf16, float temperature,
                           float top_p, const DenseChunks& dc, int32_t* out_count, double* out_stats,
-                          hipStream_t stream);
+                          hipStream_t stream, const FilterParams* rowp = nullptr);
 
 struct TreeOut {
     int32_t* node_token;
@@ -174,24 +200,32 @@ struct WalkOut {
     uint32_t* flags;
 };
 
+// rowp (nullable): requests whose rows skip the top-k stream are left to the
+// dense walk.
 hipError_t launch_tree_walk(int32_t batch, int32_t B, int32_t V, const SparseOut& sup,
                             uint64_t seed, uint64_t offset, const uint32_t* request_ids,
                             const int32_t* node_token, const int32_t* node_parent,
-                            const int32_t* num_nodes, const WalkOut& o, hipStream_t stream);
+                            const int32_t* num_nodes, const WalkOut& o, hipStream_t stream,
+                            const FilterParams* rowp = nullptr);
 
 // Dense tree mode (filters without top-k).  The build takes the top-K supports
 // and rescales them to the full softmax, or to the nucleus when the chunk sums
 // are over a nucleus (sup.stats holds the top-K normaliser on entry, the new
 // one on exit); `limit` (nullable) caps each row's count at its nucleus size.
 // The walk samples node rows from exact chunk statistics.
+// rowp (nullable): only the rows that are not kRowTopK are rescaled (each at
+// its own temperature), and `limit` applies to the kRowNucleus rows.
 hipError_t launch_dense_support_scale(int64_t rows, float temperature, const DenseChunks& dc,
-                                      const int32_t* limit, const SparseOut& sup, hipStream_t stream);
+                                      const int32_t* limit, const SparseOut& sup, hipStream_t stream,
+                                      const FilterParams* rowp = nullptr);
 
+// rowp (nullable): only the requests whose rows are not kRowTopK walk here,
+// each at its own temperature.
 hipError_t launch_tree_walk_dense(const RowSource& src, int32_t batch, int32_t B, int32_t V, int64_t vocab,
                                   bool bf16, float temperature, const DenseChunks& dc, uint64_t seed,
                                   uint64_t offset, const uint32_t* request_ids, const int32_t* node_token,
                                   const int32_t* node_parent, const int32_t* num_nodes, const WalkOut& o,
-                                  hipStream_t stream);
+                                  hipStream_t stream, const FilterParams* rowp = nullptr);
 
 // Tree-suffix attention merged with the prefix state (head dimension 128,
 // bf16 tensors, fp32 log-sum-exps); one workgroup per (request, kv head).

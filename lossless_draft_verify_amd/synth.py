@@ -40,13 +40,17 @@ class Workload:
     K: int = 1
     V: int = 0
     order: int = 0       # filter order: 0 top-k first, 1 joint
-    mixed: bool = False  # request b takes MIXED_SETS[b % len] instead of the scalars above
+    sets: tuple = ()     # per-request sets: request b takes sets[b % len] instead of the scalars above
     note: str = field(default="", compare=False)
+
+    @property
+    def mixed(self) -> bool:
+        return len(self.sets) > 0
 
     def request_params(self, b: int):
         """(temperature, top_k, top_p, order) of request b."""
-        if self.mixed:
-            return MIXED_SETS[b % len(MIXED_SETS)]
+        if self.sets:
+            return self.sets[b % len(self.sets)]
         return (self.temperature, self.top_k, self.top_p, self.order)
 
     @property
@@ -75,8 +79,14 @@ def _const(v, n):
 
 # Per-request parameter sets of the mixed workload: greedy, the pages' top-k 50 /
 # top-p 0.95, no top-p, a large k, a tiny k and the joint order.
-MIXED_SETS = [(0.0, 0, 1.0, 0), (1.0, 50, 0.95, 0), (0.7, 20, 1.0, 0), (1.3, 256, 0.9, 0), (1.0, 3, 0.5, 0),
-              (1.0, 50, 0.9, 1), (0.5, 8, 0.8, 0), (1.0, 100, 0.99, 1)]
+MIXED_SETS = ((0.0, 0, 1.0, 0), (1.0, 50, 0.95, 0), (0.7, 20, 1.0, 0), (1.3, 256, 0.9, 0), (1.0, 3, 0.5, 0),
+              (1.0, 50, 0.9, 1), (0.5, 8, 0.8, 0), (1.0, 100, 0.99, 1))
+
+# Per-request sets over both paths: greedy, top-k 50 / top-p 0.95, the full
+# softmax at two temperatures, a nucleus without top-k, joint-order sets at two
+# temperatures and a large k.
+MIXED_FULL_SETS = ((0.0, 0, 1.0, 0), (1.0, 50, 0.95, 0), (1.0, 0, 1.0, 0), (0.8, 0, 0.9, 0), (1.0, 50, 0.9, 1),
+                   (0.7, 100, 0.9, 1), (1.3, 256, 0.9, 0), (0.6, 0, 1.0, 0))
 
 WORKLOADS = {
     "tiny": Workload("tiny", "linear", batch=2, B=4, vocab=1000, dtype="f32", slope=1.0,
@@ -97,8 +107,14 @@ WORKLOADS = {
     "linear_8_1_8_mixed": Workload("linear_8_1_8_mixed", "linear", batch=64, B=8, vocab=VOCAB_QWEN3,
                                    dtype="f32", slope=1.2,
                                    sigma=tuple(0.3 + 0.1 * j for j in range(8)), temperature=1.0,
-                                   top_k=50, top_p=0.95, seed=42, cycles=1000, mixed=True,
+                                   top_k=50, top_p=0.95, seed=42, cycles=1000, sets=MIXED_SETS,
                                    note="Linear 8/1/8, 64 requests, per-request parameters"),
+    # the headline shape with per-request sets that mix top-k and full-vocabulary rows
+    "linear_8_1_8_mixed_full": Workload("linear_8_1_8_mixed_full", "linear", batch=64, B=8, vocab=VOCAB_QWEN3,
+                                        dtype="f32", slope=1.2,
+                                        sigma=tuple(0.3 + 0.1 * j for j in range(8)), temperature=1.0,
+                                        top_k=50, top_p=0.95, seed=42, cycles=1000, sets=MIXED_FULL_SETS,
+                                        note="Linear 8/1/8, 64 requests, top-k and full-vocabulary sets"),
     # the headline shape with top-k off: a full-vocabulary nucleus at top-p 0.95
     "linear_8_1_8_nucleus": Workload("linear_8_1_8_nucleus", "linear", batch=64, B=8, vocab=VOCAB_QWEN3,
                                      dtype="f32", slope=1.2,

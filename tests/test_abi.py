@@ -240,10 +240,20 @@ def test_per_request_parameter_checks(lib):
     # supports sized for the largest k (256), plus one parameter set per row
     assert nmix >= 4 * 17 * 256 * 12 + 4 * 17 * 40
     assert ws(uno.OP_SAMPLE_LINEAR, 3, mixed)[0] == INVALID            # one set per request
+    # top-k sets beside full-softmax and nucleus sets: the call also holds
+    # chunk statistics of every row (max fp32 + sum fp64 per 2048-logit chunk)
+    # and the dense samplers' scratch
     dense = _sp_array((1.0, 50, 0.95, 0), (1.0, 0, 1.0, 0))
-    assert ws(uno.OP_SAMPLE_LINEAR, 2, dense)[0] == UNSUPPORTED        # top-k off: not per request
+    st, nd = ws(uno.OP_SAMPLE_LINEAR, 2, dense)
+    assert st == OK and nd >= 2 * 17 * 75 * 12
+    nuc = _sp_array((0.7, 0, 0.9, 0), (1.3, 0, 1.0, 0))
+    assert ws(uno.OP_SAMPLE_LINEAR, 2, nuc)[0] == OK
     joint_t = _sp_array((1.0, 50, 0.9, 1), (0.5, 50, 0.9, 1))
-    assert ws(uno.OP_SAMPLE_LINEAR, 2, joint_t)[0] == UNSUPPORTED      # joint sets with two temperatures
+    assert ws(uno.OP_SAMPLE_LINEAR, 2, joint_t)[0] == OK               # joint sets, each at its own temperature
+    # a full-vocabulary build takes its K candidates from the top-k stream
+    st, _ = (lib.uno_workspace_bytes_ex(uno.OP_BUILD_TREE, 2, 2, 300, 2, N, F32, dense[0], dense[1],
+                                        ctypes.byref(n)), 0)
+    assert st == UNSUPPORTED
     bad = _sp_array((1.0, 50, 0.95, 0), (-1.0, 50, 0.95, 0))
     assert ws(uno.OP_SAMPLE_LINEAR, 2, bad)[0] == INVALID
     assert ws(uno.OP_BUILD_TREE, 4, mixed)[0] == OK

@@ -61,19 +61,21 @@ def test_linear_dense_reduced():
 
 
 def test_linear_dense_full_size_sampled_requests():
-    # full batch 256 in one launch; the oracle checks a sample of the requests
+    # full batch 256 in one launch; the oracle checks 16 requests spread over it
     dev = device()
     w = synth.WORKLOADS["linear_dense"]
     draft, target = synth.linear_inputs(w, cycle=0, device=dev)
     g = uno.sample_linear(draft, target, w.temperature, w.top_k, w.top_p, w.seed, 0)
     torch.cuda.synchronize()
-    pick = np.array([0, 1, 77, 128, 200, 255])
-    o = oracle.linear(synth.as_float32_numpy(draft[pick]), synth.as_float32_numpy(target[pick]),
+    pick = np.array([0, 1, 17, 40, 63, 77, 100, 128, 141, 170, 199, 200, 222, 240, 254, 255])
+    pt = torch.from_numpy(pick).to(dev)
+    o = oracle.linear(synth.as_float32_numpy(draft[pt]), synth.as_float32_numpy(target[pt]),
                       w.temperature, w.top_k, w.top_p, seed=w.seed, offset=0,
                       request_ids=pick.astype(np.uint32))
-    t = Tally()
+    t = Tally("linear_dense b256 sample")
     gg = {k: np_of(g[k])[pick] for k in ("tokens", "accept_len", "proposals")}
     t.compare(gg, o, ("tokens", "accept_len", "proposals"), "linear_dense b256 sample")
+    t.check_rate()
     acc = np_of(g["accept_len"])
     assert acc.min() >= 1 and acc.max() <= w.B + 1
     say(f"linear_dense b256: mean accept_len {acc.mean():.3f}, excused {t.excused}")
