@@ -64,7 +64,8 @@ typedef enum {
     UNO_ERR_INVALID_ARG = -1,   /* a size, pointer or parameter is out of range      */
     UNO_ERR_UNSUPPORTED = -2,   /* valid request the library does not implement      */
     UNO_ERR_WORKSPACE = -3,     /* ws is NULL, too small or misaligned                 */
-    UNO_ERR_HIP = -4            /* a HIP launch failed (see uno_last_hip_error)        */
+    UNO_ERR_HIP = -4,           /* a HIP launch failed (see uno_last_hip_error)        */
+    UNO_ERR_SCRATCH_LIMIT = -5  /* the allocation-free entry point's fixed scratch is too small */
 } uno_status_t;
 
 typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype_t;
@@ -263,6 +264,28 @@ int uno_tree_attention(const void* q, const void* k, const void* v, const void* 
                        const float* lse_prefix, const int32_t* node_parent, const int32_t* num_nodes,
                        int32_t dtype, int32_t batch, int32_t n, int32_t Hq, int32_t Hkv, int32_t D,
                        float scale, void* out, float* out_lse, hipStream_t stream);
+
+/* Allocation-free linear cycle, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  uno_sample_linear with the same arguments, but without a
+ * workspace argument: the workspace is a fixed array of
+ * UNO_NOALLOC_SCRATCH_BYTES in device memory that the library holds on each
+ * GPU it runs on until the process ends (its address is looked up once per
+ * device, on the first call there).  The call allocates nothing and calls no
+ * allocating routine.  A call whose workspace (uno_workspace_bytes for
+ * UNO_OP_SAMPLE_LINEAR with the same arguments) exceeds the array returns
+ * UNO_ERR_SCRATCH_LIMIT and launches nothing; other errors as for
+ * uno_sample_linear.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (different streams, or threads not ordered with each
+ * other) race and must be serialised by the caller; the array keeps the last
+ * call's contents, which no call reads before writing.  The GPU is the one
+ * `stream` belongs to (the current device for the null stream). */
+#define UNO_NOALLOC_SCRATCH_BYTES (32u << 20)
+int uno_sample_linear_noalloc(const void* draft, const void* target, int32_t dtype, int32_t batch,
+                              int32_t B, int64_t vocab, const uno_sampling_t* sp, uint64_t seed,
+                              uint64_t offset, const uint32_t* request_ids,
+                              int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_proposals,
+                              uint32_t* out_flags, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* uno_status_string(int status);

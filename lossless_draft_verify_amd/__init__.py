@@ -31,7 +31,9 @@ OP_FILTER, OP_SAMPLE_LINEAR, OP_BUILD_TREE, OP_VERIFY_TREE = 0, 1, 2, 3
 MAX_TOP_K = 256
 ORDER_TOPK_FIRST, ORDER_JOINT = 0, 1     # uno_order_t
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
-           -3: "workspace missing, too small or misaligned", -4: "HIP launch failure"}
+           -3: "workspace missing, too small or misaligned", -4: "HIP launch failure",
+           -5: "workspace exceeds the allocation-free entry point's fixed scratch"}
+NOALLOC_SCRATCH_BYTES = 32 << 20       # UNO_NOALLOC_SCRATCH_BYTES
 
 
 class UnoError(RuntimeError):
@@ -79,9 +81,11 @@ def load_library():
                                            P, P, P, ctypes.c_size_t, P]
         lib.uno_tree_attention.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                            P, P, P]
+        lib.uno_sample_linear_noalloc.argtypes = [P, P, i32, i32, i32, i64, SP, u64, u64, P, P, P, P, P, P]
         for f in ("uno_workspace_bytes", "uno_filter", "uno_sample_linear", "uno_build_tree",
                   "uno_verify_tree", "uno_tree_attention", "uno_last_hip_error", "uno_workspace_bytes_ex",
-                  "uno_filter_ex", "uno_sample_linear_ex", "uno_build_tree_ex", "uno_verify_tree_ex"):
+                  "uno_filter_ex", "uno_sample_linear_ex", "uno_build_tree_ex", "uno_verify_tree_ex",
+                  "uno_sample_linear_noalloc"):
             getattr(lib, f).restype = ctypes.c_int
         lib.uno_status_string.argtypes = [ctypes.c_int]
         lib.uno_status_string.restype = ctypes.c_char_p

@@ -702,6 +702,7 @@ const char* uno_status_string(int status)
     case UNO_ERR_UNSUPPORTED: return "unsupported configuration";
     case UNO_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case UNO_ERR_HIP: return "HIP launch failure";
+    case UNO_ERR_SCRATCH_LIMIT: return "workspace exceeds the allocation-free entry point's fixed scratch";
     default: return "unknown status";
     }
 }

@@ -259,3 +259,18 @@ def test_per_request_parameter_checks(lib):
     assert ws(uno.OP_BUILD_TREE, 4, mixed)[0] == OK
     assert ws(uno.OP_VERIFY_TREE, 4, mixed)[0] == OK
     assert ws(uno.OP_FILTER, 4, mixed)[0] == OK
+
+
+def test_noalloc_rejects_workspace_beyond_its_scratch(lib):
+    # the size check runs on the host before anything else: a dense linear call
+    # whose chunk statistics alone exceed the fixed scratch is refused
+    N = 151936
+    need = _ws(lib, uno.OP_SAMPLE_LINEAR, 1200, 16, 1, 16, N, BF16, sp(0.7, 0, 1.0))[1]
+    assert need > uno.NOALLOC_SCRATCH_BYTES
+    f = lib.uno_sample_linear_noalloc
+    o = ctypes.c_void_p(0x30000)
+    assert f(FAKE, FAKE, BF16, 1200, 16, N, sp(0.7, 0, 1.0), 1, 0, None, o, o, None, None, None) == -5
+    assert lib.uno_status_string(-5) not in (b"ok", b"unknown status")
+    # argument errors come first, as for uno_sample_linear
+    assert f(FAKE, FAKE, F32, 2, 0, 1000, sp(), 1, 0, None, o, o, None, None, None) == INVALID
+    assert f(FAKE, FAKE, F32, 2, 4, 1000, None, 1, 0, None, o, o, None, None, None) == INVALID
