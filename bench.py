@@ -99,6 +99,49 @@ def traffic_probe(args, w, lib, pool, dt, sp, stream, dev):
         f"of {src.numel() * src.element_size()} bytes")
 
 
+def read_reference(lib, pool, nbytes, row_bytes, n, stream, dev):
+    """Achievable streaming rate on this device: uno_stream_read over the same
+    rows the filter reads, once with one workgroup per row (the top-k stream's
+    decomposition) and once in 2048 equal ranges; HIP events on the launch
+    stream over n launches each."""
+    import ctypes
+    import torch
+    out = {"bytes": nbytes}
+    res = torch.empty(nbytes // row_bytes + 4096, dtype=torch.int32, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flat = (nbytes // 2048 + 15) // 16 * 16
+    for key, wg in (("row_per_workgroup", row_bytes), ("flat", flat)):
+        def go(i):
+            st = lib.uno_stream_read(ctypes.c_void_p(pool[i % len(pool)]["all"].data_ptr()), nbytes, wg,
+                                     ctypes.c_void_p(res.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+            assert st == 0, st
+        for i in range(10):
+            go(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(n):
+            go(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / n
+        out[key + "_us"] = round(us, 2)
+        out[key + "_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        log(f"[bench] read-only reference ({key}, {nbytes // wg} workgroups): {us:.1f} us -> "
+            f"{out[key + '_gbs']:.0f} GB/s")
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def bench_tree_attention(args, uno, synth, dev):
     """uno_tree_attention at a tree workload's verify shape: K timed calls."""
     import torch
@@ -146,7 +189,8 @@ def bench_tree_attention(args, uno, synth, dev):
             reps += 1
         el = time.perf_counter() - t0
         cpu = {"value": round(reps * T / el, 1), "unit": "verify tokens/s", "cores": oracle.num_threads(),
-               "kind": "oracle", "sample": f"{reps} calls of {args.workload} ({T} tokens each), {el:.1f} s"}
+               "cpu_model": cpu_model(), "kind": "oracle",
+               "sample": f"{reps} calls of {args.workload} ({T} tokens each), {el:.1f} s"}
     res = {
         "metric": "verify tokens/s (tree-suffix attention merged with the prefix state)",
         "value": round(T / (us * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -335,11 +379,15 @@ def main():
         alg_bytes = nrows * w.vocab * w.elem_bytes
         achieved = alg_bytes / (k_us * 1e-6) / 1e9
         traffic = traffic_entry()
+        ref = read_reference(lib, pool, alg_bytes, w.vocab * w.elem_bytes, n_f, stream, dev)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": DOMINANT, "kernel_us": round(k_us, 2), "bytes_per_launch": alg_bytes}
+                    "kernel": DOMINANT, "kernel_us": round(k_us, 2), "bytes_per_launch": alg_bytes,
+                    "read_reference": ref,
+                    "frac_of_read_reference": round(achieved / ref["flat_gbs"], 4)}
         log(f"[bench] {DOMINANT}: {k_us:.1f} us/launch over {n_f} launches -> {achieved:.0f} GB/s "
-            f"({100 * achieved / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+            f"({100 * achieved / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}, "
+            f"{100 * achieved / ref['flat_gbs']:.1f}% of the read-only reference)")
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload ----------
     cpu = None
@@ -380,7 +428,8 @@ def main():
                 n_req += hi - lo
                 rows += (hi - lo) * (w.B + w.V + 1)
         el = time.perf_counter() - t0
-        cpu = {"value": round(rows / el, 1), "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
+        cpu = {"value": round(rows / el, 1), "unit": "rows/s", "cores": oracle.num_threads(),
+               "cpu_model": cpu_model(), "kind": "oracle",
                "sample": f"{n_req} request-cycles ({rows} rows) of {w.name}, {el:.1f} s"}
         log(f"[bench] oracle: {rows / el:.0f} rows/s on {oracle.num_threads()} threads ({n_req} requests)")
 

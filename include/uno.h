@@ -287,6 +287,16 @@ int uno_sample_linear_noalloc(const void* draft, const void* target, int32_t dty
                               int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_proposals,
                               uint32_t* out_flags, hipStream_t stream);
 
+/* Measurement aid, not part of the sampling path: reads `bytes` of device
+ * memory at `buf` once, in ranges of wg_bytes per workgroup, with the load
+ * idiom of the top-k stream (16-byte non-temporal loads, the next iteration's
+ * loads in flight), and writes one folded word per workgroup to
+ * out[ceil(bytes / wg_bytes)].  Its duration is the achievable streaming rate
+ * of that decomposition on the device (wg_bytes = one logit row: the top-k
+ * stream's; small equal ranges: the chip's).  bytes and wg_bytes must be
+ * multiples of 16 and buf 16-byte aligned (else UNO_ERR_INVALID_ARG). */
+int uno_stream_read(const void* buf, int64_t bytes, int64_t wg_bytes, uint32_t* out, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* uno_status_string(int status);
 

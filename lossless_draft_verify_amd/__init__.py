@@ -82,10 +82,11 @@ def load_library():
         lib.uno_tree_attention.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                            P, P, P]
         lib.uno_sample_linear_noalloc.argtypes = [P, P, i32, i32, i32, i64, SP, u64, u64, P, P, P, P, P, P]
+        lib.uno_stream_read.argtypes = [P, i64, i64, P, P]
         for f in ("uno_workspace_bytes", "uno_filter", "uno_sample_linear", "uno_build_tree",
                   "uno_verify_tree", "uno_tree_attention", "uno_last_hip_error", "uno_workspace_bytes_ex",
                   "uno_filter_ex", "uno_sample_linear_ex", "uno_build_tree_ex", "uno_verify_tree_ex",
-                  "uno_sample_linear_noalloc"):
+                  "uno_sample_linear_noalloc", "uno_stream_read"):
             getattr(lib, f).restype = ctypes.c_int
         lib.uno_status_string.argtypes = [ctypes.c_int]
         lib.uno_status_string.restype = ctypes.c_char_p

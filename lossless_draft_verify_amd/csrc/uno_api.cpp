@@ -694,6 +694,15 @@ int uno_tree_attention(const void* q, const void* k, const void* v, const void* 
                                             static_cast<uint16_t*>(out), out_lse, stream));
 }
 
+int uno_stream_read(const void* buf, int64_t bytes, int64_t wg_bytes, uint32_t* out, hipStream_t stream)
+{
+    if (bytes < 0 || wg_bytes <= 0 || bytes % 16 != 0 || wg_bytes % 16 != 0) return UNO_ERR_INVALID_ARG;
+    if (bytes == 0) return UNO_OK;
+    if ((bytes + wg_bytes - 1) / wg_bytes > 0x7FFFFFFF) return UNO_ERR_INVALID_ARG;
+    if (buf == nullptr || out == nullptr || !aligned(buf, 16)) return UNO_ERR_INVALID_ARG;
+    return hip_status(launch_stream_read(buf, bytes, wg_bytes, out, stream));
+}
+
 const char* uno_status_string(int status)
 {
     switch (status) {

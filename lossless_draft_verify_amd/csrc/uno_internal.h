@@ -234,4 +234,8 @@ hipError_t launch_tree_attention(const uint16_t* q, const uint16_t* k, const uin
                                  int32_t batch, int32_t n, int32_t Hq, int32_t Hkv, float scale, uint16_t* out,
                                  float* out_lse, hipStream_t stream);
 
+// Read-only streaming reference: workgroup g reads bytes [g*wg_bytes,
+// (g+1)*wg_bytes) of buf once and writes one folded word to out[g].
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int64_t wg_bytes, uint32_t* out, hipStream_t stream);
+
 }  // namespace uno

@@ -274,3 +274,14 @@ def test_noalloc_rejects_workspace_beyond_its_scratch(lib):
     # argument errors come first, as for uno_sample_linear
     assert f(FAKE, FAKE, F32, 2, 0, 1000, sp(), 1, 0, None, o, o, None, None, None) == INVALID
     assert f(FAKE, FAKE, F32, 2, 4, 1000, None, 1, 0, None, o, o, None, None, None) == INVALID
+
+
+def test_stream_read_argument_checks(lib):
+    o = ctypes.c_void_p(0x30000)
+    f = lib.uno_stream_read
+    assert f(FAKE, 1000, 16, o, None) == INVALID          # bytes not a multiple of 16
+    assert f(FAKE, 1024, 24, o, None) == INVALID          # range not a multiple of 16
+    assert f(FAKE, 1024, 0, o, None) == INVALID
+    assert f(FAKE_ODD, 1024, 16, o, None) == INVALID      # misaligned buffer
+    assert f(FAKE, 1024, 16, None, None) == INVALID
+    assert f(None, 0, 16, None, None) == OK               # nothing to read

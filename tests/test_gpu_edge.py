@@ -124,3 +124,24 @@ def test_side_stream_matches_default_stream():
         s.synchronize()
         for key in ("tokens", "accept_len", "proposals"):
             assert torch.equal(got[key], ref[key]), key
+
+
+@pytest.mark.parametrize("nbytes,wg", [(607744 * 5, 607744), (1 << 20, 4096), (16 * 1000 + 48, 1024)])
+def test_stream_read_folds_every_word_once(nbytes, wg):
+    # the bandwidth reference reads each 16-byte vector of its range exactly
+    # once: per workgroup, the XOR of all its 32-bit words
+    dev = device()
+    lib = uno.load_library()
+    import ctypes
+    rng = np.random.default_rng(65)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(dev)
+    groups = (nbytes + wg - 1) // wg
+    out = torch.zeros(groups, dtype=torch.int32, device=dev)
+    st = lib.uno_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, wg, ctypes.c_void_p(out.data_ptr()),
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    got = np_of(out).view(np.uint32)
+    words = wg // 4
+    want = [np.bitwise_xor.reduce(host[g * words:(g + 1) * words]) for g in range(groups)]
+    assert np.array_equal(got, np.array(want, dtype=np.uint32))
