@@ -627,13 +627,18 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
 #pragma unroll
         for (int d = 0; d < kStreamDepth - 1; ++d) load_iter(d, xr[d]);
         if (cnt == 0 && k <= kWave) {
-            // Seed the threshold from the first iteration: the k-th largest lane
-            // maximum has at least k logits at or above it, all admitted below.
+            // Seed the threshold from the first two iterations (only the first
+            // when there is no second: a shape-only load holds one lane's data):
+            // the k-th largest lane maximum has at least k logits at or above
+            // it, all admitted below.
             float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, V::get(xr[0][u], e));
+                for (int e = 0; e < EPV; ++e) {
+                    mx = fmaxf(mx, V::get(xr[0][u], e));
+                    if (kStreamDepth > 2 && nfull > 1) mx = fmaxf(mx, V::get(xr[1][u], e));
+                }
             uint32_t km = float_key(mx);
             km = (km <= kKeyPosInf && km > kKeyNegInf) ? km : kKeyNegInf;
             const uint32_t t0 = wave_kth_largest_of_lanes(km, k);
