@@ -218,12 +218,19 @@ __device__ __forceinline__ int block_rank_topk(const uint2* lst, int stride, con
             ok[g] = order_key(c.x, (int32_t)c.y);
         }
         __syncthreads();
+        // sixteen keys per step, read as eight 16-byte words (ok is 16-byte aligned)
+        const ulonglong2* ok2 = reinterpret_cast<const ulonglong2*>(ok);
         for (int g = tid; g < n; g += nthreads) {
             const uint64_t p = ok[g];
             int rank = 0;
             int j = 0;
-            for (; j + 4 <= n; j += 4)
-                rank += (ok[j] > p) + (ok[j + 1] > p) + (ok[j + 2] > p) + (ok[j + 3] > p);
+            for (; j + 16 <= n; j += 16) {
+                ulonglong2 a[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) a[t] = ok2[(j >> 1) + t];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) rank += (a[t].x > p) + (a[t].y > p);
+            }
             for (; j < n; ++j) rank += (ok[j] > p);
             place(p, rank);
         }
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     __shared__ uint32_t s_sk[kMaxK];
     __shared__ int32_t s_sid[kMaxK];
     __shared__ double s_e[kMaxK];
-    __shared__ double s_cx[kMaxK + 1];
+    __shared__ __align__(16) double s_cx[kMaxK + 1];
     __shared__ double s_scal[1];
     __shared__ uint32_t s_b[kWaves];
     __shared__ uint32_t s_mx[kWaves];
@@ -677,17 +684,17 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     // block would rank several times k entries, so there b is the wave's own
     // q-th largest key (truncated to 24 bits).
     const int quota = (k + kWaves - 1) / kWaves;
+    // the wave's candidates, read once into registers as (key, id); padding
+    // slots hold key 0, below every admitted key
+    RegList<kCapE> L;
+    reg_load(L, buf, cnt, lane);
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int q = 0; q < kCapE; ++q) lmax = L.kv[q] > lmax ? L.kv[q] : lmax;
     uint32_t b = 0;
     if (cnt >= quota && quota > kWave / 2) {
-        RegList<kCapE> L;
-        reg_load(L, buf, cnt, lane);
         b = reg_kth_key(L, quota, 8);
     } else if (cnt >= quota) {
-        uint32_t lmax = 0;
-        for (int j = lane; j < cnt; j += kWave) {
-            const uint32_t kj = float_key(__uint_as_float(buf[j].x));
-            lmax = kj > lmax ? kj : lmax;
-        }
         // largest 16-bit prefix t with at least quota lane maxima >= t
         for (int bit = 31; bit >= 16; --bit) {
             const uint32_t cand = b | (1u << bit);
@@ -710,23 +717,17 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     for (int o = 1; o < kWaves; ++o) B = s_b[o] < B ? s_b[o] : B;
     // this wave's entries with key >= B, compacted in place as (key, id)
     int ns = 0;
-    uint32_t mx = 0;
-    for (int j = 0; j < cnt; j += kWave) {
-        const int i = j + lane;
-        uint2 c = make_uint2(0u, 0u);
-        bool keep = false;
-        if (i < cnt) {
-            c = buf[i];
-            c.x = float_key(__uint_as_float(c.x));
-            keep = c.x >= B;
-            mx = c.x > mx ? c.x : mx;
-        }
+#pragma unroll
+    for (int q = 0; q < kCapE; ++q) {
+        if (q * kWave >= cnt) break;
+        const bool keep = L.kv[q] != 0u && L.kv[q] >= B;
         const uint64_t mk = __ballot(keep);
         if (keep)
-            buf[(int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, (uint32_t)ns))] = c;
+            buf[(int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, (uint32_t)ns))] =
+                make_uint2(L.kv[q], (uint32_t)L.iv[q]);
         ns += __popcll(mk);
     }
-    mx = wave_max_u32(mx);
+    const uint32_t mx = wave_ext_u32<true>(lmax);
     if (lane == 0) { s_ns[w] = ns; s_mx[w] = mx; }
     __syncthreads();
     // softmax numerators are formed during the rank when this block finalises
@@ -771,7 +772,12 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
 
 // One workgroup per row: the S segment lists (each sorted, at most k entries)
 // are pruned by the best full list's k-th entry, ranked together and
-// finalised.  Every global read is spread over the workgroup.
+// finalised.  Every global read of the row -- its parameters, whether it is
+// present, the segment counts and all S lists (part_cap entries each, the
+// largest k) -- is issued before any is used, so the row pays one memory
+// round trip before its LDS work.
+constexpr int kMergePer = kMergeCap / kThreads;     // list entries per thread
+static_assert(kMaxSegments <= kWave, "the merge reduces the per-list bounds in one wave");
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     RowSource src, int64_t rows, FilterParams fp_all, SparseOut out, int S,
     const uint32_t* part_key, const int32_t* part_id, const int32_t* part_n, int part_cap,
@@ -781,93 +787,111 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
     __shared__ uint32_t s_sk[kMaxK];
     __shared__ int32_t s_sid[kMaxK];
     __shared__ double s_e[kMaxK];
-    __shared__ double s_cx[kMaxK + 1];
+    __shared__ __align__(16) double s_cx[kMaxK + 1];
     __shared__ double s_scal[1];
     __shared__ int s_segn[kMaxSegments];
-    __shared__ uint64_t s_wp[kWaves];
-    __shared__ uint64_t s_wq[kWaves];
-    __shared__ uint32_t s_wt[kWaves];
+    __shared__ uint32_t s_first[kMaxSegments];     // per list: its first key
+    __shared__ uint64_t s_kth[kMaxSegments];       // per list: order key of entry k - 1
+    __shared__ uint64_t s_qth[kMaxSegments];       // per list: order key of entry quota - 1
+    __shared__ uint64_t s_bound;
+    __shared__ uint32_t s_top;
     __shared__ int s_n;
 
     const int lane = lane_id();
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r = blockIdx.x;
     if (r >= rows) return;
+    const int tid = (int)threadIdx.x;
+    const int total = S * part_cap;              // <= kMergeCap (topk_segments)
+    const int64_t lbase = r * S * (int64_t)part_cap;
+    uint32_t ck[kMergePer];
+    int32_t ci[kMergePer];
+#pragma unroll
+    for (int j = 0; j < kMergePer; ++j) {
+        const int g = j * kThreads + tid;
+        ck[j] = 0u;
+        ci[j] = 0;
+        if (g < total) {
+            ck[j] = part_key[lbase + g];
+            ci[j] = part_id[lbase + g];
+        }
+    }
+    const int segn = tid < S ? part_n[r * S + tid] : 0;
     const FilterParams fp = rowp ? rowp[r] : fp_all;
+    const bool present = row_pointer(src, r, 1) != nullptr;
     if (fp.skip_topk) {
         pad_skipped_row(out, r);
         return;
     }
-    if (row_pointer(src, r, 1) == nullptr) {
-        if (threadIdx.x == 0) out.count[r] = -1;
+    if (!present) {
+        if (tid == 0) out.count[r] = -1;
         return;
     }
     const int k = fp.k;
-    // Per segment: its count, its first key, and two lower bounds on the row's
+    // Per list: its count, its first key, and two lower bounds on the row's
     // k-th entry -- the k-th entry of a full list, and (quota q = ceil(k/S)) the
     // smallest of the lists' q-th entries, valid when every list holds q.
     const int quota = (k + S - 1) / S;
-    uint64_t p = 0, pq = ~0ull;
-    uint32_t top = 0;
-    for (int sg = threadIdx.x; sg < S; sg += kThreads) {
-        const int64_t base = (r * S + sg) * (int64_t)part_cap;
-        const int ns = part_n[r * S + sg];
-        s_segn[sg] = ns;
-        if (ns > 0) top = part_key[base] > top ? part_key[base] : top;    // lists are sorted
-        if (ns == k) {
-            const uint64_t q = order_key(part_key[base + k - 1], part_id[base + k - 1]);
-            p = q > p ? q : p;
+    if (tid < S) s_segn[tid] = segn;
+#pragma unroll
+    for (int j = 0; j < kMergePer; ++j) {
+        const int g = j * kThreads + tid;
+        if (g < total) {
+            const int sg = g / part_cap, i = g - sg * part_cap;
+            if (i == 0) s_first[sg] = ck[j];
+            if (i == k - 1) s_kth[sg] = order_key(ck[j], ci[j]);
+            if (i == quota - 1) s_qth[sg] = order_key(ck[j], ci[j]);
         }
-        const uint64_t qq = (ns >= quota) ? order_key(part_key[base + quota - 1], part_id[base + quota - 1]) : 0ull;
-        pq = qq < pq ? qq : pq;
     }
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) {
-        const uint64_t po = __shfl_xor(p, d, kWave);
-        const uint64_t qo = __shfl_xor(pq, d, kWave);
-        const uint32_t to = __shfl_xor(top, d, kWave);
-        p = po > p ? po : p;
-        pq = qo < pq ? qo : pq;
-        top = to > top ? to : top;
-    }
-    if (lane == 0) { s_wp[w] = p; s_wq[w] = pq; s_wt[w] = top; }
-    if (threadIdx.x == 0) s_n = 0;
     __syncthreads();
-    uint64_t pstar = 0, pquota = ~0ull;
-    top = 0;
+    if (tid < kWave) {          // S <= kMaxSegments <= one wave
+        uint64_t p = 0, pq = ~0ull;
+        uint32_t top = 0;
+        if (lane < S) {
+            const int ns = s_segn[lane];
+            if (ns > 0) top = s_first[lane];    // lists are sorted
+            if (ns == k) p = s_kth[lane];
+            pq = (ns >= quota) ? s_qth[lane] : 0ull;
+        }
 #pragma unroll
-    for (int o = 0; o < kWaves; ++o) {
-        pstar = s_wp[o] > pstar ? s_wp[o] : pstar;
-        pquota = s_wq[o] < pquota ? s_wq[o] : pquota;
-        top = s_wt[o] > top ? s_wt[o] : top;
+        for (int d = kWave / 2; d >= 1; d >>= 1) {
+            const uint64_t po = __shfl_xor(p, d, kWave);
+            const uint64_t qo = __shfl_xor(pq, d, kWave);
+            const uint32_t to = __shfl_xor(top, d, kWave);
+            p = po > p ? po : p;
+            pq = qo < pq ? qo : pq;
+            top = to > top ? to : top;
+        }
+        if (lane == 0) {
+            s_bound = pq > p ? pq : p;
+            s_top = top;
+            s_n = 0;
+        }
     }
-    pstar = pquota > pstar ? pquota : pstar;
-    // candidates at or above the bound, gathered from all segments at once
-    const int total = S * k;
-    for (int g0 = 0; g0 < total; g0 += kThreads) {
-        const int g = g0 + (int)threadIdx.x;
-        const int sg = g / k, i = g - sg * k;
-        uint32_t kk = 0;
-        int32_t ii = 0;
+    __syncthreads();
+    const uint64_t pstar = s_bound;
+    const uint32_t top = s_top;
+    // candidates at or above the bound, from the registers, compacted to LDS
+#pragma unroll
+    for (int j = 0; j < kMergePer; ++j) {
+        if (j * kThreads >= total) break;
+        const int g = j * kThreads + tid;
         bool keep = false;
         if (g < total) {
-            const int64_t base = (r * S + sg) * (int64_t)part_cap;
-            kk = part_key[base + i];
-            ii = part_id[base + i];
-            keep = i < s_segn[sg] && order_key(kk, ii) >= pstar;
+            const int sg = g / part_cap, i = g - sg * part_cap;
+            keep = i < s_segn[sg] && i < k && order_key(ck[j], ci[j]) >= pstar;
         }
         const uint64_t m = __ballot(keep);
         int pos0 = 0;
         if (lane == 0 && m) pos0 = atomicAdd(&s_n, __popcll(m));
         pos0 = __shfl(pos0, 0, kWave);
-        if (keep) s_cand[pos0 + __popcll(m & lanes_below(lane))] = make_uint2(kk, (uint32_t)ii);
+        if (keep) s_cand[pos0 + __popcll(m & lanes_below(lane))] = make_uint2(ck[j], (uint32_t)ci[j]);
     }
     __syncthreads();
     const int n = block_rank_topk<1>(s_cand, 0, &s_n, k, s_sk, s_sid, fp.greedy ? nullptr : s_e,
-                                     (double)key_float(top), (double)fp.temperature, threadIdx.x, kThreads,
+                                     (double)key_float(top), (double)fp.temperature, tid, kThreads,
                                      reinterpret_cast<uint64_t*>(s_cx));
     __syncthreads();
-    if (threadIdx.x < kWave) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane, s_scal, s_cx);
+    if (tid < kWave) finalize_row(s_sk, s_sid, s_e, n, fp, out, r, lane, s_scal, s_cx);
 }
 
 // ---- dense chunk statistics --------------------------------------------------

@@ -358,9 +358,14 @@ __device__ __forceinline__ double slot_get_f64(const double (&a)[N], int i)
 // FS register slots per lane for the frontier and for the node records: at
 // most 1 + V entries are ever live, since a popped entry's slot takes its next
 // sibling and only first children need new slots (FS = ceil((V + 1) / 64)).
+// Four waves stage the candidate table, every load in flight at once; wave 0
+// alone then expands the tree.
+constexpr int kBuildThreads = 256;
+constexpr int kBuildPer = kMaxTreeVK / kBuildThreads;     // table entries per thread
+
 template <int FS>
-__global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_t B, int32_t K, int32_t V,
-                                                           SparseOut sup, TreeOut o)
+__global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch, int32_t B, int32_t K, int32_t V,
+                                                                   SparseOut sup, TreeOut o)
 {
     __shared__ int32_t c_id[kMaxTreeVK];       // depth d, rank r at d*K + r (B*K <= V*K <= 2048)
     __shared__ double c_p[kMaxTreeVK];
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_
         const int d = s * kWave + lane;
         int n = 0;
         double f = 0.0;
-        if (d < B) {
+        if (d < B && threadIdx.x < kWave) {
             n = sup.count[rbase + d];
             f = sup.probs[(rbase + d) * cap];
         }
@@ -386,15 +391,33 @@ __global__ __launch_bounds__(kWave) void tree_build_kernel(int32_t batch, int32_
     }
     // the candidate table is read whole (supports are padded to cap); entries
     // past a count are never used
-    const int kk = K < cap ? K : cap;
-    for (int i = lane; i < B * K; i += kWave) {
-        const int d = i / K, r = i - d * K;
-        if (r < kk) {
-            c_id[i] = sup.ids[(rbase + d) * cap + r];
-            c_p[i] = sup.probs[(rbase + d) * cap + r];
+    {
+        const int kk = K < cap ? K : cap;
+        int32_t tid[kBuildPer];
+        double tpr[kBuildPer];
+#pragma unroll
+        for (int j = 0; j < kBuildPer; ++j) {
+            const int i = j * kBuildThreads + (int)threadIdx.x;
+            const int d = i / K, r = i - d * K;
+            tid[j] = 0;
+            tpr[j] = 0.0;
+            if (i < B * K && r < kk) {
+                tid[j] = sup.ids[(rbase + d) * cap + r];
+                tpr[j] = sup.probs[(rbase + d) * cap + r];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kBuildPer; ++j) {
+            const int i = j * kBuildThreads + (int)threadIdx.x;
+            const int d = i / K, r = i - d * K;
+            if (i < B * K && r < kk) {
+                c_id[i] = tid[j];
+                c_p[i] = tpr[j];
+            }
         }
     }
-    wave_sync();
+    __syncthreads();
+    if (threadIdx.x >= kWave) return;
 
     uint64_t fs[FS];                                   // frontier: score bits (0 = empty)
     uint32_t ft[FS];                                   // frontier: tie word (~0 = empty)
@@ -1662,12 +1685,13 @@ hipError_t launch_tree_build(int32_t batch, int32_t B, int32_t K, int32_t V, con
                              const TreeOut& o, hipStream_t stream)
 {
     // live frontier entries <= 1 + V
+    const dim3 grid((unsigned)batch);
     if (V + 1 <= kWave)
-        tree_build_kernel<1><<<dim3((unsigned)batch), kWave, 0, stream>>>(batch, B, K, V, sup, o);
+        tree_build_kernel<1><<<grid, kBuildThreads, 0, stream>>>(batch, B, K, V, sup, o);
     else if (V + 1 <= 2 * kWave)
-        tree_build_kernel<2><<<dim3((unsigned)batch), kWave, 0, stream>>>(batch, B, K, V, sup, o);
+        tree_build_kernel<2><<<grid, kBuildThreads, 0, stream>>>(batch, B, K, V, sup, o);
     else
-        tree_build_kernel<3><<<dim3((unsigned)batch), kWave, 0, stream>>>(batch, B, K, V, sup, o);
+        tree_build_kernel<3><<<grid, kBuildThreads, 0, stream>>>(batch, B, K, V, sup, o);
     return hipGetLastError();
 }
 
