@@ -23,7 +23,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libuno.so")
+# UNO_LIBRARY names another build of the library (for instance the
+# sanitizer build of the host code); by default the in-tree libuno.so.
+_LIB_PATH = os.environ.get("UNO_LIBRARY") or os.path.join(_HERE, "libuno.so")
 _lock = threading.Lock()
 _lib = None
 

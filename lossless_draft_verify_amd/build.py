@@ -21,21 +21,30 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
+# The host code of the library under AddressSanitizer and UBSan (device code
+# unchanged), for checking the C ABI's host logic on the CPU; load it with
+# UNO_LIBRARY=<path> and clang's ASan runtime preloaded.
+LIB_SAN = os.path.join(HERE, "libuno_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out = LIB_SAN if sanitize else LIB
+    tmp = out + ".tmp%d" % os.getpid()
     srcs = []
     for s in SOURCES:
         p = os.path.join(CSRC, s)
         srcs += (["-x", "hip", p] if s.endswith(".hip") else ["-x", "hip", p])
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include"), "-o", tmp] + srcs
+    cmd = [HIPCC] + FLAGS + (SAN_FLAGS if sanitize else []) + ["-I", os.path.join(HERE, "..", "include"), "-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed (exit %d)" % res.returncode)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def is_stale() -> bool:
@@ -49,4 +58,4 @@ def is_stale() -> bool:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))

@@ -31,12 +31,22 @@ ORDER_TOPK_FIRST = 0
 ORDER_JOINT = 1
 
 
+# UNO_ORACLE_SANITIZE=1 builds and loads an AddressSanitizer + UBSan build
+# instead (liboracle_san.so); the process must then start with gcc's libasan
+# preloaded (LD_PRELOAD=$(gcc -print-file-name=libasan.so)).
+_SANITIZE = os.environ.get("UNO_ORACLE_SANITIZE", "") == "1"
+if _SANITIZE:
+    _LIB = os.path.join(_HERE, "liboracle_san.so")
+
+
 def build(force: bool = False) -> str:
     """Compile ``uno_oracle.c`` into ``liboracle.so`` (gcc, -O2, OpenMP)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
-               "-o", tmp, _SRC, "-lm"]
+        opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                "-fno-sanitize-recover=undefined"] if _SANITIZE else ["-O2"])
+        cmd = ["gcc"] + opt + ["-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
