@@ -896,7 +896,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
 
 // ---- dense chunk statistics --------------------------------------------------
 template <bool BF16, bool COUNT>
-__global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
+__global__ __launch_bounds__(kThreads, 5) void dense_chunk_kernel(
     RowSource src, int64_t rows, int64_t N, double log2e_over_T, int64_t exact_rows, DenseChunks dc,
     const FilterParams* rowp, int select)
 {
@@ -934,6 +934,7 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
                 const int64_t slot = r * nc + c;
                 dc.cmax[slot] = -INFINITY; dc.csum[slot] = 0.0;
                 if (COUNT) dc.ccount[slot] = 0;
+                if (dc.cerr) dc.cerr[slot] = 0.0f;
             }
         return;
     }
@@ -957,13 +958,15 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
         float mx;
         double s;
         uint32_t cntf;
+        float err = 0.0f;
         if (exact) chunk_stats_exact<COUNT>(x, ex, &mx, &s, &cntf);
-        else chunk_stats_fast<COUNT>(x, log2e_over_T32, &mx, &s, &cntf);
+        else chunk_stats_fast<COUNT>(x, log2e_over_T32, &mx, &s, &cntf, &err);
         if (lane == 0) {
             const int64_t slot = r * nc + c;
             dc.cmax[slot] = mx;
             dc.csum[slot] = (mx < INFINITY) ? s : NAN;
             if (COUNT) dc.ccount[slot] = (int32_t)cntf;
+            if (dc.cerr) dc.cerr[slot] = err;
         }
     };
     int c = c0;
@@ -998,7 +1001,7 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
 #pragma unroll 1
         for (int i = lane; i < n; i += kWave) mx = fmaxf(mx, load_scalar<BF16>(base, i));
         mx = wave_max_f32(mx);
-        double sum = 0.0;
+        double sum = 0.0, ty = 0.0;
         uint32_t cntf = 0;
         if (mx > -INFINITY && mx < INFINITY) {
             const double md = (double)mx;
@@ -1012,18 +1015,23 @@ __global__ __launch_bounds__(kThreads) void dense_chunk_kernel(
                     if (exact) {
                         sum += ex((double)v - md);
                     } else {
-                        const float y = (fmaxf(v, -3.0e38f) - mx) * log2e_over_T32;
-                        sum += (double)__builtin_amdgcn_exp2f(fmaxf(y, -200.0f));
+                        const float y = fmaxf((v - mx) * log2e_over_T32, -200.0f);
+                        const float t = __builtin_amdgcn_exp2f(y);
+                        sum += (double)t;
+                        ty += (double)t * (double)y;
                     }
                 }
             }
         }
         sum = wave_sum_f64(sum);
+        ty = wave_sum_f64(ty);
         if (lane == 0) {
             const int64_t slot = r * nc + c;
             dc.cmax[slot] = mx;
             dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
             if (COUNT) dc.ccount[slot] = (int32_t)cntf;
+            if (dc.cerr)
+                dc.cerr[slot] = exact ? 0.0f : (float)((1.0 + 2e-3) * (kFastExpRel * sum - kFastArgRel * ty) + 0x1p-114);
         }
     }
 }

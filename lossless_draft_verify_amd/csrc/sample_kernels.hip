@@ -637,7 +637,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
 
 // ---- dense linear ------------------------------------------------------------------
 constexpr int kDenseThreads = 256;
-constexpr int kProposeMaxThreads = 1024;   // dense_propose_kernel: up to one wave per proposal
+constexpr int kProposeMaxThreads = 512;    // dense_propose_kernel: up to eight waves, one proposal each at a time
 constexpr int kDenseWaves = kDenseThreads / kWave;
 constexpr int kPerLane = kDenseChunk / kWave;   // 32 logits per lane per chunk
 
@@ -677,9 +677,11 @@ __device__ __forceinline__ double chunk_term(const float* cm, const double* cs, 
 }
 
 // Row max m and normaliser S from chunk statistics; S accumulates 64-chunk
-// blocks of an inclusive wave scan, the same sums dense_locate walks.
+// blocks of an inclusive wave scan, the same sums dense_locate walks.  With
+// chunk error bounds ce, *E_out bounds |S - exact S| (0 when every chunk is
+// exact).
 __device__ bool dense_row_stat(const float* cm, const double* cs, int nc, const DenseExp& ex, int lane,
-                               float* m_out, double* S_out)
+                               float* m_out, double* S_out, const float* ce = nullptr, double* E_out = nullptr)
 {
     float m = -INFINITY;
     bool bad = false;
@@ -690,13 +692,15 @@ __device__ bool dense_row_stat(const float* cm, const double* cs, int nc, const 
     m = wave_max_f32(m);
     bad = __ballot(bad) != 0ull;
     if (bad || !(m > -INFINITY)) { *m_out = NAN; *S_out = NAN; return false; }
-    double S = 0.0;
+    double S = 0.0, E = 0.0;
     for (int base = 0; base < nc; base += kWave) {
         const int c = base + lane;
         const double term = (c < nc) ? chunk_term(cm, cs, c, m, ex) : 0.0;
         const double incl = wave_incl_scan_f64(term, lane);
         S += __shfl(incl, kWave - 1, kWave);
+        if (ce != nullptr && c < nc && cm[c] > -INFINITY) E += (double)ce[c] * ex((double)cm[c] - (double)m);
     }
+    if (E_out) *E_out = (ce != nullptr) ? wave_sum_f64(E) * (1.0 + 1e-6) : 0.0;
     *m_out = m;
     *S_out = S;
     return S > 0.0;
@@ -737,8 +741,10 @@ __device__ int dense_last_positive_chunk(int nc, TermF term_of, int lane)
 
 // Smallest element of a chunk (weights from wf, element layout of load_chunk)
 // whose cumulative weight exceeds tau; the last positive element if none does.
+// *margin (when given): the distance from tau to the nearer end of the picked
+// element's cumulative interval, -1 when tau lies in no interval.
 template <int EPV, typename WeightF>
-__device__ int pick_in_chunk(WeightF wf, double tau, int lane)
+__device__ int pick_in_chunk(WeightF wf, double tau, int lane, double* margin = nullptr)
 {
     constexpr int NV = kPerLane / EPV;
     double run = 0.0;
@@ -758,12 +764,17 @@ __device__ int pick_in_chunk(WeightF wf, double tau, int lane)
         if (hit) {
             const int l = wave_first_lane(hit);
             int ep = -1;
+            double mg = -1.0;
             if (lane == l) {
                 double cc = run + (incl - lsum);
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
+                    const double prev = cc;
                     cc += wl[e];
-                    if (ep < 0 && cc > tau) ep = e;
+                    if (ep < 0 && cc > tau) {
+                        ep = e;
+                        mg = fmin(tau - prev, cc - tau);
+                    }
                 }
                 if (ep < 0) {
 #pragma unroll
@@ -772,11 +783,13 @@ __device__ int pick_in_chunk(WeightF wf, double tau, int lane)
                 }
             }
             ep = __shfl(ep, l, kWave);
+            if (margin) *margin = __shfl(mg, l, kWave);
             return (j * kWave + l) * EPV + ep;
         }
         run += __shfl(incl, kWave - 1, kWave);
     }
     for (int d = kWave / 2; d >= 1; d >>= 1) last_pos = max(last_pos, __shfl_xor(last_pos, d, kWave));
+    if (margin) *margin = -1.0;
     return last_pos;
 }
 
@@ -817,31 +830,55 @@ __device__ __forceinline__ uint64_t row_keep(const DenseChunks& dc, int64_t r)
 }
 
 // Sample a dense filtered row p = exp((z - m)/T) / S (over the logits the keep
-// threshold admits) with uniform u.
+// threshold admits) with uniform u: the chunk from the chunk sums, then the
+// element from the chunk's exact terms.  With chunk error bounds ce and the
+// row's bound E (> 0: fast sums), *certain tells whether the pick is the one
+// exact sums give: the target's offset inside the chunk can be off by at most
+// (u E + the bound of the chunks before it) / the chunk's scale, so the pick
+// stands when its cumulative interval holds the offset with more than that
+// to spare.  With exact sums (E == 0) the pick is certain.
 template <bool BF16>
 __device__ int32_t dense_sample_row(const char* row, int64_t N, const float* cm, const double* cs, int nc,
-                                    float m, double S, double u, const DenseExp& ex, int lane, uint64_t thr)
+                                    float m, double S, double u, const DenseExp& ex, int lane, uint64_t thr,
+                                    const float* ce = nullptr, double E = 0.0, bool* certain = nullptr)
 {
     auto term = [&](int c) { return chunk_term(cm, cs, c, m, ex); };
+    const bool fast = ce != nullptr && E > 0.0;
     const double t = u * S;
     double before;
     int c = dense_locate(nc, t, term, lane, &before);
-    double tau;
+    double tau, scale = 1.0, ebefore = 0.0;
     if (c < 0) {
         c = dense_last_positive_chunk(nc, term, lane);
+        if (certain) *certain = !fast;
         if (c < 0) return -1;
         tau = INFINITY;
     } else {
-        tau = (t - before) / ex((double)cm[c] - (double)m);
+        scale = ex((double)cm[c] - (double)m);
+        tau = (t - before) / scale;
+        if (fast) {
+            // error bound of the chunks before c, relative to the row max
+            double eb = 0.0;
+            for (int k = lane; k < c; k += kWave)
+                if (cm[k] > -INFINITY) eb += (double)ce[k] * ex((double)cm[k] - (double)m);
+            ebefore = wave_sum_f64(eb);
+        }
     }
     float x[kPerLane];
     load_chunk<BF16>(row, N, c, x, lane);
     const double mc = (double)cm[c];
     constexpr int EPV = Vec<BF16>::EPV;
     auto wf = [&](int i) { return dense_keeps(thr, x[i], chunk_elem_id<EPV>(c, i, lane)) ? ex((double)x[i] - mc) : 0.0; };
-    const int l = pick_in_chunk<Vec<BF16>::EPV>(wf, tau, lane);
+    double margin = -1.0;
+    const int l = pick_in_chunk<Vec<BF16>::EPV>(wf, tau, lane, &margin);
+    if (certain && tau < INFINITY) {
+        // the fp64 sums themselves round at the 1e-12 level, far inside the bound
+        const double bound = ((u * E + ebefore) * (1.0 + 1e-6) + 1e-12 * S) / scale;
+        *certain = !fast || margin > bound;
+    }
     return l < 0 ? -1 : (int32_t)(c * (int64_t)kDenseChunk + l);
 }
+
 
 // Global row index of local row i of request b (draft rows 0..B-1, then target 0..B).
 __device__ __forceinline__ int64_t linear_row(int32_t batch, int32_t B, int b, int i)
@@ -859,15 +896,90 @@ __device__ __forceinline__ float load_one(const char* row, int64_t i)
     }
 }
 
-// Row stats of every row, proposals, acceptance and the first rejection.
+// Proposals and acceptance in three kernels.  Rows may carry fast chunk sums
+// with error bounds (dc.cerr): every draw and every acceptance test is
+// certified against them.
+//  - dense_propose_kernel: row statistics, the draws, and the acceptance test
+//    of every proposal whose draw is certain.  acc[j]: 1 accepted, 0
+//    rejected, 2 test not certain, 3 draw not certain.
+//  - dense_redo_rows_kernel (chip-wide): exact chunk sums for the rows those
+//    uncertain results read: q_j of an uncertain draw; q_j and p_j of an
+//    uncertain test before the first certain rejection.
+//  - dense_settle_kernel: the uncertain draws and tests again from the exact
+//    rows, the rare test that is still uncertain (a redrawn proposal's test
+//    on a fast target row) after the block has made its rows exact, and the
+//    first rejection.
+
+// Row statistics of row r (one wave) into row_m / row_S / row_E.
+__device__ __forceinline__ void row_stat_to(const DenseChunks& dc, int64_t r, const DenseExp& ex, int lane,
+                                            float* row_m, double* row_S, double* row_E)
+{
+    const int nc = dc.nchunks;
+    float m;
+    double S, E;
+    dense_row_stat(dc.cmax + r * nc, dc.csum + r * nc, nc, ex, lane, &m, &S, dc.cerr ? dc.cerr + r * nc : nullptr,
+                   &E);
+    if (lane == 0) { row_m[r] = m; row_S[r] = S; row_E[r] = E; }
+}
+
+// Draw of proposal j of request b (uniform 0 of draw (request, j)) from draft
+// row q_j with the row's current statistics; *certain as dense_sample_row.
+template <bool BF16>
+__device__ __forceinline__ int32_t propose_draw(const RowSource& src, int32_t batch, int32_t B, int64_t N,
+                                                const DenseChunks& dc, const DenseExp& ex, uint64_t seed,
+                                                uint64_t offset, uint32_t req, int b, int j, const float* row_m,
+                                                const double* row_S, const double* row_E, int lane, bool* certain,
+                                                uint32_t* flags)
+{
+    const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
+    const int nc = dc.nchunks;
+    const int64_t qr = linear_row(batch, B, b, j);
+    const double Sq = row_S[qr];
+    *certain = true;
+    if (!(Sq > 0.0)) { *flags |= 1u; return -1; }
+    return dense_sample_row<BF16>(row_pointer(src, qr, N * Vec<BF16>::ESZ), N, dc.cmax + qr * nc, dc.csum + qr * nc,
+                                  nc, row_m[qr], Sq, d.u[0], ex, lane, row_keep(dc, qr),
+                                  dc.cerr ? dc.cerr + qr * nc : nullptr, row_E[qr], certain);
+}
+
+// Acceptance test u1 q(y) < p(y) of proposal j: 1 accepted, 0 rejected, 2
+// when the two sides differ by no more than their sums' error bounds allow.
+template <bool BF16>
+__device__ __forceinline__ int propose_test(const RowSource& src, int32_t batch, int32_t B, int64_t N,
+                                            const DenseChunks& dc, const DenseExp& ex, uint64_t seed, uint64_t offset,
+                                            uint32_t req, int b, int j, int32_t y, const float* row_m,
+                                            const double* row_S, const double* row_E, uint32_t* flags)
+{
+    if (y < 0) return 0;
+    const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
+    const int64_t row_bytes = N * Vec<BF16>::ESZ;
+    const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
+    const double Sq = row_S[qr], Sp = row_S[pr];
+    const double qy = ex((double)load_one<BF16>(row_pointer(src, qr, row_bytes), y) - (double)row_m[qr]) / Sq;
+    double py = 0.0;
+    if (Sp > 0.0) {
+        const float zp = load_one<BF16>(row_pointer(src, pr, row_bytes), y);
+        if (dense_keeps(row_keep(dc, pr), zp, y)) py = ex((double)zp - (double)row_m[pr]) / Sp;
+    } else {
+        *flags |= 1u;
+    }
+    const double lhs = d.u[1] * qy;
+    const double Eq = row_E[qr], Ep = row_E[pr];
+    if (Eq > 0.0 || Ep > 0.0) {
+        const double rq = Eq / Sq, rp = (Sp > 0.0) ? Ep / Sp : 0.0;
+        const double bound = (lhs * rq + py * rp) * (1.0 + 1e-3) + 1e-12 * (lhs + py);
+        if (!(fabs(lhs - py) > bound)) return 2;
+    }
+    return (lhs < py) ? 1 : 0;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kProposeMaxThreads) void dense_propose_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
-    uint64_t seed, uint64_t offset, const uint32_t* req_ids, float* row_m, double* row_S,
-    int32_t* jstar_out, int32_t* y_out, uint32_t* flag_out, LinearOut o, const FilterParams* rowp)
+    uint64_t seed, uint64_t offset, const uint32_t* req_ids, float* row_m, double* row_S, double* row_E,
+    int32_t* y_scr, int32_t* acc, uint32_t* flag_out, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
-    __shared__ int32_t s_acc[kMaxLinearB];
     __shared__ uint32_t s_flags;
     if (rowp) {                              // per-request parameters: the request's own temperature
         const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
@@ -875,77 +987,207 @@ __global__ __launch_bounds__(kProposeMaxThreads) void dense_propose_kernel(
         log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
     }
     load_exp2_table(s_exp2);
+    if (threadIdx.x == 0) s_flags = 0;
     __syncthreads();
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nw = (int)(blockDim.x / kWave);
     const int b = blockIdx.x;
     const DenseExp ex{ log2e_over_T, s_exp2 };
     const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
-    const int nc = dc.nchunks;
-    const int64_t row_bytes = N * Vec<BF16>::ESZ;
-    if (threadIdx.x == 0) s_flags = 0;
-
-    const int nw = (int)(blockDim.x / kWave);   // one wave per proposal, up to 16
-    for (int i = w; i < 2 * B + 1; i += nw) {
-        const int64_t r = linear_row(batch, B, b, i);
-        float m;
-        double S;
-        dense_row_stat(dc.cmax + r * nc, dc.csum + r * nc, nc, ex, lane, &m, &S);
-        if (lane == 0) { row_m[r] = m; row_S[r] = S; }
-    }
+    for (int i = w; i < 2 * B + 1; i += nw) row_stat_to(dc, linear_row(batch, B, b, i), ex, lane, row_m, row_S, row_E);
     __syncthreads();
-
     uint32_t flags = 0;
     for (int j = w; j < B; j += nw) {
-        const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
-        const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
-        const float mq = row_m[qr], mp = row_m[pr];
-        const double Sq = row_S[qr], Sp = row_S[pr];
-        const char* qrow = row_pointer(src, qr, row_bytes);
-        const char* prow = row_pointer(src, pr, row_bytes);
-        int32_t y = -1;
-        int acc = 0;
-        if (Sq > 0.0) {
-            y = dense_sample_row<BF16>(qrow, N, dc.cmax + qr * nc, dc.csum + qr * nc, nc, mq, Sq, d.u[0], ex, lane,
-                                       row_keep(dc, qr));
-        } else {
-            flags |= 1u;
-        }
-        if (y >= 0) {
-            const double qy = ex((double)load_one<BF16>(qrow, y) - (double)mq) / Sq;
-            double py = 0.0;
-            if (Sp > 0.0) {
-                const float zp = load_one<BF16>(prow, y);
-                if (dense_keeps(row_keep(dc, pr), zp, y)) py = ex((double)zp - (double)mp) / Sp;
-            } else {
-                flags |= 1u;
+        bool certain;
+        const int32_t y = propose_draw<BF16>(src, batch, B, N, dc, ex, seed, offset, req, b, j, row_m, row_S, row_E,
+                                             lane, &certain, &flags);
+        const int a = certain ? propose_test<BF16>(src, batch, B, N, dc, ex, seed, offset, req, b, j, y, row_m,
+                                                   row_S, row_E, &flags)
+                              : 3;
+        if (lane == 0) { y_scr[(int64_t)b * B + j] = y; acc[(int64_t)b * B + j] = a; }
+    }
+    if (flags && lane == 0) atomicOr(&s_flags, flags);
+    __syncthreads();
+    if (threadIdx.x == 0) flag_out[b] = s_flags;
+}
+
+// Exact chunk statistics of chunk c of row r (one wave), bound 0.
+template <bool BF16>
+__device__ __forceinline__ void exact_chunk_to(const char* row, int64_t N, int64_t r, int c, const DenseChunks& dc,
+                                               const DenseExp& ex, int lane)
+{
+    float x[kPerLane];
+    load_chunk<BF16>(row, N, c, x, lane);
+    float mx;
+    double sum;
+    uint32_t cntf;
+    chunk_stats_exact<true>(x, ex, &mx, &sum, &cntf);
+    if (lane == 0) {
+        const int64_t slot = r * dc.nchunks + c;
+        dc.cmax[slot] = mx;
+        dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
+        if (dc.ccount) dc.ccount[slot] = (int32_t)cntf;
+        if (dc.cerr) dc.cerr[slot] = 0.0f;
+    }
+}
+
+// Rows of request b whose uncertain results need exact sums (see above);
+// their chunks dealt over gridDim.y workgroups, round robin over the waves.
+template <bool BF16>
+__global__ __launch_bounds__(kDenseThreads) void dense_redo_rows_kernel(
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
+    const int32_t* acc, const double* row_E, const FilterParams* rowp)
+{
+    __shared__ double s_exp2[kExp2Entries];
+    __shared__ int64_t s_rows[2 * kMaxLinearB];
+    __shared__ int s_n;
+    if (rowp) {
+        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
+        if (f.dense == kRowTopK) return;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
+    const int b = blockIdx.x;
+    if (threadIdx.x == 0) {
+        int n = 0;
+        bool counts = true;                  // tests count up to the first certain rejection
+        for (int j = 0; j < B; ++j) {
+            const int a = acc[(int64_t)b * B + j];
+            if (a == 3) s_rows[n++] = linear_row(batch, B, b, j);
+            if (a == 0) counts = false;
+            if (a == 2 && counts) {
+                const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
+                if (row_E[qr] > 0.0) s_rows[n++] = qr;
+                if (row_E[pr] > 0.0) s_rows[n++] = pr;
             }
-            acc = (d.u[1] * qy < py) ? 1 : 0;
         }
-        if (lane == 0) {
-            s_acc[j] = acc;
-            y_out[(int64_t)b * B + j] = y;
-            if (o.proposals) o.proposals[(int64_t)b * B + j] = y;
+        s_n = n;
+    }
+    __syncthreads();
+    const int n = s_n;
+    if (n == 0) return;
+    load_exp2_table(s_exp2);
+    __syncthreads();
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nc = dc.nchunks;
+    const DenseExp ex{ log2e_over_T, s_exp2 };
+    const int64_t row_bytes = N * Vec<BF16>::ESZ;
+    for (int k = 0; k < n; ++k) {
+        const int64_t r = s_rows[k];
+        const char* row = row_pointer(src, r, row_bytes);
+        for (int c = blockIdx.y * kDenseWaves + w; c < nc; c += gridDim.y * kDenseWaves)
+            exact_chunk_to<BF16>(row, N, r, c, dc, ex, lane);
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kProposeMaxThreads) void dense_settle_kernel(
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
+    uint64_t seed, uint64_t offset, const uint32_t* req_ids, float* row_m, double* row_S, double* row_E,
+    const int32_t* y_scr, const int32_t* acc, int32_t* jstar_out, int32_t* y_out, uint32_t* flag_out,
+    LinearOut o, const FilterParams* rowp)
+{
+    __shared__ double s_exp2[kExp2Entries];
+    __shared__ int32_t s_acc[kMaxLinearB];
+    __shared__ int32_t s_y[kMaxLinearB];
+    __shared__ uint32_t s_flags;
+    __shared__ int s_any;
+    if (rowp) {
+        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
+        if (f.dense == kRowTopK) return;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
+    const int b = blockIdx.x;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nw = (int)(blockDim.x / kWave);
+    if (threadIdx.x == 0) { s_flags = 0; s_any = 0; }
+    __syncthreads();
+    for (int j = threadIdx.x; j < B; j += blockDim.x) {
+        const int a = acc[(int64_t)b * B + j];
+        s_acc[j] = a;
+        s_y[j] = y_scr[(int64_t)b * B + j];
+        if (a >= 2) atomicOr(&s_any, 1);
+    }
+    __syncthreads();
+    uint32_t flags = 0;
+    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+    if (s_any) {
+        load_exp2_table(s_exp2);
+        __syncthreads();
+        const DenseExp ex{ log2e_over_T, s_exp2 };
+        // the redone rows' statistics, then the draws and tests again
+        for (int j = w; j < B; j += nw) {
+            const int a = s_acc[j];
+            if (a < 2) continue;
+            const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
+            row_stat_to(dc, qr, ex, lane, row_m, row_S, row_E);
+            row_stat_to(dc, pr, ex, lane, row_m, row_S, row_E);
+        }
+        __syncthreads();
+        for (int j = w; j < B; j += nw) {
+            const int a = s_acc[j];
+            if (a < 2) continue;
+            int32_t y = s_y[j];
+            if (a == 3) {
+                bool certain;
+                y = propose_draw<BF16>(src, batch, B, N, dc, ex, seed, offset, req, b, j, row_m, row_S, row_E, lane,
+                                       &certain, &flags);
+            }
+            const int a2 = propose_test<BF16>(src, batch, B, N, dc, ex, seed, offset, req, b, j, y, row_m, row_S,
+                                              row_E, &flags);
+            if (lane == 0) { s_y[j] = y; s_acc[j] = a2; }
+        }
+        __syncthreads();
+        // a test still uncertain before the first rejection: exact rows here
+        for (int j = 0; j < B; ++j) {        // uniform: s_acc is in LDS
+            const int a = s_acc[j];
+            if (a == 0) break;
+            if (a != 2) continue;
+            const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
+            const int64_t row_bytes = N * Vec<BF16>::ESZ;
+            for (int k = 0; k < 2; ++k) {
+                const int64_t r = k == 0 ? qr : pr;
+                if (!(row_E[r] > 0.0)) continue;
+                for (int c = w; c < dc.nchunks; c += nw)
+                    exact_chunk_to<BF16>(row_pointer(src, r, row_bytes), N, r, c, dc, ex, lane);
+                __syncthreads();
+                if (w == 0) row_stat_to(dc, r, ex, lane, row_m, row_S, row_E);
+                __syncthreads();
+            }
+            if (w == 0) {
+                const int a2 = propose_test<BF16>(src, batch, B, N, dc, ex, seed, offset, req, b, j, s_y[j], row_m,
+                                                  row_S, row_E, &flags);
+                if (lane == 0) s_acc[j] = a2 == 1 ? 1 : 0;
+            }
+            __syncthreads();
+            if (s_acc[j] == 0) break;
         }
     }
     if (flags && lane == 0) atomicOr(&s_flags, flags);
+    for (int j = threadIdx.x; j < B; j += blockDim.x) {
+        y_out[(int64_t)b * B + j] = s_y[j];
+        if (o.proposals) o.proposals[(int64_t)b * B + j] = s_y[j];
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
         int js = B;
         for (int j = 0; j < B; ++j)
-            if (!s_acc[j]) { js = j; break; }
+            if (s_acc[j] == 0) { js = j; break; }
         jstar_out[b] = js;
-        flag_out[b] = s_flags;
+        flag_out[b] |= s_flags;
     }
 }
 
-// Exact chunk statistics of the target row each request draws its last token
-// from (p_j* after a rejection, the bonus row p_B otherwise).  The chunk pass
-// gave target rows fast sums, which only enter acceptance ratios.
+// Exact chunk statistics of the rows each request draws its last token from:
+// the target row p_j* and the draft row q_j* after a rejection (the residual
+// reads both), the bonus row p_B otherwise.  Rows the proposal kernel already
+// made exact (bound 0) are skipped.
 template <bool BF16>
 __global__ __launch_bounds__(kDenseThreads) void dense_exact_row_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
-    const int32_t* jstar_in, const FilterParams* rowp)
+    const int32_t* jstar_in, const double* row_E, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
     if (rowp) {                              // a nucleus request's rows are exact already
@@ -953,28 +1195,37 @@ __global__ __launch_bounds__(kDenseThreads) void dense_exact_row_kernel(
         if (f.dense != kRowFull) return;
         log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
     }
+    const int b = blockIdx.x;
+    const int js = jstar_in[b];
+    const int64_t pr = linear_row(batch, B, b, B + (js < B ? js : B));
+    const int64_t qr = js < B ? linear_row(batch, B, b, js) : -1;
+    const bool do_p = row_E[pr] > 0.0, do_q = qr >= 0 && row_E[qr] > 0.0;
+    if (!do_p && !do_q) return;
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int b = blockIdx.x;
     const int nc = dc.nchunks;
-    const int js = jstar_in[b];
-    const int64_t pr = linear_row(batch, B, b, B + (js < B ? js : B));
     const DenseExp ex{ log2e_over_T, s_exp2 };
-    // the row's chunks dealt over gridDim.y workgroups, round robin over their waves
-    for (int c = blockIdx.y * kDenseWaves + w; c < nc; c += gridDim.y * kDenseWaves) {
-        float x[kPerLane];
-        load_chunk<BF16>(row_pointer(src, pr, N * Vec<BF16>::ESZ), N, c, x, lane);
-        float mx;
-        double sum;
-        uint32_t cntf;
-        chunk_stats_exact<true>(x, ex, &mx, &sum, &cntf);
-        if (lane == 0) {
-            const int64_t slot = pr * nc + c;
-            dc.cmax[slot] = mx;
-            dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
-            if (dc.ccount) dc.ccount[slot] = (int32_t)cntf;
+    // the rows' chunks dealt over gridDim.y workgroups, round robin over their waves
+    for (int k = 0; k < 2; ++k) {
+        const int64_t r = k == 0 ? pr : qr;
+        if (k == 0 ? !do_p : !do_q) continue;
+        const char* row = row_pointer(src, r, N * Vec<BF16>::ESZ);
+        for (int c = blockIdx.y * kDenseWaves + w; c < nc; c += gridDim.y * kDenseWaves) {
+            float x[kPerLane];
+            load_chunk<BF16>(row, N, c, x, lane);
+            float mx;
+            double sum;
+            uint32_t cntf;
+            chunk_stats_exact<true>(x, ex, &mx, &sum, &cntf);
+            if (lane == 0) {
+                const int64_t slot = r * nc + c;
+                dc.cmax[slot] = mx;
+                dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
+                if (dc.ccount) dc.ccount[slot] = (int32_t)cntf;
+                if (dc.cerr) dc.cerr[slot] = 0.0f;
+            }
         }
     }
 }
@@ -1005,7 +1256,9 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
     float mpf;
     double Sp;
     dense_row_stat(dc.cmax + pr * nc, dc.csum + pr * nc, nc, ex, lane, &mpf, &Sp);   // exact chunks
-    const double Sq = row_S[qr];
+    float mqf;
+    double Sq;
+    dense_row_stat(dc.cmax + qr * nc, dc.csum + qr * nc, nc, ex, lane, &mqf, &Sq);   // exact chunks
     // the request's chunks dealt over gridDim.y workgroups, round robin over their waves
     for (int c = c0; c < nc; c += gridDim.y * kDenseWaves) {
         double total = 0.0;
@@ -1015,7 +1268,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
             float xp[kPerLane], xq[kPerLane];
             load_chunk<BF16>(row_pointer(src, pr, row_bytes), N, c, xp, lane);
             if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
-            const double mp = (double)mpf, mq = (double)row_m[qr];
+            const double mp = (double)mpf, mq = (double)mqf;
             const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
             const uint64_t tp = row_keep(dc, pr), tq = row_keep(dc, qr);
             constexpr int EPV = Vec<BF16>::EPV;
@@ -1067,7 +1320,9 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
         fl |= 1u;
     } else if (js < B) {
         const int64_t qr = linear_row(batch, B, b, js);
-        const double Sq = row_S[qr];
+        float mqf;
+        double Sq;
+        dense_row_stat(dc.cmax + qr * nc, dc.csum + qr * nc, nc, ex, lane, &mqf, &Sq);   // exact chunks
         const bool q_ok = Sq > 0.0;
         const double* R = resid + (int64_t)b * nc;
         auto rterm = [&](int c) { return R[c]; };
@@ -1086,7 +1341,7 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
             float xp[kPerLane], xq[kPerLane];
             load_chunk<BF16>(prow, N, c, xp, lane);
             if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
-            const double mpd = (double)mp, mq = (double)row_m[qr];
+            const double mpd = (double)mp, mq = (double)mqf;
             const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
             const uint64_t tp = row_keep(dc, pr), tq = row_keep(dc, qr);
             constexpr int EPV = Vec<BF16>::EPV;
@@ -1650,16 +1905,22 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
     const int want = (2048 + batch - 1) / batch;
     const int gy = per_req < want ? per_req : want;
     const dim3 rgrid((unsigned)batch, (unsigned)gy);
-    // the proposals of a request run side by side: one wave each (4 to 16 waves)
+    // the proposals of a request run side by side: one wave each (4 to 8 waves)
     const int pw = B < kDenseWaves ? kDenseWaves : (B > kProposeMaxThreads / kWave ? kProposeMaxThreads / kWave : B);
     const unsigned pthreads = (unsigned)(pw * kWave);
     if (bf16) {
         dense_propose_kernel<true><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
-            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
-            sc.flags, o, rowp);
+            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
+            sc.flags, rowp);
+        if (dc.cerr && !exact_all)
+            dense_redo_rows_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.acc,
+                                                                             sc.row_E, rowp);
+        dense_settle_kernel<true><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
+            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
+            sc.jstar, sc.y, sc.flags, o, rowp);
         if (!exact_all)
             dense_exact_row_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
-                                                                              rowp);
+                                                                             sc.row_E, rowp);
         dense_residual_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid, rowp);
         dense_finish_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
@@ -1667,11 +1928,17 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
             sc.flags, sc.resid, o, rowp);
     } else {
         dense_propose_kernel<false><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
-            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
-            sc.flags, o, rowp);
+            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
+            sc.flags, rowp);
+        if (dc.cerr && !exact_all)
+            dense_redo_rows_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.acc,
+                                                                             sc.row_E, rowp);
+        dense_settle_kernel<false><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
+            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
+            sc.jstar, sc.y, sc.flags, o, rowp);
         if (!exact_all)
-            dense_exact_row_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc,
-                                                                               sc.jstar, rowp);
+            dense_exact_row_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
+                                                                             sc.row_E, rowp);
         dense_residual_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid, rowp);
         dense_finish_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(

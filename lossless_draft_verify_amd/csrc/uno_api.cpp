@@ -137,7 +137,7 @@ struct SparseWs {
     int part_cap;        // entries per segment list (the largest k)
 };
 
-DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bool keep);
+DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bool keep, bool err = false);
 
 // Supports (when own_supports; in id order with cumulative sums when id_order)
 // and segment partials for `rows` top-k rows with supports of m.k entries;
@@ -172,14 +172,16 @@ void carve_sparse(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool ow
 }
 
 // Chunk statistics; the finite counts only for uno_filter, whose dense mode
-// reports each row's support size (the samplers never read them).
-DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bool keep)
+// reports each row's support size (the samplers never read them); error
+// bounds for the linear samplers, which certify draws made from fast sums.
+DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bool keep, bool err)
 {
     DenseChunks dc;
     dc.nchunks = dense_nchunks(vocab);
     dc.cmax = cv.take<float>((size_t)rows * dc.nchunks);
     dc.csum = cv.take<double>((size_t)rows * dc.nchunks);
     dc.ccount = counts ? cv.take<int32_t>((size_t)rows * dc.nchunks) : nullptr;
+    dc.cerr = err ? cv.take<float>((size_t)rows * dc.nchunks) : nullptr;
     dc.keep = keep ? cv.take<uint64_t>((size_t)rows) : nullptr;
     return dc;
 }
@@ -189,8 +191,10 @@ DenseScratch carve_dense_scratch(Carve& cv, int64_t rows, int32_t batch, int32_t
     DenseScratch s;
     s.row_m = cv.take<float>((size_t)rows);
     s.row_S = cv.take<double>((size_t)rows);
+    s.row_E = cv.take<double>((size_t)rows);
     s.jstar = cv.take<int32_t>((size_t)batch);
     s.y = cv.take<int32_t>((size_t)batch * B);
+    s.acc = cv.take<int32_t>((size_t)batch * B);
     s.flags = cv.take<uint32_t>((size_t)batch);
     s.resid = cv.take<double>((size_t)batch * nchunks);
     return s;
@@ -200,11 +204,11 @@ DenseScratch carve_dense_scratch(Carve& cv, int64_t rows, int32_t batch, int32_t
 // joint-order rows and the full-vocabulary rows share (a row is one or the
 // other).
 void carve_per_request(Carve& cv, int64_t rows, int64_t vocab, const Mode& m, bool counts, SparseWs* sw,
-                       DenseChunks* dc)
+                       DenseChunks* dc, bool err = false)
 {
     sw->rowp = cv.take<FilterParams>((size_t)rows);
     if (m.any_dense || m.joint) {
-        *dc = carve_chunks(cv, rows, vocab, counts, m.any_nucleus);
+        *dc = carve_chunks(cv, rows, vocab, counts, m.any_nucleus, err);
         if (m.joint) sw->full = *dc;
     }
 }
@@ -344,10 +348,10 @@ int layout_linear(int64_t batch, int32_t B, int64_t vocab, int32_t dtype, const 
     if (st) return st;
     if (batch == 0) return UNO_OK;
     const int64_t rows = batch * (2 * (int64_t)B + 1);
-    if (m->per_request) carve_per_request(cv, rows, vocab, *m, false, sw, dc);
+    if (m->per_request) carve_per_request(cv, rows, vocab, *m, false, sw, dc, true);
     if (m->any_sparse) carve_sparse(cv, rows, vocab, *m, true, true, sw);
     if (m->any_dense) {
-        if (!m->per_request) *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
+        if (!m->per_request) *dc = carve_chunks(cv, rows, vocab, false, m->nucleus, true);
         *ds = carve_dense_scratch(cv, rows, (int32_t)batch, B, dc->nchunks);
     }
     return UNO_OK;
@@ -494,14 +498,15 @@ int uno_sample_linear_ex(const void* draft, const void* target, int32_t dtype, i
         if (e == hipSuccess) e = launch_linear_sparse(batch, B, sw.sup, seed, offset, request_ids, o, stream, rowp);
     }
     if (e == hipSuccess && m.any_dense) {
-        // draft rows are sampled from (exact sums); target rows enter only
-        // acceptance ratios, except the one each request draws its last token
-        // from, which the dense linear path recomputes exactly (a nucleus
-        // needs exact sums on every row: one set, all rows; per request, the
-        // chunk pass makes the nucleus rows exact itself)
+        // fast sums with error bounds on every row: the samplers certify each
+        // draw and acceptance against the bounds and redo the rare uncertain
+        // ones from exact sums; the rows each request draws its last token
+        // from are recomputed exactly (a nucleus needs exact sums on every
+        // row: one set, all rows; per request, the chunk pass makes the
+        // nucleus rows exact itself)
         const bool exact_all = !m.per_request && m.nucleus;
-        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, exact_all ? rows : (int64_t)batch * B,
-                                stream, rowp, kChunkDenseRows);
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, exact_all ? rows : 0, stream, rowp,
+                                kChunkDenseRows);
         if (e == hipSuccess && m.any_nucleus)
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream, rowp);
         if (e == hipSuccess)

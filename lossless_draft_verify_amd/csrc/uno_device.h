@@ -333,30 +333,51 @@ __device__ __forceinline__ void chunk_stats_exact(const float (&x)[PER_LANE], co
     *cnt_out = cntf;
 }
 
-// Fast: terms from the fp32 exponential (relative error near 1e-7), summed in
-// fp64.  Good enough for a normaliser that only enters a probability ratio;
-// never used where a CDF is inverted.
+// Fast: terms t = 2^y from the fp32 exponential, y = fl(fl(z - m) * c) with
+// c = fl(log2(e)/T), summed in fp64, with a bound on the chunk sum's error.
+// The bound (a certificate for callers that invert a CDF from these sums):
+//  - v_exp_f32 is within 0.712 * 2^-23 relative of 2^y for every fp32 y in
+//    [-126, 0) (checked exhaustively on gfx950 against exp2 in double), so
+//    kFastExpRel = 2^-23 bounds it;
+//  - y carries three fp32 roundings (difference, constant, product):
+//    |y - y_exact| <= 3.0002 * 2^-24 * |y|, which moves the term by at most
+//    kFastArgRel * |y| relative (ln 2 * 3.0002 * 2^-24, with room for the
+//    exponential's curvature at |y| <= 200);
+//  - y is clamped at -200 (NaN, -inf and negligible terms) and results below
+//    2^-126 may flush to 0: at most 2^-126 per term.
+// So |sum - exact| <= kFastExpRel * sum + kFastArgRel * sum(t * |y|) + 2048 * 2^-126;
+// the factor (1 + 2e-3) covers the fp32 sum of t * |y|, the fp64 sums and the
+// rounding of the result to float.
+constexpr double kFastExpRel = 0x1p-23;
+constexpr double kFastArgRel = 1.2397e-7;
+
 template <bool COUNT, int PER_LANE>
 __device__ __forceinline__ void chunk_stats_fast(const float (&x)[PER_LANE], float log2e_over_T, float* m_out,
-                                                 double* s_out, uint32_t* cnt_out)
+                                                 double* s_out, uint32_t* cnt_out, float* err_out)
 {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) mx = fmaxf(mx, x[i]);
     mx = wave_max_f32(mx);
     double s = 0.0;
+    float a = 0.0f;            // sum of t * y (every y <= 0)
     uint32_t cntf = 0;
     if (mx > -INFINITY && mx < INFINITY) {
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i) {
             if (COUNT) cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
-            // fmaxf maps NaN to the large negative bound; its term is 0
-            const float y = (fmaxf(x[i], -3.0e38f) - mx) * log2e_over_T;
-            s += (double)__builtin_amdgcn_exp2f(fmaxf(y, -200.0f));
+            // NaN and -inf give y = NaN or -inf, which the clamp maps to -200
+            const float y = fmaxf((x[i] - mx) * log2e_over_T, -200.0f);
+            const float t = __builtin_amdgcn_exp2f(y);
+            s += (double)t;
+            a = fmaf(t, y, a);
         }
     }
     *m_out = mx;
-    *s_out = wave_sum_f64(s);
+    s = wave_sum_f64(s);
+    const double ty = wave_sum_f64((double)a);
+    *s_out = s;
+    *err_out = (float)((1.0 + 2e-3) * (kFastExpRel * s - kFastArgRel * ty) + 0x1p-114);
     *cnt_out = cntf;
 }
 

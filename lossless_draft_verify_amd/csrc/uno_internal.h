@@ -66,6 +66,9 @@ struct DenseChunks {
     float* cmax;       // [rows][nchunks]
     double* csum;      // [rows][nchunks]
     int32_t* ccount;   // [rows][nchunks], or nullptr when no caller needs the counts
+    // [rows][nchunks] bound on |csum - exact sum| for chunks summed with fp32
+    // exponentials (0 for exact chunks), or nullptr when every row is exact
+    float* cerr;
     int32_t nchunks;
     // [rows] keep thresholds of a full-vocabulary nucleus, or nullptr: logit i of
     // row r is in the support iff order_key(float_key(z_i), i) >= keep[r] (the
@@ -155,15 +158,19 @@ hipError_t launch_linear_sparse(int32_t batch, int32_t B, const SparseOut& sup, 
 struct DenseScratch {
     float* row_m;      // [rows]
     double* row_S;     // [rows]
+    double* row_E;     // [rows] bound on |row_S - exact S| (0: exact sums)
     int32_t* jstar;    // [batch]
     int32_t* y;        // [batch][B]
+    int32_t* acc;      // [batch][B] acceptance results before they are settled
     uint32_t* flags;   // [batch]
     double* resid;     // [batch][nchunks]
 };
 
 // With exact_all every row's chunk sums are already exact (the nucleus needs
-// them); otherwise target rows have fast sums and the row each request draws
-// its last token from is recomputed exactly.  rowp (nullable): per-row
+// them); otherwise every row has fast sums with error bounds, the proposal
+// kernel certifies its draws and acceptance tests against them (redoing the
+// uncertain ones from exact sums), and the rows each request draws its last
+// token from are recomputed exactly.  rowp (nullable): per-row
 // parameters; only the requests whose rows are not kRowTopK are sampled, each
 // at its own temperature (a nucleus request's target rows are exact already).
 hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, int64_t vocab,
