@@ -640,6 +640,7 @@ constexpr int kDenseThreads = 256;
 constexpr int kProposeMaxThreads = 512;    // dense_propose_kernel: up to eight waves, one proposal each at a time
 constexpr int kDenseWaves = kDenseThreads / kWave;
 constexpr int kPerLane = kDenseChunk / kWave;   // 32 logits per lane per chunk
+constexpr int kListGroups = 1024;              // workgroups of dense_exact_list_kernel
 
 // Chunk c of a row into registers: element (j*64 + lane)*EPV + e at x[j*EPV + e];
 // -inf past the end of the row.
@@ -902,9 +903,10 @@ __device__ __forceinline__ float load_one(const char* row, int64_t i)
 //  - dense_propose_kernel: row statistics, the draws, and the acceptance test
 //    of every proposal whose draw is certain.  acc[j]: 1 accepted, 0
 //    rejected, 2 test not certain, 3 draw not certain.
-//  - dense_redo_rows_kernel (chip-wide): exact chunk sums for the rows those
-//    uncertain results read: q_j of an uncertain draw; q_j and p_j of an
-//    uncertain test before the first certain rejection.
+//  - dense_exact_list_kernel (chip-wide): exact chunk sums for the rows those
+//    uncertain results read (the first exact-row list, which the proposal
+//    kernel fills): q_j of an uncertain draw; q_j and p_j of an uncertain
+//    test before the first certain rejection.
 //  - dense_settle_kernel: the uncertain draws and tests again from the exact
 //    rows, the rare test that is still uncertain (a redrawn proposal's test
 //    on a fast target row) after the block has made its rows exact, and the
@@ -977,9 +979,10 @@ template <bool BF16>
 __global__ __launch_bounds__(kProposeMaxThreads) void dense_propose_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
     uint64_t seed, uint64_t offset, const uint32_t* req_ids, float* row_m, double* row_S, double* row_E,
-    int32_t* y_scr, int32_t* acc, uint32_t* flag_out, const FilterParams* rowp)
+    int32_t* y_scr, int32_t* acc, uint32_t* flag_out, int64_t* xrows, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
+    __shared__ int32_t s_acc[kMaxLinearB];
     __shared__ uint32_t s_flags;
     if (rowp) {                              // per-request parameters: the request's own temperature
         const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
@@ -1005,11 +1008,39 @@ __global__ __launch_bounds__(kProposeMaxThreads) void dense_propose_kernel(
         const int a = certain ? propose_test<BF16>(src, batch, B, N, dc, ex, seed, offset, req, b, j, y, row_m,
                                                    row_S, row_E, &flags)
                               : 3;
-        if (lane == 0) { y_scr[(int64_t)b * B + j] = y; acc[(int64_t)b * B + j] = a; }
+        if (lane == 0) { y_scr[(int64_t)b * B + j] = y; acc[(int64_t)b * B + j] = a; s_acc[j] = a; }
     }
     if (flags && lane == 0) atomicOr(&s_flags, flags);
     __syncthreads();
-    if (threadIdx.x == 0) flag_out[b] = s_flags;
+    if (threadIdx.x == 0) {
+        flag_out[b] = s_flags;
+        // the rows whose uncertain results need exact sums go to the first
+        // exact-row list: q_j of an uncertain draw; q_j and p_j of an
+        // uncertain test before the first certain rejection
+        if (dc.xcount != nullptr) {
+            // two passes over the results: count, reserve, write
+            int64_t* out = nullptr;
+            for (int pass = 0; pass < 2; ++pass) {
+                int n = 0;
+                bool counts = true;
+                auto put = [&](int64_t r) { if (out) out[n] = r; ++n; };
+                for (int j = 0; j < B; ++j) {
+                    const int a = s_acc[j];
+                    if (a == 3) put(linear_row(batch, B, b, j));
+                    if (a == 0) counts = false;
+                    if (a == 2 && counts) {
+                        const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
+                        if (row_E[qr] > 0.0) put(qr);
+                        if (row_E[pr] > 0.0) put(pr);
+                    }
+                }
+                if (pass == 0) {
+                    if (n == 0) break;
+                    out = xrows + atomicAdd(&dc.xcount[0], (uint32_t)n);
+                }
+            }
+        }
+    }
 }
 
 // Exact chunk statistics of chunk c of row r (one wave), bound 0.
@@ -1032,52 +1063,30 @@ __device__ __forceinline__ void exact_chunk_to(const char* row, int64_t N, int64
     }
 }
 
-// Rows of request b whose uncertain results need exact sums (see above);
-// their chunks dealt over gridDim.y workgroups, round robin over the waves.
+// Exact chunk statistics for the rows of an exact-row list (count rows at
+// rows[0 ..]): chunk t % nchunks of row rows[t / nchunks] for every task t,
+// dealt one per wave over a fixed grid, so a few rows still spread over the
+// whole chip.  Each row keeps its own temperature (per-request sets).
 template <bool BF16>
-__global__ __launch_bounds__(kDenseThreads) void dense_redo_rows_kernel(
-    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
-    const int32_t* acc, const double* row_E, const FilterParams* rowp)
+__global__ __launch_bounds__(kDenseThreads) void dense_exact_list_kernel(
+    RowSource src, int64_t N, double log2e_over_T, DenseChunks dc, const int64_t* rows, const uint32_t* count,
+    const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
-    __shared__ int64_t s_rows[2 * kMaxLinearB];
-    __shared__ int s_n;
-    if (rowp) {
-        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
-        if (f.dense == kRowTopK) return;
-        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
-    }
-    const int b = blockIdx.x;
-    if (threadIdx.x == 0) {
-        int n = 0;
-        bool counts = true;                  // tests count up to the first certain rejection
-        for (int j = 0; j < B; ++j) {
-            const int a = acc[(int64_t)b * B + j];
-            if (a == 3) s_rows[n++] = linear_row(batch, B, b, j);
-            if (a == 0) counts = false;
-            if (a == 2 && counts) {
-                const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
-                if (row_E[qr] > 0.0) s_rows[n++] = qr;
-                if (row_E[pr] > 0.0) s_rows[n++] = pr;
-            }
-        }
-        s_n = n;
-    }
-    __syncthreads();
-    const int n = s_n;
-    if (n == 0) return;
+    const int nc = dc.nchunks;
+    const int64_t tasks = (int64_t)(*count) * nc;
+    if ((int64_t)blockIdx.x * kDenseWaves >= tasks) return;
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nc = dc.nchunks;
-    const DenseExp ex{ log2e_over_T, s_exp2 };
     const int64_t row_bytes = N * Vec<BF16>::ESZ;
-    for (int k = 0; k < n; ++k) {
-        const int64_t r = s_rows[k];
-        const char* row = row_pointer(src, r, row_bytes);
-        for (int c = blockIdx.y * kDenseWaves + w; c < nc; c += gridDim.y * kDenseWaves)
-            exact_chunk_to<BF16>(row, N, r, c, dc, ex, lane);
+    for (int64_t t = (int64_t)blockIdx.x * kDenseWaves + w; t < tasks; t += (int64_t)gridDim.x * kDenseWaves) {
+        const int64_t r = rows[t / nc];
+        const int c = (int)(t - (t / nc) * nc);
+        const double c2 = rowp ? 1.4426950408889634074 / (double)rowp[r].temperature : log2e_over_T;
+        const DenseExp ex{ c2, s_exp2 };
+        exact_chunk_to<BF16>(row_pointer(src, r, row_bytes), N, r, c, dc, ex, lane);
     }
 }
 
@@ -1180,62 +1189,14 @@ __global__ __launch_bounds__(kProposeMaxThreads) void dense_settle_kernel(
     }
 }
 
-// Exact chunk statistics of the rows each request draws its last token from:
-// the target row p_j* and the draft row q_j* after a rejection (the residual
-// reads both), the bonus row p_B otherwise.  Rows the proposal kernel already
-// made exact (bound 0) are skipped.
+// Residual mass per chunk from exact terms and exact sums, for requests that
+// rejected a proposal (with redo: only those whose last draw was not certain).
 template <bool BF16>
-__global__ __launch_bounds__(kDenseThreads) void dense_exact_row_kernel(
+__global__ __launch_bounds__(kDenseThreads) void dense_residual_exact_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
-    const int32_t* jstar_in, const double* row_E, const FilterParams* rowp)
+    const int32_t* jstar_in, const int32_t* redo, double* resid, const FilterParams* rowp)
 {
-    __shared__ double s_exp2[kExp2Entries];
-    if (rowp) {                              // a nucleus request's rows are exact already
-        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
-        if (f.dense != kRowFull) return;
-        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
-    }
-    const int b = blockIdx.x;
-    const int js = jstar_in[b];
-    const int64_t pr = linear_row(batch, B, b, B + (js < B ? js : B));
-    const int64_t qr = js < B ? linear_row(batch, B, b, js) : -1;
-    const bool do_p = row_E[pr] > 0.0, do_q = qr >= 0 && row_E[qr] > 0.0;
-    if (!do_p && !do_q) return;
-    load_exp2_table(s_exp2);
-    __syncthreads();
-    const int lane = lane_id();
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nc = dc.nchunks;
-    const DenseExp ex{ log2e_over_T, s_exp2 };
-    // the rows' chunks dealt over gridDim.y workgroups, round robin over their waves
-    for (int k = 0; k < 2; ++k) {
-        const int64_t r = k == 0 ? pr : qr;
-        if (k == 0 ? !do_p : !do_q) continue;
-        const char* row = row_pointer(src, r, N * Vec<BF16>::ESZ);
-        for (int c = blockIdx.y * kDenseWaves + w; c < nc; c += gridDim.y * kDenseWaves) {
-            float x[kPerLane];
-            load_chunk<BF16>(row, N, c, x, lane);
-            float mx;
-            double sum;
-            uint32_t cntf;
-            chunk_stats_exact<true>(x, ex, &mx, &sum, &cntf);
-            if (lane == 0) {
-                const int64_t slot = r * nc + c;
-                dc.cmax[slot] = mx;
-                dc.csum[slot] = (mx < INFINITY) ? sum : NAN;
-                if (dc.ccount) dc.ccount[slot] = (int32_t)cntf;
-                if (dc.cerr) dc.cerr[slot] = 0.0f;
-            }
-        }
-    }
-}
-
-// Residual mass per chunk for requests that rejected a proposal.
-template <bool BF16>
-__global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
-    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
-    const float* row_m, const double* row_S, const int32_t* jstar_in, double* resid, const FilterParams* rowp)
-{
+    if (redo && !redo[blockIdx.x]) return;
     const int nc = dc.nchunks;
     __shared__ double s_exp2[kExp2Entries];
     if (rowp) {
@@ -1285,14 +1246,15 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
     }
 }
 
-// Residual (or bonus) sample and the cycle's outputs.
+// Residual (or bonus) sample from exact sums and the cycle's outputs (with
+// redo: only for the requests whose certified draw was not certain).
 template <bool BF16>
-__global__ __launch_bounds__(kWave) void dense_finish_kernel(
+__global__ __launch_bounds__(kWave) void dense_finish_exact_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
-    uint64_t seed, uint64_t offset, const uint32_t* req_ids, const float* row_m, const double* row_S,
-    const int32_t* jstar_in, const int32_t* y_in, const uint32_t* flag_in, const double* resid,
-    LinearOut o, const FilterParams* rowp)
+    uint64_t seed, uint64_t offset, const uint32_t* req_ids, const int32_t* jstar_in, const int32_t* y_in,
+    const uint32_t* flag_in, const int32_t* redo, const double* resid, LinearOut o, const FilterParams* rowp)
 {
+    if (redo && !redo[blockIdx.x]) return;
     __shared__ double s_exp2[kExp2Entries];
     if (rowp) {
         const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
@@ -1364,6 +1326,219 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
         fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp, d.u[2], ex, lane,
                                      row_keep(dc, pr));
     }
+    int32_t* tok = o.tokens + (int64_t)b * (B + 1);
+    for (int j = lane; j <= B; j += kWave) tok[j] = (j < js) ? y_in[(int64_t)b * B + j] : (j == js ? fin : -1);
+    if (lane == 0) {
+        o.accept_len[b] = js + 1;
+        if (o.flags) o.flags[b] = fl;
+    }
+}
+
+// Residual weights of chunk c from fp32 terms: r(x) = max(0, p(x) - q(x)) with
+// p(x) = t_p(x) * Ap, t_p = 2^y (y as in the chunk pass, relative to the
+// chunk's maximum) and Ap = (the chunk's scale to the row maximum) / Sp, the
+// same for q.  ResidualTerms holds one chunk of both rows in registers.
+struct ResidualChunk {
+    float mpc, mqc;         // chunk maxima of p and q
+    double Ap, Aq;          // chunk scale / row normaliser
+    float Ap32, Aq32;
+};
+
+__device__ __forceinline__ ResidualChunk residual_chunk(const DenseChunks& dc, int64_t pr, int64_t qr, int c,
+                                                        double mp, double Sp, double mq, double Sq, bool q_ok,
+                                                        double log2e_over_T)
+{
+    ResidualChunk k;
+    const int nc = dc.nchunks;
+    k.mpc = dc.cmax[pr * nc + c];
+    k.mqc = q_ok ? dc.cmax[qr * nc + c] : 0.0f;
+    k.Ap = (k.mpc > -INFINITY) ? exp2(((double)k.mpc - mp) * log2e_over_T) / Sp : 0.0;
+    k.Aq = (q_ok && k.mqc > -INFINITY) ? exp2(((double)k.mqc - mq) * log2e_over_T) / Sq : 0.0;
+    k.Ap32 = (float)k.Ap;
+    k.Aq32 = (float)k.Aq;
+    return k;
+}
+
+// One element's fp32 terms and residual weight.
+__device__ __forceinline__ float residual_weight(const ResidualChunk& k, float xp, float xq, bool kp, bool kq,
+                                                 float c32, float* tp, float* yp, float* tq, float* yq)
+{
+    *yp = fmaxf((xp - k.mpc) * c32, -200.0f);
+    *tp = kp ? __builtin_amdgcn_exp2f(*yp) : 0.0f;
+    *yq = fmaxf((xq - k.mqc) * c32, -200.0f);
+    *tq = kq ? __builtin_amdgcn_exp2f(*yq) : 0.0f;
+    return fmaxf(fmaf(*tp, k.Ap32, -(*tq * k.Aq32)), 0.0f);
+}
+
+// Residual mass per chunk for requests that rejected a proposal, from fp32
+// terms, and a bound on each chunk total's error: the terms' own error (as in
+// the chunk pass), the row normalisers' bounds, and 2^-22 of the chunk's p
+// and q mass for the fp32 products and difference (max(0, .) moves nothing
+// by more than its argument does).  The bound holds for every partial sum of
+// the chunk's weights too.
+template <bool BF16>
+__global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
+    const float* row_m, const double* row_S, const double* row_E, const int32_t* jstar_in, double* resid,
+    double* resid_err, const FilterParams* rowp)
+{
+    const int nc = dc.nchunks;
+    if (rowp) {
+        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
+        if (f.dense == kRowTopK) return;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int b = blockIdx.x;
+    const int c0 = blockIdx.y * kDenseWaves + w;
+    const int js = jstar_in[b];
+    if (js >= B || c0 >= nc) return;
+    const int64_t qr = linear_row(batch, B, b, js), pr = linear_row(batch, B, b, B + js);
+    const double Sp = row_S[pr], Sq = row_S[qr];
+    const bool q_ok = Sq > 0.0;
+    const double rp = (Sp > 0.0) ? row_E[pr] / Sp : 0.0, rq = q_ok ? row_E[qr] / Sq : 0.0;
+    const double mp = (double)row_m[pr], mq = (double)row_m[qr];
+    const float c32 = (float)log2e_over_T;
+    const int64_t row_bytes = N * Vec<BF16>::ESZ;
+    const uint64_t tp_thr = row_keep(dc, pr), tq_thr = row_keep(dc, qr);
+    constexpr int EPV = Vec<BF16>::EPV;
+    for (int c = c0; c < nc; c += gridDim.y * kDenseWaves) {
+        double total = 0.0, err = 0.0;
+        if (Sp > 0.0) {
+            float xp[kPerLane], xq[kPerLane];
+            load_chunk<BF16>(row_pointer(src, pr, row_bytes), N, c, xp, lane);
+            if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
+            const ResidualChunk k = residual_chunk(dc, pr, qr, c, mp, Sp, mq, Sq, q_ok, log2e_over_T);
+            float sp = 0.0f, typ = 0.0f, sq = 0.0f, tyq = 0.0f;
+            double r = 0.0;
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) {
+                const int64_t id = chunk_elem_id<EPV>(c, i, lane);
+                float tp, yp, tq, yq;
+                const float rw = residual_weight(k, xp[i], q_ok ? xq[i] : -INFINITY, dense_keeps(tp_thr, xp[i], id),
+                                                 q_ok && dense_keeps(tq_thr, xq[i], id), c32, &tp, &yp, &tq, &yq);
+                sp += tp;
+                typ = fmaf(tp, yp, typ);
+                sq += tq;
+                tyq = fmaf(tq, yq, tyq);
+                r += (double)rw;
+            }
+            total = wave_sum_f64(r);
+            const double SP = wave_sum_f64((double)sp), TYP = wave_sum_f64((double)typ);
+            const double SQ = wave_sum_f64((double)sq), TYQ = wave_sum_f64((double)tyq);
+            const double mass_p = k.Ap * SP, mass_q = k.Aq * SQ;
+            err = (1.0 + 2e-3) * (k.Ap * (kFastExpRel * SP - kFastArgRel * TYP) +
+                                  k.Aq * (kFastExpRel * SQ - kFastArgRel * TYQ) + mass_p * rp + mass_q * rq +
+                                  0x1p-22 * (mass_p + mass_q)) + 0x1p-100;
+        }
+        if (lane == 0) {
+            resid[(int64_t)b * nc + c] = total;
+            resid_err[(int64_t)b * nc + c] = err;
+        }
+    }
+}
+
+// Residual (or bonus) sample from the fast sums, certified against their
+// bounds, and the cycle's outputs for the requests where it is certain; the
+// rest are flagged for the exact kernels.
+template <bool BF16>
+__global__ __launch_bounds__(kWave) void dense_finish_kernel(
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
+    uint64_t seed, uint64_t offset, const uint32_t* req_ids, const float* row_m, const double* row_S,
+    const double* row_E, const int32_t* jstar_in, const int32_t* y_in, const uint32_t* flag_in, const double* resid,
+    const double* resid_err, int32_t* redo, int64_t* xrows1, LinearOut o, const FilterParams* rowp)
+{
+    __shared__ double s_exp2[kExp2Entries];
+    if (rowp) {
+        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
+        if (f.dense == kRowTopK) {
+            if (threadIdx.x == 0) redo[blockIdx.x] = 0;
+            return;
+        }
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
+    load_exp2_table(s_exp2);
+    __syncthreads();
+    const int lane = lane_id();
+    const int b = blockIdx.x;
+    const DenseExp ex{ log2e_over_T, s_exp2 };
+    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+    const int nc = dc.nchunks;
+    const int64_t row_bytes = N * Vec<BF16>::ESZ;
+    const int js = jstar_in[b];
+    const Draw d = uno_draw(seed, req, (uint32_t)js, offset);
+    uint32_t fl = flag_in[b];
+    int32_t fin = -1;
+    bool certain = true;
+    const int64_t pr = linear_row(batch, B, b, B + js);
+    const char* prow = row_pointer(src, pr, row_bytes);
+    const double Sp = row_S[pr];
+    if (!(Sp > 0.0)) {
+        fl |= 1u;
+    } else if (js < B) {
+        const int64_t qr = linear_row(batch, B, b, js);
+        const double Sq = row_S[qr];
+        const bool q_ok = Sq > 0.0;
+        const double* R = resid + (int64_t)b * nc;
+        const double* RE = resid_err + (int64_t)b * nc;
+        double Rtot = 0.0, Etot = 0.0;
+        for (int c = lane; c < nc; c += kWave) { Rtot += R[c]; Etot += RE[c]; }
+        Rtot = wave_sum_f64(Rtot);
+        Etot = wave_sum_f64(Etot);
+        certain = false;
+        if (Rtot > 2.0 * Etot) {             // certainly a positive residual
+            const double t = d.u[2] * Rtot;
+            auto rterm = [&](int c) { return R[c]; };
+            double before;
+            const int c = dense_locate(nc, t, rterm, lane, &before);
+            if (c >= 0) {
+                double eb = 0.0;
+                for (int k = lane; k < c; k += kWave) eb += RE[k];
+                eb = wave_sum_f64(eb);
+                float xp[kPerLane], xq[kPerLane];
+                load_chunk<BF16>(prow, N, c, xp, lane);
+                if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
+                const ResidualChunk k = residual_chunk(dc, pr, qr, c, (double)row_m[pr], Sp, (double)row_m[qr], Sq,
+                                                       q_ok, log2e_over_T);
+                const float c32 = (float)log2e_over_T;
+                const uint64_t tp_thr = row_keep(dc, pr), tq_thr = row_keep(dc, qr);
+                constexpr int EPV = Vec<BF16>::EPV;
+                auto wf = [&](int i) {
+                    const int64_t id = chunk_elem_id<EPV>(c, i, lane);
+                    float tp, yp, tq, yq;
+                    return (double)residual_weight(k, xp[i], q_ok ? xq[i] : -INFINITY, dense_keeps(tp_thr, xp[i], id),
+                                                   q_ok && dense_keeps(tq_thr, xq[i], id), c32, &tp, &yp, &tq, &yq);
+                };
+                double margin = -1.0;
+                const int l = pick_in_chunk<EPV>(wf, t - before, lane, &margin);
+                const double bound = d.u[2] * Etot + eb + RE[c] + 1e-12 * Rtot;
+                if (l >= 0 && margin > bound) {
+                    certain = true;
+                    fin = (int32_t)(c * (int64_t)kDenseChunk + l);
+                }
+            }
+        }
+    } else {
+        fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, row_m[pr], Sp, d.u[2], ex,
+                                     lane, row_keep(dc, pr), dc.cerr ? dc.cerr + pr * nc : nullptr, row_E[pr],
+                                     &certain);
+    }
+    if (lane == 0) {
+        redo[b] = certain ? 0 : 1;
+        if (!certain && dc.xcount != nullptr) {
+            // the rows the exact kernels need exact: p, and q after a rejection
+            const int64_t qr = js < B ? linear_row(batch, B, b, js) : -1;
+            const bool wp = row_E[pr] > 0.0, wq = qr >= 0 && row_E[qr] > 0.0;
+            const uint32_t n = (wp ? 1u : 0u) + (wq ? 1u : 0u);
+            if (n > 0) {
+                int64_t* out = xrows1 + atomicAdd(&dc.xcount[1], n);
+                if (wp) *out++ = pr;
+                if (wq) *out = qr;
+            }
+        }
+    }
+    if (!certain) return;
     int32_t* tok = o.tokens + (int64_t)b * (B + 1);
     for (int j = lane; j <= B; j += kWave) tok[j] = (j < js) ? y_in[(int64_t)b * B + j] : (j == js ? fin : -1);
     if (lane == 0) {
@@ -1905,45 +2080,79 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
     const int want = (2048 + batch - 1) / batch;
     const int gy = per_req < want ? per_req : want;
     const dim3 rgrid((unsigned)batch, (unsigned)gy);
+    // the exact residual runs for the few requests whose last draw was not
+    // certain: one chunk per wave for each of them
+    const dim3 xgrid((unsigned)batch, (unsigned)per_req);
+    const int64_t rows = (int64_t)batch * (2 * B + 1);
     // the proposals of a request run side by side: one wave each (4 to 8 waves)
     const int pw = B < kDenseWaves ? kDenseWaves : (B > kProposeMaxThreads / kWave ? kProposeMaxThreads / kWave : B);
     const unsigned pthreads = (unsigned)(pw * kWave);
     if (bf16) {
         dense_propose_kernel<true><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
-            sc.flags, rowp);
-        if (dc.cerr && !exact_all)
-            dense_redo_rows_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.acc,
-                                                                             sc.row_E, rowp);
+            sc.flags, sc.xrows, rowp);
+        if (dc.xcount && !exact_all)
+            dense_exact_list_kernel<true><<<dim3(kListGroups), kDenseThreads, 0, stream>>>(src, vocab, c, dc, sc.xrows,
+                                                                                       dc.xcount, rowp);
         dense_settle_kernel<true><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
             sc.jstar, sc.y, sc.flags, o, rowp);
-        if (!exact_all)
-            dense_exact_row_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
-                                                                             sc.row_E, rowp);
-        dense_residual_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(
-            src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid, rowp);
-        dense_finish_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
-            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
-            sc.flags, sc.resid, o, rowp);
+        if (exact_all) {
+            // every row exact already: exact residual and draw for every request
+            dense_residual_exact_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
+                                                                                  nullptr, sc.resid, rowp);
+            dense_finish_exact_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, nullptr, sc.resid, o,
+                rowp);
+        } else {
+            // certified draws from the fast sums; the exact kernels take the uncertain ones
+            dense_residual_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(
+                src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.resid, sc.resid_err, rowp);
+            dense_finish_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.y,
+                sc.flags, sc.resid, sc.resid_err, sc.fin_redo, sc.xrows + rows, o, rowp);
+            dense_exact_list_kernel<true><<<dim3(kListGroups), kDenseThreads, 0, stream>>>(src, vocab, c, dc,
+                                                                                       sc.xrows + rows, dc.xcount + 1,
+                                                                                       rowp);
+            dense_residual_exact_kernel<true><<<xgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
+                                                                                  sc.fin_redo, sc.resid, rowp);
+            dense_finish_exact_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, sc.fin_redo, sc.resid,
+                o, rowp);
+        }
     } else {
         dense_propose_kernel<false><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
-            sc.flags, rowp);
-        if (dc.cerr && !exact_all)
-            dense_redo_rows_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.acc,
-                                                                             sc.row_E, rowp);
+            sc.flags, sc.xrows, rowp);
+        if (dc.xcount && !exact_all)
+            dense_exact_list_kernel<false><<<dim3(kListGroups), kDenseThreads, 0, stream>>>(src, vocab, c, dc, sc.xrows,
+                                                                                       dc.xcount, rowp);
         dense_settle_kernel<false><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
             sc.jstar, sc.y, sc.flags, o, rowp);
-        if (!exact_all)
-            dense_exact_row_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
-                                                                             sc.row_E, rowp);
-        dense_residual_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(
-            src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.jstar, sc.resid, rowp);
-        dense_finish_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
-            src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.jstar, sc.y,
-            sc.flags, sc.resid, o, rowp);
+        if (exact_all) {
+            // every row exact already: exact residual and draw for every request
+            dense_residual_exact_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
+                                                                                  nullptr, sc.resid, rowp);
+            dense_finish_exact_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, nullptr, sc.resid, o,
+                rowp);
+        } else {
+            // certified draws from the fast sums; the exact kernels take the uncertain ones
+            dense_residual_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(
+                src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.resid, sc.resid_err, rowp);
+            dense_finish_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.y,
+                sc.flags, sc.resid, sc.resid_err, sc.fin_redo, sc.xrows + rows, o, rowp);
+            dense_exact_list_kernel<false><<<dim3(kListGroups), kDenseThreads, 0, stream>>>(src, vocab, c, dc,
+                                                                                       sc.xrows + rows, dc.xcount + 1,
+                                                                                       rowp);
+            dense_residual_exact_kernel<false><<<xgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
+                                                                                  sc.fin_redo, sc.resid, rowp);
+            dense_finish_exact_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, sc.fin_redo, sc.resid,
+                o, rowp);
+        }
     }
     return hipGetLastError();
 }

@@ -182,6 +182,7 @@ DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bo
     dc.csum = cv.take<double>((size_t)rows * dc.nchunks);
     dc.ccount = counts ? cv.take<int32_t>((size_t)rows * dc.nchunks) : nullptr;
     dc.cerr = err ? cv.take<float>((size_t)rows * dc.nchunks) : nullptr;
+    dc.xcount = err ? cv.take<uint32_t>(2) : nullptr;
     dc.keep = keep ? cv.take<uint64_t>((size_t)rows) : nullptr;
     return dc;
 }
@@ -197,6 +198,9 @@ DenseScratch carve_dense_scratch(Carve& cv, int64_t rows, int32_t batch, int32_t
     s.acc = cv.take<int32_t>((size_t)batch * B);
     s.flags = cv.take<uint32_t>((size_t)batch);
     s.resid = cv.take<double>((size_t)batch * nchunks);
+    s.resid_err = cv.take<double>((size_t)batch * nchunks);
+    s.fin_redo = cv.take<int32_t>((size_t)batch);
+    s.xrows = cv.take<int64_t>((size_t)2 * rows);
     return s;
 }
 
