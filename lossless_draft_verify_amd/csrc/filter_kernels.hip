@@ -906,7 +906,7 @@ __global__ __launch_bounds__(kThreads, 5) void dense_chunk_kernel(
     constexpr int NV = PER_LANE / EPV;                      // vectors per lane
     __shared__ double s_exp2[kExp2Entries];
     // the samplers' exact-row list counters start every call at 0
-    if (dc.xcount != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) dc.xcount[threadIdx.x] = 0u;
+    if (dc.xcount != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 3) dc.xcount[threadIdx.x] = 0u;
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r = blockIdx.x;

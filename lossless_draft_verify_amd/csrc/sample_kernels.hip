@@ -640,7 +640,8 @@ constexpr int kDenseThreads = 256;
 constexpr int kProposeMaxThreads = 512;    // dense_propose_kernel: up to eight waves, one proposal each at a time
 constexpr int kDenseWaves = kDenseThreads / kWave;
 constexpr int kPerLane = kDenseChunk / kWave;   // 32 logits per lane per chunk
-constexpr int kListGroups = 1024;              // workgroups of dense_exact_list_kernel
+constexpr int kListGroups = 768;               // workgroups of dense_exact_list_kernel (one round)
+constexpr int kExactJobs = 24;                 // grid rows of the exact fallback kernels over listed requests
 
 // Chunk c of a row into registers: element (j*64 + lane)*EPV + e at x[j*EPV + e];
 // -inf past the end of the row.
@@ -1190,28 +1191,33 @@ __global__ __launch_bounds__(kProposeMaxThreads) void dense_settle_kernel(
 }
 
 // Residual mass per chunk from exact terms and exact sums, for requests that
-// rejected a proposal (with redo: only those whose last draw was not certain).
+// rejected a proposal: every request (one per blockIdx.x) or, with a list,
+// the listed requests (those whose certified draw was not certain), dealt
+// over the grid's rows.
 template <bool BF16>
 __global__ __launch_bounds__(kDenseThreads) void dense_residual_exact_kernel(
-    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
-    const int32_t* jstar_in, const int32_t* redo, double* resid, const FilterParams* rowp)
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T0, DenseChunks dc,
+    const int32_t* jstar_in, const int32_t* list, const uint32_t* list_n, double* resid, const FilterParams* rowp)
 {
-    if (redo && !redo[blockIdx.x]) return;
+    const int njobs = list ? (int)*list_n : (int)gridDim.x;
+    if ((int)blockIdx.x >= njobs) return;
     const int nc = dc.nchunks;
     __shared__ double s_exp2[kExp2Entries];
-    if (rowp) {
-        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
-        if (f.dense == kRowTopK) return;
-        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
-    }
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int b = blockIdx.x;
+    for (int job = blockIdx.x; job < njobs; job += gridDim.x) {
+    const int b = list ? list[job] : job;
+    double log2e_over_T = log2e_over_T0;
+    if (rowp) {
+        const FilterParams& f = rowp[(int64_t)b * B];
+        if (f.dense == kRowTopK) continue;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
     const int c0 = blockIdx.y * kDenseWaves + w;
     const int js = jstar_in[b];
-    if (js >= B || c0 >= nc) return;
+    if (js >= B || c0 >= nc) continue;
     const DenseExp ex{ log2e_over_T, s_exp2 };
     const int64_t qr = linear_row(batch, B, b, js), pr = linear_row(batch, B, b, B + js);
     float mpf;
@@ -1244,27 +1250,33 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_exact_kernel(
         }
         if (lane == 0) resid[(int64_t)b * nc + c] = total;
     }
+    }
 }
 
-// Residual (or bonus) sample from exact sums and the cycle's outputs (with
-// redo: only for the requests whose certified draw was not certain).
+// Residual (or bonus) sample from exact sums and the cycle's outputs: every
+// request (one per workgroup) or, with a list, the listed requests (those
+// whose certified draw was not certain), dealt over the workgroups.
 template <bool BF16>
 __global__ __launch_bounds__(kWave) void dense_finish_exact_kernel(
-    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
+    RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T0, DenseChunks dc,
     uint64_t seed, uint64_t offset, const uint32_t* req_ids, const int32_t* jstar_in, const int32_t* y_in,
-    const uint32_t* flag_in, const int32_t* redo, const double* resid, LinearOut o, const FilterParams* rowp)
+    const uint32_t* flag_in, const int32_t* list, const uint32_t* list_n, const double* resid, LinearOut o,
+    const FilterParams* rowp)
 {
-    if (redo && !redo[blockIdx.x]) return;
+    const int njobs = list ? (int)*list_n : (int)gridDim.x;
+    if ((int)blockIdx.x >= njobs) return;
     __shared__ double s_exp2[kExp2Entries];
-    if (rowp) {
-        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
-        if (f.dense == kRowTopK) return;
-        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
-    }
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
-    const int b = blockIdx.x;
+    for (int job = blockIdx.x; job < njobs; job += gridDim.x) {
+    const int b = list ? list[job] : job;
+    double log2e_over_T = log2e_over_T0;
+    if (rowp) {
+        const FilterParams& f = rowp[(int64_t)b * B];
+        if (f.dense == kRowTopK) continue;
+        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+    }
     const DenseExp ex{ log2e_over_T, s_exp2 };
     const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
     const int nc = dc.nchunks;
@@ -1332,6 +1344,7 @@ __global__ __launch_bounds__(kWave) void dense_finish_exact_kernel(
         o.accept_len[b] = js + 1;
         if (o.flags) o.flags[b] = fl;
     }
+    }
 }
 
 // Residual weights of chunk c from fp32 terms: r(x) = max(0, p(x) - q(x)) with
@@ -1376,7 +1389,7 @@ __device__ __forceinline__ float residual_weight(const ResidualChunk& k, float x
 // and q mass for the fp32 products and difference (max(0, .) moves nothing
 // by more than its argument does).  The bound holds for every partial sum of
 // the chunk's weights too.
-template <bool BF16>
+template <bool BF16, bool KEEP>
 __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
     const float* row_m, const double* row_S, const double* row_E, const int32_t* jstar_in, double* resid,
@@ -1412,12 +1425,20 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
             const ResidualChunk k = residual_chunk(dc, pr, qr, c, mp, Sp, mq, Sq, q_ok, log2e_over_T);
             float sp = 0.0f, typ = 0.0f, sq = 0.0f, tyq = 0.0f;
             double r = 0.0;
+            // without keep thresholds (KEEP false: no nucleus rows) the
+            // per-logit support test is skipped: a NaN or -inf logit's clamped
+            // term 2^-200 is far below the bound's 2^-100
 #pragma unroll
             for (int i = 0; i < kPerLane; ++i) {
-                const int64_t id = chunk_elem_id<EPV>(c, i, lane);
+                bool kp = true, kq = q_ok;
+                if constexpr (KEEP) {
+                    const int64_t id = chunk_elem_id<EPV>(c, i, lane);
+                    kp = dense_keeps(tp_thr, xp[i], id);
+                    kq = q_ok && dense_keeps(tq_thr, xq[i], id);
+                }
                 float tp, yp, tq, yq;
-                const float rw = residual_weight(k, xp[i], q_ok ? xq[i] : -INFINITY, dense_keeps(tp_thr, xp[i], id),
-                                                 q_ok && dense_keeps(tq_thr, xq[i], id), c32, &tp, &yp, &tq, &yq);
+                const float rw = residual_weight(k, xp[i], q_ok ? xq[i] : -INFINITY, kp, kq, c32, &tp, &yp, &tq,
+                                                 &yq);
                 sp += tp;
                 typ = fmaf(tp, yp, typ);
                 sq += tq;
@@ -1447,7 +1468,7 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
     uint64_t seed, uint64_t offset, const uint32_t* req_ids, const float* row_m, const double* row_S,
     const double* row_E, const int32_t* jstar_in, const int32_t* y_in, const uint32_t* flag_in, const double* resid,
-    const double* resid_err, int32_t* redo, int64_t* xrows1, LinearOut o, const FilterParams* rowp)
+    const double* resid_err, int32_t* redo, int64_t* xrows1, int32_t* xreq, LinearOut o, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
     if (rowp) {
@@ -1527,6 +1548,7 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
     if (lane == 0) {
         redo[b] = certain ? 0 : 1;
         if (!certain && dc.xcount != nullptr) {
+            xreq[atomicAdd(&dc.xcount[2], 1u)] = b;
             // the rows the exact kernels need exact: p, and q after a rejection
             const int64_t qr = js < B ? linear_row(batch, B, b, js) : -1;
             const bool wp = row_E[pr] > 0.0, wq = qr >= 0 && row_E[qr] > 0.0;
@@ -2082,7 +2104,7 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
     const dim3 rgrid((unsigned)batch, (unsigned)gy);
     // the exact residual runs for the few requests whose last draw was not
     // certain: one chunk per wave for each of them
-    const dim3 xgrid((unsigned)batch, (unsigned)per_req);
+    const dim3 xgrid((unsigned)kExactJobs, (unsigned)per_req);
     const int64_t rows = (int64_t)batch * (2 * B + 1);
     // the proposals of a request run side by side: one wave each (4 to 8 waves)
     const int pw = B < kDenseWaves ? kDenseWaves : (B > kProposeMaxThreads / kWave ? kProposeMaxThreads / kWave : B);
@@ -2100,25 +2122,29 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
         if (exact_all) {
             // every row exact already: exact residual and draw for every request
             dense_residual_exact_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
-                                                                                  nullptr, sc.resid, rowp);
+                                                                                  nullptr, nullptr, sc.resid, rowp);
             dense_finish_exact_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
-                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, nullptr, sc.resid, o,
-                rowp);
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, nullptr, nullptr,
+                sc.resid, o, rowp);
         } else {
             // certified draws from the fast sums; the exact kernels take the uncertain ones
-            dense_residual_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(
-                src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.resid, sc.resid_err, rowp);
+            if (dc.keep)
+                dense_residual_kernel<true, true><<<rgrid, kDenseThreads, 0, stream>>>(
+                    src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.resid, sc.resid_err, rowp);
+            else
+                dense_residual_kernel<true, false><<<rgrid, kDenseThreads, 0, stream>>>(
+                    src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.resid, sc.resid_err, rowp);
             dense_finish_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
                 src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.y,
-                sc.flags, sc.resid, sc.resid_err, sc.fin_redo, sc.xrows + rows, o, rowp);
+                sc.flags, sc.resid, sc.resid_err, sc.fin_redo, sc.xrows + rows, sc.xreq, o, rowp);
             dense_exact_list_kernel<true><<<dim3(kListGroups), kDenseThreads, 0, stream>>>(src, vocab, c, dc,
                                                                                        sc.xrows + rows, dc.xcount + 1,
                                                                                        rowp);
             dense_residual_exact_kernel<true><<<xgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
-                                                                                  sc.fin_redo, sc.resid, rowp);
-            dense_finish_exact_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
-                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, sc.fin_redo, sc.resid,
-                o, rowp);
+                                                                                  sc.xreq, dc.xcount + 2, sc.resid, rowp);
+            dense_finish_exact_kernel<true><<<dim3(kExactJobs), kWave, 0, stream>>>(
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, sc.xreq,
+                dc.xcount + 2, sc.resid, o, rowp);
         }
     } else {
         dense_propose_kernel<false><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
@@ -2133,25 +2159,29 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
         if (exact_all) {
             // every row exact already: exact residual and draw for every request
             dense_residual_exact_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
-                                                                                  nullptr, sc.resid, rowp);
+                                                                                  nullptr, nullptr, sc.resid, rowp);
             dense_finish_exact_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
-                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, nullptr, sc.resid, o,
-                rowp);
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, nullptr, nullptr,
+                sc.resid, o, rowp);
         } else {
             // certified draws from the fast sums; the exact kernels take the uncertain ones
-            dense_residual_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(
-                src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.resid, sc.resid_err, rowp);
+            if (dc.keep)
+                dense_residual_kernel<false, true><<<rgrid, kDenseThreads, 0, stream>>>(
+                    src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.resid, sc.resid_err, rowp);
+            else
+                dense_residual_kernel<false, false><<<rgrid, kDenseThreads, 0, stream>>>(
+                    src, batch, B, vocab, c, dc, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.resid, sc.resid_err, rowp);
             dense_finish_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
                 src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.jstar, sc.y,
-                sc.flags, sc.resid, sc.resid_err, sc.fin_redo, sc.xrows + rows, o, rowp);
+                sc.flags, sc.resid, sc.resid_err, sc.fin_redo, sc.xrows + rows, sc.xreq, o, rowp);
             dense_exact_list_kernel<false><<<dim3(kListGroups), kDenseThreads, 0, stream>>>(src, vocab, c, dc,
                                                                                        sc.xrows + rows, dc.xcount + 1,
                                                                                        rowp);
             dense_residual_exact_kernel<false><<<xgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
-                                                                                  sc.fin_redo, sc.resid, rowp);
-            dense_finish_exact_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
-                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, sc.fin_redo, sc.resid,
-                o, rowp);
+                                                                                  sc.xreq, dc.xcount + 2, sc.resid, rowp);
+            dense_finish_exact_kernel<false><<<dim3(kExactJobs), kWave, 0, stream>>>(
+                src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, sc.xreq,
+                dc.xcount + 2, sc.resid, o, rowp);
         }
     }
     return hipGetLastError();

@@ -182,7 +182,7 @@ DenseChunks carve_chunks(Carve& cv, int64_t rows, int64_t vocab, bool counts, bo
     dc.csum = cv.take<double>((size_t)rows * dc.nchunks);
     dc.ccount = counts ? cv.take<int32_t>((size_t)rows * dc.nchunks) : nullptr;
     dc.cerr = err ? cv.take<float>((size_t)rows * dc.nchunks) : nullptr;
-    dc.xcount = err ? cv.take<uint32_t>(2) : nullptr;
+    dc.xcount = err ? cv.take<uint32_t>(3) : nullptr;
     dc.keep = keep ? cv.take<uint64_t>((size_t)rows) : nullptr;
     return dc;
 }
@@ -201,6 +201,7 @@ DenseScratch carve_dense_scratch(Carve& cv, int64_t rows, int32_t batch, int32_t
     s.resid_err = cv.take<double>((size_t)batch * nchunks);
     s.fin_redo = cv.take<int32_t>((size_t)batch);
     s.xrows = cv.take<int64_t>((size_t)2 * rows);
+    s.xreq = cv.take<int32_t>((size_t)batch);
     return s;
 }
 

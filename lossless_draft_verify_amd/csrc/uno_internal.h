@@ -69,8 +69,9 @@ struct DenseChunks {
     // [rows][nchunks] bound on |csum - exact sum| for chunks summed with fp32
     // exponentials (0 for exact chunks), or nullptr when every row is exact
     float* cerr;
-    // [2] counters of the linear samplers' lists of rows to make exact, set to
-    // 0 by the chunk pass (which runs before any sampler appends), or nullptr
+    // [3] counters of the linear samplers' lists (two of rows to make exact,
+    // one of requests), set to 0 by the chunk pass (which runs before any
+    // sampler appends), or nullptr
     uint32_t* xcount;
     int32_t nchunks;
     // [rows] keep thresholds of a full-vocabulary nucleus, or nullptr: logit i of
@@ -170,6 +171,7 @@ struct DenseScratch {
     double* resid_err; // [batch][nchunks] bound on |resid - exact| of the fp32 residual totals
     int32_t* fin_redo; // [batch] the last draw was not certain: the exact kernels take it again
     int64_t* xrows;    // [2][batch * (2B + 1)] rows to make exact: after the draws, after the last draw
+    int32_t* xreq;     // [batch] requests whose last draw the exact kernels take
 };
 
 // With exact_all every row's chunk sums are already exact (the nucleus needs
