@@ -425,7 +425,11 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
 {
     using V = Vec<BF16>;
     constexpr int EPV = V::EPV, ESZ = V::ESZ;
-    constexpr int U = kStreamVecs;                     // 16-byte vectors per lane per iteration
+    // 16-byte vectors per lane per iteration and iterations in flight: the
+    // joint variant, fp64-bound, keeps four vectors with one iteration ahead
+    // so its running sum is rescaled half as often
+    constexpr int U = JOINT ? 4 : kStreamVecs;
+    constexpr int DEPTH = JOINT ? 2 : kStreamDepth;
     constexpr int kPerIter = U * EPV;                  // logits per lane per iteration
     // a streaming cut must leave room for one whole vector of candidates per lane
     constexpr int kCutLimit = (kCap - kWave * EPV < kCap / 2) ? kCap - kWave * EPV : kCap / 2;
@@ -612,14 +616,14 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
         }
     };
 
-    // Whole iterations, kStreamDepth - 1 of them loaded ahead of the one being
+    // Whole iterations, DEPTH - 1 of them loaded ahead of the one being
     // processed: two vectors per lane per iteration with two iterations ahead
     // keep more loads in flight per byte of registers than four vectors with
     // one ahead (a read-only sweep of the same 1088-row split: 104.7 against
     // 112.8 us for 661 MB).
     constexpr int64_t kStep = (int64_t)U * kWave;
     const int64_t nfull = (we - wb) / kStep;
-    typename V::T xr[kStreamDepth][U];
+    typename V::T xr[DEPTH][U];
     // Iteration i's vectors.  Past the last whole iteration the loads only keep
     // the pipeline's shape: on 4-byte rows one vector per u for every lane (a
     // few cache lines), on 2-byte rows a re-read of the last iteration
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     };
     if (nfull > 0) {
 #pragma unroll
-        for (int d = 0; d < kStreamDepth - 1; ++d) load_iter(d, xr[d]);
+        for (int d = 0; d < DEPTH - 1; ++d) load_iter(d, xr[d]);
         if (cnt == 0 && k <= kWave) {
             // Seed the threshold from the first two iterations (only the first
             // when there is no second: a shape-only load holds one lane's data):
@@ -644,7 +648,7 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
                     mx = fmaxf(mx, V::get(xr[0][u], e));
-                    if (kStreamDepth > 2 && nfull > 1) mx = fmaxf(mx, V::get(xr[1][u], e));
+                    if (DEPTH > 2 && nfull > 1) mx = fmaxf(mx, V::get(xr[1][u], e));
                 }
             uint32_t km = float_key(mx);
             km = (km <= kKeyPosInf && km > kKeyNegInf) ? km : kKeyNegInf;
@@ -653,10 +657,10 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
         }
     }
     for (int64_t it = 0; it < nfull; ++it) {
-        load_iter(it + kStreamDepth - 1, xr[kStreamDepth - 1]);
+        load_iter(it + DEPTH - 1, xr[DEPTH - 1]);
         process(xr[0], wb + it * kStep);
 #pragma unroll
-        for (int d = 0; d < kStreamDepth - 1; ++d)
+        for (int d = 0; d < DEPTH - 1; ++d)
 #pragma unroll
             for (int u = 0; u < U; ++u) xr[d][u] = xr[d + 1][u];
     }
