@@ -672,6 +672,51 @@ __device__ __forceinline__ void load_chunk(const char* row, int64_t N, int64_t c
     }
 }
 
+// Chunk c of a row as the raw vectors load_chunk reads (same element layout:
+// entry i is element (i/EPV*64 + lane)*EPV + i%EPV); -inf past the end of the
+// row.  Half the registers of the unpacked floats for 2-byte rows.
+template <bool BF16>
+struct RawChunk {
+    using V = Vec<BF16>;
+    static constexpr int EPV = V::EPV, NV = kPerLane / EPV;
+    typename V::T v[NV];
+
+    __device__ __forceinline__ void load(const char* row, int64_t N, int64_t c, int lane)
+    {
+        const int64_t beg = c * kDenseChunk;
+        const int64_t n = (N - beg < kDenseChunk) ? (N - beg) : kDenseChunk;
+        if (n == kDenseChunk && (((uintptr_t)(row + beg * V::ESZ)) & 15u) == 0) {
+            const typename V::T* p = reinterpret_cast<const typename V::T*>(row + beg * V::ESZ);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) v[j] = V::load_stream(p + j * kWave + lane);
+            return;
+        }
+        // offsets from one per-lane base and compile-time constants, so that
+        // nothing here is worth hoisting out of a caller's loop
+        const int lim = (int)n - lane * EPV;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int k0 = j * kWave * EPV;
+            if constexpr (BF16) {
+                const uint16_t* h = reinterpret_cast<const uint16_t*>(row) + beg + lane * EPV;
+                uint32_t wd[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = (k0 + 2 * e < lim) ? h[k0 + 2 * e] : 0xFF80u;
+                    const uint32_t hi = (k0 + 2 * e + 1 < lim) ? h[k0 + 2 * e + 1] : 0xFF80u;
+                    wd[e] = lo | (hi << 16);
+                }
+                v[j] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            } else {
+                const float* f = reinterpret_cast<const float*>(row) + beg + lane * EPV;
+                v[j] = make_float4(k0 < lim ? f[k0] : -INFINITY, k0 + 1 < lim ? f[k0 + 1] : -INFINITY,
+                                   k0 + 2 < lim ? f[k0 + 2] : -INFINITY, k0 + 3 < lim ? f[k0 + 3] : -INFINITY);
+            }
+        }
+    }
+    __device__ __forceinline__ float get(int i) const { return V::get(v[i / EPV], i % EPV); }
+};
+
 // Chunk-stat term of chunk c relative to the row max m.
 __device__ __forceinline__ double chunk_term(const float* cm, const double* cs, int c, float m, const DenseExp& ex)
 {
@@ -1384,11 +1429,15 @@ __device__ __forceinline__ float residual_weight(const ResidualChunk& k, float x
 }
 
 // Residual mass per chunk for requests that rejected a proposal, from fp32
-// terms, and a bound on each chunk total's error: the terms' own error (as in
-// the chunk pass), the row normalisers' bounds, and 2^-22 of the chunk's p
-// and q mass for the fp32 products and difference (max(0, .) moves nothing
-// by more than its argument does).  The bound holds for every partial sum of
-// the chunk's weights too.
+// terms, and a bound on each chunk total's error: the terms' own error, the
+// row normalisers' bounds, and 2^-22 of the chunk's p and q mass for the fp32
+// products and difference (max(0, .) moves nothing by more than its argument
+// does).  The bound holds for every partial sum of the chunk's weights too.
+// The terms are the chunk pass's own (same maximum, same fp32 arithmetic), so
+// for rows whose chunk sums are still the fast ones (row bound > 0) and
+// without keep thresholds, the chunk pass's error and sum bound them; rows
+// made exact since then have lost those, and their term errors are summed
+// here from the terms.
 template <bool BF16, bool KEEP>
 __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
@@ -1408,50 +1457,75 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_kernel(
     const int js = jstar_in[b];
     if (js >= B || c0 >= nc) return;
     const int64_t qr = linear_row(batch, B, b, js), pr = linear_row(batch, B, b, B + js);
-    const double Sp = row_S[pr], Sq = row_S[qr];
-    const bool q_ok = Sq > 0.0;
-    const double rp = (Sp > 0.0) ? row_E[pr] / Sp : 0.0, rq = q_ok ? row_E[qr] / Sq : 0.0;
-    const double mp = (double)row_m[pr], mq = (double)row_m[qr];
-    const float c32 = (float)log2e_over_T;
     const int64_t row_bytes = N * Vec<BF16>::ESZ;
+    const char* prow = row_pointer(src, pr, row_bytes);
+    const char* qrow = row_pointer(src, qr, row_bytes);
+    const float c32 = (float)log2e_over_T;
     const uint64_t tp_thr = row_keep(dc, pr), tq_thr = row_keep(dc, qr);
     constexpr int EPV = Vec<BF16>::EPV;
     for (int c = c0; c < nc; c += gridDim.y * kDenseWaves) {
+        // the chunk's loads go out with the row statistics' (both rows exist
+        // whatever their statistics say)
+        RawChunk<BF16> xp, xq;
+        xp.load(prow, N, c, lane);
+        xq.load(qrow, N, c, lane);
+        const double Sp = row_S[pr], Sq = row_S[qr];
+        const double Ep = row_E[pr], Eq = row_E[qr];
+        const bool q_ok = Sq > 0.0;
         double total = 0.0, err = 0.0;
         if (Sp > 0.0) {
-            float xp[kPerLane], xq[kPerLane];
-            load_chunk<BF16>(row_pointer(src, pr, row_bytes), N, c, xp, lane);
-            if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
-            const ResidualChunk k = residual_chunk(dc, pr, qr, c, mp, Sp, mq, Sq, q_ok, log2e_over_T);
-            float sp = 0.0f, typ = 0.0f, sq = 0.0f, tyq = 0.0f;
-            double r = 0.0;
-            // without keep thresholds (KEEP false: no nucleus rows) the
-            // per-logit support test is skipped: a NaN or -inf logit's clamped
-            // term 2^-200 is far below the bound's 2^-100
+            const double rp = Ep / Sp, rq = q_ok ? Eq / Sq : 0.0;
+            const ResidualChunk k = residual_chunk(dc, pr, qr, c, (double)row_m[pr], Sp, (double)row_m[qr], Sq, q_ok,
+                                                   log2e_over_T);
+            const bool light = !KEEP && dc.cerr != nullptr && Ep > 0.0 && (!q_ok || Eq > 0.0);
+            double tep, teq, mass_p, mass_q;     // term errors and masses, scaled to the row normalisers
+            if (light) {
+                double r = 0.0;
 #pragma unroll
-            for (int i = 0; i < kPerLane; ++i) {
-                bool kp = true, kq = q_ok;
-                if constexpr (KEEP) {
-                    const int64_t id = chunk_elem_id<EPV>(c, i, lane);
-                    kp = dense_keeps(tp_thr, xp[i], id);
-                    kq = q_ok && dense_keeps(tq_thr, xq[i], id);
+                for (int i = 0; i < kPerLane; ++i) {
+                    float tp, yp, tq, yq;
+                    r += (double)residual_weight(k, xp.get(i), q_ok ? xq.get(i) : -INFINITY, true, q_ok, c32, &tp,
+                                                 &yp, &tq, &yq);
                 }
-                float tp, yp, tq, yq;
-                const float rw = residual_weight(k, xp[i], q_ok ? xq[i] : -INFINITY, kp, kq, c32, &tp, &yp, &tq,
-                                                 &yq);
-                sp += tp;
-                typ = fmaf(tp, yp, typ);
-                sq += tq;
-                tyq = fmaf(tq, yq, tyq);
-                r += (double)rw;
+                total = wave_sum_f64(r);
+                const int64_t sp_ = pr * nc + c, sq_ = qr * nc + c;
+                const double ep = (double)dc.cerr[sp_], eq = q_ok ? (double)dc.cerr[sq_] : 0.0;
+                tep = k.Ap * ep;
+                teq = k.Aq * eq;
+                mass_p = k.Ap * (dc.csum[sp_] + ep);
+                mass_q = q_ok ? k.Aq * (dc.csum[sq_] + eq) : 0.0;
+            } else {
+                float sp = 0.0f, typ = 0.0f, sq = 0.0f, tyq = 0.0f;
+                double r = 0.0;
+                // without keep thresholds (KEEP false: no nucleus rows) the
+                // per-logit support test is skipped: a NaN or -inf logit's
+                // clamped term 2^-200 is far below the bound's 2^-100
+#pragma unroll
+                for (int i = 0; i < kPerLane; ++i) {
+                    const float vp = xp.get(i), vq = xq.get(i);
+                    bool kp = true, kq = q_ok;
+                    if constexpr (KEEP) {
+                        const int64_t id = chunk_elem_id<EPV>(c, i, lane);
+                        kp = dense_keeps(tp_thr, vp, id);
+                        kq = q_ok && dense_keeps(tq_thr, vq, id);
+                    }
+                    float tp, yp, tq, yq;
+                    const float rw = residual_weight(k, vp, q_ok ? vq : -INFINITY, kp, kq, c32, &tp, &yp, &tq, &yq);
+                    sp += tp;
+                    typ = fmaf(tp, yp, typ);
+                    sq += tq;
+                    tyq = fmaf(tq, yq, tyq);
+                    r += (double)rw;
+                }
+                total = wave_sum_f64(r);
+                const double SP = wave_sum_f64((double)sp), TYP = wave_sum_f64((double)typ);
+                const double SQ = wave_sum_f64((double)sq), TYQ = wave_sum_f64((double)tyq);
+                tep = k.Ap * (kFastExpRel * SP - kFastArgRel * TYP);
+                teq = k.Aq * (kFastExpRel * SQ - kFastArgRel * TYQ);
+                mass_p = k.Ap * SP;
+                mass_q = k.Aq * SQ;
             }
-            total = wave_sum_f64(r);
-            const double SP = wave_sum_f64((double)sp), TYP = wave_sum_f64((double)typ);
-            const double SQ = wave_sum_f64((double)sq), TYQ = wave_sum_f64((double)tyq);
-            const double mass_p = k.Ap * SP, mass_q = k.Aq * SQ;
-            err = (1.0 + 2e-3) * (k.Ap * (kFastExpRel * SP - kFastArgRel * TYP) +
-                                  k.Aq * (kFastExpRel * SQ - kFastArgRel * TYQ) + mass_p * rp + mass_q * rq +
-                                  0x1p-22 * (mass_p + mass_q)) + 0x1p-100;
+            err = (1.0 + 2e-3) * (tep + teq + mass_p * rp + mass_q * rq + 0x1p-22 * (mass_p + mass_q)) + 0x1p-100;
         }
         if (lane == 0) {
             resid[(int64_t)b * nc + c] = total;
