@@ -173,16 +173,6 @@ __device__ __forceinline__ float thr_float(uint32_t t)
     return key_float(t == 0x7FFFFFFFu ? 0x7FFFFFFEu : t);
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
-{
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) {
-        const uint32_t o = __shfl_xor(v, d, kWave);
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
 // Filter-order position key: larger means earlier (key desc, then id asc).
 
 // Block-wide ranking of the candidates held in L lists (list o: lst[o*stride ..
@@ -707,7 +697,7 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     }
     if constexpr (JOINT) {
         if (jrow) {    // the wave's maximum and sum relative to it
-            const uint32_t kw = wave_max_u32(float_key(jm));
+            const uint32_t kw = wave_ext_u32<true>(float_key(jm));
             const float mw = key_float(kw);
             double part = (jm > -INFINITY) ? js * jex((double)jm - (double)mw) : 0.0;
             part = wave_sum_f64(part);
@@ -856,16 +846,22 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
             if (ns == k) p = s_kth[lane];
             pq = (ns >= quota) ? s_qth[lane] : 0ull;
         }
-#pragma unroll
-        for (int d = kWave / 2; d >= 1; d >>= 1) {
-            const uint64_t po = __shfl_xor(p, d, kWave);
-            const uint64_t qo = __shfl_xor(pq, d, kWave);
-            const uint32_t to = __shfl_xor(top, d, kWave);
+        // DPP reductions (the wave_ext_u32 pattern): the results land in lane 63
+        auto step = [&](auto ctrl, auto rmask) __attribute__((always_inline)) {
+            constexpr int C = decltype(ctrl)::value, M = decltype(rmask)::value;
+            const uint64_t po = dpp_u64<C, M>(p, p), qo = dpp_u64<C, M>(pq, pq);
+            const uint32_t to = (uint32_t)__builtin_amdgcn_update_dpp((int)top, (int)top, C, M, 0xF, false);
             p = po > p ? po : p;
             pq = qo < pq ? qo : pq;
             top = to > top ? to : top;
-        }
-        if (lane == 0) {
+        };
+        step(std::integral_constant<int, 0xB1>(), std::integral_constant<int, 0xF>());
+        step(std::integral_constant<int, 0x4E>(), std::integral_constant<int, 0xF>());
+        step(std::integral_constant<int, 0x141>(), std::integral_constant<int, 0xF>());
+        step(std::integral_constant<int, 0x140>(), std::integral_constant<int, 0xF>());
+        step(std::integral_constant<int, 0x142>(), std::integral_constant<int, 0xA>());
+        step(std::integral_constant<int, 0x143>(), std::integral_constant<int, 0xC>());
+        if (lane == kWave - 1) {
             s_bound = pq > p ? pq : p;
             s_top = top;
             s_n = 0;
@@ -887,7 +883,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(
         const uint64_t m = __ballot(keep);
         int pos0 = 0;
         if (lane == 0 && m) pos0 = atomicAdd(&s_n, __popcll(m));
-        pos0 = __shfl(pos0, 0, kWave);
+        pos0 = __builtin_amdgcn_readlane(pos0, 0);
         if (keep) s_cand[pos0 + __popcll(m & lanes_below(lane))] = make_uint2(ck[j], (uint32_t)ci[j]);
     }
     __syncthreads();
@@ -1006,7 +1002,7 @@ __global__ __launch_bounds__(kThreads, 5) void dense_chunk_kernel(
         float mx = -INFINITY;
 #pragma unroll 1
         for (int i = lane; i < n; i += kWave) mx = fmaxf(mx, load_scalar<BF16>(base, i));
-        mx = wave_max_f32(mx);
+        mx = wave_max_f32_lds(mx);
         double sum = 0.0, ty = 0.0;
         uint32_t cntf = 0;
         if (mx > -INFINITY && mx < INFINITY) {
@@ -1029,8 +1025,8 @@ __global__ __launch_bounds__(kThreads, 5) void dense_chunk_kernel(
                 }
             }
         }
-        sum = wave_sum_f64(sum);
-        ty = wave_sum_f64(ty);
+        sum = wave_sum_f64_lds(sum);
+        ty = wave_sum_f64_lds(ty);
         if (lane == 0) {
             const int64_t slot = r * nc + c;
             dc.cmax[slot] = mx;

@@ -324,35 +324,18 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
 // Everything a pop touches lives in registers, spread over the lanes: entry
 // (or node, or depth) i sits in lane i % 64 of slot i / 64.  The frontier is
 // an unordered set; each pop is a wave maximum of the score's high word, and
-// only lanes that tie on it go on to the low word and then the tie word.  The
-// only memory access of a pop is the next sibling's probability, from the
-// candidate table (first K ids and probabilities of each depth's filtered
-// row) staged in LDS.
+// only lanes that tie on it go on to the low word and then the tie word.
+// Each entry carries its parent's score and the probability of its next
+// sibling, so the pop that takes it writes that sibling (parent score times
+// probability, the product the oracle forms) without a memory access; the
+// probability of the sibling after it is read from the candidate table (first
+// K ids and probabilities of each depth's filtered row, staged in LDS) while
+// the rest of the pop runs.  Per-depth counts and first two probabilities sit
+// in registers, read by uniform lane index.
 
 __device__ __forceinline__ uint32_t tree_tie(int depth, int parent, int rank)
 {
     return ((uint32_t)depth << 20) | ((uint32_t)parent << 12) | (uint32_t)rank;
-}
-
-// Lane (i % 64) of slot (i / 64), i uniform.
-template <int N>
-__device__ __forceinline__ int slot_get_i32(const int (&a)[N], int i)
-{
-    int r = 0;
-#pragma unroll
-    for (int q = 0; q < N; ++q)
-        if ((i >> 6) == q) r = __builtin_amdgcn_readlane(a[q], i & (kWave - 1));
-    return r;
-}
-
-template <int N>
-__device__ __forceinline__ double slot_get_f64(const double (&a)[N], int i)
-{
-    double r = 0.0;
-#pragma unroll
-    for (int q = 0; q < N; ++q)
-        if ((i >> 6) == q) r = readlane_f64(a[q], i & (kWave - 1));
-    return r;
 }
 
 // FS register slots per lane for the frontier and for the node records: at
@@ -362,6 +345,31 @@ __device__ __forceinline__ double slot_get_f64(const double (&a)[N], int i)
 // alone then expands the tree.
 constexpr int kBuildThreads = 256;
 constexpr int kBuildPer = kMaxTreeVK / kBuildThreads;     // table entries per thread
+
+// Slot i / 64 of lane i % 64 of a per-lane array (i uniform), without branches.
+template <int N>
+__device__ __forceinline__ int sel_i32(const int (&a)[N], int i)
+{
+    int r = __builtin_amdgcn_readlane(a[0], i & (kWave - 1));
+#pragma unroll
+    for (int q = 1; q < N; ++q) {
+        const int v = __builtin_amdgcn_readlane(a[q], i & (kWave - 1));
+        r = (i >> 6) == q ? v : r;
+    }
+    return r;
+}
+
+template <int N>
+__device__ __forceinline__ double sel_f64(const double (&a)[N], int i)
+{
+    double r = readlane_f64(a[0], i & (kWave - 1));
+#pragma unroll
+    for (int q = 1; q < N; ++q) {
+        const double v = readlane_f64(a[q], i & (kWave - 1));
+        r = (i >> 6) == q ? v : r;
+    }
+    return r;
+}
 
 template <int FS>
 __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch, int32_t B, int32_t K, int32_t V,
@@ -374,25 +382,28 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
     const int b = blockIdx.x;
     const int cap = sup.cap;
     const int64_t rbase = (int64_t)b * B;
-    // per depth (B <= 128): candidate count (at most K) and first probability
+    const int kk = K < cap ? K : cap;
+    // per depth (B <= 128): candidate count (at most K), first and second
+    // probability (-1 when there is no second candidate)
     int cn[2];
-    double p0[2];
+    double p0[2], p1[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const int d = s * kWave + lane;
         int n = 0;
-        double f = 0.0;
+        double f0 = 0.0, f1 = -1.0;
         if (d < B && threadIdx.x < kWave) {
             n = sup.count[rbase + d];
-            f = sup.probs[(rbase + d) * cap];
+            f0 = sup.probs[(rbase + d) * cap];
+            if (kk > 1) f1 = sup.probs[(rbase + d) * cap + 1];
         }
         cn[s] = n > 0 ? (n < K ? n : K) : 0;
-        p0[s] = f;
+        p0[s] = f0;
+        p1[s] = cn[s] > 1 ? f1 : -1.0;
     }
     // the candidate table is read whole (supports are padded to cap); entries
     // past a count are never used
     {
-        const int kk = K < cap ? K : cap;
         int32_t tid[kBuildPer];
         double tpr[kBuildPer];
 #pragma unroll
@@ -421,21 +432,32 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
 
     uint64_t fs[FS];                                   // frontier: score bits (0 = empty)
     uint32_t ft[FS];                                   // frontier: tie word (~0 = empty)
+    double fp[FS];                                     // frontier: parent's score
+    double fn[FS];                                     // frontier: next sibling's probability (-1: none)
     double ns[FS];                                     // node records: score
     uint32_t nt[FS];                                   // node records: tie word of the entry
 #pragma unroll
-    for (int q = 0; q < FS; ++q) { fs[q] = 0ull; ft[q] = ~0u; ns[q] = 0.0; nt[q] = 0u; }
+    for (int q = 0; q < FS; ++q) { fs[q] = 0ull; ft[q] = ~0u; fp[q] = 0.0; fn[q] = -1.0; ns[q] = 0.0; nt[q] = 0u; }
     if (lane == 0) ns[0] = 1.0;
-    auto put = [&](int slot, double sc, uint32_t tie) __attribute__((always_inline)) {
-        const int qs = slot >> 6, ls = slot & (kWave - 1);
+    auto put = [&](int slot, double sc, uint32_t tie, double psc, double nsp) __attribute__((always_inline)) {
+        const int qs = slot >> 6;
+        const bool mine = lane == (slot & (kWave - 1));
 #pragma unroll
-        for (int q = 0; q < FS; ++q)
-            if (q == qs && lane == ls) { fs[q] = (uint64_t)__double_as_longlong(sc); ft[q] = tie; }
+        for (int q = 0; q < FS; ++q) {
+            const bool m = mine && q == qs;
+            fs[q] = m ? (uint64_t)__double_as_longlong(sc) : fs[q];
+            ft[q] = m ? tie : ft[q];
+            fp[q] = m ? psc : fp[q];
+            fn[q] = m ? nsp : fn[q];
+        }
     };
 
     int nf = 0;                                        // slots handed out (uniform)
     int live = 0;
-    if (__builtin_amdgcn_readlane(cn[0], 0) > 0) { put(nf++, 1.0 * readlane_f64(p0[0], 0), tree_tie(1, 0, 0)); ++live; }
+    if (sel_i32(cn, 0) > 0) {
+        put(nf++, 1.0 * sel_f64(p0, 0), tree_tie(1, 0, 0), 1.0, sel_f64(p1, 0));
+        ++live;
+    }
     int num = 1;
     while (num <= V && live > 0) {
         // this lane's best slot
@@ -463,26 +485,38 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
         const int wq = __builtin_amdgcn_readlane(bq, wl);
         const double score = __longlong_as_double(
             (long long)(((uint64_t)hm << 32) | (uint32_t)__builtin_amdgcn_readlane((int)bl, wl)));
-        // the owner of the winning entry frees its slot, which the sibling reuses
+        const int slot = wq * kWave + wl;
+        double psc = readlane_f64(fp[0], wl), nsp = readlane_f64(fn[0], wl);
 #pragma unroll
-        for (int q = 0; q < FS; ++q)
-            if (lane == wl && q == wq) { fs[q] = 0ull; ft[q] = ~0u; }
-        --live;
+        for (int q = 1; q < FS; ++q) {
+            const double a = readlane_f64(fp[q], wl), c = readlane_f64(fn[q], wl);
+            psc = wq == q ? a : psc;
+            nsp = wq == q ? c : nsp;
+        }
         const int depth = (int)(tie >> 20), parent = (int)((tie >> 12) & 0xFFu), rank = (int)(tie & 0xFFFu);
-        int si = (depth - 1) * K + rank + 1;
+        // the probability of the sibling after the next one, from LDS; used last
+        int si = (depth - 1) * K + rank + 2;
         si = si < kMaxTreeVK ? si : kMaxTreeVK - 1;
-        const double sp = c_p[si];
+        const double sp2 = c_p[si];
+        const bool has2 = rank + 2 < sel_i32(cn, depth - 1);
+        // the node
 #pragma unroll
-        for (int q = 0; q < FS; ++q)
-            if (q == (num >> 6) && lane == (num & (kWave - 1))) { ns[q] = score; nt[q] = tie; }
-        if (rank + 1 < slot_get_i32(cn, depth - 1)) {
-            put(wq * kWave + wl, slot_get_f64(ns, parent) * sp, tree_tie(depth, parent, rank + 1));
+        for (int q = 0; q < FS; ++q) {
+            const bool m = q == (num >> 6) && lane == (num & (kWave - 1));
+            ns[q] = m ? score : ns[q];
+            nt[q] = m ? tie : nt[q];
+        }
+        // its first child in a new slot
+        const bool child = depth < B && sel_i32(cn, depth) > 0;
+        if (child) {
+            put(nf++, score * sel_f64(p0, depth), tree_tie(depth + 1, num, 0), score, sel_f64(p1, depth));
             ++live;
         }
-        if (depth < B && slot_get_i32(cn, depth) > 0) {
-            put(nf++, score * slot_get_f64(p0, depth), tree_tie(depth + 1, num, 0));
-            ++live;
-        }
+        // its next sibling in the slot it leaves (or the slot emptied)
+        const bool sib = !(nsp < 0.0);
+        put(slot, sib ? psc * nsp : 0.0, sib ? tree_tie(depth, parent, rank + 1) : ~0u, psc,
+            (sib && has2) ? sp2 : -1.0);
+        live -= sib ? 0 : 1;
         ++num;
     }
     const int64_t ob = (int64_t)b * (V + 1);
@@ -744,7 +778,7 @@ __device__ bool dense_row_stat(const float* cm, const double* cs, int nc, const 
         const int c = base + lane;
         const double term = (c < nc) ? chunk_term(cm, cs, c, m, ex) : 0.0;
         const double incl = wave_incl_scan_f64(term, lane);
-        S += __shfl(incl, kWave - 1, kWave);
+        S += lane_value(incl, kWave - 1);
         if (ce != nullptr && c < nc && cm[c] > -INFINITY) E += (double)ce[c] * ex((double)cm[c] - (double)m);
     }
     if (E_out) *E_out = (ce != nullptr) ? wave_sum_f64(E) * (1.0 + 1e-6) : 0.0;
@@ -766,10 +800,10 @@ __device__ int dense_locate(int nc, double t, TermF term_of, int lane, double* b
         const uint64_t hit = __ballot(c < nc && term > 0.0 && C + incl > t);
         if (hit) {
             const int l = wave_first_lane(hit);
-            *before = C + __shfl(incl - term, l, kWave);
+            *before = C + lane_value(incl - term, l);
             return base + l;
         }
-        C += __shfl(incl, kWave - 1, kWave);
+        C += lane_value(incl, kWave - 1);
     }
     *before = C;
     return -1;
@@ -782,7 +816,7 @@ __device__ int dense_last_positive_chunk(int nc, TermF term_of, int lane)
     int best = -1;
     for (int c = lane; c < nc; c += kWave)
         if (term_of(c) > 0.0) best = c;
-    for (int d = kWave / 2; d >= 1; d >>= 1) best = max(best, __shfl_xor(best, d, kWave));
+    best = wave_max_i32(best);
     return best;
 }
 
@@ -829,13 +863,13 @@ __device__ int pick_in_chunk(WeightF wf, double tau, int lane, double* margin = 
                         if (ep < 0 && wl[e] > 0.0) ep = e;
                 }
             }
-            ep = __shfl(ep, l, kWave);
-            if (margin) *margin = __shfl(mg, l, kWave);
+            ep = lane_value(ep, l);
+            if (margin) *margin = lane_value(mg, l);
             return (j * kWave + l) * EPV + ep;
         }
-        run += __shfl(incl, kWave - 1, kWave);
+        run += lane_value(incl, kWave - 1);
     }
-    for (int d = kWave / 2; d >= 1; d >>= 1) last_pos = max(last_pos, __shfl_xor(last_pos, d, kWave));
+    last_pos = wave_max_i32(last_pos);
     if (margin) *margin = -1.0;
     return last_pos;
 }
@@ -852,7 +886,7 @@ __device__ double chunk_total(WeightF wf, int lane)
 #pragma unroll
         for (int e = 0; e < EPV; ++e) lsum += wf(j * EPV + e);
         const double incl = wave_incl_scan_f64(lsum, lane);
-        run += __shfl(incl, kWave - 1, kWave);
+        run += lane_value(incl, kWave - 1);
     }
     return run;
 }
@@ -943,12 +977,14 @@ __device__ __forceinline__ float load_one(const char* row, int64_t i)
     }
 }
 
-// Proposals and acceptance in three kernels.  Rows may carry fast chunk sums
+// Proposals and acceptance in four kernels.  Rows may carry fast chunk sums
 // with error bounds (dc.cerr): every draw and every acceptance test is
 // certified against them.
-//  - dense_propose_kernel: row statistics, the draws, and the acceptance test
-//    of every proposal whose draw is certain.  acc[j]: 1 accepted, 0
-//    rejected, 2 test not certain, 3 draw not certain.
+//  - dense_row_stat_kernel (chip-wide, one wave per row): every row's
+//    maximum, normaliser and bound.
+//  - dense_propose_kernel: the draws, and the acceptance test of every
+//    proposal whose draw is certain.  acc[j]: 1 accepted, 0 rejected, 2 test
+//    not certain, 3 draw not certain.
 //  - dense_exact_list_kernel (chip-wide): exact chunk sums for the rows those
 //    uncertain results read (the first exact-row list, which the proposal
 //    kernel fills): q_j of an uncertain draw; q_j and p_j of an uncertain
@@ -1021,6 +1057,85 @@ __device__ __forceinline__ int propose_test(const RowSource& src, int32_t batch,
     return (lhs < py) ? 1 : 0;
 }
 
+// Every row's maximum, normaliser and bound from its chunk statistics, two
+// rows per wave (rows of the linear layout; with per-request sets each at its
+// own temperature, top-k rows skipped).  For rows of at most 128 chunks every
+// load of both rows is issued before any is used; the sums are dense_row_stat's
+// (the same terms, scans and order), so the statistics are the same.
+constexpr int kRowStatThreads = 1024;
+constexpr int kRowStatWaves = kRowStatThreads / kWave;
+
+__global__ __launch_bounds__(kRowStatThreads) void dense_row_stat_kernel(int64_t rows, double log2e_over_T,
+                                                                         DenseChunks dc, float* row_m, double* row_S,
+                                                                         double* row_E, const FilterParams* rowp)
+{
+    __shared__ double s_exp2[kExp2Entries];
+    load_exp2_table(s_exp2);
+    __syncthreads();
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t r0 = 2 * ((int64_t)blockIdx.x * kRowStatWaves + w);
+    if (r0 >= rows) return;
+    const int nc = dc.nchunks;
+    bool on[2];
+    double c2[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int64_t r = r0 + k;
+        on[k] = r < rows;
+        c2[k] = log2e_over_T;
+        if (on[k] && rowp) {
+            const FilterParams& f = rowp[r];
+            on[k] = f.dense != kRowTopK;
+            c2[k] = 1.4426950408889634074 / (double)f.temperature;
+        }
+    }
+    if (nc > 2 * kWave) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            if (on[k]) row_stat_to(dc, r0 + k, DenseExp{ c2[k], s_exp2 }, lane, row_m, row_S, row_E);
+        return;
+    }
+    float cm[2][2], ce[2][2];
+    double cs[2][2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = q * kWave + lane;
+            const bool in = on[k] && c < nc;
+            const int64_t slot = (r0 + k) * nc + c;
+            cm[k][q] = in ? dc.cmax[slot] : -INFINITY;
+            cs[k][q] = in ? dc.csum[slot] : 0.0;
+            ce[k][q] = (in && dc.cerr) ? dc.cerr[slot] : 0.0f;
+        }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (!on[k]) continue;
+        const DenseExp ex{ c2[k], s_exp2 };
+        float m = fmaxf(cm[k][0], cm[k][1]);
+        const bool bad = __ballot(cm[k][0] == INFINITY || cm[k][1] == INFINITY) != 0ull;
+        m = wave_max_f32(m);
+        double S = NAN, E = 0.0;
+        if (!bad && m > -INFINITY) {
+            S = 0.0;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (q * kWave >= nc) break;
+                const double sc = (cm[k][q] > -INFINITY) ? ex((double)cm[k][q] - (double)m) : 0.0;
+                const double term = cm[k][q] > -INFINITY ? cs[k][q] * sc : 0.0;
+                const double incl = wave_incl_scan_f64(term, lane);
+                S += lane_value(incl, kWave - 1);
+                E += (double)ce[k][q] * sc;
+            }
+            E = dc.cerr ? wave_sum_f64(E) * (1.0 + 1e-6) : 0.0;
+        } else {
+            m = NAN;
+        }
+        if (lane == 0) { row_m[r0 + k] = m; row_S[r0 + k] = S; row_E[r0 + k] = E; }
+    }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kProposeMaxThreads) void dense_propose_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T, DenseChunks dc,
@@ -1044,8 +1159,6 @@ __global__ __launch_bounds__(kProposeMaxThreads) void dense_propose_kernel(
     const int b = blockIdx.x;
     const DenseExp ex{ log2e_over_T, s_exp2 };
     const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
-    for (int i = w; i < 2 * B + 1; i += nw) row_stat_to(dc, linear_row(batch, B, b, i), ex, lane, row_m, row_S, row_E);
-    __syncthreads();
     uint32_t flags = 0;
     for (int j = w; j < B; j += nw) {
         bool certain;
@@ -1349,7 +1462,7 @@ __global__ __launch_bounds__(kWave) void dense_finish_exact_kernel(
         for (int base = 0; base < nc; base += kWave) {
             const int c = base + lane;
             const double incl = wave_incl_scan_f64(c < nc ? R[c] : 0.0, lane);
-            Rtot += __shfl(incl, kWave - 1, kWave);
+            Rtot += lane_value(incl, kWave - 1);
         }
         if (Rtot > 0.0) {
             const double t = d.u[2] * Rtot;
@@ -1810,18 +1923,18 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
                 if (hit) {
                     const int l = wave_first_lane(hit);
                     found = top - l;
-                    fa = run + __shfl(incl - mb, l, kWave);
-                    fc = crun + __shfl(cincl - cb, l, kWave);
+                    fa = run + lane_value(incl - mb, l);
+                    fc = crun + lane_value(cincl - cb, l);
                 } else {
                     const uint64_t nz = __ballot(filled);
                     if (nz) {
                         const int l = 63 - __clzll((long long)nz);
                         last = top - l;
-                        la = run + __shfl(incl - mb, l, kWave);
-                        lc = crun + __shfl(cincl - cb, l, kWave);
+                        la = run + lane_value(incl - mb, l);
+                        lc = crun + lane_value(cincl - cb, l);
                     }
-                    run += __shfl(incl, kWave - 1, kWave);
-                    crun += __shfl(cincl, kWave - 1, kWave);
+                    run += lane_value(incl, kWave - 1);
+                    crun += lane_value(cincl, kWave - 1);
                 }
             }
             if (found < 0) { found = last; fa = la; fc = lc; }   // target past the summed mass: keep all
@@ -1927,7 +2040,7 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
                     const double incl = wave_incl_scan_f64(e, lane);
                     const uint64_t hit = __ballot(j < (int)ntot && run + incl >= target);
                     if (hit) jcut = top + wave_first_lane(hit);
-                    run += __shfl(incl, kWave - 1, kWave);
+                    run += lane_value(incl, kWave - 1);
                 }
                 if (jcut < 0) jcut = (int)ntot - 1;
                 if (lane == 0) s_bin = jcut;
@@ -1939,8 +2052,8 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
             // run's kept candidates
             for (int c = w; c < nc; c += kNucWaves) {
                 const int q = (c - w) / kNucWaves;
-                const int b = __shfl(run_b, q, kWave), e = __shfl(run_e, q, kWave);
-                const double ab = __shfl(above, q, kWave);
+                const int b = lane_value(run_b, q), e = lane_value(run_e, q);
+                const double ab = lane_value(above, q);
                 const float mcf = cm[c];
                 double add = 0.0;
                 if (mcf > -INFINITY)
@@ -2019,7 +2132,7 @@ __global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, 
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) nl += (finite_f32(x[j * EPV + e]) && float_key(x[j * EPV + e]) == tau) ? 1 : 0;
                 const double incl = wave_incl_scan_f64((double)nl, lane);
-                const double tot = __shfl(incl, kWave - 1, kWave);
+                const double tot = lane_value(incl, kWave - 1);
                 if ((double)need <= tot) {
                     const uint64_t at = __ballot((double)need <= incl && (double)need > incl - (double)nl);
                     const int l = wave_first_lane(at);
@@ -2184,6 +2297,8 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
     const int pw = B < kDenseWaves ? kDenseWaves : (B > kProposeMaxThreads / kWave ? kProposeMaxThreads / kWave : B);
     const unsigned pthreads = (unsigned)(pw * kWave);
     if (bf16) {
+        dense_row_stat_kernel<<<dim3((unsigned)((rows + 2 * kRowStatWaves - 1) / (2 * kRowStatWaves))), kRowStatThreads, 0,
+                                stream>>>(rows, c, dc, sc.row_m, sc.row_S, sc.row_E, rowp);
         dense_propose_kernel<true><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
             sc.flags, sc.xrows, rowp);
@@ -2221,6 +2336,8 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
                 dc.xcount + 2, sc.resid, o, rowp);
         }
     } else {
+        dense_row_stat_kernel<<<dim3((unsigned)((rows + 2 * kRowStatWaves - 1) / (2 * kRowStatWaves))), kRowStatThreads, 0,
+                                stream>>>(rows, c, dc, sc.row_m, sc.row_S, sc.row_E, rowp);
         dense_propose_kernel<false><<<dim3((unsigned)batch), pthreads, 0, stream>>>(
             src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.row_m, sc.row_S, sc.row_E, sc.y, sc.acc,
             sc.flags, sc.xrows, rowp);

@@ -105,34 +105,112 @@ __device__ __forceinline__ Draw uno_draw(uint64_t seed, uint32_t req, uint32_t p
 }
 
 // ---- wave reductions --------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane)
+// All on the VALU's DPP lane moves (no LDS round trips): within each 16-lane
+// row first, then across rows by broadcasting lane 15 of a row into the next
+// row and lane 31 into rows 2-3.  DPP controls: quad_perm [1,0,3,2] 0xB1,
+// [2,3,0,1] 0x4E; row_shr:n 0x110+n; row_mirror 0x140; row_half_mirror 0x141;
+// row_bcast:15 0x142; row_bcast:31 0x143.  A lane whose row the row mask
+// leaves out, or whose row_shr source lies before its row, receives `old`.
+
+// Value of lane l (l uniform).
+__device__ __forceinline__ double readlane_f64(double v, int l)
 {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
-    return v;
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ double lane_value(double v, int l) { return readlane_f64(v, l); }
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v, double old)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v), o = (uint64_t)__double_as_longlong(old);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)o, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF,
+                                                              false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(o >> 32), (int)(uint32_t)(b >> 32), CTRL,
+                                                              ROW_MASK, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v, uint64_t old)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)old, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF,
+                                                              false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(old >> 32), (int)(uint32_t)(v >> 32), CTRL,
+                                                              ROW_MASK, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v, float old)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xF,
+                                                      false));
+}
+
+// Inclusive prefix sum over the wave's lanes (in lane order).
 __device__ __forceinline__ double wave_incl_scan_f64(double v, int lane)
 {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const double o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
+    (void)lane;
+    v += dpp_f64<0x111>(v, 0.0);
+    v += dpp_f64<0x112>(v, 0.0);
+    v += dpp_f64<0x114>(v, 0.0);
+    v += dpp_f64<0x118>(v, 0.0);
+    v += dpp_f64<0x142, 0xA>(v, 0.0);
+    v += dpp_f64<0x143, 0xC>(v, 0.0);
     return v;
 }
 
+// Sum over the wave, returned to every lane.
 __device__ __forceinline__ double wave_sum_f64(double v)
+{
+    v += dpp_f64<0xB1>(v, 0.0);
+    v += dpp_f64<0x4E>(v, 0.0);
+    v += dpp_f64<0x141>(v, 0.0);
+    v += dpp_f64<0x140>(v, 0.0);
+    v += dpp_f64<0x142, 0xA>(v, 0.0);
+    v += dpp_f64<0x143, 0xC>(v, 0.0);
+    return readlane_f64(v, kWave - 1);
+}
+
+// Maximum over the wave, returned to every lane.
+__device__ __forceinline__ int wave_max_i32(int v)
+{
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+// Maximum over the wave (NaN lanes ignored, as fmaxf does), returned to every lane.
+__device__ __forceinline__ float wave_max_f32(float v)
+{
+    v = fmaxf(v, dpp_f32<0xB1>(v, v));
+    v = fmaxf(v, dpp_f32<0x4E>(v, v));
+    v = fmaxf(v, dpp_f32<0x141>(v, v));
+    v = fmaxf(v, dpp_f32<0x140>(v, v));
+    v = fmaxf(v, dpp_f32<0x142, 0xA>(v, v));
+    v = fmaxf(v, dpp_f32<0x143, 0xC>(v, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// The same sum and maximum by LDS butterflies (ds_bpermute): slower to
+// return, but they leave the VALU to a kernel that streams at the HBM rate
+// with fp32 work per element (the dense chunk pass).
+__device__ __forceinline__ double wave_sum_f64_lds(double v)
 {
 #pragma unroll
     for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
     return v;
 }
 
-__device__ __forceinline__ float wave_max_f32(float v)
+__device__ __forceinline__ float wave_max_f32_lds(float v)
 {
 #pragma unroll
     for (int d = kWave / 2; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
@@ -159,15 +237,6 @@ __device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v)
     v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
     v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
     return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
-}
-
-// Lane l's value of a double (l uniform).
-__device__ __forceinline__ double readlane_f64(double v, int l)
-{
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // ---- logit rows --------------------------------------------------------------
@@ -308,7 +377,7 @@ __device__ __forceinline__ void chunk_stats_exact(const float (&x)[PER_LANE], co
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) mx = fmaxf(mx, x[i]);
-    mx = wave_max_f32(mx);
+    mx = wave_max_f32_lds(mx);
     double s0 = 0.0, s1 = 0.0;
     uint32_t cntf = 0;
     if (mx > -INFINITY && mx < INFINITY) {
@@ -329,7 +398,7 @@ __device__ __forceinline__ void chunk_stats_exact(const float (&x)[PER_LANE], co
         }
     }
     *m_out = mx;
-    *s_out = wave_sum_f64(s0 + s1);
+    *s_out = wave_sum_f64_lds(s0 + s1);
     *cnt_out = cntf;
 }
 
@@ -358,7 +427,7 @@ __device__ __forceinline__ void chunk_stats_fast(const float (&x)[PER_LANE], flo
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) mx = fmaxf(mx, x[i]);
-    mx = wave_max_f32(mx);
+    mx = wave_max_f32_lds(mx);
     double s = 0.0;
     float a = 0.0f;            // sum of t * y (every y <= 0)
     uint32_t cntf = 0;
@@ -374,8 +443,8 @@ __device__ __forceinline__ void chunk_stats_fast(const float (&x)[PER_LANE], flo
         }
     }
     *m_out = mx;
-    s = wave_sum_f64(s);
-    const double ty = wave_sum_f64((double)a);
+    s = wave_sum_f64_lds(s);
+    const double ty = wave_sum_f64_lds((double)a);
     *s_out = s;
     *err_out = (float)((1.0 + 2e-3) * (kFastExpRel * s - kFastArgRel * ty) + 0x1p-114);
     *cnt_out = cntf;
