@@ -414,11 +414,16 @@ __device__ __forceinline__ void chunk_stats_exact(const float (&x)[PER_LANE], co
 //    exponential's curvature at |y| <= 200);
 //  - y is clamped at -200 (NaN, -inf and negligible terms) and results below
 //    2^-126 may flush to 0: at most 2^-126 per term.
-// So |sum - exact| <= kFastExpRel * sum + kFastArgRel * sum(t * |y|) + 2048 * 2^-126;
-// the factor (1 + 2e-3) covers the fp32 sum of t * |y|, the fp64 sums and the
-// rounding of the result to float.
+//  - the terms are added four at a time in fp32 (a two-level tree of
+//    non-negative values: within 2^-23 relative of each group's sum, plus at
+//    most 2^-126 per addition flushed) before each group joins the fp64 sum:
+//    kFastSumRel = 2^-23 of the sum.
+// So |sum - exact| <= (kFastExpRel + kFastSumRel) * sum + kFastArgRel * sum(t * |y|)
+// + 3584 * 2^-126; the factor (1 + 2e-3) covers the fp32 sum of t * |y|, the
+// fp64 sums and the rounding of the result to float.
 constexpr double kFastExpRel = 0x1p-23;
 constexpr double kFastArgRel = 1.2397e-7;
+constexpr double kFastSumRel = 0x1p-23;
 
 template <bool COUNT, int PER_LANE>
 __device__ __forceinline__ void chunk_stats_fast(const float (&x)[PER_LANE], float log2e_over_T, float* m_out,
@@ -432,21 +437,26 @@ __device__ __forceinline__ void chunk_stats_fast(const float (&x)[PER_LANE], flo
     float a = 0.0f;            // sum of t * y (every y <= 0)
     uint32_t cntf = 0;
     if (mx > -INFINITY && mx < INFINITY) {
+        static_assert(PER_LANE % 4 == 0, "terms are summed four at a time");
 #pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) {
-            if (COUNT) cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i])));
-            // NaN and -inf give y = NaN or -inf, which the clamp maps to -200
-            const float y = fmaxf((x[i] - mx) * log2e_over_T, -200.0f);
-            const float t = __builtin_amdgcn_exp2f(y);
-            s += (double)t;
-            a = fmaf(t, y, a);
+        for (int i = 0; i < PER_LANE; i += 4) {
+            float t4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (COUNT) cntf += (uint32_t)__popcll(__ballot(finite_f32(x[i + e])));
+                // NaN and -inf give y = NaN or -inf, which the clamp maps to -200
+                const float y = fmaxf((x[i + e] - mx) * log2e_over_T, -200.0f);
+                t4[e] = __builtin_amdgcn_exp2f(y);
+                a = fmaf(t4[e], y, a);
+            }
+            s += (double)((t4[0] + t4[1]) + (t4[2] + t4[3]));
         }
     }
     *m_out = mx;
     s = wave_sum_f64_lds(s);
     const double ty = wave_sum_f64_lds((double)a);
     *s_out = s;
-    *err_out = (float)((1.0 + 2e-3) * (kFastExpRel * s - kFastArgRel * ty) + 0x1p-114);
+    *err_out = (float)((1.0 + 2e-3) * ((kFastExpRel + kFastSumRel) * s - kFastArgRel * ty) + 0x1p-114);
     *cnt_out = cntf;
 }
 
