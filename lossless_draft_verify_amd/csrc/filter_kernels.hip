@@ -490,6 +490,19 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
         t = __builtin_amdgcn_readfirstlane(t);
         if (t > thr_key) { thr_key = t; thr = thr_float(t); }
     };
+    // An early cut while the list is still short (at most kSmallCut entries,
+    // read with four slots per lane): the seed threshold admits the upper tail
+    // of the first logits seen, and raising it at kSmallCut entries costs a
+    // third of a full-buffer cut and usually leaves none to do.  Only for a
+    // wave range of at least kSmallCutRange iterations (a short range seldom
+    // fills the buffer at all).
+    constexpr int kSmallE = 4, kSmallCut = kSmallE * kWave, kSmallCutRange = 16;
+    auto small_cut = [&]() __attribute__((always_inline)) {
+        uint32_t t;
+        cnt = __builtin_amdgcn_readfirstlane(wave_cut<kSmallE>(buf, cnt, k, kSmallCut / 2, lane, &t));
+        t = __builtin_amdgcn_readfirstlane(t);
+        if (t > thr_key) { thr_key = t; thr = thr_float(t); }
+    };
     auto scalar_part = [&](int64_t beg, int64_t n) __attribute__((always_inline)) {   // n <= 64, ids increase with lane
         if (cnt > kCap - kWave) compact();
         float v = 0.0f;
@@ -580,6 +593,17 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
         int total = 0;
 #pragma unroll
         for (int i = 0; i < kPerIter; ++i) total += __popcll(m[i]);
+        if (k <= kSmallCut / 4 && cnt >= 2 * k && cnt <= kSmallCut && cnt + total > kSmallCut &&
+            we - wb >= (int64_t)kSmallCutRange * U * kWave) {
+            small_cut();
+            total = 0;
+#pragma unroll
+            for (int i = 0; i < kPerIter; ++i) {
+                pass[i] = V::get(x[i / EPV], i % EPV) > thr;
+                m[i] = __ballot(pass[i]);
+                total += __popcll(m[i]);
+            }
+        }
         if (cnt + total > kCap) {
             compact();
             total = 0;
