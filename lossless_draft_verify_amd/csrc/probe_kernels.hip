@@ -1,12 +1,12 @@
 // probe_kernels.hip -- read-only streaming reference for the HBM roofline.
 //
-// Each workgroup reads its own contiguous range once with the load idiom of the
-// top-k stream (16-byte non-temporal loads, four per lane per iteration, the
-// next iteration's loads in flight, each of the four waves a quarter of the
-// range) and does nothing with the data but fold it into one word, so its
-// duration is what that access pattern alone costs.  With one range per logit
-// row it has the top-k stream's decomposition; with many equal ranges it
-// measures the chip's streaming rate.
+// Each workgroup reads its own contiguous range once with 16-byte non-temporal
+// loads (four per lane per iteration, the next iteration's loads in flight
+// while one is folded, each of the four waves a quarter of the range) and does
+// nothing with the data but fold it into one word, so its duration is what
+// streaming those bytes costs on this chip.  With one range per logit row it
+// has the top-k stream's decomposition; with many equal ranges it measures the
+// chip's streaming rate.
 #include "uno_device.h"
 #include "uno_internal.h"
 
@@ -29,20 +29,25 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4*
     constexpr int64_t kStep = (int64_t)kProbeU * kWave;
     const int64_t nfull = (we - wb) / kStep;
     uint32_t acc = 0;
-    uint4 xc[kProbeU], xn[kProbeU];
+    // two buffers in turn, each at a fixed place: copying the next buffer into
+    // the current one would wait on its loads (111.3 against 102.5 us for the
+    // 1088-row split of 661 MB)
+    uint4 xa[kProbeU], xb[kProbeU];
     if (nfull > 0) {
 #pragma unroll
-        for (int u = 0; u < kProbeU; ++u) xc[u] = Vec<true>::load_stream(buf + wb + u * kWave + lane);
+        for (int u = 0; u < kProbeU; ++u) xa[u] = Vec<true>::load_stream(buf + wb + u * kWave + lane);
     }
-    for (int64_t it = 0; it < nfull; ++it) {
+    auto step = [&](int64_t it, uint4 (&cur)[kProbeU], uint4 (&nxt)[kProbeU]) __attribute__((always_inline)) {
         const bool more = it + 1 < nfull;
         const uint4* pn = buf + wb + (more ? (it + 1) * kStep : it * kStep) + lane;
 #pragma unroll
-        for (int u = 0; u < kProbeU; ++u) xn[u] = Vec<true>::load_stream(pn + u * kWave);
+        for (int u = 0; u < kProbeU; ++u) nxt[u] = Vec<true>::load_stream(pn + u * kWave);
 #pragma unroll
-        for (int u = 0; u < kProbeU; ++u) acc ^= xc[u].x ^ xc[u].y ^ xc[u].z ^ xc[u].w;
-#pragma unroll
-        for (int u = 0; u < kProbeU; ++u) xc[u] = xn[u];
+        for (int u = 0; u < kProbeU; ++u) acc ^= cur[u].x ^ cur[u].y ^ cur[u].z ^ cur[u].w;
+    };
+    for (int64_t it = 0; it < nfull; it += 2) {
+        step(it, xa, xb);
+        if (it + 1 < nfull) step(it + 1, xb, xa);
     }
     for (int64_t v = wb + nfull * kStep + lane; v < we; v += kWave) {
         const uint4 x = Vec<true>::load_stream(buf + v);
