@@ -1411,97 +1411,213 @@ __global__ __launch_bounds__(kDenseThreads) void dense_residual_exact_kernel(
     }
 }
 
+// Vectors j0 .. j0 + NJ - 1 of chunk c of a row (the layout of load_chunk:
+// element (j*64 + lane)*EPV + e at x[(j - j0)*EPV + e]); -inf past the end.
+template <bool BF16, int NJ>
+__device__ __forceinline__ void load_chunk_part(const char* row, int64_t N, int64_t c, int j0, float* x, int lane)
+{
+    using V = Vec<BF16>;
+    constexpr int EPV = V::EPV, ESZ = V::ESZ;
+    const int64_t beg = c * kDenseChunk;
+    const int64_t n = (N - beg < kDenseChunk) ? (N - beg) : kDenseChunk;
+    if (n == kDenseChunk && ((((uintptr_t)(row + beg * ESZ)) & 15u) == 0)) {
+        const typename V::T* p = reinterpret_cast<const typename V::T*>(row + beg * ESZ);
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+            const typename V::T v = V::load_stream(p + (j0 + jj) * kWave + lane);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) x[jj * EPV + e] = V::get(v, e);
+        }
+    } else {
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const int64_t i = (int64_t)((j0 + jj) * kWave + lane) * EPV + e;
+                x[jj * EPV + e] = (i < n) ? load_scalar<BF16>(row, beg + i) : -INFINITY;
+            }
+    }
+}
+
 // Residual (or bonus) sample from exact sums and the cycle's outputs: every
 // request (one per workgroup) or, with a list, the listed requests (those
-// whose certified draw was not certain), dealt over the workgroups.
+// whose certified draw was not certain), dealt over the workgroups.  Four
+// waves per request: the two rows' statistics and the residual total side by
+// side, then the picked chunk's residual weights a quarter of its vectors per
+// wave.  The cumulative sums are those of one wave stepping through the chunk
+// (each 64-lane block's total added in block order), so the pick is the same.
+constexpr int kFinishWaves = 4;
+constexpr int kFinishThreads = kFinishWaves * kWave;
+
 template <bool BF16>
-__global__ __launch_bounds__(kWave) void dense_finish_exact_kernel(
+__global__ __launch_bounds__(kFinishThreads) void dense_finish_exact_kernel(
     RowSource src, int32_t batch, int32_t B, int64_t N, double log2e_over_T0, DenseChunks dc,
     uint64_t seed, uint64_t offset, const uint32_t* req_ids, const int32_t* jstar_in, const int32_t* y_in,
     const uint32_t* flag_in, const int32_t* list, const uint32_t* list_n, const double* resid, LinearOut o,
     const FilterParams* rowp)
 {
+    constexpr int EPV = Vec<BF16>::EPV;
+    constexpr int NV = kPerLane / EPV;                 // 64-lane blocks of a chunk
+    constexpr int NVW = NV / kFinishWaves;             // blocks per wave
+    static_assert(NV % kFinishWaves == 0, "a chunk's blocks split evenly over the waves");
     const int njobs = list ? (int)*list_n : (int)gridDim.x;
     if ((int)blockIdx.x >= njobs) return;
     __shared__ double s_exp2[kExp2Entries];
+    __shared__ double s_S[3];            // Sp, Sq, residual total
+    __shared__ float s_m[2];             // row maxima of p and q
+    __shared__ double s_bt[NV];          // block totals of the picked chunk
+    __shared__ int s_hit[kFinishWaves], s_last[kFinishWaves];
+    __shared__ int s_fin;
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     for (int job = blockIdx.x; job < njobs; job += gridDim.x) {
-    const int b = list ? list[job] : job;
-    double log2e_over_T = log2e_over_T0;
-    if (rowp) {
-        const FilterParams& f = rowp[(int64_t)b * B];
-        if (f.dense == kRowTopK) continue;
-        log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
-    }
-    const DenseExp ex{ log2e_over_T, s_exp2 };
-    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
-    const int nc = dc.nchunks;
-    const int64_t row_bytes = N * Vec<BF16>::ESZ;
-    const int js = jstar_in[b];
-    const Draw d = uno_draw(seed, req, (uint32_t)js, offset);
-    uint32_t fl = flag_in[b];
-    int32_t fin = -1;
-    const int64_t pr = linear_row(batch, B, b, B + js);
-    const char* prow = row_pointer(src, pr, row_bytes);
-    float mp;
-    double Sp;
-    dense_row_stat(dc.cmax + pr * nc, dc.csum + pr * nc, nc, ex, lane, &mp, &Sp);   // exact chunks
-    if (!(Sp > 0.0)) {
-        fl |= 1u;
-    } else if (js < B) {
-        const int64_t qr = linear_row(batch, B, b, js);
-        float mqf;
-        double Sq;
-        dense_row_stat(dc.cmax + qr * nc, dc.csum + qr * nc, nc, ex, lane, &mqf, &Sq);   // exact chunks
-        const bool q_ok = Sq > 0.0;
+        const int b = list ? list[job] : job;
+        double log2e_over_T = log2e_over_T0;
+        if (rowp) {
+            const FilterParams& f = rowp[(int64_t)b * B];
+            if (f.dense == kRowTopK) continue;
+            log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
+        }
+        const DenseExp ex{ log2e_over_T, s_exp2 };
+        const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+        const int nc = dc.nchunks;
+        const int64_t row_bytes = N * Vec<BF16>::ESZ;
+        const int js = jstar_in[b];
+        const Draw d = uno_draw(seed, req, (uint32_t)js, offset);
+        const int64_t pr = linear_row(batch, B, b, B + js);
+        const int64_t qr = linear_row(batch, B, b, js < B ? js : 0);
+        const char* prow = row_pointer(src, pr, row_bytes);
         const double* R = resid + (int64_t)b * nc;
         auto rterm = [&](int c) { return R[c]; };
-        double Rtot = 0.0;
-        for (int base = 0; base < nc; base += kWave) {
-            const int c = base + lane;
-            const double incl = wave_incl_scan_f64(c < nc ? R[c] : 0.0, lane);
-            Rtot += lane_value(incl, kWave - 1);
+        // the rows' statistics (exact chunks) and the residual total, side by side
+        if (w == 0 || (w == 1 && js < B)) {
+            const int64_t r = w == 0 ? pr : qr;
+            float m;
+            double S;
+            dense_row_stat(dc.cmax + r * nc, dc.csum + r * nc, nc, ex, lane, &m, &S);
+            if (lane == 0) { s_m[w] = m; s_S[w] = S; }
+        } else if (w == 2 && js < B) {
+            double Rtot = 0.0;
+            for (int base = 0; base < nc; base += kWave) {
+                const int c = base + lane;
+                const double incl = wave_incl_scan_f64(c < nc ? R[c] : 0.0, lane);
+                Rtot += lane_value(incl, kWave - 1);
+            }
+            if (lane == 0) s_S[2] = Rtot;
         }
-        if (Rtot > 0.0) {
-            const double t = d.u[2] * Rtot;
-            double before;
-            int c = dense_locate(nc, t, rterm, lane, &before);
-            double tau = t - before;
-            if (c < 0) { c = dense_last_positive_chunk(nc, rterm, lane); tau = INFINITY; }
-            float xp[kPerLane], xq[kPerLane];
-            load_chunk<BF16>(prow, N, c, xp, lane);
-            if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
-            const double mpd = (double)mp, mq = (double)mqf;
-            const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
-            const uint64_t tp = row_keep(dc, pr), tq = row_keep(dc, qr);
-            constexpr int EPV = Vec<BF16>::EPV;
-            auto wf = [&](int i) {
-                const int64_t id = chunk_elem_id<EPV>(c, i, lane);
-                const double pv = dense_keeps(tp, xp[i], id) ? ex((double)xp[i] - mpd) * iSp : 0.0;
-                const double qv = (q_ok && dense_keeps(tq, xq[i], id)) ? ex((double)xq[i] - mq) * iSq : 0.0;
-                const double dl = pv - qv;
-                return dl > 0.0 ? dl : 0.0;
-            };
-            const int l = pick_in_chunk<EPV>(wf, tau, lane);
-            fin = l < 0 ? -1 : (int32_t)(c * (int64_t)kDenseChunk + l);
+        __syncthreads();
+        const float mp = s_m[0];
+        const double Sp = s_S[0];
+        uint32_t fl = flag_in[b];
+        int32_t fin = -1;
+        bool fallback = false;
+        if (!(Sp > 0.0)) {
+            fl |= 1u;
+        } else if (js < B) {
+            const float mqf = s_m[1];
+            const double Sq = s_S[1], Rtot = s_S[2];
+            const bool q_ok = Sq > 0.0;
+            if (Rtot > 0.0) {
+                const double t = d.u[2] * Rtot;
+                double before;
+                int c = dense_locate(nc, t, rterm, lane, &before);
+                double tau = t - before;
+                if (c < 0) { c = dense_last_positive_chunk(nc, rterm, lane); tau = INFINITY; }
+                // this wave's blocks of chunk c: weights, block totals
+                float xp[NVW * EPV], xq[NVW * EPV];
+                load_chunk_part<BF16, NVW>(prow, N, c, w * NVW, xp, lane);
+                if (q_ok) load_chunk_part<BF16, NVW>(row_pointer(src, qr, row_bytes), N, c, w * NVW, xq, lane);
+                const double mpd = (double)mp, mq = (double)mqf;
+                const double iSp = 1.0 / Sp, iSq = q_ok ? 1.0 / Sq : 0.0;
+                const uint64_t tp = row_keep(dc, pr), tq = row_keep(dc, qr);
+                double wl[NVW * EPV], lsum[NVW], incl[NVW];
+                int last_pos = -1;
+#pragma unroll
+                for (int jj = 0; jj < NVW; ++jj) {
+                    const int j = w * NVW + jj;
+                    lsum[jj] = 0.0;
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        const int i = jj * EPV + e;
+                        const int64_t id = chunk_elem_id<EPV>(c, j * EPV + e, lane);
+                        const double pv = dense_keeps(tp, xp[i], id) ? ex((double)xp[i] - mpd) * iSp : 0.0;
+                        const double qv = (q_ok && dense_keeps(tq, xq[i], id)) ? ex((double)xq[i] - mq) * iSq : 0.0;
+                        const double dl = pv - qv;
+                        wl[i] = dl > 0.0 ? dl : 0.0;
+                        lsum[jj] += wl[i];
+                        if (wl[i] > 0.0) last_pos = (j * kWave + lane) * EPV + e;
+                    }
+                    incl[jj] = wave_incl_scan_f64(lsum[jj], lane);
+                    if (lane == kWave - 1) s_bt[j] = incl[jj];
+                }
+                last_pos = wave_max_i32(last_pos);
+                __syncthreads();
+                // the running sum before this wave's first block, in block order
+                double run = 0.0;
+                for (int j = 0; j < w * NVW; ++j) run += s_bt[j];
+                int hit_at = -1;
+#pragma unroll
+                for (int jj = 0; jj < NVW; ++jj) {
+                    if (hit_at >= 0) break;
+                    const uint64_t hit = __ballot(run + incl[jj] > tau);
+                    if (hit) {
+                        const int l = wave_first_lane(hit);
+                        int ep = -1;
+                        if (lane == l) {
+                            double cc = run + (incl[jj] - lsum[jj]);
+#pragma unroll
+                            for (int e = 0; e < EPV; ++e) {
+                                cc += wl[jj * EPV + e];
+                                if (ep < 0 && cc > tau) ep = e;
+                            }
+                            if (ep < 0) {
+#pragma unroll
+                                for (int e = EPV - 1; e >= 0; --e)
+                                    if (ep < 0 && wl[jj * EPV + e] > 0.0) ep = e;
+                            }
+                        }
+                        ep = lane_value(ep, l);
+                        hit_at = ((w * NVW + jj) * kWave + l) * EPV + ep;
+                    }
+                    run += lane_value(incl[jj], kWave - 1);
+                }
+                if (lane == 0) { s_hit[w] = hit_at; s_last[w] = last_pos; }
+                __syncthreads();
+                int l = -1, lp = -1;
+                for (int q = 0; q < kFinishWaves; ++q) {
+                    if (l < 0 && s_hit[q] >= 0) l = s_hit[q];
+                    lp = s_last[q] > lp ? s_last[q] : lp;
+                }
+                if (l < 0) l = lp;
+                fin = l < 0 ? -1 : (int32_t)(c * (int64_t)kDenseChunk + l);
+            } else {
+                fl |= 2u;
+            }
+            fallback = fin < 0;
         } else {
-            fl |= 2u;
+            fallback = true;
         }
-        if (fin < 0)
-            fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp, d.u[2], ex, lane,
-                                         row_keep(dc, pr));
-    } else {
-        fin = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp, d.u[2], ex, lane,
-                                     row_keep(dc, pr));
-    }
-    int32_t* tok = o.tokens + (int64_t)b * (B + 1);
-    for (int j = lane; j <= B; j += kWave) tok[j] = (j < js) ? y_in[(int64_t)b * B + j] : (j == js ? fin : -1);
-    if (lane == 0) {
-        o.accept_len[b] = js + 1;
-        if (o.flags) o.flags[b] = fl;
-    }
+        if (fallback) {
+            // the bonus draw, or a residual without mass: from p (one wave)
+            if (w == 0) {
+                const int32_t f = dense_sample_row<BF16>(prow, N, dc.cmax + pr * nc, dc.csum + pr * nc, nc, mp, Sp,
+                                                         d.u[2], ex, lane, row_keep(dc, pr));
+                if (lane == 0) s_fin = f;
+            }
+            __syncthreads();
+            fin = s_fin;
+        }
+        if (w == 0) {
+            int32_t* tok = o.tokens + (int64_t)b * (B + 1);
+            for (int j = lane; j <= B; j += kWave) tok[j] = (j < js) ? y_in[(int64_t)b * B + j] : (j == js ? fin : -1);
+            if (lane == 0) {
+                o.accept_len[b] = js + 1;
+                if (o.flags) o.flags[b] = fl;
+            }
+        }
+        __syncthreads();       // the LDS above is reused by the next job
     }
 }
 
@@ -2312,7 +2428,7 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
             // every row exact already: exact residual and draw for every request
             dense_residual_exact_kernel<true><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
                                                                                   nullptr, nullptr, sc.resid, rowp);
-            dense_finish_exact_kernel<true><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+            dense_finish_exact_kernel<true><<<dim3((unsigned)batch), kFinishThreads, 0, stream>>>(
                 src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, nullptr, nullptr,
                 sc.resid, o, rowp);
         } else {
@@ -2331,7 +2447,7 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
                                                                                        rowp);
             dense_residual_exact_kernel<true><<<xgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
                                                                                   sc.xreq, dc.xcount + 2, sc.resid, rowp);
-            dense_finish_exact_kernel<true><<<dim3(kExactJobs), kWave, 0, stream>>>(
+            dense_finish_exact_kernel<true><<<dim3(kExactJobs), kFinishThreads, 0, stream>>>(
                 src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, sc.xreq,
                 dc.xcount + 2, sc.resid, o, rowp);
         }
@@ -2351,7 +2467,7 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
             // every row exact already: exact residual and draw for every request
             dense_residual_exact_kernel<false><<<rgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
                                                                                   nullptr, nullptr, sc.resid, rowp);
-            dense_finish_exact_kernel<false><<<dim3((unsigned)batch), kWave, 0, stream>>>(
+            dense_finish_exact_kernel<false><<<dim3((unsigned)batch), kFinishThreads, 0, stream>>>(
                 src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, nullptr, nullptr,
                 sc.resid, o, rowp);
         } else {
@@ -2370,7 +2486,7 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
                                                                                        rowp);
             dense_residual_exact_kernel<false><<<xgrid, kDenseThreads, 0, stream>>>(src, batch, B, vocab, c, dc, sc.jstar,
                                                                                   sc.xreq, dc.xcount + 2, sc.resid, rowp);
-            dense_finish_exact_kernel<false><<<dim3(kExactJobs), kWave, 0, stream>>>(
+            dense_finish_exact_kernel<false><<<dim3(kExactJobs), kFinishThreads, 0, stream>>>(
                 src, batch, B, vocab, c, dc, seed, offset, request_ids, sc.jstar, sc.y, sc.flags, sc.xreq,
                 dc.xcount + 2, sc.resid, o, rowp);
         }
