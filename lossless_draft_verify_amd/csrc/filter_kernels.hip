@@ -153,14 +153,15 @@ __device__ __forceinline__ int wave_cut(Cand* buf, int cnt, int k, int limit, in
     return c;
 }
 
-// k-th largest of one key per lane (k <= 64), by bitwise search over ballots.
-__device__ __forceinline__ uint32_t wave_kth_largest_of_lanes(uint32_t v, int k)
+// k-th largest (k <= 128) of two keys per lane, truncated to its 16-bit bin:
+// the largest t with low 16 bits zero and at least k of the keys >= t.
+__device__ __forceinline__ uint32_t wave_kth_largest_of_lane_pairs(uint32_t a, uint32_t b, int k)
 {
     uint32_t prefix = 0;
 #pragma unroll 1
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = prefix | (1u << b);
-        if (__popcll(__ballot(v >= cand)) >= k) prefix = cand;
+    for (int bit = 31; bit >= 16; --bit) {
+        const uint32_t cand = prefix | (1u << bit);
+        if (__popcll(__ballot(a >= cand)) + __popcll(__ballot(b >= cand)) >= k) prefix = cand;
     }
     return prefix;
 }
@@ -651,22 +652,33 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     if (nfull > 0) {
 #pragma unroll
         for (int d = 0; d < DEPTH - 1; ++d) load_iter(d, xr[d]);
-        if (cnt == 0 && k <= kWave) {
+        if (cnt == 0 && k <= 2 * kWave) {
             // Seed the threshold from the first two iterations (only the first
-            // when there is no second: a shape-only load holds one lane's data):
-            // the k-th largest lane maximum has at least k logits at or above
-            // it, all admitted below.
-            float mx = -INFINITY;
+            // when there is no second: a shape-only load holds one lane's data).
+            // Each lane keeps its two largest logits (NaN taken as -inf through
+            // the maximum with thr_init, which is -inf); the k-th largest of
+            // those 128 values, truncated to its 16-bit key bin, has at least
+            // k logits at or above it, all admitted below.  Two per lane put
+            // the seed near the k-th largest of all 128 * U * EPV logits read,
+            // where the largest per lane alone sat several times lower.
+            const float ninf = fp.thr_init;
+            float m1 = ninf, m2 = ninf;
+            auto take = [&](float z) __attribute__((always_inline)) {
+                z = fmaxf(z, ninf);
+                m2 = fmaxf(m2, fminf(m1, z));
+                m1 = fmaxf(m1, z);
+            };
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
-                    mx = fmaxf(mx, V::get(xr[0][u], e));
-                    if (DEPTH > 2 && nfull > 1) mx = fmaxf(mx, V::get(xr[1][u], e));
+                    take(V::get(xr[0][u], e));
+                    if (DEPTH > 2 && nfull > 1) take(V::get(xr[1][u], e));
                 }
-            uint32_t km = float_key(mx);
-            km = (km <= kKeyPosInf && km > kKeyNegInf) ? km : kKeyNegInf;
-            const uint32_t t0 = wave_kth_largest_of_lanes(km, k);
+            uint32_t k1 = float_key(m1), k2 = float_key(m2);
+            k1 = (k1 <= kKeyPosInf && k1 > kKeyNegInf) ? k1 : kKeyNegInf;
+            k2 = (k2 <= kKeyPosInf && k2 > kKeyNegInf) ? k2 : kKeyNegInf;
+            const uint32_t t0 = wave_kth_largest_of_lane_pairs(k1, k2, k);
             if (t0 > kKeyNegInf + 1u) { thr_key = t0 - 1u; thr = thr_float(thr_key); }
         }
     }
