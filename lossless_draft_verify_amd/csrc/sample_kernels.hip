@@ -383,12 +383,14 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
     const int cap = sup.cap;
     const int64_t rbase = (int64_t)b * B;
     const int kk = K < cap ? K : cap;
-    // per depth (B <= 128): candidate count (at most K), first and second
-    // probability (-1 when there is no second candidate)
-    int cn[2];
-    double p0[2], p1[2];
+    // per depth (B <= 128; B <= V < 64 when FS == 1): candidate count (at
+    // most K), first and second probability (-1 when there is no second
+    // candidate)
+    constexpr int DS = FS == 1 ? 1 : 2;
+    int cn[DS];
+    double p0[DS], p1[DS];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < DS; ++s) {
         const int d = s * kWave + lane;
         int n = 0;
         double f0 = 0.0, f1 = -1.0;
@@ -485,7 +487,6 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
         const int wq = __builtin_amdgcn_readlane(bq, wl);
         const double score = __longlong_as_double(
             (long long)(((uint64_t)hm << 32) | (uint32_t)__builtin_amdgcn_readlane((int)bl, wl)));
-        const int slot = wq * kWave + wl;
         double psc = readlane_f64(fp[0], wl), nsp = readlane_f64(fn[0], wl);
 #pragma unroll
         for (int q = 1; q < FS; ++q) {
@@ -512,10 +513,21 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
             put(nf++, score * sel_f64(p0, depth), tree_tie(depth + 1, num, 0), score, sel_f64(p1, depth));
             ++live;
         }
-        // its next sibling in the slot it leaves (or the slot emptied)
+        // its next sibling in the slot it leaves (or the slot emptied); the
+        // slot keeps its parent score, the sibling's parent's
         const bool sib = !(nsp < 0.0);
-        put(slot, sib ? psc * nsp : 0.0, sib ? tree_tie(depth, parent, rank + 1) : ~0u, psc,
-            (sib && has2) ? sp2 : -1.0);
+        {
+            const double sc = sib ? psc * nsp : 0.0;
+            const uint32_t st = sib ? tree_tie(depth, parent, rank + 1) : ~0u;
+            const double sn = (sib && has2) ? sp2 : -1.0;
+#pragma unroll
+            for (int q = 0; q < FS; ++q) {
+                const bool m = lane == wl && q == wq;
+                fs[q] = m ? (uint64_t)__double_as_longlong(sc) : fs[q];
+                ft[q] = m ? st : ft[q];
+                fn[q] = m ? sn : fn[q];
+            }
+        }
         live -= sib ? 0 : 1;
         ++num;
     }
