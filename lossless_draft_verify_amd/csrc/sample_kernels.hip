@@ -371,6 +371,22 @@ __device__ __forceinline__ double sel_f64(const double (&a)[N], int i)
     return r;
 }
 
+// Wave maximum: within rows of 16 lanes by DPP, then across the four rows'
+// results by lane reads and scalar maxima (no row broadcasts and their waits).
+__device__ __forceinline__ uint32_t wave_max_u32_rows(uint32_t v)
+{
+    auto mx = [](uint32_t a, uint32_t b) __attribute__((always_inline)) { return a > b ? a : b; };
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    return mx(mx(r0, r1), mx(r2, r3));
+}
+
 template <int FS>
 __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch, int32_t B, int32_t K, int32_t V,
                                                                    SparseOut sup, TreeOut o)
@@ -441,12 +457,15 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
 #pragma unroll
     for (int q = 0; q < FS; ++q) { fs[q] = 0ull; ft[q] = ~0u; fp[q] = 0.0; fn[q] = -1.0; ns[q] = 0.0; nt[q] = 0u; }
     if (lane == 0) ns[0] = 1.0;
+    // the lane that holds slot i of a per-lane array, and its register slot
+    // (every slot is below 64 when FS == 1)
+    auto at = [&](int i, int q) __attribute__((always_inline)) {
+        return FS == 1 ? lane == i : (lane == (i & (kWave - 1)) && q == (i >> 6));
+    };
     auto put = [&](int slot, double sc, uint32_t tie, double psc, double nsp) __attribute__((always_inline)) {
-        const int qs = slot >> 6;
-        const bool mine = lane == (slot & (kWave - 1));
 #pragma unroll
         for (int q = 0; q < FS; ++q) {
-            const bool m = mine && q == qs;
+            const bool m = at(slot, q);
             fs[q] = m ? (uint64_t)__double_as_longlong(sc) : fs[q];
             ft[q] = m ? tie : ft[q];
             fp[q] = m ? psc : fp[q];
@@ -471,7 +490,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
             if (fs[q] > bs || (fs[q] == bs && ft[q] < bt)) { bs = fs[q]; bt = ft[q]; bq = q; }
         // the wave's best: high score word, then (on ties) low word, tie word
         const uint32_t bh = (uint32_t)(bs >> 32), bl = (uint32_t)bs;
-        const uint32_t hm = wave_ext_u32<true>(bh);
+        const uint32_t hm = wave_max_u32_rows(bh);
         uint64_t hit = __ballot(bh == hm);
         if (__popcll(hit) > 1) {
             const uint32_t lm = wave_ext_u32<true>(bh == hm ? bl : 0u);
@@ -482,7 +501,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
                 hit = __ballot(c && bt == tm);
             }
         }
-        const int wl = wave_first_lane(hit);
+        const int wl = __builtin_ctzll(hit);            // some lane holds the maximum
         const uint32_t tie = (uint32_t)__builtin_amdgcn_readlane((int)bt, wl);
         const int wq = __builtin_amdgcn_readlane(bq, wl);
         const double score = __longlong_as_double(
@@ -503,7 +522,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
         // the node
 #pragma unroll
         for (int q = 0; q < FS; ++q) {
-            const bool m = q == (num >> 6) && lane == (num & (kWave - 1));
+            const bool m = at(num, q);
             ns[q] = m ? score : ns[q];
             nt[q] = m ? tie : nt[q];
         }
@@ -519,10 +538,10 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
         {
             const double sc = sib ? psc * nsp : 0.0;
             const uint32_t st = sib ? tree_tie(depth, parent, rank + 1) : ~0u;
-            const double sn = (sib && has2) ? sp2 : -1.0;
+            const double sn = has2 ? sp2 : -1.0;       // read only while the slot is live
 #pragma unroll
             for (int q = 0; q < FS; ++q) {
-                const bool m = lane == wl && q == wq;
+                const bool m = at(wq * kWave + wl, q);
                 fs[q] = m ? (uint64_t)__double_as_longlong(sc) : fs[q];
                 ft[q] = m ? st : ft[q];
                 fn[q] = m ? sn : fn[q];
