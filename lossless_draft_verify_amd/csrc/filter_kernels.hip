@@ -27,6 +27,7 @@ constexpr int kStreamVecs = 2;  // 16-byte vectors per lane per streaming iterat
 constexpr int kStreamDepth = 3; // iterations whose loads are in flight at once (the one processed included)
 constexpr int kMaxK = 256;      // UNO_MAX_TOP_K
 constexpr int64_t kSegmentTarget = 1024;   // workgroups the top-k stream aims for (four per CU)
+constexpr int64_t kWideBelow = 512;        // launches with fewer segments take eight waves per segment
 
 // ---- candidate buffers and register-resident lists ----------------------------
 // A streaming candidate is (raw float bits of the logit, token id); keys are
@@ -403,19 +404,23 @@ __device__ __forceinline__ void pad_skipped_row(const SparseOut& out, int64_t r)
 }
 
 // ---- top-k stream ------------------------------------------------------------
-// Block (r, seg): four waves stream quarters of segment seg of row r, each
+// Block (r, seg): NW waves stream equal parts of segment seg of row r, each
 // keeping candidates in its own LDS buffer behind a rising admission
-// threshold; then every wave cuts its buffer to its exact top-k, the four
+// threshold; then every wave cuts its buffer to its exact top-k, the NW
 // lists are pruned by the best per-wave k-th entry and ranked together.  With
 // one segment the block also finalises the row; otherwise it writes the
-// segment's sorted top-k for topk_merge_kernel.
-template <bool BF16, bool JOINT>
-__global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
+// segment's sorted top-k for topk_merge_kernel.  Four waves per block, or
+// eight when a launch has few segments (most CUs would hold one block or
+// none), which halves each wave's range there.
+template <bool BF16, bool JOINT, int NW>
+__global__ __launch_bounds__(NW * kWave, JOINT ? 3 : 5) void topk_stream_kernel(
     RowSource src, int64_t rows, int64_t N, FilterParams fp_all, SparseOut out, int S,
     uint32_t* part_key, int32_t* part_id, int32_t* part_n, int part_cap, const FilterParams* rowp)
 {
     using V = Vec<BF16>;
     constexpr int EPV = V::EPV, ESZ = V::ESZ;
+    constexpr int kT = NW * kWave;                     // threads per workgroup
+    static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
     // 16-byte vectors per lane per iteration and iterations in flight: the
     // joint variant, fp64-bound, keeps four vectors with one iteration ahead
     // so its running sum is rescaled half as often
@@ -424,17 +429,17 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     constexpr int kPerIter = U * EPV;                  // logits per lane per iteration
     // a streaming cut must leave room for one whole vector of candidates per lane
     constexpr int kCutLimit = (kCap - kWave * EPV < kCap / 2) ? kCap - kWave * EPV : kCap / 2;
-    __shared__ Cand s_buf[kWaves * kCap];
+    __shared__ Cand s_buf[NW * kCap];
     __shared__ uint32_t s_sk[kMaxK];
     __shared__ int32_t s_sid[kMaxK];
     __shared__ double s_e[kMaxK];
     __shared__ __align__(16) double s_cx[kMaxK + 1];
     __shared__ double s_scal[1];
-    __shared__ uint32_t s_b[kWaves];
-    __shared__ uint32_t s_mx[kWaves];
-    __shared__ int s_ns[kWaves];
-    __shared__ uint32_t s_jm[kWaves];
-    __shared__ double s_js[kWaves];
+    __shared__ uint32_t s_b[NW];
+    __shared__ uint32_t s_mx[NW];
+    __shared__ int s_ns[NW];
+    __shared__ uint32_t s_jm[NW];
+    __shared__ double s_js[NW];
     __shared__ double s_exp2[JOINT ? kExp2Entries : 1];
     if constexpr (JOINT) {
         load_exp2_table(s_exp2);
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     }
     const RowGeom g = row_geom<BF16>(row, N);
     const int64_t vb = g.nvec * seg / S, ve = g.nvec * (seg + 1) / S;
-    const int64_t wb = vb + (ve - vb) * w / kWaves, we = vb + (ve - vb) * (w + 1) / kWaves;
+    const int64_t wb = vb + (ve - vb) * w / NW, we = vb + (ve - vb) * (w + 1) / NW;
 
     Cand* buf = s_buf + w * kCap;
     const int k = fp.k;
@@ -703,17 +708,17 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
         }
     }
 
-    if (seg == S - 1 && w == kWaves - 1 && g.tail_beg < N) scalar_part(g.tail_beg, N - g.tail_beg);
+    if (seg == S - 1 && w == NW - 1 && g.tail_beg < N) scalar_part(g.tail_beg, N - g.tail_beg);
 
-    // Bound: with quota q = ceil(k/4), each wave finds a key b with at least q
-    // of its entries at or above it, so the smallest of the four waves' bounds
+    // Bound: with quota q = ceil(k/NW), each wave finds a key b with at least q
+    // of its entries at or above it, so the smallest of the NW waves' bounds
     // has at least k: the block's k-th entry lies at or above it.  Without q
     // entries in every wave there is no bound (B = 0).  For small q, b is the
     // q-th largest of the lane maxima (truncated to its 16-bit key bin); a
     // larger q would push that down to the smallest lane maximum, and the
     // block would rank several times k entries, so there b is the wave's own
     // q-th largest key (truncated to 24 bits).
-    const int quota = (k + kWaves - 1) / kWaves;
+    const int quota = (k + NW - 1) / NW;
     // the wave's candidates, read once into registers as (key, id); padding
     // slots hold key 0, below every admitted key
     RegList<kCapE> L;
@@ -744,7 +749,7 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     __syncthreads();
     uint32_t B = s_b[0];
 #pragma unroll
-    for (int o = 1; o < kWaves; ++o) B = s_b[o] < B ? s_b[o] : B;
+    for (int o = 1; o < NW; ++o) B = s_b[o] < B ? s_b[o] : B;
     // this wave's entries with key >= B, compacted in place as (key, id)
     int ns = 0;
 #pragma unroll
@@ -763,16 +768,16 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
     // softmax numerators are formed during the rank when this block finalises
     uint32_t top = s_mx[0];
 #pragma unroll
-    for (int o = 1; o < kWaves; ++o) top = s_mx[o] > top ? s_mx[o] : top;
+    for (int o = 1; o < NW; ++o) top = s_mx[o] > top ? s_mx[o] : top;
     const bool want_e = (S == 1) && !fp.greedy;
     // The rank and the one-wave finalisation start at a different wave in each
     // block, so co-resident blocks spread these short serial phases over the
     // four SIMDs instead of stacking them on one.
-    const int rot = (int)(blockIdx.x & (kWaves - 1));
-    const int trot = (int)((threadIdx.x + rot * kWave) & (kThreads - 1));
-    const int n = block_rank_topk<kWaves>(s_buf, kCap, s_ns, k, s_sk, s_sid, want_e ? s_e : nullptr,
-                                          (double)key_float(top), (double)fp.temperature, trot, kThreads,
-                                          reinterpret_cast<uint64_t*>(s_cx));
+    const int rot = (int)(blockIdx.x & (NW - 1));
+    const int trot = (int)((threadIdx.x + rot * kWave) & (kT - 1));
+    const int n = block_rank_topk<NW>(s_buf, kCap, s_ns, k, s_sk, s_sid, want_e ? s_e : nullptr,
+                                      (double)key_float(top), (double)fp.temperature, trot, kT,
+                                      reinterpret_cast<uint64_t*>(s_cx));
     __syncthreads();
     if (S == 1) {
         if (w == rot) {
@@ -781,10 +786,10 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
                 if (jrow) {    // the row's full normaliser relative to its maximum
                     uint32_t km = s_jm[0];
 #pragma unroll
-                    for (int o = 1; o < kWaves; ++o) km = s_jm[o] > km ? s_jm[o] : km;
+                    for (int o = 1; o < NW; ++o) km = s_jm[o] > km ? s_jm[o] : km;
                     const double mr = (double)key_float(km);
 #pragma unroll
-                    for (int o = 0; o < kWaves; ++o)
+                    for (int o = 0; o < NW; ++o)
                         if (s_jm[o] > kKeyNegInf) s_full += s_js[o] * jex((double)key_float(s_jm[o]) - mr);
                 }
             }
@@ -792,7 +797,7 @@ __global__ __launch_bounds__(kThreads, JOINT ? 3 : 5) void topk_stream_kernel(
         }
     } else {
         const int64_t base = (r * S + seg) * (int64_t)part_cap;
-        for (int i = threadIdx.x; i < n; i += kThreads) {
+        for (int i = threadIdx.x; i < n; i += kT) {
             part_key[base + i] = s_sk[i];
             part_id[base + i] = s_sid[i];
         }
@@ -1166,21 +1171,32 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
 {
     if (rows == 0) return hipSuccess;
     if (joint_sums && S != 1) return hipErrorInvalidValue;
-    dim3 grid((unsigned)(rows * S));
+    const dim3 grid((unsigned)(rows * S));
+    // eight waves per segment when the launch would leave most CUs idle
+    const bool wide = !joint_sums && rows * S < kWideBelow;
     if (joint_sums) {
         if (bf16)
-            topk_stream_kernel<true, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
-                                                                          part_id, part_n, part_cap, rowp);
+            topk_stream_kernel<true, true, 4><<<grid, 4 * kWave, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
+                                                                              part_id, part_n, part_cap, rowp);
         else
-            topk_stream_kernel<false, true><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
-                                                                           part_id, part_n, part_cap, rowp);
+            topk_stream_kernel<false, true, 4><<<grid, 4 * kWave, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
+                                                                               part_id, part_n, part_cap, rowp);
+    } else if (wide) {
+        if (bf16)
+            topk_stream_kernel<true, false, 8><<<grid, 8 * kWave, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
+                                                                               part_id, part_n, part_cap, rowp);
+        else
+            topk_stream_kernel<false, false, 8><<<grid, 8 * kWave, 0, stream>>>(src, rows, vocab, fp, out, S,
+                                                                                part_key, part_id, part_n, part_cap,
+                                                                                rowp);
     } else {
         if (bf16)
-            topk_stream_kernel<true, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
-                                                                           part_id, part_n, part_cap, rowp);
+            topk_stream_kernel<true, false, 4><<<grid, 4 * kWave, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
+                                                                               part_id, part_n, part_cap, rowp);
         else
-            topk_stream_kernel<false, false><<<grid, kThreads, 0, stream>>>(src, rows, vocab, fp, out, S, part_key,
-                                                                            part_id, part_n, part_cap, rowp);
+            topk_stream_kernel<false, false, 4><<<grid, 4 * kWave, 0, stream>>>(src, rows, vocab, fp, out, S,
+                                                                                part_key, part_id, part_n, part_cap,
+                                                                                rowp);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
