@@ -62,6 +62,18 @@ __device__ __forceinline__ void wave_load_support(const int32_t* ids, const doub
     }
 }
 
+// Entries n and above of R become padding (as wave_load_support leaves them).
+__device__ __forceinline__ void wave_mask_support(WaveRow& R, int n, int lane)
+{
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        const bool in = q * kWave + lane < n;
+        R.id[q] = in ? R.id[q] : 0x7FFFFFFF;
+        R.w[q] = in ? R.w[q] : 0.0;
+        R.c[q] = in ? R.c[q] : 0.0;
+    }
+}
+
 // Inverse CDF over the n id-ordered entries of R with uniform u: the first
 // entry whose inclusive cumulative weight exceeds u * W (W the total); when
 // rounding leaves none, the last entry with positive weight.  Returns its id
@@ -573,6 +585,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
 // ---- tree walk (one workgroup per request) ---------------------------------------
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / kWave;
+constexpr int kWalkAhead = 3;     // nodes per wave whose supports are read up front
 
 // LDS copy of one request's tree and every node's depth.  Node arrays are read
 // at once (all V + 1 slots); depths come from pointer jumping: (anc, dist)
@@ -659,42 +672,46 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     int nn = num_nodes[b];
     nn = nn < 1 ? 1 : (nn > V + 1 ? V + 1 : nn);
     const int64_t ob = (int64_t)b * (V + 1);
+    // The wave's first kWalkAhead nodes (n = w + a * 16): their supports are
+    // read at once, before the depths are known, so every round trip overlaps
+    // (a row past num_nodes is read, in bounds, and ignored).  Further nodes
+    // (more than 48 in a tree) are read one at a time afterwards.
+    WaveRow R[kWalkAhead];
+    int cnt[kWalkAhead];
+#pragma unroll
+    for (int a = 0; a < kWalkAhead; ++a) {
+        const int n = w + a * kWalkWaves;
+        cnt[a] = 0;
+        if (n <= V) {
+            cnt[a] = sup.count[ob + n];
+            wave_load_support(sup.ids + (ob + n) * cap, sup.probs + (ob + n) * cap, sup.cum + (ob + n) * cap, cap,
+                              cap, R[a], lane);
+        }
+    }
     tree_depths(node_token, node_parent, ob, nn, V, L);
     // every node's sample, drawn with the uniform of its depth
-    // the next node's support is loaded while this one is sampled
-    auto node_live = [&](int n, int* cnt) __attribute__((always_inline)) {
+    auto sample_node = [&](int n, WaveRow& Rw, int c) __attribute__((always_inline)) {
         const int dep = L.dep[n];
-        *cnt = sup.count[ob + n];
-        return dep >= 0 && dep <= B && *cnt > 0;
-    };
-    WaveRow R;
-    int cnt = 0;
-    bool live = false;
-    if (w < nn) {
-        live = node_live(w, &cnt);
-        wave_load_support(sup.ids + (ob + w) * cap, sup.probs + (ob + w) * cap, sup.cum + (ob + w) * cap,
-                          live ? cnt : 0, cap, R, lane);
-    }
-    for (int n = w; n < nn; n += kWalkWaves) {
-        const int nx = n + kWalkWaves;
-        WaveRow Rn;
-        int cntn = 0;
-        bool liven = false;
-        if (nx < nn) {
-            liven = node_live(nx, &cntn);
-            wave_load_support(sup.ids + (ob + nx) * cap, sup.probs + (ob + nx) * cap, sup.cum + (ob + nx) * cap,
-                              liven ? cntn : 0, cap, Rn, lane);
-        }
         int32_t t = -1;
-        if (live) {
-            const Draw d = uno_draw(seed, req, (uint32_t)L.dep[n], offset);
+        if (dep >= 0 && dep <= B && c > 0) {
+            wave_mask_support(Rw, c, lane);
+            const Draw d = uno_draw(seed, req, (uint32_t)dep, offset);
             double dummy;
-            t = wave_sample_cum(R, cnt, d.u[2], &dummy, lane);
+            t = wave_sample_cum(Rw, c, d.u[2], &dummy, lane);
         }
         if (lane == 0) s_t[n] = t;
-        R = Rn;
-        cnt = cntn;
-        live = liven;
+    };
+#pragma unroll
+    for (int a = 0; a < kWalkAhead; ++a) {
+        const int n = w + a * kWalkWaves;
+        if (n < nn) sample_node(n, R[a], cnt[a]);
+    }
+    for (int n = w + kWalkAhead * kWalkWaves; n < nn; n += kWalkWaves) {
+        WaveRow Rn;
+        const int c = sup.count[ob + n];
+        wave_load_support(sup.ids + (ob + n) * cap, sup.probs + (ob + n) * cap, sup.cum + (ob + n) * cap, cap, cap,
+                          Rn, lane);
+        sample_node(n, Rn, c);
     }
     __syncthreads();
     if (w == 0) follow_path(b, B, nn, s_t, L, o, lane);
