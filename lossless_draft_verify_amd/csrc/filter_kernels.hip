@@ -154,15 +154,20 @@ __device__ __forceinline__ int wave_cut(Cand* buf, int cnt, int k, int limit, in
     return c;
 }
 
-// k-th largest (k <= 128) of two keys per lane, truncated to its 16-bit bin:
-// the largest t with low 16 bits zero and at least k of the keys >= t.
-__device__ __forceinline__ uint32_t wave_kth_largest_of_lane_pairs(uint32_t a, uint32_t b, int k)
+// k-th largest (k <= 64 P) of P keys per lane (P = 2: a, b; P = 4: a to d),
+// truncated to its 16-bit bin: the largest t with low 16 bits zero and at
+// least k of the keys >= t.
+template <int P>
+__device__ __forceinline__ uint32_t wave_kth_largest_of_lane_keys(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                                                  int k)
 {
     uint32_t prefix = 0;
 #pragma unroll 1
     for (int bit = 31; bit >= 16; --bit) {
-        const uint32_t cand = prefix | (1u << bit);
-        if (__popcll(__ballot(a >= cand)) + __popcll(__ballot(b >= cand)) >= k) prefix = cand;
+        const uint32_t t = prefix | (1u << bit);
+        int n = __popcll(__ballot(a >= t)) + __popcll(__ballot(b >= t));
+        if constexpr (P == 4) n += __popcll(__ballot(c >= t)) + __popcll(__ballot(d >= t));
+        if (n >= k) prefix = t;
     }
     return prefix;
 }
@@ -657,33 +662,50 @@ __global__ __launch_bounds__(NW * kWave, JOINT ? 3 : 5) void topk_stream_kernel(
     if (nfull > 0) {
 #pragma unroll
         for (int d = 0; d < DEPTH - 1; ++d) load_iter(d, xr[d]);
-        if (cnt == 0 && k <= 2 * kWave) {
+        if (cnt == 0) {
             // Seed the threshold from the first two iterations (only the first
             // when there is no second: a shape-only load holds one lane's data).
-            // Each lane keeps its two largest logits (NaN taken as -inf through
+            // Each lane keeps its P largest logits (NaN taken as -inf through
             // the maximum with thr_init, which is -inf); the k-th largest of
-            // those 128 values, truncated to its 16-bit key bin, has at least
-            // k logits at or above it, all admitted below.  Two per lane put
-            // the seed near the k-th largest of all 128 * U * EPV logits read,
-            // where the largest per lane alone sat several times lower.
+            // those 64 P values, truncated to its 16-bit key bin, has at least
+            // k logits at or above it, all admitted below.  P = 2 for k <= 128
+            // and 4 up to k = 256: several per lane put the seed near the k-th
+            // largest of all 128 * U * EPV logits read, where the largest per
+            // lane alone sat several times lower; four cost more than they save
+            // for the smaller k.
             const float ninf = fp.thr_init;
-            float m1 = ninf, m2 = ninf;
-            auto take = [&](float z) __attribute__((always_inline)) {
-                z = fmaxf(z, ninf);
-                m2 = fmaxf(m2, fminf(m1, z));
-                m1 = fmaxf(m1, z);
+            float m1 = ninf, m2 = ninf, m3 = ninf, m4 = ninf;
+            auto seed = [&](auto four) __attribute__((always_inline)) {
+                constexpr bool F = decltype(four)::value;
+                auto take = [&](float z) __attribute__((always_inline)) {
+                    z = fmaxf(z, ninf);
+                    if constexpr (F) {
+                        m4 = fmaxf(m4, fminf(m3, z));
+                        m3 = fmaxf(m3, fminf(m2, z));
+                    }
+                    m2 = fmaxf(m2, fminf(m1, z));
+                    m1 = fmaxf(m1, z);
+                };
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        take(V::get(xr[0][u], e));
+                        if (DEPTH > 2 && nfull > 1) take(V::get(xr[1][u], e));
+                    }
             };
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    take(V::get(xr[0][u], e));
-                    if (DEPTH > 2 && nfull > 1) take(V::get(xr[1][u], e));
-                }
-            uint32_t k1 = float_key(m1), k2 = float_key(m2);
-            k1 = (k1 <= kKeyPosInf && k1 > kKeyNegInf) ? k1 : kKeyNegInf;
-            k2 = (k2 <= kKeyPosInf && k2 > kKeyNegInf) ? k2 : kKeyNegInf;
-            const uint32_t t0 = wave_kth_largest_of_lane_pairs(k1, k2, k);
+            auto valid = [](uint32_t x) __attribute__((always_inline)) {
+                return (x <= kKeyPosInf && x > kKeyNegInf) ? x : kKeyNegInf;
+            };
+            uint32_t t0;
+            if (k <= 2 * kWave) {
+                seed(std::false_type());
+                t0 = wave_kth_largest_of_lane_keys<2>(valid(float_key(m1)), valid(float_key(m2)), 0u, 0u, k);
+            } else {
+                seed(std::true_type());
+                t0 = wave_kth_largest_of_lane_keys<4>(valid(float_key(m1)), valid(float_key(m2)),
+                                                      valid(float_key(m3)), valid(float_key(m4)), k);
+            }
             if (t0 > kKeyNegInf + 1u) { thr_key = t0 - 1u; thr = thr_float(thr_key); }
         }
     }
