@@ -1229,14 +1229,16 @@ hipError_t launch_topk_filter(const RowSource& src, int64_t rows, int64_t vocab,
 
 hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                                float temperature, const DenseChunks& dc, int64_t exact_rows, hipStream_t stream,
-                               const FilterParams* rowp, int select)
+                               const FilterParams* rowp, int select, int64_t active_rows)
 {
     if (rows == 0) return hipSuccess;
     const double c = 1.4426950408889634074 / (double)temperature;
-    // about two rounds of workgroups over the chip at least: few rows are
-    // split over several workgroups each (at most one chunk per wave)
+    // about two rounds of workgroups over the chip at least: few rows (or few
+    // selected rows) are split over several workgroups each (at most one
+    // chunk per wave)
     const int64_t per_row_max = (dc.nchunks + kWaves - 1) / kWaves;
-    int64_t g = (2048 + rows - 1) / rows;
+    const int64_t busy = (active_rows >= 0 && active_rows < rows) ? (active_rows > 0 ? active_rows : 1) : rows;
+    int64_t g = (2048 + busy - 1) / busy;
     if (g > per_row_max) g = per_row_max;
     if (g < 1) g = 1;
     dim3 grid((unsigned)rows, (unsigned)g);

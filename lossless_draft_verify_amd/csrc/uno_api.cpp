@@ -30,7 +30,19 @@ struct Mode {
     bool any_nucleus;// some set is a nucleus
     int32_t k;       // largest effective k over the top-k sets (1 when there is none)
     float joint_T;   // one set in the joint order: its temperature
+    int64_t n_sets;  // parameter sets of the call, and how many are in the joint order / full-vocabulary
+    int64_t n_joint_sets;
+    int64_t n_dense_sets;
 };
+
+// Rows a per-request chunk pass takes (select: kChunkJointRows or
+// kChunkDenseRows): every set covers the same number of rows.
+int64_t chunk_rows(const Mode& m, int64_t rows, int select)
+{
+    if (!m.per_request || m.n_sets < 1) return rows;
+    const int64_t n = select == kChunkJointRows ? m.n_joint_sets : m.n_dense_sets;
+    return (rows * n + m.n_sets - 1) / m.n_sets;
+}
 
 int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
 {
@@ -55,6 +67,9 @@ int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
     m->any_nucleus = m->nucleus;
     m->any_full = !m->sparse && !m->nucleus;
     m->joint_T = T;
+    m->n_sets = 1;
+    m->n_joint_sets = m->joint ? 1 : 0;
+    m->n_dense_sets = m->sparse ? 0 : 1;
     if (!m->sparse && vocab > (int64_t)65535 * 4 * kDenseChunk) return UNO_ERR_UNSUPPORTED;
     return UNO_OK;
 }
@@ -83,6 +98,9 @@ int check_set(const SpSet& s, int64_t requests, int64_t vocab, Mode* m)
         Mode mi;
         const int st = check_sampling(&s.sp[i], vocab, &mi);
         if (st) return st;
+        all.n_sets += 1;
+        all.n_joint_sets += mi.joint ? 1 : 0;
+        all.n_dense_sets += mi.sparse ? 0 : 1;
         all.greedy = all.greedy && mi.greedy;
         all.topk_on = all.topk_on || mi.topk_on;
         all.topp_on = all.topp_on || mi.topp_on;
@@ -302,7 +320,8 @@ hipError_t launch_sparse_filter(const RowSource& src, int64_t rows, int64_t voca
         fp.joint = 1;
     } else if (m.joint) {
         const hipError_t e = launch_dense_chunks(src, rows, vocab, bf16, m.joint_T, sw.full, rows, stream,
-                                                 m.per_request ? sw.rowp : nullptr, kChunkJointRows);
+                                                 m.per_request ? sw.rowp : nullptr, kChunkJointRows,
+                                                 chunk_rows(m, rows, kChunkJointRows));
         if (e != hipSuccess) return e;
         fp.full_cmax = sw.full.cmax;
         fp.full_csum = sw.full.csum;
@@ -455,7 +474,8 @@ int uno_filter_ex(const void* logits, int32_t dtype, int64_t rows, int64_t vocab
         e = launch_sparse_filter(src, rows, vocab, bf16, sps, m, sw, out, stream);
     }
     if (e == hipSuccess && m.any_dense) {
-        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream, rowp, kChunkDenseRows);
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream, rowp, kChunkDenseRows,
+                                chunk_rows(m, rows, kChunkDenseRows));
         if (e == hipSuccess && m.any_nucleus)
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, out_count, out_stats, stream,
                                rowp);
@@ -511,7 +531,7 @@ int uno_sample_linear_ex(const void* draft, const void* target, int32_t dtype, i
         // nucleus rows exact itself)
         const bool exact_all = !m.per_request && m.nucleus;
         e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, exact_all ? rows : 0, stream, rowp,
-                                kChunkDenseRows);
+                                kChunkDenseRows, chunk_rows(m, rows, kChunkDenseRows));
         if (e == hipSuccess && m.any_nucleus)
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream, rowp);
         if (e == hipSuccess)
@@ -555,7 +575,7 @@ int uno_build_tree_ex(const void* draft, int32_t dtype, int32_t batch, int32_t B
         e = expand_row_params(sps, vocab, map, sw, K, stream);
         if (e == hipSuccess && m.any_dense)
             e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream, sw.rowp,
-                                    kChunkDenseRows);
+                                    kChunkDenseRows, chunk_rows(m, rows, kChunkDenseRows));
         if (e == hipSuccess && m.any_nucleus)
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, sw.nucleus_n, nullptr, stream,
                                sw.rowp);
@@ -628,7 +648,8 @@ int uno_verify_tree_ex(const void* target, int32_t dtype, int32_t batch, int32_t
     if (e == hipSuccess && m.any_dense) {
         // every node row a walk may sample gets exact chunk statistics (and
         // its nucleus when top-p is on)
-        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream, rowp, kChunkDenseRows);
+        e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream, rowp, kChunkDenseRows,
+                                chunk_rows(m, rows, kChunkDenseRows));
         if (e == hipSuccess && m.any_nucleus)
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream, rowp);
         if (e == hipSuccess)

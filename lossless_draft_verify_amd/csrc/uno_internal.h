@@ -136,9 +136,11 @@ constexpr int kChunkDenseRows = 2;   // rows whose set is not kRowTopK
 // rowp (nullable, device): per-row parameters; the pass then takes only the
 // rows `select` names (nothing read or written for the others), each at its
 // own temperature, and joint-order and nucleus rows always get exact sums.
+// active_rows (when >= 0): how many rows the selection takes, which sets how
+// many workgroups share each row.
 hipError_t launch_dense_chunks(const RowSource& src, int64_t rows, int64_t vocab, bool bf16,
                                float temperature, const DenseChunks& dc, int64_t exact_rows, hipStream_t stream,
-                               const FilterParams* rowp = nullptr, int select = 0);
+                               const FilterParams* rowp = nullptr, int select = 0, int64_t active_rows = -1);
 
 // rowp (nullable): per-row temperatures; only the kRowFull rows are written.
 hipError_t launch_dense_row_stats(int64_t rows, float temperature, const DenseChunks& dc,
