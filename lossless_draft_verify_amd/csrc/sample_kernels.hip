@@ -1937,18 +1937,21 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
 // collects them (as order keys) together with the chunk sums above the bin;
 // the collected logits are ranked in LDS and the cut is the first whose
 // inclusive mass, counted from the top in the filter order, reaches the target.
-constexpr int kNucThreads = 256;
-constexpr int kNucWaves = kNucThreads / kWave;
 constexpr int kNucBins = 2048;
-constexpr int kNucCand = kNucBins / 2 / kNucWaves;   // collected logits per wave (in s_cnt)
+constexpr int64_t kNucWideRows = 256;   // nucleus rows up to which a row takes eight waves
 
-// Three workgroups per CU (168 VGPRs; a few spills, outside the streaming
-// loops' loads); the LDS of four would not fit.
-template <bool BF16>
-__global__ __launch_bounds__(kNucThreads, 3) void nucleus_kernel(RowSource src, int64_t N, double log2e_over_T,
-                                                              double top_p, DenseChunks dc, int32_t* out_count,
-                                                              double* out_stats, const FilterParams* rowp)
+// NW waves per row: four, at three workgroups per CU (168 VGPRs; a few
+// spills, outside the streaming loops' loads; the LDS of four would not fit),
+// or eight when at most one row per CU is cut, where a wave's serial chunks,
+// not the chip, set the time.
+template <bool BF16, int NW>
+__global__ __launch_bounds__(NW * kWave, NW == 4 ? 3 : 2) void nucleus_kernel(
+    RowSource src, int64_t N, double log2e_over_T, double top_p, DenseChunks dc, int32_t* out_count,
+    double* out_stats, const FilterParams* rowp)
 {
+    constexpr int kNucWaves = NW;
+    constexpr int kNucThreads = NW * kWave;
+    constexpr int kNucCand = kNucBins / 2 / kNucWaves;   // collected logits per wave (in s_cnt)
     __shared__ double s_exp2[kExp2Entries];
     __shared__ double s_mass[kNucBins];
     __shared__ uint32_t s_cnt[kNucBins];
@@ -2597,17 +2600,25 @@ hipError_t launch_dense_support_scale(int64_t rows, float temperature, const Den
 
 hipError_t launch_nucleus(const RowSource& src, int64_t rows, int64_t vocab, bool bf16, float temperature,
                           float top_p, const DenseChunks& dc, int32_t* out_count, double* out_stats,
-                          hipStream_t stream, const FilterParams* rowp)
+                          hipStream_t stream, const FilterParams* rowp, int64_t active_rows)
 {
     if (rows == 0) return hipSuccess;
     if (dc.keep == nullptr) return hipErrorInvalidValue;
     const double c = 1.4426950408889634074 / (double)temperature;
-    if (bf16)
-        nucleus_kernel<true><<<dim3((unsigned)rows), kNucThreads, 0, stream>>>(src, vocab, c, (double)top_p, dc,
-                                                                             out_count, out_stats, rowp);
+    const dim3 grid((unsigned)rows);
+    const bool wide = (active_rows >= 0 ? active_rows : rows) <= kNucWideRows;
+    if (bf16 && wide)
+        nucleus_kernel<true, 8><<<grid, 8 * kWave, 0, stream>>>(src, vocab, c, (double)top_p, dc, out_count, out_stats,
+                                                                rowp);
+    else if (bf16)
+        nucleus_kernel<true, 4><<<grid, 4 * kWave, 0, stream>>>(src, vocab, c, (double)top_p, dc, out_count, out_stats,
+                                                                rowp);
+    else if (wide)
+        nucleus_kernel<false, 8><<<grid, 8 * kWave, 0, stream>>>(src, vocab, c, (double)top_p, dc, out_count,
+                                                                 out_stats, rowp);
     else
-        nucleus_kernel<false><<<dim3((unsigned)rows), kNucThreads, 0, stream>>>(src, vocab, c, (double)top_p, dc,
-                                                                              out_count, out_stats, rowp);
+        nucleus_kernel<false, 4><<<grid, 4 * kWave, 0, stream>>>(src, vocab, c, (double)top_p, dc, out_count,
+                                                                 out_stats, rowp);
     return hipGetLastError();
 }
 

@@ -30,9 +30,10 @@ struct Mode {
     bool any_nucleus;// some set is a nucleus
     int32_t k;       // largest effective k over the top-k sets (1 when there is none)
     float joint_T;   // one set in the joint order: its temperature
-    int64_t n_sets;  // parameter sets of the call, and how many are in the joint order / full-vocabulary
+    int64_t n_sets;  // parameter sets of the call, and how many are in the joint order / full-vocabulary / nucleus
     int64_t n_joint_sets;
     int64_t n_dense_sets;
+    int64_t n_nucleus_sets;
 };
 
 // Rows a per-request chunk pass takes (select: kChunkJointRows or
@@ -42,6 +43,13 @@ int64_t chunk_rows(const Mode& m, int64_t rows, int select)
     if (!m.per_request || m.n_sets < 1) return rows;
     const int64_t n = select == kChunkJointRows ? m.n_joint_sets : m.n_dense_sets;
     return (rows * n + m.n_sets - 1) / m.n_sets;
+}
+
+// Rows a nucleus cut takes.
+int64_t nucleus_rows(const Mode& m, int64_t rows)
+{
+    if (!m.per_request || m.n_sets < 1) return rows;
+    return (rows * m.n_nucleus_sets + m.n_sets - 1) / m.n_sets;
 }
 
 int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
@@ -70,6 +78,7 @@ int check_sampling(const uno_sampling_t* sp, int64_t vocab, Mode* m)
     m->n_sets = 1;
     m->n_joint_sets = m->joint ? 1 : 0;
     m->n_dense_sets = m->sparse ? 0 : 1;
+    m->n_nucleus_sets = m->nucleus ? 1 : 0;
     if (!m->sparse && vocab > (int64_t)65535 * 4 * kDenseChunk) return UNO_ERR_UNSUPPORTED;
     return UNO_OK;
 }
@@ -101,6 +110,7 @@ int check_set(const SpSet& s, int64_t requests, int64_t vocab, Mode* m)
         all.n_sets += 1;
         all.n_joint_sets += mi.joint ? 1 : 0;
         all.n_dense_sets += mi.sparse ? 0 : 1;
+        all.n_nucleus_sets += mi.nucleus ? 1 : 0;
         all.greedy = all.greedy && mi.greedy;
         all.topk_on = all.topk_on || mi.topk_on;
         all.topp_on = all.topp_on || mi.topp_on;
@@ -478,7 +488,7 @@ int uno_filter_ex(const void* logits, int32_t dtype, int64_t rows, int64_t vocab
                                 chunk_rows(m, rows, kChunkDenseRows));
         if (e == hipSuccess && m.any_nucleus)
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, out_count, out_stats, stream,
-                               rowp);
+                               rowp, nucleus_rows(m, rows));
         if (e == hipSuccess && m.any_full)
             e = launch_dense_row_stats(rows, sp->temperature, dc, out_count, out_stats, stream, rowp);
     }
@@ -533,7 +543,8 @@ int uno_sample_linear_ex(const void* draft, const void* target, int32_t dtype, i
         e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, exact_all ? rows : 0, stream, rowp,
                                 kChunkDenseRows, chunk_rows(m, rows, kChunkDenseRows));
         if (e == hipSuccess && m.any_nucleus)
-            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream, rowp);
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream, rowp,
+                               nucleus_rows(m, rows));
         if (e == hipSuccess)
             e = launch_linear_dense(src, batch, B, vocab, bf16, sp->temperature, dc, ds, seed, offset,
                                     request_ids, o, exact_all, stream, rowp);
@@ -578,7 +589,7 @@ int uno_build_tree_ex(const void* draft, int32_t dtype, int32_t batch, int32_t B
                                     kChunkDenseRows, chunk_rows(m, rows, kChunkDenseRows));
         if (e == hipSuccess && m.any_nucleus)
             e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, sw.nucleus_n, nullptr, stream,
-                               sw.rowp);
+                               sw.rowp, nucleus_rows(m, rows));
         if (e == hipSuccess) e = launch_sparse_filter(src, rows, vocab, bf16, sps, m, sw, sw.sup, stream);
         if (e == hipSuccess && m.any_dense)
             e = launch_dense_support_scale(rows, sp->temperature, dc, sw.nucleus_n, sw.sup, stream, sw.rowp);
@@ -651,7 +662,8 @@ int uno_verify_tree_ex(const void* target, int32_t dtype, int32_t batch, int32_t
         e = launch_dense_chunks(src, rows, vocab, bf16, sp->temperature, dc, rows, stream, rowp, kChunkDenseRows,
                                 chunk_rows(m, rows, kChunkDenseRows));
         if (e == hipSuccess && m.any_nucleus)
-            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream, rowp);
+            e = launch_nucleus(src, rows, vocab, bf16, sp->temperature, sp->top_p, dc, nullptr, nullptr, stream, rowp,
+                               nucleus_rows(m, rows));
         if (e == hipSuccess)
             e = launch_tree_walk_dense(src, batch, B, V, vocab, bf16, sp->temperature, dc, seed, offset,
                                        request_ids, node_token, node_parent, num_nodes, o, stream, rowp);

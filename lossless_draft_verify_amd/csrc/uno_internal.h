@@ -194,10 +194,11 @@ hipError_t launch_linear_dense(const RowSource& src, int32_t batch, int32_t B, i
 // support, and (when non-null) the support sizes and (m, S) statistics.
 // rowp (nullable): per-row parameters; kRowNucleus rows are cut at their own
 // temperature and top_p, kRowFull rows get keep = 0 (the whole vocabulary),
-// kRowTopK rows are left alone.
+// kRowTopK rows are left alone.  active_rows (when >= 0): how many rows are
+// nucleus rows, which sets the workgroup size.
 hipError_t launch_nucleus(const RowSource& src, int64_t rows, int64_t vocab, bool bf16, float temperature,
                           float top_p, const DenseChunks& dc, int32_t* out_count, double* out_stats,
-                          hipStream_t stream, const FilterParams* rowp = nullptr);
+                          hipStream_t stream, const FilterParams* rowp = nullptr, int64_t active_rows = -1);
 
 struct TreeOut {
     int32_t* node_token;
