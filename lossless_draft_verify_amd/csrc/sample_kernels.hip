@@ -337,13 +337,13 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
 // (or node, or depth) i sits in lane i % 64 of slot i / 64.  The frontier is
 // an unordered set; each pop is a wave maximum of the score's high word, and
 // only lanes that tie on it go on to the low word and then the tie word.
-// Each entry carries its parent's score and the probability of its next
-// sibling, so the pop that takes it writes that sibling (parent score times
-// probability, the product the oracle forms) without a memory access; the
-// probability of the sibling after it is read from the candidate table (first
-// K ids and probabilities of each depth's filtered row, staged in LDS) while
-// the rest of the pop runs.  Per-depth counts and first two probabilities sit
-// in registers, read by uniform lane index.
+// An entry is its score and tie word only: the pop that takes it reads the
+// parent's score from the node records (by lane) and the next sibling's
+// probability from the candidate table (first K ids and probabilities of each
+// depth's filtered row, staged in LDS; the read is issued as soon as the entry
+// is known and used last), and writes that sibling (parent score times
+// probability, the product the oracle forms) into the entry's slot.  Per-depth
+// counts and first probabilities sit in registers, read by uniform lane index.
 
 __device__ __forceinline__ uint32_t tree_tie(int depth, int parent, int rank)
 {
@@ -412,24 +412,21 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
     const int64_t rbase = (int64_t)b * B;
     const int kk = K < cap ? K : cap;
     // per depth (B <= 128; B <= V < 64 when FS == 1): candidate count (at
-    // most K), first and second probability (-1 when there is no second
-    // candidate)
+    // most K) and first probability
     constexpr int DS = FS == 1 ? 1 : 2;
     int cn[DS];
-    double p0[DS], p1[DS];
+    double p0[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
         const int d = s * kWave + lane;
         int n = 0;
-        double f0 = 0.0, f1 = -1.0;
+        double f0 = 0.0;
         if (d < B && threadIdx.x < kWave) {
             n = sup.count[rbase + d];
             f0 = sup.probs[(rbase + d) * cap];
-            if (kk > 1) f1 = sup.probs[(rbase + d) * cap + 1];
         }
         cn[s] = n > 0 ? (n < K ? n : K) : 0;
         p0[s] = f0;
-        p1[s] = cn[s] > 1 ? f1 : -1.0;
     }
     // the candidate table is read whole (supports are padded to cap); entries
     // past a count are never used
@@ -462,33 +459,29 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
 
     uint64_t fs[FS];                                   // frontier: score bits (0 = empty)
     uint32_t ft[FS];                                   // frontier: tie word (~0 = empty)
-    double fp[FS];                                     // frontier: parent's score
-    double fn[FS];                                     // frontier: next sibling's probability (-1: none)
     double ns[FS];                                     // node records: score
     uint32_t nt[FS];                                   // node records: tie word of the entry
 #pragma unroll
-    for (int q = 0; q < FS; ++q) { fs[q] = 0ull; ft[q] = ~0u; fp[q] = 0.0; fn[q] = -1.0; ns[q] = 0.0; nt[q] = 0u; }
+    for (int q = 0; q < FS; ++q) { fs[q] = 0ull; ft[q] = ~0u; ns[q] = 0.0; nt[q] = 0u; }
     if (lane == 0) ns[0] = 1.0;
     // the lane that holds slot i of a per-lane array, and its register slot
     // (every slot is below 64 when FS == 1)
     auto at = [&](int i, int q) __attribute__((always_inline)) {
         return FS == 1 ? lane == i : (lane == (i & (kWave - 1)) && q == (i >> 6));
     };
-    auto put = [&](int slot, double sc, uint32_t tie, double psc, double nsp) __attribute__((always_inline)) {
+    auto put = [&](int slot, double sc, uint32_t tie) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < FS; ++q) {
             const bool m = at(slot, q);
             fs[q] = m ? (uint64_t)__double_as_longlong(sc) : fs[q];
             ft[q] = m ? tie : ft[q];
-            fp[q] = m ? psc : fp[q];
-            fn[q] = m ? nsp : fn[q];
         }
     };
 
     int nf = 0;                                        // slots handed out (uniform)
     int live = 0;
     if (sel_i32(cn, 0) > 0) {
-        put(nf++, 1.0 * sel_f64(p0, 0), tree_tie(1, 0, 0), 1.0, sel_f64(p1, 0));
+        put(nf++, 1.0 * sel_f64(p0, 0), tree_tie(1, 0, 0));
         ++live;
     }
     int num = 1;
@@ -518,19 +511,14 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
         const int wq = __builtin_amdgcn_readlane(bq, wl);
         const double score = __longlong_as_double(
             (long long)(((uint64_t)hm << 32) | (uint32_t)__builtin_amdgcn_readlane((int)bl, wl)));
-        double psc = readlane_f64(fp[0], wl), nsp = readlane_f64(fn[0], wl);
-#pragma unroll
-        for (int q = 1; q < FS; ++q) {
-            const double a = readlane_f64(fp[q], wl), c = readlane_f64(fn[q], wl);
-            psc = wq == q ? a : psc;
-            nsp = wq == q ? c : nsp;
-        }
         const int depth = (int)(tie >> 20), parent = (int)((tie >> 12) & 0xFFu), rank = (int)(tie & 0xFFFu);
-        // the probability of the sibling after the next one, from LDS; used last
-        int si = (depth - 1) * K + rank + 2;
+        // the next sibling's probability, from LDS (used last)
+        int si = (depth - 1) * K + rank + 1;
         si = si < kMaxTreeVK ? si : kMaxTreeVK - 1;
-        const double sp2 = c_p[si];
-        const bool has2 = rank + 2 < sel_i32(cn, depth - 1);
+        const double sp1 = c_p[si];
+        const bool sib = rank + 1 < sel_i32(cn, depth - 1);
+        // the parent's score, from the node records
+        const double psc = sel_f64(ns, parent);
         // the node
 #pragma unroll
         for (int q = 0; q < FS; ++q) {
@@ -541,24 +529,11 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(int32_t batch
         // its first child in a new slot
         const bool child = depth < B && sel_i32(cn, depth) > 0;
         if (child) {
-            put(nf++, score * sel_f64(p0, depth), tree_tie(depth + 1, num, 0), score, sel_f64(p1, depth));
+            put(nf++, score * sel_f64(p0, depth), tree_tie(depth + 1, num, 0));
             ++live;
         }
-        // its next sibling in the slot it leaves (or the slot emptied); the
-        // slot keeps its parent score, the sibling's parent's
-        const bool sib = !(nsp < 0.0);
-        {
-            const double sc = sib ? psc * nsp : 0.0;
-            const uint32_t st = sib ? tree_tie(depth, parent, rank + 1) : ~0u;
-            const double sn = has2 ? sp2 : -1.0;       // read only while the slot is live
-#pragma unroll
-            for (int q = 0; q < FS; ++q) {
-                const bool m = at(wq * kWave + wl, q);
-                fs[q] = m ? (uint64_t)__double_as_longlong(sc) : fs[q];
-                ft[q] = m ? st : ft[q];
-                fn[q] = m ? sn : fn[q];
-            }
-        }
+        // its next sibling in the slot it leaves (or the slot emptied)
+        put(wq * kWave + wl, sib ? psc * sp1 : 0.0, sib ? tree_tie(depth, parent, rank + 1) : ~0u);
         live -= sib ? 0 : 1;
         ++num;
     }
