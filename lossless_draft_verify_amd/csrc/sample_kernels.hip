@@ -39,30 +39,26 @@ struct WaveRow {
     double c[kQ];      // inclusive cumulative sums in id order (supports that carry them)
 };
 
-// Load the n <= cap <= 256 entries of a support (unordered); slots past n hold
-// id INT32_MAX, weight 0.
-__device__ __forceinline__ void wave_load_support(const int32_t* ids, const double* p, const double* cum, int n,
-                                                  int cap, WaveRow& R, int lane)
+// The first cap slots of a support as stored (no count applied: slots past
+// cap hold id INT32_MAX, weight 0), so no loaded value is read here.
+__device__ __forceinline__ void wave_load_support_raw(const int32_t* ids, const double* p, const double* cum,
+                                                      int cap, WaveRow& R, int lane)
 {
-    // every slot below cap is read (the filter pads supports to cap), so the
-    // loads do not wait for the count
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
         const int i = q * kWave + lane;
-        int32_t id = 0x7FFFFFFF;
-        double w = 0.0, c = 0.0;
+        R.id[q] = 0x7FFFFFFF;
+        R.w[q] = 0.0;
+        R.c[q] = 0.0;
         if (q * kWave < cap && i < cap) {
-            id = ids[i];
-            w = p[i];
-            if (cum) c = cum[i];
+            R.id[q] = ids[i];
+            R.w[q] = p[i];
+            if (cum) R.c[q] = cum[i];
         }
-        R.id[q] = (i < n) ? id : 0x7FFFFFFF;
-        R.w[q] = (i < n) ? w : 0.0;
-        R.c[q] = (i < n) ? c : 0.0;
     }
 }
 
-// Entries n and above of R become padding (as wave_load_support leaves them).
+// Entries n and above of R become padding (id INT32_MAX, weight 0).
 __device__ __forceinline__ void wave_mask_support(WaveRow& R, int n, int lane)
 {
 #pragma unroll
@@ -240,10 +236,19 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
     uint32_t flags = 0;
     for (int j = w; j <= B; j += kLinWaves) {
         const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
+        // every read of this position first, one round trip: both counts in
+        // one lane-indexed load (lane 0: p_j, lane 1: q_j), both supports
+        // unmasked; nothing reads a loaded value until all are issued
         const int64_t pr = pbase + j;
-        const int np = sup.count[pr];
-        WaveRow P;                       // p_j (id order, with its cumulative sums), loaded up front
-        wave_load_support(sup.ids + pr * cap, sup.probs + pr * cap, sup.cum + pr * cap, np, cap, P, lane);
+        const int64_t qr = qbase + j;
+        const int cpair = sup.count[((lane & 1) && j < B) ? qr : pr];
+        WaveRow P;                       // p_j (id order, with its cumulative sums)
+        wave_load_support_raw(sup.ids + pr * cap, sup.probs + pr * cap, sup.cum + pr * cap, cap, P, lane);
+        WaveRow Q;                       // q_j (j < B)
+        if (j < B) wave_load_support_raw(sup.ids + qr * cap, sup.probs + qr * cap, sup.cum + qr * cap, cap, Q, lane);
+        const int np = __builtin_amdgcn_readlane(cpair, 0);
+        const int nq = j < B ? __builtin_amdgcn_readlane(cpair, 1) : 0;
+        wave_mask_support(P, np, lane);
         int32_t fin = -1;
         uint32_t ffl = 0;
         if (j == B) {                    // bonus draw
@@ -253,12 +258,9 @@ __global__ __launch_bounds__(kLinThreads) void linear_sparse_kernel(
             if (lane == 0) { s_fin[j] = fin; s_ffl[j] = ffl; }
             continue;
         }
-        const int64_t qr = qbase + j;
-        const int nq = sup.count[qr];
+        wave_mask_support(Q, nq, lane);
         int32_t y = -1;
         double qy = 0.0;
-        WaveRow Q;
-        wave_load_support(sup.ids + qr * cap, sup.probs + qr * cap, sup.cum + qr * cap, nq, cap, Q, lane);
         if (nq > 0) y = wave_sample_cum(Q, nq, d.u[0], &qy, lane);
         else flags |= 1u;
         int acc = 0;
@@ -651,19 +653,22 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     // read at once, before the depths are known, so every round trip overlaps
     // (a row past num_nodes is read, in bounds, and ignored).  Further nodes
     // (more than 48 in a tree) are read one at a time afterwards.
+    // (the counts in one lane-indexed load, lane a: node w + 16 a, read only
+    // after every load is issued)
     WaveRow R[kWalkAhead];
-    int cnt[kWalkAhead];
+    const int na = w + (lane < kWalkAhead ? lane : 0) * kWalkWaves;
+    const int cnt_l = na <= V ? sup.count[ob + na] : 0;
 #pragma unroll
     for (int a = 0; a < kWalkAhead; ++a) {
         const int n = w + a * kWalkWaves;
-        cnt[a] = 0;
-        if (n <= V) {
-            cnt[a] = sup.count[ob + n];
-            wave_load_support(sup.ids + (ob + n) * cap, sup.probs + (ob + n) * cap, sup.cum + (ob + n) * cap, cap,
-                              cap, R[a], lane);
-        }
+        if (n <= V)
+            wave_load_support_raw(sup.ids + (ob + n) * cap, sup.probs + (ob + n) * cap, sup.cum + (ob + n) * cap, cap,
+                                  R[a], lane);
     }
     tree_depths(node_token, node_parent, ob, nn, V, L);
+    int cnt[kWalkAhead];
+#pragma unroll
+    for (int a = 0; a < kWalkAhead; ++a) cnt[a] = __builtin_amdgcn_readlane(cnt_l, a);
     // every node's sample, drawn with the uniform of its depth
     auto sample_node = [&](int n, WaveRow& Rw, int c) __attribute__((always_inline)) {
         const int dep = L.dep[n];
@@ -683,10 +688,9 @@ __global__ __launch_bounds__(kWalkThreads) void tree_walk_kernel(
     }
     for (int n = w + kWalkAhead * kWalkWaves; n < nn; n += kWalkWaves) {
         WaveRow Rn;
-        const int c = sup.count[ob + n];
-        wave_load_support(sup.ids + (ob + n) * cap, sup.probs + (ob + n) * cap, sup.cum + (ob + n) * cap, cap, cap,
-                          Rn, lane);
-        sample_node(n, Rn, c);
+        wave_load_support_raw(sup.ids + (ob + n) * cap, sup.probs + (ob + n) * cap, sup.cum + (ob + n) * cap, cap, Rn,
+                              lane);
+        sample_node(n, Rn, sup.count[ob + n]);
     }
     __syncthreads();
     if (w == 0) follow_path(b, B, nn, s_t, L, o, lane);
