@@ -1097,13 +1097,29 @@ __global__ __launch_bounds__(kRowStatThreads) void dense_row_stat_kernel(int64_t
                                                                          double* row_E, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
-    load_exp2_table(s_exp2);
-    __syncthreads();
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t r0 = 2 * ((int64_t)blockIdx.x * kRowStatWaves + w);
-    if (r0 >= rows) return;
     const int nc = dc.nchunks;
+    // rows of at most 128 chunks: both rows' chunk statistics are read first
+    // (unconditionally within the rows; the per-row parameters applied
+    // afterwards), so they travel with the table's loads
+    float cm[2][2], ce[2][2];
+    double cs[2][2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = q * kWave + lane;
+            const bool in = nc <= 2 * kWave && r0 + k < rows && c < nc;
+            const int64_t slot = (r0 + k) * nc + c;
+            cm[k][q] = in ? dc.cmax[slot] : -INFINITY;
+            cs[k][q] = in ? dc.csum[slot] : 0.0;
+            ce[k][q] = (in && dc.cerr) ? dc.cerr[slot] : 0.0f;
+        }
+    load_exp2_table(s_exp2);
+    __syncthreads();
+    if (r0 >= rows) return;
     bool on[2];
     double c2[2];
 #pragma unroll
@@ -1123,19 +1139,6 @@ __global__ __launch_bounds__(kRowStatThreads) void dense_row_stat_kernel(int64_t
             if (on[k]) row_stat_to(dc, r0 + k, DenseExp{ c2[k], s_exp2 }, lane, row_m, row_S, row_E);
         return;
     }
-    float cm[2][2], ce[2][2];
-    double cs[2][2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = q * kWave + lane;
-            const bool in = on[k] && c < nc;
-            const int64_t slot = (r0 + k) * nc + c;
-            cm[k][q] = in ? dc.cmax[slot] : -INFINITY;
-            cs[k][q] = in ? dc.csum[slot] : 0.0;
-            ce[k][q] = (in && dc.cerr) ? dc.cerr[slot] : 0.0f;
-        }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         if (!on[k]) continue;
