@@ -1804,30 +1804,32 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
     const double* resid_err, int32_t* redo, int64_t* xrows1, int32_t* xreq, LinearOut o, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
+    const int b = blockIdx.x;
+    // the request's own reads go out together with its parameter set's, and
+    // the p row's sum before the table's, so each costs no round trip of its own
+    const int js = jstar_in[b];
+    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+    uint32_t fl = flag_in[b];
     if (rowp) {
-        const FilterParams& f = rowp[(int64_t)blockIdx.x * B];
+        const FilterParams& f = rowp[(int64_t)b * B];
         if (f.dense == kRowTopK) {
-            if (threadIdx.x == 0) redo[blockIdx.x] = 0;
+            if (threadIdx.x == 0) redo[b] = 0;
             return;
         }
         log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
     }
+    const int64_t pr = linear_row(batch, B, b, B + js);
+    const double Sp = row_S[pr];
     load_exp2_table(s_exp2);
     __syncthreads();
     const int lane = lane_id();
-    const int b = blockIdx.x;
     const DenseExp ex{ log2e_over_T, s_exp2 };
-    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
     const int nc = dc.nchunks;
     const int64_t row_bytes = N * Vec<BF16>::ESZ;
-    const int js = jstar_in[b];
     const Draw d = uno_draw(seed, req, (uint32_t)js, offset);
-    uint32_t fl = flag_in[b];
     int32_t fin = -1;
     bool certain = true;
-    const int64_t pr = linear_row(batch, B, b, B + js);
     const char* prow = row_pointer(src, pr, row_bytes);
-    const double Sp = row_S[pr];
     if (!(Sp > 0.0)) {
         fl |= 1u;
     } else if (js < B) {
