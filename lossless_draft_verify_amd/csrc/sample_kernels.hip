@@ -950,31 +950,71 @@ __device__ int32_t dense_sample_row(const char* row, int64_t N, const float* cm,
                                     float m, double S, double u, const DenseExp& ex, int lane, uint64_t thr,
                                     const float* ce = nullptr, double E = 0.0, bool* certain = nullptr)
 {
-    auto term = [&](int c) { return chunk_term(cm, cs, c, m, ex); };
     const bool fast = ce != nullptr && E > 0.0;
     const double t = u * S;
     double before;
-    int c = dense_locate(nc, t, term, lane, &before);
-    double tau, scale = 1.0, ebefore = 0.0;
-    if (c < 0) {
-        c = dense_last_positive_chunk(nc, term, lane);
-        if (certain) *certain = !fast;
-        if (c < 0) return -1;
-        tau = INFINITY;
-    } else {
-        scale = ex((double)cm[c] - (double)m);
-        tau = (t - before) / scale;
-        if (fast) {
-            // error bound of the chunks before c, relative to the row max
-            double eb = 0.0;
-            for (int k = lane; k < c; k += kWave)
-                if (cm[k] > -INFINITY) eb += (double)ce[k] * ex((double)cm[k] - (double)m);
-            ebefore = wave_sum_f64(eb);
+    int c;
+    double tau, scale = 1.0, ebefore = 0.0, mc;
+    if (nc <= 2 * kWave) {
+        // At most two chunks per lane: every statistic the draw reads is read
+        // before any is used, and the terms, scans and sums below are formed
+        // from the registers in the same order as from memory.
+        float m0 = -INFINITY, m1 = -INFINITY, e0 = 0.0f, e1 = 0.0f;
+        double s0 = 0.0, s1 = 0.0;
+        if (lane < nc) {
+            m0 = cm[lane];
+            s0 = cs[lane];
+            if (fast) e0 = ce[lane];
         }
+        if (lane + kWave < nc) {
+            m1 = cm[lane + kWave];
+            s1 = cs[lane + kWave];
+            if (fast) e1 = ce[lane + kWave];
+        }
+        const double x0 = (m0 > -INFINITY) ? ex((double)m0 - (double)m) : 0.0;
+        const double x1 = (m1 > -INFINITY) ? ex((double)m1 - (double)m) : 0.0;
+        const double t0 = (m0 > -INFINITY) ? s0 * x0 : 0.0, t1 = (m1 > -INFINITY) ? s1 * x1 : 0.0;
+        auto term = [&](int k) { return k < kWave ? t0 : t1; };     // k = lane or lane + 64
+        c = dense_locate(nc, t, term, lane, &before);
+        if (c < 0) {
+            c = dense_last_positive_chunk(nc, term, lane);
+            if (certain) *certain = !fast;
+            if (c < 0) return -1;
+            tau = INFINITY;
+        } else {
+            scale = lane_value(c < kWave ? x0 : x1, c & (kWave - 1));
+            tau = (t - before) / scale;
+            if (fast) {
+                double eb = 0.0;
+                if (lane < c && m0 > -INFINITY) eb += (double)e0 * x0;
+                if (lane + kWave < c && m1 > -INFINITY) eb += (double)e1 * x1;
+                ebefore = wave_sum_f64(eb);
+            }
+        }
+        mc = (double)__int_as_float(lane_value(__float_as_int(c < kWave ? m0 : m1), c & (kWave - 1)));
+    } else {
+        auto term = [&](int k) { return chunk_term(cm, cs, k, m, ex); };
+        c = dense_locate(nc, t, term, lane, &before);
+        if (c < 0) {
+            c = dense_last_positive_chunk(nc, term, lane);
+            if (certain) *certain = !fast;
+            if (c < 0) return -1;
+            tau = INFINITY;
+        } else {
+            scale = ex((double)cm[c] - (double)m);
+            tau = (t - before) / scale;
+            if (fast) {
+                // error bound of the chunks before c, relative to the row max
+                double eb = 0.0;
+                for (int k = lane; k < c; k += kWave)
+                    if (cm[k] > -INFINITY) eb += (double)ce[k] * ex((double)cm[k] - (double)m);
+                ebefore = wave_sum_f64(eb);
+            }
+        }
+        mc = (double)cm[c];
     }
     float x[kPerLane];
     load_chunk<BF16>(row, N, c, x, lane);
-    const double mc = (double)cm[c];
     constexpr int EPV = Vec<BF16>::EPV;
     auto wf = [&](int i) { return dense_keeps(thr, x[i], chunk_elem_id<EPV>(c, i, lane)) ? ex((double)x[i] - mc) : 0.0; };
     double margin = -1.0;
@@ -1065,17 +1105,22 @@ __device__ __forceinline__ int propose_test(const RowSource& src, int32_t batch,
     const Draw d = uno_draw(seed, req, (uint32_t)j, offset);
     const int64_t row_bytes = N * Vec<BF16>::ESZ;
     const int64_t qr = linear_row(batch, B, b, j), pr = linear_row(batch, B, b, B + j);
+    // every read of the test goes out before any is used (both rows of a
+    // linear cycle are always present, and y is inside them)
+    const float zq = load_one<BF16>(row_pointer(src, qr, row_bytes), y);
+    const float zp = load_one<BF16>(row_pointer(src, pr, row_bytes), y);
     const double Sq = row_S[qr], Sp = row_S[pr];
-    const double qy = ex((double)load_one<BF16>(row_pointer(src, qr, row_bytes), y) - (double)row_m[qr]) / Sq;
+    const float mq = row_m[qr], mp = row_m[pr];
+    const double Eq = row_E[qr], Ep = row_E[pr];
+    const uint64_t thr = row_keep(dc, pr);
+    const double qy = ex((double)zq - (double)mq) / Sq;
     double py = 0.0;
     if (Sp > 0.0) {
-        const float zp = load_one<BF16>(row_pointer(src, pr, row_bytes), y);
-        if (dense_keeps(row_keep(dc, pr), zp, y)) py = ex((double)zp - (double)row_m[pr]) / Sp;
+        if (dense_keeps(thr, zp, y)) py = ex((double)zp - (double)mp) / Sp;
     } else {
         *flags |= 1u;
     }
     const double lhs = d.u[1] * qy;
-    const double Eq = row_E[qr], Ep = row_E[pr];
     if (Eq > 0.0 || Ep > 0.0) {
         const double rq = Eq / Sq, rp = (Sp > 0.0) ? Ep / Sp : 0.0;
         const double bound = (lhs * rq + py * rp) * (1.0 + 1e-3) + 1e-12 * (lhs + py);
