@@ -1883,20 +1883,39 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
         const bool q_ok = Sq > 0.0;
         const double* R = resid + (int64_t)b * nc;
         const double* RE = resid_err + (int64_t)b * nc;
+        // rows of at most 128 chunks keep both lists in registers (two chunks
+        // per lane), read once; the sums run in the same order either way
+        const bool regs = nc <= 2 * kWave;
+        double r0 = 0.0, r1 = 0.0, e0 = 0.0, e1 = 0.0;
+        if (regs) {
+            if (lane < nc) { r0 = R[lane]; e0 = RE[lane]; }
+            if (lane + kWave < nc) { r1 = R[lane + kWave]; e1 = RE[lane + kWave]; }
+        }
         double Rtot = 0.0, Etot = 0.0;
-        for (int c = lane; c < nc; c += kWave) { Rtot += R[c]; Etot += RE[c]; }
+        if (regs) {
+            Rtot = (Rtot + r0) + r1;
+            Etot = (Etot + e0) + e1;
+        } else {
+            for (int c = lane; c < nc; c += kWave) { Rtot += R[c]; Etot += RE[c]; }
+        }
         Rtot = wave_sum_f64(Rtot);
         Etot = wave_sum_f64(Etot);
         certain = false;
         if (Rtot > 2.0 * Etot) {             // certainly a positive residual
             const double t = d.u[2] * Rtot;
-            auto rterm = [&](int c) { return R[c]; };
+            auto rterm = [&](int c) { return regs ? (c < kWave ? r0 : r1) : R[c]; };
             double before;
             const int c = dense_locate(nc, t, rterm, lane, &before);
             if (c >= 0) {
                 double eb = 0.0;
-                for (int k = lane; k < c; k += kWave) eb += RE[k];
+                if (regs) {
+                    if (lane < c) eb += e0;
+                    if (lane + kWave < c) eb += e1;
+                } else {
+                    for (int k = lane; k < c; k += kWave) eb += RE[k];
+                }
                 eb = wave_sum_f64(eb);
+                const double ec = regs ? lane_value(c < kWave ? e0 : e1, c & (kWave - 1)) : RE[c];
                 float xp[kPerLane], xq[kPerLane];
                 load_chunk<BF16>(prow, N, c, xp, lane);
                 if (q_ok) load_chunk<BF16>(row_pointer(src, qr, row_bytes), N, c, xq, lane);
@@ -1913,7 +1932,7 @@ __global__ __launch_bounds__(kWave) void dense_finish_kernel(
                 };
                 double margin = -1.0;
                 const int l = pick_in_chunk<EPV>(wf, t - before, lane, &margin);
-                const double bound = d.u[2] * Etot + eb + RE[c] + 1e-12 * Rtot;
+                const double bound = d.u[2] * Etot + eb + ec + 1e-12 * Rtot;
                 if (l >= 0 && margin > bound) {
                     certain = true;
                     fin = (int32_t)(c * (int64_t)kDenseChunk + l);
