@@ -195,3 +195,24 @@ def test_linear_8_1_8_nucleus_reduced_batch():
         acc.append(gg["accept_len"])
     t.check_rate()
     say(f"linear_8_1_8 nucleus b8: mean accept_len {np.concatenate(acc).mean():.3f}, excused {t.excused}")
+
+
+# ---- rows of more than 128 dense chunks ----------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("T,p", [(0.9, 1.0), (1.1, 0.9)])
+def test_dense_rows_of_more_than_128_chunks(dtype, T, p):
+    # 300007 logits: 146 whole chunks of 2048 and a ragged one, so the dense
+    # draws read their chunk statistics from memory rather than from two
+    # registers per lane, and bf16 rows start off 16-byte boundaries
+    dev = device()
+    rng = np.random.default_rng(61)
+    batch, B, N = 3, 3, 300007
+    R = (rng.standard_normal((batch, B + 1, N)) * 2).astype(np.float32)
+    d = (R[:, :B] + 0.5 * rng.standard_normal((batch, B, N))).astype(np.float32)
+    draft = torch.from_numpy(d).to(dev).to(dtype).contiguous()
+    target = torch.from_numpy(R).to(dev).to(dtype).contiguous()
+    t = Tally(f"long dense rows {dtype} T{T} p{p}")
+    for c in range(3):
+        _run(draft, target, T, 0, p, 7, 500 + c, tally=t, label=f"long dense rows {dtype} T{T} p{p} cycle {c}")
+    t.check_rate()

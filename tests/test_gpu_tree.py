@@ -194,9 +194,10 @@ def test_dense_tree_8_16_8_reduced_batch():
 
 @pytest.mark.parametrize("B,K,V,T,N,bf16", [(3, 3, 10, 1.0, 5000, False), (2, 8, 16, 0.5, 4099, True),
                                             (5, 16, 128, 1.0, 3 * 2048, False), (4, 256, 8, 1.0, 700, False),
-                                            (6, 4, 20, 2.0, 257, True)])
+                                            (6, 4, 20, 2.0, 257, True), (3, 4, 12, 1.0, 300007, True)])
 def test_dense_tree_shapes(B, K, V, T, N, bf16):
-    # several chunks and a ragged tail, K up to the top-k limit, V up to 128
+    # several chunks and a ragged tail, K up to the top-k limit, V up to 128,
+    # rows of more than 128 chunks
     dev = device()
     rng = np.random.default_rng(B * 1000 + K + N)
     batch = 10
