@@ -2392,53 +2392,102 @@ __global__ __launch_bounds__(NW * kWave, NW == 4 ? 3 : 2) void nucleus_kernel(
 // ---- dense tree (full-vocabulary filters) ------------------------------------------
 // Target-sampled walk over node rows whose filter keeps the whole vocabulary:
 // each live node's token is drawn from its row's exact chunk statistics (one
-// wave per node, the uniform of the node's depth), then wave 0 follows the
-// path as in the sparse walk.
+// wave per node row over the whole chip, the uniform of the node's depth),
+// then one wave per request follows the path as in the sparse walk.
+// Every node row's draw for the dense walk, one wave per row over the whole
+// chip (a request's nodes side by side on several CUs): the node's depth from
+// the request's parent links, held three per lane, the row statistics from
+// its chunk sums, and the draw with the uniform of that depth; -1 where the
+// walk cannot take it (no valid path to the root, deeper than B, past the
+// request's node count, or no mass).
+constexpr int kDrawThreads = 256;
+constexpr int kDrawWaves = kDrawThreads / kWave;
+static_assert(kMaxNodes <= 3 * kWave, "a wave holds a request's parent links three per lane");
+
 template <bool BF16>
-__global__ __launch_bounds__(kWalkThreads) void dense_walk_kernel(
+__global__ __launch_bounds__(kDrawThreads) void dense_node_draw_kernel(
     RowSource src, int32_t batch, int32_t B, int32_t V, int64_t N, double log2e_over_T, DenseChunks dc,
-    uint64_t seed, uint64_t offset, const uint32_t* req_ids, const int32_t* node_token,
-    const int32_t* node_parent, const int32_t* num_nodes, WalkOut o, const FilterParams* rowp)
+    uint64_t seed, uint64_t offset, const uint32_t* req_ids, const int32_t* node_parent,
+    const int32_t* num_nodes, int32_t* node_draw, const FilterParams* rowp)
 {
     __shared__ double s_exp2[kExp2Entries];
-    __shared__ TreeLds L;
-    __shared__ int32_t s_t[kMaxNodes];
-    if (rowp) {
-        const FilterParams& f = rowp[(int64_t)blockIdx.x * (V + 1)];
-        if (f.dense == kRowTopK) return;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t rows = (int64_t)batch * (V + 1);
+    const int64_t r = (int64_t)blockIdx.x * kDrawWaves + w;
+    const bool live = r < rows;                                    // wave-uniform
+    const int b = live ? (int)(r / (V + 1)) : 0;
+    const int n = (int)(r - (int64_t)b * (V + 1));
+    const int64_t ob = (int64_t)b * (V + 1);
+    // the request's reads go out before the table's
+    int nn = live ? num_nodes[b] : 1;
+    const uint32_t req = (live && req_ids) ? req_ids[b] : (uint32_t)b;
+    int p0 = -1, p1 = -1, p2 = -1;
+    if (live) {
+        if (lane <= V) p0 = node_parent[ob + lane];
+        if (lane + kWave <= V) p1 = node_parent[ob + lane + kWave];
+        if (lane + 2 * kWave <= V) p2 = node_parent[ob + lane + 2 * kWave];
+    }
+    bool dense = live;
+    if (live && rowp) {
+        const FilterParams& f = rowp[ob];
+        dense = f.dense != kRowTopK;
         log2e_over_T = 1.4426950408889634074 / (double)f.temperature;
     }
     load_exp2_table(s_exp2);
-    const int lane = lane_id();
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    __syncthreads();
+    if (!dense) return;
+    nn = nn < 1 ? 1 : (nn > V + 1 ? V + 1 : nn);
+    // depth: the root is node 0; a node's parent must precede it, so a walk up
+    // the links ends at the root or at an invalid link within n steps
+    int dep = -1;
+    if (n < nn) {
+        int x = n, d = 0;
+        while (x > 0) {
+            const int pr = __builtin_amdgcn_readlane(x < kWave ? p0 : (x < 2 * kWave ? p1 : p2), x & (kWave - 1));
+            if (!(pr >= 0 && pr < x)) { d = -1; break; }
+            x = pr;
+            ++d;
+        }
+        dep = d;
+    }
+    int32_t t = -1;
+    if (dep >= 0 && dep <= B) {
+        const DenseExp ex{ log2e_over_T, s_exp2 };
+        const int nc = dc.nchunks;
+        const float* cm = dc.cmax + r * nc;
+        const double* cs = dc.csum + r * nc;
+        float m;
+        double S;
+        if (dense_row_stat(cm, cs, nc, ex, lane, &m, &S)) {
+            const Draw dr = uno_draw(seed, req, (uint32_t)dep, offset);
+            t = dense_sample_row<BF16>(row_pointer(src, r, N * Vec<BF16>::ESZ), N, cm, cs, nc, m, S, dr.u[2], ex,
+                                       lane, row_keep(dc, r));
+        }
+    }
+    if (lane == 0) node_draw[r] = t;
+}
+
+// The dense walk itself, one workgroup per request: the depths and links in
+// LDS, then one wave follows the path through the node draws.
+constexpr int kFollowThreads = 192;
+static_assert(kFollowThreads >= kMaxNodes, "tree_depths takes one thread per node");
+
+__global__ __launch_bounds__(kFollowThreads) void dense_walk_kernel(int32_t B, int32_t V, const int32_t* node_token,
+                                                                   const int32_t* node_parent,
+                                                                   const int32_t* num_nodes, const int32_t* node_draw,
+                                                                   WalkOut o, const FilterParams* rowp)
+{
+    __shared__ TreeLds L;
+    __shared__ int32_t s_t[kMaxNodes];
     const int b = blockIdx.x;
-    const uint32_t req = req_ids ? req_ids[b] : (uint32_t)b;
+    const int64_t ob = (int64_t)b * (V + 1);
+    if (rowp && rowp[ob].dense == kRowTopK) return;
     int nn = num_nodes[b];
     nn = nn < 1 ? 1 : (nn > V + 1 ? V + 1 : nn);
-    const int64_t ob = (int64_t)b * (V + 1);
-    tree_depths(node_token, node_parent, ob, nn, V, L);      // its barriers also publish the table
-    const DenseExp ex{ log2e_over_T, s_exp2 };
-    const int nc = dc.nchunks;
-    const int64_t row_bytes = N * Vec<BF16>::ESZ;
-    for (int n = w; n < nn; n += kWalkWaves) {
-        const int dep = L.dep[n];
-        int32_t t = -1;
-        if (dep >= 0 && dep <= B) {
-            const int64_t r = ob + n;
-            const float* cm = dc.cmax + r * nc;
-            const double* cs = dc.csum + r * nc;
-            float m;
-            double S;
-            if (dense_row_stat(cm, cs, nc, ex, lane, &m, &S)) {
-                const Draw d = uno_draw(seed, req, (uint32_t)dep, offset);
-                t = dense_sample_row<BF16>(row_pointer(src, r, row_bytes), N, cm, cs, nc, m, S, d.u[2], ex, lane,
-                                           row_keep(dc, r));
-            }
-        }
-        if (lane == 0) s_t[n] = t;
-    }
-    __syncthreads();
-    if (w == 0) follow_path(b, B, nn, s_t, L, o, lane);
+    for (int n = (int)threadIdx.x; n < nn; n += kFollowThreads) s_t[n] = node_draw[ob + n];
+    tree_depths(node_token, node_parent, ob, nn, V, L);      // its barriers also publish s_t
+    if (threadIdx.x < kWave) follow_path(b, B, nn, s_t, L, o, lane_id());
 }
 
 // Tree build over full-vocabulary filters: the top-K supports come normalised
@@ -2621,18 +2670,23 @@ hipError_t launch_tree_walk(int32_t batch, int32_t B, int32_t V, const SparseOut
 hipError_t launch_tree_walk_dense(const RowSource& src, int32_t batch, int32_t B, int32_t V, int64_t vocab,
                                   bool bf16, float temperature, const DenseChunks& dc, uint64_t seed,
                                   uint64_t offset, const uint32_t* request_ids, const int32_t* node_token,
-                                  const int32_t* node_parent, const int32_t* num_nodes, const WalkOut& o,
-                                  hipStream_t stream, const FilterParams* rowp)
+                                  const int32_t* node_parent, const int32_t* num_nodes, int32_t* node_draw,
+                                  const WalkOut& o, hipStream_t stream, const FilterParams* rowp)
 {
+    if (node_draw == nullptr || V + 1 > kMaxNodes) return hipErrorInvalidValue;
     const double c = 1.4426950408889634074 / (double)temperature;
+    const int64_t rows = (int64_t)batch * (V + 1);
+    const dim3 dgrid((unsigned)((rows + kDrawWaves - 1) / kDrawWaves));
     if (bf16)
-        dense_walk_kernel<true><<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
-            src, batch, B, V, vocab, c, dc, seed, offset, request_ids, node_token, node_parent, num_nodes, o,
-            rowp);
+        dense_node_draw_kernel<true><<<dgrid, kDrawThreads, 0, stream>>>(src, batch, B, V, vocab, c, dc, seed, offset,
+                                                                        request_ids, node_parent, num_nodes,
+                                                                        node_draw, rowp);
     else
-        dense_walk_kernel<false><<<dim3((unsigned)batch), kWalkThreads, 0, stream>>>(
-            src, batch, B, V, vocab, c, dc, seed, offset, request_ids, node_token, node_parent, num_nodes, o,
-            rowp);
+        dense_node_draw_kernel<false><<<dgrid, kDrawThreads, 0, stream>>>(src, batch, B, V, vocab, c, dc, seed,
+                                                                         offset, request_ids, node_parent, num_nodes,
+                                                                         node_draw, rowp);
+    dense_walk_kernel<<<dim3((unsigned)batch), kFollowThreads, 0, stream>>>(B, V, node_token, node_parent, num_nodes,
+                                                                            node_draw, o, rowp);
     return hipGetLastError();
 }
 

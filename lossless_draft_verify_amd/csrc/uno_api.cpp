@@ -161,6 +161,7 @@ struct SparseWs {
     int32_t* part_n;
     DenseChunks full;    // joint order: exact chunk statistics of the rows
     int32_t* nucleus_n;  // tree build with nucleus rows: support sizes
+    int32_t* node_draw;  // dense tree walk: every node row's draw
     FilterParams* rowp;  // per-request parameters: one set per row
     int part_cap;        // entries per segment list (the largest k)
 };
@@ -422,6 +423,7 @@ int layout_tree(int32_t op, int64_t batch, int32_t B, int32_t K, int32_t V, int6
         // the walk samples top-k rows in id order
         if (m->any_sparse) carve_sparse(cv, rows, vocab, *m, true, true, sw);
         if (m->any_dense && !m->per_request) *dc = carve_chunks(cv, rows, vocab, false, m->nucleus);
+        sw->node_draw = m->any_dense ? cv.take<int32_t>((size_t)rows) : nullptr;
     }
     return UNO_OK;
 }
@@ -666,7 +668,8 @@ int uno_verify_tree_ex(const void* target, int32_t dtype, int32_t batch, int32_t
                                nucleus_rows(m, rows));
         if (e == hipSuccess)
             e = launch_tree_walk_dense(src, batch, B, V, vocab, bf16, sp->temperature, dc, seed, offset,
-                                       request_ids, node_token, node_parent, num_nodes, o, stream, rowp);
+                                       request_ids, node_token, node_parent, num_nodes, sw.node_draw, o, stream,
+                                       rowp);
     }
     return hip_status(e);
 }

@@ -238,12 +238,13 @@ hipError_t launch_dense_support_scale(int64_t rows, float temperature, const Den
                                       const FilterParams* rowp = nullptr);
 
 // rowp (nullable): only the requests whose rows are not kRowTopK walk here,
-// each at its own temperature.
+// each at its own temperature.  node_draw: batch * (V + 1) entries of
+// workspace, every node row's draw, which the walk then follows.
 hipError_t launch_tree_walk_dense(const RowSource& src, int32_t batch, int32_t B, int32_t V, int64_t vocab,
                                   bool bf16, float temperature, const DenseChunks& dc, uint64_t seed,
                                   uint64_t offset, const uint32_t* request_ids, const int32_t* node_token,
-                                  const int32_t* node_parent, const int32_t* num_nodes, const WalkOut& o,
-                                  hipStream_t stream, const FilterParams* rowp = nullptr);
+                                  const int32_t* node_parent, const int32_t* num_nodes, int32_t* node_draw,
+                                  const WalkOut& o, hipStream_t stream, const FilterParams* rowp = nullptr);
 
 // Tree-suffix attention merged with the prefix state (head dimension 128,
 // bf16 tensors, fp32 log-sum-exps); one workgroup per (request, kv head).
