@@ -89,7 +89,7 @@ def test_workspace_sizes(lib):
     st, nbd = _ws(lib, uno.OP_BUILD_TREE, 1, 16, 32, 32, N, F32, sp(1.0, 0, 1.0))
     assert st == OK and nbd >= 16 * nch * (4 + 8) + 16 * 32 * (4 + 8) + 16 * 16
     st, nvd = _ws(lib, uno.OP_VERIFY_TREE, 1, 16, 1, 32, N, F32, sp(1.0, 0, 1.0))
-    assert st == OK and nvd >= 33 * nch * (4 + 8)
+    assert st == OK and nvd >= 33 * nch * (4 + 8) + 33 * 4      # and one draw per node row
     # joint order: exact chunk statistics of every filtered row on top of the supports
     st, nj = _ws(lib, uno.OP_SAMPLE_LINEAR, 64, 8, 1, 8, N, F32, sp(order=uno.ORDER_JOINT))
     assert st == OK and nj >= n + 1088 * nch * (4 + 8)
